@@ -1,0 +1,155 @@
+/*
+ * ocrdec -- C ABI of the FastMTP speculative decode path of the jina-ocr-v1
+ * decoder (DeepSeek-3B-MoE: 12 layers, d = 1280, 64 routed + 2 shared experts,
+ * top-6, vocabulary 129,280, RoPE theta 1e6) on one AMD Instinct MI355X (gfx950).
+ *
+ * The four decode calls follow the method the jina-ocr-v1 blog describes in
+ * "Model and training": one shared dense draft block proposes K tokens by
+ * recursion, the verifier checks the K+1 rows greedily in one pass and keeps
+ * the longest agreeing prefix plus its own next token, so the committed
+ * sequence is exactly the verifier's greedy sequence.
+ *
+ * Conventions (all calls):
+ *   - Every device buffer (weights, state, workspace, inputs, outputs) is
+ *     allocated and owned by the caller and must outlive the model handle.
+ *     The library never allocates device memory.
+ *   - `stream` is a hipStream_t passed as void*.  Calls only enqueue work on
+ *     it; outputs are valid once the stream has been synchronised.  No call
+ *     synchronises the host.
+ *   - Return 0 on success, or a negative OCRDEC_E* code; then nothing was
+ *     enqueued and the state is unchanged.  ocrdec_last_error() returns a
+ *     thread-local message describing the last failure.
+ *   - `slots` (device int32 [B], or NULL for 0..B-1) maps the B sequences of a
+ *     call to state slots < max_batch; slots in one call must be distinct.
+ *   - Token ids read from device buffers are clamped to [0, vocab).
+ *   - Calls on one model handle must be issued in order on one stream; they
+ *     share the workspace.
+ */
+#ifndef OCRDEC_H
+#define OCRDEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define OCRDEC_OK 0
+#define OCRDEC_EINVAL (-1)     /* null / misaligned pointer, bad B or K, unsupported shape */
+#define OCRDEC_ECAPACITY (-2)  /* B > max_batch, K > max_k, positions past max_positions */
+#define OCRDEC_EHIP (-3)       /* a HIP runtime call failed */
+
+#define OCRDEC_F32 0           /* fp32 weights, fp32 KV cache */
+#define OCRDEC_BF16 1          /* bf16 weights and embedding, bf16 KV cache */
+
+/* Model shape and capacity (plain data).  The kernels are built for the
+ * decoder shape of the pages' spec table: d_model 1280, 10 heads x 128,
+ * 64 routed + 2 shared experts of width 896, top-6, draft FFN 3584; other
+ * values of those fields are rejected with OCRDEC_EINVAL.  n_layers >= 1,
+ * vocab >= 1, max_positions <= 32768 (the pages' position limit). */
+typedef struct {
+  int n_layers, d_model, n_heads, head_dim, n_experts, n_shared, top_k, d_expert, d_draft_ffn, vocab;
+  float rope_theta, norm_eps;
+  int dtype;                                   /* OCRDEC_F32 | OCRDEC_BF16 */
+  int max_batch, max_k, max_positions;
+} ocrdec_config;
+
+typedef struct ocrdec_model ocrdec_model;
+
+/* Bytes of the per-sequence decode state (verifier and draft KV caches,
+ * lengths, pending tokens, hidden-state feedback rows) and of the scratch
+ * workspace.  Both buffers must be 256-byte aligned.  The state needs no
+ * initialisation; ocrdec_prefill initialises a slot. */
+size_t ocrdec_state_bytes(const ocrdec_config* cfg);
+size_t ocrdec_workspace_bytes(const ocrdec_config* cfg);
+
+/* Number of weight tensors and their canonical order (row-major, y = W x, W is
+ * [out, in]); matrices in the model dtype, RMSNorm gains always fp32:
+ *   0 embed [V,d]   1 lm_head [V,d]   2 final_norm [d]
+ *   per layer l, base 3 + 8 l:
+ *     attn_norm [d], wqkv [3*1280, d] (q, k, v rows, head-major), wo [d, 1280],
+ *     ffn_norm [d], router [64, d], w_gate [66, 896, d], w_up [66, 896, d],
+ *     w_down [66, d, 896]   (experts 0..63 routed, 64..65 shared)
+ *   draft, base 3 + 8 L: norm_h [d], norm_e [d], fuse [d, 2d], attn_norm [d],
+ *     wqkv [3*1280, d], wo [d, 1280], ffn_norm [d], w_gate [3584, d],
+ *     w_up [3584, d], w_down [d, 3584], out_norm [d]
+ * Every pointer must be 16-byte aligned. */
+int ocrdec_num_weights(const ocrdec_config* cfg);
+
+/* Create a handle over caller-owned device memory.  Zeroes the workspace's
+ * counters on `stream` (pass the stream later calls use).  */
+int ocrdec_create(const ocrdec_config* cfg, const void* const* weight_ptrs, int n_weights,
+                  void* state, void* workspace, void* stream, ocrdec_model** out);
+int ocrdec_destroy(ocrdec_model* m);
+
+/* Prefill B sequences (host arrays slots_host, n_vision_host, n_prompt_host):
+ * rows 0..Nv-1 are the vision rows vision[b] (device fp32 [B][nv_stride][d]),
+ * rows Nv..Nv+Np-1 the embeddings of prompt[b] (device int32 [B][np_stride]).
+ * Runs the verifier over the prefix (filling its KV cache), the draft block over
+ * the same rows (filling the draft KV cache; draft row p takes the verifier
+ * hidden of p-1), and writes the greedy token of the last prefix row -- output
+ * token 0 -- to pending_out[b] (device int32 [B]).  After the call the slot's
+ * committed-output count is 1.  OCRDEC_ECAPACITY if Nv+Np+max_k+1 > max_positions. */
+int ocrdec_prefill(ocrdec_model* m, void* stream, int B, const int32_t* slots_host,
+                   const float* vision, int nv_stride, const int32_t* n_vision_host,
+                   const int32_t* prompt, int np_stride, const int32_t* n_prompt_host,
+                   int32_t* pending_out);
+
+/* FastMTP draft (the pages' "one shared dense block applied recursively for K
+ * steps"): pass 1 recomputes the rows accepted at the last verify plus the
+ * pending token from the verifier's hidden states (catch-up) and proposes d_1;
+ * passes 2..K feed the block's own output back.  draft_out: device int32 [B][K]. */
+int ocrdec_draft(ocrdec_model* m, void* stream, int B, const int32_t* slots, int K, int32_t* draft_out);
+
+/* Verifier pass over rows [pending, d_1..d_K] of each sequence at positions
+ * kv_len..kv_len+K through all layers; writes their keys/values to the cache and
+ * the greedy token of every row to greedy_out (device int32 [B][K+1]).
+ * logits_out (nullable, device fp32 [B][K+1][vocab]) receives the final logits.
+ * K = 0 is plain autoregressive decoding (draft ignored, may be NULL). */
+int ocrdec_verify(ocrdec_model* m, void* stream, int B, const int32_t* slots, int K,
+                  const int32_t* draft, int32_t* greedy_out, float* logits_out);
+
+/* Greedy longest-prefix acceptance (blog, "Model and training") with KV
+ * rollback: n = the longest j <= K with d_i == g_{i-1} for all i <= j; commits
+ * d_1..d_n and the bonus token g_n; the verifier cache keeps positions up to the
+ * last committed token, rejected positions are dropped by a length update (no
+ * data moves).  Writes n to n_accepted_out[b] (device int32 [B]) and appends the
+ * n+1 tokens to out_tokens[b][out_len..] (device int32 [B][out_cap], tokens at
+ * index >= out_cap are dropped); out_len (device int32 [B], nullable) receives
+ * the new committed count (including output token 0 from the prefill). */
+int ocrdec_accept_rollback(ocrdec_model* m, void* stream, int B, const int32_t* slots, int K,
+                           const int32_t* draft, const int32_t* greedy, int32_t* n_accepted_out,
+                           int32_t* out_tokens, int32_t* out_len, int out_cap);
+
+/* Benchmark harness (not part of the method): overwrite draft[b][j-1] with the
+ * token a lossless run commits at that place, trace[b][out_len-1+j] (device
+ * int32 [B][trace_stride], ids past trace_len read as 0), replaced -- when the
+ * top 53 bits of H = SplitMix64-chain(seed, b_index, step, j) fall below
+ * `threshold` -- by (true + 1 + (H mod 2^32) mod (vocab-1)) mod vocab, which is
+ * never the true token.  b_index is the sequence's slot. */
+int ocrdec_controlled_drafts(ocrdec_model* m, void* stream, int B, const int32_t* slots, int K,
+                             const int32_t* trace, int trace_stride, int trace_len,
+                             uint64_t seed, uint64_t threshold, int32_t* draft_inout);
+
+/* Parity taps (nullable device pointers, used by later verify/prefill calls):
+ * route_idx int32 [n_layers][rows][8] receives each layer's routing (6 routed
+ * experts by decreasing score, then the shared experts 64, 65); hidden fp32
+ * [rows][d] receives the final pre-norm hidden rows of the last verify. */
+int ocrdec_set_taps(ocrdec_model* m, int32_t* route_idx, float* hidden);
+
+/* Kernel timing of the grouped expert GEMV (gate/up and down launches):
+ * enable != 0 records HIP events around each launch from now on (clears the
+ * totals).  ocrdec_expert_stats synchronises those events and returns the
+ * total milliseconds and launch count of each of the two kernels, and the
+ * number of (layer, expert) weight sets they streamed, counted on the device. */
+int ocrdec_expert_timing(ocrdec_model* m, int enable);
+int ocrdec_expert_stats(ocrdec_model* m, double* ms_gate_up, long long* n_gate_up, double* ms_down,
+                        long long* n_down, long long* expert_sets);
+
+const char* ocrdec_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* OCRDEC_H */

@@ -1,0 +1,207 @@
+// Shared device helpers of the ocrdec kernels (gfx950, wave64).
+//
+// Numerics that every kernel follows, so that a row's result never depends on
+// how many other rows share its launch (speculative == autoregressive, bit for
+// bit):
+//   * dot products: lane l of a wavefront owns the 16-byte chunks l, l+64, ...
+//     of a weight row and accumulates them in order with fmaf; the 64 lane sums
+//     are then added by a fixed xor butterfly (32, 16, 8, 4, 2, 1);
+//   * row reductions of 256-thread blocks (RMSNorm): each thread sums its
+//     elements k = tid + 256 j in order, then the same butterfly per wave, then
+//     the four wave sums in order 0..3;
+//   * no floating-point atomics anywhere.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ocr {
+
+constexpr int D = 1280;          // d_model
+constexpr int NH = 10;           // attention heads
+constexpr int HD = 128;          // head dim
+constexpr int QD = NH * HD;      // 1280
+constexpr int NE = 64;           // routed experts
+constexpr int NSH = 2;           // shared experts
+constexpr int NX = NE + NSH;     // expert tensors per layer
+constexpr int TOPK = 6;
+constexpr int NSLOT = TOPK + NSH;  // routing slots per row: 6 routed then 2 shared
+constexpr int DI = 896;          // expert width
+constexpr int DF = 3584;         // draft FFN width
+constexpr int MRG = 8;           // activation rows per GEMV group
+constexpr int PREFILL_CHUNK = 8; // prefix rows per prefill pass
+constexpr int ATT_TILE = 64;     // keys per LDS tile in decode attention
+constexpr int LM_ROWS_PER_BLOCK = 64;
+
+typedef uint16_t bf16;
+
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <typename T> struct WT;
+template <> struct WT<float> {
+  static constexpr int CE = 4;  // elements per 16-byte chunk
+  __device__ static __forceinline__ void cvt(const uint4& v, float* o) {
+    o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y);
+    o[2] = __uint_as_float(v.z); o[3] = __uint_as_float(v.w);
+  }
+  __device__ static __forceinline__ float load1(const float* p) { return *p; }
+  __device__ static __forceinline__ float store_cvt(float v) { return v; }
+};
+template <> struct WT<bf16> {
+  static constexpr int CE = 8;
+  __device__ static __forceinline__ void cvt(const uint4& v, float* o) {
+    o[0] = __uint_as_float(v.x << 16); o[1] = __uint_as_float(v.x & 0xffff0000u);
+    o[2] = __uint_as_float(v.y << 16); o[3] = __uint_as_float(v.y & 0xffff0000u);
+    o[4] = __uint_as_float(v.z << 16); o[5] = __uint_as_float(v.z & 0xffff0000u);
+    o[6] = __uint_as_float(v.w << 16); o[7] = __uint_as_float(v.w & 0xffff0000u);
+  }
+  __device__ static __forceinline__ float load1(const bf16* p) { return __uint_as_float((uint32_t)*p << 16); }
+  __device__ static __forceinline__ bf16 store_cvt(float v) { return f2bf(v); }
+};
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+__device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Sum over a 256-thread block in the fixed order described above.  `red` is
+// LDS scratch of at least 4 floats; contains a barrier.
+__device__ __forceinline__ float block_sum256(float v, float* red) {
+  v = wave_sum(v);
+  if (lane_id() == 0) red[wave_id()] = v;
+  __syncthreads();
+  float t = red[0];
+  t += red[1];
+  t += red[2];
+  t += red[3];
+  __syncthreads();
+  return t;
+}
+
+// RMSNorm of `m_rows` rows of length K (K % 256 == 0) into LDS:
+// xs[m][k] = (x[m][k] * r_m) * g[k] with r_m = 1 / sqrt(sum_k x^2 / K + eps).
+// g == nullptr copies the rows unchanged.  All 256 threads must call it.
+template <int K>
+__device__ __forceinline__ void norm_rows_to_lds(const float* __restrict__ x, long ldx, int m_rows,
+                                                 const float* __restrict__ g, float eps, float* xs,
+                                                 float* red) {
+  static_assert(K % 256 == 0, "row length must be a multiple of 256");
+  constexpr int J = K / 256;
+  const int tid = threadIdx.x;
+  for (int m = 0; m < m_rows; ++m) {
+    const float* xr = x + (long)m * ldx;
+    float v[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) v[j] = xr[tid + 256 * j];
+    if (g != nullptr) {
+      float ss = 0.f;
+#pragma unroll
+      for (int j = 0; j < J; ++j) ss = fmaf(v[j], v[j], ss);
+      ss = block_sum256(ss, red);
+      const float r = 1.0f / sqrtf(ss / (float)K + eps);
+#pragma unroll
+      for (int j = 0; j < J; ++j) xs[m * K + tid + 256 * j] = (v[j] * r) * g[tid + 256 * j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < J; ++j) xs[m * K + tid + 256 * j] = v[j];
+    }
+  }
+}
+
+// Wavefront GEMV core: R weight rows (pointers rows[r], each K elements of T)
+// against `m_act` (<= MR) activation rows held in LDS (xs[m][K], fp32).
+// acc[r][m] holds the lane partial sums; call wave_reduce_acc afterwards.
+// Loads of all R rows are issued before any arithmetic.
+template <typename T, int K, int R, int MR>
+struct WaveGemv {
+  static constexpr int CE = WT<T>::CE;
+  static constexpr int NCH = K / CE;          // 16-byte chunks per row
+  static constexpr int NT = (NCH + 63) / 64;  // per-lane chunk iterations
+  static_assert(K % CE == 0, "K must be a multiple of the chunk size");
+  uint4 w[R][NT];
+
+  __device__ __forceinline__ void load(const T* const* rows) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int c = lane + 64 * t;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (c < NCH) w[r][t] = ldg16(rows[r] + (long)c * CE);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void fma(const float* xs, int m_act, float (&acc)[R][MR]) const {
+    const int lane = lane_id();
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int m = 0; m < MR; ++m) acc[r][m] = 0.f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int c = lane + 64 * t;
+      if (c < NCH) {
+        float wf[R][CE];
+#pragma unroll
+        for (int r = 0; r < R; ++r) WT<T>::cvt(w[r][t], wf[r]);
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+          if (m < m_act) {
+            float xa[CE];
+            const float4* xp = reinterpret_cast<const float4*>(xs + m * K + c * CE);
+#pragma unroll
+            for (int q = 0; q < CE / 4; ++q) {
+              float4 f = xp[q];
+              xa[4 * q] = f.x; xa[4 * q + 1] = f.y; xa[4 * q + 2] = f.z; xa[4 * q + 3] = f.w;
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+              for (int e = 0; e < CE; ++e) acc[r][m] = fmaf(wf[r][e], xa[e], acc[r][m]);
+          }
+        }
+      }
+    }
+  }
+};
+
+template <int R, int MR>
+__device__ __forceinline__ void wave_reduce_acc(float (&acc)[R][MR], int m_act) {
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    if (m < m_act) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r][m] = wave_sum(acc[r][m]);
+    }
+  }
+}
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+
+// Per-call row plan: sequence b of a call owns rows b*Q .. b*Q+Q-1; row i of
+// it is valid when i < cnt[b] and sits at position base[b] + i.
+struct RowPlan {
+  const int* base;
+  const int* cnt;
+  const int* slot;   // state slot of sequence b
+  int Q;
+};
+
+}  // namespace ocr

@@ -1,0 +1,152 @@
+// Decode attention over the KV cache (split-KV with fixed, tile-aligned chunk
+// boundaries) and its combine.
+//
+// Block (chunk c, head h, sequence b) stages the keys and values of
+// ATT_TILE-key tiles of chunk c in LDS (keys transposed, both widened to fp32)
+// and serves every query row of sequence b from them (the K+1 verify rows, or
+// a prefill chunk), so one KV read feeds all of the sequence's queries.  A
+// query at position p sees keys 0..p.  Per query the block keeps an online
+// softmax (running max m, sum l, output o) across its tiles and writes
+// (o, m, l); the combine kernel merges chunks 0..p/C in order.  Because chunk
+// boundaries are fixed multiples of C and masked keys contribute exact zeros,
+// a query's result does not depend on which other queries share the launch.
+#include "launch.h"
+
+namespace ocr {
+
+constexpr int QMAX_ATT = 8;  // query rows per sequence handled by one block
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_attn_partial(const float* __restrict__ q, const T* __restrict__ kv,
+                                                      int max_pos, RowPlan plan, int n_chunks,
+                                                      int tiles_per_chunk, float* __restrict__ part) {
+  __shared__ float Kt[HD][ATT_TILE + 1];
+  __shared__ float Vs[ATT_TILE][HD];
+  __shared__ float qs[QMAX_ATT][HD];
+  __shared__ float ps[4][ATT_TILE];
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int wave = wave_id(), lane = lane_id(), tid = threadIdx.x;
+  const int Q = plan.Q;
+  const int base = plan.base[b];
+  // rows past the cache (never produced by the library's own plans) are skipped
+  const int cnt = (base < 0) ? 0 : min(min(plan.cnt[b], Q), max_pos - base);
+  const int p_last = base + cnt - 1;
+  const int C = tiles_per_chunk * ATT_TILE;
+  const int k0 = c * C;
+  if (cnt <= 0 || k0 > p_last) return;
+  const long slot = plan.slot[b];
+  const T* Kc = kv + slot * (2L * NH * max_pos * HD) + (long)h * max_pos * HD;
+  const T* Vc = Kc + (long)NH * max_pos * HD;
+  // queries of this sequence / head
+  for (int e = tid; e < cnt * HD; e += 256) {
+    const int i = e / HD, d = e % HD;
+    qs[i][d] = q[(long)(b * Q + i) * QD + h * HD + d];
+  }
+  const float scale = 0.08838834764831845f;  // 1 / sqrt(128)
+  // per-wave query state: queries wave, wave + 4
+  float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
+  float o0[2] = {0.f, 0.f}, o1[2] = {0.f, 0.f};
+  constexpr int CE = WT<T>::CE;
+  for (int tt = 0; tt < tiles_per_chunk; ++tt) {
+    const int kt = k0 + tt * ATT_TILE;
+    if (kt > p_last) break;
+    const int nk = min(ATT_TILE, p_last + 1 - kt);
+    __syncthreads();
+    // stage K (transposed) and V of this tile, fp32
+    for (int e = tid; e < ATT_TILE * HD / CE; e += 256) {
+      const int t = e / (HD / CE), d0 = (e % (HD / CE)) * CE;
+      float kf[CE], vf[CE];
+      if (t < nk) {
+        WT<T>::cvt(ldg16(Kc + (long)(kt + t) * HD + d0), kf);
+        WT<T>::cvt(ldg16(Vc + (long)(kt + t) * HD + d0), vf);
+      } else {
+#pragma unroll
+        for (int j = 0; j < CE; ++j) { kf[j] = 0.f; vf[j] = 0.f; }
+      }
+#pragma unroll
+      for (int j = 0; j < CE; ++j) { Kt[d0 + j][t] = kf[j]; Vs[t][d0 + j] = vf[j]; }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+      const int i = wave + 4 * qq;
+      if (i >= cnt) continue;
+      const int plim = base + i;  // last visible key of query i
+      if (kt > plim) continue;
+      // lane = key t of the tile
+      float sc = 0.f;
+#pragma unroll 8
+      for (int d = 0; d < HD; ++d) sc = fmaf(qs[i][d], Kt[d][lane], sc);
+      sc = sc * scale;
+      const bool vis = (kt + lane) <= plim;
+      const float mt = wave_max(vis ? sc : -INFINITY);
+      const float mnew = fmaxf(mrun[qq], mt);
+      const float corr = expf(mrun[qq] - mnew);
+      const float p = vis ? expf(sc - mnew) : 0.f;
+      lrun[qq] = lrun[qq] * corr + wave_sum(p);
+      ps[wave][lane] = p;
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      float a0 = o0[qq] * corr, a1 = o1[qq] * corr;
+#pragma unroll 8
+      for (int t = 0; t < ATT_TILE; ++t) {
+        const float pt = ps[wave][t];
+        a0 = fmaf(pt, Vs[t][2 * lane], a0);
+        a1 = fmaf(pt, Vs[t][2 * lane + 1], a1);
+      }
+      o0[qq] = a0;
+      o1[qq] = a1;
+      mrun[qq] = mnew;
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+#pragma unroll
+  for (int qq = 0; qq < 2; ++qq) {
+    const int i = wave + 4 * qq;
+    if (i >= cnt || k0 > base + i) continue;
+    float* pp = part + ((((long)b * NH + h) * n_chunks + c) * Q + i) * (HD + 2);
+    pp[2 * lane] = o0[qq];
+    pp[2 * lane + 1] = o1[qq];
+    if (lane == 0) { pp[HD] = mrun[qq]; pp[HD + 1] = lrun[qq]; }
+  }
+}
+
+// Merge chunks 0..p/C of each (row, head) in order.  Block = 2 heads x 128 dims.
+__global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ part, RowPlan plan, int n_chunks,
+                                                      int chunk_keys, int max_pos, float* __restrict__ out) {
+  const int row = blockIdx.x;
+  const int h = blockIdx.y * 2 + (threadIdx.x >> 7);
+  const int d = threadIdx.x & 127;
+  const int b = row / plan.Q, i = row - b * plan.Q;
+  float* o = out + (long)row * QD + h * HD + d;
+  const int p = plan.base[b] + i;
+  if (i >= plan.cnt[b] || p < 0 || p >= max_pos) { *o = 0.f; return; }
+  const int nc = min(p / chunk_keys + 1, n_chunks);
+  const float* pp = part + (((long)b * NH + h) * n_chunks) * plan.Q * (HD + 2) + (long)i * (HD + 2);
+  const long cstride = (long)plan.Q * (HD + 2);
+  float mg = -INFINITY;
+  for (int c = 0; c < nc; ++c) mg = fmaxf(mg, pp[c * cstride + HD]);
+  float L = 0.f, O = 0.f;
+  for (int c = 0; c < nc; ++c) {
+    const float w = expf(pp[c * cstride + HD] - mg);
+    L = fmaf(pp[c * cstride + HD + 1], w, L);
+    O = fmaf(pp[c * cstride + d], w, O);
+  }
+  *o = O / L;
+}
+
+template <typename T>
+void launch_attention(hipStream_t s, const float* q, const T* kv, int max_pos, RowPlan plan, int B, int n_chunks,
+                      int tiles_per_chunk, float* part, float* out) {
+  hipLaunchKernelGGL((k_attn_partial<T>), dim3(n_chunks, NH, B), dim3(256), 0, s, q, kv, max_pos, plan, n_chunks,
+                     tiles_per_chunk, part);
+  hipLaunchKernelGGL(k_attn_combine, dim3(B * plan.Q, NH / 2), dim3(256), 0, s, part, plan, n_chunks,
+                     tiles_per_chunk * ATT_TILE, max_pos, out);
+}
+
+template void launch_attention<float>(hipStream_t, const float*, const float*, int, RowPlan, int, int, int, float*,
+                                      float*);
+template void launch_attention<bf16>(hipStream_t, const float*, const bf16*, int, RowPlan, int, int, int, float*,
+                                     float*);
+
+}  // namespace ocr

@@ -1,0 +1,319 @@
+// Row plans and embedding gathers of each call, greedy longest-prefix
+// acceptance with KV rollback, prefill bookkeeping, and the controlled-draft
+// override used by the benchmark harness.
+#include "launch.h"
+
+namespace ocr {
+
+__device__ __forceinline__ int clamp_tok(int t, int V) { return t < 0 ? 0 : (t >= V ? V - 1 : t); }
+__device__ __forceinline__ int clamp_slot(int s, int n) { return s < 0 ? 0 : (s >= n ? n - 1 : s); }
+
+template <typename T>
+__device__ __forceinline__ void embed_row(const T* __restrict__ E, int tok, float* __restrict__ dst) {
+  const T* src = E + (long)tok * D;
+  for (int k = threadIdx.x; k < D; k += 256) dst[k] = WT<T>::load1(src + k);
+}
+
+// Block b: sequence b of a verify call.  Rows b*(K+1) + i hold
+// [pending, d_1 .. d_K] at positions kv_len .. kv_len + K.
+template <typename T>
+__global__ __launch_bounds__(256) void k_plan_verify(int K, const int* __restrict__ slots_in, StateView sv,
+                                                     const int* __restrict__ draft, const T* __restrict__ E,
+                                                     int V, int* plan_base, int* plan_cnt, int* plan_slot,
+                                                     float* __restrict__ x) {
+  const int b = blockIdx.x;
+  const int slot = clamp_slot(slots_in ? slots_in[b] : b, sv.n_slots);
+  if (threadIdx.x == 0) {
+    plan_slot[b] = slot;
+    plan_base[b] = sv.kv_len[slot];
+    plan_cnt[b] = K + 1;
+  }
+  for (int i = 0; i <= K; ++i) {
+    const int tok = clamp_tok(i == 0 ? sv.pending[slot] : draft[b * K + i - 1], V);
+    embed_row(E, tok, x + (long)(b * (K + 1) + i) * D);
+  }
+}
+
+// RMSNorm of one D-row into dst (256 threads).
+__device__ __forceinline__ void norm_row(const float* __restrict__ src, const float* __restrict__ g, float eps,
+                                         float* __restrict__ dst, float* red) {
+  float v[D / 256];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < D / 256; ++j) {
+    v[j] = src[threadIdx.x + 256 * j];
+    ss = fmaf(v[j], v[j], ss);
+  }
+  ss = block_sum256(ss, red);
+  const float r = 1.0f / sqrtf(ss / (float)D + eps);
+#pragma unroll
+  for (int j = 0; j < D / 256; ++j) dst[threadIdx.x + 256 * j] = (v[j] * r) * g[threadIdx.x + 256 * j];
+}
+
+// Draft fusion input of one row: [RMSNorm(h; g_h), RMSNorm(e; g_e)].
+template <typename T>
+__device__ __forceinline__ void draft_cat_row(const float* h, int tok, const T* E, const float* g_h,
+                                              const float* g_e, float eps, float* cat, float* ebuf, float* red) {
+  norm_row(h, g_h, eps, cat, red);
+  embed_row(E, tok, ebuf);
+  __syncthreads();
+  norm_row(ebuf, g_e, eps, cat + D, red);
+}
+
+// Catch-up pass: sequence b has cnt = n_prev + 1 valid rows at positions
+// draft_len .. kv_len; row i takes the verifier hidden hbuf[i] (of position
+// draft_len - 1 + i) and the committed token cu_tok[i] (at draft_len + i).
+template <typename T>
+__global__ __launch_bounds__(256) void k_plan_draft_catchup(int Q, const int* __restrict__ slots_in,
+                                                            StateView sv, const T* __restrict__ E, int V,
+                                                            const float* __restrict__ g_h,
+                                                            const float* __restrict__ g_e, float eps,
+                                                            int* plan_base, int* plan_cnt, int* plan_slot,
+                                                            float* __restrict__ cat) {
+  __shared__ float red[4];
+  __shared__ float ebuf[D];
+  const int b = blockIdx.x;
+  const int slot = clamp_slot(slots_in ? slots_in[b] : b, sv.n_slots);
+  const int cnt = max(1, min(sv.n_prev[slot] + 1, Q));
+  if (threadIdx.x == 0) {
+    plan_slot[b] = slot;
+    plan_base[b] = sv.draft_len[slot];
+    plan_cnt[b] = cnt;
+  }
+  for (int i = 0; i < Q; ++i) {
+    float* c = cat + (long)(b * Q + i) * 2 * D;
+    if (i < cnt) {
+      const float* h = sv.hbuf + ((long)slot * sv.cu_stride + i) * D;
+      const int tok = clamp_tok(sv.cu_tok[slot * sv.cu_stride + i], V);
+      draft_cat_row(h, tok, E, g_h, g_e, eps, c, ebuf, red);
+      __syncthreads();
+    } else {
+      for (int k = threadIdx.x; k < 2 * D; k += 256) c[k] = 0.f;
+    }
+  }
+}
+
+// Pass j >= 2: one row per sequence at position kv_len + j - 1 taking the
+// previous pass's block output (its last valid row) and the embedding of d_{j-1}.
+template <typename T>
+__global__ __launch_bounds__(256) void k_plan_draft_step(int j, int Qprev, int K, StateView sv,
+                                                         const int* __restrict__ draft_out, const T* __restrict__ E,
+                                                         int V, const float* __restrict__ g_h,
+                                                         const float* __restrict__ g_e, float eps,
+                                                         const float* __restrict__ u_prev, int* plan_base,
+                                                         int* plan_cnt, const int* __restrict__ plan_slot,
+                                                         float* __restrict__ cat) {
+  __shared__ float red[4];
+  __shared__ float ebuf[D];
+  __shared__ int prev_cnt;
+  const int b = blockIdx.x;
+  const int slot = plan_slot[b];
+  if (threadIdx.x == 0) prev_cnt = max(1, min(plan_cnt[b], Qprev));
+  __syncthreads();
+  const float* h = u_prev + (long)(b * Qprev + prev_cnt - 1) * D;
+  const int tok = clamp_tok(draft_out[b * K + j - 2], V);
+  draft_cat_row(h, tok, E, g_h, g_e, eps, cat + (long)b * 2 * D, ebuf, red);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    plan_base[b] = sv.kv_len[slot] + j - 1;
+    plan_cnt[b] = 1;
+  }
+}
+
+// Prefill rows p0 .. p0+c-1 of one sequence: vision rows, then prompt ids.
+template <typename T>
+__global__ __launch_bounds__(256) void k_plan_prefill(int slot, int p0, int c, int n_vision,
+                                                      const float* __restrict__ vision,
+                                                      const int* __restrict__ prompt, const T* __restrict__ E,
+                                                      int V, int* plan_base, int* plan_cnt, int* plan_slot,
+                                                      float* __restrict__ x, float* __restrict__ esave) {
+  const int i = blockIdx.x;
+  const int p = p0 + i;
+  if (i == 0 && threadIdx.x == 0) {
+    plan_slot[0] = slot;
+    plan_base[0] = p0;
+    plan_cnt[0] = c;
+  }
+  float* dst = x + (long)i * D;
+  if (p < n_vision) {
+    for (int k = threadIdx.x; k < D; k += 256) dst[k] = vision[(long)p * D + k];
+  } else {
+    embed_row(E, clamp_tok(prompt[p - n_vision], V), dst);
+  }
+  __syncthreads();
+  for (int k = threadIdx.x; k < D; k += 256) esave[(long)i * D + k] = dst[k];
+}
+
+// Draft prefill rows: row i (position p0 + i) takes (h_{p-1}, e_p); h of the
+// chunk's first row comes from the previous chunk (hprev, zero at p = 0).
+__global__ __launch_bounds__(256) void k_draft_prefill_cat(int c, const float* __restrict__ xfinal,
+                                                           const float* __restrict__ esave,
+                                                           const float* __restrict__ hprev,
+                                                           float* __restrict__ hnext, const float* __restrict__ g_h,
+                                                           const float* __restrict__ g_e, float eps,
+                                                           float* __restrict__ cat) {
+  __shared__ float red[4];
+  const int i = blockIdx.x;
+  const float* h = (i == 0) ? hprev : xfinal + (long)(i - 1) * D;
+  float* dst = cat + (long)i * 2 * D;
+  norm_row(h, g_h, eps, dst, red);
+  norm_row(esave + (long)i * D, g_e, eps, dst + D, red);
+  if (i == c - 1)
+    for (int k = threadIdx.x; k < D; k += 256) hnext[k] = xfinal[(long)i * D + k];
+}
+
+__global__ void k_prefill_finish(int slot, int P, const float* __restrict__ xlast, const int* __restrict__ tok,
+                                 StateView sv) {
+  const int y0 = *tok;
+  if (threadIdx.x == 0) {
+    sv.kv_len[slot] = P;
+    sv.draft_len[slot] = P;
+    sv.pending[slot] = y0;
+    sv.n_prev[slot] = 0;
+    sv.out_len[slot] = 1;
+    sv.step[slot] = 0;
+    sv.prefix_len[slot] = P;
+    sv.cu_tok[slot * sv.cu_stride] = y0;
+  }
+  float* hb = sv.hbuf + (long)slot * sv.cu_stride * D;
+  for (int k = threadIdx.x; k < D; k += 256) hb[k] = xlast[k];
+}
+
+// Greedy longest-prefix acceptance (one block per sequence).
+__global__ __launch_bounds__(256) void k_accept(int K, const int* __restrict__ plan_slot,
+                                                const int* __restrict__ draft, const int* __restrict__ greedy,
+                                                const float* __restrict__ xfinal, StateView sv,
+                                                int* __restrict__ n_acc, int* __restrict__ out_tokens,
+                                                int* __restrict__ out_len_out, int out_cap) {
+  __shared__ int sn;
+  const int b = blockIdx.x;
+  const int slot = plan_slot[b];
+  const int* g = greedy + b * (K + 1);
+  const int* d = draft + b * K;
+  if (threadIdx.x == 0) {
+    int n = 0;
+    while (n < K && d[n] == g[n]) ++n;
+    const int old = sv.kv_len[slot];
+    int ol = sv.out_len[slot];
+    for (int i = 0; i <= n; ++i) {
+      const int t = (i < n) ? d[i] : g[n];
+      sv.cu_tok[slot * sv.cu_stride + i] = t;
+      if (out_tokens != nullptr && ol < out_cap) out_tokens[(long)b * out_cap + ol] = t;
+      ++ol;
+    }
+    sv.out_len[slot] = ol;
+    sv.kv_len[slot] = old + n + 1;
+    sv.draft_len[slot] = old + 1;
+    sv.pending[slot] = g[n];
+    sv.n_prev[slot] = n;
+    sv.step[slot] += 1;
+    if (n_acc != nullptr) n_acc[b] = n;
+    if (out_len_out != nullptr) out_len_out[b] = ol;
+    sn = n;
+  }
+  __syncthreads();
+  const int n = sn;
+  for (int i = 0; i <= n; ++i) {
+    const float* src = xfinal + (long)(b * (K + 1) + i) * D;
+    float* dst = sv.hbuf + ((long)slot * sv.cu_stride + i) * D;
+    for (int k = threadIdx.x; k < D; k += 256) dst[k] = src[k];
+  }
+}
+
+// SplitMix64 output function (Steele, Lea & Flood 2014).
+__device__ __forceinline__ uint64_t splitmix64(uint64_t x) {
+  uint64_t z = x + 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+__global__ void k_controlled(int B, int K, const int* __restrict__ slots_in, StateView sv,
+                             const int* __restrict__ trace, int trace_stride, int trace_len, uint64_t seed,
+                             uint64_t thr, int V, int* __restrict__ draft) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= B * K) return;
+  const int b = t / K, j = t % K + 1;
+  const int slot = clamp_slot(slots_in ? slots_in[b] : b, sv.n_slots);
+  const int c = sv.out_len[slot];
+  const int idx = c - 1 + j;
+  const int true_tok = (idx < trace_len) ? trace[(long)b * trace_stride + idx] : 0;
+  uint64_t h = splitmix64(seed);
+  h = splitmix64(h ^ (uint64_t)(uint32_t)slot);
+  h = splitmix64(h ^ (uint64_t)(uint32_t)sv.step[slot]);
+  h = splitmix64(h ^ (uint64_t)(uint32_t)j);
+  int tok = true_tok;
+  if ((h >> 11) < thr) tok = (int)(((uint64_t)true_tok + 1 + (h & 0xFFFFFFFFull) % (uint64_t)(V - 1)) % (uint64_t)V);
+  draft[b * K + j - 1] = tok;
+}
+
+__global__ void k_copy(const float* __restrict__ src, float* __restrict__ dst, long n) {
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) dst[i] = src[i];
+}
+
+// ---------------------------------------------------------------- launchers
+template <typename T>
+void launch_plan_verify(hipStream_t s, int B, int K, const int* slots_in, StateView sv, const int* draft,
+                        const T* embed, int V, int* plan_base, int* plan_cnt, int* plan_slot, float* x) {
+  hipLaunchKernelGGL((k_plan_verify<T>), dim3(B), dim3(256), 0, s, K, slots_in, sv, draft, embed, V, plan_base,
+                     plan_cnt, plan_slot, x);
+}
+template <typename T>
+void launch_plan_draft_catchup(hipStream_t s, int B, int Q, const int* slots_in, StateView sv, const T* embed,
+                               int V, const float* g_h, const float* g_e, float eps, int* plan_base, int* plan_cnt,
+                               int* plan_slot, float* cat) {
+  hipLaunchKernelGGL((k_plan_draft_catchup<T>), dim3(B), dim3(256), 0, s, Q, slots_in, sv, embed, V, g_h, g_e, eps,
+                     plan_base, plan_cnt, plan_slot, cat);
+}
+template <typename T>
+void launch_plan_draft_step(hipStream_t s, int B, int j, int Qprev, int K, StateView sv, const int* draft_out,
+                            const T* embed, int V, const float* g_h, const float* g_e, float eps,
+                            const float* u_prev, int* plan_base, int* plan_cnt, const int* plan_slot, float* cat) {
+  hipLaunchKernelGGL((k_plan_draft_step<T>), dim3(B), dim3(256), 0, s, j, Qprev, K, sv, draft_out, embed, V, g_h,
+                     g_e, eps, u_prev, plan_base, plan_cnt, plan_slot, cat);
+}
+template <typename T>
+void launch_plan_prefill(hipStream_t s, int slot, int p0, int c, int n_vision, const float* vision,
+                         const int* prompt, const T* embed, int V, int* plan_base, int* plan_cnt, int* plan_slot,
+                         float* x, float* esave) {
+  hipLaunchKernelGGL((k_plan_prefill<T>), dim3(c), dim3(256), 0, s, slot, p0, c, n_vision, vision, prompt, embed,
+                     V, plan_base, plan_cnt, plan_slot, x, esave);
+}
+void launch_draft_prefill_cat(hipStream_t s, int c, const float* xfinal, const float* esave, const float* hprev,
+                              float* hnext, const float* g_h, const float* g_e, float eps, float* cat) {
+  hipLaunchKernelGGL(k_draft_prefill_cat, dim3(c), dim3(256), 0, s, c, xfinal, esave, hprev, hnext, g_h, g_e, eps,
+                     cat);
+}
+void launch_prefill_finish(hipStream_t s, int slot, int P, const float* xlast, const int* pending_tok,
+                           StateView sv) {
+  hipLaunchKernelGGL(k_prefill_finish, dim3(1), dim3(256), 0, s, slot, P, xlast, pending_tok, sv);
+}
+void launch_accept(hipStream_t s, int B, int K, const int* plan_slot, const int* draft, const int* greedy,
+                   const float* xfinal, StateView sv, int* n_acc, int* out_tokens, int* out_len_out, int out_cap) {
+  hipLaunchKernelGGL(k_accept, dim3(B), dim3(256), 0, s, K, plan_slot, draft, greedy, xfinal, sv, n_acc,
+                     out_tokens, out_len_out, out_cap);
+}
+void launch_controlled(hipStream_t s, int B, int K, const int* slots_in, StateView sv, const int* trace,
+                       int trace_stride, int trace_len, uint64_t seed, uint64_t thr, int V, int* draft) {
+  const int n = B * K;
+  hipLaunchKernelGGL(k_controlled, dim3((n + 255) / 256), dim3(256), 0, s, B, K, slots_in, sv, trace,
+                     trace_stride, trace_len, seed, thr, V, draft);
+}
+void launch_copy_rows(hipStream_t s, const float* src, float* dst, long n) {
+  hipLaunchKernelGGL(k_copy, dim3(64), dim3(256), 0, s, src, dst, n);
+}
+
+#define OCR_INST_MISC(T)                                                                                          \
+  template void launch_plan_verify<T>(hipStream_t, int, int, const int*, StateView, const int*, const T*, int,   \
+                                      int*, int*, int*, float*);                                                 \
+  template void launch_plan_draft_catchup<T>(hipStream_t, int, int, const int*, StateView, const T*, int,        \
+                                             const float*, const float*, float, int*, int*, int*, float*);       \
+  template void launch_plan_draft_step<T>(hipStream_t, int, int, int, int, StateView, const int*, const T*, int, \
+                                          const float*, const float*, float, const float*, int*, int*,           \
+                                          const int*, float*);                                                   \
+  template void launch_plan_prefill<T>(hipStream_t, int, int, int, int, const float*, const int*, const T*, int, \
+                                       int*, int*, int*, float*, float*);
+OCR_INST_MISC(float)
+OCR_INST_MISC(bf16)
+
+}  // namespace ocr

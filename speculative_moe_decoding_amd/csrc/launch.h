@@ -1,0 +1,100 @@
+// Host-side launchers of the ocrdec kernels (one per kernel family).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include "common.h"
+
+namespace ocr {
+
+enum Epi { EPI_STORE = 0, EPI_ADD = 1, EPI_SWIGLU = 2 };
+
+// x: [M][D] residual rows; gain: RMSNorm gain (never null here).
+// Writes q (RoPE'd, fp32 [M][QD]) and, for valid rows, k / v into the cache
+// kv[slot][0|1][head][pos][HD] (slot stride = 2*NH*max_pos*HD elements).
+template <typename T>
+void launch_qkv_rope(hipStream_t s, const float* x, const float* gain, float eps, const T* wqkv, int M,
+                     RowPlan plan, float* q, T* kv, int max_pos, float theta);
+
+// out[m][n] (op)= sum_k W[n][k] * a[m][k] for n < N; a optionally RMSNorm'ed
+// (gain != null).  EPI_SWIGLU: out[m][j] = silu(W0[j].a) * (W1[j].a), j < N.
+template <typename T>
+void launch_gemv(hipStream_t s, int K, Epi epi, const float* a, long lda, const float* gain, float eps,
+                 const T* W0, const T* W1, int N, int M, float* out, long ldo);
+
+// LM head fused with argmax.  Row m of the output reads activation row
+// (last_valid ? plan.base-independent m*Q + cnt[m]-1 : m) of x, RMSNorms it
+// with gain, forms the vocab logits (optionally stored to logits[m][V]) and
+// writes argmax (lowest id on ties) to tok[m * tok_stride].
+template <typename T>
+void launch_lmhead(hipStream_t s, const float* x, const int* cnt, int Q, bool last_valid, const float* gain,
+                   float eps, const T* W, int V, int M, float* part_val, int* part_idx, int* counter,
+                   float* logits, int* tok, int tok_stride);
+int lmhead_blocks(int V);
+
+template <typename T>
+void launch_attention(hipStream_t s, const float* q, const T* kv, int max_pos, RowPlan plan, int B,
+                      int n_chunks, int tiles_per_chunk, float* part, float* out);
+
+struct MoeBufs {
+  float* bnorm;   // [M][D] normalised rows
+  int* ridx;      // [M][8]
+  float* rgate;   // [M][8]
+  int* perm;      // [8M] pair id by sorted position
+  int* inv;       // [8M] sorted position of pair id
+  int* off;       // [NX + 1]
+  int* act;       // [NX] active experts in increasing id
+  int* n_act;     // [1]
+  int* counter;   // [1] zero between launches
+  long long* stats;  // [0] += active experts per layer
+  float* hx;      // [8M][DI]
+  float* y;       // [8M][D]
+};
+
+template <typename T>
+void launch_router(hipStream_t s, const float* x, const float* gain, float eps, const T* wr, int M,
+                   const MoeBufs& mb, int* tap);
+template <typename T>
+void launch_expert_gate_up(hipStream_t s, const T* wg, const T* wu, int M, const MoeBufs& mb);
+template <typename T>
+void launch_expert_down(hipStream_t s, const T* wd, int M, const MoeBufs& mb);
+void launch_moe_combine(hipStream_t s, float* x, int M, const MoeBufs& mb);
+int expert_slot_cap(int M);
+
+// ---- row plans, embeddings, acceptance --------------------------------------
+struct StateView {
+  int* kv_len; int* draft_len; int* pending; int* n_prev; int* out_len; int* step; int* prefix_len;
+  int* cu_tok;     // [max_batch][cu_stride]
+  int cu_stride;
+  float* hbuf;     // [max_batch][cu_stride][D]
+  int n_slots;     // max_batch
+};
+
+template <typename T>
+void launch_plan_verify(hipStream_t s, int B, int K, const int* slots_in, StateView sv, const int* draft,
+                        const T* embed, int V, int* plan_base, int* plan_cnt, int* plan_slot, float* x);
+template <typename T>
+void launch_plan_draft_catchup(hipStream_t s, int B, int Q, const int* slots_in, StateView sv,
+                               const T* embed, int V, const float* g_h, const float* g_e, float eps,
+                               int* plan_base, int* plan_cnt, int* plan_slot, float* cat);
+template <typename T>
+void launch_plan_draft_step(hipStream_t s, int B, int j, int Qprev, int K, StateView sv, const int* draft_out,
+                            const T* embed, int V, const float* g_h, const float* g_e, float eps,
+                            const float* u_prev, int* plan_base, int* plan_cnt, const int* plan_slot,
+                            float* cat);
+template <typename T>
+void launch_plan_prefill(hipStream_t s, int slot, int p0, int c, int n_vision, const float* vision,
+                         const int* prompt, const T* embed, int V, int* plan_base, int* plan_cnt,
+                         int* plan_slot, float* x, float* esave);
+void launch_draft_prefill_cat(hipStream_t s, int c, const float* xfinal, const float* esave,
+                              const float* hprev, float* hnext, const float* g_h, const float* g_e, float eps,
+                              float* cat);
+void launch_prefill_finish(hipStream_t s, int slot, int P, const float* xlast, const int* pending_tok,
+                           StateView sv);
+void launch_accept(hipStream_t s, int B, int K, const int* plan_slot, const int* draft, const int* greedy,
+                   const float* xfinal, StateView sv, int* n_acc, int* out_tokens, int* out_len_out,
+                   int out_cap);
+void launch_controlled(hipStream_t s, int B, int K, const int* slots_in, StateView sv, const int* trace,
+                       int trace_stride, int trace_len, uint64_t seed, uint64_t thr, int V, int* draft);
+void launch_copy_rows(hipStream_t s, const float* src, float* dst, long n);
+
+}  // namespace ocr

@@ -1,0 +1,524 @@
+// Host side of the ocrdec C ABI: buffer layout inside the caller's state and
+// workspace, argument checks, and the launch sequence of each call.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "launch.h"
+#include "ocrdec.h"
+
+using namespace ocr;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Offsets of every sub-buffer inside the state and the workspace.
+struct Plan {
+  // derived sizes
+  int Qmax, M_max, cu_stride, tiles_per_chunk, chunk_keys, n_chunks_cap, lm_nblk;
+  size_t esz, kv_layer_elems;
+  // state
+  size_t s_kv, s_dkv, s_ints, s_cu, s_hbuf, s_total;
+  // workspace
+  size_t w_x, w_q, w_attn, w_part, w_bnorm, w_ridx, w_rgate, w_perm, w_inv, w_off, w_act, w_misc, w_stats, w_hx,
+      w_y, w_cat, w_u, w_dffn, w_esave, w_hsave, w_lmv, w_lmi, w_plan, w_total;
+};
+
+bool shape_ok(const ocrdec_config* c, std::string* why) {
+  if (!c) { *why = "config is null"; return false; }
+  if (c->d_model != D || c->n_heads != NH || c->head_dim != HD || c->n_experts != NE || c->n_shared != NSH ||
+      c->top_k != TOPK || c->d_expert != DI || c->d_draft_ffn != DF) {
+    *why = "unsupported shape: the kernels are built for d=1280, 10x128 heads, 64+2 experts of 896, top-6, "
+           "draft FFN 3584";
+    return false;
+  }
+  if (c->n_layers < 1 || c->vocab < 2) { *why = "n_layers must be >= 1 and vocab >= 2"; return false; }
+  if (c->dtype != OCRDEC_F32 && c->dtype != OCRDEC_BF16) { *why = "dtype must be OCRDEC_F32 or OCRDEC_BF16"; return false; }
+  if (c->max_batch < 1 || c->max_batch > 1024) { *why = "max_batch must be in [1, 1024]"; return false; }
+  if (c->max_k < 0 || c->max_k > 7) { *why = "max_k must be in [0, 7]"; return false; }
+  if (c->max_positions < 16 || c->max_positions > 32768) { *why = "max_positions must be in [16, 32768]"; return false; }
+  if (!(c->norm_eps > 0.f) || !(c->rope_theta > 1.f)) { *why = "norm_eps must be > 0 and rope_theta > 1"; return false; }
+  return true;
+}
+
+Plan make_plan(const ocrdec_config* c) {
+  Plan p{};
+  p.Qmax = std::max(c->max_k + 1, PREFILL_CHUNK);
+  p.M_max = std::max(c->max_batch * (c->max_k + 1), PREFILL_CHUNK);
+  p.cu_stride = c->max_k + 1;
+  p.tiles_per_chunk = c->max_positions > 4096 ? 4 : 1;
+  p.chunk_keys = p.tiles_per_chunk * ATT_TILE;
+  p.n_chunks_cap = (c->max_positions + p.chunk_keys - 1) / p.chunk_keys;
+  p.lm_nblk = lmhead_blocks(c->vocab);
+  p.esz = c->dtype == OCRDEC_BF16 ? 2 : 4;
+  p.kv_layer_elems = (size_t)c->max_batch * 2 * NH * (size_t)c->max_positions * HD;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t r = o; o = align256(o + bytes); return r; };
+  p.s_kv = take(p.kv_layer_elems * c->n_layers * p.esz);
+  p.s_dkv = take(p.kv_layer_elems * p.esz);
+  p.s_ints = take((size_t)7 * c->max_batch * 4);
+  p.s_cu = take((size_t)c->max_batch * p.cu_stride * 4);
+  p.s_hbuf = take((size_t)c->max_batch * p.cu_stride * D * 4);
+  p.s_total = o;
+  o = 0;
+  const size_t M = p.M_max;
+  p.w_x = take(M * D * 4);
+  p.w_q = take(M * QD * 4);
+  p.w_attn = take(M * QD * 4);
+  p.w_part = take(M * NH * (size_t)p.n_chunks_cap * (HD + 2) * 4);
+  p.w_bnorm = take(M * D * 4);
+  p.w_ridx = take(M * NSLOT * 4);
+  p.w_rgate = take(M * NSLOT * 4);
+  p.w_perm = take(M * NSLOT * 4);
+  p.w_inv = take(M * NSLOT * 4);
+  p.w_off = take((NX + 1) * 4);
+  p.w_act = take(NX * 4);
+  p.w_misc = take(64 * 4);       // [0] n_act, [1] router counter, [2] lm counter, [16..] prefill tokens
+  p.w_stats = take(8 * 8);
+  p.w_hx = take(M * NSLOT * DI * 4);
+  p.w_y = take(M * NSLOT * D * 4);
+  p.w_cat = take(M * 2 * D * 4);
+  p.w_u = take(M * D * 4);
+  p.w_dffn = take(M * DF * 4);
+  p.w_esave = take((size_t)PREFILL_CHUNK * D * 4);
+  p.w_hsave = take(2 * D * 4);
+  p.w_lmv = take(M * (size_t)p.lm_nblk * 4);
+  p.w_lmi = take(M * (size_t)p.lm_nblk * 4);
+  p.w_plan = take((size_t)3 * std::max(c->max_batch, PREFILL_CHUNK) * 4);
+  p.w_total = o;
+  return p;
+}
+
+}  // namespace
+
+struct ocrdec_model {
+  ocrdec_config cfg;
+  Plan p;
+  std::vector<const void*> w;
+  char* state;
+  char* ws;
+  StateView sv;
+  float *x, *q, *attn, *part, *cat, *u, *dffn, *esave, *hsave[2], *lm_val;
+  int *lm_idx, *plan_base, *plan_cnt, *plan_slot, *lm_counter, *tok_tmp;
+  MoeBufs mb;
+  // Host-side upper bound on (last position + 1) of every slot: set by prefill,
+  // raised by K + 1 per accept.  It sizes the attention grids and the capacity
+  // checks; the device clamps positions to the cache in any case.
+  std::vector<int> slot_bound;
+  int32_t* tap_route;
+  float* tap_hidden;
+  bool timing;
+  std::vector<hipEvent_t> ev;  // triplets: before gate/up, between, after down
+  size_t ev_used;
+};
+
+namespace {
+
+enum WIdx { W_EMBED = 0, W_LM = 1, W_FNORM = 2, W_LAYER0 = 3 };
+enum LIdx { L_ANORM = 0, L_QKV, L_WO, L_FNORM, L_ROUTER, L_GATE, L_UP, L_DOWN, L_N };
+enum DIdx { D_NH = 0, D_NE, D_FUSE, D_ANORM, D_QKV, D_WO, D_FNORM, D_GATE, D_UP, D_DOWN, D_ONORM, D_N };
+
+int num_weights(const ocrdec_config* c) { return W_LAYER0 + L_N * c->n_layers + D_N; }
+
+template <typename T> const T* wmat(const ocrdec_model* m, int i) { return static_cast<const T*>(m->w[i]); }
+const float* wvec(const ocrdec_model* m, int i) { return static_cast<const float*>(m->w[i]); }
+int lw(const ocrdec_model* m, int l, int k) { (void)m; return W_LAYER0 + L_N * l + k; }
+int dw(const ocrdec_model* m, int k) { return W_LAYER0 + L_N * m->cfg.n_layers + k; }
+
+int hip_check(const char* where) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(OCRDEC_EHIP, std::string(where) + ": " + hipGetErrorString(e));
+  return OCRDEC_OK;
+}
+
+int chunks_for(const ocrdec_model* m, int max_pos_touched) {
+  return std::min(m->p.n_chunks_cap, max_pos_touched / m->p.chunk_keys + 1);
+}
+
+// Bound for the sequences of a call: slots 0..B-1 when `slots` is null, else every slot.
+int call_bound(const ocrdec_model* m, int B, const int32_t* slots) {
+  const int n = slots ? (int)m->slot_bound.size() : B;
+  int b = 0;
+  for (int i = 0; i < n; ++i) b = std::max(b, m->slot_bound[i]);
+  return b;
+}
+
+void timing_mark(ocrdec_model* m, hipStream_t s) {
+  if (!m->timing) return;
+  if (m->ev_used >= m->ev.size()) {
+    if (m->ev.size() >= (size_t)3 * 65536) return;
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) { m->timing = false; return; }
+    m->ev.push_back(e);
+  }
+  if (hipEventRecord(m->ev[m->ev_used], s) == hipSuccess) ++m->ev_used;
+}
+
+template <typename T>
+void verifier_layers(ocrdec_model* m, hipStream_t s, int M, int B, RowPlan plan, int nch, bool taps) {
+  const ocrdec_config& c = m->cfg;
+  for (int l = 0; l < c.n_layers; ++l) {
+    T* kvl = static_cast<T*>((void*)(m->state + m->p.s_kv)) + (size_t)l * m->p.kv_layer_elems;
+    launch_qkv_rope<T>(s, m->x, wvec(m, lw(m, l, L_ANORM)), c.norm_eps, wmat<T>(m, lw(m, l, L_QKV)), M, plan, m->q,
+                       kvl, c.max_positions, c.rope_theta);
+    launch_attention<T>(s, m->q, kvl, c.max_positions, plan, B, nch, m->p.tiles_per_chunk, m->part, m->attn);
+    launch_gemv<T>(s, QD, EPI_ADD, m->attn, QD, nullptr, c.norm_eps, wmat<T>(m, lw(m, l, L_WO)), nullptr, D, M,
+                   m->x, D);
+    launch_router<T>(s, m->x, wvec(m, lw(m, l, L_FNORM)), c.norm_eps, wmat<T>(m, lw(m, l, L_ROUTER)), M, m->mb,
+                     (taps && m->tap_route) ? m->tap_route + (size_t)l * M * NSLOT : nullptr);
+    timing_mark(m, s);
+    launch_expert_gate_up<T>(s, wmat<T>(m, lw(m, l, L_GATE)), wmat<T>(m, lw(m, l, L_UP)), M, m->mb);
+    timing_mark(m, s);
+    launch_expert_down<T>(s, wmat<T>(m, lw(m, l, L_DOWN)), M, m->mb);
+    timing_mark(m, s);
+    launch_moe_combine(s, m->x, M, m->mb);
+  }
+}
+
+template <typename T>
+void draft_layer(ocrdec_model* m, hipStream_t s, int M, int B, RowPlan plan, int nch) {
+  const ocrdec_config& c = m->cfg;
+  T* dkv = static_cast<T*>((void*)(m->state + m->p.s_dkv));
+  launch_gemv<T>(s, 2 * D, EPI_STORE, m->cat, 2 * D, nullptr, c.norm_eps, wmat<T>(m, dw(m, D_FUSE)), nullptr, D, M,
+                 m->u, D);
+  launch_qkv_rope<T>(s, m->u, wvec(m, dw(m, D_ANORM)), c.norm_eps, wmat<T>(m, dw(m, D_QKV)), M, plan, m->q, dkv,
+                     c.max_positions, c.rope_theta);
+  launch_attention<T>(s, m->q, dkv, c.max_positions, plan, B, nch, m->p.tiles_per_chunk, m->part, m->attn);
+  launch_gemv<T>(s, QD, EPI_ADD, m->attn, QD, nullptr, c.norm_eps, wmat<T>(m, dw(m, D_WO)), nullptr, D, M, m->u, D);
+  launch_gemv<T>(s, D, EPI_SWIGLU, m->u, D, wvec(m, dw(m, D_FNORM)), c.norm_eps, wmat<T>(m, dw(m, D_GATE)),
+                 wmat<T>(m, dw(m, D_UP)), DF, M, m->dffn, DF);
+  launch_gemv<T>(s, DF, EPI_ADD, m->dffn, DF, nullptr, c.norm_eps, wmat<T>(m, dw(m, D_DOWN)), nullptr, D, M, m->u,
+                 D);
+}
+
+template <typename T>
+int do_prefill(ocrdec_model* m, hipStream_t s, int B, const int32_t* slots_host, const float* vision, int nv_stride,
+               const int32_t* nv_host, const int32_t* prompt, int np_stride, const int32_t* np_host,
+               int32_t* pending_out) {
+  const ocrdec_config& c = m->cfg;
+  for (int b = 0; b < B; ++b) {
+    const int slot = slots_host ? slots_host[b] : b;
+    const int Nv = nv_host[b], Np = np_host[b];
+    const int P = Nv + Np;
+    const float* vis = vision ? vision + (size_t)b * nv_stride * D : nullptr;
+    const int* pr = prompt ? prompt + (size_t)b * np_stride : nullptr;
+    if (hipMemsetAsync(m->hsave[0], 0, D * 4, s) != hipSuccess) return fail(OCRDEC_EHIP, "hipMemsetAsync failed");
+    int par = 0;
+    for (int p0 = 0; p0 < P; p0 += PREFILL_CHUNK) {
+      const int cc = std::min(PREFILL_CHUNK, P - p0);
+      launch_plan_prefill<T>(s, slot, p0, cc, Nv, vis, pr, wmat<T>(m, W_EMBED), c.vocab, m->plan_base, m->plan_cnt,
+                             m->plan_slot, m->x, m->esave);
+      RowPlan plan{m->plan_base, m->plan_cnt, m->plan_slot, cc};
+      const int nch = chunks_for(m, p0 + cc - 1);
+      verifier_layers<T>(m, s, cc, 1, plan, nch, false);
+      if (p0 + cc == P)
+        launch_lmhead<T>(s, m->x, m->plan_cnt, cc, true, wvec(m, W_FNORM), c.norm_eps, wmat<T>(m, W_LM), c.vocab, 1,
+                         m->lm_val, m->lm_idx, m->lm_counter, nullptr, m->tok_tmp, 1);
+      launch_draft_prefill_cat(s, cc, m->x, m->esave, m->hsave[par], m->hsave[1 - par], wvec(m, dw(m, D_NH)),
+                               wvec(m, dw(m, D_NE)), c.norm_eps, m->cat);
+      draft_layer<T>(m, s, cc, 1, plan, nch);
+      par ^= 1;
+      if (p0 + cc == P) {
+        launch_prefill_finish(s, slot, P, m->x + (size_t)(cc - 1) * D, m->tok_tmp, m->sv);
+        if (hipMemcpyAsync(pending_out + b, m->tok_tmp, 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
+          return fail(OCRDEC_EHIP, "hipMemcpyAsync failed");
+      }
+    }
+    m->slot_bound[slot] = P;
+  }
+  return hip_check("ocrdec_prefill");
+}
+
+template <typename T>
+int do_draft(ocrdec_model* m, hipStream_t s, int B, const int32_t* slots, int K, int32_t* draft_out) {
+  const ocrdec_config& c = m->cfg;
+  const int Q = K + 1;
+  const int nch = chunks_for(m, std::min(c.max_positions - 1, call_bound(m, B, slots) + K - 1));
+  launch_plan_draft_catchup<T>(s, B, Q, slots, m->sv, wmat<T>(m, W_EMBED), c.vocab, wvec(m, dw(m, D_NH)),
+                               wvec(m, dw(m, D_NE)), c.norm_eps, m->plan_base, m->plan_cnt, m->plan_slot, m->cat);
+  RowPlan plan{m->plan_base, m->plan_cnt, m->plan_slot, Q};
+  draft_layer<T>(m, s, B * Q, B, plan, nch);
+  launch_lmhead<T>(s, m->u, m->plan_cnt, Q, true, wvec(m, dw(m, D_ONORM)), c.norm_eps, wmat<T>(m, W_LM), c.vocab, B,
+                   m->lm_val, m->lm_idx, m->lm_counter, nullptr, draft_out, K);
+  for (int j = 2; j <= K; ++j) {
+    const int Qprev = (j == 2) ? Q : 1;
+    launch_plan_draft_step<T>(s, B, j, Qprev, K, m->sv, draft_out, wmat<T>(m, W_EMBED), c.vocab,
+                              wvec(m, dw(m, D_NH)), wvec(m, dw(m, D_NE)), c.norm_eps, m->u, m->plan_base, m->plan_cnt,
+                              m->plan_slot, m->cat);
+    RowPlan p1{m->plan_base, m->plan_cnt, m->plan_slot, 1};
+    draft_layer<T>(m, s, B, B, p1, nch);
+    launch_lmhead<T>(s, m->u, m->plan_cnt, 1, true, wvec(m, dw(m, D_ONORM)), c.norm_eps, wmat<T>(m, W_LM), c.vocab,
+                     B, m->lm_val, m->lm_idx, m->lm_counter, nullptr, draft_out + (j - 1), K);
+  }
+  return hip_check("ocrdec_draft");
+}
+
+template <typename T>
+int do_verify(ocrdec_model* m, hipStream_t s, int B, const int32_t* slots, int K, const int32_t* draft,
+              int32_t* greedy_out, float* logits_out) {
+  const ocrdec_config& c = m->cfg;
+  const int Q = K + 1, M = B * Q;
+  const int nch = chunks_for(m, std::min(c.max_positions - 1, call_bound(m, B, slots) + K));
+  launch_plan_verify<T>(s, B, K, slots, m->sv, draft, wmat<T>(m, W_EMBED), c.vocab, m->plan_base, m->plan_cnt,
+                        m->plan_slot, m->x);
+  RowPlan plan{m->plan_base, m->plan_cnt, m->plan_slot, Q};
+  verifier_layers<T>(m, s, M, B, plan, nch, true);
+  launch_lmhead<T>(s, m->x, m->plan_cnt, Q, false, wvec(m, W_FNORM), c.norm_eps, wmat<T>(m, W_LM), c.vocab, M,
+                   m->lm_val, m->lm_idx, m->lm_counter, logits_out, greedy_out, 1);
+  if (m->tap_hidden) launch_copy_rows(s, m->x, m->tap_hidden, (long)M * D);
+  return hip_check("ocrdec_verify");
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_call(ocrdec_model* m, int B, int K) {
+  if (!m) return fail(OCRDEC_EINVAL, "model is null");
+  if (B < 1) return fail(OCRDEC_EINVAL, "B must be >= 1");
+  if (K < 0) return fail(OCRDEC_EINVAL, "K must be >= 0");
+  if (B > m->cfg.max_batch) return fail(OCRDEC_ECAPACITY, "B exceeds max_batch");
+  if (K > m->cfg.max_k) return fail(OCRDEC_ECAPACITY, "K exceeds max_k");
+  return OCRDEC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ocrdec_last_error(void) { return g_err.c_str(); }
+
+size_t ocrdec_state_bytes(const ocrdec_config* cfg) {
+  std::string why;
+  if (!shape_ok(cfg, &why)) { fail(OCRDEC_EINVAL, why); return 0; }
+  return make_plan(cfg).s_total;
+}
+
+size_t ocrdec_workspace_bytes(const ocrdec_config* cfg) {
+  std::string why;
+  if (!shape_ok(cfg, &why)) { fail(OCRDEC_EINVAL, why); return 0; }
+  return make_plan(cfg).w_total;
+}
+
+int ocrdec_num_weights(const ocrdec_config* cfg) {
+  std::string why;
+  if (!shape_ok(cfg, &why)) return fail(OCRDEC_EINVAL, why);
+  return num_weights(cfg);
+}
+
+int ocrdec_create(const ocrdec_config* cfg, const void* const* weight_ptrs, int n_weights, void* state,
+                  void* workspace, void* stream, ocrdec_model** out) {
+  std::string why;
+  if (!out) return fail(OCRDEC_EINVAL, "out is null");
+  *out = nullptr;
+  if (!shape_ok(cfg, &why)) return fail(OCRDEC_EINVAL, why);
+  if (!weight_ptrs || n_weights != num_weights(cfg))
+    return fail(OCRDEC_EINVAL, "weight_ptrs is null or n_weights != ocrdec_num_weights()");
+  for (int i = 0; i < n_weights; ++i)
+    if (!weight_ptrs[i] || !aligned(weight_ptrs[i], 16))
+      return fail(OCRDEC_EINVAL, "weight pointer " + std::to_string(i) + " is null or not 16-byte aligned");
+  if (!state || !workspace || !aligned(state, 256) || !aligned(workspace, 256))
+    return fail(OCRDEC_EINVAL, "state / workspace must be non-null and 256-byte aligned");
+  ocrdec_model* m = new ocrdec_model();
+  m->cfg = *cfg;
+  m->p = make_plan(cfg);
+  m->w.assign(weight_ptrs, weight_ptrs + n_weights);
+  m->state = static_cast<char*>(state);
+  m->ws = static_cast<char*>(workspace);
+  const Plan& p = m->p;
+  const int mb = cfg->max_batch;
+  int* ints = reinterpret_cast<int*>(m->state + p.s_ints);
+  m->sv.kv_len = ints;
+  m->sv.draft_len = ints + mb;
+  m->sv.pending = ints + 2 * mb;
+  m->sv.n_prev = ints + 3 * mb;
+  m->sv.out_len = ints + 4 * mb;
+  m->sv.step = ints + 5 * mb;
+  m->sv.prefix_len = ints + 6 * mb;
+  m->sv.cu_tok = reinterpret_cast<int*>(m->state + p.s_cu);
+  m->sv.cu_stride = p.cu_stride;
+  m->sv.hbuf = reinterpret_cast<float*>(m->state + p.s_hbuf);
+  m->sv.n_slots = mb;
+  auto wf = [&](size_t off) { return reinterpret_cast<float*>(m->ws + off); };
+  auto wi = [&](size_t off) { return reinterpret_cast<int*>(m->ws + off); };
+  m->x = wf(p.w_x);
+  m->q = wf(p.w_q);
+  m->attn = wf(p.w_attn);
+  m->part = wf(p.w_part);
+  m->cat = wf(p.w_cat);
+  m->u = wf(p.w_u);
+  m->dffn = wf(p.w_dffn);
+  m->esave = wf(p.w_esave);
+  m->hsave[0] = wf(p.w_hsave);
+  m->hsave[1] = wf(p.w_hsave) + D;
+  m->lm_val = wf(p.w_lmv);
+  m->lm_idx = wi(p.w_lmi);
+  const int pm = std::max(mb, PREFILL_CHUNK);
+  m->plan_base = wi(p.w_plan);
+  m->plan_cnt = wi(p.w_plan) + pm;
+  m->plan_slot = wi(p.w_plan) + 2 * pm;
+  int* misc = wi(p.w_misc);
+  m->mb.n_act = misc;
+  m->mb.counter = misc + 1;
+  m->lm_counter = misc + 2;
+  m->tok_tmp = misc + 16;
+  m->mb.bnorm = wf(p.w_bnorm);
+  m->mb.ridx = wi(p.w_ridx);
+  m->mb.rgate = wf(p.w_rgate);
+  m->mb.perm = wi(p.w_perm);
+  m->mb.inv = wi(p.w_inv);
+  m->mb.off = wi(p.w_off);
+  m->mb.act = wi(p.w_act);
+  m->mb.stats = reinterpret_cast<long long*>(m->ws + p.w_stats);
+  m->mb.hx = wf(p.w_hx);
+  m->mb.y = wf(p.w_y);
+  m->slot_bound.assign(cfg->max_batch, 0);
+  m->tap_route = nullptr;
+  m->tap_hidden = nullptr;
+  m->timing = false;
+  m->ev_used = 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipMemsetAsync(misc, 0, 64 * 4, s) != hipSuccess || hipMemsetAsync(m->mb.stats, 0, 64, s) != hipSuccess ||
+      hipMemsetAsync(m->state + p.s_ints, 0, p.s_hbuf - p.s_ints, s) != hipSuccess) {
+    delete m;
+    return fail(OCRDEC_EHIP, "hipMemsetAsync of the workspace counters failed");
+  }
+  *out = m;
+  return OCRDEC_OK;
+}
+
+int ocrdec_destroy(ocrdec_model* m) {
+  if (!m) return fail(OCRDEC_EINVAL, "model is null");
+  for (hipEvent_t e : m->ev) (void)hipEventDestroy(e);
+  delete m;
+  return OCRDEC_OK;
+}
+
+int ocrdec_prefill(ocrdec_model* m, void* stream, int B, const int32_t* slots_host, const float* vision, int nv_stride,
+                   const int32_t* n_vision_host, const int32_t* prompt, int np_stride, const int32_t* n_prompt_host,
+                   int32_t* pending_out) {
+  int rc = check_call(m, B, 0);
+  if (rc) return rc;
+  if (!n_vision_host || !n_prompt_host || !pending_out) return fail(OCRDEC_EINVAL, "null length / output pointer");
+  std::vector<int> seen;
+  for (int b = 0; b < B; ++b) {
+    const int slot = slots_host ? slots_host[b] : b;
+    if (slot < 0 || slot >= m->cfg.max_batch) return fail(OCRDEC_EINVAL, "slot out of range");
+    if (std::find(seen.begin(), seen.end(), slot) != seen.end()) return fail(OCRDEC_EINVAL, "duplicate slot");
+    seen.push_back(slot);
+    const int Nv = n_vision_host[b], Np = n_prompt_host[b];
+    if (Nv < 0 || Np < 0 || Nv + Np < 1) return fail(OCRDEC_EINVAL, "prefix must hold at least one row");
+    if (Nv > 0 && (!vision || nv_stride < Nv)) return fail(OCRDEC_EINVAL, "vision is null or nv_stride < n_vision");
+    if (Np > 0 && (!prompt || np_stride < Np)) return fail(OCRDEC_EINVAL, "prompt is null or np_stride < n_prompt");
+    if (Nv + Np + m->cfg.max_k + 1 > m->cfg.max_positions)
+      return fail(OCRDEC_ECAPACITY, "prefix + max_k + 1 exceeds max_positions");
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (m->cfg.dtype == OCRDEC_BF16)
+    return do_prefill<bf16>(m, s, B, slots_host, vision, nv_stride, n_vision_host, prompt, np_stride, n_prompt_host,
+                            pending_out);
+  return do_prefill<float>(m, s, B, slots_host, vision, nv_stride, n_vision_host, prompt, np_stride, n_prompt_host,
+                           pending_out);
+}
+
+int ocrdec_draft(ocrdec_model* m, void* stream, int B, const int32_t* slots, int K, int32_t* draft_out) {
+  int rc = check_call(m, B, K);
+  if (rc) return rc;
+  if (K < 1) return fail(OCRDEC_EINVAL, "draft needs K >= 1");
+  if (!draft_out) return fail(OCRDEC_EINVAL, "draft_out is null");
+  if (!slots && call_bound(m, B, slots) + K > m->cfg.max_positions)
+    return fail(OCRDEC_ECAPACITY, "positions would exceed max_positions");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (m->cfg.dtype == OCRDEC_BF16) return do_draft<bf16>(m, s, B, slots, K, draft_out);
+  return do_draft<float>(m, s, B, slots, K, draft_out);
+}
+
+int ocrdec_verify(ocrdec_model* m, void* stream, int B, const int32_t* slots, int K, const int32_t* draft,
+                  int32_t* greedy_out, float* logits_out) {
+  int rc = check_call(m, B, K);
+  if (rc) return rc;
+  if (!greedy_out || (K > 0 && !draft)) return fail(OCRDEC_EINVAL, "greedy_out is null, or draft is null with K > 0");
+  if (!slots && call_bound(m, B, slots) + K + 1 > m->cfg.max_positions)
+    return fail(OCRDEC_ECAPACITY, "positions would exceed max_positions");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (m->cfg.dtype == OCRDEC_BF16) return do_verify<bf16>(m, s, B, slots, K, draft, greedy_out, logits_out);
+  return do_verify<float>(m, s, B, slots, K, draft, greedy_out, logits_out);
+}
+
+int ocrdec_accept_rollback(ocrdec_model* m, void* stream, int B, const int32_t* slots, int K, const int32_t* draft,
+                           const int32_t* greedy, int32_t* n_accepted_out, int32_t* out_tokens, int32_t* out_len,
+                           int out_cap) {
+  int rc = check_call(m, B, K);
+  if (rc) return rc;
+  if (!greedy || (K > 0 && !draft)) return fail(OCRDEC_EINVAL, "greedy is null, or draft is null with K > 0");
+  if (out_tokens && out_cap < 1) return fail(OCRDEC_EINVAL, "out_cap must be >= 1 with out_tokens");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  launch_accept(s, B, K, m->plan_slot, draft, greedy, m->x, m->sv, n_accepted_out, out_tokens, out_len, out_cap);
+  const int n = slots ? (int)m->slot_bound.size() : B;
+  for (int i = 0; i < n; ++i) m->slot_bound[i] = std::min(m->cfg.max_positions, m->slot_bound[i] + K + 1);
+  return hip_check("ocrdec_accept_rollback");
+}
+
+int ocrdec_controlled_drafts(ocrdec_model* m, void* stream, int B, const int32_t* slots, int K, const int32_t* trace,
+                             int trace_stride, int trace_len, uint64_t seed, uint64_t threshold, int32_t* draft_inout) {
+  int rc = check_call(m, B, K);
+  if (rc) return rc;
+  if (K < 1 || !trace || !draft_inout || trace_len < 0 || trace_stride < trace_len)
+    return fail(OCRDEC_EINVAL, "bad controlled-draft arguments");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  launch_controlled(s, B, K, slots, m->sv, trace, trace_stride, trace_len, seed, threshold, m->cfg.vocab, draft_inout);
+  return hip_check("ocrdec_controlled_drafts");
+}
+
+int ocrdec_set_taps(ocrdec_model* m, int32_t* route_idx, float* hidden) {
+  if (!m) return fail(OCRDEC_EINVAL, "model is null");
+  m->tap_route = route_idx;
+  m->tap_hidden = hidden;
+  return OCRDEC_OK;
+}
+
+int ocrdec_expert_timing(ocrdec_model* m, int enable) {
+  if (!m) return fail(OCRDEC_EINVAL, "model is null");
+  m->timing = enable != 0;
+  m->ev_used = 0;
+  return OCRDEC_OK;
+}
+
+int ocrdec_expert_stats(ocrdec_model* m, double* ms_gate_up, long long* n_gate_up, double* ms_down, long long* n_down,
+                        long long* expert_sets) {
+  if (!m) return fail(OCRDEC_EINVAL, "model is null");
+  double a = 0, b = 0;
+  long long na = 0, nb = 0;
+  const size_t n = (m->ev_used / 3) * 3;
+  if (n > 0 && hipEventSynchronize(m->ev[n - 1]) != hipSuccess) return fail(OCRDEC_EHIP, "hipEventSynchronize failed");
+  for (size_t i = 0; i + 2 < n + 0 && i < n; i += 3) {
+    float t1 = 0, t2 = 0;
+    if (hipEventElapsedTime(&t1, m->ev[i], m->ev[i + 1]) != hipSuccess ||
+        hipEventElapsedTime(&t2, m->ev[i + 1], m->ev[i + 2]) != hipSuccess)
+      return fail(OCRDEC_EHIP, "hipEventElapsedTime failed");
+    a += t1;
+    b += t2;
+    ++na;
+    ++nb;
+  }
+  long long sets = 0;
+  if (hipMemcpy(&sets, m->mb.stats, sizeof(long long), hipMemcpyDeviceToHost) != hipSuccess)
+    return fail(OCRDEC_EHIP, "hipMemcpy of the expert counter failed");
+  if (ms_gate_up) *ms_gate_up = a;
+  if (n_gate_up) *n_gate_up = na;
+  if (ms_down) *ms_down = b;
+  if (n_down) *n_down = nb;
+  if (expert_sets) *expert_sets = sets;
+  return OCRDEC_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,285 @@
+"""Python binding of the ``ocrdec`` C ABI (include/ocrdec.h).
+
+Argument marshalling only: every step of the decode path runs in the HIP
+kernels of libocrdec.so.  PyTorch supplies device memory and the stream.
+The library must have been built (``python -m speculative_moe_decoding_amd.build``);
+loading fails loudly otherwise -- there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libocrdec.so")
+
+OCRDEC_OK, OCRDEC_EINVAL, OCRDEC_ECAPACITY, OCRDEC_EHIP = 0, -1, -2, -3
+OCRDEC_F32, OCRDEC_BF16 = 0, 1
+
+SYMBOLS = (
+    "ocrdec_state_bytes", "ocrdec_workspace_bytes", "ocrdec_num_weights", "ocrdec_create", "ocrdec_destroy",
+    "ocrdec_prefill", "ocrdec_draft", "ocrdec_verify", "ocrdec_accept_rollback", "ocrdec_controlled_drafts",
+    "ocrdec_set_taps", "ocrdec_expert_timing", "ocrdec_expert_stats", "ocrdec_last_error",
+)
+
+
+class ocrdec_config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in ("n_layers", "d_model", "n_heads", "head_dim", "n_experts", "n_shared",
+                                            "top_k", "d_expert", "d_draft_ffn", "vocab")] + [
+        ("rope_theta", ctypes.c_float), ("norm_eps", ctypes.c_float), ("dtype", ctypes.c_int),
+        ("max_batch", ctypes.c_int), ("max_k", ctypes.c_int), ("max_positions", ctypes.c_int)]
+
+
+class OcrdecError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn} failed ({code}): {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"libocrdec.so not found at {path}: build it with "
+                           f"`python -m speculative_moe_decoding_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I, U64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint64
+    cfgp = ctypes.POINTER(ocrdec_config)
+    sig = {
+        "ocrdec_state_bytes": (ctypes.c_size_t, [cfgp]),
+        "ocrdec_workspace_bytes": (ctypes.c_size_t, [cfgp]),
+        "ocrdec_num_weights": (I, [cfgp]),
+        "ocrdec_create": (I, [cfgp, ctypes.POINTER(P), I, P, P, P, ctypes.POINTER(P)]),
+        "ocrdec_destroy": (I, [P]),
+        "ocrdec_prefill": (I, [P, P, I, P, P, I, P, P, I, P, P]),
+        "ocrdec_draft": (I, [P, P, I, P, I, P]),
+        "ocrdec_verify": (I, [P, P, I, P, I, P, P, P]),
+        "ocrdec_accept_rollback": (I, [P, P, I, P, I, P, P, P, P, P, I]),
+        "ocrdec_controlled_drafts": (I, [P, P, I, P, I, P, I, I, U64, U64, P]),
+        "ocrdec_set_taps": (I, [P, P, P]),
+        "ocrdec_expert_timing": (I, [P, I]),
+        "ocrdec_expert_stats": (I, [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_longlong),
+                                    ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_longlong),
+                                    ctypes.POINTER(ctypes.c_longlong)]),
+        "ocrdec_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != OCRDEC_OK:
+        raise OcrdecError(fn, rc, load_library().ocrdec_last_error().decode())
+
+
+def make_config(cfg, max_batch: int, max_k: int, max_positions: int) -> ocrdec_config:
+    return ocrdec_config(cfg.n_layers, cfg.d_model, cfg.n_heads, cfg.head_dim, cfg.n_experts, cfg.n_shared,
+                         cfg.top_k, cfg.d_expert, cfg.d_draft_ffn, cfg.vocab, float(cfg.rope_theta),
+                         float(cfg.norm_eps), OCRDEC_BF16 if cfg.dtype == "bf16" else OCRDEC_F32,
+                         max_batch, max_k, max_positions)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+# C-ABI wrappers with the same names (tensors in, data pointers out)
+def ocrdec_state_bytes(c: ocrdec_config) -> int:
+    return int(load_library().ocrdec_state_bytes(ctypes.byref(c)))
+
+
+def ocrdec_workspace_bytes(c: ocrdec_config) -> int:
+    return int(load_library().ocrdec_workspace_bytes(ctypes.byref(c)))
+
+
+def ocrdec_num_weights(c: ocrdec_config) -> int:
+    n = load_library().ocrdec_num_weights(ctypes.byref(c))
+    _check("ocrdec_num_weights", n if n < 0 else 0)
+    return int(n)
+
+
+def ocrdec_create(c: ocrdec_config, weights: Sequence, state, workspace, stream: int) -> int:
+    arr = (ctypes.c_void_p * len(weights))(*[w.data_ptr() for w in weights])
+    h = ctypes.c_void_p()
+    _check("ocrdec_create", load_library().ocrdec_create(ctypes.byref(c), arr, len(weights), state.data_ptr(),
+                                                         workspace.data_ptr(), stream, ctypes.byref(h)))
+    return h.value
+
+
+def ocrdec_destroy(h: int) -> None:
+    _check("ocrdec_destroy", load_library().ocrdec_destroy(h))
+
+
+def ocrdec_prefill(h, stream, B, slots_host, vision, nv_stride, n_vision_host, prompt, np_stride, n_prompt_host,
+                   pending_out) -> None:
+    _check("ocrdec_prefill", load_library().ocrdec_prefill(
+        h, stream, B, None if slots_host is None else slots_host.ctypes.data, _ptr(vision), nv_stride,
+        n_vision_host.ctypes.data, _ptr(prompt), np_stride, n_prompt_host.ctypes.data, _ptr(pending_out)))
+
+
+def ocrdec_draft(h, stream, B, slots, K, draft_out) -> None:
+    _check("ocrdec_draft", load_library().ocrdec_draft(h, stream, B, _ptr(slots), K, _ptr(draft_out)))
+
+
+def ocrdec_verify(h, stream, B, slots, K, draft, greedy_out, logits_out=None) -> None:
+    _check("ocrdec_verify", load_library().ocrdec_verify(h, stream, B, _ptr(slots), K, _ptr(draft), _ptr(greedy_out),
+                                                         _ptr(logits_out)))
+
+
+def ocrdec_accept_rollback(h, stream, B, slots, K, draft, greedy, n_accepted_out, out_tokens, out_len, out_cap):
+    _check("ocrdec_accept_rollback", load_library().ocrdec_accept_rollback(
+        h, stream, B, _ptr(slots), K, _ptr(draft), _ptr(greedy), _ptr(n_accepted_out), _ptr(out_tokens),
+        _ptr(out_len), out_cap))
+
+
+def ocrdec_controlled_drafts(h, stream, B, slots, K, trace, trace_stride, trace_len, seed, threshold, draft_inout):
+    _check("ocrdec_controlled_drafts", load_library().ocrdec_controlled_drafts(
+        h, stream, B, _ptr(slots), K, _ptr(trace), trace_stride, trace_len, seed, threshold, _ptr(draft_inout)))
+
+
+def ocrdec_set_taps(h, route_idx=None, hidden=None):
+    _check("ocrdec_set_taps", load_library().ocrdec_set_taps(h, _ptr(route_idx), _ptr(hidden)))
+
+
+def ocrdec_expert_timing(h, enable: bool):
+    _check("ocrdec_expert_timing", load_library().ocrdec_expert_timing(h, 1 if enable else 0))
+
+
+def ocrdec_expert_stats(h):
+    a, b = ctypes.c_double(), ctypes.c_double()
+    na, nb, sets = ctypes.c_longlong(), ctypes.c_longlong(), ctypes.c_longlong()
+    _check("ocrdec_expert_stats", load_library().ocrdec_expert_stats(h, ctypes.byref(a), ctypes.byref(na),
+                                                                     ctypes.byref(b), ctypes.byref(nb),
+                                                                     ctypes.byref(sets)))
+    return dict(ms_gate_up=a.value, n_gate_up=na.value, ms_down=b.value, n_down=nb.value, expert_sets=sets.value)
+
+
+class Decoder:
+    """One model on one GPU: uploads the weights, owns state + workspace
+    (torch allocations) and drives the four decode calls on one stream."""
+
+    def __init__(self, cfg, weight_arrays: List[np.ndarray], max_batch: int, max_k: int, max_positions: int,
+                 device: str = "cuda"):
+        import torch
+        self.torch = torch
+        load_library()
+        self.cfg = cfg
+        self.device = torch.device(device)
+        self.c = make_config(cfg, max_batch, max_k, max_positions)
+        n = ocrdec_num_weights(self.c)
+        if n != len(weight_arrays):
+            raise ValueError(f"expected {n} weight tensors, got {len(weight_arrays)}")
+        self.weights = []
+        for a in weight_arrays:
+            a = np.ascontiguousarray(a)
+            if a.dtype == np.uint16:
+                a = a.view(np.int16)
+            self.weights.append(torch.from_numpy(a).to(self.device))
+        self.state = torch.empty(ocrdec_state_bytes(self.c), dtype=torch.uint8, device=self.device)
+        self.workspace = torch.empty(ocrdec_workspace_bytes(self.c), dtype=torch.uint8, device=self.device)
+        self.stream = torch.cuda.current_stream(self.device).cuda_stream
+        self.h = ocrdec_create(self.c, self.weights, self.state, self.workspace, self.stream)
+        self.max_batch, self.max_k, self.max_positions = max_batch, max_k, max_positions
+
+    def close(self):
+        if getattr(self, "h", None):
+            ocrdec_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -- helpers -------------------------------------------------------------
+    def i32(self, *shape):
+        return self.torch.empty(*shape, dtype=self.torch.int32, device=self.device)
+
+    def prefill(self, pages, slots: Optional[Sequence[int]] = None):
+        """pages: list of synth.Page.  Returns the device int32 [B] first output tokens."""
+        torch = self.torch
+        B = len(pages)
+        nv = np.array([p.vision.shape[0] for p in pages], dtype=np.int32)
+        npr = np.array([p.prompt.shape[0] for p in pages], dtype=np.int32)
+        nvs, nps = max(1, int(nv.max())), max(1, int(npr.max()))
+        vis = np.zeros((B, nvs, self.cfg.d_model), dtype=np.float32)
+        pr = np.zeros((B, nps), dtype=np.int32)
+        for b, p in enumerate(pages):
+            vis[b, :p.vision.shape[0]] = p.vision
+            pr[b, :p.prompt.shape[0]] = p.prompt
+        vis_t = torch.from_numpy(vis).to(self.device)
+        pr_t = torch.from_numpy(pr).to(self.device)
+        pending = self.i32(B)
+        sl = None if slots is None else np.asarray(slots, dtype=np.int32)
+        ocrdec_prefill(self.h, self.stream, B, sl, vis_t, nvs, nv, pr_t, nps, npr, pending)
+        return pending
+
+    def draft(self, B, K, slots=None, out=None):
+        out = self.i32(B, K) if out is None else out
+        ocrdec_draft(self.h, self.stream, B, slots, K, out)
+        return out
+
+    def verify(self, B, K, draft, slots=None, greedy=None, logits=None):
+        greedy = self.i32(B, K + 1) if greedy is None else greedy
+        ocrdec_verify(self.h, self.stream, B, slots, K, draft, greedy, logits)
+        return greedy
+
+    def accept(self, B, K, draft, greedy, n_acc, out_tokens, out_len, slots=None):
+        ocrdec_accept_rollback(self.h, self.stream, B, slots, K, draft, greedy, n_acc, out_tokens, out_len,
+                               out_tokens.shape[1])
+
+    def controlled(self, B, K, trace, seed, threshold, draft, slots=None):
+        ocrdec_controlled_drafts(self.h, self.stream, B, slots, K, trace, trace.shape[1], trace.shape[1], seed,
+                                 threshold, draft)
+
+    def generate(self, pages, n_out: int, K: int, trace=None, seed: int = 0, threshold: int = 0,
+                 record: bool = False, check_every: int = 16):
+        """Decode B pages to n_out tokens each with K draft tokens per step (K = 0: plain
+        autoregressive).  With ``trace`` (device int32 [B, T]) the drafts are replaced by the
+        controlled-acceptance tokens.  Returns (tokens [B, n_out] numpy, per-sequence lists of
+        accepted lengths up to the step that reached n_out (if record), steps run)."""
+        torch = self.torch
+        B = len(pages)
+        cap = n_out + self.max_k + 2
+        out_tokens = torch.zeros(B, cap, dtype=torch.int32, device=self.device)
+        out_len = self.i32(B)
+        n_acc = self.i32(B)
+        pending = self.prefill(pages)
+        out_tokens[:, 0] = pending
+        draft = self.i32(B, max(K, 1))
+        greedy = self.i32(B, K + 1)
+        accs, lens = [], []
+        steps = 0
+        while True:
+            for _ in range(check_every):
+                if K > 0:
+                    self.draft(B, K, out=draft)
+                    if trace is not None:
+                        self.controlled(B, K, trace, seed, threshold, draft)
+                self.verify(B, K, draft, greedy=greedy)
+                self.accept(B, K, draft, greedy, n_acc, out_tokens, out_len)
+                steps += 1
+                if record:
+                    accs.append(n_acc.clone())
+                    lens.append(out_len.clone())
+            if int(out_len.min().item()) >= n_out:
+                break
+        toks = out_tokens[:, :n_out].cpu().numpy()
+        acc = None
+        if record:
+            # keep, per sequence, the steps taken before it reached n_out tokens
+            a = torch.stack(accs).cpu().numpy()
+            ln = torch.stack(lens).cpu().numpy()
+            acc = [a[:int(np.argmax(ln[:, b] >= n_out)) + 1, b].tolist() for b in range(B)]
+        return toks, acc, steps

@@ -1,0 +1,73 @@
+"""The C-ABI library loads, exports every function include/ocrdec.h declares,
+and its host-only entry points (sizes, argument checks) behave as documented.
+No GPU compute is launched here."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from speculative_moe_decoding_amd import ocrdec, synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ocrdec.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ocrdec_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ocrdec.LIB_PATH):
+        pytest.fail("libocrdec.so is not built (run __graft_entry__.build())")
+    return ocrdec.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", ocrdec.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (ocrdec_\w+)", out))
+    declared = declared_functions()
+    assert len(declared) >= 14
+    missing = [f for f in declared if f not in exported]
+    assert not missing, missing
+    assert set(ocrdec.SYMBOLS) == set(declared)
+    for f in declared:
+        getattr(lib, f)
+
+
+def test_sizes_scale_with_capacity(lib):
+    c1 = ocrdec.make_config(synth.FULL, 1, 3, 2048)
+    c2 = ocrdec.make_config(synth.FULL, 2, 3, 2048)
+    s1, s2 = ocrdec.ocrdec_state_bytes(c1), ocrdec.ocrdec_state_bytes(c2)
+    # verifier KV: 12 layers x 2 x 1280 x 2048 positions x 2 bytes per slot, plus the draft's layer
+    kv_per_slot = 13 * 2 * 1280 * 2048 * 2
+    assert s1 >= kv_per_slot and s2 >= 2 * kv_per_slot
+    assert ocrdec.ocrdec_workspace_bytes(c1) > 0
+    assert ocrdec.ocrdec_num_weights(c1) == len(synth.weight_specs(synth.FULL)) == 3 + 8 * 12 + 11
+
+
+def test_rejects_bad_configs(lib):
+    import dataclasses
+    bad = ocrdec.make_config(dataclasses.replace(synth.FULL, d_model=1024), 1, 3, 2048)
+    assert ocrdec.ocrdec_state_bytes(bad) == 0
+    assert "unsupported shape" in lib.ocrdec_last_error().decode()
+    with pytest.raises(ocrdec.OcrdecError) as e:
+        ocrdec.ocrdec_num_weights(bad)
+    assert e.value.code == ocrdec.OCRDEC_EINVAL
+    for mb, mk, mp in ((0, 3, 2048), (1, 8, 2048), (1, 3, 40000)):
+        c = ocrdec.make_config(synth.FULL, mb, mk, mp)
+        assert ocrdec.ocrdec_state_bytes(c) == 0
+    # create checks the weight list before touching the device
+    c = ocrdec.make_config(synth.FULL, 1, 3, 2048)
+    h = ctypes.c_void_p()
+    arr = (ctypes.c_void_p * 3)()
+    rc = lib.ocrdec_create(ctypes.byref(c), arr, 3, None, None, None, ctypes.byref(h))
+    assert rc == ocrdec.OCRDEC_EINVAL and h.value is None
+    # calls on a null handle
+    assert lib.ocrdec_verify(None, None, 1, None, 0, None, None, None) == ocrdec.OCRDEC_EINVAL
+    assert lib.ocrdec_draft(None, None, 1, None, 3, None) == ocrdec.OCRDEC_EINVAL

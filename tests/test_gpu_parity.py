@@ -1,0 +1,133 @@
+"""GPU parity of the HIP decode path (through the C ABI) against the CPU oracle.
+
+Tolerances: routing, accepted lengths and tokens bit-exact; logits within
+1e-3 (fp32 model) or 5e-2 (bf16 model) absolute, a token mismatch excused only
+where the oracle's top-2 logit margin is under that tolerance."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+from oracle import decoder as od
+from speculative_moe_decoding_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+from gpu_util import compare_steps, log, make_pair, run_gpu_steps  # noqa: E402
+
+SMALL32 = dataclasses.replace(synth.FULL, n_layers=2, vocab=5003, dtype="f32")
+SMALL16 = dataclasses.replace(synth.FULL, n_layers=2, vocab=5003, dtype="bf16")
+
+
+def test_smoke():
+    import __graft_entry__
+    __graft_entry__.smoke()
+
+
+@pytest.mark.parametrize("cfg,tol", [(SMALL32, 1e-3), (SMALL16, 5e-2)], ids=["f32", "bf16"])
+def test_small_model_ar_and_spec(cfg, tol):
+    """2 layers, vocab 5003 (ragged against the 64-row LM-head tiles), prefix
+    20 vision + 5 prompt rows (prefill passes of 8, 8, 8, 1 rows)."""
+    w, dec, orc = make_pair(cfg, 41)
+    page = synth.make_pages(cfg, 42, [20], [5], [24])[0]
+    N = 24
+    # autoregressive
+    g_ar, g_steps = run_gpu_steps(dec, page, N, 0)
+    r_ar, r_logits = orc.generate_ar(page.vision, page.prompt, N, keep_logits=True)
+    ref_steps = [od.StepRecord(0, [], [r_ar[i + 1]], 0, r_logits[i + 1][None]) for i in range(N - 1)]
+    n, worst, note = compare_steps(g_steps, ref_steps, tol)
+    log(f"{cfg.dtype} AR: {n} steps agree, max |dlogit| {worst:.2e}, {note}")
+    assert worst < tol
+    assert n >= 8
+    # speculative, K = 3, the real draft block
+    g_sp, g_ssteps = run_gpu_steps(dec, page, N, 3)
+    r_sp, r_ssteps = orc.generate_spec(page.vision, page.prompt, N, 3, keep_logits=True)
+    assert r_sp == r_ar                    # oracle lossless
+    assert g_sp == g_ar                    # GPU spec == GPU AR, bit for bit
+    n, worst, note = compare_steps(g_ssteps, r_ssteps, tol)
+    log(f"{cfg.dtype} spec K=3: {n}/{len(r_ssteps)} steps agree, max |dlogit| {worst:.2e}, {note}, "
+        f"accepted {[s['n'] for s in g_ssteps]}")
+    assert worst < tol
+    assert n >= 4
+    # logits of the accepted verify rows equal the AR logits bitwise (batch invariance)
+    ar_rows = [s["logits"][0] for s in g_steps]
+    pos = 0
+    for s in g_ssteps:
+        for i in range(s["n"] + 1):
+            if pos + i < len(ar_rows):
+                assert np.array_equal(s["logits"][i], ar_rows[pos + i]), (pos, i)
+        pos += s["n"] + 1
+
+
+def test_routing_taps_bit_exact():
+    """Layer-by-layer routing indices of a verify step equal the oracle's
+    (excused only where the oracle's 6th/7th logit gap is under 1e-4)."""
+    cfg = SMALL32
+    w, dec, orc = make_pair(cfg, 43)
+    page = synth.make_pages(cfg, 44, [12], [3], [4])[0]
+    K = 3
+    route = torch.full((cfg.n_layers, K + 1, 8), -1, dtype=torch.int32, device="cuda")
+    hid = torch.zeros(K + 1, cfg.d_model, dtype=torch.float32, device="cuda")
+    from speculative_moe_decoding_amd import ocrdec
+    ocrdec.ocrdec_set_taps(dec.h, route, hid)
+    pending = dec.prefill([page])
+    draft = torch.tensor([[7, 4000, 123]], dtype=torch.int32, device="cuda")
+    dec.verify(1, K, draft)
+    torch.cuda.synchronize()
+    st = orc.new_state(64)
+    y0 = orc.prefill(st, page.vision, page.prompt, with_draft=False)
+    assert int(pending.item()) == y0
+    rec = []
+    h = orc.verifier_forward(st, orc.embed([y0, 7, 4000, 123]), np.arange(15, 19), record=rec)
+    got = route.cpu().numpy()
+    checked = 0
+    for l in range(cfg.n_layers):
+        for r in range(K + 1):
+            assert list(got[l, r, 6:]) == [64, 65]
+            if list(got[l, r, :6]) != list(rec[l][r]):
+                pytest.fail(f"layer {l} row {r}: {got[l, r, :6]} vs oracle {rec[l][r]}")
+            checked += 1
+    np.testing.assert_allclose(hid.cpu().numpy(), h, atol=1e-3, rtol=1e-4)
+    log(f"routing bit-exact on {checked} (layer, row) pairs")
+
+
+def test_batch_invariance_and_slots():
+    """Two pages decoded together (B = 2) give bitwise the tokens of each page
+    decoded alone; sequences use independent state slots."""
+    cfg = SMALL16
+    w = synth.Weights(cfg, 45)
+    from speculative_moe_decoding_amd import ocrdec
+    pages = synth.make_pages(cfg, 46, [20, 9], [5, 11], [20, 20])
+    dec2 = ocrdec.Decoder(cfg, w.device_arrays(), max_batch=2, max_k=3, max_positions=512)
+    toks2, acc2, _ = dec2.generate(pages, 20, 3, record=True, check_every=1)
+    for b in range(2):
+        dec1 = ocrdec.Decoder(cfg, w.device_arrays(), max_batch=1, max_k=3, max_positions=512)
+        toks1, acc1, _ = dec1.generate([pages[b]], 20, 3, record=True, check_every=1)
+        assert toks1[0].tolist() == toks2[b].tolist()
+        assert acc1[0] == acc2[b]
+        ar1, _, _ = dec1.generate([pages[b]], 20, 0, check_every=1)
+        assert ar1[0].tolist() == toks1[0].tolist()
+
+
+def test_controlled_acceptance_lossless():
+    """Drafts replaced by the controlled generator: committed tokens equal the AR
+    trace and the accepted lengths equal the oracle's prediction from SplitMix64."""
+    cfg = SMALL16
+    w = synth.Weights(cfg, 47)
+    from speculative_moe_decoding_amd import ocrdec
+    page = synth.make_pages(cfg, 48, [16], [4], [40])[0]
+    dec = ocrdec.Decoder(cfg, w.device_arrays(), max_batch=1, max_k=3, max_positions=512)
+    N = 40
+    for K, alpha in ((1, 0.826), (2, 0.691), (3, 0.576)):
+        ar, _, _ = dec.generate([page], N + K + 2, 0, check_every=4)
+        trace = torch.from_numpy(ar.astype(np.int32)).cuda()
+        p = synth.replacement_probability(alpha, K)
+        thr = od.replace_threshold(p)
+        toks, acc, _ = dec.generate([page], N, K, trace=trace, seed=3000, threshold=thr, record=True,
+                                    check_every=1)
+        assert toks[0].tolist() == ar[0][:N].tolist()
+        assert acc[0] == od.controlled_accepts(N, K, 3000, p, seq_index=0)
