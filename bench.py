@@ -1,0 +1,291 @@
+#!/usr/bin/env python3
+"""Decode benchmark of the ocrdec HIP path on one MI355X.
+
+Workload (the pages' L4 table setting, batch 1, K = 3, re-created
+synthetically): the 12-layer bf16 DeepSeek-3B-MoE decoder with random-init
+weights (seed 1234), one Base-mode page = 256 vision rows ~ N(0,1) + 32 prompt
+ids (seed 2001), FastMTP K = 3.  The draft block runs every step (its cost is
+real) but its tokens are replaced by the controlled-acceptance drafts: the
+verifier's own greedy continuation (from a K = 0 run), each slot replaced with
+probability p = 0.2515, which gives the table's 57.6 % acceptance.  Output is
+lossless, so the committed tokens equal the K = 0 trace (checked).
+
+One step = draft (3 passes) + controlled override + verify (4 rows through
+12 MoE layers + LM head) + accept.  The default 405 steps are the 1,085 output
+tokens of one page (the pages' mean tokens per page).
+
+Prints one JSON line (stdout).  `value` = output tokens / s of the timed steps.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "output tokens/s @batch1 K=3 (12-layer MoE, bf16); % of MI355X HBM peak"
+HBM_PEAK_GBS = 8000.0
+D, I, V, L = 1280, 896, 129280, 12
+EXPERT_GATE_UP_BYTES = 2 * I * D * 2          # gate + up rows of one expert, bf16
+EXPERT_DOWN_BYTES = D * I * 2
+DENSE_LAYER_BYTES = 2 * (3 * 1280 * D + D * 1280 + 64 * D)   # qkv, o, router (bf16)
+LM_HEAD_BYTES = 2 * V * D
+KV_POS_BYTES = 2 * 2 * 1280                   # k + v of one position, one layer, bf16
+DRAFT_PASS_BYTES = 2 * (2 * D * D + 3 * 1280 * D + D * 1280 + 3 * 3584 * D) + LM_HEAD_BYTES
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "speculative_moe_decoding_amd", "csrc")
+    for f in ("common.h", "kernels_moe.hip"):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(launch_bytes: float):
+    """HBM traffic per expert gate/up launch from the committed rocprofv3 PMC
+    summary, if it was taken on the current kernel source."""
+    p = os.path.join(ROOT, "profiles", "expert_gate_up_traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except Exception:
+        return None
+    if d.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(w, page, K, p, seed, n_prefix_vision=32, n_prompt=32, n_trace=12, n_steps=6):
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+    from oracle import decoder as od
+    orc = od.Oracle(w.cfg, w.f32)
+    vis = page.vision[:n_prefix_vision]
+    prm = page.prompt[:n_prompt]
+    t0 = time.time()
+    trace, _ = orc.generate_ar(vis, prm, n_trace + K + 2)
+    t1 = time.time()
+    prop = od.controlled_proposer(trace, seed, p, w.cfg.vocab)
+    st_t0 = time.time()
+    toks, steps = orc.generate_spec(vis, prm, n_trace, K, proposer=prop, draft_for_cost=True, max_steps=n_steps)
+    t2 = time.time()
+    # time of the speculative steps alone: total minus the prefill, measured separately
+    st = orc.new_state(vis.shape[0] + len(prm) + 8)
+    t3 = time.time()
+    orc.prefill(st, vis, prm, with_draft=True)
+    t_prefill = time.time() - t3
+    t_steps = max(1e-9, (t2 - st_t0) - t_prefill)
+    committed = sum(s.accepted + 1 for s in steps)
+    assert toks == trace[:len(toks)]
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except Exception:
+        cores = os.cpu_count()
+    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    return dict(value=committed / t_steps, unit="tokens/s", cores=min(cores, threads), kind="oracle",
+                sample=(f"fp64 NumPy oracle, same 12-layer bf16 weights, {len(steps)} speculative steps "
+                        f"(K={K}, draft block run for cost, controlled drafts p={p:.4f}) after a "
+                        f"{vis.shape[0]}+{len(prm)}-row prefix (not the 288-row one, to bound the "
+                        f"prefill); {committed} tokens in {t_steps:.1f}s; AR trace {t1 - t0:.1f}s untimed"))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=405)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--k", type=int, default=3)
+    ap.add_argument("--alpha", type=float, default=0.576)
+    ap.add_argument("--instrumented-steps", type=int, default=120)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}); the decode of independent pages "
+              f"shards data-parallel with no exchange, see DESIGN.md.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    from speculative_moe_decoding_amd import ocrdec, synth
+
+    K, S, W = args.k, args.steps, args.warmup
+    wl = synth.WORKLOADS["base_page_bf16"]
+    cfg = wl["cfg"]
+    t = time.time()
+    w = synth.Weights(cfg, wl["weight_seed"])
+    page = synth.make_pages(cfg, wl["input_seed"], [wl["n_vision"]], [wl["n_prompt"]], [wl["n_out"]])[0]
+    log(f"weights generated in {time.time() - t:.1f}s")
+    P = page.prefix_len
+    n_trace = (max(S, W, args.instrumented_steps) + 2) * (K + 1) + 2
+    max_pos = min(32768, P + n_trace + 4 * (K + 1) + 64)
+    dec = ocrdec.Decoder(cfg, w.device_arrays(), max_batch=1, max_k=K, max_positions=max_pos)
+    torch.cuda.synchronize()
+    p = synth.replacement_probability(args.alpha, K)
+    thr = int(p * float(1 << 53))
+    seed = 3000
+
+    # K = 0 greedy trace (also the AR reference for the lossless check)
+    torch.cuda.synchronize()
+    t = time.time()
+    ar, _, ar_steps = dec.generate([page], n_trace, 0, check_every=64)
+    torch.cuda.synchronize()
+    t_ar = time.time() - t
+    trace = torch.from_numpy(ar.astype(np.int32)).cuda()
+    log(f"K=0 trace: {n_trace} tokens, {ar_steps} steps in {t_ar:.2f}s")
+
+    B = 1
+    draft = dec.i32(B, K)
+    greedy = dec.i32(B, K + 1)
+    n_acc = dec.i32(B)
+    out_tokens = torch.zeros(B, n_trace + K + 2, dtype=torch.int32, device="cuda")
+    out_len = dec.i32(B)
+
+    def start_page():
+        pend = dec.prefill([page])
+        out_tokens[:, 0] = pend
+
+    def step():
+        dec.draft(B, K, out=draft)
+        dec.controlled(B, K, trace, seed, thr, draft)
+        dec.verify(B, K, draft, greedy=greedy)
+        dec.accept(B, K, draft, greedy, n_acc, out_tokens, out_len)
+
+    # warmup
+    start_page()
+    for _ in range(W):
+        step()
+    torch.cuda.synchronize()
+    # prefill time of one page
+    torch.cuda.synchronize()
+    t = time.time()
+    start_page()
+    torch.cuda.synchronize()
+    t_prefill = time.time() - t
+    # timed region: exactly S steps from the start of the page
+    torch.cuda.synchronize()
+    t0 = time.time()
+    for _ in range(S):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.time() - t0
+    committed = int(out_len.item()) - 1
+    got = out_tokens[0, :committed + 1].cpu().numpy()
+    lossless = bool(np.array_equal(got, ar[0][:committed + 1]))
+    tok_s = committed / elapsed
+    tau = (committed) / S
+    log(f"timed: {S} steps, {committed} tokens in {elapsed * 1e3:.1f} ms -> {tok_s:.1f} tok/s, tau {tau:.3f}, "
+        f"lossless {lossless}")
+
+    # instrumented pass: events around draft / verify, per-launch events around the expert kernels
+    Si = min(args.instrumented_steps, S)
+    start_page()
+    torch.cuda.synchronize()
+    ocrdec.ocrdec_expert_timing(dec.h, True)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(Si)]
+    accs = torch.zeros(Si, dtype=torch.int32, device="cuda")
+    for i in range(Si):
+        ev[i][0].record()
+        dec.draft(B, K, out=draft)
+        dec.controlled(B, K, trace, seed, thr, draft)
+        ev[i][1].record()
+        dec.verify(B, K, draft, greedy=greedy)
+        ev[i][2].record()
+        dec.accept(B, K, draft, greedy, n_acc, out_tokens, out_len)
+        accs[i:i + 1].copy_(n_acc)
+    torch.cuda.synchronize()
+    st = ocrdec.ocrdec_expert_stats(dec.h)
+    ocrdec.ocrdec_expert_timing(dec.h, False)
+    draft_ms = np.array([a.elapsed_time(b) for a, b, _ in ev])
+    verify_ms = np.array([b.elapsed_time(c) for _, b, c in ev])
+    acc_np = accs.cpu().numpy()
+    pos = P + np.concatenate([[0], np.cumsum(acc_np + 1)[:-1]])       # kv_len at each verify
+    sets = st["expert_sets"]
+    n_up = st["n_gate_up"]
+    pairs = 8 * (K + 1)
+    up_bytes = sets * EXPERT_GATE_UP_BYTES + n_up * pairs * (D + I) * 4
+    up_ms = st["ms_gate_up"]
+    achieved = up_bytes / (up_ms * 1e-3) / 1e9
+    verify_bytes = (L * Si * DENSE_LAYER_BYTES + sets * 3 * I * D * 2 + Si * LM_HEAD_BYTES
+                    + L * KV_POS_BYTES * float(np.sum(pos + K + 1)))
+    verify_gbs = verify_bytes / (verify_ms.sum() * 1e-3) / 1e9
+    draft_bytes = Si * K * DRAFT_PASS_BYTES
+    log(f"verify {verify_ms.mean():.3f} ms/step ({verify_gbs:.0f} GB/s, "
+        f"{verify_gbs / HBM_PEAK_GBS * 100:.1f}% of HBM), draft {draft_ms.mean():.3f} ms/step; "
+        f"expert gate/up {up_ms / max(1, n_up) * 1e3:.1f} us/launch -> {achieved:.0f} GB/s; "
+        f"{sets / (L * Si):.2f} active experts / layer")
+
+    traffic = load_traffic(up_bytes / max(1, n_up))
+    result = {
+        "metric": METRIC,
+        "value": round(tok_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": S,
+        "warmup": W,
+        "ms_per_step": round(elapsed / S * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "base_page_bf16: 12-layer DeepSeek-3B-MoE decoder (d=1280, 64+2 experts, top-6, "
+                        "V=129280), random-init bf16 weights, one page = 256 vision + 32 prompt rows, "
+                        "batch 1, FastMTP K=3 with controlled acceptance 57.6%",
+            "batch": B, "K": K, "alpha_target": args.alpha, "prefix_rows": P,
+            "compute": "bf16 weights and KV cache, fp32 activations and accumulation",
+        },
+        "roofline": {
+            "kernel": "k_expert_gate_up (grouped expert GEMV, gate+up)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "launches": n_up,
+            "avg_launch_us": round(up_ms / max(1, n_up) * 1e3, 2),
+            "algorithmic_bytes_per_launch": round(up_bytes / max(1, n_up)),
+        },
+        "tau": round(tau, 4),
+        "alpha": round((tau - 1) / K, 4),
+        "lossless_vs_ar": lossless,
+        "pages_per_s": round(1.0 / (t_prefill + 1085 / tok_s), 4),
+        "prefill_ms": round(t_prefill * 1e3, 2),
+        "ar_tok_per_s": round((n_trace - 1) / t_ar, 1),
+        "verify_step": {"ms": round(float(verify_ms.mean()), 4), "GB_per_s": round(verify_gbs, 1),
+                        "frac_hbm": round(verify_gbs / HBM_PEAK_GBS, 4),
+                        "algorithmic_GB": round(verify_bytes / Si / 1e9, 4),
+                        "active_experts_per_layer": round(sets / (L * Si), 2)},
+        "draft_step": {"ms": round(float(draft_ms.mean()), 4),
+                       "GB_per_s": round(draft_bytes / (draft_ms.sum() * 1e-3) / 1e9, 1)},
+        "expert_down": {"avg_launch_us": round(st["ms_down"] / max(1, st["n_down"]) * 1e3, 2),
+                        "GB_per_s": round(sets * EXPERT_DOWN_BYTES / (st["ms_down"] * 1e-3) / 1e9, 1)},
+    }
+    if not args.no_cpu_baseline:
+        t = time.time()
+        result["cpu_baseline"] = cpu_baseline(w, page, K, p, seed)
+        log(f"cpu baseline: {result['cpu_baseline']['value']:.3f} tok/s ({time.time() - t:.1f}s)")
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

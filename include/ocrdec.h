@@ -142,8 +142,9 @@ int ocrdec_set_taps(ocrdec_model* m, int32_t* route_idx, float* hidden);
  * enable != 0 records HIP events around each launch from now on (clears the
  * totals).  ocrdec_expert_stats synchronises those events and returns the
  * total milliseconds and launch count of each of the two kernels, and the
- * number of (layer, expert) weight sets they streamed, counted on the device. */
-int ocrdec_expert_timing(ocrdec_model* m, int enable);
+ * number of (layer, expert) weight sets they streamed since timing was enabled,
+ * counted on the device. */
+int ocrdec_expert_timing(ocrdec_model* m, int enable);  /* synchronises the device */
 int ocrdec_expert_stats(ocrdec_model* m, double* ms_gate_up, long long* n_gate_up, double* ms_down,
                         long long* n_down, long long* expert_sets);
 

@@ -35,6 +35,9 @@ Readings of what the pages leave open (each is also listed in the design doc):
   index, gate = the softmax probability (no renormalisation); the two shared
   experts have gate 1; experts are SwiGLU, F(b) = W_d (silu(W_g b) * W_u b);
   untied embedding and LM head; greedy argmax takes the lowest id on ties.
+  Precision: a bf16 model stores its matrices and its KV cache in bf16; the
+  oracle computes on the stored values and rounds keys (after RoPE) and values
+  to bf16 where they enter the cache; everything else stays float64.
   Draft: the row at position p takes (h_{p-1}, e_p) -- the verifier's pre-norm
   final hidden of the previous position and the input embedding of p -- fuses
   u = W_f [RMSNorm(h); RMSNorm(e)], runs one dense pre-norm block (attention
@@ -155,6 +158,14 @@ def moe(b: np.ndarray, W_r, W_g, W_u, W_d, n_experts: int, n_shared: int, top_k:
     return y, idx
 
 
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round to the nearest bfloat16 value (8 significant bits, ties to even),
+    directly from float64.  A bf16 model stores its KV cache in bf16."""
+    x = np.asarray(x, F64)
+    m, e = np.frexp(x)                      # x = m * 2^e, 0.5 <= |m| < 1
+    return np.ldexp(np.rint(m * 256.0) / 256.0, e)
+
+
 def greedy(logits: np.ndarray) -> np.ndarray:
     """Greedy token: argmax of the float32-rounded logits, lowest id on ties."""
     return np.argmax(np.asarray(logits, F64).astype(np.float32), axis=-1)
@@ -214,6 +225,7 @@ class StepRecord:
     greedy: List[int]           # g_0..g_K of the verifier
     accepted: int               # n
     logits: Optional[np.ndarray] = None   # [K+1, V] verifier logits (kept on request)
+    draft_margins: Optional[List[float]] = None   # top-2 margin of each draft pass's logits
 
 
 class Oracle:
@@ -261,6 +273,8 @@ class Oracle:
         v = qkv[:, 2 * Hd:].reshape(T, c.n_heads, c.head_dim)
         q = rope(q, pos, c.rope_theta)
         k = rope(k, pos, c.rope_theta)
+        if getattr(c, "dtype", "f32") == "bf16":
+            k, v = round_bf16(k), round_bf16(v)
         K_cache[pos] = k
         V_cache[pos] = v
         L = int(pos[-1]) + 1
@@ -353,30 +367,39 @@ class Oracle:
         pos = np.arange(st.draft_len, st.kv_len + 1)
         assert len(pos) == len(st.cu) == st.hbuf.shape[0]
         u = self.draft_forward(st, st.hbuf, self.embed(st.cu), pos)
-        d = [int(greedy(self.draft_logits(u[-1:]))[0])]
+        lg = self.draft_logits(u[-1:])
+        d = [int(greedy(lg)[0])]
+        st.draft_margins = [float(top2_margin(lg)[0])]
         prev = u[-1:]
         for j in range(2, K + 1):
             u = self.draft_forward(st, prev, self.embed([d[-1]]), [st.kv_len + j - 1])
-            d.append(int(greedy(self.draft_logits(u))[0]))
+            lg = self.draft_logits(u)
+            d.append(int(greedy(lg)[0]))
+            st.draft_margins.append(float(top2_margin(lg)[0]))
             prev = u
         return d
 
     def generate_spec(self, vision, prompt, n_out: int, K: int,
                       proposer: Optional[Callable] = None, keep_logits: bool = False,
-                      seq_index: int = 0):
+                      seq_index: int = 0, draft_for_cost: bool = False, max_steps: Optional[int] = None):
         """FastMTP speculative decoding with greedy longest-prefix acceptance.
 
         proposer(step, committed_tokens, K) -> K tokens replaces the draft block
         (losslessness tests, controlled acceptance); None runs the draft block.
+        draft_for_cost runs the draft block even when a proposer replaces its
+        tokens (as the controlled-acceptance benchmark does); max_steps bounds
+        the number of speculative steps.
         Returns (tokens[:n_out], [StepRecord])."""
         P = vision.shape[0] + len(prompt)
         st = self.new_state(P + n_out + K + 2)
-        self.prefill(st, vision, prompt, with_draft=proposer is None)
+        self.prefill(st, vision, prompt, with_draft=proposer is None or draft_for_cost)
         steps: List[StepRecord] = []
-        while len(st.out) < n_out:
+        while len(st.out) < n_out and (max_steps is None or len(steps) < max_steps):
             if proposer is None:
                 d = self.draft_propose(st, K)
             else:
+                if draft_for_cost:
+                    self.draft_propose(st, K)
                 d = [int(t) for t in proposer(len(steps), list(st.out), K)]
             q = st.kv_len
             rows = [st.out[-1]] + d
@@ -387,7 +410,8 @@ class Oracle:
             while n < K and d[n] == g[n]:
                 n += 1
             st.out += d[:n] + [g[n]]
-            steps.append(StepRecord(q, d, g, n, lg if keep_logits else None))
+            steps.append(StepRecord(q, d, g, n, lg if keep_logits else None,
+                                    st.draft_margins if proposer is None else None))
             # rollback: verifier KV keeps positions < q + n + 1; the draft KV keeps
             # position q (computed from a true verifier hidden); the next catch-up
             # recomputes draft rows q+1 .. q+n+1 from the verifier hiddens h[0..n].
@@ -409,6 +433,7 @@ class SeqState:
     hbuf: Optional[np.ndarray] = None
     cu: list = dataclasses.field(default_factory=list)
     first_logits: Optional[np.ndarray] = None
+    draft_margins: Optional[list] = None
 
 
 # ----------------------------------------------------------------------------

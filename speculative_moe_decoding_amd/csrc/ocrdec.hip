@@ -121,6 +121,7 @@ struct ocrdec_model {
   bool timing;
   std::vector<hipEvent_t> ev;  // triplets: before gate/up, between, after down
   size_t ev_used;
+  long long stats_base;        // device expert counter when timing was enabled
 };
 
 namespace {
@@ -386,6 +387,7 @@ int ocrdec_create(const ocrdec_config* cfg, const void* const* weight_ptrs, int 
   m->tap_hidden = nullptr;
   m->timing = false;
   m->ev_used = 0;
+  m->stats_base = 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (hipMemsetAsync(misc, 0, 64 * 4, s) != hipSuccess || hipMemsetAsync(m->mb.stats, 0, 64, s) != hipSuccess ||
       hipMemsetAsync(m->state + p.s_ints, 0, p.s_hbuf - p.s_ints, s) != hipSuccess) {
@@ -490,6 +492,10 @@ int ocrdec_expert_timing(ocrdec_model* m, int enable) {
   if (!m) return fail(OCRDEC_EINVAL, "model is null");
   m->timing = enable != 0;
   m->ev_used = 0;
+  m->stats_base = 0;
+  if (hipDeviceSynchronize() != hipSuccess ||
+      hipMemcpy(&m->stats_base, m->mb.stats, sizeof(long long), hipMemcpyDeviceToHost) != hipSuccess)
+    return fail(OCRDEC_EHIP, "reading the expert counter failed");
   return OCRDEC_OK;
 }
 
@@ -500,7 +506,7 @@ int ocrdec_expert_stats(ocrdec_model* m, double* ms_gate_up, long long* n_gate_u
   long long na = 0, nb = 0;
   const size_t n = (m->ev_used / 3) * 3;
   if (n > 0 && hipEventSynchronize(m->ev[n - 1]) != hipSuccess) return fail(OCRDEC_EHIP, "hipEventSynchronize failed");
-  for (size_t i = 0; i + 2 < n + 0 && i < n; i += 3) {
+  for (size_t i = 0; i + 2 < n; i += 3) {
     float t1 = 0, t2 = 0;
     if (hipEventElapsedTime(&t1, m->ev[i], m->ev[i + 1]) != hipSuccess ||
         hipEventElapsedTime(&t2, m->ev[i + 1], m->ev[i + 2]) != hipSuccess)
@@ -517,7 +523,7 @@ int ocrdec_expert_stats(ocrdec_model* m, double* ms_gate_up, long long* n_gate_u
   if (n_gate_up) *n_gate_up = na;
   if (ms_down) *ms_down = b;
   if (n_down) *n_down = nb;
-  if (expert_sets) *expert_sets = sets;
+  if (expert_sets) *expert_sets = sets - m->stats_base;
   return OCRDEC_OK;
 }
 

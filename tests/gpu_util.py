@@ -61,10 +61,11 @@ def run_gpu_steps(dec, page, n_out, K, with_logits=True, proposer=None):
 
 
 def compare_steps(gpu_steps, ref_steps, tol, check_drafts=True):
-    """Step records must agree exactly (drafts, greedy tokens, accepted lengths)
-    until the first place where the oracle's top-2 logit margin is under tol,
-    and the logits must agree within tol up to there.  Returns (steps compared,
-    max |logit diff|, excused flip or None)."""
+    """Step records must agree exactly (drafts, greedy tokens, accepted lengths);
+    a mismatch is excused only where the oracle's top-2 logit margin is under
+    tol, and comparison stops there (the two runs then follow different
+    sequences).  Logits must agree within tol on every compared row.  Returns
+    (steps compared, max |logit diff|, note on an excused flip or None)."""
     worst = 0.0
     for s, (g, r) in enumerate(zip(gpu_steps, ref_steps)):
         n_rows = r.accepted + 1
@@ -73,14 +74,14 @@ def compare_steps(gpu_steps, ref_steps, tol, check_drafts=True):
             worst = max(worst, float(np.abs(g["logits"][:n_rows] - r.logits[:n_rows]).max()))
         near = bool((margins < tol).any())
         if check_drafts and g["drafts"] != r.drafts:
-            if near:
-                return s, worst, f"step {s}: draft differs after a near tie"
-            raise AssertionError(f"step {s}: drafts {g['drafts']} != oracle {r.drafts}")
+            j = next(i for i in range(len(r.drafts)) if g["drafts"][i] != r.drafts[i])
+            if r.draft_margins is not None and r.draft_margins[j] < tol:
+                return s, worst, f"step {s}: draft {j} differs at a near tie (margin {r.draft_margins[j]:.2e})"
+            raise AssertionError(f"step {s}: drafts {g['drafts']} != oracle {r.drafts} "
+                                 f"(margins {r.draft_margins})")
         if g["greedy"][:n_rows] != r.greedy[:n_rows] or g["n"] != r.accepted:
             if near:
                 return s, worst, f"step {s}: greedy differs at a near tie (margin {margins.min():.2e})"
             raise AssertionError(f"step {s}: greedy {g['greedy']} n={g['n']} != oracle {r.greedy} n={r.accepted}; "
                                  f"margins {margins}")
-        if near:
-            return s + 1, worst, f"step {s}: near tie (margin {margins.min():.2e}), stop comparing"
-    return len(ref_steps), worst, None
+    return min(len(gpu_steps), len(ref_steps)), worst, None

@@ -181,6 +181,29 @@ def test_moe_terms():
         np.testing.assert_allclose(y[t:t + 1], want, rtol=1e-12)
 
 
+def test_round_bf16_worked_values():
+    # bf16 keeps 8 significant bits: spacing 2^-7 at 1.0, ties go to the even mantissa
+    x = np.array([1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -7, -(1 + 2 ** -8 + 2 ** -20), 3.0, 0.0, 1e-3])
+    want = [1.0, 1.0, 1 + 2 ** -6, 1 + 2 ** -7, -(1 + 2 ** -7), 3.0, 0.0, 0.00099945068359375]
+    np.testing.assert_array_equal(od.round_bf16(x), want)
+    # agrees with float32 -> bf16 round-to-nearest-even wherever the float32 step is exact
+    r = np.random.default_rng(9).standard_normal(4096).astype(np.float32)
+    u = r.view(np.uint32).astype(np.uint64)
+    bits = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint32) << 16
+    np.testing.assert_array_equal(od.round_bf16(r.astype(np.float64)), bits.view(np.float32).astype(np.float64))
+
+
+def test_bf16_model_rounds_kv_cache():
+    cfg = dataclasses.replace(TINY, dtype="bf16")
+    m = tiny_model(cfg=cfg)
+    vision, prompt = tiny_page()
+    st = m.new_state(16)
+    m.verifier_forward(st, m.prefix_rows(vision, prompt), np.arange(8))
+    kv = st.kv[:, :, :8]
+    np.testing.assert_array_equal(od.round_bf16(kv), kv)
+    assert np.abs(kv).max() > 0
+
+
 def test_greedy_ties_and_fp32_decision():
     assert od.greedy(np.array([[0.5, 2.0, 2.0, -1.0]]))[0] == 1
     # differences below float32 resolution are ties, decided by the lowest id
