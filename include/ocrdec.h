@@ -148,6 +148,14 @@ int ocrdec_expert_timing(ocrdec_model* m, int enable);  /* synchronises the devi
 int ocrdec_expert_stats(ocrdec_model* m, double* ms_gate_up, long long* n_gate_up, double* ms_down,
                         long long* n_down, long long* expert_sets);
 
+/* Benchmark harness: replay the grouped expert gate/up GEMV n_rounds times over
+ * the weights of every layer in turn (n_rounds * n_layers back-to-back launches
+ * on `stream`), with the routing of the last verify call, so that a pair of
+ * events around the call times the kernel alone.  If expert_sets_per_launch
+ * (host, nullable) is given, the call first synchronises the stream and stores
+ * that routing's active-expert count there. */
+int ocrdec_replay_expert_gate_up(ocrdec_model* m, void* stream, int n_rounds, int* expert_sets_per_launch);
+
 const char* ocrdec_last_error(void);
 
 #ifdef __cplusplus

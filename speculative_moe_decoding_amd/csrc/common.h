@@ -124,6 +124,48 @@ __device__ __forceinline__ void norm_rows_to_lds(const float* __restrict__ x, lo
   }
 }
 
+// RMSNorm of `m_rows` activation rows into LDS, one wavefront per row (rows
+// w, w + n_waves, ...): lane l sums x[k]^2 over k = l + 64 j in order, the 64
+// lane sums go through the xor butterfly, r = 1 / sqrt(sum / K + eps), and
+// xs[m][k] = (x[k] * r) * g[k].  g == nullptr copies the rows unchanged.
+// Row m is read from x + src_row(m) * ldx.  No barrier inside.
+template <int K, typename SrcRow>
+__device__ __forceinline__ void norm_rows_wave(const float* __restrict__ x, long ldx, SrcRow src_row, int m_rows,
+                                               const float* __restrict__ g, float eps, float* xs, int n_waves) {
+  static_assert(K % 64 == 0, "row length must be a multiple of 64");
+  constexpr int J = K / 64;
+  const int lane = lane_id();
+  for (int m = wave_id(); m < m_rows; m += n_waves) {
+    const float* xr = x + (long)src_row(m) * ldx;
+    float v[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) v[j] = xr[lane + 64 * j];
+    if (g != nullptr) {
+      float ss = 0.f;
+#pragma unroll
+      for (int j = 0; j < J; ++j) ss = fmaf(v[j], v[j], ss);
+      ss = wave_sum(ss);
+      const float r = 1.0f / sqrtf(ss / (float)K + eps);
+#pragma unroll
+      for (int j = 0; j < J; ++j) xs[m * K + lane + 64 * j] = (v[j] * r) * g[lane + 64 * j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < J; ++j) xs[m * K + lane + 64 * j] = v[j];
+    }
+  }
+}
+
+// Raise a kernel's dynamic-LDS limit once (needed above 64 KiB).
+template <typename F>
+inline void allow_lds(F* kernel, size_t bytes) {
+  if (bytes > 65536) (void)hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+struct RowIdentity {
+  int base;
+  __device__ __forceinline__ int operator()(int m) const { return base + m; }
+};
+
 // Wavefront GEMV core: R weight rows (pointers rows[r], each K elements of T)
 // against `m_act` (<= MR) activation rows held in LDS (xs[m][K], fp32).
 // acc[r][m] holds the lane partial sums; call wave_reduce_acc afterwards.

@@ -11,14 +11,21 @@
 
 namespace ocr {
 
-// cos / sin of pos * theta^(-2i/HD): angle in fp64, rounded to fp32.
-__device__ __forceinline__ void rope_cs(int pos, int i, float theta, float& c, float& s) {
-  const double inv = pow((double)theta, -(double)(2 * i) / (double)HD);
-  const double a = (double)pos * inv;
-  double sd, cd;
-  sincos(a, &sd, &cd);
-  c = (float)cd;
-  s = (float)sd;
+// RoPE table: tab[pos][i] = (cos, sin) of pos * theta^(-2i/HD) for i < HD/2,
+// angle in fp64, rounded to fp32.  Built once per model handle.
+__global__ void k_rope_table(int max_pos, float theta, float2* __restrict__ tab) {
+  const long n = (long)max_pos * (HD / 2);
+  for (long e = blockIdx.x * (long)blockDim.x + threadIdx.x; e < n; e += (long)gridDim.x * blockDim.x) {
+    const int pos = (int)(e / (HD / 2)), i = (int)(e % (HD / 2));
+    const double inv = pow((double)theta, -(double)(2 * i) / (double)HD);
+    double sd, cd;
+    sincos((double)pos * inv, &sd, &cd);
+    tab[e] = make_float2((float)cd, (float)sd);
+  }
+}
+
+void launch_rope_table(hipStream_t s, int max_pos, float theta, float2* tab) {
+  hipLaunchKernelGGL(k_rope_table, dim3(256), dim3(256), 0, s, max_pos, theta, tab);
 }
 
 // Rotate the pair (a, b) = (x_i, x_{i+64}) by the angle with cosine c, sine s.
@@ -29,15 +36,15 @@ __device__ __forceinline__ void rot(float a, float b, float c, float s, float& o
 
 // One wavefront = one "quad" of 4 output rows.  q / k quads are rows
 // {2u, 2u+1, 2u+64, 2u+65} of one head so that both halves of a RoPE pair land
-// in the same wavefront; v quads are 4 consecutive rows.
+// in the same wavefront; v quads are 4 consecutive rows.  Weight loads are
+// issued first; the RMSNorm of the activation rows overlaps them.
 template <typename T, int MR>
 __global__ __launch_bounds__(256) void k_qkv_rope(const float* __restrict__ x, const float* __restrict__ gain,
                                                   float eps, const T* __restrict__ wqkv, int M, RowPlan plan,
                                                   float* __restrict__ q, T* __restrict__ kv, int max_pos,
-                                                  float theta) {
+                                                  const float2* __restrict__ rope) {
   extern __shared__ float smem[];
   float* xs = smem;
-  float* red = smem + MR * D;
   const int wave = wave_id(), lane = lane_id();
   const int quad = blockIdx.x * 4 + wave;  // 0 .. 959
   const int m0 = blockIdx.y * MR;
@@ -56,7 +63,7 @@ __global__ __launch_bounds__(256) void k_qkv_rope(const float* __restrict__ x, c
   for (int r = 0; r < 4; ++r) rows[r] = wqkv + (long)ri[r] * D;
   WaveGemv<T, D, 4, MR> g;
   g.load(rows);
-  norm_rows_to_lds<D>(x + (long)m0 * D, D, m_act, gain, eps, xs, red);
+  norm_rows_wave<D>(x, D, RowIdentity{m0}, m_act, gain, eps, xs, 4);
   __syncthreads();
   float acc[4][MR];
   g.fma(xs, m_act, acc);
@@ -67,25 +74,26 @@ __global__ __launch_bounds__(256) void k_qkv_rope(const float* __restrict__ x, c
     if (lane == m && m < m_act) {
       const int row = m0 + m;
       const int b = row / plan.Q, i = row - b * plan.Q;
-      const bool valid = i < plan.cnt[b];
       const int pos = plan.base[b] + i;
+      const bool valid = i < plan.cnt[b] && pos >= 0 && pos < max_pos;
       const long slot = plan.slot[b];
       if (sec < 2) {
-        float c0, s0, c1, s1, o[4];
-        rope_cs(pos, 2 * u, theta, c0, s0);
-        rope_cs(pos, 2 * u + 1, theta, c1, s1);
-        rot(acc[0][m], acc[2][m], c0, s0, o[0], o[2]);
-        rot(acc[1][m], acc[3][m], c1, s1, o[1], o[3]);
+        const int pc = min(max(pos, 0), max_pos - 1);
+        const float2 cs0 = rope[(long)pc * (HD / 2) + 2 * u];
+        const float2 cs1 = rope[(long)pc * (HD / 2) + 2 * u + 1];
+        float o[4];
+        rot(acc[0][m], acc[2][m], cs0.x, cs0.y, o[0], o[2]);
+        rot(acc[1][m], acc[3][m], cs1.x, cs1.y, o[1], o[3]);
         const int dims[4] = {2 * u, 2 * u + 1, 2 * u + 64, 2 * u + 65};
         if (sec == 0) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) q[(long)row * QD + h * HD + dims[r]] = o[r];
-        } else if (valid && pos >= 0 && pos < max_pos) {
+        } else if (valid) {
           T* kd = kv + slot * slot_stride + ((long)h * max_pos + pos) * HD;
 #pragma unroll
           for (int r = 0; r < 4; ++r) kd[dims[r]] = WT<T>::store_cvt(o[r]);
         }
-      } else if (valid && pos >= 0 && pos < max_pos) {
+      } else if (valid) {
         T* vd = kv + slot * slot_stride + ((long)(NH + h) * max_pos + pos) * HD + 4 * u;
 #pragma unroll
         for (int r = 0; r < 4; ++r) vd[r] = WT<T>::store_cvt(acc[r][m]);
@@ -96,21 +104,16 @@ __global__ __launch_bounds__(256) void k_qkv_rope(const float* __restrict__ x, c
 
 template <typename T>
 void launch_qkv_rope(hipStream_t s, const float* x, const float* gain, float eps, const T* wqkv, int M,
-                     RowPlan plan, float* q, T* kv, int max_pos, float theta) {
+                     RowPlan plan, float* q, T* kv, int max_pos, const float2* rope) {
   const dim3 blk(256);
-  if (M <= 1) {
-    hipLaunchKernelGGL((k_qkv_rope<T, 1>), dim3(240, 1), blk, (1 * D + 4) * 4, s, x, gain, eps, wqkv, M, plan, q,
-                       kv, max_pos, theta);
-  } else if (M <= 2) {
-    hipLaunchKernelGGL((k_qkv_rope<T, 2>), dim3(240, 1), blk, (2 * D + 4) * 4, s, x, gain, eps, wqkv, M, plan, q,
-                       kv, max_pos, theta);
-  } else if (M <= 4) {
-    hipLaunchKernelGGL((k_qkv_rope<T, 4>), dim3(240, 1), blk, (4 * D + 4) * 4, s, x, gain, eps, wqkv, M, plan, q,
-                       kv, max_pos, theta);
-  } else {
-    hipLaunchKernelGGL((k_qkv_rope<T, MRG>), dim3(240, (M + MRG - 1) / MRG), blk, (MRG * D + 4) * 4, s, x, gain,
-                       eps, wqkv, M, plan, q, kv, max_pos, theta);
-  }
+#define OCR_QKV_CASE(MRV)                                                                                     \
+  hipLaunchKernelGGL((k_qkv_rope<T, MRV>), dim3(240, (M + MRV - 1) / MRV), blk, (size_t)MRV * D * 4, s, x, gain, \
+                     eps, wqkv, M, plan, q, kv, max_pos, rope);
+  if (M <= 1) OCR_QKV_CASE(1)
+  else if (M <= 2) OCR_QKV_CASE(2)
+  else if (M <= 4) OCR_QKV_CASE(4)
+  else OCR_QKV_CASE(MRG)
+#undef OCR_QKV_CASE
 }
 
 // Generic GEMV.  Each wavefront owns R consecutive output rows (EPI_SWIGLU: R/2
@@ -121,7 +124,6 @@ __global__ __launch_bounds__(256) void k_gemv(const float* __restrict__ a, long 
                                               int M, float* __restrict__ out, long ldo) {
   extern __shared__ float smem[];
   float* xs = smem;
-  float* red = smem + MR * K;
   const int wave = wave_id(), lane = lane_id();
   constexpr int UNITS = (EPI == EPI_SWIGLU) ? R / 2 : R;
   const int n0 = (blockIdx.x * 4 + wave) * UNITS;
@@ -144,7 +146,7 @@ __global__ __launch_bounds__(256) void k_gemv(const float* __restrict__ a, long 
   }
   WaveGemv<T, K, R, MR> g;
   g.load(rows);
-  norm_rows_to_lds<K>(a + (long)m0 * lda, lda, m_act, gain, eps, xs, red);
+  norm_rows_wave<K>(a, lda, RowIdentity{m0}, m_act, gain, eps, xs, 4);
   __syncthreads();
   float acc[R][MR];
   g.fma(xs, m_act, acc);
@@ -174,7 +176,7 @@ static void gemv_dispatch(hipStream_t s, const float* a, long lda, const float* 
   const dim3 blk(256);
 #define OCR_GEMV_CASE(MRV)                                                                                   \
   {                                                                                                          \
-    const size_t lds = ((size_t)MRV * K + 4) * 4;                                                            \
+    const size_t lds = (size_t)MRV * K * 4;                                                            \
     if (lds > 65536) {                                                                                       \
       static const bool attr_set = (hipFuncSetAttribute((const void*)k_gemv<T, K, R, MRV, EPI>,              \
                                                         hipFuncAttributeMaxDynamicSharedMemorySize,          \
@@ -211,131 +213,152 @@ void launch_gemv(hipStream_t s, int K, Epi epi, const float* a, long lda, const 
   }
 }
 
-// LM head + argmax, stage 1: each block scores LM_ROWS_PER_BLOCK vocab rows
-// (4 wavefronts x 4 tiles x 4 rows) for up to MR activation rows, keeps the
-// best (value, lowest id) per row; the last block to finish reduces the
-// per-block bests.
+// LM head + argmax, stage 1: block (x, y) scores LM_ROWS_PER_BLOCK vocab rows
+// (4 wavefronts x LM_TILES tiles x 4 rows, next tile's loads in flight while the
+// current one is reduced) for activation rows y*MR .. y*MR+MR-1 and writes the
+// best (value, lowest id) per row to part[row][x].  Output row m reads
+// activation row (last_valid ? m*Q + cnt[m] - 1 : m) and RMSNorms it.
+constexpr int LM_TILES = LM_ROWS_PER_BLOCK / 16;
+
+struct LmSrcRow {
+  const int* cnt;
+  int Q, last_valid, base;
+  __device__ __forceinline__ int operator()(int m) const {
+    const int om = base + m;
+    return last_valid ? om * Q + cnt[om] - 1 : om;
+  }
+};
+
 template <typename T, int MR>
 __global__ __launch_bounds__(256) void k_lmhead(const float* __restrict__ x, const int* __restrict__ cnt, int Q,
                                                 int last_valid, const float* __restrict__ gain, float eps,
                                                 const T* __restrict__ W, int V, int M,
                                                 float* __restrict__ part_val, int* __restrict__ part_idx,
-                                                int* __restrict__ counter, float* __restrict__ logits,
-                                                int* __restrict__ tok, int tok_stride) {
+                                                float* __restrict__ logits) {
   extern __shared__ float smem[];
   float* xs = smem;
-  float* red = smem + MR * D;
   __shared__ float bv[4][MR];
   __shared__ int bi[4][MR];
-  __shared__ int is_last;
   const int wave = wave_id(), lane = lane_id();
   const int nblk = gridDim.x;
-  for (int m0 = 0; m0 < M; m0 += MR) {
-    const int m_act = min(MR, M - m0);
-    // gather + normalise the activation rows of this group
-    for (int m = 0; m < m_act; ++m) {
-      const int om = m0 + m;
-      const int src = last_valid ? om * Q + cnt[om] - 1 : om;
-      norm_rows_to_lds<D>(x + (long)src * D, D, 1, gain, eps, xs + m * D, red);
-    }
-    __syncthreads();
-    float best[MR];
-    int besti[MR];
+  const int m0 = blockIdx.y * MR;
+  const int m_act = min(MR, M - m0);
+  const int vbase = blockIdx.x * LM_ROWS_PER_BLOCK + wave * 4;
+  WaveGemv<T, D, 4, MR> g[2];
+  {
+    const T* rows[4];
 #pragma unroll
-    for (int m = 0; m < MR; ++m) { best[m] = -INFINITY; besti[m] = 0x7fffffff; }
-#pragma unroll 1
-    for (int t = 0; t < 4; ++t) {
-      const int v0 = blockIdx.x * LM_ROWS_PER_BLOCK + wave * 16 + t * 4;
+    for (int r = 0; r < 4; ++r) rows[r] = W + (long)min(vbase + r, V - 1) * D;
+    g[0].load(rows);
+  }
+  norm_rows_wave<D>(x, D, LmSrcRow{cnt, Q, last_valid, m0}, m_act, gain, eps, xs, 4);
+  __syncthreads();
+  float best[MR];
+  int besti[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) { best[m] = -INFINITY; besti[m] = 0x7fffffff; }
+#pragma unroll
+  for (int t = 0; t < LM_TILES; ++t) {
+    if (t + 1 < LM_TILES) {
       const T* rows[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) rows[r] = W + (long)min(v0 + r, V - 1) * D;
-      WaveGemv<T, D, 4, MR> g;
-      g.load(rows);
-      float acc[4][MR];
-      g.fma(xs, m_act, acc);
-      wave_reduce_acc<4, MR>(acc, m_act);
+      for (int r = 0; r < 4; ++r) rows[r] = W + (long)min(vbase + (t + 1) * 16 + r, V - 1) * D;
+      g[(t + 1) & 1].load(rows);
+    }
+    float acc[4][MR];
+    g[t & 1].fma(xs, m_act, acc);
+    wave_reduce_acc<4, MR>(acc, m_act);
+    const int v0 = vbase + t * 16;
 #pragma unroll
-      for (int m = 0; m < MR; ++m) {
-        if (m < m_act) {
+    for (int m = 0; m < MR; ++m) {
+      if (m < m_act) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int v = v0 + r;
-            if (v < V) {
-              const float val = acc[r][m];
-              if (val > best[m]) { best[m] = val; besti[m] = v; }  // v increases: ties keep the lower id
-              if (logits != nullptr && lane == r) logits[(long)(m0 + m) * V + v] = val;
-            }
+        for (int r = 0; r < 4; ++r) {
+          const int v = v0 + r;
+          if (v < V) {
+            const float val = acc[r][m];
+            if (val > best[m]) { best[m] = val; besti[m] = v; }  // v increases: ties keep the lower id
+            if (logits != nullptr && lane == r) logits[(long)(m0 + m) * V + v] = val;
           }
         }
       }
     }
-    if (lane == 0) {
-#pragma unroll
-      for (int m = 0; m < MR; ++m) { bv[wave][m] = best[m]; bi[wave][m] = besti[m]; }
-    }
-    __syncthreads();
-    if (threadIdx.x < m_act) {
-      const int m = threadIdx.x;
-      float v = bv[0][m];
-      int id = bi[0][m];
-      for (int w = 1; w < 4; ++w) {
-        if (bv[w][m] > v || (bv[w][m] == v && bi[w][m] < id)) { v = bv[w][m]; id = bi[w][m]; }
-      }
-      part_val[(long)(m0 + m) * nblk + blockIdx.x] = v;
-      part_idx[(long)(m0 + m) * nblk + blockIdx.x] = id;
-    }
-    __syncthreads();
   }
-  // stage 2: the last block reduces the per-block bests
-  __threadfence();
-  if (threadIdx.x == 0) is_last = (atomicAdd(counter, 1) == nblk - 1);
+  if (lane == 0) {
+#pragma unroll
+    for (int m = 0; m < MR; ++m) { bv[wave][m] = best[m]; bi[wave][m] = besti[m]; }
+  }
   __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-  for (int m = wave; m < M; m += 4) {
-    float v = -INFINITY;
-    int id = 0x7fffffff;
-    for (int b = lane; b < nblk; b += 64) {
-      const float pv = __builtin_nontemporal_load(part_val + (long)m * nblk + b);
-      const int pi = __builtin_nontemporal_load(part_idx + (long)m * nblk + b);
-      if (pv > v || (pv == v && pi < id)) { v = pv; id = pi; }
+  if (threadIdx.x < m_act) {
+    const int m = threadIdx.x;
+    float v = bv[0][m];
+    int id = bi[0][m];
+    for (int w = 1; w < 4; ++w) {
+      if (bv[w][m] > v || (bv[w][m] == v && bi[w][m] < id)) { v = bv[w][m]; id = bi[w][m]; }
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(v, off, 64);
-      const int oi = __shfl_xor(id, off, 64);
-      if (ov > v || (ov == v && oi < id)) { v = ov; id = oi; }
-    }
-    if (lane == 0) tok[(long)m * tok_stride] = id;
+    part_val[(long)(m0 + m) * nblk + blockIdx.x] = v;
+    part_idx[(long)(m0 + m) * nblk + blockIdx.x] = id;
   }
-  if (threadIdx.x == 0) *counter = 0;
+}
+
+// Stage 2: one block per output row reduces the per-block bests.
+__global__ __launch_bounds__(256) void k_argmax_final(const float* __restrict__ part_val,
+                                                      const int* __restrict__ part_idx, int nblk,
+                                                      int* __restrict__ tok, int tok_stride) {
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  const int m = blockIdx.x;
+  const int wave = wave_id(), lane = lane_id();
+  float v = -INFINITY;
+  int id = 0x7fffffff;
+  for (int b = threadIdx.x; b < nblk; b += 256) {
+    const float pv = part_val[(long)m * nblk + b];
+    const int pi = part_idx[(long)m * nblk + b];
+    if (pv > v || (pv == v && pi < id)) { v = pv; id = pi; }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float ov = __shfl_xor(v, off, 64);
+    const int oi = __shfl_xor(id, off, 64);
+    if (ov > v || (ov == v && oi < id)) { v = ov; id = oi; }
+  }
+  if (lane == 0) { sv[wave] = v; si[wave] = id; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    v = sv[0];
+    id = si[0];
+    for (int w = 1; w < 4; ++w)
+      if (sv[w] > v || (sv[w] == v && si[w] < id)) { v = sv[w]; id = si[w]; }
+    tok[(long)m * tok_stride] = id;
+  }
 }
 
 int lmhead_blocks(int V) { return (V + LM_ROWS_PER_BLOCK - 1) / LM_ROWS_PER_BLOCK; }
 
 template <typename T>
 void launch_lmhead(hipStream_t s, const float* x, const int* cnt, int Q, bool last_valid, const float* gain,
-                   float eps, const T* W, int V, int M, float* part_val, int* part_idx, int* counter,
-                   float* logits, int* tok, int tok_stride) {
+                   float eps, const T* W, int V, int M, float* part_val, int* part_idx, float* logits, int* tok,
+                   int tok_stride) {
   const int nb = lmhead_blocks(V);
   const dim3 blk(256);
-#define OCR_LM_CASE(MRV)                                                                                    \
-  hipLaunchKernelGGL((k_lmhead<T, MRV>), dim3(nb), blk, ((size_t)MRV * D + 4) * 4, s, x, cnt, Q,             \
-                     (int)last_valid, gain, eps, W, V, M, part_val, part_idx, counter, logits, tok, tok_stride);
+#define OCR_LM_CASE(MRV)                                                                                       \
+  hipLaunchKernelGGL((k_lmhead<T, MRV>), dim3(nb, (M + MRV - 1) / MRV), blk, (size_t)MRV * D * 4, s, x, cnt, Q, \
+                     (int)last_valid, gain, eps, W, V, M, part_val, part_idx, logits);
   if (M <= 1) OCR_LM_CASE(1)
   else if (M <= 2) OCR_LM_CASE(2)
   else if (M <= 4) OCR_LM_CASE(4)
   else OCR_LM_CASE(MRG)
 #undef OCR_LM_CASE
+  hipLaunchKernelGGL(k_argmax_final, dim3(M), blk, 0, s, part_val, part_idx, nb, tok, tok_stride);
 }
 
 #define OCR_INST_DENSE(T)                                                                                       \
   template void launch_qkv_rope<T>(hipStream_t, const float*, const float*, float, const T*, int, RowPlan,     \
-                                   float*, T*, int, float);                                                    \
+                                   float*, T*, int, const float2*);                                            \
   template void launch_gemv<T>(hipStream_t, int, Epi, const float*, long, const float*, float, const T*,       \
                                const T*, int, int, float*, long);                                              \
   template void launch_lmhead<T>(hipStream_t, const float*, const int*, int, bool, const float*, float,        \
-                                 const T*, int, int, float*, int*, int*, float*, int*, int);
+                                 const T*, int, int, float*, int*, float*, int*, int);
 OCR_INST_DENSE(float)
 OCR_INST_DENSE(bf16)
 

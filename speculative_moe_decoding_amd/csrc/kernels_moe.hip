@@ -10,92 +10,51 @@
 
 namespace ocr {
 
-// One block per row.  The last block to finish also sorts all pairs.
-template <typename T>
-__global__ __launch_bounds__(256) void k_router(const float* __restrict__ x, const float* __restrict__ gain,
-                                                float eps, const T* __restrict__ wr, int M, MoeBufs mb,
-                                                int* __restrict__ tap) {
-  __shared__ float xs[D];
-  __shared__ float red[4];
-  __shared__ float lg[NE];
-  __shared__ int is_last;
-  const int row = blockIdx.x;
-  const int wave = wave_id(), lane = lane_id(), tid = threadIdx.x;
-  norm_rows_to_lds<D>(x + (long)row * D, D, 1, gain, eps, xs, red);
-  __syncthreads();
-  for (int k = tid; k < D; k += 256) mb.bnorm[(long)row * D + k] = xs[k];
-  // 64 logits: wave w computes experts 16w .. 16w+15, 4 rows at a time
-#pragma unroll 1
-  for (int t = 0; t < 4; ++t) {
-    const int e0 = wave * 16 + t * 4;
-    const T* rows[4];
+// Top-6 of the 64 logits of one row held one per lane (lane = expert id), ties
+// to the lower id; writes the 8 routing slots of the row.  One wavefront.
+__device__ __forceinline__ void top6_row(float v, int row, const MoeBufs& mb, int* tap, int* pe) {
+  const int lane = lane_id();
+  bool taken = false;
+  int sel[TOPK];
+  float selv[TOPK];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) rows[r] = wr + (long)(e0 + r) * D;
-    WaveGemv<T, D, 4, 1> g;
-    g.load(rows);
-    float acc[4][1];
-    g.fma(xs, 1, acc);
-    wave_reduce_acc<4, 1>(acc, 1);
-    if (lane < 4) lg[e0 + lane] = (lane == 0) ? acc[0][0] : (lane == 1) ? acc[1][0] : (lane == 2) ? acc[2][0] : acc[3][0];
-  }
-  __syncthreads();
-  if (wave == 0) {
-    const float v = lg[lane];
-    // top-6 by logit (the softmax is increasing), ties to the lower expert id
-    bool taken = false;
-    int sel[TOPK];
-    float selv[TOPK];
+  for (int j = 0; j < TOPK; ++j) {
+    float bv = taken ? -INFINITY : v;
+    int bi = taken ? 0x7fffffff : lane;
 #pragma unroll
-    for (int j = 0; j < TOPK; ++j) {
-      float bv = taken ? -INFINITY : v;
-      int bi = taken ? 0x7fffffff : lane;
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(bv, off, 64);
-        const int oi = __shfl_xor(bi, off, 64);
-        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-      }
-      sel[j] = bi;
-      selv[j] = bv;
-      if (lane == bi) taken = true;
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off, 64);
+      const int oi = __shfl_xor(bi, off, 64);
+      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
     }
-    // softmax over all 64 routed experts; max = the top-1 logit
-    const float mx = selv[0];
-    const float ex = expf(v - mx);
-    const float sum = wave_sum(ex);
-    if (lane < TOPK) {
-      float gv = 0.f;
-      int gi = 0;
+    sel[j] = bi;
+    selv[j] = bv;
+    if (lane == bi) taken = true;
+  }
+  // softmax over all 64 routed experts; max = the top-1 logit
+  const float mx = selv[0];
+  const float ex = expf(v - mx);
+  const float sum = wave_sum(ex);
+  if (lane < NSLOT) {
+    float gv = 1.0f;
+    int gi = NE + (lane - TOPK);
 #pragma unroll
-      for (int j = 0; j < TOPK; ++j)
-        if (lane == j) { gi = sel[j]; gv = expf(selv[j] - mx) / sum; }
-      mb.ridx[row * NSLOT + lane] = gi;
-      mb.rgate[row * NSLOT + lane] = gv;
-      if (tap != nullptr) tap[row * NSLOT + lane] = gi;
-    } else if (lane < NSLOT) {
-      mb.ridx[row * NSLOT + lane] = NE + (lane - TOPK);
-      mb.rgate[row * NSLOT + lane] = 1.0f;
-      if (tap != nullptr) tap[row * NSLOT + lane] = NE + (lane - TOPK);
-    }
+    for (int j = 0; j < TOPK; ++j)
+      if (lane == j) { gi = sel[j]; gv = expf(selv[j] - mx) / sum; }
+    mb.ridx[row * NSLOT + lane] = gi;
+    mb.rgate[row * NSLOT + lane] = gv;
+    if (tap != nullptr) tap[row * NSLOT + lane] = gi;
+    if (pe != nullptr) pe[row * NSLOT + lane] = gi;
   }
-  // ---- last block: stable counting sort of the 8M pairs by expert
-  __threadfence();
+}
+
+// Stable counting sort of the P = 8M pairs (expert ids in pe[], LDS) by expert;
+// all threads of the block take part.  cnt / off: LDS [NX + 1].
+__device__ __forceinline__ void sort_pairs(const int* pe, int P, int* cnt, int* off, const MoeBufs& mb) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  for (int e = tid; e <= NX; e += nt) cnt[e] = 0;
   __syncthreads();
-  if (tid == 0) is_last = (atomicAdd(mb.counter, 1) == (int)gridDim.x - 1);
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-  __shared__ int cnt[NX + 1];
-  __shared__ int off[NX + 1];
-  extern __shared__ int pe[];  // expert id of every pair
-  const int P = M * NSLOT;
-  for (int e = tid; e <= NX; e += 256) cnt[e] = 0;
-  __syncthreads();
-  for (int p = tid; p < P; p += 256) {
-    const int e = __builtin_nontemporal_load(mb.ridx + p);
-    pe[p] = e;
-    atomicAdd(&cnt[e], 1);
-  }
+  for (int p = tid; p < P; p += nt) atomicAdd(&cnt[pe[p]], 1);
   __syncthreads();
   if (tid == 0) {
     int acc = 0, na = 0;
@@ -107,11 +66,10 @@ __global__ __launch_bounds__(256) void k_router(const float* __restrict__ x, con
     off[NX] = acc;
     *mb.n_act = na;
     mb.stats[0] += na;
-    *mb.counter = 0;
   }
   __syncthreads();
-  for (int e = tid; e <= NX; e += 256) mb.off[e] = off[e];
-  for (int p = tid; p < P; p += 256) {
+  for (int e = tid; e <= NX; e += nt) mb.off[e] = off[e];
+  for (int p = tid; p < P; p += nt) {
     const int e = pe[p];
     int rank = 0;
     for (int q = 0; q < p; ++q) rank += (pe[q] == e);
@@ -121,13 +79,106 @@ __global__ __launch_bounds__(256) void k_router(const float* __restrict__ x, con
   }
 }
 
+// Small batches (M <= 8): one block of 16 wavefronts does everything.
+// Wavefront w streams router rows 4w..4w+3 (loads issued first), RMSNorms
+// rows w, w+16, ...; then top-6 per row and the sort, all in LDS.
+template <typename T, int MR>
+__global__ __launch_bounds__(1024) void k_router_small(const float* __restrict__ x, const float* __restrict__ gain,
+                                                       float eps, const T* __restrict__ wr, int M, MoeBufs mb,
+                                                       int* __restrict__ tap) {
+  extern __shared__ float xs[];  // [MR][D]
+  __shared__ float lg[MR][NE];
+  __shared__ int pe[MR * NSLOT];
+  __shared__ int cnt[NX + 1], off[NX + 1];
+  const int wave = wave_id(), lane = lane_id();
+  const T* rows[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) rows[r] = wr + (long)(wave * 4 + r) * D;
+  WaveGemv<T, D, 4, MR> g;
+  g.load(rows);
+  norm_rows_wave<D>(x, D, RowIdentity{0}, M, gain, eps, xs, 16);
+  __syncthreads();
+  for (int k = threadIdx.x; k < M * D; k += 1024) mb.bnorm[k] = xs[k];
+  float acc[4][MR];
+  g.fma(xs, M, acc);
+  wave_reduce_acc<4, MR>(acc, M);
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    if (m < M && lane < 4) {
+      const float v = (lane == 0) ? acc[0][m] : (lane == 1) ? acc[1][m] : (lane == 2) ? acc[2][m] : acc[3][m];
+      lg[m][wave * 4 + lane] = v;
+    }
+  }
+  __syncthreads();
+  for (int m = wave; m < M; m += 16) top6_row(lg[m][lane], m, mb, tap, pe);
+  __syncthreads();
+  sort_pairs(pe, M * NSLOT, cnt, off, mb);
+}
+
+// Larger batches: one block per row computes its logits and top-6 ...
+template <typename T>
+__global__ __launch_bounds__(256) void k_router_rows(const float* __restrict__ x, const float* __restrict__ gain,
+                                                     float eps, const T* __restrict__ wr, MoeBufs mb,
+                                                     int* __restrict__ tap) {
+  __shared__ float xs[D];
+  __shared__ float lg[NE];
+  const int row = blockIdx.x;
+  const int wave = wave_id(), lane = lane_id();
+  WaveGemv<T, D, 4, 1> g[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const T* rows[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) rows[r] = wr + (long)(wave * 16 + t * 4 + r) * D;
+    g[t].load(rows);
+  }
+  if (wave == 0) norm_rows_wave<D>(x, D, RowIdentity{row}, 1, gain, eps, xs, 1);
+  __syncthreads();
+  for (int k = threadIdx.x; k < D; k += 256) mb.bnorm[(long)row * D + k] = xs[k];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    float acc[4][1];
+    g[t].fma(xs, 1, acc);
+    wave_reduce_acc<4, 1>(acc, 1);
+    if (lane < 4)
+      lg[wave * 16 + t * 4 + lane] =
+          (lane == 0) ? acc[0][0] : (lane == 1) ? acc[1][0] : (lane == 2) ? acc[2][0] : acc[3][0];
+  }
+  __syncthreads();
+  if (wave == 0) top6_row(lg[lane], row, mb, tap, nullptr);
+}
+
+// ... and one block sorts all pairs.
+__global__ __launch_bounds__(1024) void k_sort_pairs(int M, MoeBufs mb) {
+  extern __shared__ int pe[];
+  __shared__ int cnt[NX + 1], off[NX + 1];
+  const int P = M * NSLOT;
+  for (int p = threadIdx.x; p < P; p += 1024) pe[p] = mb.ridx[p];
+  __syncthreads();
+  sort_pairs(pe, P, cnt, off, mb);
+}
+
 int expert_slot_cap(int M) { return min(NE, TOPK * M) + NSH; }
 
 template <typename T>
 void launch_router(hipStream_t s, const float* x, const float* gain, float eps, const T* wr, int M,
                    const MoeBufs& mb, int* tap) {
-  const size_t lds = (size_t)M * NSLOT * sizeof(int);
-  hipLaunchKernelGGL((k_router<T>), dim3(M), dim3(256), lds, s, x, gain, eps, wr, M, mb, tap);
+#define OCR_ROUTER_CASE(MRV)                                                                                  \
+  {                                                                                                           \
+    static const bool lds_ok = (allow_lds(k_router_small<T, MRV>, (size_t)MRV * D * 4), true);                \
+    (void)lds_ok;                                                                                             \
+    hipLaunchKernelGGL((k_router_small<T, MRV>), dim3(1), dim3(1024), (size_t)MRV * D * 4, s, x, gain, eps, wr, \
+                       M, mb, tap);                                                                           \
+  }
+  if (M <= 1) OCR_ROUTER_CASE(1)
+  else if (M <= 2) OCR_ROUTER_CASE(2)
+  else if (M <= 4) OCR_ROUTER_CASE(4)
+  else if (M <= 8) OCR_ROUTER_CASE(8)
+  else {
+    hipLaunchKernelGGL((k_router_rows<T>), dim3(M), dim3(256), 0, s, x, gain, eps, wr, mb, tap);
+    hipLaunchKernelGGL(k_sort_pairs, dim3(1), dim3(1024), (size_t)M * NSLOT * sizeof(int), s, M, mb);
+  }
+#undef OCR_ROUTER_CASE
 }
 
 // Gate/up: block (tile, expert slot); wavefront w computes units j, j+1 of the

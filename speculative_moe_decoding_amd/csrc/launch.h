@@ -13,7 +13,9 @@ enum Epi { EPI_STORE = 0, EPI_ADD = 1, EPI_SWIGLU = 2 };
 // kv[slot][0|1][head][pos][HD] (slot stride = 2*NH*max_pos*HD elements).
 template <typename T>
 void launch_qkv_rope(hipStream_t s, const float* x, const float* gain, float eps, const T* wqkv, int M,
-                     RowPlan plan, float* q, T* kv, int max_pos, float theta);
+                     RowPlan plan, float* q, T* kv, int max_pos, const float2* rope);
+// tab[pos][i] = (cos, sin)(pos * theta^(-2i/128)), i < 64, for pos < max_pos.
+void launch_rope_table(hipStream_t s, int max_pos, float theta, float2* tab);
 
 // out[m][n] (op)= sum_k W[n][k] * a[m][k] for n < N; a optionally RMSNorm'ed
 // (gain != null).  EPI_SWIGLU: out[m][j] = silu(W0[j].a) * (W1[j].a), j < N.
@@ -21,14 +23,14 @@ template <typename T>
 void launch_gemv(hipStream_t s, int K, Epi epi, const float* a, long lda, const float* gain, float eps,
                  const T* W0, const T* W1, int N, int M, float* out, long ldo);
 
-// LM head fused with argmax.  Row m of the output reads activation row
-// (last_valid ? plan.base-independent m*Q + cnt[m]-1 : m) of x, RMSNorms it
-// with gain, forms the vocab logits (optionally stored to logits[m][V]) and
-// writes argmax (lowest id on ties) to tok[m * tok_stride].
+// LM head fused with argmax (two launches: per-block bests, then the final
+// reduction).  Output row m reads activation row (last_valid ? m*Q + cnt[m]-1
+// : m) of x, RMSNorms it with gain, forms the vocab logits (optionally stored to
+// logits[m][V]) and writes the argmax (lowest id on ties) to tok[m * tok_stride].
 template <typename T>
 void launch_lmhead(hipStream_t s, const float* x, const int* cnt, int Q, bool last_valid, const float* gain,
-                   float eps, const T* W, int V, int M, float* part_val, int* part_idx, int* counter,
-                   float* logits, int* tok, int tok_stride);
+                   float eps, const T* W, int V, int M, float* part_val, int* part_idx, float* logits, int* tok,
+                   int tok_stride);
 int lmhead_blocks(int V);
 
 template <typename T>
@@ -44,7 +46,6 @@ struct MoeBufs {
   int* off;       // [NX + 1]
   int* act;       // [NX] active experts in increasing id
   int* n_act;     // [1]
-  int* counter;   // [1] zero between launches
   long long* stats;  // [0] += active experts per layer
   float* hx;      // [8M][DI]
   float* y;       // [8M][D]

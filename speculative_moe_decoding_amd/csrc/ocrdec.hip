@@ -29,7 +29,7 @@ struct Plan {
   int Qmax, M_max, cu_stride, tiles_per_chunk, chunk_keys, n_chunks_cap, lm_nblk;
   size_t esz, kv_layer_elems;
   // state
-  size_t s_kv, s_dkv, s_ints, s_cu, s_hbuf, s_total;
+  size_t s_kv, s_dkv, s_ints, s_cu, s_hbuf, s_rope, s_total;
   // workspace
   size_t w_x, w_q, w_attn, w_part, w_bnorm, w_ridx, w_rgate, w_perm, w_inv, w_off, w_act, w_misc, w_stats, w_hx,
       w_y, w_cat, w_u, w_dffn, w_esave, w_hsave, w_lmv, w_lmi, w_plan, w_total;
@@ -70,6 +70,7 @@ Plan make_plan(const ocrdec_config* c) {
   p.s_ints = take((size_t)7 * c->max_batch * 4);
   p.s_cu = take((size_t)c->max_batch * p.cu_stride * 4);
   p.s_hbuf = take((size_t)c->max_batch * p.cu_stride * D * 4);
+  p.s_rope = take((size_t)c->max_positions * (HD / 2) * 8);
   p.s_total = o;
   o = 0;
   const size_t M = p.M_max;
@@ -84,7 +85,7 @@ Plan make_plan(const ocrdec_config* c) {
   p.w_inv = take(M * NSLOT * 4);
   p.w_off = take((NX + 1) * 4);
   p.w_act = take(NX * 4);
-  p.w_misc = take(64 * 4);       // [0] n_act, [1] router counter, [2] lm counter, [16..] prefill tokens
+  p.w_misc = take(64 * 4);       // [0] n_act, [16..] prefill tokens
   p.w_stats = take(8 * 8);
   p.w_hx = take(M * NSLOT * DI * 4);
   p.w_y = take(M * NSLOT * D * 4);
@@ -110,8 +111,9 @@ struct ocrdec_model {
   char* ws;
   StateView sv;
   float *x, *q, *attn, *part, *cat, *u, *dffn, *esave, *hsave[2], *lm_val;
-  int *lm_idx, *plan_base, *plan_cnt, *plan_slot, *lm_counter, *tok_tmp;
+  int *lm_idx, *plan_base, *plan_cnt, *plan_slot, *tok_tmp;
   MoeBufs mb;
+  const float2* rope;
   // Host-side upper bound on (last position + 1) of every slot: set by prefill,
   // raised by K + 1 per accept.  It sizes the attention grids and the capacity
   // checks; the device clamps positions to the cache in any case.
@@ -122,6 +124,7 @@ struct ocrdec_model {
   std::vector<hipEvent_t> ev;  // triplets: before gate/up, between, after down
   size_t ev_used;
   long long stats_base;        // device expert counter when timing was enabled
+  int last_verify_rows;        // M of the last verify call (0 before any)
 };
 
 namespace {
@@ -172,7 +175,7 @@ void verifier_layers(ocrdec_model* m, hipStream_t s, int M, int B, RowPlan plan,
   for (int l = 0; l < c.n_layers; ++l) {
     T* kvl = static_cast<T*>((void*)(m->state + m->p.s_kv)) + (size_t)l * m->p.kv_layer_elems;
     launch_qkv_rope<T>(s, m->x, wvec(m, lw(m, l, L_ANORM)), c.norm_eps, wmat<T>(m, lw(m, l, L_QKV)), M, plan, m->q,
-                       kvl, c.max_positions, c.rope_theta);
+                       kvl, c.max_positions, m->rope);
     launch_attention<T>(s, m->q, kvl, c.max_positions, plan, B, nch, m->p.tiles_per_chunk, m->part, m->attn);
     launch_gemv<T>(s, QD, EPI_ADD, m->attn, QD, nullptr, c.norm_eps, wmat<T>(m, lw(m, l, L_WO)), nullptr, D, M,
                    m->x, D);
@@ -194,7 +197,7 @@ void draft_layer(ocrdec_model* m, hipStream_t s, int M, int B, RowPlan plan, int
   launch_gemv<T>(s, 2 * D, EPI_STORE, m->cat, 2 * D, nullptr, c.norm_eps, wmat<T>(m, dw(m, D_FUSE)), nullptr, D, M,
                  m->u, D);
   launch_qkv_rope<T>(s, m->u, wvec(m, dw(m, D_ANORM)), c.norm_eps, wmat<T>(m, dw(m, D_QKV)), M, plan, m->q, dkv,
-                     c.max_positions, c.rope_theta);
+                     c.max_positions, m->rope);
   launch_attention<T>(s, m->q, dkv, c.max_positions, plan, B, nch, m->p.tiles_per_chunk, m->part, m->attn);
   launch_gemv<T>(s, QD, EPI_ADD, m->attn, QD, nullptr, c.norm_eps, wmat<T>(m, dw(m, D_WO)), nullptr, D, M, m->u, D);
   launch_gemv<T>(s, D, EPI_SWIGLU, m->u, D, wvec(m, dw(m, D_FNORM)), c.norm_eps, wmat<T>(m, dw(m, D_GATE)),
@@ -225,7 +228,7 @@ int do_prefill(ocrdec_model* m, hipStream_t s, int B, const int32_t* slots_host,
       verifier_layers<T>(m, s, cc, 1, plan, nch, false);
       if (p0 + cc == P)
         launch_lmhead<T>(s, m->x, m->plan_cnt, cc, true, wvec(m, W_FNORM), c.norm_eps, wmat<T>(m, W_LM), c.vocab, 1,
-                         m->lm_val, m->lm_idx, m->lm_counter, nullptr, m->tok_tmp, 1);
+                         m->lm_val, m->lm_idx, nullptr, m->tok_tmp, 1);
       launch_draft_prefill_cat(s, cc, m->x, m->esave, m->hsave[par], m->hsave[1 - par], wvec(m, dw(m, D_NH)),
                                wvec(m, dw(m, D_NE)), c.norm_eps, m->cat);
       draft_layer<T>(m, s, cc, 1, plan, nch);
@@ -251,7 +254,7 @@ int do_draft(ocrdec_model* m, hipStream_t s, int B, const int32_t* slots, int K,
   RowPlan plan{m->plan_base, m->plan_cnt, m->plan_slot, Q};
   draft_layer<T>(m, s, B * Q, B, plan, nch);
   launch_lmhead<T>(s, m->u, m->plan_cnt, Q, true, wvec(m, dw(m, D_ONORM)), c.norm_eps, wmat<T>(m, W_LM), c.vocab, B,
-                   m->lm_val, m->lm_idx, m->lm_counter, nullptr, draft_out, K);
+                   m->lm_val, m->lm_idx, nullptr, draft_out, K);
   for (int j = 2; j <= K; ++j) {
     const int Qprev = (j == 2) ? Q : 1;
     launch_plan_draft_step<T>(s, B, j, Qprev, K, m->sv, draft_out, wmat<T>(m, W_EMBED), c.vocab,
@@ -260,7 +263,7 @@ int do_draft(ocrdec_model* m, hipStream_t s, int B, const int32_t* slots, int K,
     RowPlan p1{m->plan_base, m->plan_cnt, m->plan_slot, 1};
     draft_layer<T>(m, s, B, B, p1, nch);
     launch_lmhead<T>(s, m->u, m->plan_cnt, 1, true, wvec(m, dw(m, D_ONORM)), c.norm_eps, wmat<T>(m, W_LM), c.vocab,
-                     B, m->lm_val, m->lm_idx, m->lm_counter, nullptr, draft_out + (j - 1), K);
+                     B, m->lm_val, m->lm_idx, nullptr, draft_out + (j - 1), K);
   }
   return hip_check("ocrdec_draft");
 }
@@ -275,8 +278,9 @@ int do_verify(ocrdec_model* m, hipStream_t s, int B, const int32_t* slots, int K
                         m->plan_slot, m->x);
   RowPlan plan{m->plan_base, m->plan_cnt, m->plan_slot, Q};
   verifier_layers<T>(m, s, M, B, plan, nch, true);
+  m->last_verify_rows = M;
   launch_lmhead<T>(s, m->x, m->plan_cnt, Q, false, wvec(m, W_FNORM), c.norm_eps, wmat<T>(m, W_LM), c.vocab, M,
-                   m->lm_val, m->lm_idx, m->lm_counter, logits_out, greedy_out, 1);
+                   m->lm_val, m->lm_idx, logits_out, greedy_out, 1);
   if (m->tap_hidden) launch_copy_rows(s, m->x, m->tap_hidden, (long)M * D);
   return hip_check("ocrdec_verify");
 }
@@ -349,6 +353,7 @@ int ocrdec_create(const ocrdec_config* cfg, const void* const* weight_ptrs, int 
   m->sv.cu_stride = p.cu_stride;
   m->sv.hbuf = reinterpret_cast<float*>(m->state + p.s_hbuf);
   m->sv.n_slots = mb;
+  m->rope = reinterpret_cast<const float2*>(m->state + p.s_rope);
   auto wf = [&](size_t off) { return reinterpret_cast<float*>(m->ws + off); };
   auto wi = [&](size_t off) { return reinterpret_cast<int*>(m->ws + off); };
   m->x = wf(p.w_x);
@@ -369,8 +374,6 @@ int ocrdec_create(const ocrdec_config* cfg, const void* const* weight_ptrs, int 
   m->plan_slot = wi(p.w_plan) + 2 * pm;
   int* misc = wi(p.w_misc);
   m->mb.n_act = misc;
-  m->mb.counter = misc + 1;
-  m->lm_counter = misc + 2;
   m->tok_tmp = misc + 16;
   m->mb.bnorm = wf(p.w_bnorm);
   m->mb.ridx = wi(p.w_ridx);
@@ -388,9 +391,15 @@ int ocrdec_create(const ocrdec_config* cfg, const void* const* weight_ptrs, int 
   m->timing = false;
   m->ev_used = 0;
   m->stats_base = 0;
+  m->last_verify_rows = 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (hipMemsetAsync(misc, 0, 64 * 4, s) != hipSuccess || hipMemsetAsync(m->mb.stats, 0, 64, s) != hipSuccess ||
       hipMemsetAsync(m->state + p.s_ints, 0, p.s_hbuf - p.s_ints, s) != hipSuccess) {
+    delete m;
+    return fail(OCRDEC_EHIP, "hipMemsetAsync of the workspace counters failed");
+  }
+  launch_rope_table(s, cfg->max_positions, cfg->rope_theta, reinterpret_cast<float2*>(m->state + p.s_rope));
+  if (hipGetLastError() != hipSuccess) {
     delete m;
     return fail(OCRDEC_EHIP, "hipMemsetAsync of the workspace counters failed");
   }
@@ -479,6 +488,29 @@ int ocrdec_controlled_drafts(ocrdec_model* m, void* stream, int B, const int32_t
   hipStream_t s = static_cast<hipStream_t>(stream);
   launch_controlled(s, B, K, slots, m->sv, trace, trace_stride, trace_len, seed, threshold, m->cfg.vocab, draft_inout);
   return hip_check("ocrdec_controlled_drafts");
+}
+
+int ocrdec_replay_expert_gate_up(ocrdec_model* m, void* stream, int n_rounds, int* expert_sets_per_launch) {
+  if (!m || n_rounds < 0) return fail(OCRDEC_EINVAL, "bad replay arguments");
+  if (m->last_verify_rows < 1) return fail(OCRDEC_EINVAL, "no verify call to replay");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (expert_sets_per_launch) {
+    int na = 0;
+    if (hipStreamSynchronize(s) != hipSuccess ||
+        hipMemcpy(&na, m->mb.n_act, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess)
+      return fail(OCRDEC_EHIP, "reading the active-expert count failed");
+    *expert_sets_per_launch = na;
+  }
+  const int M = m->last_verify_rows;
+  for (int r = 0; r < n_rounds; ++r) {
+    for (int l = 0; l < m->cfg.n_layers; ++l) {
+      if (m->cfg.dtype == OCRDEC_BF16)
+        launch_expert_gate_up<bf16>(s, wmat<bf16>(m, lw(m, l, L_GATE)), wmat<bf16>(m, lw(m, l, L_UP)), M, m->mb);
+      else
+        launch_expert_gate_up<float>(s, wmat<float>(m, lw(m, l, L_GATE)), wmat<float>(m, lw(m, l, L_UP)), M, m->mb);
+    }
+  }
+  return hip_check("ocrdec_replay_expert_gate_up");
 }
 
 int ocrdec_set_taps(ocrdec_model* m, int32_t* route_idx, float* hidden) {

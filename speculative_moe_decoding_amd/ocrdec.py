@@ -21,7 +21,8 @@ OCRDEC_F32, OCRDEC_BF16 = 0, 1
 SYMBOLS = (
     "ocrdec_state_bytes", "ocrdec_workspace_bytes", "ocrdec_num_weights", "ocrdec_create", "ocrdec_destroy",
     "ocrdec_prefill", "ocrdec_draft", "ocrdec_verify", "ocrdec_accept_rollback", "ocrdec_controlled_drafts",
-    "ocrdec_set_taps", "ocrdec_expert_timing", "ocrdec_expert_stats", "ocrdec_last_error",
+    "ocrdec_set_taps", "ocrdec_expert_timing", "ocrdec_expert_stats", "ocrdec_replay_expert_gate_up",
+    "ocrdec_last_error",
 )
 
 
@@ -67,6 +68,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "ocrdec_expert_stats": (I, [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_longlong),
                                     ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_longlong),
                                     ctypes.POINTER(ctypes.c_longlong)]),
+        "ocrdec_replay_expert_gate_up": (I, [P, P, I, ctypes.POINTER(I)]),
         "ocrdec_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -162,6 +164,13 @@ def ocrdec_expert_stats(h):
                                                                      ctypes.byref(b), ctypes.byref(nb),
                                                                      ctypes.byref(sets)))
     return dict(ms_gate_up=a.value, n_gate_up=na.value, ms_down=b.value, n_down=nb.value, expert_sets=sets.value)
+
+
+def ocrdec_replay_expert_gate_up(h, stream, n_rounds: int, want_count: bool = False):
+    na = ctypes.c_int()
+    _check("ocrdec_replay_expert_gate_up", load_library().ocrdec_replay_expert_gate_up(
+        h, stream, n_rounds, ctypes.byref(na) if want_count else None))
+    return na.value if want_count else None
 
 
 class Decoder:
