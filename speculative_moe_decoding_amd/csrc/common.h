@@ -80,6 +80,14 @@ __device__ __forceinline__ float wave_max(float v) {
 
 __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// Streaming (non-temporal) 16-byte load of weights that are read once per
+// launch: keeps them from displacing the activations and KV tiles in the caches.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ldg16_stream(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Sum over a 256-thread block in the fixed order described above.  `red` is
 // LDS scratch of at least 4 floats; contains a barrier.
 __device__ __forceinline__ float block_sum256(float v, float* red) {
@@ -185,7 +193,7 @@ struct WaveGemv {
       const int c = lane + 64 * t;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        if (c < NCH) w[r][t] = ldg16(rows[r] + (long)c * CE);
+        if (c < NCH) w[r][t] = ldg16_stream(rows[r] + (long)c * CE);
       }
     }
   }

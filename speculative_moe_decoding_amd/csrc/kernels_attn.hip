@@ -20,10 +20,11 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_attn_partial(const float* __restrict__ q, const T* __restrict__ kv,
                                                       int max_pos, RowPlan plan, int n_chunks,
                                                       int tiles_per_chunk, float* __restrict__ part) {
-  __shared__ float Kt[HD][ATT_TILE + 1];
-  __shared__ float Vs[ATT_TILE][HD];
-  __shared__ float qs[QMAX_ATT][HD];
-  __shared__ float ps[4][ATT_TILE];
+  // keys transposed in groups of 4 dims: Kq[d/4][t] = (k_t[d..d+3]); values row-major
+  __shared__ float4 Kq[HD / 4][ATT_TILE];
+  __shared__ float2 Vs[ATT_TILE][HD / 2];
+  __shared__ float4 qs[QMAX_ATT][HD / 4];
+  __shared__ float4 ps[4][ATT_TILE / 4];
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int wave = wave_id(), lane = lane_id(), tid = threadIdx.x;
   const int Q = plan.Q;
@@ -37,34 +38,57 @@ __global__ __launch_bounds__(256) void k_attn_partial(const float* __restrict__ 
   const long slot = plan.slot[b];
   const T* Kc = kv + slot * (2L * NH * max_pos * HD) + (long)h * max_pos * HD;
   const T* Vc = Kc + (long)NH * max_pos * HD;
-  // queries of this sequence / head
-  for (int e = tid; e < cnt * HD; e += 256) {
-    const int i = e / HD, d = e % HD;
-    qs[i][d] = q[(long)(b * Q + i) * QD + h * HD + d];
+  constexpr int CE = WT<T>::CE;
+  constexpr int CPR = HD / CE;                         // 16-byte chunks per key row
+  constexpr int NLD = ATT_TILE * CPR / 256;            // chunks per thread per tile
+  // queries of this sequence / head (all loads first)
+  {
+    float4 qv[QMAX_ATT * HD / 4 / 256];
+#pragma unroll
+    for (int j = 0; j < QMAX_ATT * HD / 4 / 256; ++j) {
+      const int e = tid + 256 * j, i = e / (HD / 4), d4 = e % (HD / 4);
+      qv[j] = (i < cnt) ? reinterpret_cast<const float4*>(q + (long)(b * Q + i) * QD + h * HD)[d4]
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int j = 0; j < QMAX_ATT * HD / 4 / 256; ++j) {
+      const int e = tid + 256 * j;
+      qs[e / (HD / 4)][e % (HD / 4)] = qv[j];
+    }
   }
   const float scale = 0.08838834764831845f;  // 1 / sqrt(128)
-  // per-wave query state: queries wave, wave + 4
   float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
   float o0[2] = {0.f, 0.f}, o1[2] = {0.f, 0.f};
-  constexpr int CE = WT<T>::CE;
   for (int tt = 0; tt < tiles_per_chunk; ++tt) {
     const int kt = k0 + tt * ATT_TILE;
     if (kt > p_last) break;
     const int nk = min(ATT_TILE, p_last + 1 - kt);
-    __syncthreads();
-    // stage K (transposed) and V of this tile, fp32
-    for (int e = tid; e < ATT_TILE * HD / CE; e += 256) {
-      const int t = e / (HD / CE), d0 = (e % (HD / CE)) * CE;
-      float kf[CE], vf[CE];
+    // issue every K / V load of the tile, then stage (fp32) in LDS
+    uint4 kr[NLD], vr[NLD];
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      const int e = tid + 256 * j, t = e / CPR, d0 = (e % CPR) * CE;
       if (t < nk) {
-        WT<T>::cvt(ldg16(Kc + (long)(kt + t) * HD + d0), kf);
-        WT<T>::cvt(ldg16(Vc + (long)(kt + t) * HD + d0), vf);
+        kr[j] = ldg16(Kc + (long)(kt + t) * HD + d0);
+        vr[j] = ldg16(Vc + (long)(kt + t) * HD + d0);
       } else {
-#pragma unroll
-        for (int j = 0; j < CE; ++j) { kf[j] = 0.f; vf[j] = 0.f; }
+        kr[j] = make_uint4(0, 0, 0, 0);
+        vr[j] = make_uint4(0, 0, 0, 0);
       }
+    }
+    __syncthreads();  // the previous tile's LDS reads are done
 #pragma unroll
-      for (int j = 0; j < CE; ++j) { Kt[d0 + j][t] = kf[j]; Vs[t][d0 + j] = vf[j]; }
+    for (int j = 0; j < NLD; ++j) {
+      const int e = tid + 256 * j, t = e / CPR, d0 = (e % CPR) * CE;
+      float kf[CE], vf[CE];
+      WT<T>::cvt(kr[j], kf);
+      WT<T>::cvt(vr[j], vf);
+#pragma unroll
+      for (int g = 0; g < CE / 4; ++g) {
+        Kq[d0 / 4 + g][t] = make_float4(kf[4 * g], kf[4 * g + 1], kf[4 * g + 2], kf[4 * g + 3]);
+        Vs[t][d0 / 2 + 2 * g] = make_float2(vf[4 * g], vf[4 * g + 1]);
+        Vs[t][d0 / 2 + 2 * g + 1] = make_float2(vf[4 * g + 2], vf[4 * g + 3]);
+      }
     }
     __syncthreads();
 #pragma unroll
@@ -73,10 +97,17 @@ __global__ __launch_bounds__(256) void k_attn_partial(const float* __restrict__ 
       if (i >= cnt) continue;
       const int plim = base + i;  // last visible key of query i
       if (kt > plim) continue;
-      // lane = key t of the tile
+      // lane = key t of the tile: s = q . k over 128 dims, 4 at a time, in order
       float sc = 0.f;
 #pragma unroll 8
-      for (int d = 0; d < HD; ++d) sc = fmaf(qs[i][d], Kt[d][lane], sc);
+      for (int d4 = 0; d4 < HD / 4; ++d4) {
+        const float4 qv = qs[i][d4];
+        const float4 kv4 = Kq[d4][lane];
+        sc = fmaf(qv.x, kv4.x, sc);
+        sc = fmaf(qv.y, kv4.y, sc);
+        sc = fmaf(qv.z, kv4.z, sc);
+        sc = fmaf(qv.w, kv4.w, sc);
+      }
       sc = sc * scale;
       const bool vis = (kt + lane) <= plim;
       const float mt = wave_max(vis ? sc : -INFINITY);
@@ -84,15 +115,20 @@ __global__ __launch_bounds__(256) void k_attn_partial(const float* __restrict__ 
       const float corr = expf(mrun[qq] - mnew);
       const float p = vis ? expf(sc - mnew) : 0.f;
       lrun[qq] = lrun[qq] * corr + wave_sum(p);
-      ps[wave][lane] = p;
+      reinterpret_cast<float*>(ps[wave])[lane] = p;
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
       float a0 = o0[qq] * corr, a1 = o1[qq] * corr;
-#pragma unroll 8
-      for (int t = 0; t < ATT_TILE; ++t) {
-        const float pt = ps[wave][t];
-        a0 = fmaf(pt, Vs[t][2 * lane], a0);
-        a1 = fmaf(pt, Vs[t][2 * lane + 1], a1);
+#pragma unroll 4
+      for (int t4 = 0; t4 < ATT_TILE / 4; ++t4) {
+        const float4 pt = ps[wave][t4];
+        const float pv[4] = {pt.x, pt.y, pt.z, pt.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float2 v2 = Vs[4 * t4 + u][lane];
+          a0 = fmaf(pv[u], v2.x, a0);
+          a1 = fmaf(pv[u], v2.y, a1);
+        }
       }
       o0[qq] = a0;
       o1[qq] = a1;
@@ -105,8 +141,7 @@ __global__ __launch_bounds__(256) void k_attn_partial(const float* __restrict__ 
     const int i = wave + 4 * qq;
     if (i >= cnt || k0 > base + i) continue;
     float* pp = part + ((((long)b * NH + h) * n_chunks + c) * Q + i) * (HD + 2);
-    pp[2 * lane] = o0[qq];
-    pp[2 * lane + 1] = o1[qq];
+    reinterpret_cast<float2*>(pp)[lane] = make_float2(o0[qq], o1[qq]);
     if (lane == 0) { pp[HD] = mrun[qq]; pp[HD + 1] = lrun[qq]; }
   }
 }

@@ -46,6 +46,7 @@ struct MoeBufs {
   int* off;       // [NX + 1]
   int* act;       // [NX] active experts in increasing id
   int* n_act;     // [1]
+  int4* slot_info;  // [NX] (expert, first pair, end pair, n_act); expert -1 past n_act
   long long* stats;  // [0] += active experts per layer
   float* hx;      // [8M][DI]
   float* y;       // [8M][D]

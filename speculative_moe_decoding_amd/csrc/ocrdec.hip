@@ -31,7 +31,7 @@ struct Plan {
   // state
   size_t s_kv, s_dkv, s_ints, s_cu, s_hbuf, s_rope, s_total;
   // workspace
-  size_t w_x, w_q, w_attn, w_part, w_bnorm, w_ridx, w_rgate, w_perm, w_inv, w_off, w_act, w_misc, w_stats, w_hx,
+  size_t w_x, w_q, w_attn, w_part, w_bnorm, w_ridx, w_rgate, w_perm, w_inv, w_off, w_act, w_slot, w_misc, w_stats, w_hx,
       w_y, w_cat, w_u, w_dffn, w_esave, w_hsave, w_lmv, w_lmi, w_plan, w_total;
 };
 
@@ -85,6 +85,7 @@ Plan make_plan(const ocrdec_config* c) {
   p.w_inv = take(M * NSLOT * 4);
   p.w_off = take((NX + 1) * 4);
   p.w_act = take(NX * 4);
+  p.w_slot = take(NX * 16);
   p.w_misc = take(64 * 4);       // [0] n_act, [16..] prefill tokens
   p.w_stats = take(8 * 8);
   p.w_hx = take(M * NSLOT * DI * 4);
@@ -288,6 +289,7 @@ int do_verify(ocrdec_model* m, hipStream_t s, int B, const int32_t* slots, int K
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 int check_call(ocrdec_model* m, int B, int K) {
+  (void)hipGetLastError();  // launch errors are checked after this call's launches
   if (!m) return fail(OCRDEC_EINVAL, "model is null");
   if (B < 1) return fail(OCRDEC_EINVAL, "B must be >= 1");
   if (K < 0) return fail(OCRDEC_EINVAL, "K must be >= 0");
@@ -382,6 +384,7 @@ int ocrdec_create(const ocrdec_config* cfg, const void* const* weight_ptrs, int 
   m->mb.inv = wi(p.w_inv);
   m->mb.off = wi(p.w_off);
   m->mb.act = wi(p.w_act);
+  m->mb.slot_info = reinterpret_cast<int4*>(m->ws + p.w_slot);
   m->mb.stats = reinterpret_cast<long long*>(m->ws + p.w_stats);
   m->mb.hx = wf(p.w_hx);
   m->mb.y = wf(p.w_y);
@@ -393,15 +396,17 @@ int ocrdec_create(const ocrdec_config* cfg, const void* const* weight_ptrs, int 
   m->stats_base = 0;
   m->last_verify_rows = 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (hipMemsetAsync(misc, 0, 64 * 4, s) != hipSuccess || hipMemsetAsync(m->mb.stats, 0, 64, s) != hipSuccess ||
-      hipMemsetAsync(m->state + p.s_ints, 0, p.s_hbuf - p.s_ints, s) != hipSuccess) {
-    delete m;
-    return fail(OCRDEC_EHIP, "hipMemsetAsync of the workspace counters failed");
+  (void)hipGetLastError();  // clear an error left by earlier, unrelated runtime calls
+  hipError_t err = hipMemsetAsync(misc, 0, 64 * 4, s);
+  if (err == hipSuccess) err = hipMemsetAsync(m->mb.stats, 0, 64, s);
+  if (err == hipSuccess) err = hipMemsetAsync(m->state + p.s_ints, 0, p.s_hbuf - p.s_ints, s);
+  if (err == hipSuccess) {
+    launch_rope_table(s, cfg->max_positions, cfg->rope_theta, reinterpret_cast<float2*>(m->state + p.s_rope));
+    err = hipGetLastError();
   }
-  launch_rope_table(s, cfg->max_positions, cfg->rope_theta, reinterpret_cast<float2*>(m->state + p.s_rope));
-  if (hipGetLastError() != hipSuccess) {
+  if (err != hipSuccess) {
     delete m;
-    return fail(OCRDEC_EHIP, "hipMemsetAsync of the workspace counters failed");
+    return fail(OCRDEC_EHIP, std::string("initialising the state / workspace failed: ") + hipGetErrorString(err));
   }
   *out = m;
   return OCRDEC_OK;
