@@ -110,6 +110,7 @@ def main() -> int:
     ap.add_argument("--alpha", type=float, default=0.576)
     ap.add_argument("--instrumented-steps", type=int, default=120)
     ap.add_argument("--replay-rounds", type=int, default=40)
+    ap.add_argument("--eager", action="store_true", help="issue the four calls per step instead of graph replays")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 512 MiB device copy (calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -176,11 +177,21 @@ def main() -> int:
         dec.verify(B, K, draft, greedy=greedy)
         dec.accept(B, K, draft, greedy, n_acc, out_tokens, out_len)
 
-    # warmup
+    def steps(n):
+        if args.eager:
+            for _ in range(n):
+                step()
+        else:
+            dec.decode_steps(B, K, n, draft, greedy, n_acc, out_tokens, out_len, trace, seed, thr)
+
+    # warmup (also records the step graphs of every attention chunk count the timed steps meet)
     start_page()
-    for _ in range(W):
-        step()
+    steps(W)
     torch.cuda.synchronize()
+    if not args.eager:
+        start_page()
+        steps(S)
+        torch.cuda.synchronize()
     # prefill time of one page
     torch.cuda.synchronize()
     t = time.time()
@@ -190,8 +201,7 @@ def main() -> int:
     # timed region: exactly S steps from the start of the page
     torch.cuda.synchronize()
     t0 = time.time()
-    for _ in range(S):
-        step()
+    steps(S)
     torch.cuda.synchronize()
     elapsed = time.time() - t0
     committed = int(out_len.item()) - 1
@@ -276,6 +286,7 @@ def main() -> int:
                         "batch 1, FastMTP K=3 with controlled acceptance 57.6%",
             "batch": B, "K": K, "alpha_target": args.alpha, "prefix_rows": P,
             "compute": "bf16 weights and KV cache, fp32 activations and accumulation",
+            "launch": "eager calls" if args.eager else "HIP graph per decode step",
         },
         "roofline": {
             "kernel": "k_expert_gate_up (grouped expert GEMV, gate+up)",

@@ -132,6 +132,26 @@ int ocrdec_controlled_drafts(ocrdec_model* m, void* stream, int B, const int32_t
                              const int32_t* trace, int trace_stride, int trace_len,
                              uint64_t seed, uint64_t threshold, int32_t* draft_inout);
 
+/* Controlled-draft parameters for ocrdec_decode_steps (see
+ * ocrdec_controlled_drafts). */
+typedef struct {
+  const int32_t* trace;
+  int trace_stride, trace_len;
+  uint64_t seed, threshold;
+} ocrdec_controlled_cfg;
+
+/* n_steps speculative steps of the B sequences: per step ocrdec_draft (K >= 1),
+ * the controlled override when ctrl is non-null, ocrdec_verify and
+ * ocrdec_accept_rollback, with the same results as issuing those calls one by
+ * one.  Each step is recorded once per call shape as a HIP graph (on a
+ * library-private capture stream) and replayed on `stream`; the graphs are
+ * cached in the handle.  draft (device int32 [B][K]) and greedy ([B][K+1]) are
+ * caller scratch; n_accepted / out_tokens / out_len as in
+ * ocrdec_accept_rollback (values of the last step). */
+int ocrdec_decode_steps(ocrdec_model* m, void* stream, int B, const int32_t* slots, int K, int n_steps,
+                        const ocrdec_controlled_cfg* ctrl, int32_t* draft, int32_t* greedy,
+                        int32_t* n_accepted_out, int32_t* out_tokens, int32_t* out_len, int out_cap);
+
 /* Parity taps (nullable device pointers, used by later verify/prefill calls):
  * route_idx int32 [n_layers][rows][8] receives each layer's routing (6 routed
  * experts by decreasing score, then the shared experts 64, 65); hidden fp32

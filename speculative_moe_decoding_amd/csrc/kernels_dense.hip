@@ -34,10 +34,10 @@ __device__ __forceinline__ void rot(float a, float b, float c, float s, float& o
   o2 = fmaf(b, c, a * s);
 }
 
-// One wavefront = one "quad" of 4 output rows.  q / k quads are rows
-// {2u, 2u+1, 2u+64, 2u+65} of one head so that both halves of a RoPE pair land
-// in the same wavefront; v quads are 4 consecutive rows.  Weight loads are
-// issued first; the RMSNorm of the activation rows overlaps them.
+// One wavefront = one pair of output rows: q / k pairs are rows {u, u+64} of
+// one head (the two halves of a RoPE pair), v pairs are rows {2u, 2u+1}.  Weight
+// loads are issued first; lane m fetches the cos/sin of its row's position
+// while they are in flight; the RMSNorm of the activation rows overlaps them.
 template <typename T, int MR>
 __global__ __launch_bounds__(256) void k_qkv_rope(const float* __restrict__ x, const float* __restrict__ gain,
                                                   float eps, const T* __restrict__ wqkv, int M, RowPlan plan,
@@ -46,57 +46,59 @@ __global__ __launch_bounds__(256) void k_qkv_rope(const float* __restrict__ x, c
   extern __shared__ float smem[];
   float* xs = smem;
   const int wave = wave_id(), lane = lane_id();
-  const int quad = blockIdx.x * 4 + wave;  // 0 .. 959
+  const int pr = blockIdx.x * 4 + wave;  // 0 .. 1919
   const int m0 = blockIdx.y * MR;
   const int m_act = min(MR, M - m0);
-  const int sec = quad / 320, rem = quad % 320, h = rem / 32, u = rem % 32;
-  int ri[4];
+  const int sec = pr / 640, rem = pr % 640, h = rem / 64, u = rem % 64;
+  int r0, r1;
   if (sec < 2) {
-    const int b0 = sec * QD + h * HD + 2 * u;
-    ri[0] = b0; ri[1] = b0 + 1; ri[2] = b0 + 64; ri[3] = b0 + 65;
+    r0 = sec * QD + h * HD + u;
+    r1 = r0 + 64;
   } else {
-    const int b0 = 2 * QD + h * HD + 4 * u;
-    ri[0] = b0; ri[1] = b0 + 1; ri[2] = b0 + 2; ri[3] = b0 + 3;
+    r0 = 2 * QD + h * HD + 2 * u;
+    r1 = r0 + 1;
   }
-  const T* rows[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) rows[r] = wqkv + (long)ri[r] * D;
-  WaveGemv<T, D, 4, MR> g;
+  const T* rows[2] = {wqkv + (long)r0 * D, wqkv + (long)r1 * D};
+  WaveGemv<T, D, 2, MR> g;
   g.load(rows);
+  // lane m < m_act: this row's position, validity and rotation
+  int pos = 0, b = 0, i = 0;
+  bool valid = false;
+  float2 cs = make_float2(1.f, 0.f);
+  if (lane < m_act) {
+    const int row = m0 + lane;
+    b = row / plan.Q;
+    i = row - b * plan.Q;
+    pos = plan.base[b] + i;
+    valid = i < plan.cnt[b] && pos >= 0 && pos < max_pos;
+    if (sec < 2) cs = rope[(long)min(max(pos, 0), max_pos - 1) * (HD / 2) + u];
+  }
   norm_rows_wave<D>(x, D, RowIdentity{m0}, m_act, gain, eps, xs, 4);
   __syncthreads();
-  float acc[4][MR];
+  float acc[2][MR];
   g.fma(xs, m_act, acc);
-  wave_reduce_acc<4, MR>(acc, m_act);
+  wave_reduce_acc<2, MR>(acc, m_act);
   const long slot_stride = 2L * NH * max_pos * HD;
 #pragma unroll
   for (int m = 0; m < MR; ++m) {
     if (lane == m && m < m_act) {
       const int row = m0 + m;
-      const int b = row / plan.Q, i = row - b * plan.Q;
-      const int pos = plan.base[b] + i;
-      const bool valid = i < plan.cnt[b] && pos >= 0 && pos < max_pos;
       const long slot = plan.slot[b];
       if (sec < 2) {
-        const int pc = min(max(pos, 0), max_pos - 1);
-        const float2 cs0 = rope[(long)pc * (HD / 2) + 2 * u];
-        const float2 cs1 = rope[(long)pc * (HD / 2) + 2 * u + 1];
-        float o[4];
-        rot(acc[0][m], acc[2][m], cs0.x, cs0.y, o[0], o[2]);
-        rot(acc[1][m], acc[3][m], cs1.x, cs1.y, o[1], o[3]);
-        const int dims[4] = {2 * u, 2 * u + 1, 2 * u + 64, 2 * u + 65};
+        float o0, o1;
+        rot(acc[0][m], acc[1][m], cs.x, cs.y, o0, o1);
         if (sec == 0) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) q[(long)row * QD + h * HD + dims[r]] = o[r];
+          q[(long)row * QD + h * HD + u] = o0;
+          q[(long)row * QD + h * HD + u + 64] = o1;
         } else if (valid) {
           T* kd = kv + slot * slot_stride + ((long)h * max_pos + pos) * HD;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) kd[dims[r]] = WT<T>::store_cvt(o[r]);
+          kd[u] = WT<T>::store_cvt(o0);
+          kd[u + 64] = WT<T>::store_cvt(o1);
         }
       } else if (valid) {
-        T* vd = kv + slot * slot_stride + ((long)(NH + h) * max_pos + pos) * HD + 4 * u;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) vd[r] = WT<T>::store_cvt(acc[r][m]);
+        T* vd = kv + slot * slot_stride + ((long)(NH + h) * max_pos + pos) * HD + 2 * u;
+        vd[0] = WT<T>::store_cvt(acc[0][m]);
+        vd[1] = WT<T>::store_cvt(acc[1][m]);
       }
     }
   }
@@ -107,7 +109,7 @@ void launch_qkv_rope(hipStream_t s, const float* x, const float* gain, float eps
                      RowPlan plan, float* q, T* kv, int max_pos, const float2* rope) {
   const dim3 blk(256);
 #define OCR_QKV_CASE(MRV)                                                                                     \
-  hipLaunchKernelGGL((k_qkv_rope<T, MRV>), dim3(240, (M + MRV - 1) / MRV), blk, (size_t)MRV * D * 4, s, x, gain, \
+  hipLaunchKernelGGL((k_qkv_rope<T, MRV>), dim3(480, (M + MRV - 1) / MRV), blk, (size_t)MRV * D * 4, s, x, gain, \
                      eps, wqkv, M, plan, q, kv, max_pos, rope);
   if (M <= 1) OCR_QKV_CASE(1)
   else if (M <= 2) OCR_QKV_CASE(2)

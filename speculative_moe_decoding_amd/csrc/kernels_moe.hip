@@ -11,8 +11,10 @@
 namespace ocr {
 
 // Top-6 of the 64 logits of one row held one per lane (lane = expert id), ties
-// to the lower id; writes the 8 routing slots of the row.  One wavefront.
-__device__ __forceinline__ void top6_row(float v, int row, const MoeBufs& mb, int* tap, int* pe) {
+// to the lower id, and the gates: lanes 0..5 get the chosen experts by
+// decreasing score with their softmax probability (over all 64 routed
+// experts), lanes 6..7 the shared experts 64, 65 with gate 1.  One wavefront.
+__device__ __forceinline__ void top6_slots(float v, int& gi, float& gv) {
   const int lane = lane_id();
   bool taken = false;
   int sel[TOPK];
@@ -31,52 +33,201 @@ __device__ __forceinline__ void top6_row(float v, int row, const MoeBufs& mb, in
     selv[j] = bv;
     if (lane == bi) taken = true;
   }
-  // softmax over all 64 routed experts; max = the top-1 logit
-  const float mx = selv[0];
+  const float mx = selv[0];  // softmax max = the top-1 logit
   const float ex = expf(v - mx);
   const float sum = wave_sum(ex);
-  if (lane < NSLOT) {
-    float gv = 1.0f;
-    int gi = NE + (lane - TOPK);
+  gv = 1.0f;
+  gi = NE + (lane - TOPK);
 #pragma unroll
-    for (int j = 0; j < TOPK; ++j)
-      if (lane == j) { gi = sel[j]; gv = expf(selv[j] - mx) / sum; }
-    mb.ridx[row * NSLOT + lane] = gi;
-    mb.rgate[row * NSLOT + lane] = gv;
-    if (tap != nullptr) tap[row * NSLOT + lane] = gi;
-    if (pe != nullptr) pe[row * NSLOT + lane] = gi;
+  for (int j = 0; j < TOPK; ++j)
+    if (lane == j) { gi = sel[j]; gv = expf(selv[j] - mx) / sum; }
+}
+
+// Routing of up to 8 rows held in LDS.
+struct RouteLds {
+  int pe[64];        // expert of pair p = row * 8 + slot
+  float pg[64];      // gate of pair p
+  int perm[64];      // pair id by sorted position
+  int inv[64];       // sorted position of pair id
+  int cnt[NX + 1], off[NX + 1], act[NX + 1];
+  int na;
+};
+
+// Stable counting sort of P <= 64 pairs by one wavefront (lane = pair): ranks
+// by ballots over the distinct experts present, offsets by a wavefront scan
+// (routed experts 0..63 in id order, then the shared experts 64, 65).
+__device__ __forceinline__ void sort_pairs_wave(int P, RouteLds& r) {
+  const int lane = lane_id();
+  const bool valid = lane < P;
+  const int e = valid ? r.pe[lane] : -1;
+  const uint64_t lt = (1ull << lane) - 1ull;
+  for (int x = lane; x <= NX; x += 64) r.cnt[x] = 0;
+  uint64_t todo = __ballot(valid);
+  int rank = 0;
+  while (todo) {
+    const int leader = __builtin_ctzll(todo);
+    const int el = __shfl(e, leader, 64);
+    const uint64_t same = __ballot(valid && e == el);
+    if (valid && e == el) rank = __popcll(same & lt);
+    if (lane == 0) r.cnt[el] = __popcll(same);
+    todo &= ~same;
+  }
+  const int c = r.cnt[lane];
+  int incl = c;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += o;
+  }
+  r.off[lane] = incl - c;
+  const int routed = __shfl(incl, 63, 64);
+  const uint64_t amask = __ballot(c > 0);
+  if (c > 0) r.act[__popcll(amask & lt)] = lane;
+  int na = __popcll(amask);
+  const int c64 = r.cnt[NE], c65 = r.cnt[NE + 1];
+  if (lane == 0) {
+    r.off[NE] = routed;
+    r.off[NE + 1] = routed + c64;
+    r.off[NX] = routed + c64 + c65;
+    if (c64 > 0) r.act[na] = NE;
+    if (c65 > 0) r.act[na + (c64 > 0)] = NE + 1;
+    r.na = na + (c64 > 0) + (c65 > 0);
+  }
+  if (valid) {
+    const int pos = r.off[e] + rank;
+    r.perm[pos] = lane;
+    r.inv[lane] = pos;
   }
 }
 
-// Publish the sorted order: off[e], the active experts in increasing id and,
-// per expert slot s < NX, slot_info[s] = (e, first pair, end pair, n_act)
-// (e = -1 past n_act).  Counts the active experts into stats[0].
-__device__ __forceinline__ void publish_slots(const int* off, const int* act, int na, const MoeBufs& mb, int tid,
-                                              int nt) {
-  for (int e = tid; e <= NX; e += nt) mb.off[e] = off[e];
-  for (int sl = tid; sl < NX; sl += nt) {
-    if (sl < na) {
-      const int e = act[sl];
+// Route M <= 8 rows from their logits (rlogit[m][64]) into LDS; all 256
+// threads of the block call it (two barriers inside).  Wavefront w handles rows
+// w, w+4: lane e counts the experts that beat it (larger logit, or equal with a
+// lower id) -- its rank; ranks 0..5 are the routed slots in decreasing order.
+// Gates: softmax over the 64 logits, max = the top-1 logit, sum by the xor
+// butterfly.  Same selection as top6_slots.
+__device__ __forceinline__ void route_rows(const float* __restrict__ rlogit, int M, RouteLds& r) {
+  __shared__ float lg[4][NE];
+  const int wave = wave_id(), lane = lane_id();
+  for (int m = wave; m < M; m += 4) {
+    const float v = rlogit[m * NE + lane];
+    lg[wave][lane] = v;
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    int rank = 0;
+    float mx = v;
+#pragma unroll 16
+    for (int o = 0; o < NE; ++o) {
+      const float u = lg[wave][o];
+      rank += (u > v || (u == v && o < lane)) ? 1 : 0;
+      mx = fmaxf(mx, u);
+    }
+    const float sum = wave_sum(expf(v - mx));
+    if (rank < TOPK) {
+      r.pe[m * NSLOT + rank] = lane;
+      r.pg[m * NSLOT + rank] = expf(v - mx) / sum;
+    }
+    if (lane < NSH) {
+      r.pe[m * NSLOT + TOPK + lane] = NE + lane;
+      r.pg[m * NSLOT + TOPK + lane] = 1.0f;
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  __syncthreads();
+  if (wave == 0) sort_pairs_wave(M * NSLOT, r);
+  __syncthreads();
+}
+
+// Publish the routing of the LDS copy for the kernels that follow (down,
+// combine) and the taps; counts the active experts into stats[0].
+__device__ __forceinline__ void publish_route(const RouteLds& r, int M, const MoeBufs& mb, int* tap) {
+  const int tid = threadIdx.x;
+  const int P = M * NSLOT;
+  for (int p = tid; p < P; p += 256) {
+    mb.ridx[p] = r.pe[p];
+    mb.rgate[p] = r.pg[p];
+    mb.perm[p] = r.perm[p];
+    mb.inv[p] = r.inv[p];
+    if (tap != nullptr) tap[p] = r.pe[p];
+  }
+  for (int e = tid; e <= NX; e += 256) mb.off[e] = r.off[e];
+  for (int sl = tid; sl < NX; sl += 256) {
+    if (sl < r.na) {
+      const int e = r.act[sl];
       mb.act[sl] = e;
-      mb.slot_info[sl] = make_int4(e, off[e], off[e + 1], na);
+      mb.slot_info[sl] = make_int4(e, r.off[e], r.off[e + 1], r.na);
     } else {
-      mb.slot_info[sl] = make_int4(-1, 0, 0, na);
+      mb.slot_info[sl] = make_int4(-1, 0, 0, r.na);
     }
   }
   if (tid == 0) {
-    *mb.n_act = na;
-    mb.stats[0] += na;
+    *mb.n_act = r.na;
+    mb.stats[0] += r.na;
   }
 }
 
-// Stable counting sort of the P = 8M pairs (expert ids in pe[], LDS) by expert;
-// all threads of the block take part.  cnt / off / act: LDS [NX + 1].
-__device__ __forceinline__ void sort_pairs(const int* pe, int P, int* cnt, int* off, int* act, int* na_s,
-                                           const MoeBufs& mb) {
-  const int tid = threadIdx.x, nt = blockDim.x;
-  for (int e = tid; e <= NX; e += nt) cnt[e] = 0;
+// Router logits: wavefront w of block x computes expert 4x + w for every row
+// (RMSNorm'ed with the FFN gain in the prologue; block 0 also stores the
+// normalised rows for the experts).  rlogit[m][e] fp32.
+template <typename T, int MR>
+__global__ __launch_bounds__(256) void k_router_logits(const float* __restrict__ x, const float* __restrict__ gain,
+                                                       float eps, const T* __restrict__ wr, int M,
+                                                       float* __restrict__ bnorm, float* __restrict__ rlogit) {
+  extern __shared__ float xs[];  // [MR][D]
+  const int wave = wave_id(), lane = lane_id();
+  const int e = blockIdx.x * 4 + wave;
+  const int m0 = blockIdx.y * MR;
+  const int m_act = min(MR, M - m0);
+  const T* rows[1] = {wr + (long)e * D};
+  WaveGemv<T, D, 1, MR> g;
+  g.load(rows);
+  norm_rows_wave<D>(x, D, RowIdentity{m0}, m_act, gain, eps, xs, 4);
   __syncthreads();
-  for (int p = tid; p < P; p += nt) atomicAdd(&cnt[pe[p]], 1);
+  if (blockIdx.x == 0)
+    for (int k = threadIdx.x; k < m_act * D; k += 256) bnorm[(long)m0 * D + k] = xs[k];
+  float acc[1][MR];
+  g.fma(xs, m_act, acc);
+  wave_reduce_acc<1, MR>(acc, m_act);
+#pragma unroll
+  for (int m = 0; m < MR; ++m)
+    if (lane == 0 && m < m_act) rlogit[(long)(m0 + m) * NE + e] = acc[0][m];
+}
+
+// M <= 8: top-6 per row and the sort by one block, published to global.
+__global__ __launch_bounds__(256) void k_route_small(const float* __restrict__ rlogit, int M, MoeBufs mb,
+                                                     int* __restrict__ tap) {
+  __shared__ RouteLds r;
+  route_rows(rlogit, M, r);
+  publish_route(r, M, mb, tap);
+}
+
+// Larger batches: top-6 per row (one wavefront per row) into global ...
+__global__ __launch_bounds__(256) void k_topk_rows(const float* __restrict__ rlogit, int M, MoeBufs mb,
+                                                   int* __restrict__ tap) {
+  const int m = blockIdx.x * 4 + wave_id();
+  if (m >= M) return;
+  const int lane = lane_id();
+  int gi;
+  float gv;
+  top6_slots(rlogit[(long)m * NE + lane], gi, gv);
+  if (lane < NSLOT) {
+    mb.ridx[m * NSLOT + lane] = gi;
+    mb.rgate[m * NSLOT + lane] = gv;
+    if (tap != nullptr) tap[m * NSLOT + lane] = gi;
+  }
+}
+
+// ... and one block sorts all pairs (stable counting sort by expert id).
+__global__ __launch_bounds__(1024) void k_sort_pairs(int M, MoeBufs mb) {
+  extern __shared__ int pe[];
+  __shared__ int cnt[NX + 1], off[NX + 1], act[NX + 1];
+  __shared__ int na_s;
+  const int tid = threadIdx.x;
+  const int P = M * NSLOT;
+  for (int p = tid; p < P; p += 1024) pe[p] = mb.ridx[p];
+  for (int e = tid; e <= NX; e += 1024) cnt[e] = 0;
+  __syncthreads();
+  for (int p = tid; p < P; p += 1024) atomicAdd(&cnt[pe[p]], 1);
   __syncthreads();
   if (tid == 0) {
     int acc = 0, na = 0;
@@ -86,11 +237,22 @@ __device__ __forceinline__ void sort_pairs(const int* pe, int P, int* cnt, int* 
       acc += cnt[e];
     }
     off[NX] = acc;
-    *na_s = na;
+    na_s = na;
+    *mb.n_act = na;
+    mb.stats[0] += na;
   }
   __syncthreads();
-  publish_slots(off, act, *na_s, mb, tid, nt);
-  for (int p = tid; p < P; p += nt) {
+  const int na = na_s;
+  for (int e = tid; e <= NX; e += 1024) mb.off[e] = off[e];
+  for (int sl = tid; sl < NX; sl += 1024) {
+    if (sl < na) {
+      mb.act[sl] = act[sl];
+      mb.slot_info[sl] = make_int4(act[sl], off[act[sl]], off[act[sl] + 1], na);
+    } else {
+      mb.slot_info[sl] = make_int4(-1, 0, 0, na);
+    }
+  }
+  for (int p = tid; p < P; p += 1024) {
     const int e = pe[p];
     int rank = 0;
     for (int q = 0; q < p; ++q) rank += (pe[q] == e);
@@ -100,157 +262,27 @@ __device__ __forceinline__ void sort_pairs(const int* pe, int P, int* cnt, int* 
   }
 }
 
-// The same sort for P <= 64 pairs by one wavefront (lane = pair): ranks by
-// ballots over the distinct experts present, offsets by a wavefront scan.
-__device__ __forceinline__ void sort_pairs_wave(const int* pe, int P, int* cnt, int* off, int* act,
-                                                const MoeBufs& mb) {
-  const int lane = lane_id();
-  const bool valid = lane < P;
-  const int e = valid ? pe[lane] : -1;
-  const uint64_t lt = (1ull << lane) - 1ull;
-  for (int x = lane; x <= NX; x += 64) cnt[x] = 0;
-  uint64_t todo = __ballot(valid);
-  int rank = 0;
-  while (todo) {
-    const int leader = __builtin_ctzll(todo);
-    const int el = __shfl(e, leader, 64);
-    const uint64_t same = __ballot(valid && e == el);
-    if (valid && e == el) rank = __popcll(same & lt);
-    if (lane == 0) cnt[el] = __popcll(same);
-    todo &= ~same;
-  }
-  // exclusive scan of the routed counts (lanes = experts 0..63), then the shared experts
-  const int c = cnt[lane];
-  int incl = c;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int o = __shfl_up(incl, d, 64);
-    if (lane >= d) incl += o;
-  }
-  off[lane] = incl - c;
-  const int routed = __shfl(incl, 63, 64);
-  const uint64_t amask = __ballot(c > 0);
-  const int nr = __popcll(amask);
-  if (c > 0) act[__popcll(amask & lt)] = lane;
-  int na = nr;
-  if (lane == 0) {
-    off[NE] = routed;
-    off[NE + 1] = routed + cnt[NE];
-    off[NX] = routed + cnt[NE] + cnt[NE + 1];
-    if (cnt[NE] > 0) act[na] = NE;
-  }
-  na += (cnt[NE] > 0);
-  if (lane == 0 && cnt[NE + 1] > 0) act[na] = NE + 1;
-  na += (cnt[NE + 1] > 0);
-  if (valid) {
-    const int pos = off[e] + rank;
-    mb.perm[pos] = lane;
-    mb.inv[lane] = pos;
-  }
-  publish_slots(off, act, na, mb, lane, 64);
-}
-
-// Small batches (M <= 8): one block of 16 wavefronts does everything.
-// Wavefront w streams router rows 4w..4w+3 (loads issued first), RMSNorms
-// rows w, w+16, ...; then top-6 per row and the sort, all in LDS.
-template <typename T, int MR>
-__global__ __launch_bounds__(1024) void k_router_small(const float* __restrict__ x, const float* __restrict__ gain,
-                                                       float eps, const T* __restrict__ wr, int M, MoeBufs mb,
-                                                       int* __restrict__ tap) {
-  extern __shared__ float xs[];  // [MR][D]
-  __shared__ float lg[MR][NE];
-  __shared__ int pe[MR * NSLOT];
-  __shared__ int cnt[NX + 1], off[NX + 1], act[NX + 1];
-  const int wave = wave_id(), lane = lane_id();
-  const T* rows[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) rows[r] = wr + (long)(wave * 4 + r) * D;
-  WaveGemv<T, D, 4, MR> g;
-  g.load(rows);
-  norm_rows_wave<D>(x, D, RowIdentity{0}, M, gain, eps, xs, 16);
-  __syncthreads();
-  for (int k = threadIdx.x; k < M * D; k += 1024) mb.bnorm[k] = xs[k];
-  float acc[4][MR];
-  g.fma(xs, M, acc);
-  wave_reduce_acc<4, MR>(acc, M);
-#pragma unroll
-  for (int m = 0; m < MR; ++m) {
-    if (m < M && lane < 4) {
-      const float v = (lane == 0) ? acc[0][m] : (lane == 1) ? acc[1][m] : (lane == 2) ? acc[2][m] : acc[3][m];
-      lg[m][wave * 4 + lane] = v;
-    }
-  }
-  __syncthreads();
-  for (int m = wave; m < M; m += 16) top6_row(lg[m][lane], m, mb, tap, pe);
-  __syncthreads();
-  if (wave == 0) sort_pairs_wave(pe, M * NSLOT, cnt, off, act, mb);
-}
-
-// Larger batches: one block per row computes its logits and top-6 ...
-template <typename T>
-__global__ __launch_bounds__(256) void k_router_rows(const float* __restrict__ x, const float* __restrict__ gain,
-                                                     float eps, const T* __restrict__ wr, MoeBufs mb,
-                                                     int* __restrict__ tap) {
-  __shared__ float xs[D];
-  __shared__ float lg[NE];
-  const int row = blockIdx.x;
-  const int wave = wave_id(), lane = lane_id();
-  WaveGemv<T, D, 4, 1> g[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const T* rows[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) rows[r] = wr + (long)(wave * 16 + t * 4 + r) * D;
-    g[t].load(rows);
-  }
-  if (wave == 0) norm_rows_wave<D>(x, D, RowIdentity{row}, 1, gain, eps, xs, 1);
-  __syncthreads();
-  for (int k = threadIdx.x; k < D; k += 256) mb.bnorm[(long)row * D + k] = xs[k];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    float acc[4][1];
-    g[t].fma(xs, 1, acc);
-    wave_reduce_acc<4, 1>(acc, 1);
-    if (lane < 4)
-      lg[wave * 16 + t * 4 + lane] =
-          (lane == 0) ? acc[0][0] : (lane == 1) ? acc[1][0] : (lane == 2) ? acc[2][0] : acc[3][0];
-  }
-  __syncthreads();
-  if (wave == 0) top6_row(lg[lane], row, mb, tap, nullptr);
-}
-
-// ... and one block sorts all pairs.
-__global__ __launch_bounds__(1024) void k_sort_pairs(int M, MoeBufs mb) {
-  extern __shared__ int pe[];
-  __shared__ int cnt[NX + 1], off[NX + 1], act[NX + 1];
-  __shared__ int na_s;
-  const int P = M * NSLOT;
-  for (int p = threadIdx.x; p < P; p += 1024) pe[p] = mb.ridx[p];
-  __syncthreads();
-  sort_pairs(pe, P, cnt, off, act, &na_s, mb);
-}
-
 int expert_slot_cap(int M) { return min(NE, TOPK * M) + NSH; }
 
+// Router: logits in a 16-block kernel, then the top-6 and the sort (one block
+// for M <= 8, a per-row kernel and a sort kernel beyond).
 template <typename T>
 void launch_router(hipStream_t s, const float* x, const float* gain, float eps, const T* wr, int M,
                    const MoeBufs& mb, int* tap) {
-#define OCR_ROUTER_CASE(MRV)                                                                                  \
-  {                                                                                                           \
-    static const bool lds_ok = (allow_lds(k_router_small<T, MRV>, (size_t)MRV * D * 4), true);                \
-    (void)lds_ok;                                                                                             \
-    hipLaunchKernelGGL((k_router_small<T, MRV>), dim3(1), dim3(1024), (size_t)MRV * D * 4, s, x, gain, eps, wr, \
-                       M, mb, tap);                                                                           \
-  }
-  if (M <= 1) OCR_ROUTER_CASE(1)
-  else if (M <= 2) OCR_ROUTER_CASE(2)
-  else if (M <= 4) OCR_ROUTER_CASE(4)
-  else if (M <= 8) OCR_ROUTER_CASE(8)
-  else {
-    hipLaunchKernelGGL((k_router_rows<T>), dim3(M), dim3(256), 0, s, x, gain, eps, wr, mb, tap);
+#define OCR_RL_CASE(MRV)                                                                                   \
+  hipLaunchKernelGGL((k_router_logits<T, MRV>), dim3(NE / 4, (M + MRV - 1) / MRV), dim3(256),              \
+                     (size_t)MRV * D * 4, s, x, gain, eps, wr, M, mb.bnorm, mb.rlogit);
+  if (M <= 1) OCR_RL_CASE(1)
+  else if (M <= 2) OCR_RL_CASE(2)
+  else if (M <= 4) OCR_RL_CASE(4)
+  else OCR_RL_CASE(MRG)
+#undef OCR_RL_CASE
+  if (M <= MRG) {
+    hipLaunchKernelGGL(k_route_small, dim3(1), dim3(256), 0, s, mb.rlogit, M, mb, tap);
+  } else {
+    hipLaunchKernelGGL(k_topk_rows, dim3((M + 3) / 4), dim3(256), 0, s, mb.rlogit, M, mb, tap);
     hipLaunchKernelGGL(k_sort_pairs, dim3(1), dim3(1024), (size_t)M * NSLOT * sizeof(int), s, M, mb);
   }
-#undef OCR_ROUTER_CASE
 }
 
 // Gather the activation rows m < m_act (row_of(m) into src) into LDS;
@@ -275,20 +307,35 @@ __device__ __forceinline__ void gather_rows(const float* __restrict__ src, SrcRo
   }
 }
 
-// Gate/up: block (x, slot s) of expert e = slot_info[s].e; wavefront w owns
-// units j0 .. j0+UPW-1, j0 = UPW (4x + w): rows gate[j] then up[j], all loads
-// issued at once.  The (at most MR) pairs routed to e get
-// hx[pair][j] = silu(gate . b) * (up . b).
-template <typename T, int MR, int UPW>
+// Gate/up: block (x, slot s) handles active expert s; wavefront w owns units
+// j0 .. j0+UPW-1, j0 = UPW (4x + w): rows gate[j] then up[j], all loads issued
+// at once.  The (at most MR) pairs routed to the expert get
+// hx[pair][j] = silu(gate . b) * (up . b).  With ROUTE (M <= 8) every block
+// first routes the M rows from the router logits itself (identical in every
+// block) and block (0, 0) publishes that routing; otherwise the slot table
+// comes from the sort kernel.
+template <typename T, int MR, int UPW, bool ROUTE>
 __global__ __launch_bounds__(256) void k_expert_gate_up(const T* __restrict__ wg, const T* __restrict__ wu,
-                                                        MoeBufs mb) {
+                                                        int M, MoeBufs mb, int* __restrict__ tap) {
   extern __shared__ float xs[];
-  const int4 info = mb.slot_info[blockIdx.y];
-  const int e = info.x;
-  if (e < 0) return;
-  const int k0 = info.y;
-  const int m_act = min(MR, info.z - k0);
+  __shared__ RouteLds r;
   const int wave = wave_id(), lane = lane_id();
+  int e, k0, k1;
+  if (ROUTE) {
+    route_rows(mb.rlogit, M, r);
+    if (blockIdx.x == 0 && blockIdx.y == 0) publish_route(r, M, mb, tap);
+    if ((int)blockIdx.y >= r.na) return;
+    e = r.act[blockIdx.y];
+    k0 = r.off[e];
+    k1 = r.off[e + 1];
+  } else {
+    const int4 info = mb.slot_info[blockIdx.y];
+    e = info.x;
+    if (e < 0) return;
+    k0 = info.y;
+    k1 = info.z;
+  }
+  const int m_act = min(MR, k1 - k0);
   const int j0 = (blockIdx.x * 4 + wave) * UPW;
   const T* gbase = wg + ((long)e * DI + j0) * D;
   const T* ubase = wu + ((long)e * DI + j0) * D;
@@ -300,7 +347,8 @@ __global__ __launch_bounds__(256) void k_expert_gate_up(const T* __restrict__ wg
   }
   WaveGemv<T, D, 2 * UPW, MR> g;
   g.load(rows);
-  gather_rows<D>(mb.bnorm, [&](int m) { return mb.perm[k0 + m] / NSLOT; }, m_act, xs);
+  if (ROUTE) gather_rows<D>(mb.bnorm, [&](int m) { return r.perm[k0 + m] / NSLOT; }, m_act, xs);
+  else gather_rows<D>(mb.bnorm, [&](int m) { return mb.perm[k0 + m] / NSLOT; }, m_act, xs);
   __syncthreads();
   float acc[2 * UPW][MR];
   g.fma(xs, m_act, acc);
@@ -426,10 +474,11 @@ constexpr int GU_UPW = OCR_GU_UPW;   // gate/up units per wavefront
 constexpr int DN_RPW = OCR_DN_RPW;   // down rows per wavefront
 
 template <typename T>
-void launch_expert_gate_up(hipStream_t s, const T* wg, const T* wu, int M, const MoeBufs& mb) {
+void launch_expert_gate_up(hipStream_t s, const T* wg, const T* wu, int M, const MoeBufs& mb, int* tap) {
   const dim3 grid(DI / (4 * GU_UPW), expert_slot_cap(M));
 #define OCR_GU_CASE(MRV) \
-  hipLaunchKernelGGL((k_expert_gate_up<T, MRV, GU_UPW>), grid, dim3(256), (size_t)MRV * D * 4, s, wg, wu, mb);
+  hipLaunchKernelGGL((k_expert_gate_up<T, MRV, GU_UPW, false>), grid, dim3(256), (size_t)MRV * D * 4, s, wg, wu, \
+                     M, mb, tap);
   if (M <= 1) OCR_GU_CASE(1)
   else if (M <= 2) OCR_GU_CASE(2)
   else if (M <= 4) OCR_GU_CASE(4)
@@ -476,7 +525,7 @@ void launch_moe_combine(hipStream_t s, float* x, int M, const MoeBufs& mb) {
 #define OCR_INST_MOE(T)                                                                                  \
   template void launch_router<T>(hipStream_t, const float*, const float*, float, const T*, int,          \
                                  const MoeBufs&, int*);                                                  \
-  template void launch_expert_gate_up<T>(hipStream_t, const T*, const T*, int, const MoeBufs&);          \
+  template void launch_expert_gate_up<T>(hipStream_t, const T*, const T*, int, const MoeBufs&, int*);          \
   template void launch_expert_down<T>(hipStream_t, const T*, int, const MoeBufs&);
 OCR_INST_MOE(float)
 OCR_INST_MOE(bf16)

@@ -48,6 +48,7 @@ struct MoeBufs {
   int* n_act;     // [1]
   int4* slot_info;  // [NX] (expert, first pair, end pair, n_act); expert -1 past n_act
   long long* stats;  // [0] += active experts per layer
+  float* rlogit;  // [M][64] router logits
   float* hx;      // [8M][DI]
   float* y;       // [8M][D]
 };
@@ -56,7 +57,7 @@ template <typename T>
 void launch_router(hipStream_t s, const float* x, const float* gain, float eps, const T* wr, int M,
                    const MoeBufs& mb, int* tap);
 template <typename T>
-void launch_expert_gate_up(hipStream_t s, const T* wg, const T* wu, int M, const MoeBufs& mb);
+void launch_expert_gate_up(hipStream_t s, const T* wg, const T* wu, int M, const MoeBufs& mb, int* tap);
 template <typename T>
 void launch_expert_down(hipStream_t s, const T* wd, int M, const MoeBufs& mb);
 void launch_moe_combine(hipStream_t s, float* x, int M, const MoeBufs& mb);

@@ -4,7 +4,9 @@
 
 #include <algorithm>
 #include <cstring>
+#include <map>
 #include <string>
+#include <tuple>
 #include <vector>
 
 #include "launch.h"
@@ -31,7 +33,7 @@ struct Plan {
   // state
   size_t s_kv, s_dkv, s_ints, s_cu, s_hbuf, s_rope, s_total;
   // workspace
-  size_t w_x, w_q, w_attn, w_part, w_bnorm, w_ridx, w_rgate, w_perm, w_inv, w_off, w_act, w_slot, w_misc, w_stats, w_hx,
+  size_t w_x, w_q, w_attn, w_part, w_bnorm, w_ridx, w_rgate, w_perm, w_inv, w_off, w_act, w_slot, w_rlogit, w_misc, w_stats, w_hx,
       w_y, w_cat, w_u, w_dffn, w_esave, w_hsave, w_lmv, w_lmi, w_plan, w_total;
 };
 
@@ -86,6 +88,7 @@ Plan make_plan(const ocrdec_config* c) {
   p.w_off = take((NX + 1) * 4);
   p.w_act = take(NX * 4);
   p.w_slot = take(NX * 16);
+  p.w_rlogit = take(M * NE * 4);
   p.w_misc = take(64 * 4);       // [0] n_act, [16..] prefill tokens
   p.w_stats = take(8 * 8);
   p.w_hx = take(M * NSLOT * DI * 4);
@@ -126,6 +129,8 @@ struct ocrdec_model {
   size_t ev_used;
   long long stats_base;        // device expert counter when timing was enabled
   int last_verify_rows;        // M of the last verify call (0 before any)
+  hipStream_t capture_stream;  // private stream the decode-step graphs are recorded on
+  std::map<std::vector<uintptr_t>, hipGraphExec_t> graphs;  // by call shape
 };
 
 namespace {
@@ -180,10 +185,11 @@ void verifier_layers(ocrdec_model* m, hipStream_t s, int M, int B, RowPlan plan,
     launch_attention<T>(s, m->q, kvl, c.max_positions, plan, B, nch, m->p.tiles_per_chunk, m->part, m->attn);
     launch_gemv<T>(s, QD, EPI_ADD, m->attn, QD, nullptr, c.norm_eps, wmat<T>(m, lw(m, l, L_WO)), nullptr, D, M,
                    m->x, D);
+    int* tap = (taps && m->tap_route) ? m->tap_route + (size_t)l * M * NSLOT : nullptr;
     launch_router<T>(s, m->x, wvec(m, lw(m, l, L_FNORM)), c.norm_eps, wmat<T>(m, lw(m, l, L_ROUTER)), M, m->mb,
-                     (taps && m->tap_route) ? m->tap_route + (size_t)l * M * NSLOT : nullptr);
+                     tap);
     timing_mark(m, s);
-    launch_expert_gate_up<T>(s, wmat<T>(m, lw(m, l, L_GATE)), wmat<T>(m, lw(m, l, L_UP)), M, m->mb);
+    launch_expert_gate_up<T>(s, wmat<T>(m, lw(m, l, L_GATE)), wmat<T>(m, lw(m, l, L_UP)), M, m->mb, tap);
     timing_mark(m, s);
     launch_expert_down<T>(s, wmat<T>(m, lw(m, l, L_DOWN)), M, m->mb);
     timing_mark(m, s);
@@ -249,7 +255,8 @@ template <typename T>
 int do_draft(ocrdec_model* m, hipStream_t s, int B, const int32_t* slots, int K, int32_t* draft_out) {
   const ocrdec_config& c = m->cfg;
   const int Q = K + 1;
-  const int nch = chunks_for(m, std::min(c.max_positions - 1, call_bound(m, B, slots) + K - 1));
+  // same chunk count as the verify of this step (a decode-step graph is keyed on it)
+  const int nch = chunks_for(m, std::min(c.max_positions - 1, call_bound(m, B, slots) + K));
   launch_plan_draft_catchup<T>(s, B, Q, slots, m->sv, wmat<T>(m, W_EMBED), c.vocab, wvec(m, dw(m, D_NH)),
                                wvec(m, dw(m, D_NE)), c.norm_eps, m->plan_base, m->plan_cnt, m->plan_slot, m->cat);
   RowPlan plan{m->plan_base, m->plan_cnt, m->plan_slot, Q};
@@ -385,6 +392,7 @@ int ocrdec_create(const ocrdec_config* cfg, const void* const* weight_ptrs, int 
   m->mb.off = wi(p.w_off);
   m->mb.act = wi(p.w_act);
   m->mb.slot_info = reinterpret_cast<int4*>(m->ws + p.w_slot);
+  m->mb.rlogit = wf(p.w_rlogit);
   m->mb.stats = reinterpret_cast<long long*>(m->ws + p.w_stats);
   m->mb.hx = wf(p.w_hx);
   m->mb.y = wf(p.w_y);
@@ -395,6 +403,7 @@ int ocrdec_create(const ocrdec_config* cfg, const void* const* weight_ptrs, int 
   m->ev_used = 0;
   m->stats_base = 0;
   m->last_verify_rows = 0;
+  m->capture_stream = nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // clear an error left by earlier, unrelated runtime calls
   hipError_t err = hipMemsetAsync(misc, 0, 64 * 4, s);
@@ -415,6 +424,8 @@ int ocrdec_create(const ocrdec_config* cfg, const void* const* weight_ptrs, int 
 int ocrdec_destroy(ocrdec_model* m) {
   if (!m) return fail(OCRDEC_EINVAL, "model is null");
   for (hipEvent_t e : m->ev) (void)hipEventDestroy(e);
+  for (auto& kv : m->graphs) (void)hipGraphExecDestroy(kv.second);
+  if (m->capture_stream) (void)hipStreamDestroy(m->capture_stream);
   delete m;
   return OCRDEC_OK;
 }
@@ -510,12 +521,84 @@ int ocrdec_replay_expert_gate_up(ocrdec_model* m, void* stream, int n_rounds, in
   for (int r = 0; r < n_rounds; ++r) {
     for (int l = 0; l < m->cfg.n_layers; ++l) {
       if (m->cfg.dtype == OCRDEC_BF16)
-        launch_expert_gate_up<bf16>(s, wmat<bf16>(m, lw(m, l, L_GATE)), wmat<bf16>(m, lw(m, l, L_UP)), M, m->mb);
+        launch_expert_gate_up<bf16>(s, wmat<bf16>(m, lw(m, l, L_GATE)), wmat<bf16>(m, lw(m, l, L_UP)), M, m->mb,
+                                    nullptr);
       else
-        launch_expert_gate_up<float>(s, wmat<float>(m, lw(m, l, L_GATE)), wmat<float>(m, lw(m, l, L_UP)), M, m->mb);
+        launch_expert_gate_up<float>(s, wmat<float>(m, lw(m, l, L_GATE)), wmat<float>(m, lw(m, l, L_UP)), M, m->mb,
+                                     nullptr);
     }
   }
   return hip_check("ocrdec_replay_expert_gate_up");
+}
+
+int ocrdec_decode_steps(ocrdec_model* m, void* stream, int B, const int32_t* slots, int K, int n_steps,
+                        const ocrdec_controlled_cfg* ctrl, int32_t* draft, int32_t* greedy,
+                        int32_t* n_accepted_out, int32_t* out_tokens, int32_t* out_len, int out_cap) {
+  int rc = check_call(m, B, K);
+  if (rc) return rc;
+  if (K < 1 || n_steps < 0 || !draft || !greedy) return fail(OCRDEC_EINVAL, "bad decode-step arguments");
+  if (out_tokens && out_cap < 1) return fail(OCRDEC_EINVAL, "out_cap must be >= 1 with out_tokens");
+  if (ctrl && (!ctrl->trace || ctrl->trace_len < 0 || ctrl->trace_stride < ctrl->trace_len))
+    return fail(OCRDEC_EINVAL, "bad controlled-draft arguments");
+  if (m->timing) return fail(OCRDEC_EINVAL, "expert timing is on; use the individual calls");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!m->capture_stream && hipStreamCreateWithFlags(&m->capture_stream, hipStreamNonBlocking) != hipSuccess)
+    return fail(OCRDEC_EHIP, "creating the capture stream failed");
+  for (int step = 0; step < n_steps; ++step) {
+    const int bound = call_bound(m, B, slots);
+    if (!slots && bound + K + 1 > m->cfg.max_positions)
+      return fail(OCRDEC_ECAPACITY, "positions would exceed max_positions");
+    const int nch = chunks_for(m, std::min(m->cfg.max_positions - 1, bound + K));
+    std::vector<uintptr_t> key = {(uintptr_t)B, (uintptr_t)K, (uintptr_t)nch, (uintptr_t)slots,
+                                  (uintptr_t)draft, (uintptr_t)greedy, (uintptr_t)n_accepted_out,
+                                  (uintptr_t)out_tokens, (uintptr_t)out_len, (uintptr_t)out_cap,
+                                  (uintptr_t)m->tap_route, (uintptr_t)m->tap_hidden};
+    if (ctrl) {
+      key.push_back((uintptr_t)ctrl->trace);
+      key.push_back((uintptr_t)ctrl->trace_stride);
+      key.push_back((uintptr_t)ctrl->trace_len);
+      key.push_back((uintptr_t)ctrl->seed);
+      key.push_back((uintptr_t)ctrl->threshold);
+    }
+    auto it = m->graphs.find(key);
+    if (it == m->graphs.end()) {
+      if (m->graphs.size() >= 256) {
+        for (auto& kv : m->graphs) (void)hipGraphExecDestroy(kv.second);
+        m->graphs.clear();
+      }
+      hipStream_t cs = m->capture_stream;
+      if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess)
+        return fail(OCRDEC_EHIP, "hipStreamBeginCapture failed");
+      int r1 = m->cfg.dtype == OCRDEC_BF16 ? do_draft<bf16>(m, cs, B, slots, K, draft)
+                                             : do_draft<float>(m, cs, B, slots, K, draft);
+      if (r1 == OCRDEC_OK && ctrl)
+        launch_controlled(cs, B, K, slots, m->sv, ctrl->trace, ctrl->trace_stride, ctrl->trace_len, ctrl->seed,
+                          ctrl->threshold, m->cfg.vocab, draft);
+      if (r1 == OCRDEC_OK)
+        r1 = m->cfg.dtype == OCRDEC_BF16 ? do_verify<bf16>(m, cs, B, slots, K, draft, greedy, nullptr)
+                                         : do_verify<float>(m, cs, B, slots, K, draft, greedy, nullptr);
+      if (r1 == OCRDEC_OK)
+        launch_accept(cs, B, K, m->plan_slot, draft, greedy, m->x, m->sv, n_accepted_out, out_tokens, out_len,
+                      out_cap);
+      hipGraph_t graph = nullptr;
+      const hipError_t ec = hipStreamEndCapture(cs, &graph);
+      if (r1 != OCRDEC_OK || ec != hipSuccess) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return r1 != OCRDEC_OK ? r1 : fail(OCRDEC_EHIP, std::string("hipStreamEndCapture: ") + hipGetErrorString(ec));
+      }
+      hipGraphExec_t exec = nullptr;
+      const hipError_t ei = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+      (void)hipGraphDestroy(graph);
+      if (ei != hipSuccess) return fail(OCRDEC_EHIP, std::string("hipGraphInstantiate: ") + hipGetErrorString(ei));
+      it = m->graphs.emplace(key, exec).first;
+    }
+    const hipError_t el = hipGraphLaunch(it->second, s);
+    if (el != hipSuccess) return fail(OCRDEC_EHIP, std::string("hipGraphLaunch: ") + hipGetErrorString(el));
+    const int n = slots ? (int)m->slot_bound.size() : B;
+    for (int i = 0; i < n; ++i) m->slot_bound[i] = std::min(m->cfg.max_positions, m->slot_bound[i] + K + 1);
+    m->last_verify_rows = B * (K + 1);
+  }
+  return OCRDEC_OK;
 }
 
 int ocrdec_set_taps(ocrdec_model* m, int32_t* route_idx, float* hidden) {

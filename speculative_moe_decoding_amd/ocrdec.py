@@ -22,7 +22,7 @@ SYMBOLS = (
     "ocrdec_state_bytes", "ocrdec_workspace_bytes", "ocrdec_num_weights", "ocrdec_create", "ocrdec_destroy",
     "ocrdec_prefill", "ocrdec_draft", "ocrdec_verify", "ocrdec_accept_rollback", "ocrdec_controlled_drafts",
     "ocrdec_set_taps", "ocrdec_expert_timing", "ocrdec_expert_stats", "ocrdec_replay_expert_gate_up",
-    "ocrdec_last_error",
+    "ocrdec_decode_steps", "ocrdec_last_error",
 )
 
 
@@ -31,6 +31,11 @@ class ocrdec_config(ctypes.Structure):
                                             "top_k", "d_expert", "d_draft_ffn", "vocab")] + [
         ("rope_theta", ctypes.c_float), ("norm_eps", ctypes.c_float), ("dtype", ctypes.c_int),
         ("max_batch", ctypes.c_int), ("max_k", ctypes.c_int), ("max_positions", ctypes.c_int)]
+
+
+class ocrdec_controlled_cfg(ctypes.Structure):
+    _fields_ = [("trace", ctypes.c_void_p), ("trace_stride", ctypes.c_int), ("trace_len", ctypes.c_int),
+                ("seed", ctypes.c_uint64), ("threshold", ctypes.c_uint64)]
 
 
 class OcrdecError(RuntimeError):
@@ -69,6 +74,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                     ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_longlong),
                                     ctypes.POINTER(ctypes.c_longlong)]),
         "ocrdec_replay_expert_gate_up": (I, [P, P, I, ctypes.POINTER(I)]),
+        "ocrdec_decode_steps": (I, [P, P, I, P, I, I, ctypes.POINTER(ocrdec_controlled_cfg), P, P, P, P, P, I]),
         "ocrdec_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -166,6 +172,13 @@ def ocrdec_expert_stats(h):
     return dict(ms_gate_up=a.value, n_gate_up=na.value, ms_down=b.value, n_down=nb.value, expert_sets=sets.value)
 
 
+def ocrdec_decode_steps(h, stream, B, slots, K, n_steps, ctrl, draft, greedy, n_accepted_out, out_tokens, out_len,
+                        out_cap):
+    _check("ocrdec_decode_steps", load_library().ocrdec_decode_steps(
+        h, stream, B, _ptr(slots), K, n_steps, None if ctrl is None else ctypes.byref(ctrl), _ptr(draft),
+        _ptr(greedy), _ptr(n_accepted_out), _ptr(out_tokens), _ptr(out_len), out_cap))
+
+
 def ocrdec_replay_expert_gate_up(h, stream, n_rounds: int, want_count: bool = False):
     na = ctypes.c_int()
     _check("ocrdec_replay_expert_gate_up", load_library().ocrdec_replay_expert_gate_up(
@@ -252,8 +265,17 @@ class Decoder:
         ocrdec_controlled_drafts(self.h, self.stream, B, slots, K, trace, trace.shape[1], trace.shape[1], seed,
                                  threshold, draft)
 
+    def decode_steps(self, B, K, n_steps, draft, greedy, n_acc, out_tokens, out_len, trace=None, seed=0,
+                     threshold=0, slots=None):
+        """n_steps graph-replayed speculative steps (see ocrdec_decode_steps)."""
+        ctrl = None
+        if trace is not None:
+            ctrl = ocrdec_controlled_cfg(trace.data_ptr(), trace.shape[1], trace.shape[1], seed, threshold)
+        ocrdec_decode_steps(self.h, self.stream, B, slots, K, n_steps, ctrl, draft, greedy, n_acc, out_tokens,
+                            out_len, out_tokens.shape[1])
+
     def generate(self, pages, n_out: int, K: int, trace=None, seed: int = 0, threshold: int = 0,
-                 record: bool = False, check_every: int = 16):
+                 record: bool = False, check_every: int = 16, graphs: bool = False):
         """Decode B pages to n_out tokens each with K draft tokens per step (K = 0: plain
         autoregressive).  With ``trace`` (device int32 [B, T]) the drafts are replaced by the
         controlled-acceptance tokens.  Returns (tokens [B, n_out] numpy, per-sequence lists of
@@ -271,6 +293,13 @@ class Decoder:
         accs, lens = [], []
         steps = 0
         while True:
+            if graphs and K > 0 and not record:
+                self.decode_steps(B, K, check_every, draft, greedy, n_acc, out_tokens, out_len, trace, seed,
+                                  threshold)
+                steps += check_every
+                if int(out_len.min().item()) >= n_out:
+                    break
+                continue
             for _ in range(check_every):
                 if K > 0:
                     self.draft(B, K, out=draft)

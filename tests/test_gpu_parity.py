@@ -131,3 +131,26 @@ def test_controlled_acceptance_lossless():
                                     check_every=1)
         assert toks[0].tolist() == ar[0][:N].tolist()
         assert acc[0] == od.controlled_accepts(N, K, 3000, p, seq_index=0)
+
+
+def test_graph_steps_match_eager_calls():
+    """Decode steps replayed from cached HIP graphs give the tokens and accepted
+    lengths of the individual calls, replay after replay (eager work and
+    synchronisations in between), with the real draft and with controlled drafts."""
+    cfg = SMALL16
+    w = synth.Weights(cfg, 49)
+    from speculative_moe_decoding_amd import ocrdec
+    page = synth.make_pages(cfg, 50, [30], [6], [48])[0]
+    dec = ocrdec.Decoder(cfg, w.device_arrays(), max_batch=1, max_k=3, max_positions=1024)
+    N = 48
+    ar, _, _ = dec.generate([page], N + 8, 0, check_every=8)
+    trace = torch.from_numpy(ar.astype(np.int32)).cuda()
+    thr = od.replace_threshold(synth.replacement_probability(0.576, 3))
+    for tr in (None, trace):
+        eager, _, _ = dec.generate([page], N, 3, trace=tr, seed=3000, threshold=thr, check_every=1)
+        for rep in range(3):
+            g, _, _ = dec.generate([page], N, 3, trace=tr, seed=3000, threshold=thr, check_every=2, graphs=True)
+            assert g[0].tolist() == eager[0].tolist(), rep
+            torch.cuda.synchronize()
+        assert eager[0].tolist() == ar[0][:N].tolist()
+    log("graph decode matches eager calls")
