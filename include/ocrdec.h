@@ -43,16 +43,28 @@ extern "C" {
 #define OCRDEC_F32 0           /* fp32 weights, fp32 KV cache */
 #define OCRDEC_BF16 1          /* bf16 weights and embedding, bf16 KV cache */
 
+/* Arithmetic path of the expert SwiGLU and the LM head, fixed per handle so
+ * that a row's result never depends on how many rows share a call:
+ *   OCRDEC_PATH_AUTO    matrix cores for bf16 handles with
+ *                       max_batch * (max_k + 1) > 8 and vocab >= 64, else vector;
+ *   OCRDEC_PATH_VECTOR  wavefront GEMV, fp32 activations (every dtype);
+ *   OCRDEC_PATH_MATRIX  MFMA tiles with activations rounded to bf16
+ *                       (bf16 handles with vocab >= 64 only, else OCRDEC_EINVAL). */
+#define OCRDEC_PATH_AUTO 0
+#define OCRDEC_PATH_VECTOR 1
+#define OCRDEC_PATH_MATRIX 2
+
 /* Model shape and capacity (plain data).  The kernels are built for the
  * decoder shape of the pages' spec table: d_model 1280, 10 heads x 128,
  * 64 routed + 2 shared experts of width 896, top-6, draft FFN 3584; other
  * values of those fields are rejected with OCRDEC_EINVAL.  n_layers >= 1,
- * vocab >= 1, max_positions <= 32768 (the pages' position limit). */
+ * vocab >= 2, max_positions <= 32768 (the pages' position limit). */
 typedef struct {
   int n_layers, d_model, n_heads, head_dim, n_experts, n_shared, top_k, d_expert, d_draft_ffn, vocab;
   float rope_theta, norm_eps;
   int dtype;                                   /* OCRDEC_F32 | OCRDEC_BF16 */
   int max_batch, max_k, max_positions;
+  int path;                                    /* OCRDEC_PATH_* */
 } ocrdec_config;
 
 typedef struct ocrdec_model ocrdec_model;

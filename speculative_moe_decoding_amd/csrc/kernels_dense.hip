@@ -337,6 +337,11 @@ __global__ __launch_bounds__(256) void k_argmax_final(const float* __restrict__ 
 
 int lmhead_blocks(int V) { return (V + LM_ROWS_PER_BLOCK - 1) / LM_ROWS_PER_BLOCK; }
 
+void launch_argmax_final(hipStream_t s, const float* part_val, const int* part_idx, int nblk, int M, int* tok,
+                         int tok_stride) {
+  hipLaunchKernelGGL(k_argmax_final, dim3(M), dim3(256), 0, s, part_val, part_idx, nblk, tok, tok_stride);
+}
+
 template <typename T>
 void launch_lmhead(hipStream_t s, const float* x, const int* cnt, int Q, bool last_valid, const float* gain,
                    float eps, const T* W, int V, int M, float* part_val, int* part_idx, float* logits, int* tok,
@@ -351,7 +356,7 @@ void launch_lmhead(hipStream_t s, const float* x, const int* cnt, int Q, bool la
   else if (M <= 4) OCR_LM_CASE(4)
   else OCR_LM_CASE(MRG)
 #undef OCR_LM_CASE
-  hipLaunchKernelGGL(k_argmax_final, dim3(M), blk, 0, s, part_val, part_idx, nb, tok, tok_stride);
+  launch_argmax_final(s, part_val, part_idx, nb, M, tok, tok_stride);
 }
 
 #define OCR_INST_DENSE(T)                                                                                       \

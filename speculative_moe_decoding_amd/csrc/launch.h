@@ -32,6 +32,9 @@ void launch_lmhead(hipStream_t s, const float* x, const int* cnt, int Q, bool la
                    float eps, const T* W, int V, int M, float* part_val, int* part_idx, float* logits, int* tok,
                    int tok_stride);
 int lmhead_blocks(int V);
+// Stage 2 of the argmax: tok[m * tok_stride] = best of part[m][0 .. nblk).
+void launch_argmax_final(hipStream_t s, const float* part_val, const int* part_idx, int nblk, int M, int* tok,
+                         int tok_stride);
 
 template <typename T>
 void launch_attention(hipStream_t s, const float* q, const T* kv, int max_pos, RowPlan plan, int B,
@@ -62,6 +65,15 @@ template <typename T>
 void launch_expert_down(hipStream_t s, const T* wd, int M, const MoeBufs& mb);
 void launch_moe_combine(hipStream_t s, float* x, int M, const MoeBufs& mb);
 int expert_slot_cap(int M);
+
+// Matrix-core variants (bf16 weights): the same outputs as the vector
+// launchers above, with the activations rounded to bf16 for the MFMA inputs.
+void launch_expert_gate_up_mfma(hipStream_t s, const bf16* wg, const bf16* wu, int M, const MoeBufs& mb);
+void launch_expert_down_mfma(hipStream_t s, const bf16* wd, int M, const MoeBufs& mb);
+// LM head + argmax: xn ([M][D] scratch) receives the normalised rows; V >= 16.
+void launch_lmhead_mfma(hipStream_t s, const float* x, const int* cnt, int Q, bool last_valid, const float* gain,
+                        float eps, const bf16* W, int V, int M, float* xn, float* part_val, int* part_idx,
+                        float* logits, int* tok, int tok_stride);
 
 // ---- row plans, embeddings, acceptance --------------------------------------
 struct StateView {

@@ -7,6 +7,7 @@
 #include <map>
 #include <string>
 #include <tuple>
+#include <type_traits>
 #include <vector>
 
 #include "launch.h"
@@ -51,7 +52,19 @@ bool shape_ok(const ocrdec_config* c, std::string* why) {
   if (c->max_k < 0 || c->max_k > 7) { *why = "max_k must be in [0, 7]"; return false; }
   if (c->max_positions < 16 || c->max_positions > 32768) { *why = "max_positions must be in [16, 32768]"; return false; }
   if (!(c->norm_eps > 0.f) || !(c->rope_theta > 1.f)) { *why = "norm_eps must be > 0 and rope_theta > 1"; return false; }
+  if (c->path < OCRDEC_PATH_AUTO || c->path > OCRDEC_PATH_MATRIX) { *why = "path must be OCRDEC_PATH_*"; return false; }
+  if (c->path == OCRDEC_PATH_MATRIX && (c->dtype != OCRDEC_BF16 || c->vocab < 64)) {
+    *why = "the matrix-core path needs bf16 weights and vocab >= 64";
+    return false;
+  }
   return true;
+}
+
+// Matrix cores for the experts and the LM head: fixed per handle.
+bool use_matrix_path(const ocrdec_config* c) {
+  if (c->path == OCRDEC_PATH_MATRIX) return true;
+  if (c->path == OCRDEC_PATH_VECTOR) return false;
+  return c->dtype == OCRDEC_BF16 && c->vocab >= 64 && c->max_batch * (c->max_k + 1) > MRG;
 }
 
 Plan make_plan(const ocrdec_config* c) {
@@ -129,6 +142,7 @@ struct ocrdec_model {
   size_t ev_used;
   long long stats_base;        // device expert counter when timing was enabled
   int last_verify_rows;        // M of the last verify call (0 before any)
+  bool matrix;                 // experts and LM head on the matrix cores
   hipStream_t capture_stream;  // private stream the decode-step graphs are recorded on
   std::map<std::vector<uintptr_t>, hipGraphExec_t> graphs;  // by call shape
 };
@@ -176,6 +190,44 @@ void timing_mark(ocrdec_model* m, hipStream_t s) {
 }
 
 template <typename T>
+void expert_gate_up(ocrdec_model* m, hipStream_t s, int l, int M, int* tap) {
+  if constexpr (std::is_same<T, bf16>::value) {
+    if (m->matrix) {
+      launch_expert_gate_up_mfma(s, wmat<T>(m, lw(m, l, L_GATE)), wmat<T>(m, lw(m, l, L_UP)), M, m->mb);
+      return;
+    }
+  }
+  launch_expert_gate_up<T>(s, wmat<T>(m, lw(m, l, L_GATE)), wmat<T>(m, lw(m, l, L_UP)), M, m->mb, tap);
+}
+
+template <typename T>
+void expert_down(ocrdec_model* m, hipStream_t s, int l, int M) {
+  if constexpr (std::is_same<T, bf16>::value) {
+    if (m->matrix) {
+      launch_expert_down_mfma(s, wmat<T>(m, lw(m, l, L_DOWN)), M, m->mb);
+      return;
+    }
+  }
+  launch_expert_down<T>(s, wmat<T>(m, lw(m, l, L_DOWN)), M, m->mb);
+}
+
+// LM head + argmax over M output rows (see launch_lmhead).
+template <typename T>
+void lm_head(ocrdec_model* m, hipStream_t s, const float* x, int Q, bool last_valid, const float* gain, int M,
+             float* logits, int* tok, int tok_stride) {
+  const ocrdec_config& c = m->cfg;
+  if constexpr (std::is_same<T, bf16>::value) {
+    if (m->matrix) {
+      launch_lmhead_mfma(s, x, m->plan_cnt, Q, last_valid, gain, c.norm_eps, wmat<T>(m, W_LM), c.vocab, M,
+                         m->mb.bnorm, m->lm_val, m->lm_idx, logits, tok, tok_stride);
+      return;
+    }
+  }
+  launch_lmhead<T>(s, x, m->plan_cnt, Q, last_valid, gain, c.norm_eps, wmat<T>(m, W_LM), c.vocab, M, m->lm_val,
+                   m->lm_idx, logits, tok, tok_stride);
+}
+
+template <typename T>
 void verifier_layers(ocrdec_model* m, hipStream_t s, int M, int B, RowPlan plan, int nch, bool taps) {
   const ocrdec_config& c = m->cfg;
   for (int l = 0; l < c.n_layers; ++l) {
@@ -189,9 +241,9 @@ void verifier_layers(ocrdec_model* m, hipStream_t s, int M, int B, RowPlan plan,
     launch_router<T>(s, m->x, wvec(m, lw(m, l, L_FNORM)), c.norm_eps, wmat<T>(m, lw(m, l, L_ROUTER)), M, m->mb,
                      tap);
     timing_mark(m, s);
-    launch_expert_gate_up<T>(s, wmat<T>(m, lw(m, l, L_GATE)), wmat<T>(m, lw(m, l, L_UP)), M, m->mb, tap);
+    expert_gate_up<T>(m, s, l, M, tap);
     timing_mark(m, s);
-    launch_expert_down<T>(s, wmat<T>(m, lw(m, l, L_DOWN)), M, m->mb);
+    expert_down<T>(m, s, l, M);
     timing_mark(m, s);
     launch_moe_combine(s, m->x, M, m->mb);
   }
@@ -234,8 +286,7 @@ int do_prefill(ocrdec_model* m, hipStream_t s, int B, const int32_t* slots_host,
       const int nch = chunks_for(m, p0 + cc - 1);
       verifier_layers<T>(m, s, cc, 1, plan, nch, false);
       if (p0 + cc == P)
-        launch_lmhead<T>(s, m->x, m->plan_cnt, cc, true, wvec(m, W_FNORM), c.norm_eps, wmat<T>(m, W_LM), c.vocab, 1,
-                         m->lm_val, m->lm_idx, nullptr, m->tok_tmp, 1);
+        lm_head<T>(m, s, m->x, cc, true, wvec(m, W_FNORM), 1, nullptr, m->tok_tmp, 1);
       launch_draft_prefill_cat(s, cc, m->x, m->esave, m->hsave[par], m->hsave[1 - par], wvec(m, dw(m, D_NH)),
                                wvec(m, dw(m, D_NE)), c.norm_eps, m->cat);
       draft_layer<T>(m, s, cc, 1, plan, nch);
@@ -261,8 +312,7 @@ int do_draft(ocrdec_model* m, hipStream_t s, int B, const int32_t* slots, int K,
                                wvec(m, dw(m, D_NE)), c.norm_eps, m->plan_base, m->plan_cnt, m->plan_slot, m->cat);
   RowPlan plan{m->plan_base, m->plan_cnt, m->plan_slot, Q};
   draft_layer<T>(m, s, B * Q, B, plan, nch);
-  launch_lmhead<T>(s, m->u, m->plan_cnt, Q, true, wvec(m, dw(m, D_ONORM)), c.norm_eps, wmat<T>(m, W_LM), c.vocab, B,
-                   m->lm_val, m->lm_idx, nullptr, draft_out, K);
+  lm_head<T>(m, s, m->u, Q, true, wvec(m, dw(m, D_ONORM)), B, nullptr, draft_out, K);
   for (int j = 2; j <= K; ++j) {
     const int Qprev = (j == 2) ? Q : 1;
     launch_plan_draft_step<T>(s, B, j, Qprev, K, m->sv, draft_out, wmat<T>(m, W_EMBED), c.vocab,
@@ -270,8 +320,7 @@ int do_draft(ocrdec_model* m, hipStream_t s, int B, const int32_t* slots, int K,
                               m->plan_slot, m->cat);
     RowPlan p1{m->plan_base, m->plan_cnt, m->plan_slot, 1};
     draft_layer<T>(m, s, B, B, p1, nch);
-    launch_lmhead<T>(s, m->u, m->plan_cnt, 1, true, wvec(m, dw(m, D_ONORM)), c.norm_eps, wmat<T>(m, W_LM), c.vocab,
-                     B, m->lm_val, m->lm_idx, nullptr, draft_out + (j - 1), K);
+    lm_head<T>(m, s, m->u, 1, true, wvec(m, dw(m, D_ONORM)), B, nullptr, draft_out + (j - 1), K);
   }
   return hip_check("ocrdec_draft");
 }
@@ -287,8 +336,7 @@ int do_verify(ocrdec_model* m, hipStream_t s, int B, const int32_t* slots, int K
   RowPlan plan{m->plan_base, m->plan_cnt, m->plan_slot, Q};
   verifier_layers<T>(m, s, M, B, plan, nch, true);
   m->last_verify_rows = M;
-  launch_lmhead<T>(s, m->x, m->plan_cnt, Q, false, wvec(m, W_FNORM), c.norm_eps, wmat<T>(m, W_LM), c.vocab, M,
-                   m->lm_val, m->lm_idx, logits_out, greedy_out, 1);
+  lm_head<T>(m, s, m->x, Q, false, wvec(m, W_FNORM), M, logits_out, greedy_out, 1);
   if (m->tap_hidden) launch_copy_rows(s, m->x, m->tap_hidden, (long)M * D);
   return hip_check("ocrdec_verify");
 }
@@ -403,6 +451,7 @@ int ocrdec_create(const ocrdec_config* cfg, const void* const* weight_ptrs, int 
   m->ev_used = 0;
   m->stats_base = 0;
   m->last_verify_rows = 0;
+  m->matrix = use_matrix_path(cfg);
   m->capture_stream = nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // clear an error left by earlier, unrelated runtime calls
@@ -520,12 +569,8 @@ int ocrdec_replay_expert_gate_up(ocrdec_model* m, void* stream, int n_rounds, in
   const int M = m->last_verify_rows;
   for (int r = 0; r < n_rounds; ++r) {
     for (int l = 0; l < m->cfg.n_layers; ++l) {
-      if (m->cfg.dtype == OCRDEC_BF16)
-        launch_expert_gate_up<bf16>(s, wmat<bf16>(m, lw(m, l, L_GATE)), wmat<bf16>(m, lw(m, l, L_UP)), M, m->mb,
-                                    nullptr);
-      else
-        launch_expert_gate_up<float>(s, wmat<float>(m, lw(m, l, L_GATE)), wmat<float>(m, lw(m, l, L_UP)), M, m->mb,
-                                     nullptr);
+      if (m->cfg.dtype == OCRDEC_BF16) expert_gate_up<bf16>(m, s, l, M, nullptr);
+      else expert_gate_up<float>(m, s, l, M, nullptr);
     }
   }
   return hip_check("ocrdec_replay_expert_gate_up");

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libocrdec.s
 
 OCRDEC_OK, OCRDEC_EINVAL, OCRDEC_ECAPACITY, OCRDEC_EHIP = 0, -1, -2, -3
 OCRDEC_F32, OCRDEC_BF16 = 0, 1
+OCRDEC_PATH_AUTO, OCRDEC_PATH_VECTOR, OCRDEC_PATH_MATRIX = 0, 1, 2
 
 SYMBOLS = (
     "ocrdec_state_bytes", "ocrdec_workspace_bytes", "ocrdec_num_weights", "ocrdec_create", "ocrdec_destroy",
@@ -30,7 +31,8 @@ class ocrdec_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in ("n_layers", "d_model", "n_heads", "head_dim", "n_experts", "n_shared",
                                             "top_k", "d_expert", "d_draft_ffn", "vocab")] + [
         ("rope_theta", ctypes.c_float), ("norm_eps", ctypes.c_float), ("dtype", ctypes.c_int),
-        ("max_batch", ctypes.c_int), ("max_k", ctypes.c_int), ("max_positions", ctypes.c_int)]
+        ("max_batch", ctypes.c_int), ("max_k", ctypes.c_int), ("max_positions", ctypes.c_int),
+        ("path", ctypes.c_int)]
 
 
 class ocrdec_controlled_cfg(ctypes.Structure):
@@ -90,11 +92,11 @@ def _check(fn: str, rc: int) -> None:
         raise OcrdecError(fn, rc, load_library().ocrdec_last_error().decode())
 
 
-def make_config(cfg, max_batch: int, max_k: int, max_positions: int) -> ocrdec_config:
+def make_config(cfg, max_batch: int, max_k: int, max_positions: int, path: int = 0) -> ocrdec_config:
     return ocrdec_config(cfg.n_layers, cfg.d_model, cfg.n_heads, cfg.head_dim, cfg.n_experts, cfg.n_shared,
                          cfg.top_k, cfg.d_expert, cfg.d_draft_ffn, cfg.vocab, float(cfg.rope_theta),
                          float(cfg.norm_eps), OCRDEC_BF16 if cfg.dtype == "bf16" else OCRDEC_F32,
-                         max_batch, max_k, max_positions)
+                         max_batch, max_k, max_positions, path)
 
 
 def _ptr(t) -> Optional[int]:
@@ -191,13 +193,13 @@ class Decoder:
     (torch allocations) and drives the four decode calls on one stream."""
 
     def __init__(self, cfg, weight_arrays: List[np.ndarray], max_batch: int, max_k: int, max_positions: int,
-                 device: str = "cuda"):
+                 device: str = "cuda", path: int = 0):
         import torch
         self.torch = torch
         load_library()
         self.cfg = cfg
         self.device = torch.device(device)
-        self.c = make_config(cfg, max_batch, max_k, max_positions)
+        self.c = make_config(cfg, max_batch, max_k, max_positions, path)
         n = ocrdec_num_weights(self.c)
         if n != len(weight_arrays):
             raise ValueError(f"expected {n} weight tensors, got {len(weight_arrays)}")
@@ -321,3 +323,59 @@ class Decoder:
             ln = torch.stack(lens).cpu().numpy()
             acc = [a[:int(np.argmax(ln[:, b] >= n_out)) + 1, b].tolist() for b in range(B)]
         return toks, acc, steps
+
+    def generate_ragged(self, pages, n_out, K: int, trace=None, seed: int = 0, threshold: int = 0,
+                        check_every: int = 8, record: bool = False, graphs: bool = False):
+        """Static batch with per-sequence output lengths: sequence b (slot b) leaves the
+        batch once it has n_out[b] tokens; the others go on (no refill).  ``trace``
+        (device int32 [B, T]) switches on the controlled drafts.  Returns (list of token
+        arrays, per-sequence accepted lengths of the steps up to n_out[b] if record, total
+        sequence-steps run)."""
+        torch = self.torch
+        B = len(pages)
+        n_out = np.asarray(n_out, dtype=np.int64)
+        cap = int(n_out.max()) + self.max_k + 2
+        full = torch.zeros(B, cap, dtype=torch.int32, device=self.device)
+        full[:, 0] = self.prefill(pages)
+        active = np.arange(B)
+        accs = [[] for _ in range(B)]
+        done_len = np.ones(B, dtype=np.int64)
+        seq_steps = 0
+        while len(active):
+            Bb = len(active)
+            slots = torch.from_numpy(active.astype(np.int32)).to(self.device)
+            out_t = full[torch.from_numpy(active).to(self.device)].contiguous()
+            tr = None if trace is None else trace[torch.from_numpy(active).to(self.device)].contiguous()
+            out_len, n_acc = self.i32(Bb), self.i32(Bb)
+            draft, greedy = self.i32(Bb, max(K, 1)), self.i32(Bb, K + 1)
+            while True:
+                rec = []
+                if graphs and K > 0 and not record:
+                    self.decode_steps(Bb, K, check_every, draft, greedy, n_acc, out_t, out_len, tr, seed,
+                                      threshold, slots=slots)
+                else:
+                    for _ in range(check_every):
+                        if K > 0:
+                            self.draft(Bb, K, slots=slots, out=draft)
+                            if tr is not None:
+                                self.controlled(Bb, K, tr, seed, threshold, draft, slots=slots)
+                        self.verify(Bb, K, draft, slots=slots, greedy=greedy)
+                        self.accept(Bb, K, draft, greedy, n_acc, out_t, out_len, slots=slots)
+                        if record:
+                            rec.append((n_acc.clone(), out_len.clone()))
+                seq_steps += Bb * check_every
+                if record:
+                    for a, ln in rec:
+                        a, ln = a.cpu().numpy(), ln.cpu().numpy()
+                        for i, b in enumerate(active):
+                            if done_len[b] < n_out[b]:
+                                accs[b].append(int(a[i]))
+                                done_len[b] = ln[i]
+                lens = out_len.cpu().numpy()
+                if (lens >= n_out[active]).any():
+                    break
+            full[torch.from_numpy(active).to(self.device)] = out_t
+            active = active[lens < n_out[active]]
+        host = full.cpu().numpy()
+        return [host[b, :n_out[b]] for b in range(B)], (accs if record else None), seq_steps
+

@@ -17,12 +17,13 @@ def log(*a):
     sys.stdout.flush()
 
 
-def make_pair(cfg, wseed, max_batch=1, max_k=3, max_positions=512, cache_dense=True):
+def make_pair(cfg, wseed, max_batch=1, max_k=3, max_positions=512, cache_dense=True, path=0):
     import torch
     from speculative_moe_decoding_amd import ocrdec
     t = time.time()
     w = synth.Weights(cfg, wseed)
-    dec = ocrdec.Decoder(cfg, w.device_arrays(), max_batch=max_batch, max_k=max_k, max_positions=max_positions)
+    dec = ocrdec.Decoder(cfg, w.device_arrays(), max_batch=max_batch, max_k=max_k, max_positions=max_positions,
+                         path=path)
     orc = od.Oracle(cfg, w.f32, cache_dense=cache_dense)
     torch.cuda.synchronize()
     log(f"weights + upload for {cfg.n_layers} layers / V={cfg.vocab} / {cfg.dtype}: {time.time() - t:.1f}s")
