@@ -324,30 +324,56 @@ class Decoder:
             acc = [a[:int(np.argmax(ln[:, b] >= n_out)) + 1, b].tolist() for b in range(B)]
         return toks, acc, steps
 
+    def _ragged_buffers(self, B: int, K: int, cap: int, T: int):
+        """Per-shape scratch of generate_ragged, kept so that repeated runs pass the same
+        pointers (the decode-step graphs are cached by call shape and pointers)."""
+        key = (B, K, cap, T)
+        if not hasattr(self, "_rag"):
+            self._rag = {}
+        if key not in self._rag:
+            torch = self.torch
+            self._rag[key] = dict(
+                slots=self.i32(B), out=torch.zeros(B, cap, dtype=torch.int32, device=self.device),
+                trace=torch.zeros(B, max(T, 1), dtype=torch.int32, device=self.device),
+                out_len=self.i32(B), n_acc=self.i32(B), draft=self.i32(B, max(K, 1)), greedy=self.i32(B, K + 1))
+        return self._rag[key]
+
     def generate_ragged(self, pages, n_out, K: int, trace=None, seed: int = 0, threshold: int = 0,
-                        check_every: int = 8, record: bool = False, graphs: bool = False):
+                        check_every: int = 8, record: bool = False, graphs: bool = False, timer=None):
         """Static batch with per-sequence output lengths: sequence b (slot b) leaves the
         batch once it has n_out[b] tokens; the others go on (no refill).  ``trace``
-        (device int32 [B, T]) switches on the controlled drafts.  Returns (list of token
+        (device int32 [B, T]) switches on the controlled drafts.  ``timer`` (optional
+        callable) is called after the prefill, synchronised.  Returns (list of token
         arrays, per-sequence accepted lengths of the steps up to n_out[b] if record, total
         sequence-steps run)."""
         torch = self.torch
         B = len(pages)
         n_out = np.asarray(n_out, dtype=np.int64)
         cap = int(n_out.max()) + self.max_k + 2
+        T = 0 if trace is None else int(trace.shape[1])
+        buf = self._ragged_buffers(B, K, cap, T)
         full = torch.zeros(B, cap, dtype=torch.int32, device=self.device)
         full[:, 0] = self.prefill(pages)
+        if timer is not None:
+            torch.cuda.synchronize()
+            timer()
         active = np.arange(B)
         accs = [[] for _ in range(B)]
         done_len = np.ones(B, dtype=np.int64)
         seq_steps = 0
         while len(active):
             Bb = len(active)
-            slots = torch.from_numpy(active.astype(np.int32)).to(self.device)
-            out_t = full[torch.from_numpy(active).to(self.device)].contiguous()
-            tr = None if trace is None else trace[torch.from_numpy(active).to(self.device)].contiguous()
-            out_len, n_acc = self.i32(Bb), self.i32(Bb)
-            draft, greedy = self.i32(Bb, max(K, 1)), self.i32(Bb, K + 1)
+            idx = torch.from_numpy(active).to(self.device)
+            slots = buf["slots"][:Bb]
+            slots.copy_(idx.to(torch.int32))
+            out_t = buf["out"][:Bb]
+            out_t.copy_(full[idx])
+            tr = None
+            if trace is not None:
+                tr = buf["trace"][:Bb]
+                tr.copy_(trace[idx])
+            out_len, n_acc = buf["out_len"][:Bb], buf["n_acc"][:Bb]
+            draft, greedy = buf["draft"][:Bb], buf["greedy"][:Bb]
             while True:
                 rec = []
                 if graphs and K > 0 and not record:
@@ -374,8 +400,7 @@ class Decoder:
                 lens = out_len.cpu().numpy()
                 if (lens >= n_out[active]).any():
                     break
-            full[torch.from_numpy(active).to(self.device)] = out_t
+            full[idx] = out_t
             active = active[lens < n_out[active]]
         host = full.cpu().numpy()
         return [host[b, :n_out[b]] for b in range(B)], (accs if record else None), seq_steps
-
