@@ -164,6 +164,13 @@ int ocrdec_decode_steps(ocrdec_model* m, void* stream, int B, const int32_t* slo
                         const ocrdec_controlled_cfg* ctrl, int32_t* draft, int32_t* greedy,
                         int32_t* n_accepted_out, int32_t* out_tokens, int32_t* out_len, int out_cap);
 
+/* Position bookkeeping: between synchronisations the host assumes that every
+ * step commits K + 1 tokens (an upper bound that sizes the attention grids and
+ * the OCRDEC_ECAPACITY checks).  This call synchronises `stream` and resets the
+ * bound of every slot to its true cache length, so long generations are not
+ * refused early.  Returns OCRDEC_EHIP if the read fails. */
+int ocrdec_sync_positions(ocrdec_model* m, void* stream);
+
 /* Parity taps (nullable device pointers, used by later verify/prefill calls):
  * route_idx int32 [n_layers][rows][8] receives each layer's routing (6 routed
  * experts by decreasing score, then the shared experts 64, 65); hidden fp32

@@ -646,6 +646,17 @@ int ocrdec_decode_steps(ocrdec_model* m, void* stream, int B, const int32_t* slo
   return OCRDEC_OK;
 }
 
+int ocrdec_sync_positions(ocrdec_model* m, void* stream) {
+  if (!m) return fail(OCRDEC_EINVAL, "model is null");
+  const int n = m->cfg.max_batch;
+  std::vector<int> kv(n);
+  if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess ||
+      hipMemcpy(kv.data(), m->sv.kv_len, (size_t)n * sizeof(int), hipMemcpyDeviceToHost) != hipSuccess)
+    return fail(OCRDEC_EHIP, "reading the cache lengths failed");
+  for (int i = 0; i < n; ++i) m->slot_bound[i] = std::max(0, std::min(kv[i], m->cfg.max_positions));
+  return OCRDEC_OK;
+}
+
 int ocrdec_set_taps(ocrdec_model* m, int32_t* route_idx, float* hidden) {
   if (!m) return fail(OCRDEC_EINVAL, "model is null");
   m->tap_route = route_idx;

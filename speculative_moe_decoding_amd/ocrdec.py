@@ -23,7 +23,7 @@ SYMBOLS = (
     "ocrdec_state_bytes", "ocrdec_workspace_bytes", "ocrdec_num_weights", "ocrdec_create", "ocrdec_destroy",
     "ocrdec_prefill", "ocrdec_draft", "ocrdec_verify", "ocrdec_accept_rollback", "ocrdec_controlled_drafts",
     "ocrdec_set_taps", "ocrdec_expert_timing", "ocrdec_expert_stats", "ocrdec_replay_expert_gate_up",
-    "ocrdec_decode_steps", "ocrdec_last_error",
+    "ocrdec_decode_steps", "ocrdec_sync_positions", "ocrdec_last_error",
 )
 
 
@@ -77,6 +77,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                     ctypes.POINTER(ctypes.c_longlong)]),
         "ocrdec_replay_expert_gate_up": (I, [P, P, I, ctypes.POINTER(I)]),
         "ocrdec_decode_steps": (I, [P, P, I, P, I, I, ctypes.POINTER(ocrdec_controlled_cfg), P, P, P, P, P, I]),
+        "ocrdec_sync_positions": (I, [P, P]),
         "ocrdec_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -155,6 +156,10 @@ def ocrdec_accept_rollback(h, stream, B, slots, K, draft, greedy, n_accepted_out
 def ocrdec_controlled_drafts(h, stream, B, slots, K, trace, trace_stride, trace_len, seed, threshold, draft_inout):
     _check("ocrdec_controlled_drafts", load_library().ocrdec_controlled_drafts(
         h, stream, B, _ptr(slots), K, _ptr(trace), trace_stride, trace_len, seed, threshold, _ptr(draft_inout)))
+
+
+def ocrdec_sync_positions(h, stream: int):
+    _check("ocrdec_sync_positions", load_library().ocrdec_sync_positions(h, stream))
 
 
 def ocrdec_set_taps(h, route_idx=None, hidden=None):
@@ -299,6 +304,7 @@ class Decoder:
                 self.decode_steps(B, K, check_every, draft, greedy, n_acc, out_tokens, out_len, trace, seed,
                                   threshold)
                 steps += check_every
+                ocrdec_sync_positions(self.h, self.stream)
                 if int(out_len.min().item()) >= n_out:
                     break
                 continue
@@ -313,6 +319,7 @@ class Decoder:
                 if record:
                     accs.append(n_acc.clone())
                     lens.append(out_len.clone())
+            ocrdec_sync_positions(self.h, self.stream)
             if int(out_len.min().item()) >= n_out:
                 break
         toks = out_tokens[:, :n_out].cpu().numpy()
@@ -397,6 +404,7 @@ class Decoder:
                             if done_len[b] < n_out[b]:
                                 accs[b].append(int(a[i]))
                                 done_len[b] = ln[i]
+                ocrdec_sync_positions(self.h, self.stream)
                 lens = out_len.cpu().numpy()
                 if (lens >= n_out[active]).any():
                     break

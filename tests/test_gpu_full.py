@@ -8,6 +8,8 @@
   AR output for the real draft and for the controlled-acceptance drafts at
   K = 1, 2, 3, with accepted lengths equal to the oracle's prediction, in the
   launch configuration bench.py times (batch 1, one stream, eager).
+* Gundam page (1,156 + 32 prefix, 3,568 tokens, cache past 4,096 positions):
+  lossless with graphs, accepted lengths, first steps against the oracle.
 """
 import dataclasses
 import time
@@ -99,3 +101,46 @@ def test_full_model_lossless(full):
     toks, acc, _ = dec.generate([page], 96, 3, record=True, check_every=4)
     assert toks[0].tolist() == ar[0][:96].tolist()
     log(f"real draft K=3: lossless; accepted {acc[0][:20]}")
+
+
+def test_gundam_page_lossless(full):
+    """Gundam-mode page: 1,156 vision + 32 prompt rows, 3,568 output tokens, K = 3
+    at 57.6 % controlled acceptance, so the cache grows from 1,188 to 4,756
+    positions (a handle past 4,096 positions uses 256-key attention chunks).
+    The whole page is lossless against the K = 0 run (decode-step graphs);
+    accepted lengths equal the SplitMix64 prediction over the first 600 tokens;
+    the first decode steps agree with the oracle."""
+    w, _, orc, _ = full
+    wl = synth.WORKLOADS["gundam_page_bf16"]
+    cfg = wl["cfg"]
+    from speculative_moe_decoding_amd import ocrdec
+    page = synth.make_pages(cfg, wl["input_seed"], [wl["n_vision"]], [wl["n_prompt"]], [wl["n_out"]])[0]
+    N = wl["n_out"]
+    P = page.prefix_len
+    dec = ocrdec.Decoder(cfg, w.device_arrays(), max_batch=1, max_k=3, max_positions=P + N + 160)
+    t = time.time()
+    ar, _, _ = dec.generate([page], N + 8, 0, check_every=64)
+    log(f"Gundam page: GPU AR {N + 8} tokens in {time.time() - t:.1f}s")
+    trace = torch.from_numpy(ar.astype(np.int32)).cuda()
+    p = synth.replacement_probability(0.576, 3)
+    thr = od.replace_threshold(p)
+    t = time.time()
+    toks, _, steps = dec.generate([page], N, 3, trace=trace, seed=3000, threshold=thr, check_every=16, graphs=True)
+    assert toks[0].tolist() == ar[0][:N].tolist()
+    log(f"Gundam page K=3 graphs: lossless over {N} tokens, {steps} steps, {time.time() - t:.1f}s")
+    n_rec = 600
+    toks, acc, _ = dec.generate([page], n_rec, 3, trace=trace, seed=3000, threshold=thr, record=True, check_every=8)
+    assert toks[0].tolist() == ar[0][:n_rec].tolist()
+    assert acc[0] == od.controlled_accepts(n_rec, 3, 3000, p)
+    n_chk = 4
+    _, g_steps = run_gpu_steps(dec, page, n_chk, 0)
+    t = time.time()
+    r_ar, r_logits = orc.generate_ar(page.vision, page.prompt, n_chk, keep_logits=True)
+    log(f"oracle 12-layer {P}-row prefill + {n_chk} tokens: {time.time() - t:.1f}s")
+    if int(ar[0][0]) != r_ar[0]:
+        assert od.top2_margin(r_logits[0]) < 5e-2, "first token differs without a near tie"
+        return
+    ref = [od.StepRecord(0, [], [r_ar[i + 1]], 0, r_logits[i + 1][None]) for i in range(n_chk - 1)]
+    n, worst, note = compare_steps(g_steps, ref, 5e-2)
+    log(f"Gundam page vs oracle: {n}/{n_chk - 1} steps agree, max |dlogit| {worst:.3e}, {note}")
+    assert worst < 5e-2
