@@ -112,9 +112,11 @@ def main() -> int:
     ap.add_argument("--replay-rounds", type=int, default=40)
     ap.add_argument("--eager", action="store_true", help="issue the four calls per step instead of graph replays")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="base_page_bf16", choices=["base_page_bf16", "concurrent32_bf16"],
+    ap.add_argument("--workload", default="base_page_bf16",
+                    choices=["base_page_bf16", "concurrent32_bf16", "longctx_layer_bf16"],
                     help="base_page_bf16 (default): batch 1, K=3; concurrent32_bf16: static batch of 32 "
-                         "pages, K=1, on the matrix-core path")
+                         "pages, K=1, on the matrix-core path; longctx_layer_bf16: one MoE layer + LM head "
+                         "verifying 4 rows per sequence over 32,764 cached positions, B = 1, 4, 16, 64")
     ap.add_argument("--out-scale", type=float, default=1.0,
                     help="concurrent32_bf16: scale of the per-page output lengths")
     ap.add_argument("--copy-probe", action="store_true",
@@ -138,6 +140,8 @@ def main() -> int:
 
     if args.workload == "concurrent32_bf16":
         return bench_concurrent(args)
+    if args.workload == "longctx_layer_bf16":
+        return bench_longctx(args)
 
     import numpy as np
     import torch
@@ -455,6 +459,90 @@ def bench_concurrent(args) -> int:
         "decode_s": round(t_decode, 3),
         "lossless_vs_ar": bool(lossless),
         "expert_down_avg_launch_us": round(dn_us, 2),
+        "cpu_baseline": None,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def bench_longctx(args) -> int:
+    """One MoE layer + final norm + LM head verifying 4 rows per sequence at
+    positions 32,764..32,767 over a loaded cache (keys / values ~ N(0, 1) bf16),
+    router logits = log pi + Gumbel with pi ~ rank^-1.1 (skewed expert load).
+    Per batch size: verify-call time (HIP events around back-to-back calls), its
+    algorithmic HBM bytes and rate, and the expert kernels' rates."""
+    import numpy as np
+    import torch
+    from speculative_moe_decoding_amd import ocrdec, synth
+
+    wl = synth.WORKLOADS["longctx_layer_bf16"]
+    cfg, K = wl["cfg"], 3
+    n_pos = wl["n_cached"]
+    w = synth.Weights(cfg, wl["weight_seed"])
+    t = time.time()
+    kv = torch.from_numpy(synth.longctx_kv(cfg, wl["kv_seed"], n_pos).view(np.int16)).cuda()
+    log(f"cache of {n_pos} positions generated in {time.time() - t:.1f}s")
+    rows_out = []
+    reps = max(4, min(args.steps, 20))
+    for B in wl["batches"]:
+        dec = ocrdec.Decoder(cfg, w.device_arrays(), max_batch=B, max_k=K, max_positions=n_pos + K + 1)
+        rng = np.random.default_rng([wl["input_seed"], B])
+        for b in range(B):
+            ocrdec.ocrdec_load_sequence(dec.h, dec.stream, b, n_pos, int(rng.integers(0, cfg.vocab)), kv)
+        rl = torch.from_numpy(synth.zipf_router_logits(wl["input_seed"] + B, B * (K + 1))).cuda()
+        ocrdec.ocrdec_set_router_logits(dec.h, rl)
+        draft = torch.from_numpy(rng.integers(0, cfg.vocab, size=(B, K)).astype(np.int32)).cuda()
+        greedy = dec.i32(B, K + 1)
+        for _ in range(3):
+            dec.verify(B, K, draft, greedy=greedy)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            dec.verify(B, K, draft, greedy=greedy)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        ocrdec.ocrdec_expert_timing(dec.h, True)
+        for _ in range(reps):
+            dec.verify(B, K, draft, greedy=greedy)
+        st = ocrdec.ocrdec_expert_stats(dec.h)
+        ocrdec.ocrdec_expert_timing(dec.h, False)
+        U = st["expert_sets"] / max(1, st["n_gate_up"])
+        M = B * (K + 1)
+        pairs = 8 * M
+        kv_bytes = B * (n_pos * KV_POS_BYTES + (K + 1) * KV_POS_BYTES)
+        nbytes = DENSE_LAYER_BYTES + U * 3 * I * D * 2 + LM_HEAD_BYTES + kv_bytes
+        up_us = st["ms_gate_up"] / max(1, st["n_gate_up"]) * 1e3
+        dn_us = st["ms_down"] / max(1, st["n_down"]) * 1e3
+        flops = 2.0 * pairs * 3 * I * D
+        row = {"B": B, "rows": M, "path": "matrix" if M > 8 else "vector", "verify_ms": round(ms, 4),
+               "GB_per_call": round(nbytes / 1e9, 4), "GB_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+               "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+               "kv_GB": round(kv_bytes / 1e9, 4), "active_experts": round(U, 2),
+               "expert_gate_up_us": round(up_us, 2), "expert_down_us": round(dn_us, 2),
+               "expert_GB_per_s": round(U * 3 * I * D * 2 / ((up_us + dn_us) * 1e-6) / 1e9, 1),
+               "expert_TFLOP_per_s": round(flops / ((up_us + dn_us) * 1e-6) / 1e12, 2),
+               "expert_frac_of_bf16_mfma_peak": round(flops / ((up_us + dn_us) * 1e-6) / 2.5e15, 4)}
+        rows_out.append(row)
+        log(json.dumps(row))
+        ocrdec.ocrdec_set_router_logits(dec.h, None)
+        dec.close()
+        del dec
+        torch.cuda.empty_cache()
+    best = max(rows_out, key=lambda r: r["GB_per_s"])
+    result = {
+        "metric": "verify-call HBM rate, one MoE layer + LM head over 32,768 positions (bf16)",
+        "value": best["GB_per_s"], "unit": "GB/s", "n_gpus": 1, "steps": reps, "warmup": 3,
+        "ms_per_step": best["verify_ms"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "longctx_layer_bf16: 1 MoE layer + final norm + LM head, 4 query rows per "
+                               "sequence at positions 32764..32767, cache ~N(0,1) bf16, router logits "
+                               "log pi + Gumbel with pi ~ rank^-1.1", "batches": list(wl["batches"])},
+        "roofline": {"bound": "hbm", "achieved": best["GB_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(best["GB_per_s"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": f"whole verify call at B={best['B']}"},
+        "batches": rows_out,
         "cpu_baseline": None,
     }
     print(json.dumps(result), flush=True)

@@ -171,6 +171,20 @@ int ocrdec_decode_steps(ocrdec_model* m, void* stream, int B, const int32_t* slo
  * refused early.  Returns OCRDEC_EHIP if the read fails. */
 int ocrdec_sync_positions(ocrdec_model* m, void* stream);
 
+/* Long-context benchmark harness (not part of the method).
+ * ocrdec_load_sequence: fill slot `slot` with a caller-made verifier cache of
+ * n_pos positions -- kv: device, model dtype, [n_layers][K|V][head][n_pos][128]
+ * (keys already rotated) -- and make pending_token the token at position
+ * n_pos, as a prefill would (the draft cache is not filled).  Errors:
+ * OCRDEC_EINVAL for a bad slot / token / null pointer, OCRDEC_ECAPACITY if
+ * n_pos + max_k + 1 > max_positions.
+ * ocrdec_set_router_logits: later verify calls take each layer's router logits
+ * from logits (device fp32 [n_layers][rows][64], rows = B*(K+1) of the call;
+ * the caller keeps it alive) instead of the router weights; NULL restores the
+ * router. */
+int ocrdec_load_sequence(ocrdec_model* m, void* stream, int slot, int n_pos, int pending_token, const void* kv);
+int ocrdec_set_router_logits(ocrdec_model* m, const float* logits);
+
 /* Parity taps (nullable device pointers, used by later verify/prefill calls):
  * route_idx int32 [n_layers][rows][8] receives each layer's routing (6 routed
  * experts by decreasing score, then the shared experts 64, 65); hidden fp32

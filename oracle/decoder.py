@@ -112,14 +112,14 @@ def softmax(z: np.ndarray) -> np.ndarray:
     return e / e.sum(axis=-1, keepdims=True)
 
 
-def route(b: np.ndarray, W_r: np.ndarray, top_k: int):
-    """Softmax top-k router.
+def route_logits(logits: np.ndarray, top_k: int):
+    """Softmax top-k selection from router logits [T, E].
 
-    Returns (idx [T, k] int, gate [T, k] float64, logits [T, E] float64).
-    idx lists the chosen experts by decreasing score; the choice is made on the
-    float32 rounding of the logits with ties going to the lower expert index.
-    gate is the softmax probability over all routed experts (not renormalised)."""
-    logits = linear(b, W_r)
+    Returns (idx [T, k] int, gate [T, k] float64).  idx lists the chosen experts
+    by decreasing score; the choice is made on the float32 rounding of the
+    logits with ties going to the lower expert index.  gate is the softmax
+    probability over all routed experts (not renormalised)."""
+    logits = np.asarray(logits, F64)
     lf = logits.astype(np.float32).astype(F64)
     E = logits.shape[-1]
     idx = np.empty((logits.shape[0], top_k), dtype=np.int64)
@@ -128,6 +128,14 @@ def route(b: np.ndarray, W_r: np.ndarray, top_k: int):
         idx[t] = order[:top_k]
     probs = softmax(logits)
     gate = np.take_along_axis(probs, idx, axis=-1)
+    return idx, gate
+
+
+def route(b: np.ndarray, W_r: np.ndarray, top_k: int):
+    """Softmax top-k router: route_logits of the logits W_r b.
+    Returns (idx, gate, logits)."""
+    logits = linear(b, W_r)
+    idx, gate = route_logits(logits, top_k)
     return idx, gate, logits
 
 
@@ -142,12 +150,17 @@ def swiglu(b: np.ndarray, W_g: np.ndarray, W_u: np.ndarray, W_d: np.ndarray) -> 
     return linear(silu(linear(b, W_g)) * linear(b, W_u), W_d)
 
 
-def moe(b: np.ndarray, W_r, W_g, W_u, W_d, n_experts: int, n_shared: int, top_k: int):
+def moe(b: np.ndarray, W_r, W_g, W_u, W_d, n_experts: int, n_shared: int, top_k: int, router_logits=None):
     """y = sum_shared F_s(b) + sum_{j<k} gate_j F_{idx_j}(b).
 
-    Expert tensors hold the routed experts first, then the shared ones."""
+    Expert tensors hold the routed experts first, then the shared ones.  With
+    router_logits [T, E] given, the routing is taken from them instead of W_r b
+    (the long-context benchmark's synthetic skewed routing)."""
     b = np.asarray(b, F64)
-    idx, gate, _ = route(b, W_r, top_k)
+    if router_logits is None:
+        idx, gate, _ = route(b, W_r, top_k)
+    else:
+        idx, gate = route_logits(router_logits, top_k)
     y = np.zeros_like(b)
     for s in range(n_shared):
         e = n_experts + s
@@ -281,9 +294,11 @@ class Oracle:
         o = causal_attention(q, K_cache[:L], V_cache[:L], pos)
         return x + linear(o.reshape(T, Hd), self.W(wo))
 
-    def verifier_forward(self, st: "SeqState", x_in: np.ndarray, pos: Sequence[int], record=None):
+    def verifier_forward(self, st: "SeqState", x_in: np.ndarray, pos: Sequence[int], record=None,
+                         router_logits=None):
         """Rows x_in [T, d] at consecutive positions ``pos`` through all layers.
-        Returns the pre-norm final hidden [T, d]."""
+        Returns the pre-norm final hidden [T, d].  router_logits (optional
+        [n_layers][T][E]) replaces each layer's router logits."""
         c = self.cfg
         x = np.asarray(x_in, F64).copy()
         pos = np.asarray(pos, dtype=np.int64)
@@ -292,7 +307,8 @@ class Oracle:
                                      st.kv[l, 0], st.kv[l, 1])
             b = rmsnorm(x, self.w[f"l{l}.ffn_norm"], c.norm_eps)
             y, idx = moe(b, self.W(f"l{l}.router"), self.w[f"l{l}.w_gate"], self.w[f"l{l}.w_up"],
-                         self.w[f"l{l}.w_down"], c.n_experts, c.n_shared, c.top_k)
+                         self.w[f"l{l}.w_down"], c.n_experts, c.n_shared, c.top_k,
+                         None if router_logits is None else router_logits[l])
             if record is not None:
                 record.append(idx)
             x = x + y

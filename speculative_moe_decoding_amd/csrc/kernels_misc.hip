@@ -179,6 +179,23 @@ __global__ void k_prefill_finish(int slot, int P, const float* __restrict__ xlas
   for (int k = threadIdx.x; k < D; k += 256) hb[k] = xlast[k];
 }
 
+// A slot whose verifier cache was loaded by the caller: P cached positions,
+// pending token tok, no draft history (its hidden-state feedback row is zero).
+__global__ void k_set_sequence(int slot, int P, int tok, StateView sv) {
+  if (threadIdx.x == 0) {
+    sv.kv_len[slot] = P;
+    sv.draft_len[slot] = P;
+    sv.pending[slot] = tok;
+    sv.n_prev[slot] = 0;
+    sv.out_len[slot] = 1;
+    sv.step[slot] = 0;
+    sv.prefix_len[slot] = P;
+    sv.cu_tok[slot * sv.cu_stride] = tok;
+  }
+  float* hb = sv.hbuf + (long)slot * sv.cu_stride * D;
+  for (int k = threadIdx.x; k < D; k += 256) hb[k] = 0.f;
+}
+
 // Greedy longest-prefix acceptance (one block per sequence).
 __global__ __launch_bounds__(256) void k_accept(int K, const int* __restrict__ plan_slot,
                                                 const int* __restrict__ draft, const int* __restrict__ greedy,
@@ -287,6 +304,9 @@ void launch_draft_prefill_cat(hipStream_t s, int c, const float* xfinal, const f
 void launch_prefill_finish(hipStream_t s, int slot, int P, const float* xlast, const int* pending_tok,
                            StateView sv) {
   hipLaunchKernelGGL(k_prefill_finish, dim3(1), dim3(256), 0, s, slot, P, xlast, pending_tok, sv);
+}
+void launch_set_sequence(hipStream_t s, int slot, int P, int tok, StateView sv) {
+  hipLaunchKernelGGL(k_set_sequence, dim3(1), dim3(256), 0, s, slot, P, tok, sv);
 }
 void launch_accept(hipStream_t s, int B, int K, const int* plan_slot, const int* draft, const int* greedy,
                    const float* xfinal, StateView sv, int* n_acc, int* out_tokens, int* out_len_out, int out_cap) {

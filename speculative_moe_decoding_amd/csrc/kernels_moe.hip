@@ -268,7 +268,7 @@ int expert_slot_cap(int M) { return min(NE, TOPK * M) + NSH; }
 // for M <= 8, a per-row kernel and a sort kernel beyond).
 template <typename T>
 void launch_router(hipStream_t s, const float* x, const float* gain, float eps, const T* wr, int M,
-                   const MoeBufs& mb, int* tap) {
+                   const MoeBufs& mb, int* tap, const float* logit_override) {
 #define OCR_RL_CASE(MRV)                                                                                   \
   hipLaunchKernelGGL((k_router_logits<T, MRV>), dim3(NE / 4, (M + MRV - 1) / MRV), dim3(256),              \
                      (size_t)MRV * D * 4, s, x, gain, eps, wr, M, mb.bnorm, mb.rlogit);
@@ -277,6 +277,7 @@ void launch_router(hipStream_t s, const float* x, const float* gain, float eps, 
   else if (M <= 4) OCR_RL_CASE(4)
   else OCR_RL_CASE(MRG)
 #undef OCR_RL_CASE
+  if (logit_override != nullptr) launch_copy_rows(s, logit_override, mb.rlogit, (long)M * NE);
   if (M <= MRG) {
     hipLaunchKernelGGL(k_route_small, dim3(1), dim3(256), 0, s, mb.rlogit, M, mb, tap);
   } else {
@@ -524,7 +525,7 @@ void launch_moe_combine(hipStream_t s, float* x, int M, const MoeBufs& mb) {
 
 #define OCR_INST_MOE(T)                                                                                  \
   template void launch_router<T>(hipStream_t, const float*, const float*, float, const T*, int,          \
-                                 const MoeBufs&, int*);                                                  \
+                                 const MoeBufs&, int*, const float*);                                    \
   template void launch_expert_gate_up<T>(hipStream_t, const T*, const T*, int, const MoeBufs&, int*);          \
   template void launch_expert_down<T>(hipStream_t, const T*, int, const MoeBufs&);
 OCR_INST_MOE(float)

@@ -56,9 +56,11 @@ struct MoeBufs {
   float* y;       // [8M][D]
 };
 
+// Router logits (rlogit) and the routing tables; logit_override (nullable,
+// [M][64]) replaces the computed logits before the top-6.
 template <typename T>
 void launch_router(hipStream_t s, const float* x, const float* gain, float eps, const T* wr, int M,
-                   const MoeBufs& mb, int* tap);
+                   const MoeBufs& mb, int* tap, const float* logit_override);
 template <typename T>
 void launch_expert_gate_up(hipStream_t s, const T* wg, const T* wu, int M, const MoeBufs& mb, int* tap);
 template <typename T>
@@ -105,6 +107,7 @@ void launch_draft_prefill_cat(hipStream_t s, int c, const float* xfinal, const f
                               float* cat);
 void launch_prefill_finish(hipStream_t s, int slot, int P, const float* xlast, const int* pending_tok,
                            StateView sv);
+void launch_set_sequence(hipStream_t s, int slot, int P, int tok, StateView sv);
 void launch_accept(hipStream_t s, int B, int K, const int* plan_slot, const int* draft, const int* greedy,
                    const float* xfinal, StateView sv, int* n_acc, int* out_tokens, int* out_len_out,
                    int out_cap);

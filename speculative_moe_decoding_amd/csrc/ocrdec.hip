@@ -143,6 +143,7 @@ struct ocrdec_model {
   long long stats_base;        // device expert counter when timing was enabled
   int last_verify_rows;        // M of the last verify call (0 before any)
   bool matrix;                 // experts and LM head on the matrix cores
+  const float* router_override;  // [n_layers][M][64] router logits for verify calls, or null
   hipStream_t capture_stream;  // private stream the decode-step graphs are recorded on
   std::map<std::vector<uintptr_t>, hipGraphExec_t> graphs;  // by call shape
 };
@@ -228,7 +229,8 @@ void lm_head(ocrdec_model* m, hipStream_t s, const float* x, int Q, bool last_va
 }
 
 template <typename T>
-void verifier_layers(ocrdec_model* m, hipStream_t s, int M, int B, RowPlan plan, int nch, bool taps) {
+void verifier_layers(ocrdec_model* m, hipStream_t s, int M, int B, RowPlan plan, int nch, bool taps,
+                     const float* rlog) {
   const ocrdec_config& c = m->cfg;
   for (int l = 0; l < c.n_layers; ++l) {
     T* kvl = static_cast<T*>((void*)(m->state + m->p.s_kv)) + (size_t)l * m->p.kv_layer_elems;
@@ -239,7 +241,7 @@ void verifier_layers(ocrdec_model* m, hipStream_t s, int M, int B, RowPlan plan,
                    m->x, D);
     int* tap = (taps && m->tap_route) ? m->tap_route + (size_t)l * M * NSLOT : nullptr;
     launch_router<T>(s, m->x, wvec(m, lw(m, l, L_FNORM)), c.norm_eps, wmat<T>(m, lw(m, l, L_ROUTER)), M, m->mb,
-                     tap);
+                     tap, rlog ? rlog + (size_t)l * M * NE : nullptr);
     timing_mark(m, s);
     expert_gate_up<T>(m, s, l, M, tap);
     timing_mark(m, s);
@@ -284,7 +286,7 @@ int do_prefill(ocrdec_model* m, hipStream_t s, int B, const int32_t* slots_host,
                              m->plan_slot, m->x, m->esave);
       RowPlan plan{m->plan_base, m->plan_cnt, m->plan_slot, cc};
       const int nch = chunks_for(m, p0 + cc - 1);
-      verifier_layers<T>(m, s, cc, 1, plan, nch, false);
+      verifier_layers<T>(m, s, cc, 1, plan, nch, false, nullptr);
       if (p0 + cc == P)
         lm_head<T>(m, s, m->x, cc, true, wvec(m, W_FNORM), 1, nullptr, m->tok_tmp, 1);
       launch_draft_prefill_cat(s, cc, m->x, m->esave, m->hsave[par], m->hsave[1 - par], wvec(m, dw(m, D_NH)),
@@ -334,7 +336,7 @@ int do_verify(ocrdec_model* m, hipStream_t s, int B, const int32_t* slots, int K
   launch_plan_verify<T>(s, B, K, slots, m->sv, draft, wmat<T>(m, W_EMBED), c.vocab, m->plan_base, m->plan_cnt,
                         m->plan_slot, m->x);
   RowPlan plan{m->plan_base, m->plan_cnt, m->plan_slot, Q};
-  verifier_layers<T>(m, s, M, B, plan, nch, true);
+  verifier_layers<T>(m, s, M, B, plan, nch, true, m->router_override);
   m->last_verify_rows = M;
   lm_head<T>(m, s, m->x, Q, false, wvec(m, W_FNORM), M, logits_out, greedy_out, 1);
   if (m->tap_hidden) launch_copy_rows(s, m->x, m->tap_hidden, (long)M * D);
@@ -452,6 +454,7 @@ int ocrdec_create(const ocrdec_config* cfg, const void* const* weight_ptrs, int 
   m->stats_base = 0;
   m->last_verify_rows = 0;
   m->matrix = use_matrix_path(cfg);
+  m->router_override = nullptr;
   m->capture_stream = nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // clear an error left by earlier, unrelated runtime calls
@@ -655,6 +658,37 @@ int ocrdec_sync_positions(ocrdec_model* m, void* stream) {
     return fail(OCRDEC_EHIP, "reading the cache lengths failed");
   for (int i = 0; i < n; ++i) m->slot_bound[i] = std::max(0, std::min(kv[i], m->cfg.max_positions));
   return OCRDEC_OK;
+}
+
+int ocrdec_set_router_logits(ocrdec_model* m, const float* logits) {
+  if (!m) return fail(OCRDEC_EINVAL, "model is null");
+  m->router_override = logits;
+  return OCRDEC_OK;
+}
+
+int ocrdec_load_sequence(ocrdec_model* m, void* stream, int slot, int n_pos, int pending_token, const void* kv) {
+  (void)hipGetLastError();
+  if (!m || !kv) return fail(OCRDEC_EINVAL, "model or kv is null");
+  if (slot < 0 || slot >= m->cfg.max_batch) return fail(OCRDEC_EINVAL, "slot out of range");
+  if (n_pos < 1 || n_pos + m->cfg.max_k + 1 > m->cfg.max_positions)
+    return fail(OCRDEC_ECAPACITY, "n_pos + max_k + 1 exceeds max_positions");
+  if (pending_token < 0 || pending_token >= m->cfg.vocab) return fail(OCRDEC_EINVAL, "pending_token out of range");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t esz = m->p.esz, mp = (size_t)m->cfg.max_positions;
+  const char* src = static_cast<const char*>(kv);
+  for (int l = 0; l < m->cfg.n_layers; ++l) {
+    char* dst = m->state + m->p.s_kv + ((size_t)l * m->p.kv_layer_elems + (size_t)slot * 2 * NH * mp * HD) * esz;
+    // [K|V][head] planes: n_pos rows of HD in the source, max_positions rows in the cache
+    for (int j = 0; j < 2 * NH; ++j) {
+      const hipError_t e = hipMemcpyAsync(dst + (size_t)j * mp * HD * esz,
+                                          src + (((size_t)l * 2 * NH + j) * n_pos) * HD * esz,
+                                          (size_t)n_pos * HD * esz, hipMemcpyDeviceToDevice, s);
+      if (e != hipSuccess) return fail(OCRDEC_EHIP, std::string("hipMemcpyAsync: ") + hipGetErrorString(e));
+    }
+  }
+  launch_set_sequence(s, slot, n_pos, pending_token, m->sv);
+  m->slot_bound[slot] = n_pos;
+  return hip_check("ocrdec_load_sequence");
 }
 
 int ocrdec_set_taps(ocrdec_model* m, int32_t* route_idx, float* hidden) {

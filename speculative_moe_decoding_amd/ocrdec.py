@@ -23,7 +23,8 @@ SYMBOLS = (
     "ocrdec_state_bytes", "ocrdec_workspace_bytes", "ocrdec_num_weights", "ocrdec_create", "ocrdec_destroy",
     "ocrdec_prefill", "ocrdec_draft", "ocrdec_verify", "ocrdec_accept_rollback", "ocrdec_controlled_drafts",
     "ocrdec_set_taps", "ocrdec_expert_timing", "ocrdec_expert_stats", "ocrdec_replay_expert_gate_up",
-    "ocrdec_decode_steps", "ocrdec_sync_positions", "ocrdec_last_error",
+    "ocrdec_decode_steps", "ocrdec_sync_positions", "ocrdec_load_sequence", "ocrdec_set_router_logits",
+    "ocrdec_last_error",
 )
 
 
@@ -78,6 +79,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "ocrdec_replay_expert_gate_up": (I, [P, P, I, ctypes.POINTER(I)]),
         "ocrdec_decode_steps": (I, [P, P, I, P, I, I, ctypes.POINTER(ocrdec_controlled_cfg), P, P, P, P, P, I]),
         "ocrdec_sync_positions": (I, [P, P]),
+        "ocrdec_load_sequence": (I, [P, P, I, I, I, P]),
+        "ocrdec_set_router_logits": (I, [P, P]),
         "ocrdec_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -160,6 +163,15 @@ def ocrdec_controlled_drafts(h, stream, B, slots, K, trace, trace_stride, trace_
 
 def ocrdec_sync_positions(h, stream: int):
     _check("ocrdec_sync_positions", load_library().ocrdec_sync_positions(h, stream))
+
+
+def ocrdec_load_sequence(h, stream: int, slot: int, n_pos: int, pending_token: int, kv) -> None:
+    _check("ocrdec_load_sequence", load_library().ocrdec_load_sequence(h, stream, slot, n_pos, pending_token,
+                                                                          kv.data_ptr()))
+
+
+def ocrdec_set_router_logits(h, logits=None) -> None:
+    _check("ocrdec_set_router_logits", load_library().ocrdec_set_router_logits(h, _ptr(logits)))
 
 
 def ocrdec_set_taps(h, route_idx=None, hidden=None):

@@ -228,6 +228,32 @@ def concurrent_page_lengths(seed: int, batch: int, mean_out: float = 1085.0, sig
     return (256 + 100 * n).astype(np.int64), np.maximum(out, 1)
 
 
+def longctx_kv(cfg: ModelConfig, seed: int, n_pos: int) -> np.ndarray:
+    """Synthetic verifier cache of one sequence for the long-context layer
+    benchmark: keys and values ~ N(0, 1) rounded to bf16, as bf16 bit patterns
+    in the library's cache order [layer][K|V][head][pos][head_dim] (uint16)."""
+    shape = (cfg.n_layers, 2, cfg.n_heads, n_pos, cfg.head_dim)
+    a = np.random.default_rng([seed, 4]).standard_normal(shape, dtype=np.float32)
+    return f32_to_bf16_bits(a)
+
+
+def zipf_router_logits(seed: int, rows: int, n_layers: int = 1, n_experts: int = 64, s: float = 1.1) -> np.ndarray:
+    """Skewed routing for the long-context layer benchmark: logit_e = log pi(e) +
+    Gumbel(0, 1), pi(e) proportional to rank(e)^-s over a seeded permutation of the
+    experts, so top-6 by logit samples 6 experts without replacement with
+    probabilities pi.  float32 [n_layers][rows][n_experts]."""
+    rng = np.random.default_rng([seed, 5])
+    out = np.empty((n_layers, rows, n_experts), dtype=np.float32)
+    for l in range(n_layers):
+        rank = np.empty(n_experts, dtype=np.int64)
+        rank[rng.permutation(n_experts)] = np.arange(1, n_experts + 1)
+        logp = -s * np.log(rank.astype(np.float64))
+        logp -= np.log(np.exp(logp).sum())
+        g = rng.gumbel(size=(rows, n_experts))
+        out[l] = (logp[None, :] + g).astype(np.float32)
+    return out
+
+
 # Named workloads (shapes, lengths and seeds).  Weight seeds: 1230 for the
 # 2-layer fp32 model, 1234 for the 12-layer bf16 model; input seeds 2000 + index.
 WORKLOADS = {
@@ -240,7 +266,8 @@ WORKLOADS = {
     "concurrent32_bf16": dict(cfg=FULL, weight_seed=1234, input_seed=2003, n_vision=None, n_prompt=32,
                               n_out=None, batch=32),
     "longctx_layer_bf16": dict(cfg=dataclasses.replace(FULL, n_layers=1), weight_seed=1234,
-                               input_seed=2004, n_vision=None, n_prompt=None, n_out=None, batch=None),
+                               input_seed=2004, n_vision=None, n_prompt=None, n_out=None, batch=None,
+                               n_cached=32764, batches=(1, 4, 16, 64), kv_seed=5000),
 }
 
 # Per-slot replacement probability p for the controlled-acceptance drafts: the
