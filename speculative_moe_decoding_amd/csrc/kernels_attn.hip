@@ -2,9 +2,10 @@
 // boundaries) and its combine.
 //
 // Block (chunk c, head h, sequence b) stages the keys and values of
-// ATT_TILE-key tiles of chunk c in LDS (keys transposed, both widened to fp32)
-// and serves every query row of sequence b from them (the K+1 verify rows, or
-// a prefill chunk), so one KV read feeds all of the sequence's queries.  A
+// ATT_TILE-key tiles of chunk c in LDS (keys transposed; the next tile's loads
+// in flight while the current one is used) and serves every query row of
+// sequence b from them (the K+1 verify rows, or a prefill chunk), so one KV
+// read feeds all of the sequence's queries.  A
 // query at position p sees keys 0..p.  Per query the block keeps an online
 // softmax (running max m, sum l, output o) across its tiles and writes
 // (o, m, l); the combine kernel merges chunks 0..p/C in order.  Because chunk
@@ -16,13 +17,54 @@ namespace ocr {
 
 constexpr int QMAX_ATT = 8;  // query rows per sequence handled by one block
 
+// LDS tile formats: the fp32 model stages keys / values widened to fp32; the
+// bf16 model keeps them in bf16 (half the LDS, so more blocks per CU keep more
+// KV reads in flight) and widens them as they are read.
+template <typename T> struct AttTile;
+template <> struct AttTile<float> {
+  typedef float4 K4;   // 4 key dims
+  typedef float2 V2;   // 2 value dims
+  __device__ static __forceinline__ float4 k(const K4& v) { return v; }
+  __device__ static __forceinline__ float2 v(const V2& x) { return x; }
+  __device__ static __forceinline__ void stage(const uint4& kr, const uint4& vr, int d0, int t, K4 (*Kq)[ATT_TILE],
+                                               V2 (*Vs)[HD / 2]) {
+    // a 16-byte chunk holds dims d0 .. d0+3
+    Kq[d0 / 4][t] = make_float4(__uint_as_float(kr.x), __uint_as_float(kr.y), __uint_as_float(kr.z),
+                                __uint_as_float(kr.w));
+    Vs[t][d0 / 2] = make_float2(__uint_as_float(vr.x), __uint_as_float(vr.y));
+    Vs[t][d0 / 2 + 1] = make_float2(__uint_as_float(vr.z), __uint_as_float(vr.w));
+  }
+};
+template <> struct AttTile<bf16> {
+  typedef uint2 K4;
+  typedef uint32_t V2;
+  __device__ static __forceinline__ float4 k(const K4& v) {
+    return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u), __uint_as_float(v.y << 16),
+                       __uint_as_float(v.y & 0xffff0000u));
+  }
+  __device__ static __forceinline__ float2 v(const V2& x) {
+    return make_float2(__uint_as_float(x << 16), __uint_as_float(x & 0xffff0000u));
+  }
+  __device__ static __forceinline__ void stage(const uint4& kr, const uint4& vr, int d0, int t, K4 (*Kq)[ATT_TILE],
+                                               V2 (*Vs)[HD / 2]) {
+    // a 16-byte chunk holds dims d0 .. d0+7
+    Kq[d0 / 4][t] = make_uint2(kr.x, kr.y);
+    Kq[d0 / 4 + 1][t] = make_uint2(kr.z, kr.w);
+    Vs[t][d0 / 2] = vr.x;
+    Vs[t][d0 / 2 + 1] = vr.y;
+    Vs[t][d0 / 2 + 2] = vr.z;
+    Vs[t][d0 / 2 + 3] = vr.w;
+  }
+};
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_attn_partial(const float* __restrict__ q, const T* __restrict__ kv,
                                                       int max_pos, RowPlan plan, int n_chunks,
                                                       int tiles_per_chunk, float* __restrict__ part) {
+  typedef AttTile<T> AT;
   // keys transposed in groups of 4 dims: Kq[d/4][t] = (k_t[d..d+3]); values row-major
-  __shared__ float4 Kq[HD / 4][ATT_TILE];
-  __shared__ float2 Vs[ATT_TILE][HD / 2];
+  __shared__ typename AT::K4 Kq[HD / 4][ATT_TILE];
+  __shared__ typename AT::V2 Vs[ATT_TILE][HD / 2];
   __shared__ float4 qs[QMAX_ATT][HD / 4];
   __shared__ float4 ps[4][ATT_TILE / 4];
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -35,13 +77,32 @@ __global__ __launch_bounds__(256) void k_attn_partial(const float* __restrict__ 
   const int C = tiles_per_chunk * ATT_TILE;
   const int k0 = c * C;
   if (cnt <= 0 || k0 > p_last) return;
+  const int n_tiles = min(tiles_per_chunk, (p_last - k0) / ATT_TILE + 1);
   const long slot = plan.slot[b];
   const T* Kc = kv + slot * (2L * NH * max_pos * HD) + (long)h * max_pos * HD;
   const T* Vc = Kc + (long)NH * max_pos * HD;
   constexpr int CE = WT<T>::CE;
   constexpr int CPR = HD / CE;                         // 16-byte chunks per key row
   constexpr int NLD = ATT_TILE * CPR / 256;            // chunks per thread per tile
-  // queries of this sequence / head (all loads first)
+  uint4 kr[NLD], vr[NLD];
+  // K / V loads of tile tt (rows past the last query's key read as zeros)
+  auto load_tile = [&](int tt) {
+    const int kt = k0 + tt * ATT_TILE;
+    const int nk = min(ATT_TILE, p_last + 1 - kt);
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      const int e = tid + 256 * j, t = e / CPR, d0 = (e % CPR) * CE;
+      if (t < nk) {
+        kr[j] = ldg16(Kc + (long)(kt + t) * HD + d0);
+        vr[j] = ldg16(Vc + (long)(kt + t) * HD + d0);
+      } else {
+        kr[j] = make_uint4(0, 0, 0, 0);
+        vr[j] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  load_tile(0);
+  // queries of this sequence / head
   {
     float4 qv[QMAX_ATT * HD / 4 / 256];
 #pragma unroll
@@ -59,38 +120,16 @@ __global__ __launch_bounds__(256) void k_attn_partial(const float* __restrict__ 
   const float scale = 0.08838834764831845f;  // 1 / sqrt(128)
   float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
   float o0[2] = {0.f, 0.f}, o1[2] = {0.f, 0.f};
-  for (int tt = 0; tt < tiles_per_chunk; ++tt) {
+  for (int tt = 0; tt < n_tiles; ++tt) {
     const int kt = k0 + tt * ATT_TILE;
-    if (kt > p_last) break;
-    const int nk = min(ATT_TILE, p_last + 1 - kt);
-    // issue every K / V load of the tile, then stage (fp32) in LDS
-    uint4 kr[NLD], vr[NLD];
-#pragma unroll
-    for (int j = 0; j < NLD; ++j) {
-      const int e = tid + 256 * j, t = e / CPR, d0 = (e % CPR) * CE;
-      if (t < nk) {
-        kr[j] = ldg16(Kc + (long)(kt + t) * HD + d0);
-        vr[j] = ldg16(Vc + (long)(kt + t) * HD + d0);
-      } else {
-        kr[j] = make_uint4(0, 0, 0, 0);
-        vr[j] = make_uint4(0, 0, 0, 0);
-      }
-    }
     __syncthreads();  // the previous tile's LDS reads are done
 #pragma unroll
     for (int j = 0; j < NLD; ++j) {
       const int e = tid + 256 * j, t = e / CPR, d0 = (e % CPR) * CE;
-      float kf[CE], vf[CE];
-      WT<T>::cvt(kr[j], kf);
-      WT<T>::cvt(vr[j], vf);
-#pragma unroll
-      for (int g = 0; g < CE / 4; ++g) {
-        Kq[d0 / 4 + g][t] = make_float4(kf[4 * g], kf[4 * g + 1], kf[4 * g + 2], kf[4 * g + 3]);
-        Vs[t][d0 / 2 + 2 * g] = make_float2(vf[4 * g], vf[4 * g + 1]);
-        Vs[t][d0 / 2 + 2 * g + 1] = make_float2(vf[4 * g + 2], vf[4 * g + 3]);
-      }
+      AT::stage(kr[j], vr[j], d0, t, Kq, Vs);
     }
     __syncthreads();
+    if (tt + 1 < n_tiles) load_tile(tt + 1);  // next tile in flight during this one's arithmetic
 #pragma unroll
     for (int qq = 0; qq < 2; ++qq) {
       const int i = wave + 4 * qq;
@@ -102,7 +141,7 @@ __global__ __launch_bounds__(256) void k_attn_partial(const float* __restrict__ 
 #pragma unroll 8
       for (int d4 = 0; d4 < HD / 4; ++d4) {
         const float4 qv = qs[i][d4];
-        const float4 kv4 = Kq[d4][lane];
+        const float4 kv4 = AT::k(Kq[d4][lane]);
         sc = fmaf(qv.x, kv4.x, sc);
         sc = fmaf(qv.y, kv4.y, sc);
         sc = fmaf(qv.z, kv4.z, sc);
@@ -125,7 +164,7 @@ __global__ __launch_bounds__(256) void k_attn_partial(const float* __restrict__ 
         const float pv[4] = {pt.x, pt.y, pt.z, pt.w};
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const float2 v2 = Vs[4 * t4 + u][lane];
+          const float2 v2 = AT::v(Vs[4 * t4 + u][lane]);
           a0 = fmaf(pv[u], v2.x, a0);
           a1 = fmaf(pv[u], v2.y, a1);
         }
