@@ -154,10 +154,12 @@ __device__ __forceinline__ void publish_route(const RouteLds& r, int M, const Mo
   for (int sl = tid; sl < NX; sl += 256) {
     if (sl < r.na) {
       const int e = r.act[sl];
+      int rows = 0;  // bit m: row m has a pair routed to e (pairs sort by row)
+      for (int p = r.off[e]; p < r.off[e + 1]; ++p) rows |= 1 << (r.perm[p] / NSLOT);
       mb.act[sl] = e;
-      mb.slot_info[sl] = make_int4(e, r.off[e], r.off[e + 1], r.na);
+      mb.slot_info[sl] = make_int4(e, r.off[e], r.off[e + 1], rows);
     } else {
-      mb.slot_info[sl] = make_int4(-1, 0, 0, r.na);
+      mb.slot_info[sl] = make_int4(-1, 0, 0, 0);
     }
   }
   if (tid == 0) {
@@ -286,57 +288,52 @@ void launch_router(hipStream_t s, const float* x, const float* gain, float eps, 
   }
 }
 
-// Gather the activation rows m < m_act (row_of(m) into src) into LDS;
-// 256 threads, all loads of a row issued before its LDS stores.
-template <int K, typename SrcRow>
+// Gather the activation rows m < m_act <= MR (row_of(m) into src) into LDS;
+// 256 threads, the loads of every row issued before any LDS store.
+template <int K, int MR, typename SrcRow>
 __device__ __forceinline__ void gather_rows(const float* __restrict__ src, SrcRow row_of, int m_act, float* xs) {
   static_assert(K % 256 == 0 || K == DI, "row length");
   constexpr int J = (K + 255) / 256;
-  for (int m = 0; m < m_act; ++m) {
-    const float* r = src + (long)row_of(m) * K;
-    float v[J];
+  float v[MR][J];
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const int k = threadIdx.x + 256 * j;
-      v[j] = (k < K) ? r[k] : 0.f;
+  for (int m = 0; m < MR; ++m) {
+    if (m < m_act) {
+      const float* r = src + (long)row_of(m) * K;
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int k = threadIdx.x + 256 * j;
+        v[m][j] = (k < K) ? r[k] : 0.f;
+      }
     }
+  }
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const int k = threadIdx.x + 256 * j;
-      if (k < K) xs[m * K + k] = v[j];
+  for (int m = 0; m < MR; ++m) {
+    if (m < m_act) {
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int k = threadIdx.x + 256 * j;
+        if (k < K) xs[m * K + k] = v[m][j];
+      }
     }
   }
 }
 
-// Gate/up: block (x, slot s) handles active expert s; wavefront w owns units
-// j0 .. j0+UPW-1, j0 = UPW (4x + w): rows gate[j] then up[j], all loads issued
-// at once.  The (at most MR) pairs routed to the expert get
-// hx[pair][j] = silu(gate . b) * (up . b).  With ROUTE (M <= 8) every block
-// first routes the M rows from the router logits itself (identical in every
-// block) and block (0, 0) publishes that routing; otherwise the slot table
-// comes from the sort kernel.
-template <typename T, int MR, int UPW, bool ROUTE>
+// Gate/up (M <= 8): block (x, slot s) handles active expert s; wavefront w
+// owns units j0 .. j0+UPW-1, j0 = UPW (4x + w): rows gate[j] then up[j], all
+// loads issued at once.  The (at most MR) pairs routed to the expert get
+// hx[pair][j] = silu(gate . b) * (up . b).  The slot table gives the expert,
+// its pair range and a bit mask of its rows, so the weights and the
+// normalised rows are fetched after one dependent read.
+template <typename T, int MR, int UPW>
 __global__ __launch_bounds__(256) void k_expert_gate_up(const T* __restrict__ wg, const T* __restrict__ wu,
-                                                        int M, MoeBufs mb, int* __restrict__ tap) {
+                                                        MoeBufs mb) {
   extern __shared__ float xs[];
-  __shared__ RouteLds r;
   const int wave = wave_id(), lane = lane_id();
-  int e, k0, k1;
-  if (ROUTE) {
-    route_rows(mb.rlogit, M, r);
-    if (blockIdx.x == 0 && blockIdx.y == 0) publish_route(r, M, mb, tap);
-    if ((int)blockIdx.y >= r.na) return;
-    e = r.act[blockIdx.y];
-    k0 = r.off[e];
-    k1 = r.off[e + 1];
-  } else {
-    const int4 info = mb.slot_info[blockIdx.y];
-    e = info.x;
-    if (e < 0) return;
-    k0 = info.y;
-    k1 = info.z;
-  }
-  const int m_act = min(MR, k1 - k0);
+  const int4 info = mb.slot_info[blockIdx.y];
+  const int e = info.x;
+  if (e < 0) return;
+  const int k0 = info.y;
+  const int m_act = min(MR, info.z - k0);
   const int j0 = (blockIdx.x * 4 + wave) * UPW;
   const T* gbase = wg + ((long)e * DI + j0) * D;
   const T* ubase = wu + ((long)e * DI + j0) * D;
@@ -348,8 +345,12 @@ __global__ __launch_bounds__(256) void k_expert_gate_up(const T* __restrict__ wg
   }
   WaveGemv<T, D, 2 * UPW, MR> g;
   g.load(rows);
-  if (ROUTE) gather_rows<D>(mb.bnorm, [&](int m) { return r.perm[k0 + m] / NSLOT; }, m_act, xs);
-  else gather_rows<D>(mb.bnorm, [&](int m) { return mb.perm[k0 + m] / NSLOT; }, m_act, xs);
+  const int mask = info.w;
+  gather_rows<D, MR>(mb.bnorm, [=](int m) {  // the m-th set bit of the row mask
+    int mk = mask;
+    for (int i = 0; i < m; ++i) mk &= mk - 1;
+    return __builtin_ctz(mk);
+  }, m_act, xs);
   __syncthreads();
   float acc[2 * UPW][MR];
   g.fma(xs, m_act, acc);
@@ -382,7 +383,7 @@ __global__ __launch_bounds__(256) void k_expert_down(const T* __restrict__ wd, M
   for (int r = 0; r < RPW; ++r) rows[r] = base + (long)r * DI;
   WaveGemv<T, DI, RPW, MR> g;
   g.load(rows);
-  gather_rows<DI>(mb.hx, [&](int m) { return k0 + m; }, m_act, xs);
+  gather_rows<DI, MR>(mb.hx, [&](int m) { return k0 + m; }, m_act, xs);
   __syncthreads();
   float acc[RPW][MR];
   g.fma(xs, m_act, acc);
@@ -416,7 +417,7 @@ __global__ __launch_bounds__(256) void k_expert_gate_up_groups(const T* __restri
     const T* rows[4] = {gb, gb + D, ub, ub + D};
     WaveGemv<T, D, 4, MRG> g;
     g.load(rows);
-    gather_rows<D>(mb.bnorm, [&](int m) { return mb.perm[kb + m] / NSLOT; }, m_act, xs);
+    gather_rows<D, MRG>(mb.bnorm, [&](int m) { return mb.perm[kb + m] / NSLOT; }, m_act, xs);
     __syncthreads();
     float acc[4][MRG];
     g.fma(xs, m_act, acc);
@@ -448,7 +449,7 @@ __global__ __launch_bounds__(256) void k_expert_down_groups(const T* __restrict_
     const T* rows[4] = {b, b + DI, b + 2 * DI, b + 3 * DI};
     WaveGemv<T, DI, 4, MRG> g;
     g.load(rows);
-    gather_rows<DI>(mb.hx, [&](int m) { return kb + m; }, m_act, xs);
+    gather_rows<DI, MRG>(mb.hx, [&](int m) { return kb + m; }, m_act, xs);
     __syncthreads();
     float acc[4][MRG];
     g.fma(xs, m_act, acc);
@@ -478,8 +479,7 @@ template <typename T>
 void launch_expert_gate_up(hipStream_t s, const T* wg, const T* wu, int M, const MoeBufs& mb, int* tap) {
   const dim3 grid(DI / (4 * GU_UPW), expert_slot_cap(M));
 #define OCR_GU_CASE(MRV) \
-  hipLaunchKernelGGL((k_expert_gate_up<T, MRV, GU_UPW, false>), grid, dim3(256), (size_t)MRV * D * 4, s, wg, wu, \
-                     M, mb, tap);
+  hipLaunchKernelGGL((k_expert_gate_up<T, MRV, GU_UPW>), grid, dim3(256), (size_t)MRV * D * 4, s, wg, wu, mb);
   if (M <= 1) OCR_GU_CASE(1)
   else if (M <= 2) OCR_GU_CASE(2)
   else if (M <= 4) OCR_GU_CASE(4)
