@@ -1,0 +1,77 @@
+"""Edge cases of the decode path against the oracle (small 2-layer models):
+prefixes of a single row (prompt only / vision only), the largest draft length
+K = 7, vocabularies of 2 and 65 tokens (one LM-head block; a 1-token tail past
+the 64-row tiles, on both arithmetic paths) and 64 (exactly one tile).
+Tolerances as in the other parity tests."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+from oracle import decoder as od
+from speculative_moe_decoding_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+from gpu_util import compare_steps, log, make_pair, run_gpu_steps  # noqa: E402
+from speculative_moe_decoding_amd import ocrdec  # noqa: E402
+
+
+def _ar_vs_oracle(dec, orc, page, N, tol):
+    g_ar, g_steps = run_gpu_steps(dec, page, N, 0)
+    r_ar, r_logits = orc.generate_ar(page.vision, page.prompt, N, keep_logits=True)
+    if g_ar[0] != r_ar[0]:
+        assert od.top2_margin(r_logits[0]) < tol, "first token differs without a near tie"
+        return g_ar, 0, 0.0
+    ref = [od.StepRecord(0, [], [r_ar[i + 1]], 0, r_logits[i + 1][None]) for i in range(N - 1)]
+    n, worst, note = compare_steps(g_steps, ref, tol)
+    assert worst < tol
+    return g_ar, n, worst
+
+
+@pytest.mark.parametrize("nv,npr", [(0, 1), (1, 0)], ids=["prompt_only", "vision_only"])
+def test_single_row_prefix(nv, npr):
+    cfg = dataclasses.replace(synth.FULL, n_layers=2, vocab=3001, dtype="f32")
+    w, dec, orc = make_pair(cfg, 61)
+    page = synth.make_pages(cfg, 62, [nv], [npr], [16])[0]
+    g_ar, n, worst = _ar_vs_oracle(dec, orc, page, 16, 1e-3)
+    g_sp, _ = run_gpu_steps(dec, page, 16, 3)
+    assert g_sp == g_ar
+    log(f"prefix {nv}+{npr}: {n} AR steps agree (max |dlogit| {worst:.1e}); K=3 lossless")
+
+
+def test_max_draft_length():
+    cfg = dataclasses.replace(synth.FULL, n_layers=2, vocab=3001, dtype="bf16")
+    w, dec, orc = make_pair(cfg, 63, max_k=7)
+    page = synth.make_pages(cfg, 64, [12], [3], [30])[0]
+    N = 30
+    g_ar, _ = run_gpu_steps(dec, page, N, 0)
+    g_sp, g_ss = run_gpu_steps(dec, page, N, 7)
+    assert g_sp == g_ar
+    r_sp, r_ss = orc.generate_spec(page.vision, page.prompt, N, 7, keep_logits=True)
+    n, worst, note = compare_steps(g_ss, r_ss, 5e-2)
+    log(f"K=7: {n}/{len(r_ss)} steps agree, max |dlogit| {worst:.2e}, {note}")
+    assert worst < 5e-2 and n >= 2
+    # controlled drafts at K = 7: every slot right (threshold 0) accepts all 7
+    trace = torch.from_numpy(np.asarray(g_ar + [0] * 16, dtype=np.int32)[None]).cuda()
+    toks, acc, _ = dec.generate([page], 24, 7, trace=trace, seed=1, threshold=0, record=True, check_every=1)
+    assert toks[0].tolist() == g_ar[:24]
+    assert all(a == 7 for a in acc[0][:-1])
+
+
+@pytest.mark.parametrize("vocab,dtype,path", [(2, "f32", 1), (65, "bf16", 1), (65, "bf16", 2), (64, "bf16", 2)],
+                         ids=["V2_vector", "V65_vector", "V65_matrix", "V64_matrix"])
+def test_small_vocabularies(vocab, dtype, path):
+    cfg = dataclasses.replace(synth.FULL, n_layers=2, vocab=vocab, dtype=dtype)
+    tol = 1e-3 if dtype == "f32" else 5e-2
+    w, dec, orc = make_pair(cfg, 65, path=path)
+    page = synth.make_pages(cfg, 66, [10], [4], [20])[0]
+    g_ar, n, worst = _ar_vs_oracle(dec, orc, page, 20, tol)
+    g_sp, _ = run_gpu_steps(dec, page, 20, 3)
+    assert g_sp == g_ar
+    assert all(0 <= t < vocab for t in g_ar)
+    log(f"V={vocab} {dtype} path {path}: {n} AR steps agree (max |dlogit| {worst:.1e}); K=3 lossless")
