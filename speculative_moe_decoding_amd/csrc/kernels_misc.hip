@@ -120,51 +120,81 @@ __global__ __launch_bounds__(256) void k_plan_draft_step(int j, int Qprev, int K
   }
 }
 
-// Prefill rows p0 .. p0+c-1 of one sequence: vision rows, then prompt ids.
+// Prefill pass over a group of sequences: rows j*8 + i (sequence j of the
+// group, i < cnt[j]) hold positions p0 + i of that sequence -- vision rows,
+// then prompt ids; rows past cnt[j] are zero.  esave keeps the input rows for
+// the draft prefill.  Grid (8, n).
 template <typename T>
-__global__ __launch_bounds__(256) void k_plan_prefill(int slot, int p0, int c, int n_vision,
-                                                      const float* __restrict__ vision,
-                                                      const int* __restrict__ prompt, const T* __restrict__ E,
-                                                      int V, int* plan_base, int* plan_cnt, int* plan_slot,
-                                                      float* __restrict__ x, float* __restrict__ esave) {
-  const int i = blockIdx.x;
-  const int p = p0 + i;
+__global__ __launch_bounds__(256) void k_plan_prefill(PrefillGroup g, const float* __restrict__ vision,
+                                                      int nv_stride, const int* __restrict__ prompt, int np_stride,
+                                                      const T* __restrict__ E, int V, int* plan_base,
+                                                      int* plan_cnt, int* plan_slot, float* __restrict__ x,
+                                                      float* __restrict__ esave) {
+  const int i = blockIdx.x, j = blockIdx.y;
+  const int p = g.p0 + i;
+  const int b = g.seq[j];
   if (i == 0 && threadIdx.x == 0) {
-    plan_slot[0] = slot;
-    plan_base[0] = p0;
-    plan_cnt[0] = c;
+    plan_slot[j] = g.slot[j];
+    plan_base[j] = g.p0;
+    plan_cnt[j] = g.cnt[j];
   }
-  float* dst = x + (long)i * D;
-  if (p < n_vision) {
-    for (int k = threadIdx.x; k < D; k += 256) dst[k] = vision[(long)p * D + k];
+  const long row = (long)j * PREFILL_CHUNK + i;
+  float* dst = x + row * D;
+  if (i >= g.cnt[j]) {
+    for (int k = threadIdx.x; k < D; k += 256) dst[k] = 0.f;
+  } else if (p < g.nvis[j]) {
+    const float* src = vision + ((long)b * nv_stride + p) * D;
+    for (int k = threadIdx.x; k < D; k += 256) dst[k] = src[k];
   } else {
-    embed_row(E, clamp_tok(prompt[p - n_vision], V), dst);
+    embed_row(E, clamp_tok(prompt[(long)b * np_stride + p - g.nvis[j]], V), dst);
   }
   __syncthreads();
-  for (int k = threadIdx.x; k < D; k += 256) esave[(long)i * D + k] = dst[k];
+  for (int k = threadIdx.x; k < D; k += 256) esave[row * D + k] = dst[k];
 }
 
-// Draft prefill rows: row i (position p0 + i) takes (h_{p-1}, e_p); h of the
-// chunk's first row comes from the previous chunk (hprev, zero at p = 0).
-__global__ __launch_bounds__(256) void k_draft_prefill_cat(int c, const float* __restrict__ xfinal,
+// Draft prefill rows of a group pass: row (j, i) at position p = p0 + i takes
+// (h_{p-1}, e_p); h of a pass's first row is the last verifier hidden of the
+// sequence's previous pass (hprev[slot]; a zero row at p = 0).  The pass's last
+// verifier hidden goes to hnext[slot].  Grid (8, n).
+__global__ __launch_bounds__(256) void k_draft_prefill_cat(PrefillGroup g, const float* __restrict__ xfinal,
                                                            const float* __restrict__ esave,
                                                            const float* __restrict__ hprev,
                                                            float* __restrict__ hnext, const float* __restrict__ g_h,
                                                            const float* __restrict__ g_e, float eps,
                                                            float* __restrict__ cat) {
   __shared__ float red[4];
-  const int i = blockIdx.x;
-  const float* h = (i == 0) ? hprev : xfinal + (long)(i - 1) * D;
-  float* dst = cat + (long)i * 2 * D;
+  __shared__ float zero[D];
+  const int i = blockIdx.x, j = blockIdx.y;
+  const long row = (long)j * PREFILL_CHUNK + i;
+  const int slot = g.slot[j];
+  const float* h;
+  if (i > 0) {
+    h = xfinal + (row - 1) * D;
+  } else if (g.p0 > 0) {
+    h = hprev + (long)slot * D;
+  } else {
+    for (int k = threadIdx.x; k < D; k += 256) zero[k] = 0.f;
+    __syncthreads();
+    h = zero;
+  }
+  float* dst = cat + row * 2 * D;
   norm_row(h, g_h, eps, dst, red);
-  norm_row(esave + (long)i * D, g_e, eps, dst + D, red);
-  if (i == c - 1)
-    for (int k = threadIdx.x; k < D; k += 256) hnext[k] = xfinal[(long)i * D + k];
+  norm_row(esave + row * D, g_e, eps, dst + D, red);
+  if (i == g.cnt[j] - 1)
+    for (int k = threadIdx.x; k < D; k += 256) hnext[(long)slot * D + k] = xfinal[row * D + k];
 }
 
-__global__ void k_prefill_finish(int slot, int P, const float* __restrict__ xlast, const int* __restrict__ tok,
-                                 StateView sv) {
-  const int y0 = *tok;
+// Sequences of a group whose prefix ends in this pass: state of the slot, and
+// output token 0 (the greedy token of the last prefix row, tok[j]) to
+// pending_out[seq].  Grid n.
+__global__ __launch_bounds__(256) void k_prefill_finish(PrefillGroup g, const float* __restrict__ xfinal,
+                                                        const int* __restrict__ tok, StateView sv,
+                                                        int* __restrict__ pending_out) {
+  const int j = blockIdx.x;
+  const int P = g.plen[j];
+  if (g.p0 + g.cnt[j] != P) return;
+  const int slot = g.slot[j];
+  const int y0 = tok[j];
   if (threadIdx.x == 0) {
     sv.kv_len[slot] = P;
     sv.draft_len[slot] = P;
@@ -174,9 +204,11 @@ __global__ void k_prefill_finish(int slot, int P, const float* __restrict__ xlas
     sv.step[slot] = 0;
     sv.prefix_len[slot] = P;
     sv.cu_tok[slot * sv.cu_stride] = y0;
+    pending_out[g.seq[j]] = y0;
   }
+  const float* xl = xfinal + ((long)j * PREFILL_CHUNK + g.cnt[j] - 1) * D;
   float* hb = sv.hbuf + (long)slot * sv.cu_stride * D;
-  for (int k = threadIdx.x; k < D; k += 256) hb[k] = xlast[k];
+  for (int k = threadIdx.x; k < D; k += 256) hb[k] = xl[k];
 }
 
 // A slot whose verifier cache was loaded by the caller: P cached positions,
@@ -290,20 +322,21 @@ void launch_plan_draft_step(hipStream_t s, int B, int j, int Qprev, int K, State
                      g_e, eps, u_prev, plan_base, plan_cnt, plan_slot, cat);
 }
 template <typename T>
-void launch_plan_prefill(hipStream_t s, int slot, int p0, int c, int n_vision, const float* vision,
-                         const int* prompt, const T* embed, int V, int* plan_base, int* plan_cnt, int* plan_slot,
-                         float* x, float* esave) {
-  hipLaunchKernelGGL((k_plan_prefill<T>), dim3(c), dim3(256), 0, s, slot, p0, c, n_vision, vision, prompt, embed,
-                     V, plan_base, plan_cnt, plan_slot, x, esave);
+void launch_plan_prefill(hipStream_t s, const PrefillGroup& g, const float* vision, int nv_stride,
+                         const int* prompt, int np_stride, const T* embed, int V, int* plan_base, int* plan_cnt,
+                         int* plan_slot, float* x, float* esave) {
+  hipLaunchKernelGGL((k_plan_prefill<T>), dim3(PREFILL_CHUNK, g.n), dim3(256), 0, s, g, vision, nv_stride, prompt,
+                     np_stride, embed, V, plan_base, plan_cnt, plan_slot, x, esave);
 }
-void launch_draft_prefill_cat(hipStream_t s, int c, const float* xfinal, const float* esave, const float* hprev,
-                              float* hnext, const float* g_h, const float* g_e, float eps, float* cat) {
-  hipLaunchKernelGGL(k_draft_prefill_cat, dim3(c), dim3(256), 0, s, c, xfinal, esave, hprev, hnext, g_h, g_e, eps,
-                     cat);
+void launch_draft_prefill_cat(hipStream_t s, const PrefillGroup& g, const float* xfinal, const float* esave,
+                              const float* hprev, float* hnext, const float* g_h, const float* g_e, float eps,
+                              float* cat) {
+  hipLaunchKernelGGL(k_draft_prefill_cat, dim3(PREFILL_CHUNK, g.n), dim3(256), 0, s, g, xfinal, esave, hprev, hnext,
+                     g_h, g_e, eps, cat);
 }
-void launch_prefill_finish(hipStream_t s, int slot, int P, const float* xlast, const int* pending_tok,
-                           StateView sv) {
-  hipLaunchKernelGGL(k_prefill_finish, dim3(1), dim3(256), 0, s, slot, P, xlast, pending_tok, sv);
+void launch_prefill_finish(hipStream_t s, const PrefillGroup& g, const float* xfinal, const int* tok, StateView sv,
+                           int* pending_out) {
+  hipLaunchKernelGGL(k_prefill_finish, dim3(g.n), dim3(256), 0, s, g, xfinal, tok, sv, pending_out);
 }
 void launch_set_sequence(hipStream_t s, int slot, int P, int tok, StateView sv) {
   hipLaunchKernelGGL(k_set_sequence, dim3(1), dim3(256), 0, s, slot, P, tok, sv);
@@ -331,8 +364,8 @@ void launch_copy_rows(hipStream_t s, const float* src, float* dst, long n) {
   template void launch_plan_draft_step<T>(hipStream_t, int, int, int, int, StateView, const int*, const T*, int, \
                                           const float*, const float*, float, const float*, int*, int*,           \
                                           const int*, float*);                                                   \
-  template void launch_plan_prefill<T>(hipStream_t, int, int, int, int, const float*, const int*, const T*, int, \
-                                       int*, int*, int*, float*, float*);
+  template void launch_plan_prefill<T>(hipStream_t, const PrefillGroup&, const float*, int, const int*, int,     \
+                                       const T*, int, int*, int*, int*, float*, float*);
 OCR_INST_MISC(float)
 OCR_INST_MISC(bf16)
 

@@ -98,15 +98,26 @@ void launch_plan_draft_step(hipStream_t s, int B, int j, int Qprev, int K, State
                             const T* embed, int V, const float* g_h, const float* g_e, float eps,
                             const float* u_prev, int* plan_base, int* plan_cnt, const int* plan_slot,
                             float* cat);
+// One prefill pass over up to PREFILL_GROUP sequences: chunk rows p0 ..
+// p0 + cnt[j] - 1 of sequence seq[j] (slot slot[j], n_vision nvis[j], prefix
+// length plen[j]); activation row j * PREFILL_CHUNK + i holds position p0 + i.
+constexpr int PREFILL_GROUP = 32;
+struct PrefillGroup {
+  int n, p0;
+  int seq[PREFILL_GROUP], slot[PREFILL_GROUP], cnt[PREFILL_GROUP], nvis[PREFILL_GROUP], plen[PREFILL_GROUP];
+};
 template <typename T>
-void launch_plan_prefill(hipStream_t s, int slot, int p0, int c, int n_vision, const float* vision,
-                         const int* prompt, const T* embed, int V, int* plan_base, int* plan_cnt,
+void launch_plan_prefill(hipStream_t s, const PrefillGroup& g, const float* vision, int nv_stride,
+                         const int* prompt, int np_stride, const T* embed, int V, int* plan_base, int* plan_cnt,
                          int* plan_slot, float* x, float* esave);
-void launch_draft_prefill_cat(hipStream_t s, int c, const float* xfinal, const float* esave,
+// hprev / hnext: [max_batch][D] per-slot last verifier hidden of the previous /
+// this pass (two buffers, alternating by pass).
+void launch_draft_prefill_cat(hipStream_t s, const PrefillGroup& g, const float* xfinal, const float* esave,
                               const float* hprev, float* hnext, const float* g_h, const float* g_e, float eps,
                               float* cat);
-void launch_prefill_finish(hipStream_t s, int slot, int P, const float* xlast, const int* pending_tok,
-                           StateView sv);
+// tok: [n] greedy tokens of the group's last valid rows; pending_out: [B] of the call.
+void launch_prefill_finish(hipStream_t s, const PrefillGroup& g, const float* xfinal, const int* tok, StateView sv,
+                           int* pending_out);
 void launch_set_sequence(hipStream_t s, int slot, int P, int tok, StateView sv);
 void launch_accept(hipStream_t s, int B, int K, const int* plan_slot, const int* draft, const int* greedy,
                    const float* xfinal, StateView sv, int* n_acc, int* out_tokens, int* out_len_out,

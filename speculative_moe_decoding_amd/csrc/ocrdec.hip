@@ -29,7 +29,7 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 // Offsets of every sub-buffer inside the state and the workspace.
 struct Plan {
   // derived sizes
-  int Qmax, M_max, cu_stride, tiles_per_chunk, chunk_keys, n_chunks_cap, lm_nblk;
+  int Qmax, M_max, prefill_group, cu_stride, tiles_per_chunk, chunk_keys, n_chunks_cap, lm_nblk;
   size_t esz, kv_layer_elems;
   // state
   size_t s_kv, s_dkv, s_ints, s_cu, s_hbuf, s_rope, s_total;
@@ -70,7 +70,9 @@ bool use_matrix_path(const ocrdec_config* c) {
 Plan make_plan(const ocrdec_config* c) {
   Plan p{};
   p.Qmax = std::max(c->max_k + 1, PREFILL_CHUNK);
-  p.M_max = std::max(c->max_batch * (c->max_k + 1), PREFILL_CHUNK);
+  // prefill passes take up to prefill_group sequences at PREFILL_CHUNK rows each
+  p.prefill_group = std::min(c->max_batch, PREFILL_GROUP);
+  p.M_max = std::max(c->max_batch * (c->max_k + 1), PREFILL_CHUNK * p.prefill_group);
   p.cu_stride = c->max_k + 1;
   p.tiles_per_chunk = c->max_positions > 4096 ? 4 : 1;
   p.chunk_keys = p.tiles_per_chunk * ATT_TILE;
@@ -109,8 +111,8 @@ Plan make_plan(const ocrdec_config* c) {
   p.w_cat = take(M * 2 * D * 4);
   p.w_u = take(M * D * 4);
   p.w_dffn = take(M * DF * 4);
-  p.w_esave = take((size_t)PREFILL_CHUNK * D * 4);
-  p.w_hsave = take(2 * D * 4);
+  p.w_esave = take(M * D * 4);
+  p.w_hsave = take((size_t)2 * c->max_batch * D * 4);
   p.w_lmv = take(M * (size_t)p.lm_nblk * 4);
   p.w_lmi = take(M * (size_t)p.lm_nblk * 4);
   p.w_plan = take((size_t)3 * std::max(c->max_batch, PREFILL_CHUNK) * 4);
@@ -267,40 +269,52 @@ void draft_layer(ocrdec_model* m, hipStream_t s, int M, int B, RowPlan plan, int
                  D);
 }
 
+// Prefill in passes of PREFILL_CHUNK positions: pass t takes rows 8t .. 8t+7 of
+// every sequence whose prefix reaches that far, up to prefill_group sequences
+// per launch group (each row's arithmetic is the same whatever its group).
 template <typename T>
 int do_prefill(ocrdec_model* m, hipStream_t s, int B, const int32_t* slots_host, const float* vision, int nv_stride,
                const int32_t* nv_host, const int32_t* prompt, int np_stride, const int32_t* np_host,
                int32_t* pending_out) {
   const ocrdec_config& c = m->cfg;
-  for (int b = 0; b < B; ++b) {
-    const int slot = slots_host ? slots_host[b] : b;
-    const int Nv = nv_host[b], Np = np_host[b];
-    const int P = Nv + Np;
-    const float* vis = vision ? vision + (size_t)b * nv_stride * D : nullptr;
-    const int* pr = prompt ? prompt + (size_t)b * np_stride : nullptr;
-    if (hipMemsetAsync(m->hsave[0], 0, D * 4, s) != hipSuccess) return fail(OCRDEC_EHIP, "hipMemsetAsync failed");
-    int par = 0;
-    for (int p0 = 0; p0 < P; p0 += PREFILL_CHUNK) {
-      const int cc = std::min(PREFILL_CHUNK, P - p0);
-      launch_plan_prefill<T>(s, slot, p0, cc, Nv, vis, pr, wmat<T>(m, W_EMBED), c.vocab, m->plan_base, m->plan_cnt,
-                             m->plan_slot, m->x, m->esave);
-      RowPlan plan{m->plan_base, m->plan_cnt, m->plan_slot, cc};
-      const int nch = chunks_for(m, p0 + cc - 1);
-      verifier_layers<T>(m, s, cc, 1, plan, nch, false, nullptr);
-      if (p0 + cc == P)
-        lm_head<T>(m, s, m->x, cc, true, wvec(m, W_FNORM), 1, nullptr, m->tok_tmp, 1);
-      launch_draft_prefill_cat(s, cc, m->x, m->esave, m->hsave[par], m->hsave[1 - par], wvec(m, dw(m, D_NH)),
-                               wvec(m, dw(m, D_NE)), c.norm_eps, m->cat);
-      draft_layer<T>(m, s, cc, 1, plan, nch);
-      par ^= 1;
-      if (p0 + cc == P) {
-        launch_prefill_finish(s, slot, P, m->x + (size_t)(cc - 1) * D, m->tok_tmp, m->sv);
-        if (hipMemcpyAsync(pending_out + b, m->tok_tmp, 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
-          return fail(OCRDEC_EHIP, "hipMemcpyAsync failed");
+  int maxP = 0;
+  for (int b = 0; b < B; ++b) maxP = std::max(maxP, nv_host[b] + np_host[b]);
+  std::vector<int> act;
+  for (int p0 = 0, t = 0; p0 < maxP; p0 += PREFILL_CHUNK, ++t) {
+    const float* hprev = m->hsave[t & 1];
+    float* hnext = m->hsave[(t + 1) & 1];
+    act.clear();
+    for (int b = 0; b < B; ++b)
+      if (nv_host[b] + np_host[b] > p0) act.push_back(b);
+    for (size_t g0 = 0; g0 < act.size(); g0 += m->p.prefill_group) {
+      PrefillGroup g{};
+      g.n = (int)std::min(act.size() - g0, (size_t)m->p.prefill_group);
+      g.p0 = p0;
+      bool finish = false;
+      for (int j = 0; j < g.n; ++j) {
+        const int b = act[g0 + j];
+        const int P = nv_host[b] + np_host[b];
+        g.seq[j] = b;
+        g.slot[j] = slots_host ? slots_host[b] : b;
+        g.cnt[j] = std::min(PREFILL_CHUNK, P - p0);
+        g.nvis[j] = nv_host[b];
+        g.plen[j] = P;
+        finish = finish || (p0 + g.cnt[j] == P);
       }
+      launch_plan_prefill<T>(s, g, vision, nv_stride, prompt, np_stride, wmat<T>(m, W_EMBED), c.vocab, m->plan_base,
+                             m->plan_cnt, m->plan_slot, m->x, m->esave);
+      const int M = g.n * PREFILL_CHUNK;
+      RowPlan plan{m->plan_base, m->plan_cnt, m->plan_slot, PREFILL_CHUNK};
+      const int nch = chunks_for(m, std::min(c.max_positions - 1, p0 + PREFILL_CHUNK - 1));
+      verifier_layers<T>(m, s, M, g.n, plan, nch, false, nullptr);
+      if (finish) lm_head<T>(m, s, m->x, PREFILL_CHUNK, true, wvec(m, W_FNORM), g.n, nullptr, m->tok_tmp, 1);
+      launch_draft_prefill_cat(s, g, m->x, m->esave, hprev, hnext, wvec(m, dw(m, D_NH)), wvec(m, dw(m, D_NE)),
+                               c.norm_eps, m->cat);
+      draft_layer<T>(m, s, M, g.n, plan, nch);
+      if (finish) launch_prefill_finish(s, g, m->x, m->tok_tmp, m->sv, pending_out);
     }
-    m->slot_bound[slot] = P;
   }
+  for (int b = 0; b < B; ++b) m->slot_bound[slots_host ? slots_host[b] : b] = nv_host[b] + np_host[b];
   return hip_check("ocrdec_prefill");
 }
 
@@ -424,7 +438,7 @@ int ocrdec_create(const ocrdec_config* cfg, const void* const* weight_ptrs, int 
   m->dffn = wf(p.w_dffn);
   m->esave = wf(p.w_esave);
   m->hsave[0] = wf(p.w_hsave);
-  m->hsave[1] = wf(p.w_hsave) + D;
+  m->hsave[1] = wf(p.w_hsave) + (size_t)cfg->max_batch * D;
   m->lm_val = wf(p.w_lmv);
   m->lm_idx = wi(p.w_lmi);
   const int pm = std::max(mb, PREFILL_CHUNK);
