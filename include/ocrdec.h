@@ -153,9 +153,9 @@ typedef struct {
 } ocrdec_controlled_cfg;
 
 /* n_steps speculative steps of the B sequences: per step ocrdec_draft (K >= 1),
- * the controlled override when ctrl is non-null, ocrdec_verify and
+ * the controlled override when ctrl is non-null (K >= 1), ocrdec_verify and
  * ocrdec_accept_rollback, with the same results as issuing those calls one by
- * one.  Each step is recorded once per call shape as a HIP graph (on a
+ * one (K = 0: plain autoregressive steps, draft may be NULL).  Each step is recorded once per call shape as a HIP graph (on a
  * library-private capture stream) and replayed on `stream`; the graphs are
  * cached in the handle.  draft (device int32 [B][K]) and greedy ([B][K+1]) are
  * caller scratch; n_accepted / out_tokens / out_len as in

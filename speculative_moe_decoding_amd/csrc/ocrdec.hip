@@ -598,7 +598,7 @@ int ocrdec_decode_steps(ocrdec_model* m, void* stream, int B, const int32_t* slo
                         int32_t* n_accepted_out, int32_t* out_tokens, int32_t* out_len, int out_cap) {
   int rc = check_call(m, B, K);
   if (rc) return rc;
-  if (K < 1 || n_steps < 0 || !draft || !greedy) return fail(OCRDEC_EINVAL, "bad decode-step arguments");
+  if (n_steps < 0 || !greedy || (K > 0 && !draft)) return fail(OCRDEC_EINVAL, "bad decode-step arguments");
   if (out_tokens && out_cap < 1) return fail(OCRDEC_EINVAL, "out_cap must be >= 1 with out_tokens");
   if (ctrl && (!ctrl->trace || ctrl->trace_len < 0 || ctrl->trace_stride < ctrl->trace_len))
     return fail(OCRDEC_EINVAL, "bad controlled-draft arguments");
@@ -631,9 +631,11 @@ int ocrdec_decode_steps(ocrdec_model* m, void* stream, int B, const int32_t* slo
       hipStream_t cs = m->capture_stream;
       if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess)
         return fail(OCRDEC_EHIP, "hipStreamBeginCapture failed");
-      int r1 = m->cfg.dtype == OCRDEC_BF16 ? do_draft<bf16>(m, cs, B, slots, K, draft)
-                                             : do_draft<float>(m, cs, B, slots, K, draft);
-      if (r1 == OCRDEC_OK && ctrl)
+      int r1 = OCRDEC_OK;
+      if (K > 0)
+        r1 = m->cfg.dtype == OCRDEC_BF16 ? do_draft<bf16>(m, cs, B, slots, K, draft)
+                                         : do_draft<float>(m, cs, B, slots, K, draft);
+      if (r1 == OCRDEC_OK && ctrl && K > 0)
         launch_controlled(cs, B, K, slots, m->sv, ctrl->trace, ctrl->trace_stride, ctrl->trace_len, ctrl->seed,
                           ctrl->threshold, m->cfg.vocab, draft);
       if (r1 == OCRDEC_OK)

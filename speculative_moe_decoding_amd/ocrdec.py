@@ -312,7 +312,7 @@ class Decoder:
         accs, lens = [], []
         steps = 0
         while True:
-            if graphs and K > 0 and not record:
+            if graphs and not record:
                 self.decode_steps(B, K, check_every, draft, greedy, n_acc, out_tokens, out_len, trace, seed,
                                   threshold)
                 steps += check_every
@@ -395,7 +395,7 @@ class Decoder:
             draft, greedy = buf["draft"][:Bb], buf["greedy"][:Bb]
             while True:
                 rec = []
-                if graphs and K > 0 and not record:
+                if graphs and not record:
                     self.decode_steps(Bb, K, check_every, draft, greedy, n_acc, out_t, out_len, tr, seed,
                                       threshold, slots=slots)
                 else:
