@@ -404,6 +404,10 @@ def bench_sweep_k(args) -> int:
             log(json.dumps(row))
     best = max(rows, key=lambda r: r["tok_per_s"])
     base = {m: next(r["tok_per_s"] for r in rows if r["mode"] == m and r["K"] == 0) for m in ("graph", "eager")}
+    from speculative_moe_decoding_amd import policy
+    choice = {m: policy.choose_k({r["K"]: r["ms_per_step"] for r in rows if r["mode"] == m},
+                                 {r["K"]: (r["tau"] - 1) / r["K"] for r in rows if r["mode"] == m and r["K"] > 0})
+              for m in ("graph", "eager")}
     for r in rows:
         r["speedup_vs_K0"] = round(r["tok_per_s"] / base[r["mode"]], 3)
     print(json.dumps({
@@ -412,7 +416,8 @@ def bench_sweep_k(args) -> int:
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "base_page_bf16 at K = 0..3 (graph-replayed and eager steps), controlled "
                                "acceptance at the L4 table's per-K rates", "best": {"K": best["K"],
-                                                                                    "mode": best["mode"]}},
+                                                                                    "mode": best["mode"]},
+                   "adaptive_k_choice": choice},
         "sweep": rows, "cpu_baseline": None}), flush=True)
     return 0
 
