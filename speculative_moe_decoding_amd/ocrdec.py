@@ -424,3 +424,90 @@ class Decoder:
             active = active[lens < n_out[active]]
         host = full.cpu().numpy()
         return [host[b, :n_out[b]] for b in range(B)], (accs if record else None), seq_steps
+
+    def generate_stream(self, pages, n_out, K: int, concurrency: int, trace=None, seed: int = 0,
+                        threshold: int = 0, check_every: int = 8, graphs: bool = False, refill_min: int = 1):
+        """Continuous batching over a queue of pages: at most ``concurrency`` pages in
+        flight, one state slot each; when a page has its n_out[i] tokens, its slot is
+        prefilled with the next queued page (all refills of a check in one prefill call;
+        with refill_min > 1, free slots wait until that many are free or nothing else
+        runs, so prefills run several pages per pass) while the other slots keep decoding.  ``trace`` (device int32 [n_pages, T])
+        switches on the controlled drafts (each page reads its own row).  Returns (list
+        of token arrays per page, total sequence-steps run)."""
+        torch = self.torch
+        n = len(pages)
+        n_out = np.asarray(n_out, dtype=np.int64)
+        C = min(concurrency, self.max_batch, n)
+        cap = int(n_out.max()) + self.max_k + 2
+        T = 0 if trace is None else int(trace.shape[1])
+        buf = self._ragged_buffers(C, K, cap, T)
+        out_full = torch.zeros(C, cap, dtype=torch.int32, device=self.device)
+        tr_full = None if trace is None else torch.zeros(C, T, dtype=torch.int32, device=self.device)
+        slot_page = [-1] * C
+        results = [None] * n
+        queue = 0
+        seq_steps = 0
+
+        def refill(free):
+            nonlocal queue
+            take = []
+            for s in free:
+                if queue < n:
+                    slot_page[s] = queue
+                    queue += 1
+                    take.append(s)
+                else:
+                    slot_page[s] = -1
+            if take:
+                pend = self.prefill([pages[slot_page[s]] for s in take], slots=take)
+                for j, s in enumerate(take):
+                    out_full[s].zero_()
+                    out_full[s, 0] = pend[j]
+                    if tr_full is not None:
+                        tr_full[s].copy_(trace[slot_page[s]])
+
+        refill(list(range(C)))
+        free = []
+        while any(p >= 0 for p in slot_page):
+            active = np.array([s for s in range(C) if slot_page[s] >= 0], dtype=np.int64)
+            Bb = len(active)
+            idx = torch.from_numpy(active).to(self.device)
+            slots = buf["slots"][:Bb]
+            slots.copy_(idx.to(torch.int32))
+            out_t = buf["out"][:Bb]
+            out_t.copy_(out_full[idx])
+            tr = None
+            if tr_full is not None:
+                tr = buf["trace"][:Bb]
+                tr.copy_(tr_full[idx])
+            out_len, n_acc = buf["out_len"][:Bb], buf["n_acc"][:Bb]
+            draft, greedy = buf["draft"][:Bb], buf["greedy"][:Bb]
+            target = np.array([n_out[slot_page[s]] for s in active])
+            while True:
+                if graphs:
+                    self.decode_steps(Bb, K, check_every, draft, greedy, n_acc, out_t, out_len, tr, seed,
+                                      threshold, slots=slots)
+                else:
+                    for _ in range(check_every):
+                        if K > 0:
+                            self.draft(Bb, K, slots=slots, out=draft)
+                            if tr is not None:
+                                self.controlled(Bb, K, tr, seed, threshold, draft, slots=slots)
+                        self.verify(Bb, K, draft, slots=slots, greedy=greedy)
+                        self.accept(Bb, K, draft, greedy, n_acc, out_t, out_len, slots=slots)
+                seq_steps += Bb * check_every
+                ocrdec_sync_positions(self.h, self.stream)
+                lens = out_len.cpu().numpy()
+                if (lens >= target).any():
+                    break
+            out_full[idx] = out_t
+            done = [int(s) for i, s in enumerate(active) if lens[i] >= target[i]]
+            host = out_full.cpu().numpy()
+            for s in done:
+                results[slot_page[s]] = host[s, :n_out[slot_page[s]]].copy()
+                slot_page[s] = -1
+            free += done
+            if queue < n and (len(free) >= refill_min or all(p < 0 for p in slot_page)):
+                refill(free)
+                free = []
+        return results, seq_steps

@@ -122,3 +122,29 @@ def test_concurrent32_lossless():
             assert margin < TOL, (i, r_ar[i], int(ar[b0][i]), margin)
             break
     log(f"concurrent32: {B} sequences lossless, {int(n_out.sum())} tokens, oracle agrees on sequence {b0}")
+
+
+@pytest.mark.parametrize("dtype,conc,K", [("bf16", 3, 3), ("f32", 2, 1)], ids=["matrix", "vector"])
+def test_continuous_batching_refill(dtype, conc, K):
+    """Continuous batching: 9 pages through `conc` slots; a finished page's slot is
+    prefilled with the next page while the others decode.  Every page's tokens
+    equal bitwise those of the page decoded alone on a one-slot handle of the
+    same arithmetic path, and the autoregressive stream on the batch handle."""
+    cfg = dataclasses.replace(SMALL16, dtype=dtype)
+    w = synth.Weights(cfg, 57)
+    n = 9
+    rng = np.random.default_rng(58)
+    nv = rng.integers(3, 30, size=n).tolist()
+    npr = rng.integers(1, 6, size=n).tolist()
+    n_out = rng.integers(5, 18, size=n)
+    pages = synth.make_pages(cfg, 59, nv, npr, n_out.tolist())
+    path = ocrdec.OCRDEC_PATH_MATRIX if dtype == "bf16" else ocrdec.OCRDEC_PATH_VECTOR
+    dec = ocrdec.Decoder(cfg, w.device_arrays(), max_batch=conc, max_k=K, max_positions=128, path=path)
+    toks, _ = dec.generate_stream(pages, n_out, K, conc, check_every=2, refill_min=2)
+    ar, _ = dec.generate_stream(pages, n_out, 0, conc, check_every=3)
+    one = ocrdec.Decoder(cfg, w.device_arrays(), max_batch=1, max_k=K, max_positions=128, path=path)
+    for i in range(n):
+        assert toks[i].tolist() == ar[i].tolist(), i
+        t1, _, _ = one.generate([pages[i]], int(n_out[i]), K, check_every=1)
+        assert t1[0].tolist() == toks[i].tolist(), i
+    log(f"continuous batching ({dtype}, {conc} slots, K={K}): {n} pages lossless and slot-invariant")
