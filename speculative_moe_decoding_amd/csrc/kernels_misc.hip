@@ -120,10 +120,9 @@ __global__ __launch_bounds__(256) void k_plan_draft_step(int j, int Qprev, int K
   }
 }
 
-// Prefill pass over a group of sequences: rows j*8 + i (sequence j of the
-// group, i < cnt[j]) hold positions p0 + i of that sequence -- vision rows,
-// then prompt ids; rows past cnt[j] are zero.  esave keeps the input rows for
-// the draft prefill.  Grid (8, n).
+// Prefill pass: rows j*8 + i (entry j, i < cnt[j]) hold positions p0[j] + i
+// of sequence seq[j] -- vision rows, then prompt ids; rows past cnt[j] are
+// zero.  esave keeps the input rows for the draft prefill.  Grid (8, n).
 template <typename T>
 __global__ __launch_bounds__(256) void k_plan_prefill(PrefillGroup g, const float* __restrict__ vision,
                                                       int nv_stride, const int* __restrict__ prompt, int np_stride,
@@ -131,11 +130,11 @@ __global__ __launch_bounds__(256) void k_plan_prefill(PrefillGroup g, const floa
                                                       int* plan_cnt, int* plan_slot, float* __restrict__ x,
                                                       float* __restrict__ esave) {
   const int i = blockIdx.x, j = blockIdx.y;
-  const int p = g.p0 + i;
+  const int p = g.p0[j] + i;
   const int b = g.seq[j];
   if (i == 0 && threadIdx.x == 0) {
     plan_slot[j] = g.slot[j];
-    plan_base[j] = g.p0;
+    plan_base[j] = g.p0[j];
     plan_cnt[j] = g.cnt[j];
   }
   const long row = (long)j * PREFILL_CHUNK + i;
@@ -152,10 +151,11 @@ __global__ __launch_bounds__(256) void k_plan_prefill(PrefillGroup g, const floa
   for (int k = threadIdx.x; k < D; k += 256) esave[row * D + k] = dst[k];
 }
 
-// Draft prefill rows of a group pass: row (j, i) at position p = p0 + i takes
-// (h_{p-1}, e_p); h of a pass's first row is the last verifier hidden of the
-// sequence's previous pass (hprev[slot]; a zero row at p = 0).  The pass's last
-// verifier hidden goes to hnext[slot].  Grid (8, n).
+// Draft prefill rows of a pass: row (j, i) at position p = p0[j] + i takes
+// (h_{p-1}, e_p); h of an entry's first row is the last verifier hidden of
+// the entry before it when that is the same sequence, else of the sequence's
+// previous pass (hprev[slot]; a zero row at p = 0).  The last verifier hidden
+// of a sequence's last entry in the pass goes to hnext[slot].  Grid (8, n).
 __global__ __launch_bounds__(256) void k_draft_prefill_cat(PrefillGroup g, const float* __restrict__ xfinal,
                                                            const float* __restrict__ esave,
                                                            const float* __restrict__ hprev,
@@ -170,7 +170,9 @@ __global__ __launch_bounds__(256) void k_draft_prefill_cat(PrefillGroup g, const
   const float* h;
   if (i > 0) {
     h = xfinal + (row - 1) * D;
-  } else if (g.p0 > 0) {
+  } else if (j > 0 && g.seq[j - 1] == g.seq[j]) {
+    h = xfinal + ((long)(j - 1) * PREFILL_CHUNK + g.cnt[j - 1] - 1) * D;
+  } else if (g.p0[j] > 0) {
     h = hprev + (long)slot * D;
   } else {
     for (int k = threadIdx.x; k < D; k += 256) zero[k] = 0.f;
@@ -180,19 +182,19 @@ __global__ __launch_bounds__(256) void k_draft_prefill_cat(PrefillGroup g, const
   float* dst = cat + row * 2 * D;
   norm_row(h, g_h, eps, dst, red);
   norm_row(esave + row * D, g_e, eps, dst + D, red);
-  if (i == g.cnt[j] - 1)
+  if (i == g.cnt[j] - 1 && (j + 1 == g.n || g.seq[j + 1] != g.seq[j]))
     for (int k = threadIdx.x; k < D; k += 256) hnext[(long)slot * D + k] = xfinal[row * D + k];
 }
 
-// Sequences of a group whose prefix ends in this pass: state of the slot, and
-// output token 0 (the greedy token of the last prefix row, tok[j]) to
+// Entries that end their sequence's prefix: state of the slot, and output
+// token 0 (the greedy token of the last prefix row, tok[j]) to
 // pending_out[seq].  Grid n.
 __global__ __launch_bounds__(256) void k_prefill_finish(PrefillGroup g, const float* __restrict__ xfinal,
                                                         const int* __restrict__ tok, StateView sv,
                                                         int* __restrict__ pending_out) {
   const int j = blockIdx.x;
   const int P = g.plen[j];
-  if (g.p0 + g.cnt[j] != P) return;
+  if (g.p0[j] + g.cnt[j] != P) return;
   const int slot = g.slot[j];
   const int y0 = tok[j];
   if (threadIdx.x == 0) {

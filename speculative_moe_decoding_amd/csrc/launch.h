@@ -98,13 +98,16 @@ void launch_plan_draft_step(hipStream_t s, int B, int j, int Qprev, int K, State
                             const T* embed, int V, const float* g_h, const float* g_e, float eps,
                             const float* u_prev, int* plan_base, int* plan_cnt, const int* plan_slot,
                             float* cat);
-// One prefill pass over up to PREFILL_GROUP sequences: chunk rows p0 ..
-// p0 + cnt[j] - 1 of sequence seq[j] (slot slot[j], n_vision nvis[j], prefix
-// length plen[j]); activation row j * PREFILL_CHUNK + i holds position p0 + i.
+// One prefill pass of up to PREFILL_GROUP entries; entry j is the rows p0[j]
+// .. p0[j] + cnt[j] - 1 (cnt <= PREFILL_CHUNK) of sequence seq[j] (slot
+// slot[j], n_vision nvis[j], prefix length plen[j]), in activation rows
+// j * PREFILL_CHUNK + i.  Entries of one sequence are consecutive and in
+// position order, so a long prefix fills several entries of one pass.
 constexpr int PREFILL_GROUP = 32;
 struct PrefillGroup {
-  int n, p0;
-  int seq[PREFILL_GROUP], slot[PREFILL_GROUP], cnt[PREFILL_GROUP], nvis[PREFILL_GROUP], plen[PREFILL_GROUP];
+  int n;
+  int seq[PREFILL_GROUP], slot[PREFILL_GROUP], p0[PREFILL_GROUP], cnt[PREFILL_GROUP], nvis[PREFILL_GROUP],
+      plen[PREFILL_GROUP];
 };
 template <typename T>
 void launch_plan_prefill(hipStream_t s, const PrefillGroup& g, const float* vision, int nv_stride,

@@ -70,8 +70,8 @@ bool use_matrix_path(const ocrdec_config* c) {
 Plan make_plan(const ocrdec_config* c) {
   Plan p{};
   p.Qmax = std::max(c->max_k + 1, PREFILL_CHUNK);
-  // prefill passes take up to prefill_group sequences at PREFILL_CHUNK rows each
-  p.prefill_group = std::min(c->max_batch, PREFILL_GROUP);
+  // prefill passes take up to prefill_group entries of PREFILL_CHUNK rows
+  p.prefill_group = PREFILL_GROUP;
   p.M_max = std::max(c->max_batch * (c->max_k + 1), PREFILL_CHUNK * p.prefill_group);
   p.cu_stride = c->max_k + 1;
   p.tiles_per_chunk = c->max_positions > 4096 ? 4 : 1;
@@ -115,7 +115,7 @@ Plan make_plan(const ocrdec_config* c) {
   p.w_hsave = take((size_t)2 * c->max_batch * D * 4);
   p.w_lmv = take(M * (size_t)p.lm_nblk * 4);
   p.w_lmi = take(M * (size_t)p.lm_nblk * 4);
-  p.w_plan = take((size_t)3 * std::max(c->max_batch, PREFILL_CHUNK) * 4);
+  p.w_plan = take((size_t)3 * std::max(c->max_batch, PREFILL_GROUP) * 4);
   p.w_total = o;
   return p;
 }
@@ -269,50 +269,50 @@ void draft_layer(ocrdec_model* m, hipStream_t s, int M, int B, RowPlan plan, int
                  D);
 }
 
-// Prefill in passes of PREFILL_CHUNK positions: pass t takes rows 8t .. 8t+7 of
-// every sequence whose prefix reaches that far, up to prefill_group sequences
-// per launch group (each row's arithmetic is the same whatever its group).
+// Prefill in passes of up to prefill_group entries of PREFILL_CHUNK rows: the
+// (sequence, chunk) pairs in sequence order, cut into passes, so a long prefix
+// spreads over several entries of one pass and short ones share passes.  All
+// rows' keys / values are written before the pass's attention reads them, and
+// each row's arithmetic is the same whatever its pass.
 template <typename T>
 int do_prefill(ocrdec_model* m, hipStream_t s, int B, const int32_t* slots_host, const float* vision, int nv_stride,
                const int32_t* nv_host, const int32_t* prompt, int np_stride, const int32_t* np_host,
                int32_t* pending_out) {
   const ocrdec_config& c = m->cfg;
-  int maxP = 0;
-  for (int b = 0; b < B; ++b) maxP = std::max(maxP, nv_host[b] + np_host[b]);
-  std::vector<int> act;
-  for (int p0 = 0, t = 0; p0 < maxP; p0 += PREFILL_CHUNK, ++t) {
+  std::vector<std::pair<int, int>> ent;  // (sequence, first position)
+  for (int b = 0; b < B; ++b)
+    for (int p0 = 0; p0 < nv_host[b] + np_host[b]; p0 += PREFILL_CHUNK) ent.emplace_back(b, p0);
+  int t = 0;
+  for (size_t e0 = 0; e0 < ent.size(); e0 += m->p.prefill_group, ++t) {
     const float* hprev = m->hsave[t & 1];
     float* hnext = m->hsave[(t + 1) & 1];
-    act.clear();
-    for (int b = 0; b < B; ++b)
-      if (nv_host[b] + np_host[b] > p0) act.push_back(b);
-    for (size_t g0 = 0; g0 < act.size(); g0 += m->p.prefill_group) {
-      PrefillGroup g{};
-      g.n = (int)std::min(act.size() - g0, (size_t)m->p.prefill_group);
-      g.p0 = p0;
-      bool finish = false;
-      for (int j = 0; j < g.n; ++j) {
-        const int b = act[g0 + j];
-        const int P = nv_host[b] + np_host[b];
-        g.seq[j] = b;
-        g.slot[j] = slots_host ? slots_host[b] : b;
-        g.cnt[j] = std::min(PREFILL_CHUNK, P - p0);
-        g.nvis[j] = nv_host[b];
-        g.plen[j] = P;
-        finish = finish || (p0 + g.cnt[j] == P);
-      }
-      launch_plan_prefill<T>(s, g, vision, nv_stride, prompt, np_stride, wmat<T>(m, W_EMBED), c.vocab, m->plan_base,
-                             m->plan_cnt, m->plan_slot, m->x, m->esave);
-      const int M = g.n * PREFILL_CHUNK;
-      RowPlan plan{m->plan_base, m->plan_cnt, m->plan_slot, PREFILL_CHUNK};
-      const int nch = chunks_for(m, std::min(c.max_positions - 1, p0 + PREFILL_CHUNK - 1));
-      verifier_layers<T>(m, s, M, g.n, plan, nch, false, nullptr);
-      if (finish) lm_head<T>(m, s, m->x, PREFILL_CHUNK, true, wvec(m, W_FNORM), g.n, nullptr, m->tok_tmp, 1);
-      launch_draft_prefill_cat(s, g, m->x, m->esave, hprev, hnext, wvec(m, dw(m, D_NH)), wvec(m, dw(m, D_NE)),
-                               c.norm_eps, m->cat);
-      draft_layer<T>(m, s, M, g.n, plan, nch);
-      if (finish) launch_prefill_finish(s, g, m->x, m->tok_tmp, m->sv, pending_out);
+    PrefillGroup g{};
+    g.n = (int)std::min(ent.size() - e0, (size_t)m->p.prefill_group);
+    bool finish = false;
+    int max_pos = 0;
+    for (int j = 0; j < g.n; ++j) {
+      const int b = ent[e0 + j].first, p0 = ent[e0 + j].second;
+      const int P = nv_host[b] + np_host[b];
+      g.seq[j] = b;
+      g.slot[j] = slots_host ? slots_host[b] : b;
+      g.p0[j] = p0;
+      g.cnt[j] = std::min(PREFILL_CHUNK, P - p0);
+      g.nvis[j] = nv_host[b];
+      g.plen[j] = P;
+      finish = finish || (p0 + g.cnt[j] == P);
+      max_pos = std::max(max_pos, p0 + g.cnt[j] - 1);
     }
+    launch_plan_prefill<T>(s, g, vision, nv_stride, prompt, np_stride, wmat<T>(m, W_EMBED), c.vocab, m->plan_base,
+                           m->plan_cnt, m->plan_slot, m->x, m->esave);
+    const int M = g.n * PREFILL_CHUNK;
+    RowPlan plan{m->plan_base, m->plan_cnt, m->plan_slot, PREFILL_CHUNK};
+    const int nch = chunks_for(m, std::min(c.max_positions - 1, max_pos));
+    verifier_layers<T>(m, s, M, g.n, plan, nch, false, nullptr);
+    if (finish) lm_head<T>(m, s, m->x, PREFILL_CHUNK, true, wvec(m, W_FNORM), g.n, nullptr, m->tok_tmp, 1);
+    launch_draft_prefill_cat(s, g, m->x, m->esave, hprev, hnext, wvec(m, dw(m, D_NH)), wvec(m, dw(m, D_NE)),
+                             c.norm_eps, m->cat);
+    draft_layer<T>(m, s, M, g.n, plan, nch);
+    if (finish) launch_prefill_finish(s, g, m->x, m->tok_tmp, m->sv, pending_out);
   }
   for (int b = 0; b < B; ++b) m->slot_bound[slots_host ? slots_host[b] : b] = nv_host[b] + np_host[b];
   return hip_check("ocrdec_prefill");
@@ -441,7 +441,7 @@ int ocrdec_create(const ocrdec_config* cfg, const void* const* weight_ptrs, int 
   m->hsave[1] = wf(p.w_hsave) + (size_t)cfg->max_batch * D;
   m->lm_val = wf(p.w_lmv);
   m->lm_idx = wi(p.w_lmi);
-  const int pm = std::max(mb, PREFILL_CHUNK);
+  const int pm = std::max(mb, PREFILL_GROUP);
   m->plan_base = wi(p.w_plan);
   m->plan_cnt = wi(p.w_plan) + pm;
   m->plan_slot = wi(p.w_plan) + 2 * pm;
