@@ -102,36 +102,6 @@ __device__ __forceinline__ float block_sum256(float v, float* red) {
   return t;
 }
 
-// RMSNorm of `m_rows` rows of length K (K % 256 == 0) into LDS:
-// xs[m][k] = (x[m][k] * r_m) * g[k] with r_m = 1 / sqrt(sum_k x^2 / K + eps).
-// g == nullptr copies the rows unchanged.  All 256 threads must call it.
-template <int K>
-__device__ __forceinline__ void norm_rows_to_lds(const float* __restrict__ x, long ldx, int m_rows,
-                                                 const float* __restrict__ g, float eps, float* xs,
-                                                 float* red) {
-  static_assert(K % 256 == 0, "row length must be a multiple of 256");
-  constexpr int J = K / 256;
-  const int tid = threadIdx.x;
-  for (int m = 0; m < m_rows; ++m) {
-    const float* xr = x + (long)m * ldx;
-    float v[J];
-#pragma unroll
-    for (int j = 0; j < J; ++j) v[j] = xr[tid + 256 * j];
-    if (g != nullptr) {
-      float ss = 0.f;
-#pragma unroll
-      for (int j = 0; j < J; ++j) ss = fmaf(v[j], v[j], ss);
-      ss = block_sum256(ss, red);
-      const float r = 1.0f / sqrtf(ss / (float)K + eps);
-#pragma unroll
-      for (int j = 0; j < J; ++j) xs[m * K + tid + 256 * j] = (v[j] * r) * g[tid + 256 * j];
-    } else {
-#pragma unroll
-      for (int j = 0; j < J; ++j) xs[m * K + tid + 256 * j] = v[j];
-    }
-  }
-}
-
 // RMSNorm of `m_rows` activation rows into LDS, one wavefront per row (rows
 // w, w + n_waves, ...): lane l sums x[k]^2 over k = l + 64 j in order, the 64
 // lane sums go through the xor butterfly, r = 1 / sqrt(sum / K + eps), and
