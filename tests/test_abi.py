@@ -71,3 +71,36 @@ def test_rejects_bad_configs(lib):
     # calls on a null handle
     assert lib.ocrdec_verify(None, None, 1, None, 0, None, None, None) == ocrdec.OCRDEC_EINVAL
     assert lib.ocrdec_draft(None, None, 1, None, 3, None) == ocrdec.OCRDEC_EINVAL
+
+
+def test_rejects_bad_paths_and_null_handles(lib):
+    import dataclasses
+    # the matrix-core path needs bf16 weights and a vocabulary of at least 64
+    f32 = dataclasses.replace(synth.FULL, dtype="f32")
+    c = ocrdec.make_config(f32, 4, 3, 2048, ocrdec.OCRDEC_PATH_MATRIX)
+    assert ocrdec.ocrdec_state_bytes(c) == 0
+    assert "matrix" in lib.ocrdec_last_error().decode()
+    small = dataclasses.replace(synth.FULL, vocab=32)
+    assert ocrdec.ocrdec_state_bytes(ocrdec.make_config(small, 4, 3, 2048, ocrdec.OCRDEC_PATH_MATRIX)) == 0
+    assert ocrdec.ocrdec_state_bytes(ocrdec.make_config(synth.FULL, 4, 3, 2048, 7)) == 0
+    for p in (ocrdec.OCRDEC_PATH_AUTO, ocrdec.OCRDEC_PATH_VECTOR, ocrdec.OCRDEC_PATH_MATRIX):
+        assert ocrdec.ocrdec_state_bytes(ocrdec.make_config(synth.FULL, 4, 3, 2048, p)) > 0
+    # every handle-taking entry point rejects a null handle without touching the device
+    E = ocrdec.OCRDEC_EINVAL
+    assert lib.ocrdec_destroy(None) == E
+    assert lib.ocrdec_accept_rollback(None, None, 1, None, 0, None, None, None, None, None, 1) == E
+    assert lib.ocrdec_controlled_drafts(None, None, 1, None, 1, None, 1, 1, 0, 0, None) == E
+    assert lib.ocrdec_decode_steps(None, None, 1, None, 1, 1, None, None, None, None, None, None, 1) == E
+    assert lib.ocrdec_sync_positions(None, None) == E
+    assert lib.ocrdec_load_sequence(None, None, 0, 16, 0, None) == E
+    assert lib.ocrdec_set_router_logits(None, None) == E
+    assert lib.ocrdec_set_taps(None, None, None) == E
+    assert lib.ocrdec_expert_timing(None, 1) == E
+    assert lib.ocrdec_replay_expert_gate_up(None, None, 1, None) == E
+
+
+def test_prefill_argument_checks_need_no_device(lib):
+    # a null handle, then a too-long prefix: both refused before any launch
+    nv = (ctypes.c_int32 * 1)(10)
+    npr = (ctypes.c_int32 * 1)(0)
+    assert lib.ocrdec_prefill(None, None, 1, None, None, 10, nv, None, 1, npr, None) == ocrdec.OCRDEC_EINVAL
