@@ -136,9 +136,9 @@ def main() -> int:
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+        print(f"bench.py runs on one GPU only: there is no multi-GPU path "
               f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}); the decode of independent pages "
-              f"shards data-parallel with no exchange, see DESIGN.md.", file=sys.stderr)
+              f"would shard data-parallel, one page set per GPU, with no exchange between GPUs.", file=sys.stderr)
         return 2
 
     if args.sweep_k:

@@ -26,7 +26,7 @@ Sources (jina-ocr-v1 pages):
   * blog, "Getting started": the draft head is trained with recursive
     hidden-state feedback (registered as an EAGLE-style proposer).
 
-Readings of what the pages leave open (each is also listed in the design doc):
+Readings of what the pages leave open:
   pre-norm residual blocks with RMSNorm (eps 1e-6, per-channel gain); MHA with
   10 heads of 128, no biases, scale 1/sqrt(128), causal; rotate-half RoPE over
   all 128 dims with inv_freq_i = theta^(-2i/128); every decoder layer is MoE;

@@ -8,9 +8,9 @@ Shapes come from the model tables of the jina-ocr-v1 announcement and blog
 ("Model parameters" / spec table: 12 layers, d=1280, 64 routed + 2 shared
 experts, top-6, vocabulary 129,280, RoPE theta 1e6, one recursive draft
 block).  Head count (10 x 128), expert width 896 and draft FFN width 3,584
-are this build's reading of what the pages leave open; with them the decoder
-has ~575M active and ~3.14B total parameters, matching the pages' "~570M /
-~3B (decoder)".
+are a reading of what the pages leave open; with them the decoder has ~575M
+active and ~3.14B total parameters, in line with the active and total decoder
+sizes the pages state (about 570M and 3B).
 
 Recipe (stated once, used everywhere):
   * every tensor t (index i in ``weight_specs`` order) is split into blocks of
@@ -55,7 +55,7 @@ class ModelConfig:
         return self.n_heads * self.head_dim
 
 
-# The decoder of the pages at the widths this build reads for it.
+# The decoder of the pages at the widths read for it above.
 FULL = ModelConfig()
 
 
