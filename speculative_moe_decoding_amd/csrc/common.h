@@ -146,7 +146,7 @@ struct RowIdentity {
 
 // Wavefront GEMV core: R weight rows (pointers rows[r], each K elements of T)
 // against `m_act` (<= MR) activation rows held in LDS (xs[m][K], fp32).
-// acc[r][m] holds the lane partial sums; call wave_reduce_acc afterwards.
+// acc[r][m] holds the lane partial sums; WaveTotals adds them up.
 // Loads of all R rows are issued before any arithmetic.
 template <typename T, int K, int R, int MR>
 struct WaveGemv {
@@ -202,16 +202,64 @@ struct WaveGemv {
   }
 };
 
-template <int R, int MR>
-__device__ __forceinline__ void wave_reduce_acc(float (&acc)[R][MR], int m_act) {
+// Sums each of N (a power of two <= 64) per-lane values over the wavefront
+// with the tree of wave_sum (xor offsets 32, 16, ..., 1; at every node own +
+// partner), transposed: at each of the first log2 N steps a lane keeps half of
+// its values and trades the other half with its partner, so the wavefront
+// spends N - 1 + 6 - log2 N shuffles instead of 6 N.  The sums are bitwise
+// those of wave_sum.  Lane l returns the total of value i = l >> (6 - log2 N);
+// v is overwritten.
+template <int N>
+__device__ __forceinline__ float wave_reduce_t(float (&v)[N]) {
+  static_assert(N >= 1 && N <= 64 && (N & (N - 1)) == 0, "N must be a power of two <= 64");
+  constexpr int B = __builtin_ctz(N);
+  const int lane = lane_id();
 #pragma unroll
-  for (int m = 0; m < MR; ++m) {
-    if (m < m_act) {
+  for (int s = 0; s < B; ++s) {
+    const int n = N >> s;
+    const int off = 32 >> s;
+    const bool up = (lane & off) != 0;
 #pragma unroll
-      for (int r = 0; r < R; ++r) acc[r][m] = wave_sum(acc[r][m]);
+    for (int j = 0; j < n / 2; ++j) {
+      const float lo = v[j], hi = v[j + n / 2];
+      const float recv = __shfl_xor(up ? lo : hi, off, 64);
+      v[j] = (up ? hi : lo) + recv;
     }
   }
+  float t = v[0];
+#pragma unroll
+  for (int off = 32 >> B; off >= 1; off >>= 1) t += __shfl_xor(t, off, 64);
+  return t;
 }
+
+// Totals of a WaveGemv's lane partials acc[r][m] (R a power of two): lane l
+// receives the total of value i = l >> SH, i = m R + r, SH = 6 - log2(R MR),
+// through the transposed reduction (bitwise the per-value butterfly); `lead`
+// marks one lane per value.  All lanes construct it.
+template <int R, int MR>
+struct WaveTotals {
+  static constexpr int N = R * MR;
+  static constexpr int SH = 6 - __builtin_ctz(N);
+  static_assert((R & (R - 1)) == 0, "R must be a power of two");
+  float val;
+  int r, m;
+  bool lead;
+  __device__ __forceinline__ explicit WaveTotals(float (&acc)[R][MR]) {
+    float v[N];
+#pragma unroll
+    for (int mm = 0; mm < MR; ++mm)
+#pragma unroll
+      for (int rr = 0; rr < R; ++rr) v[mm * R + rr] = acc[rr][mm];
+    val = wave_reduce_t<N>(v);
+    const int lane = lane_id();
+    const int i = lane >> SH;
+    r = i % R;
+    m = i / R;
+    lead = (lane & ((1 << SH) - 1)) == 0;
+  }
+  // The total of (r ^ x, m), from the lane that holds it; all lanes call it.
+  __device__ __forceinline__ float partner(int x) const { return __shfl_xor(val, x << SH, 64); }
+};
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 

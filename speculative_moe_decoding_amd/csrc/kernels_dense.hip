@@ -77,29 +77,28 @@ __global__ __launch_bounds__(256) void k_qkv_rope(const float* __restrict__ x, c
   __syncthreads();
   float acc[2][MR];
   g.fma(xs, m_act, acc);
-  wave_reduce_acc<2, MR>(acc, m_act);
-  const long slot_stride = 2L * NH * max_pos * HD;
-#pragma unroll
-  for (int m = 0; m < MR; ++m) {
-    if (lane == m && m < m_act) {
-      const int row = m0 + m;
-      const long slot = plan.slot[b];
-      if (sec < 2) {
-        float o0, o1;
-        rot(acc[0][m], acc[1][m], cs.x, cs.y, o0, o1);
-        if (sec == 0) {
-          q[(long)row * QD + h * HD + u] = o0;
-          q[(long)row * QD + h * HD + u + 64] = o1;
-        } else if (valid) {
-          T* kd = kv + slot * slot_stride + ((long)h * max_pos + pos) * HD;
-          kd[u] = WT<T>::store_cvt(o0);
-          kd[u + 64] = WT<T>::store_cvt(o1);
-        }
-      } else if (valid) {
-        T* vd = kv + slot * slot_stride + ((long)(NH + h) * max_pos + pos) * HD + 2 * u;
-        vd[0] = WT<T>::store_cvt(acc[0][m]);
-        vd[1] = WT<T>::store_cvt(acc[1][m]);
+  // lane with (r, m): row m's position data from lane m, the pair's other total
+  const WaveTotals<2, MR> t(acc);
+  const float other = t.partner(1);
+  const int tb = __shfl(b, t.m, 64), tpos = __shfl(pos, t.m, 64);
+  const bool tvalid = __shfl((int)valid, t.m, 64) != 0;
+  const float tc = __shfl(cs.x, t.m, 64), ts = __shfl(cs.y, t.m, 64);
+  if (t.lead && t.m < m_act) {
+    const int row = m0 + t.m;
+    const long slot_stride = 2L * NH * max_pos * HD;
+    const long slot = plan.slot[tb];
+    if (sec < 2) {
+      // rows u (r = 0) and u + 64 (r = 1) of a head: each lane rotates its own
+      float o;
+      if (t.r == 0) o = fmaf(t.val, tc, -(other * ts));
+      else o = fmaf(t.val, tc, other * ts);
+      if (sec == 0) {
+        q[(long)row * QD + h * HD + u + 64 * t.r] = o;
+      } else if (tvalid) {
+        kv[slot * slot_stride + ((long)h * max_pos + tpos) * HD + u + 64 * t.r] = WT<T>::store_cvt(o);
       }
+    } else if (tvalid) {
+      kv[slot * slot_stride + ((long)(NH + h) * max_pos + tpos) * HD + 2 * u + t.r] = WT<T>::store_cvt(t.val);
     }
   }
 }
@@ -126,7 +125,7 @@ __global__ __launch_bounds__(256) void k_gemv(const float* __restrict__ a, long 
                                               int M, float* __restrict__ out, long ldo) {
   extern __shared__ float smem[];
   float* xs = smem;
-  const int wave = wave_id(), lane = lane_id();
+  const int wave = wave_id();
   constexpr int UNITS = (EPI == EPI_SWIGLU) ? R / 2 : R;
   const int n0 = (blockIdx.x * 4 + wave) * UNITS;
   const int m0 = blockIdx.y * MR;
@@ -152,21 +151,15 @@ __global__ __launch_bounds__(256) void k_gemv(const float* __restrict__ a, long 
   __syncthreads();
   float acc[R][MR];
   g.fma(xs, m_act, acc);
-  wave_reduce_acc<R, MR>(acc, m_act);
-#pragma unroll
-  for (int m = 0; m < MR; ++m) {
-    if (lane == m && m < m_act) {
-      float* o = out + (long)(m0 + m) * ldo;
-#pragma unroll
-      for (int r = 0; r < UNITS; ++r) {
-        const int n = n0 + r;
-        if (n < N) {
-          if (EPI == EPI_SWIGLU) o[n] = silu(acc[r][m]) * acc[r + UNITS][m];
-          else if (EPI == EPI_ADD) o[n] = o[n] + acc[r][m];
-          else o[n] = acc[r][m];
-        }
-      }
-    }
+  const WaveTotals<R, MR> t(acc);
+  float up = 0.f;
+  if constexpr (EPI == EPI_SWIGLU) up = t.partner(UNITS);  // gate unit r pairs with up unit r (rows r, r + UNITS)
+  const int n = n0 + t.r;
+  if (t.lead && t.r < UNITS && t.m < m_act && n < N) {
+    float* o = out + (long)(m0 + t.m) * ldo + n;
+    if (EPI == EPI_SWIGLU) *o = silu(t.val) * up;
+    else if (EPI == EPI_ADD) *o = *o + t.val;
+    else *o = t.val;
   }
 }
 
@@ -255,10 +248,11 @@ __global__ __launch_bounds__(256) void k_lmhead(const float* __restrict__ x, con
   }
   norm_rows_wave<D>(x, D, LmSrcRow{cnt, Q, last_valid, m0}, m_act, gain, eps, xs, 4);
   __syncthreads();
-  float best[MR];
-  int besti[MR];
-#pragma unroll
-  for (int m = 0; m < MR; ++m) { best[m] = -INFINITY; besti[m] = 0x7fffffff; }
+  // Each lane keeps the running best of the (tile row r, activation row m)
+  // whose totals it receives.
+  constexpr int SH = WaveTotals<4, MR>::SH;
+  float best = -INFINITY;
+  int besti = 0x7fffffff;
 #pragma unroll
   for (int t = 0; t < LM_TILES; ++t) {
     if (t + 1 < LM_TILES) {
@@ -269,26 +263,23 @@ __global__ __launch_bounds__(256) void k_lmhead(const float* __restrict__ x, con
     }
     float acc[4][MR];
     g[t & 1].fma(xs, m_act, acc);
-    wave_reduce_acc<4, MR>(acc, m_act);
-    const int v0 = vbase + t * 16;
-#pragma unroll
-    for (int m = 0; m < MR; ++m) {
-      if (m < m_act) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int v = v0 + r;
-          if (v < V) {
-            const float val = acc[r][m];
-            if (val > best[m]) { best[m] = val; besti[m] = v; }  // v increases: ties keep the lower id
-            if (logits != nullptr && lane == r) logits[(long)(m0 + m) * V + v] = val;
-          }
-        }
-      }
+    const WaveTotals<4, MR> tot(acc);
+    const int v = vbase + t * 16 + tot.r;
+    if (tot.m < m_act && v < V) {
+      if (tot.val > best) { best = tot.val; besti = v; }  // v increases with t: ties keep the lower id
+      if (logits != nullptr && tot.lead) logits[(long)(m0 + tot.m) * V + v] = tot.val;
     }
   }
-  if (lane == 0) {
+  // best over the four tile rows of each m (lanes differing in the bits of r)
 #pragma unroll
-    for (int m = 0; m < MR; ++m) { bv[wave][m] = best[m]; bi[wave][m] = besti[m]; }
+  for (int off = 1 << SH; off <= 2 << SH; off <<= 1) {
+    const float ob = __shfl_xor(best, off, 64);
+    const int oi = __shfl_xor(besti, off, 64);
+    if (ob > best || (ob == best && oi < besti)) { best = ob; besti = oi; }
+  }
+  {
+    const int i = lane >> SH;
+    if ((lane & ((1 << SH) - 1)) == 0 && (i & 3) == 0) { bv[wave][i >> 2] = best; bi[wave][i >> 2] = besti; }
   }
   __syncthreads();
   if (threadIdx.x < m_act) {

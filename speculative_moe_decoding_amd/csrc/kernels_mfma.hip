@@ -4,13 +4,17 @@
 //
 // Tile engine: a block of four wavefronts owns a strip of weight rows (16 per
 // wavefront and per matrix) and streams the strip once per pass of up to 64
-// activation rows.  The rows are staged in LDS in chunks of 128 k, rounded to
-// bf16 (round to nearest even) and laid out as ready MFMA A fragments, two
-// chunk buffers deep; weights go straight from HBM into B fragments.  Each
-// 16x16 output block accumulates v_mfma_f32_16x16x32_bf16 over k in a fixed
-// order, so a row's result depends only on that row and the weights: the row
-// count of a call never changes it (speculative == autoregressive, bit for
-// bit, on one handle).
+// activation rows.  The rows are staged in LDS in chunks of 128 k as ready MFMA
+// A fragments, two chunk buffers deep; weights go straight from HBM into B
+// fragments.  Expert inputs are split into two bf16 parts, hi = bf16(a) and
+// lo = bf16(a - hi) (round to nearest even), and both are multiplied (about 16
+// significant bits of the fp32 activation survive, so the rounding does not
+// compound over the layers); the LM head takes hi alone (one rounding at the
+// end of the network).  Each 16x16 output block accumulates
+// v_mfma_f32_16x16x32_bf16 over k (hi then lo per k-step) in a fixed order, so
+// a row's result depends only on that row and the weights: the row count of a
+// call never changes it (speculative == autoregressive, bit for bit, on one
+// handle).
 //
 // v_mfma_f32_16x16x32_bf16 operand layout (wave64): lane l supplies
 // A[l % 16][8 (l / 16) .. +7] and B[8 (l / 16) .. +7][l % 16]; it receives
@@ -76,8 +80,13 @@ __device__ __forceinline__ void mf_load_a(float4 (&ar)[NT][2], const float* cons
   }
 }
 
-template <int NT>
-__device__ __forceinline__ void mf_store_a(MfChunk& ch, const float4 (&ar)[NT][2], int kg, int ri) {
+// a - bf16(a) for the two halves of a packed pair (exact in fp32).
+__device__ __forceinline__ float rem_lo(float a, uint32_t h) { return a - __uint_as_float(h << 16); }
+__device__ __forceinline__ float rem_hi(float a, uint32_t h) { return a - __uint_as_float(h & 0xffff0000u); }
+
+// Parts NP = 1: ch[0] = bf16(a); NP = 2: also ch[1] = bf16(a - bf16(a)).
+template <int NT, int NP>
+__device__ __forceinline__ void mf_store_a(MfChunk (&ch)[NP], const float4 (&ar)[NT][2], int kg, int ri) {
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
     uint4 v;
@@ -85,23 +94,34 @@ __device__ __forceinline__ void mf_store_a(MfChunk& ch, const float4 (&ar)[NT][2
     v.y = pack_bf16x2(ar[i][0].z, ar[i][0].w);
     v.z = pack_bf16x2(ar[i][1].x, ar[i][1].y);
     v.w = pack_bf16x2(ar[i][1].z, ar[i][1].w);
-    ch.f[i][kg >> 2][(kg & 3) * 16 + ri] = v;
+    ch[0].f[i][kg >> 2][(kg & 3) * 16 + ri] = v;
+    if constexpr (NP == 2) {
+      uint4 u;
+      u.x = pack_bf16x2(rem_lo(ar[i][0].x, v.x), rem_hi(ar[i][0].y, v.x));
+      u.y = pack_bf16x2(rem_lo(ar[i][0].z, v.y), rem_hi(ar[i][0].w, v.y));
+      u.z = pack_bf16x2(rem_lo(ar[i][1].x, v.z), rem_hi(ar[i][1].y, v.z));
+      u.w = pack_bf16x2(rem_lo(ar[i][1].z, v.w), rem_hi(ar[i][1].w, v.w));
+      ch[1].f[i][kg >> 2][(kg & 3) * 16 + ri] = u;
+    }
   }
 }
 
-template <int NT, int NB, int NS>
-__device__ __forceinline__ void mf_compute(const MfChunk& ch, const uint4 (&bq)[NB][NS][MF_SC],
+template <int NT, int NB, int NS, int NP>
+__device__ __forceinline__ void mf_compute(const MfChunk (&ch)[NP], const uint4 (&bq)[NB][NS][MF_SC],
                                            f32x4_v (&acc)[NT][NB][NS]) {
   const int lane = lane_id();
 #pragma unroll
   for (int s = 0; s < MF_SC; ++s) {
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
-      const uint4 a = ch.f[i][s][lane];
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
+      for (int p = 0; p < NP; ++p) {
+        const uint4 a = ch[p].f[i][s][lane];
 #pragma unroll
-        for (int n = 0; n < NS; ++n) acc[i][b][n] = mfma_bf16(a, bq[b][n][s], acc[i][b][n]);
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int n = 0; n < NS; ++n) acc[i][b][n] = mfma_bf16(a, bq[b][n][s], acc[i][b][n]);
+      }
     }
   }
 }
@@ -109,9 +129,10 @@ __device__ __forceinline__ void mf_compute(const MfChunk& ch, const uint4 (&bq)[
 // One pass: rows r < rows <= 16 NT (row r read from rowp(r), fp32, K long)
 // against the wavefront's weight rows w[b] + (16 n + j) K, j < 16, of NB
 // matrices: acc[i][b][n][q] = sum_k A[16 i + 4 (lane / 16) + q][k] *
-// W_b[16 n + lane % 16][k].  All 256 threads must call it; contains barriers.
-template <int K, int NT, int NB, int NS, typename RowPtr>
-__device__ __forceinline__ void mfma_pass(const bf16* const (&w)[NB], RowPtr rowp, int rows, MfChunk (&buf)[2],
+// W_b[16 n + lane % 16][k], with A in NP bf16 parts.  All 256 threads must
+// call it; contains barriers.
+template <int K, int NT, int NB, int NS, int NP, typename RowPtr>
+__device__ __forceinline__ void mfma_pass(const bf16* const (&w)[NB], RowPtr rowp, int rows, MfChunk (&buf)[2][NP],
                                           f32x4_v (&acc)[NT][NB][NS]) {
   static_assert(K % MF_KC == 0, "K must be a multiple of the chunk");
   static_assert(NT <= MF_MT, "too many tiles");
@@ -147,7 +168,7 @@ __device__ __forceinline__ void mfma_pass(const bf16* const (&w)[NB], RowPtr row
       mf_load_a(ar, src, ok, c + 1);  // activations first: waiting for them does not wait for the weights
       mf_load_b<K, NB, NS>(bq1, w, woff, c + 1);
     }
-    mf_compute<NT, NB, NS>(buf[0], bq0, acc);
+    mf_compute<NT, NB, NS, NP>(buf[0], bq0, acc);
     if (c + 1 < NC) mf_store_a(buf[1], ar, kg, ri);
     __syncthreads();
     if (c + 1 < NC) {
@@ -155,7 +176,7 @@ __device__ __forceinline__ void mfma_pass(const bf16* const (&w)[NB], RowPtr row
         mf_load_a(ar, src, ok, c + 2);
         mf_load_b<K, NB, NS>(bq0, w, woff, c + 2);
       }
-      mf_compute<NT, NB, NS>(buf[1], bq1, acc);
+      mf_compute<NT, NB, NS, NP>(buf[1], bq1, acc);
       if (c + 2 < NC) mf_store_a(buf[0], ar, kg, ri);
       __syncthreads();
     }
@@ -168,10 +189,10 @@ __device__ __forceinline__ void mfma_pass(const bf16* const (&w)[NB], RowPtr row
 template <int NT>
 __device__ __forceinline__ void gate_up_pass(const bf16* const (&w)[2], const float* __restrict__ bnorm,
                                              const int* __restrict__ perm, int kb, int rows, float* __restrict__ hx,
-                                             int j0, MfChunk (&buf)[2]) {
+                                             int j0, MfChunk (&buf)[2][2]) {
   const int lane = lane_id();
   f32x4_v acc[NT][2][1];
-  mfma_pass<D, NT, 2, 1>(w, [=](int r) { return bnorm + (long)(perm[kb + r] / NSLOT) * D; }, rows, buf, acc);
+  mfma_pass<D, NT, 2, 1, 2>(w, [=](int r) { return bnorm + (long)(perm[kb + r] / NSLOT) * D; }, rows, buf, acc);
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
 #pragma unroll
@@ -184,7 +205,7 @@ __device__ __forceinline__ void gate_up_pass(const bf16* const (&w)[2], const fl
 
 __global__ __launch_bounds__(256) void k_expert_gate_up_mfma(const bf16* __restrict__ wg,
                                                              const bf16* __restrict__ wu, MoeBufs mb) {
-  __shared__ MfChunk buf[2];
+  __shared__ MfChunk buf[2][2];
   const int4 info = mb.slot_info[blockIdx.y];
   const int e = info.x;
   if (e < 0) return;
@@ -202,10 +223,10 @@ __global__ __launch_bounds__(256) void k_expert_gate_up_mfma(const bf16* __restr
 // y[pair][n] = W_d[n] . hx[pair].
 template <int NT>
 __device__ __forceinline__ void down_pass(const bf16* const (&w)[1], const float* __restrict__ hx, int kb, int rows,
-                                          float* __restrict__ y, int n0, MfChunk (&buf)[2]) {
+                                          float* __restrict__ y, int n0, MfChunk (&buf)[2][2]) {
   const int lane = lane_id();
   f32x4_v acc[NT][1][2];
-  mfma_pass<DI, NT, 1, 2>(w, [=](int r) { return hx + (long)(kb + r) * DI; }, rows, buf, acc);
+  mfma_pass<DI, NT, 1, 2, 2>(w, [=](int r) { return hx + (long)(kb + r) * DI; }, rows, buf, acc);
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
 #pragma unroll
@@ -221,7 +242,7 @@ __device__ __forceinline__ void down_pass(const bf16* const (&w)[1], const float
 }
 
 __global__ __launch_bounds__(256) void k_expert_down_mfma(const bf16* __restrict__ wd, MoeBufs mb) {
-  __shared__ MfChunk buf[2];
+  __shared__ MfChunk buf[2][2];
   const int4 info = mb.slot_info[blockIdx.y];
   const int e = info.x;
   if (e < 0) return;
@@ -273,10 +294,10 @@ __global__ __launch_bounds__(256) void k_lm_norm(const float* __restrict__ x, co
 template <int NT>
 __device__ __forceinline__ void lm_pass(const bf16* const (&w)[1], const float* __restrict__ xn, int p0, int rows,
                                         int vj, bool vok, int V, float* __restrict__ logits, float (&bv)[4][MF_ROWS],
-                                        int (&bi)[4][MF_ROWS], MfChunk (&buf)[2]) {
+                                        int (&bi)[4][MF_ROWS], MfChunk (&buf)[2][1]) {
   const int wave = wave_id(), lane = lane_id();
   f32x4_v acc[NT][1][1];
-  mfma_pass<D, NT, 1, 1>(w, [=](int r) { return xn + (long)(p0 + r) * D; }, rows, buf, acc);
+  mfma_pass<D, NT, 1, 1, 1>(w, [=](int r) { return xn + (long)(p0 + r) * D; }, rows, buf, acc);
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
 #pragma unroll
@@ -301,7 +322,7 @@ __device__ __forceinline__ void lm_pass(const bf16* const (&w)[1], const float* 
 __global__ __launch_bounds__(256) void k_lmhead_mfma(const float* __restrict__ xn, const bf16* __restrict__ W,
                                                      int V, int M, float* __restrict__ part_val,
                                                      int* __restrict__ part_idx, float* __restrict__ logits) {
-  __shared__ MfChunk buf[2];
+  __shared__ MfChunk buf[2][1];
   __shared__ float bv[4][MF_ROWS];
   __shared__ int bi[4][MF_ROWS];
   const int wave = wave_id(), lane = lane_id();

@@ -176,7 +176,7 @@ __global__ __launch_bounds__(256) void k_router_logits(const float* __restrict__
                                                        float eps, const T* __restrict__ wr, int M,
                                                        float* __restrict__ bnorm, float* __restrict__ rlogit) {
   extern __shared__ float xs[];  // [MR][D]
-  const int wave = wave_id(), lane = lane_id();
+  const int wave = wave_id();
   const int e = blockIdx.x * 4 + wave;
   const int m0 = blockIdx.y * MR;
   const int m_act = min(MR, M - m0);
@@ -189,10 +189,8 @@ __global__ __launch_bounds__(256) void k_router_logits(const float* __restrict__
     for (int k = threadIdx.x; k < m_act * D; k += 256) bnorm[(long)m0 * D + k] = xs[k];
   float acc[1][MR];
   g.fma(xs, m_act, acc);
-  wave_reduce_acc<1, MR>(acc, m_act);
-#pragma unroll
-  for (int m = 0; m < MR; ++m)
-    if (lane == 0 && m < m_act) rlogit[(long)(m0 + m) * NE + e] = acc[0][m];
+  const WaveTotals<1, MR> t(acc);
+  if (t.lead && t.m < m_act) rlogit[(long)(m0 + t.m) * NE + e] = t.val;
 }
 
 // M <= 8: top-6 per row and the sort by one block, published to global.
@@ -328,7 +326,7 @@ template <typename T, int MR, int UPW>
 __global__ __launch_bounds__(256) void k_expert_gate_up(const T* __restrict__ wg, const T* __restrict__ wu,
                                                         MoeBufs mb) {
   extern __shared__ float xs[];
-  const int wave = wave_id(), lane = lane_id();
+  const int wave = wave_id();
   const int4 info = mb.slot_info[blockIdx.y];
   const int e = info.x;
   if (e < 0) return;
@@ -354,15 +352,9 @@ __global__ __launch_bounds__(256) void k_expert_gate_up(const T* __restrict__ wg
   __syncthreads();
   float acc[2 * UPW][MR];
   g.fma(xs, m_act, acc);
-  wave_reduce_acc<2 * UPW, MR>(acc, m_act);
-#pragma unroll
-  for (int m = 0; m < MR; ++m) {
-    if (lane == m && m < m_act) {
-      float* o = mb.hx + (long)(k0 + m) * DI + j0;
-#pragma unroll
-      for (int u = 0; u < UPW; ++u) o[u] = silu(acc[u][m]) * acc[UPW + u][m];
-    }
-  }
+  const WaveTotals<2 * UPW, MR> t(acc);
+  const float up = t.partner(UPW);  // gate unit u pairs with up unit u (r = u, UPW + u)
+  if (t.lead && t.r < UPW && t.m < m_act) mb.hx[(long)(k0 + t.m) * DI + j0 + t.r] = silu(t.val) * up;
 }
 
 // Down: block (x, slot s); wavefront w owns output rows n0 .. n0+RPW-1,
@@ -375,7 +367,7 @@ __global__ __launch_bounds__(256) void k_expert_down(const T* __restrict__ wd, M
   if (e < 0) return;
   const int k0 = info.y;
   const int m_act = min(MR, info.z - k0);
-  const int wave = wave_id(), lane = lane_id();
+  const int wave = wave_id();
   const int n0 = (blockIdx.x * 4 + wave) * RPW;
   const T* base = wd + ((long)e * D + n0) * DI;
   const T* rows[RPW];
@@ -387,15 +379,8 @@ __global__ __launch_bounds__(256) void k_expert_down(const T* __restrict__ wd, M
   __syncthreads();
   float acc[RPW][MR];
   g.fma(xs, m_act, acc);
-  wave_reduce_acc<RPW, MR>(acc, m_act);
-#pragma unroll
-  for (int m = 0; m < MR; ++m) {
-    if (lane == m && m < m_act) {
-      float* o = mb.y + (long)(k0 + m) * D + n0;
-#pragma unroll
-      for (int r = 0; r < RPW; ++r) o[r] = acc[r][m];
-    }
-  }
+  const WaveTotals<RPW, MR> t(acc);
+  if (t.lead && t.m < m_act) mb.y[(long)(k0 + t.m) * D + n0 + t.r] = t.val;
 }
 
 // Batches with more than MRG rows: the same per-row arithmetic, MRG pairs at a
@@ -407,7 +392,7 @@ __global__ __launch_bounds__(256) void k_expert_gate_up_groups(const T* __restri
   const int4 info = mb.slot_info[blockIdx.y];
   const int e = info.x;
   if (e < 0) return;
-  const int wave = wave_id(), lane = lane_id();
+  const int wave = wave_id();
   const int j = (blockIdx.x * 4 + wave) * 2;
   for (int kb = info.y; kb < info.z; kb += MRG) {
     const int m_act = min(MRG, info.z - kb);
@@ -421,15 +406,9 @@ __global__ __launch_bounds__(256) void k_expert_gate_up_groups(const T* __restri
     __syncthreads();
     float acc[4][MRG];
     g.fma(xs, m_act, acc);
-    wave_reduce_acc<4, MRG>(acc, m_act);
-#pragma unroll
-    for (int m = 0; m < MRG; ++m) {
-      if (lane == m && m < m_act) {
-        float* o = mb.hx + (long)(kb + m) * DI + j;
-        o[0] = silu(acc[0][m]) * acc[2][m];
-        o[1] = silu(acc[1][m]) * acc[3][m];
-      }
-    }
+    const WaveTotals<4, MRG> t(acc);
+    const float up = t.partner(2);  // rows gate j, j+1, up j, j+1
+    if (t.lead && t.r < 2 && t.m < m_act) mb.hx[(long)(kb + t.m) * DI + j + t.r] = silu(t.val) * up;
     __syncthreads();
   }
 }
@@ -440,7 +419,7 @@ __global__ __launch_bounds__(256) void k_expert_down_groups(const T* __restrict_
   const int4 info = mb.slot_info[blockIdx.y];
   const int e = info.x;
   if (e < 0) return;
-  const int wave = wave_id(), lane = lane_id();
+  const int wave = wave_id();
   const int n0 = (blockIdx.x * 4 + wave) * 4;
   for (int kb = info.y; kb < info.z; kb += MRG) {
     const int m_act = min(MRG, info.z - kb);
@@ -453,15 +432,8 @@ __global__ __launch_bounds__(256) void k_expert_down_groups(const T* __restrict_
     __syncthreads();
     float acc[4][MRG];
     g.fma(xs, m_act, acc);
-    wave_reduce_acc<4, MRG>(acc, m_act);
-#pragma unroll
-    for (int m = 0; m < MRG; ++m) {
-      if (lane == m && m < m_act) {
-        float* o = mb.y + (long)(kb + m) * D + n0;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] = acc[r][m];
-      }
-    }
+    const WaveTotals<4, MRG> t(acc);
+    if (t.lead && t.m < m_act) mb.y[(long)(kb + t.m) * D + n0 + t.r] = t.val;
     __syncthreads();
   }
 }

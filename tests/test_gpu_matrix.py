@@ -148,3 +148,46 @@ def test_continuous_batching_refill(dtype, conc, K):
         t1, _, _ = one.generate([pages[i]], int(n_out[i]), K, check_every=1)
         assert t1[0].tolist() == toks[i].tolist(), i
     log(f"continuous batching ({dtype}, {conc} slots, K={K}): {n} pages lossless and slot-invariant")
+
+
+def test_matrix_full_model_batch32_vs_oracle():
+    """The 12-layer bf16 decoder on the matrix cores in the launch configuration
+    of the concurrent workload: its 32 pages (256 + 100 n vision rows, n ~
+    U{0..9}, 32 prompt ids) prefilled together, then one K = 1 verify call over
+    their 64 rows.  The two pages with the shortest prefixes are checked against
+    the oracle: the first output token, and both verify rows' logits (5e-2) and
+    greedy tokens (exact unless the oracle's top-2 margin is under 5e-2)."""
+    wl = synth.WORKLOADS["concurrent32_bf16"]
+    cfg, B, K = wl["cfg"], wl["batch"], 1
+    prefix, _ = synth.concurrent_page_lengths(wl["input_seed"], B)
+    pages = synth.make_pages(cfg, wl["input_seed"], prefix.tolist(), [wl["n_prompt"]] * B, [8] * B)
+    w = synth.Weights(cfg, wl["weight_seed"])
+    max_pos = int(prefix.max()) + wl["n_prompt"] + 8
+    dec = ocrdec.Decoder(cfg, w.device_arrays(), max_batch=B, max_k=K, max_positions=max_pos)
+    pend = dec.prefill(pages)
+    drafts = np.random.default_rng(wl["input_seed"] + 7).integers(0, cfg.vocab, size=(B, K)).astype(np.int32)
+    logits = torch.empty(B, K + 1, cfg.vocab, dtype=torch.float32, device="cuda")
+    greedy = dec.verify(B, K, torch.from_numpy(drafts).cuda(), logits=logits)
+    torch.cuda.synchronize()
+    g_pend, g_tok, g_logits = pend.cpu().numpy(), greedy.cpu().numpy(), logits.cpu().numpy()
+    orc = od.Oracle(cfg, w.f32)
+    worst = 0.0
+    for b in np.argsort(prefix, kind="stable")[:2].tolist():
+        p = pages[b]
+        st = orc.new_state(p.prefix_len + K + 1)
+        y0 = orc.prefill(st, p.vision, p.prompt, with_draft=False)
+        if int(g_pend[b]) != y0:
+            assert od.top2_margin(st.first_logits[None])[0] < TOL, (b, int(g_pend[b]), y0)
+            log(f"page {b}: first token differs at a near tie; verify rows not compared")
+            continue
+        rows = [y0] + drafts[b].tolist()
+        h = orc.verifier_forward(st, orc.embed(rows), np.arange(p.prefix_len, p.prefix_len + K + 1))
+        ref = orc.lm_logits(h)
+        diff = float(np.abs(g_logits[b] - ref).max())
+        worst = max(worst, diff)
+        margins = od.top2_margin(ref)
+        for i in range(K + 1):
+            if g_tok[b, i] != od.greedy(ref[i:i + 1])[0]:
+                assert margins[i] < TOL, (b, i, margins[i])
+        log(f"page {b} (prefix {p.prefix_len}): max |dlogit| {diff:.3e} over {K + 1} verify rows")
+    assert worst < TOL
