@@ -58,7 +58,9 @@ extern "C" {
  * decoder shape of the pages' spec table: d_model 1280, 10 heads x 128,
  * 64 routed + 2 shared experts of width 896, top-6, draft FFN 3584; other
  * values of those fields are rejected with OCRDEC_EINVAL.  n_layers >= 1,
- * vocab >= 2, max_positions <= 32768 (the pages' position limit). */
+ * vocab >= 2, max_positions <= 32768 (the pages' position limit),
+ * max_batch in [1, 1024], max_k in [0, 7], max_batch * (max_k + 1) <= 1024
+ * (rows of one verify call). */
 typedef struct {
   int n_layers, d_model, n_heads, head_dim, n_experts, n_shared, top_k, d_expert, d_draft_ffn, vocab;
   float rope_theta, norm_eps;

@@ -10,39 +10,6 @@
 
 namespace ocr {
 
-// Top-6 of the 64 logits of one row held one per lane (lane = expert id), ties
-// to the lower id, and the gates: lanes 0..5 get the chosen experts by
-// decreasing score with their softmax probability (over all 64 routed
-// experts), lanes 6..7 the shared experts 64, 65 with gate 1.  One wavefront.
-__device__ __forceinline__ void top6_slots(float v, int& gi, float& gv) {
-  const int lane = lane_id();
-  bool taken = false;
-  int sel[TOPK];
-  float selv[TOPK];
-#pragma unroll
-  for (int j = 0; j < TOPK; ++j) {
-    float bv = taken ? -INFINITY : v;
-    int bi = taken ? 0x7fffffff : lane;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, 64);
-      const int oi = __shfl_xor(bi, off, 64);
-      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-    }
-    sel[j] = bi;
-    selv[j] = bv;
-    if (lane == bi) taken = true;
-  }
-  const float mx = selv[0];  // softmax max = the top-1 logit
-  const float ex = expf(v - mx);
-  const float sum = wave_sum(ex);
-  gv = 1.0f;
-  gi = NE + (lane - TOPK);
-#pragma unroll
-  for (int j = 0; j < TOPK; ++j)
-    if (lane == j) { gi = sel[j]; gv = expf(selv[j] - mx) / sum; }
-}
-
 // Routing of up to 8 rows held in LDS.
 struct RouteLds {
   int pe[64];        // expert of pair p = row * 8 + slot
@@ -100,12 +67,29 @@ __device__ __forceinline__ void sort_pairs_wave(int P, RouteLds& r) {
   }
 }
 
+// Lane e of a wavefront, holding logit v of a row whose 64 logits are in lg
+// (LDS): rank = the number of experts that beat it (a larger logit, or an
+// equal one and a lower id), so ranks 0..5 are the routed slots in decreasing
+// order; gate = its softmax probability over the 64 (max = the largest logit,
+// sum by the xor butterfly).
+__device__ __forceinline__ void rank_and_gate(const float* lg, float v, int& rank, float& gate) {
+  const int lane = lane_id();
+  int rk = 0;
+  float mx = v;
+#pragma unroll 16
+  for (int o = 0; o < NE; ++o) {
+    const float u = lg[o];
+    rk += (u > v || (u == v && o < lane)) ? 1 : 0;
+    mx = fmaxf(mx, u);
+  }
+  const float ex = expf(v - mx);
+  rank = rk;
+  gate = ex / wave_sum(ex);
+}
+
 // Route M <= 8 rows from their logits (rlogit[m][64]) into LDS; all 256
 // threads of the block call it (two barriers inside).  Wavefront w handles rows
-// w, w+4: lane e counts the experts that beat it (larger logit, or equal with a
-// lower id) -- its rank; ranks 0..5 are the routed slots in decreasing order.
-// Gates: softmax over the 64 logits, max = the top-1 logit, sum by the xor
-// butterfly.  Same selection as top6_slots.
+// w, w+4 with rank_and_gate, then wavefront 0 sorts the pairs.
 __device__ __forceinline__ void route_rows(const float* __restrict__ rlogit, int M, RouteLds& r) {
   __shared__ float lg[4][NE];
   const int wave = wave_id(), lane = lane_id();
@@ -114,18 +98,12 @@ __device__ __forceinline__ void route_rows(const float* __restrict__ rlogit, int
     lg[wave][lane] = v;
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    int rank = 0;
-    float mx = v;
-#pragma unroll 16
-    for (int o = 0; o < NE; ++o) {
-      const float u = lg[wave][o];
-      rank += (u > v || (u == v && o < lane)) ? 1 : 0;
-      mx = fmaxf(mx, u);
-    }
-    const float sum = wave_sum(expf(v - mx));
+    int rank;
+    float gate;
+    rank_and_gate(lg[wave], v, rank, gate);
     if (rank < TOPK) {
       r.pe[m * NSLOT + rank] = lane;
-      r.pg[m * NSLOT + rank] = expf(v - mx) / sum;
+      r.pg[m * NSLOT + rank] = gate;
     }
     if (lane < NSH) {
       r.pe[m * NSLOT + TOPK + lane] = NE + lane;
@@ -201,40 +179,103 @@ __global__ __launch_bounds__(256) void k_route_small(const float* __restrict__ r
   publish_route(r, M, mb, tap);
 }
 
-// Larger batches: top-6 per row (one wavefront per row) into global ...
+// Larger batches (8 < M <= 1024): top-6 per row, one wavefront per row
+// (rank_and_gate) ...
 __global__ __launch_bounds__(256) void k_topk_rows(const float* __restrict__ rlogit, int M, MoeBufs mb,
                                                    int* __restrict__ tap) {
-  const int m = blockIdx.x * 4 + wave_id();
+  __shared__ float lg[4][NE];
+  const int wave = wave_id(), lane = lane_id();
+  const int m = blockIdx.x * 4 + wave;
   if (m >= M) return;
-  const int lane = lane_id();
-  int gi;
-  float gv;
-  top6_slots(rlogit[(long)m * NE + lane], gi, gv);
-  if (lane < NSLOT) {
-    mb.ridx[m * NSLOT + lane] = gi;
-    mb.rgate[m * NSLOT + lane] = gv;
-    if (tap != nullptr) tap[m * NSLOT + lane] = gi;
+  const float v = rlogit[(long)m * NE + lane];
+  lg[wave][lane] = v;
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  int rank;
+  float gate;
+  rank_and_gate(lg[wave], v, rank, gate);
+  if (rank < TOPK) {
+    mb.ridx[m * NSLOT + rank] = lane;
+    mb.rgate[m * NSLOT + rank] = gate;
+    if (tap != nullptr) tap[m * NSLOT + rank] = lane;
+  }
+  if (lane < NSH) {
+    mb.ridx[m * NSLOT + TOPK + lane] = NE + lane;
+    mb.rgate[m * NSLOT + TOPK + lane] = 1.0f;
+    if (tap != nullptr) tap[m * NSLOT + TOPK + lane] = NE + lane;
   }
 }
 
-// ... and one block sorts all pairs (stable counting sort by expert id).
+// ... then a stable counting sort of the 8M pairs by expert in one 1024-thread
+// block.  Wavefront w owns rows [w M / 16, (w + 1) M / 16), i.e. a contiguous
+// pair range, read in segments of 64 pairs (lane = pair; all segments' loads
+// issued together).  Ballots over a segment's distinct experts give each pair
+// its rank among the range's earlier pairs of the same expert (the range's
+// running count of expert e sits in lane e, or lane e - 64 for the shared
+// experts).  The per-range counts give per-expert offsets (experts in id
+// order) and per-range bases; pair p lands at off[e] + base[w][e] + rank --
+// the permutation of any stable sort by expert id.
+constexpr int RL_WAVES = 16;
+constexpr int RL_SEGS = 8;  // segments per wavefront: M <= RL_WAVES * RL_SEGS * 8 = 1024
 __global__ __launch_bounds__(1024) void k_sort_pairs(int M, MoeBufs mb) {
-  extern __shared__ int pe[];
-  __shared__ int cnt[NX + 1], off[NX + 1], act[NX + 1];
+  __shared__ int wcnt[RL_WAVES][NX + 1];  // per range: counts, then exclusive bases
+  __shared__ int off[NX + 1], act[NX + 1];
   __shared__ int na_s;
-  const int tid = threadIdx.x;
-  const int P = M * NSLOT;
-  for (int p = tid; p < P; p += 1024) pe[p] = mb.ridx[p];
-  for (int e = tid; e <= NX; e += 1024) cnt[e] = 0;
+  const int wave = threadIdx.x >> 6, lane = lane_id(), tid = threadIdx.x;
+  const int p_lo = NSLOT * (M * wave / RL_WAVES), p_hi = NSLOT * (M * (wave + 1) / RL_WAVES);
+  const uint64_t lt = (1ull << lane) - 1ull;
+  int seg_e[RL_SEGS], seg_rank[RL_SEGS];
+#pragma unroll
+  for (int sg = 0; sg < RL_SEGS; ++sg) {
+    const int p = p_lo + 64 * sg + lane;
+    seg_e[sg] = (p < p_hi) ? mb.ridx[p] : -1;
+    seg_rank[sg] = 0;
+  }
+  int c_lo = 0, c_hi = 0;
+#pragma unroll
+  for (int sg = 0; sg < RL_SEGS; ++sg) {
+    if (p_lo + 64 * sg >= p_hi) break;
+    const int e = seg_e[sg];
+    const bool valid = e >= 0;
+    uint64_t todo = __ballot(valid);
+    int rank = 0;
+    while (todo) {
+      const int leader = __builtin_ctzll(todo);
+      const int el = __builtin_amdgcn_readlane(e, leader);
+      const uint64_t same = __ballot(e == el);
+      const int n = __popcll(same);
+      const int before = (el < NE) ? __builtin_amdgcn_readlane(c_lo, el) : __builtin_amdgcn_readlane(c_hi, el - NE);
+      if (e == el) rank = before + __popcll(same & lt);
+      if (el < NE) {
+        if (lane == el) c_lo += n;
+      } else if (lane == el - NE) {
+        c_hi += n;
+      }
+      todo &= ~same;
+    }
+    seg_rank[sg] = rank;
+  }
+  wcnt[wave][lane] = c_lo;
+  if (lane < NSH) wcnt[wave][NE + lane] = c_hi;
   __syncthreads();
-  for (int p = tid; p < P; p += 1024) atomicAdd(&cnt[pe[p]], 1);
+  // per-expert totals -> offsets; per-range exclusive bases
+  if (tid < NX) {
+    int acc = 0;
+    for (int w = 0; w < RL_WAVES; ++w) {
+      const int c = wcnt[w][tid];
+      wcnt[w][tid] = acc;
+      acc += c;
+    }
+    act[tid] = acc;  // total of expert tid (reused below as the active list)
+  }
   __syncthreads();
   if (tid == 0) {
     int acc = 0, na = 0;
     for (int e = 0; e < NX; ++e) {
+      const int c = act[e];
       off[e] = acc;
-      if (cnt[e] > 0) act[na++] = e;
-      acc += cnt[e];
+      acc += c;
+      if (c > 0) act[na++] = e;  // na <= e: entries not yet read are never overwritten
     }
     off[NX] = acc;
     na_s = na;
@@ -252,20 +293,23 @@ __global__ __launch_bounds__(1024) void k_sort_pairs(int M, MoeBufs mb) {
       mb.slot_info[sl] = make_int4(-1, 0, 0, na);
     }
   }
-  for (int p = tid; p < P; p += 1024) {
-    const int e = pe[p];
-    int rank = 0;
-    for (int q = 0; q < p; ++q) rank += (pe[q] == e);
-    const int pos = off[e] + rank;
-    mb.perm[pos] = p;
-    mb.inv[p] = pos;
+  // final positions
+#pragma unroll
+  for (int sg = 0; sg < RL_SEGS; ++sg) {
+    const int e = seg_e[sg];
+    if (e >= 0) {
+      const int p = p_lo + 64 * sg + lane;
+      const int pos = off[e] + wcnt[wave][e] + seg_rank[sg];
+      mb.perm[pos] = p;
+      mb.inv[p] = pos;
+    }
   }
 }
 
 int expert_slot_cap(int M) { return min(NE, TOPK * M) + NSH; }
 
-// Router: logits in a 16-block kernel, then the top-6 and the sort (one block
-// for M <= 8, a per-row kernel and a sort kernel beyond).
+// Router: logits in a 16-block kernel, then the top-6 and the sort (one
+// block for M <= 8; a per-row top-6 kernel and a one-block sort beyond).
 template <typename T>
 void launch_router(hipStream_t s, const float* x, const float* gain, float eps, const T* wr, int M,
                    const MoeBufs& mb, int* tap, const float* logit_override) {
@@ -282,7 +326,7 @@ void launch_router(hipStream_t s, const float* x, const float* gain, float eps, 
     hipLaunchKernelGGL(k_route_small, dim3(1), dim3(256), 0, s, mb.rlogit, M, mb, tap);
   } else {
     hipLaunchKernelGGL(k_topk_rows, dim3((M + 3) / 4), dim3(256), 0, s, mb.rlogit, M, mb, tap);
-    hipLaunchKernelGGL(k_sort_pairs, dim3(1), dim3(1024), (size_t)M * NSLOT * sizeof(int), s, M, mb);
+    hipLaunchKernelGGL(k_sort_pairs, dim3(1), dim3(1024), 0, s, M, mb);
   }
 }
 

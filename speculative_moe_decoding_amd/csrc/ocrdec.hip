@@ -50,6 +50,7 @@ bool shape_ok(const ocrdec_config* c, std::string* why) {
   if (c->dtype != OCRDEC_F32 && c->dtype != OCRDEC_BF16) { *why = "dtype must be OCRDEC_F32 or OCRDEC_BF16"; return false; }
   if (c->max_batch < 1 || c->max_batch > 1024) { *why = "max_batch must be in [1, 1024]"; return false; }
   if (c->max_k < 0 || c->max_k > 7) { *why = "max_k must be in [0, 7]"; return false; }
+  if (c->max_batch * (c->max_k + 1) > 1024) { *why = "max_batch * (max_k + 1) must be <= 1024"; return false; }
   if (c->max_positions < 16 || c->max_positions > 32768) { *why = "max_positions must be in [16, 32768]"; return false; }
   if (!(c->norm_eps > 0.f) || !(c->rope_theta > 1.f)) { *why = "norm_eps must be > 0 and rope_theta > 1"; return false; }
   if (c->path < OCRDEC_PATH_AUTO || c->path > OCRDEC_PATH_MATRIX) { *why = "path must be OCRDEC_PATH_*"; return false; }

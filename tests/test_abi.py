@@ -59,9 +59,12 @@ def test_rejects_bad_configs(lib):
     with pytest.raises(ocrdec.OcrdecError) as e:
         ocrdec.ocrdec_num_weights(bad)
     assert e.value.code == ocrdec.OCRDEC_EINVAL
-    for mb, mk, mp in ((0, 3, 2048), (1, 8, 2048), (1, 3, 40000)):
+    for mb, mk, mp in ((0, 3, 2048), (1, 8, 2048), (1, 3, 40000), (1025, 0, 2048), (257, 3, 2048)):
         c = ocrdec.make_config(synth.FULL, mb, mk, mp)
         assert ocrdec.ocrdec_state_bytes(c) == 0
+    # rows of one verify call: max_batch * (max_k + 1) up to 1024
+    assert ocrdec.ocrdec_state_bytes(ocrdec.make_config(synth.FULL, 256, 3, 64)) > 0
+    assert ocrdec.ocrdec_state_bytes(ocrdec.make_config(synth.FULL, 1024, 0, 64)) > 0
     # create checks the weight list before touching the device
     c = ocrdec.make_config(synth.FULL, 1, 3, 2048)
     h = ctypes.c_void_p()
