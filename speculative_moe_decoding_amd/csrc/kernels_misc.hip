@@ -50,19 +50,41 @@ __device__ __forceinline__ void norm_row(const float* __restrict__ src, const fl
   for (int j = 0; j < D / 256; ++j) dst[threadIdx.x + 256 * j] = (v[j] * r) * g[threadIdx.x + 256 * j];
 }
 
-// Draft fusion input of one row: [RMSNorm(h; g_h), RMSNorm(e; g_e)].
+// Draft fusion input of one row: [RMSNorm(h; g_h), RMSNorm(e; g_e)], e = E[tok]
+// (the arithmetic of norm_row; both rows' loads issued together).
 template <typename T>
-__device__ __forceinline__ void draft_cat_row(const float* h, int tok, const T* E, const float* g_h,
-                                              const float* g_e, float eps, float* cat, float* ebuf, float* red) {
-  norm_row(h, g_h, eps, cat, red);
-  embed_row(E, tok, ebuf);
-  __syncthreads();
-  norm_row(ebuf, g_e, eps, cat + D, red);
+__device__ __forceinline__ void draft_cat_row(const float* __restrict__ h, int tok, const T* __restrict__ E,
+                                              const float* __restrict__ g_h, const float* __restrict__ g_e,
+                                              float eps, float* __restrict__ cat, float* red) {
+  constexpr int J = D / 256;
+  const T* er = E + (long)tok * D;
+  float vh[J], ve[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    vh[j] = h[threadIdx.x + 256 * j];
+    ve[j] = WT<T>::load1(er + threadIdx.x + 256 * j);
+  }
+  float sh = 0.f, se = 0.f;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    sh = fmaf(vh[j], vh[j], sh);
+    se = fmaf(ve[j], ve[j], se);
+  }
+  sh = block_sum256(sh, red);
+  se = block_sum256(se, red);
+  const float rh = 1.0f / sqrtf(sh / (float)D + eps), re = 1.0f / sqrtf(se / (float)D + eps);
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int k = threadIdx.x + 256 * j;
+    cat[k] = (vh[j] * rh) * g_h[k];
+    cat[D + k] = (ve[j] * re) * g_e[k];
+  }
 }
 
 // Catch-up pass: sequence b has cnt = n_prev + 1 valid rows at positions
 // draft_len .. kv_len; row i takes the verifier hidden hbuf[i] (of position
 // draft_len - 1 + i) and the committed token cu_tok[i] (at draft_len + i).
+// Block (i, b) builds row i of sequence b; grid (Q, B).
 template <typename T>
 __global__ __launch_bounds__(256) void k_plan_draft_catchup(int Q, const int* __restrict__ slots_in,
                                                             StateView sv, const T* __restrict__ E, int V,
@@ -71,25 +93,21 @@ __global__ __launch_bounds__(256) void k_plan_draft_catchup(int Q, const int* __
                                                             int* plan_base, int* plan_cnt, int* plan_slot,
                                                             float* __restrict__ cat) {
   __shared__ float red[4];
-  __shared__ float ebuf[D];
-  const int b = blockIdx.x;
+  const int i = blockIdx.x, b = blockIdx.y;
   const int slot = clamp_slot(slots_in ? slots_in[b] : b, sv.n_slots);
   const int cnt = max(1, min(sv.n_prev[slot] + 1, Q));
-  if (threadIdx.x == 0) {
+  if (i == 0 && threadIdx.x == 0) {
     plan_slot[b] = slot;
     plan_base[b] = sv.draft_len[slot];
     plan_cnt[b] = cnt;
   }
-  for (int i = 0; i < Q; ++i) {
-    float* c = cat + (long)(b * Q + i) * 2 * D;
-    if (i < cnt) {
-      const float* h = sv.hbuf + ((long)slot * sv.cu_stride + i) * D;
-      const int tok = clamp_tok(sv.cu_tok[slot * sv.cu_stride + i], V);
-      draft_cat_row(h, tok, E, g_h, g_e, eps, c, ebuf, red);
-      __syncthreads();
-    } else {
-      for (int k = threadIdx.x; k < 2 * D; k += 256) c[k] = 0.f;
-    }
+  float* c = cat + (long)(b * Q + i) * 2 * D;
+  if (i < cnt) {
+    const float* h = sv.hbuf + ((long)slot * sv.cu_stride + i) * D;
+    const int tok = clamp_tok(sv.cu_tok[slot * sv.cu_stride + i], V);
+    draft_cat_row(h, tok, E, g_h, g_e, eps, c, red);
+  } else {
+    for (int k = threadIdx.x; k < 2 * D; k += 256) c[k] = 0.f;
   }
 }
 
@@ -104,7 +122,6 @@ __global__ __launch_bounds__(256) void k_plan_draft_step(int j, int Qprev, int K
                                                          int* plan_cnt, const int* __restrict__ plan_slot,
                                                          float* __restrict__ cat) {
   __shared__ float red[4];
-  __shared__ float ebuf[D];
   __shared__ int prev_cnt;
   const int b = blockIdx.x;
   const int slot = plan_slot[b];
@@ -112,7 +129,7 @@ __global__ __launch_bounds__(256) void k_plan_draft_step(int j, int Qprev, int K
   __syncthreads();
   const float* h = u_prev + (long)(b * Qprev + prev_cnt - 1) * D;
   const int tok = clamp_tok(draft_out[b * K + j - 2], V);
-  draft_cat_row(h, tok, E, g_h, g_e, eps, cat + (long)b * 2 * D, ebuf, red);
+  draft_cat_row(h, tok, E, g_h, g_e, eps, cat + (long)b * 2 * D, red);
   __syncthreads();
   if (threadIdx.x == 0) {
     plan_base[b] = sv.kv_len[slot] + j - 1;
@@ -313,7 +330,7 @@ template <typename T>
 void launch_plan_draft_catchup(hipStream_t s, int B, int Q, const int* slots_in, StateView sv, const T* embed,
                                int V, const float* g_h, const float* g_e, float eps, int* plan_base, int* plan_cnt,
                                int* plan_slot, float* cat) {
-  hipLaunchKernelGGL((k_plan_draft_catchup<T>), dim3(B), dim3(256), 0, s, Q, slots_in, sv, embed, V, g_h, g_e, eps,
+  hipLaunchKernelGGL((k_plan_draft_catchup<T>), dim3(Q, B), dim3(256), 0, s, Q, slots_in, sv, embed, V, g_h, g_e, eps,
                      plan_base, plan_cnt, plan_slot, cat);
 }
 template <typename T>
