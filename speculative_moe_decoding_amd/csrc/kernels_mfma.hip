@@ -204,9 +204,9 @@ __device__ __forceinline__ void gate_up_pass(const bf16* const (&w)[2], const fl
 }
 
 __global__ __launch_bounds__(256) void k_expert_gate_up_mfma(const bf16* __restrict__ wg,
-                                                             const bf16* __restrict__ wu, MoeBufs mb) {
+                                                             const bf16* __restrict__ wu, int M, MoeBufs mb) {
   __shared__ MfChunk buf[2][2];
-  const int4 info = mb.slot_info[blockIdx.y];
+  const int4 info = expert_work(mb, blockIdx.y, M);
   const int e = info.x;
   if (e < 0) return;
   const int j0 = blockIdx.x * 64 + wave_id() * 16;
@@ -241,9 +241,9 @@ __device__ __forceinline__ void down_pass(const bf16* const (&w)[1], const float
   }
 }
 
-__global__ __launch_bounds__(256) void k_expert_down_mfma(const bf16* __restrict__ wd, MoeBufs mb) {
+__global__ __launch_bounds__(256) void k_expert_down_mfma(const bf16* __restrict__ wd, int M, MoeBufs mb) {
   __shared__ MfChunk buf[2][2];
-  const int4 info = mb.slot_info[blockIdx.y];
+  const int4 info = expert_work(mb, blockIdx.y, M);
   const int e = info.x;
   if (e < 0) return;
   const int n0 = blockIdx.x * 128 + wave_id() * 32;
@@ -257,11 +257,11 @@ __global__ __launch_bounds__(256) void k_expert_down_mfma(const bf16* __restrict
 }
 
 void launch_expert_gate_up_mfma(hipStream_t s, const bf16* wg, const bf16* wu, int M, const MoeBufs& mb) {
-  hipLaunchKernelGGL(k_expert_gate_up_mfma, dim3(DI / 64, expert_slot_cap(M)), dim3(256), 0, s, wg, wu, mb);
+  hipLaunchKernelGGL(k_expert_gate_up_mfma, dim3(DI / 64, expert_slot_cap(M)), dim3(256), 0, s, wg, wu, M, mb);
 }
 
 void launch_expert_down_mfma(hipStream_t s, const bf16* wd, int M, const MoeBufs& mb) {
-  hipLaunchKernelGGL(k_expert_down_mfma, dim3(D / 128, expert_slot_cap(M)), dim3(256), 0, s, wd, mb);
+  hipLaunchKernelGGL(k_expert_down_mfma, dim3(D / 128, expert_slot_cap(M)), dim3(256), 0, s, wd, M, mb);
 }
 
 // LM head rows for the matrix cores: xn[m] = RMSNorm(x[src(m)]) * gain, one

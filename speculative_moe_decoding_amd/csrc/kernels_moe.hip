@@ -363,15 +363,16 @@ __device__ __forceinline__ void gather_rows(const float* __restrict__ src, SrcRo
 // Gate/up (M <= 8): block (x, slot s) handles active expert s; wavefront w
 // owns units j0 .. j0+UPW-1, j0 = UPW (4x + w): rows gate[j] then up[j], all
 // loads issued at once.  The (at most MR) pairs routed to the expert get
-// hx[pair][j] = silu(gate . b) * (up . b).  The slot table gives the expert,
-// its pair range and a bit mask of its rows, so the weights and the
-// normalised rows are fetched after one dependent read.
+// hx[pair][j] = silu(gate . b) * (up . b).  expert_work gives the expert, its
+// pair range and a bit mask of its rows: the shared experts' blocks need no
+// read for it, the routed ones fetch weights and normalised rows after one
+// dependent read of the routing table.
 template <typename T, int MR, int UPW>
-__global__ __launch_bounds__(256) void k_expert_gate_up(const T* __restrict__ wg, const T* __restrict__ wu,
+__global__ __launch_bounds__(256) void k_expert_gate_up(const T* __restrict__ wg, const T* __restrict__ wu, int M,
                                                         MoeBufs mb) {
   extern __shared__ float xs[];
   const int wave = wave_id();
-  const int4 info = mb.slot_info[blockIdx.y];
+  const int4 info = expert_work(mb, blockIdx.y, M);
   const int e = info.x;
   if (e < 0) return;
   const int k0 = info.y;
@@ -404,9 +405,9 @@ __global__ __launch_bounds__(256) void k_expert_gate_up(const T* __restrict__ wg
 // Down: block (x, slot s); wavefront w owns output rows n0 .. n0+RPW-1,
 // n0 = RPW (4x + w):  y[pair][n] = W_d[n] . hx[pair].
 template <typename T, int MR, int RPW>
-__global__ __launch_bounds__(256) void k_expert_down(const T* __restrict__ wd, MoeBufs mb) {
+__global__ __launch_bounds__(256) void k_expert_down(const T* __restrict__ wd, int M, MoeBufs mb) {
   extern __shared__ float xs[];
-  const int4 info = mb.slot_info[blockIdx.y];
+  const int4 info = expert_work(mb, blockIdx.y, M);
   const int e = info.x;
   if (e < 0) return;
   const int k0 = info.y;
@@ -431,9 +432,9 @@ __global__ __launch_bounds__(256) void k_expert_down(const T* __restrict__ wd, M
 // time, one tile per wavefront, the tile re-read for every group of pairs.
 template <typename T>
 __global__ __launch_bounds__(256) void k_expert_gate_up_groups(const T* __restrict__ wg, const T* __restrict__ wu,
-                                                               MoeBufs mb) {
+                                                               int M, MoeBufs mb) {
   extern __shared__ float xs[];
-  const int4 info = mb.slot_info[blockIdx.y];
+  const int4 info = expert_work(mb, blockIdx.y, M);
   const int e = info.x;
   if (e < 0) return;
   const int wave = wave_id();
@@ -458,9 +459,9 @@ __global__ __launch_bounds__(256) void k_expert_gate_up_groups(const T* __restri
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void k_expert_down_groups(const T* __restrict__ wd, MoeBufs mb) {
+__global__ __launch_bounds__(256) void k_expert_down_groups(const T* __restrict__ wd, int M, MoeBufs mb) {
   extern __shared__ float xs[];
-  const int4 info = mb.slot_info[blockIdx.y];
+  const int4 info = expert_work(mb, blockIdx.y, M);
   const int e = info.x;
   if (e < 0) return;
   const int wave = wave_id();
@@ -495,14 +496,14 @@ template <typename T>
 void launch_expert_gate_up(hipStream_t s, const T* wg, const T* wu, int M, const MoeBufs& mb, int* tap) {
   const dim3 grid(DI / (4 * GU_UPW), expert_slot_cap(M));
 #define OCR_GU_CASE(MRV) \
-  hipLaunchKernelGGL((k_expert_gate_up<T, MRV, GU_UPW>), grid, dim3(256), (size_t)MRV * D * 4, s, wg, wu, mb);
+  hipLaunchKernelGGL((k_expert_gate_up<T, MRV, GU_UPW>), grid, dim3(256), (size_t)MRV * D * 4, s, wg, wu, M, mb);
   if (M <= 1) OCR_GU_CASE(1)
   else if (M <= 2) OCR_GU_CASE(2)
   else if (M <= 4) OCR_GU_CASE(4)
   else if (M <= MRG) OCR_GU_CASE(MRG)
   else
     hipLaunchKernelGGL((k_expert_gate_up_groups<T>), dim3(DI / 8, expert_slot_cap(M)), dim3(256),
-                       (size_t)MRG * D * 4, s, wg, wu, mb);
+                       (size_t)MRG * D * 4, s, wg, wu, M, mb);
 #undef OCR_GU_CASE
 }
 
@@ -510,14 +511,14 @@ template <typename T>
 void launch_expert_down(hipStream_t s, const T* wd, int M, const MoeBufs& mb) {
   const dim3 grid(D / (4 * DN_RPW), expert_slot_cap(M));
 #define OCR_DN_CASE(MRV) \
-  hipLaunchKernelGGL((k_expert_down<T, MRV, DN_RPW>), grid, dim3(256), (size_t)MRV * DI * 4, s, wd, mb);
+  hipLaunchKernelGGL((k_expert_down<T, MRV, DN_RPW>), grid, dim3(256), (size_t)MRV * DI * 4, s, wd, M, mb);
   if (M <= 1) OCR_DN_CASE(1)
   else if (M <= 2) OCR_DN_CASE(2)
   else if (M <= 4) OCR_DN_CASE(4)
   else if (M <= MRG) OCR_DN_CASE(MRG)
   else
     hipLaunchKernelGGL((k_expert_down_groups<T>), dim3(D / 16, expert_slot_cap(M)), dim3(256),
-                       (size_t)MRG * DI * 4, s, wd, mb);
+                       (size_t)MRG * DI * 4, s, wd, M, mb);
 #undef OCR_DN_CASE
 }
 

@@ -56,6 +56,19 @@ struct MoeBufs {
   float* y;       // [8M][D]
 };
 
+// Work item of row y of an expert kernel's grid (M rows in the call): rows 0
+// and 1 are the shared experts, always active, with pairs (TOPK + y) M ..
+// (TOPK + y + 1) M - 1 (the sort puts them after the 6M routed pairs; .w = the
+// mask of all rows), so their weight loads wait for no routing read; rows
+// y >= 2 take routed slot y - 2 of the routing table (expert -1 past the routed
+// ones).  The grid is expert_slot_cap(M) rows.
+__device__ __forceinline__ int4 expert_work(const MoeBufs& mb, int y, int M) {
+  if (y < NSH) return make_int4(NE + y, (TOPK + y) * M, (TOPK + y + 1) * M, M < 31 ? (1 << M) - 1 : -1);
+  int4 info = mb.slot_info[y - NSH];
+  if (info.x >= NE) info.x = -1;
+  return info;
+}
+
 // Router logits (rlogit) and the routing tables; logit_override (nullable,
 // [M][64]) replaces the computed logits before the top-6.
 template <typename T>
