@@ -57,6 +57,72 @@ template <> struct AttTile<bf16> {
   }
 };
 
+// One query row (query i of the block's sequence, visible keys 0..plim) against
+// the staged tile of keys kt .. kt+63, by one wavefront: lane = key for the
+// scores (q . k over 128 dims, 4 at a time, in order), then lane = value-dim
+// pair for the output; the online-softmax state (mrun, lrun, o0, o1) is the
+// query's.  pw is the wavefront's 64-float LDS row for the probabilities.
+template <typename T>
+__device__ __forceinline__ void attn_tile_query(const float4* __restrict__ qrow,
+                                                const typename AttTile<T>::K4 (*Kq)[ATT_TILE],
+                                                const typename AttTile<T>::V2 (*Vs)[HD / 2], float4* pw, int kt,
+                                                int plim, float& mrun, float& lrun, float& o0, float& o1) {
+  typedef AttTile<T> AT;
+  const int lane = lane_id();
+  const float scale = 0.08838834764831845f;  // 1 / sqrt(128)
+  float sc = 0.f;
+#pragma unroll 8
+  for (int d4 = 0; d4 < HD / 4; ++d4) {
+    const float4 qv = qrow[d4];
+    const float4 kv4 = AT::k(Kq[d4][lane]);
+    sc = fmaf(qv.x, kv4.x, sc);
+    sc = fmaf(qv.y, kv4.y, sc);
+    sc = fmaf(qv.z, kv4.z, sc);
+    sc = fmaf(qv.w, kv4.w, sc);
+  }
+  sc = sc * scale;
+  const bool vis = (kt + lane) <= plim;
+  const float mt = wave_max(vis ? sc : -INFINITY);
+  const float mnew = fmaxf(mrun, mt);
+  const float corr = expf(mrun - mnew);
+  const float p = vis ? expf(sc - mnew) : 0.f;
+  lrun = lrun * corr + wave_sum(p);
+  reinterpret_cast<float*>(pw)[lane] = p;
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  float a0 = o0 * corr, a1 = o1 * corr;
+#pragma unroll 4
+  for (int t4 = 0; t4 < ATT_TILE / 4; ++t4) {
+    const float4 pt = pw[t4];
+    const float pv[4] = {pt.x, pt.y, pt.z, pt.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float2 v2 = AT::v(Vs[4 * t4 + u][lane]);
+      a0 = fmaf(pv[u], v2.x, a0);
+      a1 = fmaf(pv[u], v2.y, a1);
+    }
+  }
+  o0 = a0;
+  o1 = a1;
+  mrun = mnew;
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Merge of the chunk partials pp[c * cstride] (o[128], m, l) of one query row
+// for dims d, chunks 0..nc-1 in order: max of the m, then L and O with weights
+// exp(m_c - max), result O / L.
+__device__ __forceinline__ float attn_merge(const float* __restrict__ pp, long cstride, int nc, int d) {
+  float mg = -INFINITY;
+  for (int c = 0; c < nc; ++c) mg = fmaxf(mg, pp[c * cstride + HD]);
+  float L = 0.f, O = 0.f;
+  for (int c = 0; c < nc; ++c) {
+    const float w = expf(pp[c * cstride + HD] - mg);
+    L = fmaf(pp[c * cstride + HD + 1], w, L);
+    O = fmaf(pp[c * cstride + d], w, O);
+  }
+  return O / L;
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_attn_partial(const float* __restrict__ q, const T* __restrict__ kv,
                                                       int max_pos, RowPlan plan, int n_chunks,
@@ -117,7 +183,6 @@ __global__ __launch_bounds__(256) void k_attn_partial(const float* __restrict__ 
       qs[e / (HD / 4)][e % (HD / 4)] = qv[j];
     }
   }
-  const float scale = 0.08838834764831845f;  // 1 / sqrt(128)
   float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
   float o0[2] = {0.f, 0.f}, o1[2] = {0.f, 0.f};
   for (int tt = 0; tt < n_tiles; ++tt) {
@@ -136,43 +201,7 @@ __global__ __launch_bounds__(256) void k_attn_partial(const float* __restrict__ 
       if (i >= cnt) continue;
       const int plim = base + i;  // last visible key of query i
       if (kt > plim) continue;
-      // lane = key t of the tile: s = q . k over 128 dims, 4 at a time, in order
-      float sc = 0.f;
-#pragma unroll 8
-      for (int d4 = 0; d4 < HD / 4; ++d4) {
-        const float4 qv = qs[i][d4];
-        const float4 kv4 = AT::k(Kq[d4][lane]);
-        sc = fmaf(qv.x, kv4.x, sc);
-        sc = fmaf(qv.y, kv4.y, sc);
-        sc = fmaf(qv.z, kv4.z, sc);
-        sc = fmaf(qv.w, kv4.w, sc);
-      }
-      sc = sc * scale;
-      const bool vis = (kt + lane) <= plim;
-      const float mt = wave_max(vis ? sc : -INFINITY);
-      const float mnew = fmaxf(mrun[qq], mt);
-      const float corr = expf(mrun[qq] - mnew);
-      const float p = vis ? expf(sc - mnew) : 0.f;
-      lrun[qq] = lrun[qq] * corr + wave_sum(p);
-      reinterpret_cast<float*>(ps[wave])[lane] = p;
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-      float a0 = o0[qq] * corr, a1 = o1[qq] * corr;
-#pragma unroll 4
-      for (int t4 = 0; t4 < ATT_TILE / 4; ++t4) {
-        const float4 pt = ps[wave][t4];
-        const float pv[4] = {pt.x, pt.y, pt.z, pt.w};
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float2 v2 = AT::v(Vs[4 * t4 + u][lane]);
-          a0 = fmaf(pv[u], v2.x, a0);
-          a1 = fmaf(pv[u], v2.y, a1);
-        }
-      }
-      o0[qq] = a0;
-      o1[qq] = a1;
-      mrun[qq] = mnew;
-      __builtin_amdgcn_wave_barrier();
+      attn_tile_query<T>(qs[i], Kq, Vs, ps[wave], kt, plim, mrun[qq], lrun[qq], o0[qq], o1[qq]);
     }
   }
 #pragma unroll
@@ -197,16 +226,7 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
   if (i >= plan.cnt[b] || p < 0 || p >= max_pos) { *o = 0.f; return; }
   const int nc = min(p / chunk_keys + 1, n_chunks);
   const float* pp = part + (((long)b * NH + h) * n_chunks) * plan.Q * (HD + 2) + (long)i * (HD + 2);
-  const long cstride = (long)plan.Q * (HD + 2);
-  float mg = -INFINITY;
-  for (int c = 0; c < nc; ++c) mg = fmaxf(mg, pp[c * cstride + HD]);
-  float L = 0.f, O = 0.f;
-  for (int c = 0; c < nc; ++c) {
-    const float w = expf(pp[c * cstride + HD] - mg);
-    L = fmaf(pp[c * cstride + HD + 1], w, L);
-    O = fmaf(pp[c * cstride + d], w, O);
-  }
-  *o = O / L;
+  *o = attn_merge(pp, (long)plan.Q * (HD + 2), nc, d);
 }
 
 template <typename T>
