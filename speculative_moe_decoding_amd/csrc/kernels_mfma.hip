@@ -46,11 +46,13 @@ constexpr int MF_SC = MF_KC / 32;    // MFMA k-steps per chunk
 constexpr int MF_MT = 4;             // 16-row tiles per pass
 constexpr int MF_ROWS = 16 * MF_MT;  // activation rows per pass
 
-// One LDS chunk: f[tile][step][lane] is lane's A fragment, i.e. row
-// 16 tile + lane % 16, k = 32 step + 8 (lane / 16) .. +7 of the chunk.
-struct MfChunk {
-  uint4 f[MF_MT][MF_SC][64];
+// One LDS chunk of CT tiles: f[tile][step][lane] is lane's A fragment, i.e.
+// row 16 tile + lane % 16, k = 32 step + 8 (lane / 16) .. +7 of the chunk.
+template <int CT>
+struct MfChunkT {
+  uint4 f[CT][MF_SC][64];
 };
+typedef MfChunkT<MF_MT> MfChunk;
 
 // Passes use NT (1, 2 or 4) tiles, the fewest that hold their rows; rows of a
 // tile past the pass's row count are zero.
@@ -67,9 +69,10 @@ __device__ __forceinline__ void mf_load_b(uint4 (&bq)[NB][NS][MF_SC], const bf16
 
 // Thread tid stages the 8-element group kg = tid % 16 of row tid / 16 + 16 i
 // (tile i) of every chunk; rows past the pass read a valid row and are zeroed.
+// With a gain g (RMSNorm rows) the gains of the group are loaded alongside.
 template <int NT>
-__device__ __forceinline__ void mf_load_a(float4 (&ar)[NT][2], const float* const (&src)[NT], const bool (&ok)[NT],
-                                          int c) {
+__device__ __forceinline__ void mf_load_a(float4 (&ar)[NT][2], float4 (&gq)[2], const float* const (&src)[NT],
+                                          const bool (&ok)[NT], const float* __restrict__ g, int kg, int c) {
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
     const float4* p = reinterpret_cast<const float4*>(src[i] + c * MF_KC);
@@ -78,6 +81,16 @@ __device__ __forceinline__ void mf_load_a(float4 (&ar)[NT][2], const float* cons
     ar[i][0] = ok[i] ? a : z;
     ar[i][1] = ok[i] ? b : z;
   }
+  if (g != nullptr) {
+    const float4* gp = reinterpret_cast<const float4*>(g + c * MF_KC + 8 * kg);
+    gq[0] = gp[0];
+    gq[1] = gp[1];
+  }
+}
+
+// RMSNorm of the staged group: (a * r) * g, r the row's scale.
+__device__ __forceinline__ float4 mf_norm(const float4& a, float r, const float4& g) {
+  return make_float4((a.x * r) * g.x, (a.y * r) * g.y, (a.z * r) * g.z, (a.w * r) * g.w);
 }
 
 // a - bf16(a) for the two halves of a packed pair (exact in fp32).
@@ -85,10 +98,17 @@ __device__ __forceinline__ float rem_lo(float a, uint32_t h) { return a - __uint
 __device__ __forceinline__ float rem_hi(float a, uint32_t h) { return a - __uint_as_float(h & 0xffff0000u); }
 
 // Parts NP = 1: ch[0] = bf16(a); NP = 2: also ch[1] = bf16(a - bf16(a)).
-template <int NT, int NP>
-__device__ __forceinline__ void mf_store_a(MfChunk (&ch)[NP], const float4 (&ar)[NT][2], int kg, int ri) {
+// NORM: a is first normalised with the thread's row scales rsv and gains gq.
+template <int NT, int NP, bool NORM, int CT>
+__device__ __forceinline__ void mf_store_a(MfChunkT<CT> (&ch)[NP], float4 (&ar)[NT][2], const float4 (&gq)[2],
+                                           const float (&rsv)[NT], int kg, int ri) {
+  static_assert(NT <= CT, "chunk too small for the pass");
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
+    if constexpr (NORM) {
+      ar[i][0] = mf_norm(ar[i][0], rsv[i], gq[0]);
+      ar[i][1] = mf_norm(ar[i][1], rsv[i], gq[1]);
+    }
     uint4 v;
     v.x = pack_bf16x2(ar[i][0].x, ar[i][0].y);
     v.y = pack_bf16x2(ar[i][0].z, ar[i][0].w);
@@ -106,8 +126,8 @@ __device__ __forceinline__ void mf_store_a(MfChunk (&ch)[NP], const float4 (&ar)
   }
 }
 
-template <int NT, int NB, int NS, int NP>
-__device__ __forceinline__ void mf_compute(const MfChunk (&ch)[NP], const uint4 (&bq)[NB][NS][MF_SC],
+template <int NT, int NB, int NS, int NP, int CT>
+__device__ __forceinline__ void mf_compute(const MfChunkT<CT> (&ch)[NP], const uint4 (&bq)[NB][NS][MF_SC],
                                            f32x4_v (&acc)[NT][NB][NS]) {
   const int lane = lane_id();
 #pragma unroll
@@ -129,11 +149,13 @@ __device__ __forceinline__ void mf_compute(const MfChunk (&ch)[NP], const uint4 
 // One pass: rows r < rows <= 16 NT (row r read from rowp(r), fp32, K long)
 // against the wavefront's weight rows w[b] + (16 n + j) K, j < 16, of NB
 // matrices: acc[i][b][n][q] = sum_k A[16 i + 4 (lane / 16) + q][k] *
-// W_b[16 n + lane % 16][k], with A in NP bf16 parts.  All 256 threads must
-// call it; contains barriers.
-template <int K, int NT, int NB, int NS, int NP, typename RowPtr>
-__device__ __forceinline__ void mfma_pass(const bf16* const (&w)[NB], RowPtr rowp, int rows, MfChunk (&buf)[2][NP],
-                                          f32x4_v (&acc)[NT][NB][NS]) {
+// W_b[16 n + lane % 16][k], with A in NP bf16 parts.  With a gain g, row r of
+// A is RMSNorm'ed first: (a * rs[r]) * g (rs in LDS, one scale per pass row).
+// All 256 threads must call it; contains barriers.
+template <int K, int NT, int NB, int NS, int NP, typename RowPtr, bool NORM = false, int CT = MF_MT>
+__device__ __forceinline__ void mfma_pass(const bf16* const (&w)[NB], RowPtr rowp, int rows, MfChunkT<CT> (&buf)[2][NP],
+                                          f32x4_v (&acc)[NT][NB][NS], const float* __restrict__ g = nullptr,
+                                          const float* rs = nullptr) {
   static_assert(K % MF_KC == 0, "K must be a multiple of the chunk");
   static_assert(NT <= MF_MT, "too many tiles");
   constexpr int NC = K / MF_KC;
@@ -142,12 +164,16 @@ __device__ __forceinline__ void mfma_pass(const bf16* const (&w)[NB], RowPtr row
   const int kg = tid & 15, ri = tid >> 4;
   const float* src[NT];
   bool ok[NT];
+  float rsv[NT];
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
     const int r = ri + 16 * i;
     ok[i] = r < rows;
     src[i] = rowp(ok[i] ? r : 0) + 8 * kg;
+    rsv[i] = NORM ? rs[ok[i] ? r : 0] : 1.f;
   }
+  const float* gn = NORM ? g : nullptr;
+  float4 gq[2];
 #pragma unroll
   for (int i = 0; i < NT; ++i)
 #pragma unroll
@@ -156,28 +182,28 @@ __device__ __forceinline__ void mfma_pass(const bf16* const (&w)[NB], RowPtr row
       for (int n = 0; n < NS; ++n) acc[i][b][n] = f32x4_v{0.f, 0.f, 0.f, 0.f};
   uint4 bq0[NB][NS][MF_SC], bq1[NB][NS][MF_SC];
   float4 ar[NT][2];
-  mf_load_a(ar, src, ok, 0);
+  mf_load_a(ar, gq, src, ok, gn, kg, 0);
   mf_load_b<K, NB, NS>(bq0, w, woff, 0);
-  mf_store_a(buf[0], ar, kg, ri);
+  mf_store_a<NT, NP, NORM, CT>(buf[0], ar, gq, rsv, kg, ri);
   __syncthreads();
   // Chunk c computes from LDS buffer c % 2 and registers bq(c % 2) while
   // chunk c + 1 is loaded into the other pair; one barrier per chunk.
 #pragma unroll 1
   for (int c = 0; c < NC; c += 2) {
     if (c + 1 < NC) {
-      mf_load_a(ar, src, ok, c + 1);  // activations first: waiting for them does not wait for the weights
+      mf_load_a(ar, gq, src, ok, gn, kg, c + 1);  // activations first: waiting for them does not wait for the weights
       mf_load_b<K, NB, NS>(bq1, w, woff, c + 1);
     }
-    mf_compute<NT, NB, NS, NP>(buf[0], bq0, acc);
-    if (c + 1 < NC) mf_store_a(buf[1], ar, kg, ri);
+    mf_compute<NT, NB, NS, NP, CT>(buf[0], bq0, acc);
+    if (c + 1 < NC) mf_store_a<NT, NP, NORM, CT>(buf[1], ar, gq, rsv, kg, ri);
     __syncthreads();
     if (c + 1 < NC) {
       if (c + 2 < NC) {
-        mf_load_a(ar, src, ok, c + 2);
+        mf_load_a(ar, gq, src, ok, gn, kg, c + 2);
         mf_load_b<K, NB, NS>(bq0, w, woff, c + 2);
       }
-      mf_compute<NT, NB, NS, NP>(buf[1], bq1, acc);
-      if (c + 2 < NC) mf_store_a(buf[0], ar, kg, ri);
+      mf_compute<NT, NB, NS, NP, CT>(buf[1], bq1, acc);
+      if (c + 2 < NC) mf_store_a<NT, NP, NORM, CT>(buf[0], ar, gq, rsv, kg, ri);
       __syncthreads();
     }
   }
@@ -262,6 +288,135 @@ void launch_expert_gate_up_mfma(hipStream_t s, const bf16* wg, const bf16* wu, i
 
 void launch_expert_down_mfma(hipStream_t s, const bf16* wd, int M, const MoeBufs& mb) {
   hipLaunchKernelGGL(k_expert_down_mfma, dim3(D / 128, expert_slot_cap(M)), dim3(256), 0, s, wd, M, mb);
+}
+
+// ---- dense layers on the matrix cores -------------------------------------
+// Block (strip x, row tile y) multiplies activation rows 16 y .. 16 y + 15
+// (RMSNorm'ed first when a gain is given: the scale of each row as in
+// norm_rows_wave) with its strip of weight rows, one 16-row tile per
+// wavefront and per matrix, in one mfma_pass (inputs as bf16 hi + lo parts).
+//   DM_STORE / DM_ADD: out[m][n] = / += W0[n] . a_m, strip = rows 64 x ..;
+//   DM_SWIGLU: out[m][n] = silu(W0[n] . a_m) * (W1[n] . a_m);
+//   DM_QKV (fused RoPE and cache append, as k_qkv_rope): strip x = section
+//     x / 10 (q, k, v) of head x % 10; q / k wavefronts take rows u and u + 64
+//     (u = 16 w + j) of the head, the two halves of a RoPE pair, v wavefronts
+//     rows 32 w + j and 32 w + 16 + j.
+enum DenseMode { DM_STORE = 0, DM_ADD = 1, DM_SWIGLU = 2, DM_QKV = 3 };
+
+struct QkvOut {
+  RowPlan plan;
+  float* q;
+  bf16* kv;
+  int max_pos;
+  const float2* rope;
+};
+
+template <int K, int MODE>
+__global__ __launch_bounds__(256) void k_dense_mfma(const float* __restrict__ a, long lda,
+                                                    const float* __restrict__ gain, float eps,
+                                                    const bf16* __restrict__ W0, const bf16* __restrict__ W1, int M,
+                                                    float* __restrict__ out, long ldo, QkvOut qo) {
+  constexpr int NB = (MODE == DM_SWIGLU || MODE == DM_QKV) ? 2 : 1;
+  __shared__ MfChunkT<1> buf[2][2];
+  __shared__ float rs[16];
+  const int wave = wave_id(), lane = lane_id();
+  const int m0 = blockIdx.y * 16;
+  const int rows = min(16, M - m0);
+  const bf16* w[NB];
+  int sec = 0, h = 0, n0 = 0;
+  if constexpr (MODE == DM_QKV) {
+    sec = blockIdx.x / NH;
+    h = blockIdx.x % NH;
+    const int r0 = sec < 2 ? sec * QD + h * HD + 16 * wave : 2 * QD + h * HD + 32 * wave;
+    w[0] = W0 + (long)r0 * K;
+    w[1] = W0 + (long)(r0 + (sec < 2 ? 64 : 16)) * K;
+  } else {
+    n0 = blockIdx.x * 64 + 16 * wave;
+    w[0] = W0 + (long)n0 * K;
+    if constexpr (NB == 2) w[1] = W1 + (long)n0 * K;
+  }
+  auto rowp = [=](int r) { return a + (long)(m0 + r) * lda; };
+  f32x4_v acc[1][NB][1];
+  if (gain != nullptr) {
+    for (int r = wave; r < 16; r += 4) {
+      float ss = 0.f;
+      if (r < rows) {
+        const float* xr = a + (long)(m0 + r) * lda;
+#pragma unroll 4
+        for (int j = 0; j < K / 64; ++j) {
+          const float v = xr[lane + 64 * j];
+          ss = fmaf(v, v, ss);
+        }
+      }
+      ss = wave_sum(ss);
+      if (lane == 0) rs[r] = 1.0f / sqrtf(ss / (float)K + eps);
+    }
+    __syncthreads();
+    mfma_pass<K, 1, NB, 1, 2, decltype(rowp), true, 1>(w, rowp, rows, buf, acc, gain, rs);
+  } else {
+    mfma_pass<K, 1, NB, 1, 2, decltype(rowp), false, 1>(w, rowp, rows, buf, acc);
+  }
+  const int j = lane & 15;
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq) {
+    const int r = 4 * (lane >> 4) + qq;
+    if (r >= rows) continue;
+    const int m = m0 + r;
+    const float v0 = acc[0][0][0][qq];
+    if constexpr (MODE == DM_STORE) {
+      out[(long)m * ldo + n0 + j] = v0;
+    } else if constexpr (MODE == DM_ADD) {
+      out[(long)m * ldo + n0 + j] += v0;
+    } else if constexpr (MODE == DM_SWIGLU) {
+      out[(long)m * ldo + n0 + j] = silu(v0) * acc[0][1][0][qq];
+    } else {
+      const float v1 = acc[0][1][0][qq];
+      const RowPlan& plan = qo.plan;
+      const int b = m / plan.Q, i = m - b * plan.Q;
+      const int pos = plan.base[b] + i;
+      const bool valid = i < plan.cnt[b] && pos >= 0 && pos < qo.max_pos;
+      const long slot_stride = 2L * NH * qo.max_pos * HD;
+      if (sec < 2) {
+        const int u = 16 * wave + j;
+        const float2 cs = qo.rope[(long)min(max(pos, 0), qo.max_pos - 1) * (HD / 2) + u];
+        const float o0 = fmaf(v0, cs.x, -(v1 * cs.y));
+        const float o1 = fmaf(v1, cs.x, v0 * cs.y);
+        if (sec == 0) {
+          qo.q[(long)m * QD + h * HD + u] = o0;
+          qo.q[(long)m * QD + h * HD + u + 64] = o1;
+        } else if (valid) {
+          bf16* kd = qo.kv + (long)plan.slot[b] * slot_stride + ((long)h * qo.max_pos + pos) * HD;
+          kd[u] = f2bf(o0);
+          kd[u + 64] = f2bf(o1);
+        }
+      } else if (valid) {
+        bf16* vd = qo.kv + (long)plan.slot[b] * slot_stride + ((long)(NH + h) * qo.max_pos + pos) * HD;
+        vd[32 * wave + j] = f2bf(v0);
+        vd[32 * wave + 16 + j] = f2bf(v1);
+      }
+    }
+  }
+}
+
+void launch_gemv_mfma(hipStream_t s, int K, Epi epi, const float* a, long lda, const float* gain, float eps,
+                      const bf16* W0, const bf16* W1, int N, int M, float* out, long ldo) {
+  const dim3 grid(N / 64, (M + 15) / 16);
+  const QkvOut none{};
+#define OCR_DM(KV, MODEV) \
+  hipLaunchKernelGGL((k_dense_mfma<KV, MODEV>), grid, dim3(256), 0, s, a, lda, gain, eps, W0, W1, M, out, ldo, none)
+  if (K == D && epi == EPI_ADD) OCR_DM(D, DM_ADD);
+  else if (K == D && epi == EPI_SWIGLU) OCR_DM(D, DM_SWIGLU);
+  else if (K == D && epi == EPI_STORE) OCR_DM(D, DM_STORE);
+  else if (K == 2 * D && epi == EPI_STORE) OCR_DM(2 * D, DM_STORE);
+  else if (K == DF && epi == EPI_ADD) OCR_DM(DF, DM_ADD);
+#undef OCR_DM
+}
+
+void launch_qkv_rope_mfma(hipStream_t s, const float* x, const float* gain, float eps, const bf16* wqkv, int M,
+                          RowPlan plan, float* q, bf16* kv, int max_pos, const float2* rope) {
+  const QkvOut qo{plan, q, kv, max_pos, rope};
+  hipLaunchKernelGGL((k_dense_mfma<D, DM_QKV>), dim3(3 * NH, (M + 15) / 16), dim3(256), 0, s, x, (long)D, gain, eps,
+                     wqkv, nullptr, M, nullptr, 0L, qo);
 }
 
 // LM head rows for the matrix cores: xn[m] = RMSNorm(x[src(m)]) * gain, one

@@ -85,6 +85,13 @@ int expert_slot_cap(int M);
 // launchers above, with the activations rounded to bf16 for the MFMA inputs.
 void launch_expert_gate_up_mfma(hipStream_t s, const bf16* wg, const bf16* wu, int M, const MoeBufs& mb);
 void launch_expert_down_mfma(hipStream_t s, const bf16* wd, int M, const MoeBufs& mb);
+// Dense layers on the matrix cores (bf16 weights): the outputs of launch_gemv
+// (K, epi) in {(1280, add / store / SwiGLU), (2560, store), (3584, add)}, N a
+// multiple of 64, and of launch_qkv_rope, with the inputs as bf16 hi + lo parts.
+void launch_gemv_mfma(hipStream_t s, int K, Epi epi, const float* a, long lda, const float* gain, float eps,
+                      const bf16* W0, const bf16* W1, int N, int M, float* out, long ldo);
+void launch_qkv_rope_mfma(hipStream_t s, const float* x, const float* gain, float eps, const bf16* wqkv, int M,
+                          RowPlan plan, float* q, bf16* kv, int max_pos, const float2* rope);
 // LM head + argmax: xn ([M][D] scratch) receives the normalised rows; V >= 16.
 void launch_lmhead_mfma(hipStream_t s, const float* x, const int* cnt, int Q, bool last_valid, const float* gain,
                         float eps, const bf16* W, int V, int M, float* xn, float* part_val, int* part_idx,

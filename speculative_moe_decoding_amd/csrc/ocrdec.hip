@@ -193,10 +193,32 @@ void timing_mark(ocrdec_model* m, hipStream_t s) {
   if (hipEventRecord(m->ev[m->ev_used], s) == hipSuccess) ++m->ev_used;
 }
 
+// Arithmetic of a pass: the matrix cores for the experts and the LM head on
+// matrix-path handles, for every row count of a decode call (so a row's result
+// never depends on the call); a prefill pass of a bf16 model runs everything,
+// dense layers included, on the matrix cores whatever the handle (the prefix
+// is computed once and shared by every decode that follows).
+struct PassPath {
+  bool experts;  // grouped experts (and LM head) on the matrix cores
+  bool dense;    // QKV / O / draft GEMVs on the matrix cores
+};
+
 template <typename T>
-void expert_gate_up(ocrdec_model* m, hipStream_t s, int l, int M, int* tap) {
+PassPath decode_path(const ocrdec_model* m) {
+  return PassPath{std::is_same<T, bf16>::value && m->matrix, false};
+}
+
+template <typename T>
+PassPath prefill_path(const ocrdec_model* m) {
+  (void)m;
+  const bool bf = std::is_same<T, bf16>::value;
+  return PassPath{bf, bf};
+}
+
+template <typename T>
+void expert_gate_up(ocrdec_model* m, hipStream_t s, int l, int M, int* tap, bool mx) {
   if constexpr (std::is_same<T, bf16>::value) {
-    if (m->matrix) {
+    if (mx) {
       launch_expert_gate_up_mfma(s, wmat<T>(m, lw(m, l, L_GATE)), wmat<T>(m, lw(m, l, L_UP)), M, m->mb);
       return;
     }
@@ -205,9 +227,9 @@ void expert_gate_up(ocrdec_model* m, hipStream_t s, int l, int M, int* tap) {
 }
 
 template <typename T>
-void expert_down(ocrdec_model* m, hipStream_t s, int l, int M) {
+void expert_down(ocrdec_model* m, hipStream_t s, int l, int M, bool mx) {
   if constexpr (std::is_same<T, bf16>::value) {
-    if (m->matrix) {
+    if (mx) {
       launch_expert_down_mfma(s, wmat<T>(m, lw(m, l, L_DOWN)), M, m->mb);
       return;
     }
@@ -231,43 +253,66 @@ void lm_head(ocrdec_model* m, hipStream_t s, const float* x, int Q, bool last_va
                    m->lm_idx, logits, tok, tok_stride);
 }
 
+// Dense layers: the matrix cores (mx) or the vector GEMV.
 template <typename T>
-void verifier_layers(ocrdec_model* m, hipStream_t s, int M, int B, RowPlan plan, int nch, bool taps,
+void dense_gemv(ocrdec_model* m, hipStream_t s, bool mx, int K, Epi epi, const float* a, long lda,
+                const float* gain, const T* W0, const T* W1, int N, int M, float* out, long ldo) {
+  if constexpr (std::is_same<T, bf16>::value) {
+    if (mx) {
+      launch_gemv_mfma(s, K, epi, a, lda, gain, m->cfg.norm_eps, W0, W1, N, M, out, ldo);
+      return;
+    }
+  }
+  launch_gemv<T>(s, K, epi, a, lda, gain, m->cfg.norm_eps, W0, W1, N, M, out, ldo);
+}
+
+template <typename T>
+void dense_qkv(ocrdec_model* m, hipStream_t s, bool mx, const float* x, const float* gain, const T* W, int M,
+               RowPlan plan, T* kv) {
+  if constexpr (std::is_same<T, bf16>::value) {
+    if (mx) {
+      launch_qkv_rope_mfma(s, x, gain, m->cfg.norm_eps, W, M, plan, m->q, kv, m->cfg.max_positions, m->rope);
+      return;
+    }
+  }
+  launch_qkv_rope<T>(s, x, gain, m->cfg.norm_eps, W, M, plan, m->q, kv, m->cfg.max_positions, m->rope);
+}
+
+template <typename T>
+void verifier_layers(ocrdec_model* m, hipStream_t s, PassPath pp, int M, int B, RowPlan plan, int nch, bool taps,
                      const float* rlog) {
   const ocrdec_config& c = m->cfg;
   for (int l = 0; l < c.n_layers; ++l) {
     T* kvl = static_cast<T*>((void*)(m->state + m->p.s_kv)) + (size_t)l * m->p.kv_layer_elems;
-    launch_qkv_rope<T>(s, m->x, wvec(m, lw(m, l, L_ANORM)), c.norm_eps, wmat<T>(m, lw(m, l, L_QKV)), M, plan, m->q,
-                       kvl, c.max_positions, m->rope);
+    dense_qkv<T>(m, s, pp.dense, m->x, wvec(m, lw(m, l, L_ANORM)), wmat<T>(m, lw(m, l, L_QKV)), M, plan, kvl);
     launch_attention<T>(s, m->q, kvl, c.max_positions, plan, B, nch, m->p.tiles_per_chunk, m->part, m->attn);
-    launch_gemv<T>(s, QD, EPI_ADD, m->attn, QD, nullptr, c.norm_eps, wmat<T>(m, lw(m, l, L_WO)), nullptr, D, M,
-                   m->x, D);
+    dense_gemv<T>(m, s, pp.dense, QD, EPI_ADD, m->attn, QD, nullptr, wmat<T>(m, lw(m, l, L_WO)), nullptr, D, M,
+                  m->x, D);
     int* tap = (taps && m->tap_route) ? m->tap_route + (size_t)l * M * NSLOT : nullptr;
     launch_router<T>(s, m->x, wvec(m, lw(m, l, L_FNORM)), c.norm_eps, wmat<T>(m, lw(m, l, L_ROUTER)), M, m->mb,
                      tap, rlog ? rlog + (size_t)l * M * NE : nullptr);
     timing_mark(m, s);
-    expert_gate_up<T>(m, s, l, M, tap);
+    expert_gate_up<T>(m, s, l, M, tap, pp.experts);
     timing_mark(m, s);
-    expert_down<T>(m, s, l, M);
+    expert_down<T>(m, s, l, M, pp.experts);
     timing_mark(m, s);
     launch_moe_combine(s, m->x, M, m->mb);
   }
 }
 
 template <typename T>
-void draft_layer(ocrdec_model* m, hipStream_t s, int M, int B, RowPlan plan, int nch) {
+void draft_layer(ocrdec_model* m, hipStream_t s, PassPath pp, int M, int B, RowPlan plan, int nch) {
   const ocrdec_config& c = m->cfg;
+  const bool mx = pp.dense;
   T* dkv = static_cast<T*>((void*)(m->state + m->p.s_dkv));
-  launch_gemv<T>(s, 2 * D, EPI_STORE, m->cat, 2 * D, nullptr, c.norm_eps, wmat<T>(m, dw(m, D_FUSE)), nullptr, D, M,
-                 m->u, D);
-  launch_qkv_rope<T>(s, m->u, wvec(m, dw(m, D_ANORM)), c.norm_eps, wmat<T>(m, dw(m, D_QKV)), M, plan, m->q, dkv,
-                     c.max_positions, m->rope);
+  dense_gemv<T>(m, s, mx, 2 * D, EPI_STORE, m->cat, 2 * D, nullptr, wmat<T>(m, dw(m, D_FUSE)), nullptr, D, M, m->u,
+                D);
+  dense_qkv<T>(m, s, mx, m->u, wvec(m, dw(m, D_ANORM)), wmat<T>(m, dw(m, D_QKV)), M, plan, dkv);
   launch_attention<T>(s, m->q, dkv, c.max_positions, plan, B, nch, m->p.tiles_per_chunk, m->part, m->attn);
-  launch_gemv<T>(s, QD, EPI_ADD, m->attn, QD, nullptr, c.norm_eps, wmat<T>(m, dw(m, D_WO)), nullptr, D, M, m->u, D);
-  launch_gemv<T>(s, D, EPI_SWIGLU, m->u, D, wvec(m, dw(m, D_FNORM)), c.norm_eps, wmat<T>(m, dw(m, D_GATE)),
-                 wmat<T>(m, dw(m, D_UP)), DF, M, m->dffn, DF);
-  launch_gemv<T>(s, DF, EPI_ADD, m->dffn, DF, nullptr, c.norm_eps, wmat<T>(m, dw(m, D_DOWN)), nullptr, D, M, m->u,
-                 D);
+  dense_gemv<T>(m, s, mx, QD, EPI_ADD, m->attn, QD, nullptr, wmat<T>(m, dw(m, D_WO)), nullptr, D, M, m->u, D);
+  dense_gemv<T>(m, s, mx, D, EPI_SWIGLU, m->u, D, wvec(m, dw(m, D_FNORM)), wmat<T>(m, dw(m, D_GATE)),
+                wmat<T>(m, dw(m, D_UP)), DF, M, m->dffn, DF);
+  dense_gemv<T>(m, s, mx, DF, EPI_ADD, m->dffn, DF, nullptr, wmat<T>(m, dw(m, D_DOWN)), nullptr, D, M, m->u, D);
 }
 
 // Prefill in passes of up to prefill_group entries of PREFILL_CHUNK rows: the
@@ -308,11 +353,11 @@ int do_prefill(ocrdec_model* m, hipStream_t s, int B, const int32_t* slots_host,
     const int M = g.n * PREFILL_CHUNK;
     RowPlan plan{m->plan_base, m->plan_cnt, m->plan_slot, PREFILL_CHUNK};
     const int nch = chunks_for(m, std::min(c.max_positions - 1, max_pos));
-    verifier_layers<T>(m, s, M, g.n, plan, nch, false, nullptr);
+    verifier_layers<T>(m, s, prefill_path<T>(m), M, g.n, plan, nch, false, nullptr);
     if (finish) lm_head<T>(m, s, m->x, PREFILL_CHUNK, true, wvec(m, W_FNORM), g.n, nullptr, m->tok_tmp, 1);
     launch_draft_prefill_cat(s, g, m->x, m->esave, hprev, hnext, wvec(m, dw(m, D_NH)), wvec(m, dw(m, D_NE)),
                              c.norm_eps, m->cat);
-    draft_layer<T>(m, s, M, g.n, plan, nch);
+    draft_layer<T>(m, s, prefill_path<T>(m), M, g.n, plan, nch);
     if (finish) launch_prefill_finish(s, g, m->x, m->tok_tmp, m->sv, pending_out);
   }
   for (int b = 0; b < B; ++b) m->slot_bound[slots_host ? slots_host[b] : b] = nv_host[b] + np_host[b];
@@ -328,7 +373,7 @@ int do_draft(ocrdec_model* m, hipStream_t s, int B, const int32_t* slots, int K,
   launch_plan_draft_catchup<T>(s, B, Q, slots, m->sv, wmat<T>(m, W_EMBED), c.vocab, wvec(m, dw(m, D_NH)),
                                wvec(m, dw(m, D_NE)), c.norm_eps, m->plan_base, m->plan_cnt, m->plan_slot, m->cat);
   RowPlan plan{m->plan_base, m->plan_cnt, m->plan_slot, Q};
-  draft_layer<T>(m, s, B * Q, B, plan, nch);
+  draft_layer<T>(m, s, decode_path<T>(m), B * Q, B, plan, nch);
   lm_head<T>(m, s, m->u, Q, true, wvec(m, dw(m, D_ONORM)), B, nullptr, draft_out, K);
   for (int j = 2; j <= K; ++j) {
     const int Qprev = (j == 2) ? Q : 1;
@@ -336,7 +381,7 @@ int do_draft(ocrdec_model* m, hipStream_t s, int B, const int32_t* slots, int K,
                               wvec(m, dw(m, D_NH)), wvec(m, dw(m, D_NE)), c.norm_eps, m->u, m->plan_base, m->plan_cnt,
                               m->plan_slot, m->cat);
     RowPlan p1{m->plan_base, m->plan_cnt, m->plan_slot, 1};
-    draft_layer<T>(m, s, B, B, p1, nch);
+    draft_layer<T>(m, s, decode_path<T>(m), B, B, p1, nch);
     lm_head<T>(m, s, m->u, 1, true, wvec(m, dw(m, D_ONORM)), B, nullptr, draft_out + (j - 1), K);
   }
   return hip_check("ocrdec_draft");
@@ -351,7 +396,7 @@ int do_verify(ocrdec_model* m, hipStream_t s, int B, const int32_t* slots, int K
   launch_plan_verify<T>(s, B, K, slots, m->sv, draft, wmat<T>(m, W_EMBED), c.vocab, m->plan_base, m->plan_cnt,
                         m->plan_slot, m->x);
   RowPlan plan{m->plan_base, m->plan_cnt, m->plan_slot, Q};
-  verifier_layers<T>(m, s, M, B, plan, nch, true, m->router_override);
+  verifier_layers<T>(m, s, decode_path<T>(m), M, B, plan, nch, true, m->router_override);
   m->last_verify_rows = M;
   lm_head<T>(m, s, m->x, Q, false, wvec(m, W_FNORM), M, logits_out, greedy_out, 1);
   if (m->tap_hidden) launch_copy_rows(s, m->x, m->tap_hidden, (long)M * D);
@@ -587,8 +632,8 @@ int ocrdec_replay_expert_gate_up(ocrdec_model* m, void* stream, int n_rounds, in
   const int M = m->last_verify_rows;
   for (int r = 0; r < n_rounds; ++r) {
     for (int l = 0; l < m->cfg.n_layers; ++l) {
-      if (m->cfg.dtype == OCRDEC_BF16) expert_gate_up<bf16>(m, s, l, M, nullptr);
-      else expert_gate_up<float>(m, s, l, M, nullptr);
+      if (m->cfg.dtype == OCRDEC_BF16) expert_gate_up<bf16>(m, s, l, M, nullptr, decode_path<bf16>(m).experts);
+      else expert_gate_up<float>(m, s, l, M, nullptr, false);
     }
   }
   return hip_check("ocrdec_replay_expert_gate_up");
