@@ -398,6 +398,195 @@ __global__ __launch_bounds__(256) void k_dense_mfma(const float* __restrict__ a,
   }
 }
 
+// Decode-sized calls: the same outputs with more, smaller blocks.  Block
+// (strip x, row tile y) owns 16 weight rows per matrix; its four wavefronts
+// split k into quarters and stream their A fragments (fp32 -> bf16 hi + lo,
+// RMSNorm'ed when a gain is given) and B fragments straight from memory, a
+// DKS_PF-step register ring deep, with no LDS staging; the four partial
+// 16x16 tiles are added in LDS in wavefront order, wavefront w finishing
+// output rows 4 (lane / 16) + w.  Strips: DM_QKV 120 (q / k: 16 pair rows
+// u0 .. u0+15 and u0+64 .. of a head, 80 strips; v: 32 rows of a head as two
+// tiles, 40 strips), else N / 16.
+constexpr int DKS_PF = 4;
+
+template <int K, int MODE>
+__global__ __launch_bounds__(256) void k_dense_ks(const float* __restrict__ a, long lda,
+                                                  const float* __restrict__ gain, float eps,
+                                                  const bf16* __restrict__ W0, const bf16* __restrict__ W1, int M,
+                                                  float* __restrict__ out, long ldo, QkvOut qo) {
+  constexpr int NB = (MODE == DM_SWIGLU || MODE == DM_QKV) ? 2 : 1;
+  constexpr int KQ = K / 4;
+  constexpr int NSTEP = KQ / 32;
+  static_assert(KQ % 32 == 0, "k quarter must be a multiple of 32");
+  __shared__ float4 red[4][NB][64];
+  __shared__ float rs[16];
+  const int wave = wave_id(), lane = lane_id();
+  const int m0 = blockIdx.y * 16;
+  const int rows = min(16, M - m0);
+  const int x = blockIdx.x;
+  int sec = 0, h = 0, c0 = 0;  // c0: first output column (row of W) of the strip
+  long r0, r1 = 0;
+  if constexpr (MODE == DM_QKV) {
+    if (x < 80) {
+      sec = x / 40;
+      h = (x % 40) / 4;
+      c0 = 16 * (x % 4);
+      r0 = sec * QD + h * HD + c0;
+      r1 = r0 + 64;
+    } else {
+      sec = 2;
+      h = (x - 80) / 4;
+      c0 = 32 * ((x - 80) % 4);
+      r0 = 2 * QD + h * HD + c0;
+      r1 = r0 + 16;
+    }
+  } else {
+    c0 = 16 * x;
+    r0 = c0;
+    r1 = c0;
+  }
+  if (gain != nullptr) {
+    for (int r = wave; r < 16; r += 4) {
+      float ss = 0.f;
+      if (r < rows) {
+        const float* xr = a + (long)(m0 + r) * lda;
+#pragma unroll 4
+        for (int j = 0; j < K / 64; ++j) {
+          const float v = xr[lane + 64 * j];
+          ss = fmaf(v, v, ss);
+        }
+      }
+      ss = wave_sum(ss);
+      if (lane == 0) rs[r] = 1.0f / sqrtf(ss / (float)K + eps);
+    }
+    __syncthreads();
+  }
+  const int ar = lane & 15;          // A row of this lane
+  const bool aok = ar < rows;
+  const float* arow = a + (long)(m0 + (aok ? ar : 0)) * lda;
+  const float rscale = (gain != nullptr) ? rs[aok ? ar : 0] : 1.f;
+  const int kl = wave * KQ + 8 * (lane >> 4);  // this lane's k offset within a step
+  const bf16* wb[NB];
+  wb[0] = W0 + (r0 + (lane & 15)) * K + kl;
+  if constexpr (NB == 2) wb[1] = (MODE == DM_QKV ? W0 : W1) + (r1 + (lane & 15)) * K + kl;
+  uint4 bq[DKS_PF][NB];
+  float4 aq[DKS_PF][2], gq[DKS_PF][2];
+  auto load = [&](int t, int slot) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) bq[slot][b] = ldg16_stream(wb[b] + 32 * t);
+    const float4* ap = reinterpret_cast<const float4*>(arow + kl + 32 * t);
+    aq[slot][0] = ap[0];
+    aq[slot][1] = ap[1];
+    if (gain != nullptr) {
+      const float4* gp = reinterpret_cast<const float4*>(gain + kl + 32 * t);
+      gq[slot][0] = gp[0];
+      gq[slot][1] = gp[1];
+    }
+  };
+#pragma unroll
+  for (int t = 0; t < DKS_PF; ++t)
+    if (t < NSTEP) load(t, t);
+  f32x4_v acc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int t = 0; t < NSTEP; ++t) {
+    const int slot = t % DKS_PF;
+    float4 v0 = aq[slot][0], v1 = aq[slot][1];
+    if (gain != nullptr) {
+      v0 = mf_norm(v0, rscale, gq[slot][0]);
+      v1 = mf_norm(v1, rscale, gq[slot][1]);
+    }
+    if (!aok) {
+      v0 = make_float4(0.f, 0.f, 0.f, 0.f);
+      v1 = v0;
+    }
+    uint4 hi, lo;
+    hi.x = pack_bf16x2(v0.x, v0.y);
+    hi.y = pack_bf16x2(v0.z, v0.w);
+    hi.z = pack_bf16x2(v1.x, v1.y);
+    hi.w = pack_bf16x2(v1.z, v1.w);
+    lo.x = pack_bf16x2(rem_lo(v0.x, hi.x), rem_hi(v0.y, hi.x));
+    lo.y = pack_bf16x2(rem_lo(v0.z, hi.y), rem_hi(v0.w, hi.y));
+    lo.z = pack_bf16x2(rem_lo(v1.x, hi.z), rem_hi(v1.y, hi.z));
+    lo.w = pack_bf16x2(rem_lo(v1.z, hi.w), rem_hi(v1.w, hi.w));
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      acc[b] = mfma_bf16(hi, bq[slot][b], acc[b]);
+      acc[b] = mfma_bf16(lo, bq[slot][b], acc[b]);
+    }
+    if (t + DKS_PF < NSTEP) load(t + DKS_PF, slot);
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b) red[wave][b][lane] = make_float4(acc[b][0], acc[b][1], acc[b][2], acc[b][3]);
+  __syncthreads();
+  // wavefront w finishes element q = w of every lane's four: row 4 (lane / 16) + w, column lane % 16
+  const int r = 4 * (lane >> 4) + wave;
+  if (r >= rows) return;
+  const int m = m0 + r, j = lane & 15;
+  float v[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    float t = reinterpret_cast<const float*>(&red[0][b][lane])[wave];
+    t += reinterpret_cast<const float*>(&red[1][b][lane])[wave];
+    t += reinterpret_cast<const float*>(&red[2][b][lane])[wave];
+    t += reinterpret_cast<const float*>(&red[3][b][lane])[wave];
+    v[b] = t;
+  }
+  if constexpr (MODE == DM_STORE) {
+    out[(long)m * ldo + c0 + j] = v[0];
+  } else if constexpr (MODE == DM_ADD) {
+    out[(long)m * ldo + c0 + j] += v[0];
+  } else if constexpr (MODE == DM_SWIGLU) {
+    out[(long)m * ldo + c0 + j] = silu(v[0]) * v[NB - 1];
+  } else {
+    const RowPlan& plan = qo.plan;
+    const int b = m / plan.Q, i = m - b * plan.Q;
+    const int pos = plan.base[b] + i;
+    const bool valid = i < plan.cnt[b] && pos >= 0 && pos < qo.max_pos;
+    const long slot_stride = 2L * NH * qo.max_pos * HD;
+    if (sec < 2) {
+      const int u = c0 + j;
+      const float2 cs = qo.rope[(long)min(max(pos, 0), qo.max_pos - 1) * (HD / 2) + u];
+      const float o0 = fmaf(v[0], cs.x, -(v[NB - 1] * cs.y));
+      const float o1 = fmaf(v[NB - 1], cs.x, v[0] * cs.y);
+      if (sec == 0) {
+        qo.q[(long)m * QD + h * HD + u] = o0;
+        qo.q[(long)m * QD + h * HD + u + 64] = o1;
+      } else if (valid) {
+        bf16* kd = qo.kv + (long)plan.slot[b] * slot_stride + ((long)h * qo.max_pos + pos) * HD;
+        kd[u] = f2bf(o0);
+        kd[u + 64] = f2bf(o1);
+      }
+    } else if (valid) {
+      bf16* vd = qo.kv + (long)plan.slot[b] * slot_stride + ((long)(NH + h) * qo.max_pos + pos) * HD;
+      vd[c0 + j] = f2bf(v[0]);
+      vd[c0 + 16 + j] = f2bf(v[NB - 1]);
+    }
+  }
+}
+
+void launch_gemv_ks(hipStream_t s, int K, Epi epi, const float* a, long lda, const float* gain, float eps,
+                    const bf16* W0, const bf16* W1, int N, int M, float* out, long ldo) {
+  const dim3 grid(N / 16, (M + 15) / 16);
+  const QkvOut none{};
+#define OCR_DK(KV, MODEV) \
+  hipLaunchKernelGGL((k_dense_ks<KV, MODEV>), grid, dim3(256), 0, s, a, lda, gain, eps, W0, W1, M, out, ldo, none)
+  if (K == D && epi == EPI_ADD) OCR_DK(D, DM_ADD);
+  else if (K == D && epi == EPI_SWIGLU) OCR_DK(D, DM_SWIGLU);
+  else if (K == D && epi == EPI_STORE) OCR_DK(D, DM_STORE);
+  else if (K == 2 * D && epi == EPI_STORE) OCR_DK(2 * D, DM_STORE);
+  else if (K == DF && epi == EPI_ADD) OCR_DK(DF, DM_ADD);
+#undef OCR_DK
+}
+
+void launch_qkv_rope_ks(hipStream_t s, const float* x, const float* gain, float eps, const bf16* wqkv, int M,
+                        RowPlan plan, float* q, bf16* kv, int max_pos, const float2* rope) {
+  const QkvOut qo{plan, q, kv, max_pos, rope};
+  hipLaunchKernelGGL((k_dense_ks<D, DM_QKV>), dim3(120, (M + 15) / 16), dim3(256), 0, s, x, (long)D, gain, eps, wqkv,
+                     nullptr, M, nullptr, 0L, qo);
+}
+
 void launch_gemv_mfma(hipStream_t s, int K, Epi epi, const float* a, long lda, const float* gain, float eps,
                       const bf16* W0, const bf16* W1, int N, int M, float* out, long ldo) {
   const dim3 grid(N / 64, (M + 15) / 16);

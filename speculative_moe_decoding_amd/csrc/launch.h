@@ -92,6 +92,12 @@ void launch_gemv_mfma(hipStream_t s, int K, Epi epi, const float* a, long lda, c
                       const bf16* W0, const bf16* W1, int N, int M, float* out, long ldo);
 void launch_qkv_rope_mfma(hipStream_t s, const float* x, const float* gain, float eps, const bf16* wqkv, int M,
                           RowPlan plan, float* q, bf16* kv, int max_pos, const float2* rope);
+// The same with k split over the four wavefronts of 16-row blocks (decode-sized
+// calls: many blocks, no LDS staging).
+void launch_gemv_ks(hipStream_t s, int K, Epi epi, const float* a, long lda, const float* gain, float eps,
+                    const bf16* W0, const bf16* W1, int N, int M, float* out, long ldo);
+void launch_qkv_rope_ks(hipStream_t s, const float* x, const float* gain, float eps, const bf16* wqkv, int M,
+                        RowPlan plan, float* q, bf16* kv, int max_pos, const float2* rope);
 // LM head + argmax: xn ([M][D] scratch) receives the normalised rows; V >= 16.
 void launch_lmhead_mfma(hipStream_t s, const float* x, const int* cnt, int Q, bool last_valid, const float* gain,
                         float eps, const bf16* W, int V, int M, float* xn, float* part_val, int* part_idx,

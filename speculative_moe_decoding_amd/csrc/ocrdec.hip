@@ -193,26 +193,29 @@ void timing_mark(ocrdec_model* m, hipStream_t s) {
   if (hipEventRecord(m->ev[m->ev_used], s) == hipSuccess) ++m->ev_used;
 }
 
-// Arithmetic of a pass: the matrix cores for the experts and the LM head on
-// matrix-path handles, for every row count of a decode call (so a row's result
-// never depends on the call); a prefill pass of a bf16 model runs everything,
-// dense layers included, on the matrix cores whatever the handle (the prefix
-// is computed once and shared by every decode that follows).
+// Arithmetic of a pass.  Decode calls of a matrix-path handle run the experts,
+// the LM head and the dense layers on the matrix cores for every row count (so
+// a row's result never depends on the call; the dense layers in 16-row blocks
+// with k split over the wavefronts); a prefill pass of a bf16 model runs the
+// experts and the dense layers on the matrix cores whatever the handle (64-row
+// strips; the prefix is computed once and shared by every decode that follows).
+enum DensePath { DENSE_VECTOR = 0, DENSE_KSPLIT = 1, DENSE_STRIP = 2 };
 struct PassPath {
-  bool experts;  // grouped experts (and LM head) on the matrix cores
-  bool dense;    // QKV / O / draft GEMVs on the matrix cores
+  bool experts;  // grouped experts on the matrix cores
+  int dense;     // DensePath of the QKV / O / draft GEMVs
 };
 
 template <typename T>
 PassPath decode_path(const ocrdec_model* m) {
-  return PassPath{std::is_same<T, bf16>::value && m->matrix, false};
+  const bool mx = std::is_same<T, bf16>::value && m->matrix;
+  return PassPath{mx, mx ? DENSE_KSPLIT : DENSE_VECTOR};
 }
 
 template <typename T>
 PassPath prefill_path(const ocrdec_model* m) {
   (void)m;
   const bool bf = std::is_same<T, bf16>::value;
-  return PassPath{bf, bf};
+  return PassPath{bf, bf ? DENSE_STRIP : DENSE_VECTOR};
 }
 
 template <typename T>
@@ -253,13 +256,17 @@ void lm_head(ocrdec_model* m, hipStream_t s, const float* x, int Q, bool last_va
                    m->lm_idx, logits, tok, tok_stride);
 }
 
-// Dense layers: the matrix cores (mx) or the vector GEMV.
+// Dense layers on the path dp (DensePath).
 template <typename T>
-void dense_gemv(ocrdec_model* m, hipStream_t s, bool mx, int K, Epi epi, const float* a, long lda,
+void dense_gemv(ocrdec_model* m, hipStream_t s, int dp, int K, Epi epi, const float* a, long lda,
                 const float* gain, const T* W0, const T* W1, int N, int M, float* out, long ldo) {
   if constexpr (std::is_same<T, bf16>::value) {
-    if (mx) {
+    if (dp == DENSE_STRIP) {
       launch_gemv_mfma(s, K, epi, a, lda, gain, m->cfg.norm_eps, W0, W1, N, M, out, ldo);
+      return;
+    }
+    if (dp == DENSE_KSPLIT) {
+      launch_gemv_ks(s, K, epi, a, lda, gain, m->cfg.norm_eps, W0, W1, N, M, out, ldo);
       return;
     }
   }
@@ -267,11 +274,15 @@ void dense_gemv(ocrdec_model* m, hipStream_t s, bool mx, int K, Epi epi, const f
 }
 
 template <typename T>
-void dense_qkv(ocrdec_model* m, hipStream_t s, bool mx, const float* x, const float* gain, const T* W, int M,
+void dense_qkv(ocrdec_model* m, hipStream_t s, int dp, const float* x, const float* gain, const T* W, int M,
                RowPlan plan, T* kv) {
   if constexpr (std::is_same<T, bf16>::value) {
-    if (mx) {
+    if (dp == DENSE_STRIP) {
       launch_qkv_rope_mfma(s, x, gain, m->cfg.norm_eps, W, M, plan, m->q, kv, m->cfg.max_positions, m->rope);
+      return;
+    }
+    if (dp == DENSE_KSPLIT) {
+      launch_qkv_rope_ks(s, x, gain, m->cfg.norm_eps, W, M, plan, m->q, kv, m->cfg.max_positions, m->rope);
       return;
     }
   }
@@ -303,7 +314,7 @@ void verifier_layers(ocrdec_model* m, hipStream_t s, PassPath pp, int M, int B, 
 template <typename T>
 void draft_layer(ocrdec_model* m, hipStream_t s, PassPath pp, int M, int B, RowPlan plan, int nch) {
   const ocrdec_config& c = m->cfg;
-  const bool mx = pp.dense;
+  const int mx = pp.dense;
   T* dkv = static_cast<T*>((void*)(m->state + m->p.s_dkv));
   dense_gemv<T>(m, s, mx, 2 * D, EPI_STORE, m->cat, 2 * D, nullptr, wmat<T>(m, dw(m, D_FUSE)), nullptr, D, M, m->u,
                 D);
