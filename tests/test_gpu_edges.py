@@ -1,8 +1,8 @@
 """Edge cases of the decode path against the oracle (small 2-layer models):
 prefixes of a single row (prompt only / vision only), the largest draft length
 K = 7, vocabularies of 2 and 65 tokens (one LM-head block; a 1-token tail past
-the 64-row tiles, on both arithmetic paths) and 64 (exactly one tile).
-Tolerances as in the other parity tests."""
+the 64-row tiles, on both arithmetic paths) and 64 (exactly one tile), and the
+largest call (1,024 verify rows).  Tolerances as in the other parity tests."""
 import dataclasses
 
 import numpy as np
@@ -75,3 +75,51 @@ def test_small_vocabularies(vocab, dtype, path):
     assert g_sp == g_ar
     assert all(0 <= t < vocab for t in g_ar)
     log(f"V={vocab} {dtype} path {path}: {n} AR steps agree (max |dlogit| {worst:.1e}); K=3 lossless")
+
+
+def test_max_rows_per_call():
+    """The largest call a handle allows: max_batch 256 with K = 3, i.e. 1,024
+    verify rows (the limit of the routing sort), on the matrix path (bf16, 2
+    layers).  256 short pages are prefilled together and verified in one call
+    with random drafts.  Sampled sequences match the oracle (logits 5e-2;
+    greedy tokens exact unless the oracle's top-2 margin is under that), and
+    the same sequences verified alone (B = 1 calls on the same handle) give
+    bitwise the rows of the 1,024-row call."""
+    cfg = dataclasses.replace(synth.FULL, n_layers=2, vocab=3001, dtype="bf16")
+    B, K, tol = 256, 3, 5e-2
+    w = synth.Weights(cfg, 67)
+    dec = ocrdec.Decoder(cfg, w.device_arrays(), max_batch=B, max_k=K, max_positions=64)
+    rng = np.random.default_rng(68)
+    nv = rng.integers(1, 12, size=B)
+    npr = rng.integers(1, 6, size=B)
+    pages = synth.make_pages(cfg, 69, nv.tolist(), npr.tolist(), [4] * B)
+    pend = dec.prefill(pages)
+    drafts = rng.integers(0, cfg.vocab, size=(B, K)).astype(np.int32)
+    logits = torch.empty(B, K + 1, cfg.vocab, dtype=torch.float32, device="cuda")
+    greedy = dec.verify(B, K, torch.from_numpy(drafts).cuda(), logits=logits)
+    torch.cuda.synchronize()
+    g_pend, g_tok, g_logits = pend.cpu().numpy(), greedy.cpu().numpy(), logits.cpu().numpy()
+    orc = od.Oracle(cfg, w.f32)
+    sampled = [0, 101, B - 1]
+    for b in sampled:
+        p = pages[b]
+        st = orc.new_state(p.prefix_len + K + 1)
+        y0 = orc.prefill(st, p.vision, p.prompt, with_draft=False)
+        if int(g_pend[b]) != y0:
+            assert od.top2_margin(st.first_logits[None])[0] < tol, (b, int(g_pend[b]), y0)
+            continue
+        ids = [y0] + drafts[b].tolist()
+        ref = orc.lm_logits(orc.verifier_forward(st, orc.embed(ids), np.arange(p.prefix_len, p.prefix_len + K + 1)))
+        diff = float(np.abs(g_logits[b] - ref).max())
+        log(f"1,024-row call, sequence {b} (prefix {p.prefix_len}): max |dlogit| {diff:.2e}")
+        assert diff < tol
+        margins = od.top2_margin(ref)
+        for i in range(K + 1):
+            if g_tok[b, i] != od.greedy(ref[i:i + 1])[0]:
+                assert margins[i] < tol, (b, i, margins[i])
+    for b in sampled:
+        one = torch.empty(1, K + 1, cfg.vocab, dtype=torch.float32, device="cuda")
+        slot = torch.tensor([b], dtype=torch.int32, device="cuda")
+        dec.verify(1, K, torch.from_numpy(drafts[b:b + 1]).cuda(), slots=slot, logits=one)
+        torch.cuda.synchronize()
+        assert np.array_equal(one.cpu().numpy()[0], g_logits[b]), b
