@@ -16,6 +16,9 @@
 namespace ocr {
 
 constexpr int QMAX_ATT = 8;  // query rows per sequence handled by one block
+// Row stride of the transposed key tile: one spare element per row, so the
+// staging writes of one key's dims (one row each) fall in different LDS banks.
+constexpr int KQ_STRIDE = ATT_TILE + 1;
 
 // LDS tile formats: the fp32 model stages keys / values widened to fp32; the
 // bf16 model keeps them in bf16 (half the LDS, so more blocks per CU keep more
@@ -26,7 +29,7 @@ template <> struct AttTile<float> {
   typedef float2 V2;   // 2 value dims
   __device__ static __forceinline__ float4 k(const K4& v) { return v; }
   __device__ static __forceinline__ float2 v(const V2& x) { return x; }
-  __device__ static __forceinline__ void stage(const uint4& kr, const uint4& vr, int d0, int t, K4 (*Kq)[ATT_TILE],
+  __device__ static __forceinline__ void stage(const uint4& kr, const uint4& vr, int d0, int t, K4 (*Kq)[KQ_STRIDE],
                                                V2 (*Vs)[HD / 2]) {
     // a 16-byte chunk holds dims d0 .. d0+3
     Kq[d0 / 4][t] = make_float4(__uint_as_float(kr.x), __uint_as_float(kr.y), __uint_as_float(kr.z),
@@ -45,15 +48,12 @@ template <> struct AttTile<bf16> {
   __device__ static __forceinline__ float2 v(const V2& x) {
     return make_float2(__uint_as_float(x << 16), __uint_as_float(x & 0xffff0000u));
   }
-  __device__ static __forceinline__ void stage(const uint4& kr, const uint4& vr, int d0, int t, K4 (*Kq)[ATT_TILE],
+  __device__ static __forceinline__ void stage(const uint4& kr, const uint4& vr, int d0, int t, K4 (*Kq)[KQ_STRIDE],
                                                V2 (*Vs)[HD / 2]) {
     // a 16-byte chunk holds dims d0 .. d0+7
     Kq[d0 / 4][t] = make_uint2(kr.x, kr.y);
     Kq[d0 / 4 + 1][t] = make_uint2(kr.z, kr.w);
-    Vs[t][d0 / 2] = vr.x;
-    Vs[t][d0 / 2 + 1] = vr.y;
-    Vs[t][d0 / 2 + 2] = vr.z;
-    Vs[t][d0 / 2 + 3] = vr.w;
+    *reinterpret_cast<uint4*>(&Vs[t][d0 / 2]) = vr;
   }
 };
 
@@ -64,7 +64,7 @@ template <> struct AttTile<bf16> {
 // query's.  pw is the wavefront's 64-float LDS row for the probabilities.
 template <typename T>
 __device__ __forceinline__ void attn_tile_query(const float4* __restrict__ qrow,
-                                                const typename AttTile<T>::K4 (*Kq)[ATT_TILE],
+                                                const typename AttTile<T>::K4 (*Kq)[KQ_STRIDE],
                                                 const typename AttTile<T>::V2 (*Vs)[HD / 2], float4* pw, int kt,
                                                 int plim, float& mrun, float& lrun, float& o0, float& o1) {
   typedef AttTile<T> AT;
@@ -129,8 +129,8 @@ __global__ __launch_bounds__(256) void k_attn_partial(const float* __restrict__ 
                                                       int tiles_per_chunk, float* __restrict__ part) {
   typedef AttTile<T> AT;
   // keys transposed in groups of 4 dims: Kq[d/4][t] = (k_t[d..d+3]); values row-major
-  __shared__ typename AT::K4 Kq[HD / 4][ATT_TILE];
-  __shared__ typename AT::V2 Vs[ATT_TILE][HD / 2];
+  __shared__ typename AT::K4 Kq[HD / 4][KQ_STRIDE];
+  __shared__ __align__(16) typename AT::V2 Vs[ATT_TILE][HD / 2];
   __shared__ float4 qs[QMAX_ATT][HD / 4];
   __shared__ float4 ps[4][ATT_TILE / 4];
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
