@@ -46,8 +46,15 @@ constexpr int MF_SC = MF_KC / 32;    // MFMA k-steps per chunk
 constexpr int MF_MT = 4;             // 16-row tiles per pass
 constexpr int MF_ROWS = 16 * MF_MT;  // activation rows per pass
 
-// One LDS chunk of CT tiles: f[tile][step][lane] is lane's A fragment, i.e.
-// row 16 tile + lane % 16, k = 32 step + 8 (lane / 16) .. +7 of the chunk.
+// One LDS chunk of CT tiles: f[tile][step][mf_slot(step, lane)] is lane's A
+// fragment, i.e. row 16 tile + lane % 16, k = 32 step + 8 (lane / 16) .. +7
+// of the chunk.  The slot swizzle (low four bits xor the fragment's k-group)
+// spreads the staging writes of a wavefront, whose lanes stage four rows x
+// sixteen k-groups, over all LDS banks; a wavefront's reads of one step still
+// cover the 1 KiB row once.
+__device__ __forceinline__ int mf_slot(int step, int lane) {
+  return (lane & 48) | ((lane & 15) ^ ((4 * step + (lane >> 4)) & 15));
+}
 template <int CT>
 struct MfChunkT {
   uint4 f[CT][MF_SC][64];
@@ -114,14 +121,15 @@ __device__ __forceinline__ void mf_store_a(MfChunkT<CT> (&ch)[NP], float4 (&ar)[
     v.y = pack_bf16x2(ar[i][0].z, ar[i][0].w);
     v.z = pack_bf16x2(ar[i][1].x, ar[i][1].y);
     v.w = pack_bf16x2(ar[i][1].z, ar[i][1].w);
-    ch[0].f[i][kg >> 2][(kg & 3) * 16 + ri] = v;
+    const int slot = mf_slot(kg >> 2, (kg & 3) * 16 + ri);
+    ch[0].f[i][kg >> 2][slot] = v;
     if constexpr (NP == 2) {
       uint4 u;
       u.x = pack_bf16x2(rem_lo(ar[i][0].x, v.x), rem_hi(ar[i][0].y, v.x));
       u.y = pack_bf16x2(rem_lo(ar[i][0].z, v.y), rem_hi(ar[i][0].w, v.y));
       u.z = pack_bf16x2(rem_lo(ar[i][1].x, v.z), rem_hi(ar[i][1].y, v.z));
       u.w = pack_bf16x2(rem_lo(ar[i][1].z, v.w), rem_hi(ar[i][1].w, v.w));
-      ch[1].f[i][kg >> 2][(kg & 3) * 16 + ri] = u;
+      ch[1].f[i][kg >> 2][slot] = u;
     }
   }
 }
@@ -136,7 +144,7 @@ __device__ __forceinline__ void mf_compute(const MfChunkT<CT> (&ch)[NP], const u
     for (int i = 0; i < NT; ++i) {
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
-        const uint4 a = ch[p].f[i][s][lane];
+        const uint4 a = ch[p].f[i][s][mf_slot(s, lane)];
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
