@@ -110,15 +110,38 @@ __device__ __forceinline__ void attn_tile_query(const float4* __restrict__ qrow,
 
 // Merge of the chunk partials pp[c * cstride] (o[128], m, l) of one query row
 // for dims d, chunks 0..nc-1 in order: max of the m, then L and O with weights
-// exp(m_c - max), result O / L.
+// exp(m_c - max), result O / L.  The loads go out MG chunks at a time (the
+// partials sit in L2, so one round trip per group rather than per chunk); the
+// sums still run over c in order.
+constexpr int MG = 8;
 __device__ __forceinline__ float attn_merge(const float* __restrict__ pp, long cstride, int nc, int d) {
   float mg = -INFINITY;
-  for (int c = 0; c < nc; ++c) mg = fmaxf(mg, pp[c * cstride + HD]);
+  for (int c0 = 0; c0 < nc; c0 += MG) {
+    float mv[MG];
+#pragma unroll
+    for (int j = 0; j < MG; ++j) mv[j] = (c0 + j < nc) ? pp[(c0 + j) * cstride + HD] : -INFINITY;
+#pragma unroll
+    for (int j = 0; j < MG; ++j) mg = fmaxf(mg, mv[j]);
+  }
   float L = 0.f, O = 0.f;
-  for (int c = 0; c < nc; ++c) {
-    const float w = expf(pp[c * cstride + HD] - mg);
-    L = fmaf(pp[c * cstride + HD + 1], w, L);
-    O = fmaf(pp[c * cstride + d], w, O);
+  for (int c0 = 0; c0 < nc; c0 += MG) {
+    float mv[MG], lv[MG], ov[MG];
+#pragma unroll
+    for (int j = 0; j < MG; ++j) {
+      const bool in = c0 + j < nc;
+      const float* q = pp + (c0 + j) * cstride;
+      mv[j] = in ? q[HD] : 0.f;
+      lv[j] = in ? q[HD + 1] : 0.f;
+      ov[j] = in ? q[d] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < MG; ++j) {
+      if (c0 + j < nc) {
+        const float w = expf(mv[j] - mg);
+        L = fmaf(lv[j], w, L);
+        O = fmaf(ov[j], w, O);
+      }
+    }
   }
   return O / L;
 }
