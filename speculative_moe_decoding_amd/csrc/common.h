@@ -102,22 +102,22 @@ __device__ __forceinline__ float block_sum256(float v, float* red) {
   return t;
 }
 
-// RMSNorm of `m_rows` activation rows into LDS, one wavefront per row (rows
-// w, w + n_waves, ...): lane l sums x[k]^2 over k = l + 64 j in order, the 64
-// lane sums go through the xor butterfly, r = 1 / sqrt(sum / K + eps), and
-// xs[m][k] = (x[k] * r) * g[k].  g == nullptr copies the rows unchanged.
-// Row m is read from x + src_row(m) * ldx.  No barrier inside.
-template <int K, typename SrcRow>
+// RMSNorm of `m_rows` (<= MR) activation rows into LDS, by the block's four
+// wavefronts, one per row (rows w, w + 4, ...): lane l sums x[k]^2 over
+// k = l + 64 j in order, the 64 lane sums go through the xor butterfly,
+// r = 1 / sqrt(sum / K + eps), and xs[m][k] = (x[k] * r) * g[k].  g == nullptr
+// copies the rows unchanged.  Row m is read from x + src_row(m) * ldx.  When
+// a wavefront has two or more rows and they fit in registers, all of their
+// loads go out before the first sum (row indices clamped to the last row, so
+// the loads need no predicate).  No barrier inside.
+template <int K, int MR, typename SrcRow>
 __device__ __forceinline__ void norm_rows_wave(const float* __restrict__ x, long ldx, SrcRow src_row, int m_rows,
-                                               const float* __restrict__ g, float eps, float* xs, int n_waves) {
+                                               const float* __restrict__ g, float eps, float* xs) {
   static_assert(K % 64 == 0, "row length must be a multiple of 64");
   constexpr int J = K / 64;
-  const int lane = lane_id();
-  for (int m = wave_id(); m < m_rows; m += n_waves) {
-    const float* xr = x + (long)src_row(m) * ldx;
-    float v[J];
-#pragma unroll
-    for (int j = 0; j < J; ++j) v[j] = xr[lane + 64 * j];
+  constexpr int RW = (MR + 3) / 4;  // rows per wavefront
+  const int lane = lane_id(), w = wave_id();
+  auto finish = [&](int m, const float (&v)[J]) {
     if (g != nullptr) {
       float ss = 0.f;
 #pragma unroll
@@ -129,6 +129,27 @@ __device__ __forceinline__ void norm_rows_wave(const float* __restrict__ x, long
     } else {
 #pragma unroll
       for (int j = 0; j < J; ++j) xs[m * K + lane + 64 * j] = v[j];
+    }
+  };
+  if constexpr (RW > 1 && RW * J <= 48) {
+    if (w >= m_rows) return;
+    float v[RW][J];
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      const float* xr = x + (long)src_row(min(w + 4 * i, m_rows - 1)) * ldx;
+#pragma unroll
+      for (int j = 0; j < J; ++j) v[i][j] = xr[lane + 64 * j];
+    }
+#pragma unroll
+    for (int i = 0; i < RW; ++i)
+      if (w + 4 * i < m_rows) finish(w + 4 * i, v[i]);
+  } else {
+    for (int m = w; m < m_rows; m += 4) {
+      const float* xr = x + (long)src_row(m) * ldx;
+      float v[J];
+#pragma unroll
+      for (int j = 0; j < J; ++j) v[j] = xr[lane + 64 * j];
+      finish(m, v);
     }
   }
 }

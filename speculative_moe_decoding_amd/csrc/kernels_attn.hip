@@ -110,32 +110,57 @@ __device__ __forceinline__ void attn_tile_query(const float4* __restrict__ qrow,
 
 // Merge of the chunk partials pp[c * cstride] (o[128], m, l) of one query row
 // for dims d, chunks 0..nc-1 in order: max of the m, then L and O with weights
-// exp(m_c - max), result O / L.  The loads go out MG chunks at a time (the
-// partials sit in L2, so one round trip per group rather than per chunk); the
-// sums still run over c in order.
-constexpr int MG = 8;
-__device__ __forceinline__ float attn_merge(const float* __restrict__ pp, long cstride, int nc, int d) {
+// exp(m_c - max), result O / L.  The partials sit in L2, so the loads go out G
+// chunks at a time (one round trip per group rather than per chunk), at chunk
+// indices clamped to the last one in range so that they need no predicate;
+// repeats of the last chunk leave the max unchanged, and the sums run over
+// c < nc in order.
+template <int G>
+__device__ __forceinline__ void merge_load(const float* __restrict__ pp, long cstride, int c0, int nlim, int d,
+                                           float (&mv)[G], float (&lv)[G], float (&ov)[G]) {
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    const float* q = pp + min(c0 + j, nlim - 1) * cstride;
+    mv[j] = q[HD];
+    lv[j] = q[HD + 1];
+    ov[j] = q[d];
+  }
+}
+// nc <= G chunks already in registers
+template <int G>
+__device__ __forceinline__ float merge_regs(const float (&mv)[G], const float (&lv)[G], const float (&ov)[G],
+                                            int nc) {
   float mg = -INFINITY;
-  for (int c0 = 0; c0 < nc; c0 += MG) {
-    float mv[MG];
 #pragma unroll
-    for (int j = 0; j < MG; ++j) mv[j] = (c0 + j < nc) ? pp[(c0 + j) * cstride + HD] : -INFINITY;
+  for (int j = 0; j < G; ++j) mg = fmaxf(mg, (j < nc) ? mv[j] : -INFINITY);
+  float L = 0.f, O = 0.f;
 #pragma unroll
-    for (int j = 0; j < MG; ++j) mg = fmaxf(mg, mv[j]);
+  for (int j = 0; j < G; ++j) {
+    if (j < nc) {
+      const float w = expf(mv[j] - mg);
+      L = fmaf(lv[j], w, L);
+      O = fmaf(ov[j], w, O);
+    }
+  }
+  return O / L;
+}
+// any nc: two passes over groups of 8
+__device__ __forceinline__ float merge_loop(const float* __restrict__ pp, long cstride, int nc, int d) {
+  constexpr int G = 8;
+  float mg = -INFINITY;
+  for (int c0 = 0; c0 < nc; c0 += G) {
+    float mv[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) mv[j] = pp[min(c0 + j, nc - 1) * cstride + HD];
+#pragma unroll
+    for (int j = 0; j < G; ++j) mg = fmaxf(mg, mv[j]);
   }
   float L = 0.f, O = 0.f;
-  for (int c0 = 0; c0 < nc; c0 += MG) {
-    float mv[MG], lv[MG], ov[MG];
+  for (int c0 = 0; c0 < nc; c0 += G) {
+    float mv[G], lv[G], ov[G];
+    merge_load<G>(pp, cstride, c0, nc, d, mv, lv, ov);
 #pragma unroll
-    for (int j = 0; j < MG; ++j) {
-      const bool in = c0 + j < nc;
-      const float* q = pp + (c0 + j) * cstride;
-      mv[j] = in ? q[HD] : 0.f;
-      lv[j] = in ? q[HD + 1] : 0.f;
-      ov[j] = in ? q[d] : 0.f;
-    }
-#pragma unroll
-    for (int j = 0; j < MG; ++j) {
+    for (int j = 0; j < G; ++j) {
       if (c0 + j < nc) {
         const float w = expf(mv[j] - mg);
         L = fmaf(lv[j], w, L);
@@ -159,15 +184,24 @@ __global__ __launch_bounds__(256) void k_attn_partial(const float* __restrict__ 
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int wave = wave_id(), lane = lane_id(), tid = threadIdx.x;
   const int Q = plan.Q;
-  const int base = plan.base[b];
+  // the plan entries and this head's query rows (i < Q) go out together
+  const int base = plan.base[b], pcnt = plan.cnt[b];
+  const long slot = plan.slot[b];
+  constexpr int NQV = QMAX_ATT * HD / 4 / 256;
+  float4 qv[NQV];
+#pragma unroll
+  for (int j = 0; j < NQV; ++j) {
+    const int e = tid + 256 * j, i = e / (HD / 4), d4 = e % (HD / 4);
+    qv[j] = (i < Q) ? reinterpret_cast<const float4*>(q + (long)(b * Q + i) * QD + h * HD)[d4]
+                    : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   // rows past the cache (never produced by the library's own plans) are skipped
-  const int cnt = (base < 0) ? 0 : min(min(plan.cnt[b], Q), max_pos - base);
+  const int cnt = (base < 0) ? 0 : min(min(pcnt, Q), max_pos - base);
   const int p_last = base + cnt - 1;
   const int C = tiles_per_chunk * ATT_TILE;
   const int k0 = c * C;
   if (cnt <= 0 || k0 > p_last) return;
   const int n_tiles = min(tiles_per_chunk, (p_last - k0) / ATT_TILE + 1);
-  const long slot = plan.slot[b];
   const T* Kc = kv + slot * (2L * NH * max_pos * HD) + (long)h * max_pos * HD;
   const T* Vc = Kc + (long)NH * max_pos * HD;
   constexpr int CE = WT<T>::CE;
@@ -191,20 +225,11 @@ __global__ __launch_bounds__(256) void k_attn_partial(const float* __restrict__ 
     }
   };
   load_tile(0);
-  // queries of this sequence / head
-  {
-    float4 qv[QMAX_ATT * HD / 4 / 256];
+  // queries of this sequence / head (rows past cnt as zeros)
 #pragma unroll
-    for (int j = 0; j < QMAX_ATT * HD / 4 / 256; ++j) {
-      const int e = tid + 256 * j, i = e / (HD / 4), d4 = e % (HD / 4);
-      qv[j] = (i < cnt) ? reinterpret_cast<const float4*>(q + (long)(b * Q + i) * QD + h * HD)[d4]
-                        : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-#pragma unroll
-    for (int j = 0; j < QMAX_ATT * HD / 4 / 256; ++j) {
-      const int e = tid + 256 * j;
-      qs[e / (HD / 4)][e % (HD / 4)] = qv[j];
-    }
+  for (int j = 0; j < NQV; ++j) {
+    const int e = tid + 256 * j, i = e / (HD / 4);
+    qs[i][e % (HD / 4)] = (i < cnt) ? qv[j] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
   float o0[2] = {0.f, 0.f}, o1[2] = {0.f, 0.f};
@@ -238,6 +263,7 @@ __global__ __launch_bounds__(256) void k_attn_partial(const float* __restrict__ 
 }
 
 // Merge chunks 0..p/C of each (row, head) in order.  Block = 2 heads x 128 dims.
+constexpr int MERGE_ONE = 32;  // chunk counts merged from one batch of loads
 __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ part, RowPlan plan, int n_chunks,
                                                       int chunk_keys, int max_pos, float* __restrict__ out) {
   const int row = blockIdx.x;
@@ -245,11 +271,26 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
   const int d = threadIdx.x & 127;
   const int b = row / plan.Q, i = row - b * plan.Q;
   float* o = out + (long)row * QD + h * HD + d;
-  const int p = plan.base[b] + i;
-  if (i >= plan.cnt[b] || p < 0 || p >= max_pos) { *o = 0.f; return; }
-  const int nc = min(p / chunk_keys + 1, n_chunks);
   const float* pp = part + (((long)b * NH + h) * n_chunks) * plan.Q * (HD + 2) + (long)i * (HD + 2);
-  *o = attn_merge(pp, (long)plan.Q * (HD + 2), nc, d);
+  const long cstride = (long)plan.Q * (HD + 2);
+  // the row's merge count from the plan (rows outside it: ok false, row zero)
+  auto plan_nc = [&](bool& ok) {
+    const int p = plan.base[b] + i;
+    ok = i < plan.cnt[b] && p >= 0 && p < max_pos;
+    return ok ? min(p / chunk_keys + 1, n_chunks) : 1;
+  };
+  bool ok;
+  float r;
+  if (n_chunks <= MERGE_ONE) {
+    // one batch of loads, issued with the plan reads (their addresses do not
+    // depend on it); chunks past nc unused
+    float mv[MERGE_ONE], lv[MERGE_ONE], ov[MERGE_ONE];
+    merge_load<MERGE_ONE>(pp, cstride, 0, n_chunks, d, mv, lv, ov);
+    r = merge_regs<MERGE_ONE>(mv, lv, ov, plan_nc(ok));
+  } else {
+    r = merge_loop(pp, cstride, plan_nc(ok), d);
+  }
+  *o = ok ? r : 0.f;
 }
 
 template <typename T>

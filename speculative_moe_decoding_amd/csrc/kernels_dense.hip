@@ -61,32 +61,33 @@ __global__ __launch_bounds__(256) void k_qkv_rope(const float* __restrict__ x, c
   const T* rows[2] = {wqkv + (long)r0 * D, wqkv + (long)r1 * D};
   WaveGemv<T, D, 2, MR> g;
   g.load(rows);
-  // lane m < m_act: this row's position, validity and rotation
-  int pos = 0, b = 0, i = 0;
+  // lane m < m_act: this row's position, validity, cache slot and rotation
+  int pos = 0, b = 0, i = 0, slot = 0;
   bool valid = false;
   float2 cs = make_float2(1.f, 0.f);
   if (lane < m_act) {
     const int row = m0 + lane;
     b = row / plan.Q;
     i = row - b * plan.Q;
+    slot = plan.slot[b];
     pos = plan.base[b] + i;
     valid = i < plan.cnt[b] && pos >= 0 && pos < max_pos;
     if (sec < 2) cs = rope[(long)min(max(pos, 0), max_pos - 1) * (HD / 2) + u];
   }
-  norm_rows_wave<D>(x, D, RowIdentity{m0}, m_act, gain, eps, xs, 4);
+  norm_rows_wave<D, MR>(x, D, RowIdentity{m0}, m_act, gain, eps, xs);
   __syncthreads();
   float acc[2][MR];
   g.fma(xs, m_act, acc);
   // lane with (r, m): row m's position data from lane m, the pair's other total
   const WaveTotals<2, MR> t(acc);
   const float other = t.partner(1);
-  const int tb = __shfl(b, t.m, 64), tpos = __shfl(pos, t.m, 64);
+  const int tpos = __shfl(pos, t.m, 64), tslot = __shfl(slot, t.m, 64);
   const bool tvalid = __shfl((int)valid, t.m, 64) != 0;
   const float tc = __shfl(cs.x, t.m, 64), ts = __shfl(cs.y, t.m, 64);
   if (t.lead && t.m < m_act) {
     const int row = m0 + t.m;
     const long slot_stride = 2L * NH * max_pos * HD;
-    const long slot = plan.slot[tb];
+    const long slot = tslot;
     if (sec < 2) {
       // rows u (r = 0) and u + 64 (r = 1) of a head: each lane rotates its own
       float o;
@@ -147,7 +148,7 @@ __global__ __launch_bounds__(256) void k_gemv(const float* __restrict__ a, long 
   }
   WaveGemv<T, K, R, MR> g;
   g.load(rows);
-  norm_rows_wave<K>(a, lda, RowIdentity{m0}, m_act, gain, eps, xs, 4);
+  norm_rows_wave<K, MR>(a, lda, RowIdentity{m0}, m_act, gain, eps, xs);
   __syncthreads();
   float acc[R][MR];
   g.fma(xs, m_act, acc);
@@ -246,7 +247,7 @@ __global__ __launch_bounds__(256) void k_lmhead(const float* __restrict__ x, con
     for (int r = 0; r < 4; ++r) rows[r] = W + (long)min(vbase + r, V - 1) * D;
     g[0].load(rows);
   }
-  norm_rows_wave<D>(x, D, LmSrcRow{cnt, Q, last_valid, m0}, m_act, gain, eps, xs, 4);
+  norm_rows_wave<D, MR>(x, D, LmSrcRow{cnt, Q, last_valid, m0}, m_act, gain, eps, xs);
   __syncthreads();
   // Each lane keeps the running best of the (tile row r, activation row m)
   // whose totals it receives.
@@ -294,7 +295,12 @@ __global__ __launch_bounds__(256) void k_lmhead(const float* __restrict__ x, con
   }
 }
 
-// Stage 2: one block per output row reduces the per-block bests.
+// Stage 2: one block per output row reduces the per-block bests (largest
+// value, lowest id among equal ones: the order of the comparisons does not
+// matter).  Each thread loads AMG of them at a time, at indices clamped to the
+// last block (a repeat changes nothing), so the loads need no predicate and
+// go out together.
+constexpr int AMG = 8;
 __global__ __launch_bounds__(256) void k_argmax_final(const float* __restrict__ part_val,
                                                       const int* __restrict__ part_idx, int nblk,
                                                       int* __restrict__ tok, int tok_stride) {
@@ -304,10 +310,20 @@ __global__ __launch_bounds__(256) void k_argmax_final(const float* __restrict__ 
   const int wave = wave_id(), lane = lane_id();
   float v = -INFINITY;
   int id = 0x7fffffff;
-  for (int b = threadIdx.x; b < nblk; b += 256) {
-    const float pv = part_val[(long)m * nblk + b];
-    const int pi = part_idx[(long)m * nblk + b];
-    if (pv > v || (pv == v && pi < id)) { v = pv; id = pi; }
+  const float* rv = part_val + (long)m * nblk;
+  const int* ri = part_idx + (long)m * nblk;
+  for (int b0 = 0; b0 < nblk; b0 += 256 * AMG) {
+    float pv[AMG];
+    int pi[AMG];
+#pragma unroll
+    for (int j = 0; j < AMG; ++j) {
+      const int b = min(b0 + (int)threadIdx.x + 256 * j, nblk - 1);
+      pv[j] = rv[b];
+      pi[j] = ri[b];
+    }
+#pragma unroll
+    for (int j = 0; j < AMG; ++j)
+      if (pv[j] > v || (pv[j] == v && pi[j] < id)) { v = pv[j]; id = pi[j]; }
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {

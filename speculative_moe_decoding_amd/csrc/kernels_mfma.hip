@@ -453,6 +453,24 @@ __global__ __launch_bounds__(256) void k_dense_ks(const float* __restrict__ a, l
     r0 = c0;
     r1 = c0;
   }
+  // QKV: the plan entry, cache slot and rotation of the output row this lane
+  // finishes (row 4 (lane / 16) + wave, column lane % 16), fetched before the
+  // main loop so that the epilogue waits on no memory
+  int e_pos = 0;
+  long e_slot = 0;
+  bool e_valid = false;
+  float2 e_cs = make_float2(1.f, 0.f);
+  if constexpr (MODE == DM_QKV) {
+    const int r = 4 * (lane >> 4) + wave;
+    if (r < rows) {
+      const RowPlan& plan = qo.plan;
+      const int m = m0 + r, b = m / plan.Q, i = m - b * plan.Q;
+      e_slot = plan.slot[b];
+      e_pos = plan.base[b] + i;
+      e_valid = i < plan.cnt[b] && e_pos >= 0 && e_pos < qo.max_pos;
+      if (sec < 2) e_cs = qo.rope[(long)min(max(e_pos, 0), qo.max_pos - 1) * (HD / 2) + c0 + (lane & 15)];
+    }
+  }
   if (gain != nullptr) {
     for (int r = wave; r < 16; r += 4) {
       float ss = 0.f;
@@ -548,26 +566,21 @@ __global__ __launch_bounds__(256) void k_dense_ks(const float* __restrict__ a, l
   } else if constexpr (MODE == DM_SWIGLU) {
     out[(long)m * ldo + c0 + j] = silu(v[0]) * v[NB - 1];
   } else {
-    const RowPlan& plan = qo.plan;
-    const int b = m / plan.Q, i = m - b * plan.Q;
-    const int pos = plan.base[b] + i;
-    const bool valid = i < plan.cnt[b] && pos >= 0 && pos < qo.max_pos;
     const long slot_stride = 2L * NH * qo.max_pos * HD;
     if (sec < 2) {
       const int u = c0 + j;
-      const float2 cs = qo.rope[(long)min(max(pos, 0), qo.max_pos - 1) * (HD / 2) + u];
-      const float o0 = fmaf(v[0], cs.x, -(v[NB - 1] * cs.y));
-      const float o1 = fmaf(v[NB - 1], cs.x, v[0] * cs.y);
+      const float o0 = fmaf(v[0], e_cs.x, -(v[NB - 1] * e_cs.y));
+      const float o1 = fmaf(v[NB - 1], e_cs.x, v[0] * e_cs.y);
       if (sec == 0) {
         qo.q[(long)m * QD + h * HD + u] = o0;
         qo.q[(long)m * QD + h * HD + u + 64] = o1;
-      } else if (valid) {
-        bf16* kd = qo.kv + (long)plan.slot[b] * slot_stride + ((long)h * qo.max_pos + pos) * HD;
+      } else if (e_valid) {
+        bf16* kd = qo.kv + e_slot * slot_stride + ((long)h * qo.max_pos + e_pos) * HD;
         kd[u] = f2bf(o0);
         kd[u + 64] = f2bf(o1);
       }
-    } else if (valid) {
-      bf16* vd = qo.kv + (long)plan.slot[b] * slot_stride + ((long)(NH + h) * qo.max_pos + pos) * HD;
+    } else if (e_valid) {
+      bf16* vd = qo.kv + e_slot * slot_stride + ((long)(NH + h) * qo.max_pos + e_pos) * HD;
       vd[c0 + j] = f2bf(v[0]);
       vd[c0 + 16 + j] = f2bf(v[NB - 1]);
     }

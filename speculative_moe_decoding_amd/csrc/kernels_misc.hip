@@ -15,23 +15,43 @@ __device__ __forceinline__ void embed_row(const T* __restrict__ E, int tok, floa
 }
 
 // Block b: sequence b of a verify call.  Rows b*(K+1) + i hold
-// [pending, d_1 .. d_K] at positions kv_len .. kv_len + K.
+// [pending, d_1 .. d_K] at positions kv_len .. kv_len + K.  The draft tokens
+// are read with the slot, then every row's embedding loads go out at once
+// (row indices clamped to K, rows past K not stored).
+constexpr int QV = 8;  // rows per sequence of a verify call: K + 1 <= 8
 template <typename T>
 __global__ __launch_bounds__(256) void k_plan_verify(int K, const int* __restrict__ slots_in, StateView sv,
                                                      const int* __restrict__ draft, const T* __restrict__ E,
                                                      int V, int* plan_base, int* plan_cnt, int* plan_slot,
                                                      float* __restrict__ x) {
+  constexpr int J = D / 256;
   const int b = blockIdx.x;
+  int dt[QV - 1];
+#pragma unroll
+  for (int i = 0; i < QV - 1; ++i) dt[i] = (K > 0) ? draft[b * K + min(i, K - 1)] : 0;
   const int slot = clamp_slot(slots_in ? slots_in[b] : b, sv.n_slots);
   if (threadIdx.x == 0) {
     plan_slot[b] = slot;
     plan_base[b] = sv.kv_len[slot];
     plan_cnt[b] = K + 1;
   }
-  for (int i = 0; i <= K; ++i) {
-    const int tok = clamp_tok(i == 0 ? sv.pending[slot] : draft[b * K + i - 1], V);
-    embed_row(E, tok, x + (long)(b * (K + 1) + i) * D);
+  const int pend = sv.pending[slot];
+  float v[QV][J];
+#pragma unroll
+  for (int i = 0; i < QV; ++i) {
+    const int r = min(i, K);
+    const int tok = clamp_tok(r == 0 ? pend : dt[max(r - 1, 0)], V);
+    const T* src = E + (long)tok * D;
+#pragma unroll
+    for (int j = 0; j < J; ++j) v[i][j] = WT<T>::load1(src + threadIdx.x + 256 * j);
   }
+#pragma unroll
+  for (int i = 0; i < QV; ++i)
+    if (i <= K) {
+      float* dst = x + (long)(b * (K + 1) + i) * D;
+#pragma unroll
+      for (int j = 0; j < J; ++j) dst[threadIdx.x + 256 * j] = v[i][j];
+    }
 }
 
 // RMSNorm of one D-row into dst (256 threads).
@@ -253,39 +273,56 @@ __global__ __launch_bounds__(256) void k_accept(int K, const int* __restrict__ p
                                                 const float* __restrict__ xfinal, StateView sv,
                                                 int* __restrict__ n_acc, int* __restrict__ out_tokens,
                                                 int* __restrict__ out_len_out, int out_cap) {
+  constexpr int J = D / 256;
   __shared__ int sn;
   const int b = blockIdx.x;
+  const int lane = lane_id();
+  // the verify rows' final hidden states (rows past K clamped, not stored)
+  // are fetched before the acceptance is known
+  float hv[QV][J];
+#pragma unroll
+  for (int i = 0; i < QV; ++i) {
+    const float* src = xfinal + (long)(b * (K + 1) + min(i, K)) * D;
+#pragma unroll
+    for (int j = 0; j < J; ++j) hv[i][j] = src[threadIdx.x + 256 * j];
+  }
   const int slot = plan_slot[b];
-  const int* g = greedy + b * (K + 1);
-  const int* d = draft + b * K;
-  if (threadIdx.x == 0) {
-    int n = 0;
-    while (n < K && d[n] == g[n]) ++n;
+  if (wave_id() == 0) {
+    // lane i < K compares d_i with the verifier's g_i; n = the first mismatch
+    const int dv = (lane < K) ? draft[b * K + lane] : 0;
+    const int gv = (lane <= K) ? greedy[b * (K + 1) + lane] : 0;
     const int old = sv.kv_len[slot];
-    int ol = sv.out_len[slot];
-    for (int i = 0; i <= n; ++i) {
-      const int t = (i < n) ? d[i] : g[n];
-      sv.cu_tok[slot * sv.cu_stride + i] = t;
-      if (out_tokens != nullptr && ol < out_cap) out_tokens[(long)b * out_cap + ol] = t;
-      ++ol;
+    const int ol0 = sv.out_len[slot];
+    const uint64_t miss = __ballot(!(lane < K && dv == gv));
+    const int n = __builtin_ctzll(miss);  // <= K
+    const int gn = __shfl(gv, n, 64);
+    if (lane <= n) {
+      const int t = (lane < n) ? dv : gn;
+      sv.cu_tok[slot * sv.cu_stride + lane] = t;
+      if (out_tokens != nullptr && ol0 + lane < out_cap) out_tokens[(long)b * out_cap + ol0 + lane] = t;
     }
-    sv.out_len[slot] = ol;
-    sv.kv_len[slot] = old + n + 1;
-    sv.draft_len[slot] = old + 1;
-    sv.pending[slot] = g[n];
-    sv.n_prev[slot] = n;
-    sv.step[slot] += 1;
-    if (n_acc != nullptr) n_acc[b] = n;
-    if (out_len_out != nullptr) out_len_out[b] = ol;
-    sn = n;
+    if (lane == 0) {
+      const int ol = ol0 + n + 1;
+      sv.out_len[slot] = ol;
+      sv.kv_len[slot] = old + n + 1;
+      sv.draft_len[slot] = old + 1;
+      sv.pending[slot] = gn;
+      sv.n_prev[slot] = n;
+      sv.step[slot] += 1;
+      if (n_acc != nullptr) n_acc[b] = n;
+      if (out_len_out != nullptr) out_len_out[b] = ol;
+      sn = n;
+    }
   }
   __syncthreads();
   const int n = sn;
-  for (int i = 0; i <= n; ++i) {
-    const float* src = xfinal + (long)(b * (K + 1) + i) * D;
-    float* dst = sv.hbuf + ((long)slot * sv.cu_stride + i) * D;
-    for (int k = threadIdx.x; k < D; k += 256) dst[k] = src[k];
-  }
+#pragma unroll
+  for (int i = 0; i < QV; ++i)
+    if (i <= n) {
+      float* dst = sv.hbuf + ((long)slot * sv.cu_stride + i) * D;
+#pragma unroll
+      for (int j = 0; j < J; ++j) dst[threadIdx.x + 256 * j] = hv[i][j];
+    }
 }
 
 // SplitMix64 output function (Steele, Lea & Flood 2014).

@@ -20,25 +20,26 @@ struct RouteLds {
   int na;
 };
 
-// Stable counting sort of P <= 64 pairs by one wavefront (lane = pair): ranks
-// by ballots over the distinct experts present, offsets by a wavefront scan
-// (routed experts 0..63 in id order, then the shared experts 64, 65).
+// Stable counting sort of P <= 64 pairs by one wavefront (lane = pair): the
+// lanes holding the same expert found from one ballot per bit of the id (7
+// bits cover 0..65), rank = those below this lane, count written by the
+// lowest; offsets by a wavefront scan (routed experts 0..63 in id order, then
+// the shared experts 64, 65).
 __device__ __forceinline__ void sort_pairs_wave(int P, RouteLds& r) {
+  static_assert(NX <= 128, "expert ids must fit in 7 bits");
   const int lane = lane_id();
   const bool valid = lane < P;
-  const int e = valid ? r.pe[lane] : -1;
+  const int e = valid ? r.pe[lane] : 0;
   const uint64_t lt = (1ull << lane) - 1ull;
   for (int x = lane; x <= NX; x += 64) r.cnt[x] = 0;
-  uint64_t todo = __ballot(valid);
-  int rank = 0;
-  while (todo) {
-    const int leader = __builtin_ctzll(todo);
-    const int el = __shfl(e, leader, 64);
-    const uint64_t same = __ballot(valid && e == el);
-    if (valid && e == el) rank = __popcll(same & lt);
-    if (lane == 0) r.cnt[el] = __popcll(same);
-    todo &= ~same;
+  uint64_t same = __ballot(valid);
+#pragma unroll
+  for (int bit = 0; bit < 7; ++bit) {
+    const uint64_t set = __ballot(valid && ((e >> bit) & 1));
+    same &= ((e >> bit) & 1) ? set : ~set;
   }
+  const int rank = valid ? __popcll(same & lt) : 0;
+  if (valid && rank == 0) r.cnt[e] = __popcll(same);
   const int c = r.cnt[lane];
   int incl = c;
 #pragma unroll
@@ -117,8 +118,10 @@ __device__ __forceinline__ void route_rows(const float* __restrict__ rlogit, int
 }
 
 // Publish the routing of the LDS copy for the kernels that follow (down,
-// combine) and the taps; counts the active experts into stats[0].
-__device__ __forceinline__ void publish_route(const RouteLds& r, int M, const MoeBufs& mb, int* tap) {
+// combine) and the taps; stats[0] = st0 (its value at kernel start, read by
+// thread 0) + the active experts.
+__device__ __forceinline__ void publish_route(const RouteLds& r, int M, const MoeBufs& mb, int* tap,
+                                              long long st0) {
   const int tid = threadIdx.x;
   const int P = M * NSLOT;
   for (int p = tid; p < P; p += 256) {
@@ -142,7 +145,7 @@ __device__ __forceinline__ void publish_route(const RouteLds& r, int M, const Mo
   }
   if (tid == 0) {
     *mb.n_act = r.na;
-    mb.stats[0] += r.na;
+    mb.stats[0] = st0 + r.na;
   }
 }
 
@@ -161,7 +164,7 @@ __global__ __launch_bounds__(256) void k_router_logits(const float* __restrict__
   const T* rows[1] = {wr + (long)e * D};
   WaveGemv<T, D, 1, MR> g;
   g.load(rows);
-  norm_rows_wave<D>(x, D, RowIdentity{m0}, m_act, gain, eps, xs, 4);
+  norm_rows_wave<D, MR>(x, D, RowIdentity{m0}, m_act, gain, eps, xs);
   __syncthreads();
   if (blockIdx.x == 0)
     for (int k = threadIdx.x; k < m_act * D; k += 256) bnorm[(long)m0 * D + k] = xs[k];
@@ -175,8 +178,9 @@ __global__ __launch_bounds__(256) void k_router_logits(const float* __restrict__
 __global__ __launch_bounds__(256) void k_route_small(const float* __restrict__ rlogit, int M, MoeBufs mb,
                                                      int* __restrict__ tap) {
   __shared__ RouteLds r;
+  const long long st0 = (threadIdx.x == 0) ? mb.stats[0] : 0;  // read early: off the kernel's tail
   route_rows(rlogit, M, r);
-  publish_route(r, M, mb, tap);
+  publish_route(r, M, mb, tap, st0);
 }
 
 // Larger batches (8 < M <= 1024): top-6 per row, one wavefront per row
@@ -527,7 +531,10 @@ __global__ __launch_bounds__(256) void k_moe_combine(float* __restrict__ x, MoeB
   const int r = blockIdx.x;
   const int* inv = mb.inv + r * NSLOT;
   const float* gt = mb.rgate + r * NSLOT;
-  for (int n = threadIdx.x; n < D; n += 256) {
+  static_assert(D % 256 == 0, "row length");
+#pragma unroll
+  for (int t = 0; t < D / 256; ++t) {  // unrolled: every load of the row goes out at once
+    const int n = threadIdx.x + 256 * t;
     float acc = mb.y[(long)inv[TOPK] * D + n];
     acc += mb.y[(long)inv[TOPK + 1] * D + n];
 #pragma unroll
