@@ -295,51 +295,15 @@ __global__ __launch_bounds__(256) void k_lmhead(const float* __restrict__ x, con
   }
 }
 
-// Stage 2: one block per output row reduces the per-block bests (largest
-// value, lowest id among equal ones: the order of the comparisons does not
-// matter).  Each thread loads AMG of them at a time, at indices clamped to the
-// last block (a repeat changes nothing), so the loads need no predicate and
-// go out together.
-constexpr int AMG = 8;
+// Stage 2: one block per output row reduces the per-block bests.
 __global__ __launch_bounds__(256) void k_argmax_final(const float* __restrict__ part_val,
                                                       const int* __restrict__ part_idx, int nblk,
                                                       int* __restrict__ tok, int tok_stride) {
   __shared__ float sv[4];
   __shared__ int si[4];
   const int m = blockIdx.x;
-  const int wave = wave_id(), lane = lane_id();
-  float v = -INFINITY;
-  int id = 0x7fffffff;
-  const float* rv = part_val + (long)m * nblk;
-  const int* ri = part_idx + (long)m * nblk;
-  for (int b0 = 0; b0 < nblk; b0 += 256 * AMG) {
-    float pv[AMG];
-    int pi[AMG];
-#pragma unroll
-    for (int j = 0; j < AMG; ++j) {
-      const int b = min(b0 + (int)threadIdx.x + 256 * j, nblk - 1);
-      pv[j] = rv[b];
-      pi[j] = ri[b];
-    }
-#pragma unroll
-    for (int j = 0; j < AMG; ++j)
-      if (pv[j] > v || (pv[j] == v && pi[j] < id)) { v = pv[j]; id = pi[j]; }
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float ov = __shfl_xor(v, off, 64);
-    const int oi = __shfl_xor(id, off, 64);
-    if (ov > v || (ov == v && oi < id)) { v = ov; id = oi; }
-  }
-  if (lane == 0) { sv[wave] = v; si[wave] = id; }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    v = sv[0];
-    id = si[0];
-    for (int w = 1; w < 4; ++w)
-      if (sv[w] > v || (sv[w] == v && si[w] < id)) { v = sv[w]; id = si[w]; }
-    tok[(long)m * tok_stride] = id;
-  }
+  const int id = argmax_block(part_val + (long)m * nblk, part_idx + (long)m * nblk, nblk, sv, si);
+  if (threadIdx.x == 0) tok[(long)m * tok_stride] = id;
 }
 
 int lmhead_blocks(int V) { return (V + LM_ROWS_PER_BLOCK - 1) / LM_ROWS_PER_BLOCK; }
@@ -363,7 +327,7 @@ void launch_lmhead(hipStream_t s, const float* x, const int* cnt, int Q, bool la
   else if (M <= 4) OCR_LM_CASE(4)
   else OCR_LM_CASE(MRG)
 #undef OCR_LM_CASE
-  launch_argmax_final(s, part_val, part_idx, nb, M, tok, tok_stride);
+  if (tok != nullptr) launch_argmax_final(s, part_val, part_idx, nb, M, tok, tok_stride);
 }
 
 #define OCR_INST_DENSE(T)                                                                                       \

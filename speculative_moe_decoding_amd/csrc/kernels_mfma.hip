@@ -724,7 +724,7 @@ void launch_lmhead_mfma(hipStream_t s, const float* x, const int* cnt, int Q, bo
   hipLaunchKernelGGL(k_lm_norm, dim3((M + 3) / 4), dim3(256), 0, s, x, cnt, Q, (int)last_valid, gain, eps, M, xn);
   const int nb = lmhead_blocks(V);
   hipLaunchKernelGGL(k_lmhead_mfma, dim3(nb), dim3(256), 0, s, xn, W, V, M, part_val, part_idx, logits);
-  launch_argmax_final(s, part_val, part_idx, nb, M, tok, tok_stride);
+  if (tok != nullptr) launch_argmax_final(s, part_val, part_idx, nb, M, tok, tok_stride);
 }
 
 }  // namespace ocr

@@ -157,6 +157,98 @@ __global__ __launch_bounds__(256) void k_plan_draft_step(int j, int Qprev, int K
   }
 }
 
+// Draft pass input and fusion projection in one launch (the vector path's
+// replacement for a plan kernel above, the argmax stage 2 before it and the
+// fusion GEMV after it; same arithmetic, so the same bits).  Output row r of
+// the pass gets out[r] = W_fuse . cat_r with cat_r = [RMSNorm(h) g_h,
+// RMSNorm(E[tok]) g_e] built in LDS by every block for its rows:
+//  - catch-up (j = 1): r = b Q + i, h = hbuf[slot][i], tok = cu_tok[slot][i]
+//    for i < cnt_b = max(1, min(n_prev + 1, Q)), zero rows past cnt_b;
+//  - step (j >= 2): r = b, tok = d_{j-1} = the argmax of the previous pass's
+//    LM-head partials (also written to draft_out), h = the previous pass's
+//    output row b Qprev + pc_b - 1, pc_b = 1 past the catch-up, else cnt_b.
+// Blocks with blockIdx.x = 0 write the plan entries of their rows (no block
+// reads them).  Each wavefront owns 2 output rows, as the generic GEMV with
+// K = 2 D; grid (D / 8, ceil(M / MR)).  out must not alias u_prev.
+template <typename T>
+struct DraftIn {
+  int step, j, Q, Qprev, K, V;
+  const int* slots_in;  // catch-up: sequence -> slot (nullable: identity)
+  StateView sv;
+  const T* E;
+  const float* g_h;
+  const float* g_e;
+  float eps;
+  const float* u_prev;     // step: previous pass's output rows
+  const float* part_val;   // step: LM-head per-block bests of the previous pass, [B][nblk]
+  const int* part_idx;
+  int nblk;
+  int* draft_out;          // step: [B][K], d_{j-1} at column j - 2
+  int* plan_base;
+  int* plan_cnt;
+  int* plan_slot;
+};
+
+template <typename T, int MR>
+__global__ __launch_bounds__(256) void k_draft_fuse(DraftIn<T> a, const T* __restrict__ W, int M,
+                                                    float* __restrict__ out) {
+  extern __shared__ float smem[];
+  float* xs = smem;  // [MR][2 D]
+  __shared__ float red[4];
+  __shared__ float amv[4];
+  __shared__ int ami[4];
+  constexpr int K2 = 2 * D, R = 2;
+  const int wave = wave_id();
+  const int n0 = (blockIdx.x * 4 + wave) * R;
+  const int m0 = blockIdx.y * MR;
+  const int m_act = min(MR, M - m0);
+  const T* rows[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) rows[r] = W + (long)min(n0 + r, D - 1) * K2;
+  WaveGemv<T, K2, R, MR> g;
+  g.load(rows);
+  const bool writer = blockIdx.x == 0 && threadIdx.x == 0;
+  for (int m = 0; m < m_act; ++m) {
+    const int r = m0 + m;
+    float* c = xs + m * K2;
+    if (a.step) {
+      const int b = r;
+      const int slot = a.plan_slot[b];
+      const int pc = (a.Qprev == 1) ? 1 : max(1, min(a.sv.n_prev[slot] + 1, a.Qprev));
+      const float* h = a.u_prev + (long)(b * a.Qprev + pc - 1) * D;
+      const int id = argmax_block(a.part_val + (long)b * a.nblk, a.part_idx + (long)b * a.nblk, a.nblk, amv, ami);
+      if (writer) {
+        a.draft_out[b * a.K + a.j - 2] = id;
+        a.plan_base[b] = a.sv.kv_len[slot] + a.j - 1;
+        a.plan_cnt[b] = 1;
+      }
+      draft_cat_row(h, clamp_tok(id, a.V), a.E, a.g_h, a.g_e, a.eps, c, red);
+    } else {
+      const int b = r / a.Q, i = r - b * a.Q;
+      const int slot = clamp_slot(a.slots_in ? a.slots_in[b] : b, a.sv.n_slots);
+      const int cnt = max(1, min(a.sv.n_prev[slot] + 1, a.Q));
+      if (writer && i == 0) {
+        a.plan_slot[b] = slot;
+        a.plan_base[b] = a.sv.draft_len[slot];
+        a.plan_cnt[b] = cnt;
+      }
+      if (i < cnt) {
+        const float* h = a.sv.hbuf + ((long)slot * a.sv.cu_stride + i) * D;
+        const int tok = clamp_tok(a.sv.cu_tok[slot * a.sv.cu_stride + i], a.V);
+        draft_cat_row(h, tok, a.E, a.g_h, a.g_e, a.eps, c, red);
+      } else {
+        for (int k = threadIdx.x; k < K2; k += 256) c[k] = 0.f;
+      }
+    }
+  }
+  __syncthreads();
+  float acc[R][MR];
+  g.fma(xs, m_act, acc);
+  const WaveTotals<R, MR> t(acc);
+  const int n = n0 + t.r;
+  if (t.lead && t.m < m_act && n < D) out[(long)(m0 + t.m) * D + n] = t.val;
+}
+
 // Prefill pass: rows j*8 + i (entry j, i < cnt[j]) hold positions p0[j] + i
 // of sequence seq[j] -- vision rows, then prompt ids; rows past cnt[j] are
 // zero.  esave keeps the input rows for the draft prefill.  Grid (8, n).
@@ -378,6 +470,27 @@ void launch_plan_draft_step(hipStream_t s, int B, int j, int Qprev, int K, State
                      g_e, eps, u_prev, plan_base, plan_cnt, plan_slot, cat);
 }
 template <typename T>
+void launch_draft_fuse(hipStream_t s, int step, int j, int Q, int Qprev, int K, const int* slots_in, StateView sv,
+                       const T* embed, int V, const float* g_h, const float* g_e, float eps, const float* u_prev,
+                       const float* part_val, const int* part_idx, int nblk, int* draft_out, int* plan_base,
+                       int* plan_cnt, int* plan_slot, const T* w_fuse, int M, float* out) {
+  const DraftIn<T> a{step, j, Q, Qprev, K, V, slots_in, sv, embed, g_h, g_e, eps, u_prev, part_val, part_idx,
+                     nblk, draft_out, plan_base, plan_cnt, plan_slot};
+#define OCR_DF_CASE(MRV)                                                                               \
+  {                                                                                                    \
+    const size_t lds = (size_t)MRV * 2 * D * 4;                                                        \
+    static const bool attr_set = (allow_lds(k_draft_fuse<T, MRV>, lds), true);                         \
+    (void)attr_set;                                                                                    \
+    hipLaunchKernelGGL((k_draft_fuse<T, MRV>), dim3(D / 8, (M + MRV - 1) / MRV), dim3(256), lds, s, a, \
+                       w_fuse, M, out);                                                                \
+  }
+  if (M <= 1) OCR_DF_CASE(1)
+  else if (M <= 2) OCR_DF_CASE(2)
+  else if (M <= 4) OCR_DF_CASE(4)
+  else OCR_DF_CASE(MRG)
+#undef OCR_DF_CASE
+}
+template <typename T>
 void launch_plan_prefill(hipStream_t s, const PrefillGroup& g, const float* vision, int nv_stride,
                          const int* prompt, int np_stride, const T* embed, int V, int* plan_base, int* plan_cnt,
                          int* plan_slot, float* x, float* esave) {
@@ -417,6 +530,9 @@ void launch_copy_rows(hipStream_t s, const float* src, float* dst, long n) {
                                       int*, int*, int*, float*);                                                 \
   template void launch_plan_draft_catchup<T>(hipStream_t, int, int, const int*, StateView, const T*, int,        \
                                              const float*, const float*, float, int*, int*, int*, float*);       \
+  template void launch_draft_fuse<T>(hipStream_t, int, int, int, int, int, const int*, StateView, const T*, int,   \
+                                     const float*, const float*, float, const float*, const float*, const int*, int,  \
+                                     int*, int*, int*, int*, const T*, int, float*);                                  \
   template void launch_plan_draft_step<T>(hipStream_t, int, int, int, int, StateView, const int*, const T*, int, \
                                           const float*, const float*, float, const float*, int*, int*,           \
                                           const int*, float*);                                                   \

@@ -119,6 +119,15 @@ template <typename T>
 void launch_plan_draft_catchup(hipStream_t s, int B, int Q, const int* slots_in, StateView sv,
                                const T* embed, int V, const float* g_h, const float* g_e, float eps,
                                int* plan_base, int* plan_cnt, int* plan_slot, float* cat);
+// Draft pass input + fusion projection in one launch (vector path): step = 0
+// is the catch-up pass (M = B Q rows), step = 1 pass j >= 2 (M = B rows,
+// d_{j-1} from the LM-head partials part_val / part_idx of the previous pass,
+// written to draft_out).  out = W_fuse . cat, [M][D]; out must not alias u_prev.
+template <typename T>
+void launch_draft_fuse(hipStream_t s, int step, int j, int Q, int Qprev, int K, const int* slots_in, StateView sv,
+                       const T* embed, int V, const float* g_h, const float* g_e, float eps, const float* u_prev,
+                       const float* part_val, const int* part_idx, int nblk, int* draft_out, int* plan_base,
+                       int* plan_cnt, int* plan_slot, const T* w_fuse, int M, float* out);
 template <typename T>
 void launch_plan_draft_step(hipStream_t s, int B, int j, int Qprev, int K, StateView sv, const int* draft_out,
                             const T* embed, int V, const float* g_h, const float* g_e, float eps,

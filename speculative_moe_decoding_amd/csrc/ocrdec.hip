@@ -35,7 +35,7 @@ struct Plan {
   size_t s_kv, s_dkv, s_ints, s_cu, s_hbuf, s_rope, s_total;
   // workspace
   size_t w_x, w_q, w_attn, w_part, w_bnorm, w_ridx, w_rgate, w_perm, w_inv, w_off, w_act, w_slot, w_rlogit, w_misc, w_stats, w_hx,
-      w_y, w_cat, w_u, w_dffn, w_esave, w_hsave, w_lmv, w_lmi, w_plan, w_total;
+      w_y, w_cat, w_u, w_u2, w_dffn, w_esave, w_hsave, w_lmv, w_lmi, w_plan, w_total;
 };
 
 bool shape_ok(const ocrdec_config* c, std::string* why) {
@@ -111,6 +111,7 @@ Plan make_plan(const ocrdec_config* c) {
   p.w_y = take(M * NSLOT * D * 4);
   p.w_cat = take(M * 2 * D * 4);
   p.w_u = take(M * D * 4);
+  p.w_u2 = take((size_t)c->max_batch * D * 4);  // second output buffer of the recursive draft passes
   p.w_dffn = take(M * DF * 4);
   p.w_esave = take(M * D * 4);
   p.w_hsave = take((size_t)2 * c->max_batch * D * 4);
@@ -130,7 +131,7 @@ struct ocrdec_model {
   char* state;
   char* ws;
   StateView sv;
-  float *x, *q, *attn, *part, *cat, *u, *dffn, *esave, *hsave[2], *lm_val;
+  float *x, *q, *attn, *part, *cat, *u, *u2, *dffn, *esave, *hsave[2], *lm_val;
   int *lm_idx, *plan_base, *plan_cnt, *plan_slot, *tok_tmp;
   MoeBufs mb;
   const float2* rope;
@@ -311,19 +312,23 @@ void verifier_layers(ocrdec_model* m, hipStream_t s, PassPath pp, int M, int B, 
   }
 }
 
+// The draft block on rows u (M of them): the fusion projection of cat into
+// u (skipped when a fused launch has already written u), attention, SwiGLU FFN.
 template <typename T>
-void draft_layer(ocrdec_model* m, hipStream_t s, PassPath pp, int M, int B, RowPlan plan, int nch) {
+void draft_layer(ocrdec_model* m, hipStream_t s, PassPath pp, int M, int B, RowPlan plan, int nch, float* u,
+                 bool fused_in) {
   const ocrdec_config& c = m->cfg;
   const int mx = pp.dense;
   T* dkv = static_cast<T*>((void*)(m->state + m->p.s_dkv));
-  dense_gemv<T>(m, s, mx, 2 * D, EPI_STORE, m->cat, 2 * D, nullptr, wmat<T>(m, dw(m, D_FUSE)), nullptr, D, M, m->u,
-                D);
-  dense_qkv<T>(m, s, mx, m->u, wvec(m, dw(m, D_ANORM)), wmat<T>(m, dw(m, D_QKV)), M, plan, dkv);
+  if (!fused_in)
+    dense_gemv<T>(m, s, mx, 2 * D, EPI_STORE, m->cat, 2 * D, nullptr, wmat<T>(m, dw(m, D_FUSE)), nullptr, D, M, u,
+                  D);
+  dense_qkv<T>(m, s, mx, u, wvec(m, dw(m, D_ANORM)), wmat<T>(m, dw(m, D_QKV)), M, plan, dkv);
   launch_attention<T>(s, m->q, dkv, c.max_positions, plan, B, nch, m->p.tiles_per_chunk, m->part, m->attn);
-  dense_gemv<T>(m, s, mx, QD, EPI_ADD, m->attn, QD, nullptr, wmat<T>(m, dw(m, D_WO)), nullptr, D, M, m->u, D);
-  dense_gemv<T>(m, s, mx, D, EPI_SWIGLU, m->u, D, wvec(m, dw(m, D_FNORM)), wmat<T>(m, dw(m, D_GATE)),
+  dense_gemv<T>(m, s, mx, QD, EPI_ADD, m->attn, QD, nullptr, wmat<T>(m, dw(m, D_WO)), nullptr, D, M, u, D);
+  dense_gemv<T>(m, s, mx, D, EPI_SWIGLU, u, D, wvec(m, dw(m, D_FNORM)), wmat<T>(m, dw(m, D_GATE)),
                 wmat<T>(m, dw(m, D_UP)), DF, M, m->dffn, DF);
-  dense_gemv<T>(m, s, mx, DF, EPI_ADD, m->dffn, DF, nullptr, wmat<T>(m, dw(m, D_DOWN)), nullptr, D, M, m->u, D);
+  dense_gemv<T>(m, s, mx, DF, EPI_ADD, m->dffn, DF, nullptr, wmat<T>(m, dw(m, D_DOWN)), nullptr, D, M, u, D);
 }
 
 // Prefill in passes of up to prefill_group entries of PREFILL_CHUNK rows: the
@@ -368,7 +373,7 @@ int do_prefill(ocrdec_model* m, hipStream_t s, int B, const int32_t* slots_host,
     if (finish) lm_head<T>(m, s, m->x, PREFILL_CHUNK, true, wvec(m, W_FNORM), g.n, nullptr, m->tok_tmp, 1);
     launch_draft_prefill_cat(s, g, m->x, m->esave, hprev, hnext, wvec(m, dw(m, D_NH)), wvec(m, dw(m, D_NE)),
                              c.norm_eps, m->cat);
-    draft_layer<T>(m, s, prefill_path<T>(m), M, g.n, plan, nch);
+    draft_layer<T>(m, s, prefill_path<T>(m), M, g.n, plan, nch, m->u, false);
     if (finish) launch_prefill_finish(s, g, m->x, m->tok_tmp, m->sv, pending_out);
   }
   for (int b = 0; b < B; ++b) m->slot_bound[slots_host ? slots_host[b] : b] = nv_host[b] + np_host[b];
@@ -381,18 +386,43 @@ int do_draft(ocrdec_model* m, hipStream_t s, int B, const int32_t* slots, int K,
   const int Q = K + 1;
   // same chunk count as the verify of this step (a decode-step graph is keyed on it)
   const int nch = chunks_for(m, std::min(c.max_positions - 1, call_bound(m, B, slots) + K));
+  const PassPath pp = decode_path<T>(m);
+  const RowPlan plan{m->plan_base, m->plan_cnt, m->plan_slot, Q};
+  const RowPlan p1{m->plan_base, m->plan_cnt, m->plan_slot, 1};
+  if (pp.dense == DENSE_VECTOR) {
+    // each pass's plan, input rows and fusion projection in one launch (pass j
+    // >= 2 also takes d_{j-1} from the previous LM head's partials, so only the
+    // last pass runs the argmax stage 2); passes alternate between two output
+    // buffers since a pass reads the previous one's rows
+    const int nblk = lmhead_blocks(c.vocab);
+    const T* wf = wmat<T>(m, dw(m, D_FUSE));
+    launch_draft_fuse<T>(s, 0, 1, Q, Q, K, slots, m->sv, wmat<T>(m, W_EMBED), c.vocab, wvec(m, dw(m, D_NH)),
+                         wvec(m, dw(m, D_NE)), c.norm_eps, nullptr, nullptr, nullptr, nblk, draft_out, m->plan_base,
+                         m->plan_cnt, m->plan_slot, wf, B * Q, m->u);
+    draft_layer<T>(m, s, pp, B * Q, B, plan, nch, m->u, true);
+    lm_head<T>(m, s, m->u, Q, true, wvec(m, dw(m, D_ONORM)), B, nullptr, K == 1 ? draft_out : nullptr, K);
+    float* uprev = m->u;
+    for (int j = 2; j <= K; ++j) {
+      float* u = (uprev == m->u) ? m->u2 : m->u;
+      launch_draft_fuse<T>(s, 1, j, Q, (j == 2) ? Q : 1, K, nullptr, m->sv, wmat<T>(m, W_EMBED), c.vocab,
+                           wvec(m, dw(m, D_NH)), wvec(m, dw(m, D_NE)), c.norm_eps, uprev, m->lm_val, m->lm_idx, nblk,
+                           draft_out, m->plan_base, m->plan_cnt, m->plan_slot, wf, B, u);
+      draft_layer<T>(m, s, pp, B, B, p1, nch, u, true);
+      lm_head<T>(m, s, u, 1, true, wvec(m, dw(m, D_ONORM)), B, nullptr, j == K ? draft_out + (j - 1) : nullptr, K);
+      uprev = u;
+    }
+    return hip_check("ocrdec_draft");
+  }
   launch_plan_draft_catchup<T>(s, B, Q, slots, m->sv, wmat<T>(m, W_EMBED), c.vocab, wvec(m, dw(m, D_NH)),
                                wvec(m, dw(m, D_NE)), c.norm_eps, m->plan_base, m->plan_cnt, m->plan_slot, m->cat);
-  RowPlan plan{m->plan_base, m->plan_cnt, m->plan_slot, Q};
-  draft_layer<T>(m, s, decode_path<T>(m), B * Q, B, plan, nch);
+  draft_layer<T>(m, s, pp, B * Q, B, plan, nch, m->u, false);
   lm_head<T>(m, s, m->u, Q, true, wvec(m, dw(m, D_ONORM)), B, nullptr, draft_out, K);
   for (int j = 2; j <= K; ++j) {
     const int Qprev = (j == 2) ? Q : 1;
     launch_plan_draft_step<T>(s, B, j, Qprev, K, m->sv, draft_out, wmat<T>(m, W_EMBED), c.vocab,
                               wvec(m, dw(m, D_NH)), wvec(m, dw(m, D_NE)), c.norm_eps, m->u, m->plan_base, m->plan_cnt,
                               m->plan_slot, m->cat);
-    RowPlan p1{m->plan_base, m->plan_cnt, m->plan_slot, 1};
-    draft_layer<T>(m, s, decode_path<T>(m), B, B, p1, nch);
+    draft_layer<T>(m, s, pp, B, B, p1, nch, m->u, false);
     lm_head<T>(m, s, m->u, 1, true, wvec(m, dw(m, D_ONORM)), B, nullptr, draft_out + (j - 1), K);
   }
   return hip_check("ocrdec_draft");
@@ -492,6 +522,7 @@ int ocrdec_create(const ocrdec_config* cfg, const void* const* weight_ptrs, int 
   m->part = wf(p.w_part);
   m->cat = wf(p.w_cat);
   m->u = wf(p.w_u);
+  m->u2 = wf(p.w_u2);
   m->dffn = wf(p.w_dffn);
   m->esave = wf(p.w_esave);
   m->hsave[0] = wf(p.w_hsave);
