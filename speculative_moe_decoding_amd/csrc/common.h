@@ -334,6 +334,7 @@ struct RowPlan {
   const int* cnt;
   const int* slot;   // state slot of sequence b
   int Q;
+  int ident;         // 1: the slot of sequence b is b (slot[] holds the same)
 };
 
 }  // namespace ocr

@@ -184,62 +184,72 @@ __global__ __launch_bounds__(256) void k_attn_partial(const float* __restrict__ 
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int wave = wave_id(), lane = lane_id(), tid = threadIdx.x;
   const int Q = plan.Q;
-  // the plan entries and this head's query rows (i < Q) go out together
-  const int base = plan.base[b], pcnt = plan.cnt[b];
-  const long slot = plan.slot[b];
-  constexpr int NQV = QMAX_ATT * HD / 4 / 256;
-  float4 qv[NQV];
-#pragma unroll
-  for (int j = 0; j < NQV; ++j) {
-    const int e = tid + 256 * j, i = e / (HD / 4), d4 = e % (HD / 4);
-    qv[j] = (i < Q) ? reinterpret_cast<const float4*>(q + (long)(b * Q + i) * QD + h * HD)[d4]
-                    : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  // rows past the cache (never produced by the library's own plans) are skipped
-  const int cnt = (base < 0) ? 0 : min(min(pcnt, Q), max_pos - base);
-  const int p_last = base + cnt - 1;
   const int C = tiles_per_chunk * ATT_TILE;
   const int k0 = c * C;
-  if (cnt <= 0 || k0 > p_last) return;
-  const int n_tiles = min(tiles_per_chunk, (p_last - k0) / ATT_TILE + 1);
+  // The tile's addresses need only the slot: with identity slots the first
+  // tile's loads go out with the plan reads and this head's query rows (i < Q)
+  // (key indices clamped into the cache; rows past the last query's key are
+  // zeroed when staged).
+  const long slot = plan.ident ? (long)b : (long)plan.slot[b];
   const T* Kc = kv + slot * (2L * NH * max_pos * HD) + (long)h * max_pos * HD;
   const T* Vc = Kc + (long)NH * max_pos * HD;
   constexpr int CE = WT<T>::CE;
   constexpr int CPR = HD / CE;                         // 16-byte chunks per key row
   constexpr int NLD = ATT_TILE * CPR / 256;            // chunks per thread per tile
   uint4 kr[NLD], vr[NLD];
-  // K / V loads of tile tt (rows past the last query's key read as zeros)
   auto load_tile = [&](int tt) {
     const int kt = k0 + tt * ATT_TILE;
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      const int e = tid + 256 * j, t = e / CPR, d0 = (e % CPR) * CE;
+      const long k = min(kt + t, max_pos - 1);
+      kr[j] = ldg16(Kc + k * HD + d0);
+      vr[j] = ldg16(Vc + k * HD + d0);
+    }
+  };
+  load_tile(0);
+  constexpr int NQV = QMAX_ATT * HD / 4 / 256;
+  float4 qv[NQV];
+#pragma unroll
+  for (int j = 0; j < NQV; ++j) {
+    const int e = tid + 256 * j, i = e / (HD / 4), d4 = e % (HD / 4);
+    qv[j] = reinterpret_cast<const float4*>(q + (long)(b * Q + min(i, Q - 1)) * QD + h * HD)[d4];
+  }
+  const int base = plan.base[b], pcnt = plan.cnt[b];
+  // rows past the cache (never produced by the library's own plans) are
+  // skipped; no branch on base, so both reads go out together
+  const int cnt = min(min(pcnt, Q), max_pos - base) & -(int)(base >= 0);
+  const int p_last = base + cnt - 1;
+  // LDS staging of the tile at key kt (rows past p_last as zeros)
+  auto stage_tile = [&](int kt) {
     const int nk = min(ATT_TILE, p_last + 1 - kt);
 #pragma unroll
     for (int j = 0; j < NLD; ++j) {
       const int e = tid + 256 * j, t = e / CPR, d0 = (e % CPR) * CE;
-      if (t < nk) {
-        kr[j] = ldg16(Kc + (long)(kt + t) * HD + d0);
-        vr[j] = ldg16(Vc + (long)(kt + t) * HD + d0);
-      } else {
+      if (t >= nk) {
         kr[j] = make_uint4(0, 0, 0, 0);
         vr[j] = make_uint4(0, 0, 0, 0);
       }
+      AT::stage(kr[j], vr[j], d0, t, Kq, Vs);
     }
   };
-  load_tile(0);
-  // queries of this sequence / head (rows past cnt as zeros)
+  // the first tile and the queries (rows past cnt as zeros) are staged before
+  // the exit test, which keeps their loads ahead of it
+  stage_tile(k0);
 #pragma unroll
   for (int j = 0; j < NQV; ++j) {
     const int e = tid + 256 * j, i = e / (HD / 4);
     qs[i][e % (HD / 4)] = (i < cnt) ? qv[j] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
+  if (cnt <= 0 || k0 > p_last) return;
+  const int n_tiles = min(tiles_per_chunk, (p_last - k0) / ATT_TILE + 1);
   float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
   float o0[2] = {0.f, 0.f}, o1[2] = {0.f, 0.f};
   for (int tt = 0; tt < n_tiles; ++tt) {
     const int kt = k0 + tt * ATT_TILE;
-    __syncthreads();  // the previous tile's LDS reads are done
-#pragma unroll
-    for (int j = 0; j < NLD; ++j) {
-      const int e = tid + 256 * j, t = e / CPR, d0 = (e % CPR) * CE;
-      AT::stage(kr[j], vr[j], d0, t, Kq, Vs);
+    if (tt > 0) {
+      __syncthreads();  // the previous tile's LDS reads are done
+      stage_tile(kt);
     }
     __syncthreads();
     if (tt + 1 < n_tiles) load_tile(tt + 1);  // next tile in flight during this one's arithmetic

@@ -367,7 +367,7 @@ int do_prefill(ocrdec_model* m, hipStream_t s, int B, const int32_t* slots_host,
     launch_plan_prefill<T>(s, g, vision, nv_stride, prompt, np_stride, wmat<T>(m, W_EMBED), c.vocab, m->plan_base,
                            m->plan_cnt, m->plan_slot, m->x, m->esave);
     const int M = g.n * PREFILL_CHUNK;
-    RowPlan plan{m->plan_base, m->plan_cnt, m->plan_slot, PREFILL_CHUNK};
+    RowPlan plan{m->plan_base, m->plan_cnt, m->plan_slot, PREFILL_CHUNK, 0};
     const int nch = chunks_for(m, std::min(c.max_positions - 1, max_pos));
     verifier_layers<T>(m, s, prefill_path<T>(m), M, g.n, plan, nch, false, nullptr);
     if (finish) lm_head<T>(m, s, m->x, PREFILL_CHUNK, true, wvec(m, W_FNORM), g.n, nullptr, m->tok_tmp, 1);
@@ -387,8 +387,9 @@ int do_draft(ocrdec_model* m, hipStream_t s, int B, const int32_t* slots, int K,
   // same chunk count as the verify of this step (a decode-step graph is keyed on it)
   const int nch = chunks_for(m, std::min(c.max_positions - 1, call_bound(m, B, slots) + K));
   const PassPath pp = decode_path<T>(m);
-  const RowPlan plan{m->plan_base, m->plan_cnt, m->plan_slot, Q};
-  const RowPlan p1{m->plan_base, m->plan_cnt, m->plan_slot, 1};
+  const int ident = slots == nullptr;
+  const RowPlan plan{m->plan_base, m->plan_cnt, m->plan_slot, Q, ident};
+  const RowPlan p1{m->plan_base, m->plan_cnt, m->plan_slot, 1, ident};
   if (pp.dense == DENSE_VECTOR) {
     // each pass's plan, input rows and fusion projection in one launch (pass j
     // >= 2 also takes d_{j-1} from the previous LM head's partials, so only the
@@ -436,7 +437,7 @@ int do_verify(ocrdec_model* m, hipStream_t s, int B, const int32_t* slots, int K
   const int nch = chunks_for(m, std::min(c.max_positions - 1, call_bound(m, B, slots) + K));
   launch_plan_verify<T>(s, B, K, slots, m->sv, draft, wmat<T>(m, W_EMBED), c.vocab, m->plan_base, m->plan_cnt,
                         m->plan_slot, m->x);
-  RowPlan plan{m->plan_base, m->plan_cnt, m->plan_slot, Q};
+  RowPlan plan{m->plan_base, m->plan_cnt, m->plan_slot, Q, slots == nullptr};
   verifier_layers<T>(m, s, decode_path<T>(m), M, B, plan, nch, true, m->router_override);
   m->last_verify_rows = M;
   lm_head<T>(m, s, m->x, Q, false, wvec(m, W_FNORM), M, logits_out, greedy_out, 1);
