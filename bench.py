@@ -103,6 +103,28 @@ def cpu_baseline(w, page, K, p, seed, n_prefix_vision=32, n_prompt=32, n_trace=1
                         f"prefill); {committed} tokens in {t_steps:.1f}s; AR trace {t1 - t0:.1f}s untimed"))
 
 
+def plain_read(dec, nbytes, n_launches):
+    """Event-timed back-to-back launches of the library's plain read kernel
+    over nbytes (the same count and bracketing as the kernel replay): the rate
+    a kernel that only streams that many bytes reaches on this GPU."""
+    import torch
+    from speculative_moe_decoding_amd import ocrdec
+    buf = torch.ones(int(nbytes) // 4 + 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    nb = int(nbytes) // 16 * 16
+    ocrdec.ocrdec_read_probe(dec.stream, buf, nb, 3, sink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    ocrdec.ocrdec_read_probe(dec.stream, buf, nb, n_launches, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / n_launches
+    del buf
+    return {"bytes": nb, "launches": n_launches, "avg_launch_us": round(us, 2),
+            "GB_per_s": round(nb / (us * 1e-6) / 1e9, 1)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -292,6 +314,9 @@ def main() -> int:
     rep_bytes = na * EXPERT_GATE_UP_BYTES + pairs * (D + I) * 4
     achieved = rep_bytes / (rep_us * 1e-6) / 1e9
     log(f"expert gate/up replay: {n_rep} launches, {na} experts each, {rep_us:.2f} us/launch -> {achieved:.0f} GB/s")
+    plain = plain_read(dec, rep_bytes, n_rep)
+    log(f"plain read of the same {rep_bytes / 1e6:.1f} MB, {n_rep} launches: {plain['avg_launch_us']:.2f} us/launch "
+        f"-> {plain['GB_per_s']:.0f} GB/s")
     pmc = None if matrix else load_traffic()  # the PMC summary covers the vector kernel
     traffic, traffic_ratio = (None, None) if pmc is None else (pmc[0], round(pmc[1], 4))
     result = {
@@ -319,6 +344,7 @@ def main() -> int:
         "roofline": {
             "kernel": ("k_expert_gate_up_mfma (grouped expert GEMM, gate+up)" if matrix
                        else "k_expert_gate_up (grouped expert GEMV, gate+up)"),
+            "experts_per_launch": int(na),
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
@@ -331,6 +357,8 @@ def main() -> int:
             "algorithmic_bytes_per_launch": int(rep_bytes),
             "in_decode_avg_launch_us": round(up_ms / max(1, n_up) * 1e3, 2),
             "in_decode_GB_per_s": round(up_bytes / (up_ms * 1e-3) / 1e9, 1),
+            "plain_read_same_bytes": plain,
+            "frac_of_plain_read": round(achieved / plain["GB_per_s"], 4),
         },
         "tau": round(tau, 4),
         "alpha": round((tau - 1) / K, 4),
@@ -517,6 +545,9 @@ def bench_concurrent(args) -> int:
     log(f"expert gate/up (MFMA): {up_us:.1f} us/launch, {sets:.1f} experts -> {achieved:.0f} GB/s, "
         f"{up_flops / (up_us * 1e-6) / 1e12:.1f} TFLOP/s; down {dn_us:.1f} us; "
         f"step {ev0.elapsed_time(ev1) / Si:.3f} ms (eager)")
+    plain = plain_read(dec, up_bytes, 240)
+    log(f"plain read of the same {up_bytes / 1e6:.1f} MB: {plain['avg_launch_us']:.2f} us/launch "
+        f"-> {plain['GB_per_s']:.0f} GB/s")
     result = {
         "metric": "output tokens/s, static batch of 32 pages, K=1 (12-layer MoE, bf16)",
         "value": round(tok_s, 1),
@@ -549,6 +580,8 @@ def bench_concurrent(args) -> int:
             "algorithmic_bytes_per_launch": int(up_bytes),
             "mfma_TFLOP_per_s": round(up_flops / (up_us * 1e-6) / 1e12, 2),
             "mfma_frac_of_bf16_dense_peak": round(up_flops / (up_us * 1e-6) / 2.5e15, 4),
+            "plain_read_same_bytes": plain,
+            "frac_of_plain_read": round(achieved / plain["GB_per_s"], 4),
         },
         "pages_per_s": round(B / (t_prefill + t_decode), 3),
         "prefill_s": round(t_prefill, 3),

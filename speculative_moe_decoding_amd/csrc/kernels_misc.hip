@@ -525,6 +525,30 @@ void launch_copy_rows(hipStream_t s, const float* src, float* dst, long n) {
   hipLaunchKernelGGL(k_copy, dim3(64), dim3(256), 0, s, src, dst, n);
 }
 
+// Plain read of n16 16-byte words (grid-stride, 8 loads in flight per
+// thread), folded by xor; sink[0] is written only if the fold hits a fixed
+// value, which keeps the loads from being dropped.  Calibration only: it
+// shows what a kernel that does nothing but read reaches at a given size.
+__global__ __launch_bounds__(256) void k_read_probe(const uint4* __restrict__ p, long n16, uint32_t* sink) {
+  constexpr int U = 8;
+  uint32_t acc = 0;
+  const long stride = (long)gridDim.x * 256 * U;
+  for (long base = (long)blockIdx.x * 256 * U + threadIdx.x; base < n16; base += stride) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const long i = min(base + (long)u * 256, n16 - 1);
+      v[u] = p[i];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  if (acc == 0x9e3779b9u) sink[0] = acc;
+}
+void launch_read_probe(hipStream_t s, const void* buf, long n16, uint32_t* sink) {
+  hipLaunchKernelGGL(k_read_probe, dim3(4096), dim3(256), 0, s, static_cast<const uint4*>(buf), n16, sink);
+}
+
 #define OCR_INST_MISC(T)                                                                                          \
   template void launch_plan_verify<T>(hipStream_t, int, int, const int*, StateView, const int*, const T*, int,   \
                                       int*, int*, int*, float*);                                                 \

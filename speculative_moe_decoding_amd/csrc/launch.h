@@ -123,6 +123,8 @@ void launch_plan_draft_catchup(hipStream_t s, int B, int Q, const int* slots_in,
 // is the catch-up pass (M = B Q rows), step = 1 pass j >= 2 (M = B rows,
 // d_{j-1} from the LM-head partials part_val / part_idx of the previous pass,
 // written to draft_out).  out = W_fuse . cat, [M][D]; out must not alias u_prev.
+// Plain read of n16 16-byte words at buf (calibration; see k_read_probe).
+void launch_read_probe(hipStream_t s, const void* buf, long n16, uint32_t* sink);
 template <typename T>
 void launch_draft_fuse(hipStream_t s, int step, int j, int Q, int Qprev, int K, const int* slots_in, StateView sv,
                        const T* embed, int V, const float* g_h, const float* g_e, float eps, const float* u_prev,

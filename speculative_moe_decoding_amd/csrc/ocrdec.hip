@@ -682,6 +682,13 @@ int ocrdec_replay_expert_gate_up(ocrdec_model* m, void* stream, int n_rounds, in
   return hip_check("ocrdec_replay_expert_gate_up");
 }
 
+int ocrdec_read_probe(void* stream, const void* buf, size_t bytes, int n_launches, uint32_t* sink) {
+  if (!buf || !sink || bytes < 16 || n_launches < 0) return fail(OCRDEC_EINVAL, "bad read-probe arguments");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int i = 0; i < n_launches; ++i) launch_read_probe(s, buf, (long)(bytes / 16), sink);
+  return hip_check("ocrdec_read_probe");
+}
+
 int ocrdec_decode_steps(ocrdec_model* m, void* stream, int B, const int32_t* slots, int K, int n_steps,
                         const ocrdec_controlled_cfg* ctrl, int32_t* draft, int32_t* greedy,
                         int32_t* n_accepted_out, int32_t* out_tokens, int32_t* out_len, int out_cap) {

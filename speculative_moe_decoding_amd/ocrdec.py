@@ -24,7 +24,7 @@ SYMBOLS = (
     "ocrdec_prefill", "ocrdec_draft", "ocrdec_verify", "ocrdec_accept_rollback", "ocrdec_controlled_drafts",
     "ocrdec_set_taps", "ocrdec_expert_timing", "ocrdec_expert_stats", "ocrdec_replay_expert_gate_up",
     "ocrdec_decode_steps", "ocrdec_sync_positions", "ocrdec_load_sequence", "ocrdec_set_router_logits",
-    "ocrdec_last_error",
+    "ocrdec_read_probe", "ocrdec_last_error",
 )
 
 
@@ -81,6 +81,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "ocrdec_sync_positions": (I, [P, P]),
         "ocrdec_load_sequence": (I, [P, P, I, I, I, P]),
         "ocrdec_set_router_logits": (I, [P, P]),
+        "ocrdec_read_probe": (I, [P, P, ctypes.c_size_t, I, P]),
         "ocrdec_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -203,6 +204,10 @@ def ocrdec_replay_expert_gate_up(h, stream, n_rounds: int, want_count: bool = Fa
     _check("ocrdec_replay_expert_gate_up", load_library().ocrdec_replay_expert_gate_up(
         h, stream, n_rounds, ctypes.byref(na) if want_count else None))
     return na.value if want_count else None
+
+
+def ocrdec_read_probe(stream, buf, nbytes: int, n_launches: int, sink):
+    _check("ocrdec_read_probe", load_library().ocrdec_read_probe(stream, _ptr(buf), nbytes, n_launches, _ptr(sink)))
 
 
 class Decoder:
