@@ -103,25 +103,28 @@ def cpu_baseline(w, page, K, p, seed, n_prefix_vision=32, n_prompt=32, n_trace=1
                         f"prefill); {committed} tokens in {t_steps:.1f}s; AR trace {t1 - t0:.1f}s untimed"))
 
 
-def plain_read(dec, nbytes, n_launches):
+def plain_read(dec, nbytes, n_launches, n_regions=L):
     """Event-timed back-to-back launches of the library's plain read kernel
-    over nbytes (the same count and bracketing as the kernel replay): the rate
-    a kernel that only streams that many bytes reaches on this GPU."""
+    over nbytes (the same count and bracketing as the kernel replay), launch i
+    reading region i mod n_regions of a buffer of n_regions such regions -- as
+    the replay walks the layers' weights, so neither gets help from the GPU's
+    last-level cache: the rate a kernel that only streams that many bytes
+    reaches on this GPU."""
     import torch
     from speculative_moe_decoding_amd import ocrdec
-    buf = torch.ones(int(nbytes) // 4 + 4, dtype=torch.int32, device="cuda")
+    nb = int(nbytes) // 256 * 256
+    buf = torch.ones(n_regions * nb // 4, dtype=torch.int32, device="cuda")
     sink = torch.zeros(4, dtype=torch.int32, device="cuda")
-    nb = int(nbytes) // 16 * 16
-    ocrdec.ocrdec_read_probe(dec.stream, buf, nb, 3, sink)
+    ocrdec.ocrdec_read_probe(dec.stream, buf, nb, n_regions, 2 * n_regions, sink)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    ocrdec.ocrdec_read_probe(dec.stream, buf, nb, n_launches, sink)
+    ocrdec.ocrdec_read_probe(dec.stream, buf, nb, n_regions, n_launches, sink)
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / n_launches
     del buf
-    return {"bytes": nb, "launches": n_launches, "avg_launch_us": round(us, 2),
+    return {"bytes": nb, "regions": n_regions, "launches": n_launches, "avg_launch_us": round(us, 2),
             "GB_per_s": round(nb / (us * 1e-6) / 1e9, 1)}
 
 

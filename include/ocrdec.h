@@ -212,13 +212,17 @@ int ocrdec_expert_stats(ocrdec_model* m, double* ms_gate_up, long long* n_gate_u
 int ocrdec_replay_expert_gate_up(ocrdec_model* m, void* stream, int n_rounds, int* expert_sets_per_launch);
 
 /* Calibration (not part of the method): n_launches back-to-back launches on
- * `stream` of a kernel that only reads the first floor(bytes / 16) * 16 bytes of
- * the device buffer buf (16-byte loads, 4,096 workgroups) and writes nothing
- * but, in practice never, one word to sink (device, >= 4 bytes).  A pair of
- * events around the call gives the read rate a plain streaming kernel reaches at
- * that size, the practical ceiling for the bandwidth-bound kernels above.
- * OCRDEC_EINVAL if buf or sink is null, bytes < 16 or n_launches < 0. */
-int ocrdec_read_probe(void* stream, const void* buf, size_t bytes, int n_launches, uint32_t* sink);
+ * `stream` of a kernel that only reads `bytes` bytes (16-byte loads, 4,096
+ * workgroups) and writes nothing but, in practice never, one word to sink
+ * (device, >= 4 bytes).  Launch i reads region i mod n_regions of the device
+ * buffer buf, which holds n_regions consecutive regions of `bytes` bytes: with
+ * as many regions as a replay has layers, the reads do not hit the GPU's
+ * last-level cache any more than the replayed kernel's do.  A pair of events
+ * around the call gives the rate a plain streaming kernel reaches at that size,
+ * the practical ceiling for the bandwidth-bound kernels above.  OCRDEC_EINVAL
+ * if buf or sink is null, bytes < 16 or not a multiple of 256, n_regions < 1 or
+ * n_launches < 0. */
+int ocrdec_read_probe(void* stream, const void* buf, size_t bytes, int n_regions, int n_launches, uint32_t* sink);
 
 const char* ocrdec_last_error(void);
 

@@ -682,10 +682,12 @@ int ocrdec_replay_expert_gate_up(ocrdec_model* m, void* stream, int n_rounds, in
   return hip_check("ocrdec_replay_expert_gate_up");
 }
 
-int ocrdec_read_probe(void* stream, const void* buf, size_t bytes, int n_launches, uint32_t* sink) {
-  if (!buf || !sink || bytes < 16 || n_launches < 0) return fail(OCRDEC_EINVAL, "bad read-probe arguments");
+int ocrdec_read_probe(void* stream, const void* buf, size_t bytes, int n_regions, int n_launches, uint32_t* sink) {
+  if (!buf || !sink || bytes < 16 || bytes % 256 != 0 || n_regions < 1 || n_launches < 0)
+    return fail(OCRDEC_EINVAL, "bad read-probe arguments");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  for (int i = 0; i < n_launches; ++i) launch_read_probe(s, buf, (long)(bytes / 16), sink);
+  for (int i = 0; i < n_launches; ++i)
+    launch_read_probe(s, static_cast<const char*>(buf) + (size_t)(i % n_regions) * bytes, (long)(bytes / 16), sink);
   return hip_check("ocrdec_read_probe");
 }
 

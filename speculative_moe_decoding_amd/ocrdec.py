@@ -81,7 +81,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "ocrdec_sync_positions": (I, [P, P]),
         "ocrdec_load_sequence": (I, [P, P, I, I, I, P]),
         "ocrdec_set_router_logits": (I, [P, P]),
-        "ocrdec_read_probe": (I, [P, P, ctypes.c_size_t, I, P]),
+        "ocrdec_read_probe": (I, [P, P, ctypes.c_size_t, I, I, P]),
         "ocrdec_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -206,8 +206,9 @@ def ocrdec_replay_expert_gate_up(h, stream, n_rounds: int, want_count: bool = Fa
     return na.value if want_count else None
 
 
-def ocrdec_read_probe(stream, buf, nbytes: int, n_launches: int, sink):
-    _check("ocrdec_read_probe", load_library().ocrdec_read_probe(stream, _ptr(buf), nbytes, n_launches, _ptr(sink)))
+def ocrdec_read_probe(stream, buf, nbytes: int, n_regions: int, n_launches: int, sink):
+    _check("ocrdec_read_probe", load_library().ocrdec_read_probe(stream, _ptr(buf), nbytes, n_regions, n_launches,
+                                                                  _ptr(sink)))
 
 
 class Decoder:

@@ -100,7 +100,7 @@ def test_rejects_bad_paths_and_null_handles(lib):
     assert lib.ocrdec_set_taps(None, None, None) == E
     assert lib.ocrdec_expert_timing(None, 1) == E
     assert lib.ocrdec_replay_expert_gate_up(None, None, 1, None) == E
-    assert lib.ocrdec_read_probe(None, None, 64, 1, None) == E
+    assert lib.ocrdec_read_probe(None, None, 256, 1, 1, None) == E
 
 
 def test_prefill_argument_checks_need_no_device(lib):
