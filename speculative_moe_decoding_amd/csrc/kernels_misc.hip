@@ -360,15 +360,53 @@ __global__ void k_set_sequence(int slot, int P, int tok, StateView sv) {
 }
 
 // Greedy longest-prefix acceptance (one block per sequence).
+// Argmax stage 2 of one row by one wavefront (the block-wide version's rule:
+// largest value, lowest id among equal ones), all of a lane's loads issued
+// together (indices clamped to the last block); every lane gets the id.
+__device__ __forceinline__ int argmax_wave(const float* __restrict__ rv, const int* __restrict__ ri, int nblk) {
+  constexpr int AW = 32;
+  const int lane = lane_id();
+  float v = -INFINITY;
+  int id = 0x7fffffff;
+  for (int b0 = 0; b0 < nblk; b0 += 64 * AW) {
+    float pv[AW];
+    int pi[AW];
+#pragma unroll
+    for (int j = 0; j < AW; ++j) {
+      const int k = min(b0 + lane + 64 * j, nblk - 1);
+      pv[j] = rv[k];
+      pi[j] = ri[k];
+    }
+#pragma unroll
+    for (int j = 0; j < AW; ++j)
+      if (pv[j] > v || (pv[j] == v && pi[j] < id)) { v = pv[j]; id = pi[j]; }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float ov = __shfl_xor(v, off, 64);
+    const int oi = __shfl_xor(id, off, 64);
+    if (ov > v || (ov == v && oi < id)) { v = ov; id = oi; }
+  }
+  return id;
+}
+
+// Acceptance of sequence b (block b).  With AM the verify rows' greedy tokens
+// are first reduced here from the LM head's per-block bests (part_val /
+// part_idx, [B (K+1)][nblk]) and written to greedy_w; otherwise they are read
+// from greedy.
+template <bool AM>
 __global__ __launch_bounds__(256) void k_accept(int K, const int* __restrict__ plan_slot,
                                                 const int* __restrict__ draft, const int* __restrict__ greedy,
                                                 const float* __restrict__ xfinal, StateView sv,
                                                 int* __restrict__ n_acc, int* __restrict__ out_tokens,
-                                                int* __restrict__ out_len_out, int out_cap) {
+                                                int* __restrict__ out_len_out, int out_cap,
+                                                const float* __restrict__ part_val, const int* __restrict__ part_idx,
+                                                int nblk, int* __restrict__ greedy_w) {
   constexpr int J = D / 256;
   __shared__ int sn;
+  __shared__ int gs[QV];
   const int b = blockIdx.x;
-  const int lane = lane_id();
+  const int lane = lane_id(), wave = wave_id();
   // the verify rows' final hidden states (rows past K clamped, not stored)
   // are fetched before the acceptance is known
   float hv[QV][J];
@@ -379,10 +417,21 @@ __global__ __launch_bounds__(256) void k_accept(int K, const int* __restrict__ p
     for (int j = 0; j < J; ++j) hv[i][j] = src[threadIdx.x + 256 * j];
   }
   const int slot = plan_slot[b];
-  if (wave_id() == 0) {
+  if constexpr (AM) {
+    for (int i = wave; i <= K; i += 4) {
+      const long r = (long)b * (K + 1) + i;
+      const int id = argmax_wave(part_val + r * nblk, part_idx + r * nblk, nblk);
+      if (lane == 0) {
+        gs[i] = id;
+        greedy_w[r] = id;
+      }
+    }
+    __syncthreads();
+  }
+  if (wave == 0) {
     // lane i < K compares d_i with the verifier's g_i; n = the first mismatch
     const int dv = (lane < K) ? draft[b * K + lane] : 0;
-    const int gv = (lane <= K) ? greedy[b * (K + 1) + lane] : 0;
+    const int gv = (lane <= K) ? (AM ? gs[lane] : greedy[b * (K + 1) + lane]) : 0;
     const int old = sv.kv_len[slot];
     const int ol0 = sv.out_len[slot];
     const uint64_t miss = __ballot(!(lane < K && dv == gv));
@@ -511,9 +560,14 @@ void launch_set_sequence(hipStream_t s, int slot, int P, int tok, StateView sv) 
   hipLaunchKernelGGL(k_set_sequence, dim3(1), dim3(256), 0, s, slot, P, tok, sv);
 }
 void launch_accept(hipStream_t s, int B, int K, const int* plan_slot, const int* draft, const int* greedy,
-                   const float* xfinal, StateView sv, int* n_acc, int* out_tokens, int* out_len_out, int out_cap) {
-  hipLaunchKernelGGL(k_accept, dim3(B), dim3(256), 0, s, K, plan_slot, draft, greedy, xfinal, sv, n_acc,
-                     out_tokens, out_len_out, out_cap);
+                   const float* xfinal, StateView sv, int* n_acc, int* out_tokens, int* out_len_out, int out_cap,
+                   const float* part_val, const int* part_idx, int nblk, int* greedy_w) {
+  if (part_val != nullptr)
+    hipLaunchKernelGGL((k_accept<true>), dim3(B), dim3(256), 0, s, K, plan_slot, draft, greedy, xfinal, sv, n_acc,
+                       out_tokens, out_len_out, out_cap, part_val, part_idx, nblk, greedy_w);
+  else
+    hipLaunchKernelGGL((k_accept<false>), dim3(B), dim3(256), 0, s, K, plan_slot, draft, greedy, xfinal, sv, n_acc,
+                       out_tokens, out_len_out, out_cap, part_val, part_idx, nblk, greedy_w);
 }
 void launch_controlled(hipStream_t s, int B, int K, const int* slots_in, StateView sv, const int* trace,
                        int trace_stride, int trace_len, uint64_t seed, uint64_t thr, int V, int* draft) {

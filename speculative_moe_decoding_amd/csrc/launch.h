@@ -159,9 +159,13 @@ void launch_draft_prefill_cat(hipStream_t s, const PrefillGroup& g, const float*
 void launch_prefill_finish(hipStream_t s, const PrefillGroup& g, const float* xfinal, const int* tok, StateView sv,
                            int* pending_out);
 void launch_set_sequence(hipStream_t s, int slot, int P, int tok, StateView sv);
+// Acceptance; with part_val non-null the greedy tokens are first reduced from
+// the LM head's per-block bests (part_val / part_idx, nblk per row) and
+// written to greedy_w (the verify then skips its argmax stage 2).
 void launch_accept(hipStream_t s, int B, int K, const int* plan_slot, const int* draft, const int* greedy,
                    const float* xfinal, StateView sv, int* n_acc, int* out_tokens, int* out_len_out,
-                   int out_cap);
+                   int out_cap, const float* part_val = nullptr, const int* part_idx = nullptr, int nblk = 0,
+                   int* greedy_w = nullptr);
 void launch_controlled(hipStream_t s, int B, int K, const int* slots_in, StateView sv, const int* trace,
                        int trace_stride, int trace_len, uint64_t seed, uint64_t thr, int V, int* draft);
 void launch_copy_rows(hipStream_t s, const float* src, float* dst, long n);

@@ -431,7 +431,7 @@ int do_draft(ocrdec_model* m, hipStream_t s, int B, const int32_t* slots, int K,
 
 template <typename T>
 int do_verify(ocrdec_model* m, hipStream_t s, int B, const int32_t* slots, int K, const int32_t* draft,
-              int32_t* greedy_out, float* logits_out) {
+              int32_t* greedy_out, float* logits_out, bool greedy_in_accept = false) {
   const ocrdec_config& c = m->cfg;
   const int Q = K + 1, M = B * Q;
   const int nch = chunks_for(m, std::min(c.max_positions - 1, call_bound(m, B, slots) + K));
@@ -440,7 +440,8 @@ int do_verify(ocrdec_model* m, hipStream_t s, int B, const int32_t* slots, int K
   RowPlan plan{m->plan_base, m->plan_cnt, m->plan_slot, Q, slots == nullptr};
   verifier_layers<T>(m, s, decode_path<T>(m), M, B, plan, nch, true, m->router_override);
   m->last_verify_rows = M;
-  lm_head<T>(m, s, m->x, Q, false, wvec(m, W_FNORM), M, logits_out, greedy_out, 1);
+  // greedy_in_accept: the accept launch that follows reduces the greedy tokens
+  lm_head<T>(m, s, m->x, Q, false, wvec(m, W_FNORM), M, logits_out, greedy_in_accept ? nullptr : greedy_out, 1);
   if (m->tap_hidden) launch_copy_rows(s, m->x, m->tap_hidden, (long)M * D);
   return hip_check("ocrdec_verify");
 }
@@ -736,12 +737,13 @@ int ocrdec_decode_steps(ocrdec_model* m, void* stream, int B, const int32_t* slo
       if (r1 == OCRDEC_OK && ctrl && K > 0)
         launch_controlled(cs, B, K, slots, m->sv, ctrl->trace, ctrl->trace_stride, ctrl->trace_len, ctrl->seed,
                           ctrl->threshold, m->cfg.vocab, draft);
+      // the verify's argmax stage 2 runs inside the accept launch
       if (r1 == OCRDEC_OK)
-        r1 = m->cfg.dtype == OCRDEC_BF16 ? do_verify<bf16>(m, cs, B, slots, K, draft, greedy, nullptr)
-                                         : do_verify<float>(m, cs, B, slots, K, draft, greedy, nullptr);
+        r1 = m->cfg.dtype == OCRDEC_BF16 ? do_verify<bf16>(m, cs, B, slots, K, draft, greedy, nullptr, true)
+                                         : do_verify<float>(m, cs, B, slots, K, draft, greedy, nullptr, true);
       if (r1 == OCRDEC_OK)
         launch_accept(cs, B, K, m->plan_slot, draft, greedy, m->x, m->sv, n_accepted_out, out_tokens, out_len,
-                      out_cap);
+                      out_cap, m->lm_val, m->lm_idx, lmhead_blocks(m->cfg.vocab), greedy);
       hipGraph_t graph = nullptr;
       const hipError_t ec = hipStreamEndCapture(cs, &graph);
       if (r1 != OCRDEC_OK || ec != hipSuccess) {
