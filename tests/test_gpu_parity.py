@@ -154,3 +154,51 @@ def test_graph_steps_match_eager_calls():
             torch.cuda.synchronize()
         assert eager[0].tolist() == ar[0][:N].tolist()
     log("graph decode matches eager calls")
+
+
+def _eager_steps(dec, pages, K, n_steps, slots):
+    """n_steps individual draft / verify / accept calls with the given slot map
+    (None: identity); returns the committed tokens per sequence."""
+    from speculative_moe_decoding_amd import ocrdec  # noqa: F401
+    B = len(pages)
+    cap = n_steps * (K + 1) + 2
+    out_tokens = torch.zeros(B, cap, dtype=torch.int32, device="cuda")
+    out_len = dec.i32(B)
+    n_acc = dec.i32(B)
+    draft, greedy = dec.i32(B, max(K, 1)), dec.i32(B, K + 1)
+    out_tokens[:, 0] = dec.prefill(pages)
+    for _ in range(n_steps):
+        dec.draft(B, K, slots=slots, out=draft)
+        dec.verify(B, K, draft, slots=slots, greedy=greedy)
+        dec.accept(B, K, draft, greedy, n_acc, out_tokens, out_len, slots=slots)
+    torch.cuda.synchronize()
+    n = out_len.cpu().numpy()
+    return [out_tokens[b, :int(n[b])].cpu().numpy().tolist() for b in range(B)]
+
+
+@pytest.mark.parametrize("B,K", [(2, 3), (1, 7)])
+def test_graph_steps_batches_and_depths(B, K):
+    """Decode-step graphs (whose accept launch also reduces the verify's greedy
+    tokens) give the individual calls' tokens with several sequences and with
+    the deepest draft (8 verify rows per sequence, two per wavefront in the
+    reduction); both equal plain autoregressive decoding; and an explicit slot
+    map 0..B-1 gives the tokens of the calls without one (whose attention
+    takes the slot from the sequence index)."""
+    cfg = SMALL16
+    w = synth.Weights(cfg, 51)
+    from speculative_moe_decoding_amd import ocrdec
+    log(f"case B={B} K={K}")
+    pages = synth.make_pages(cfg, 52, [18, 11][:B], [6, 9][:B], [32] * B)
+    dec = ocrdec.Decoder(cfg, w.device_arrays(), max_batch=B, max_k=K, max_positions=512)
+    N = 32
+    eager, _, _ = dec.generate(pages, N, K, check_every=1)
+    for rep in range(2):
+        g, _, _ = dec.generate(pages, N, K, check_every=2, graphs=True)
+        assert g.tolist() == eager.tolist(), rep
+    ar, _, _ = dec.generate(pages, N, 0, check_every=4)
+    assert eager.tolist() == ar.tolist()
+    slots = torch.arange(B, dtype=torch.int32, device="cuda")
+    a = _eager_steps(dec, pages, K, 6, None)
+    b = _eager_steps(dec, pages, K, 6, slots)
+    assert a == b
+    log(f"B={B} K={K}: graphs = eager = AR over {N} tokens; slot map 0..B-1 = identity")
