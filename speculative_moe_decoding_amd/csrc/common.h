@@ -78,6 +78,38 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Wavefront sum / max on the DPP paths, with no LDS round trip: within each
+// 16-lane row, lanes exchange by quad permutes (xor 1, xor 2), then the
+// half-row and row mirrors, so that every lane of a row holds the row's total
+// (each step adds x + y on one lane and y + x on its partner: the same bits);
+// the four row totals are then read into scalars and added in row order.
+// Every lane gets the same value, whatever the call shape.
+__device__ __forceinline__ float dpp_f(float v, int ctrl) {
+  switch (ctrl) {  // the DPP control must be a constant
+    case 0xB1: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+    case 0x4E: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+    case 0x141: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+    default: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
+  }
+}
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_f(v, 0xB1);   // quad_perm [1, 0, 3, 2]: lane xor 1
+  v += dpp_f(v, 0x4E);   // quad_perm [2, 3, 0, 1]: lane xor 2
+  v += dpp_f(v, 0x141);  // row_half_mirror: the other quad of the 8-lane half
+  v += dpp_f(v, 0x140);  // row_mirror: the other half of the row
+  return ((lane_f(v, 0) + lane_f(v, 16)) + lane_f(v, 32)) + lane_f(v, 48);
+}
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp_f(v, 0xB1));
+  v = fmaxf(v, dpp_f(v, 0x4E));
+  v = fmaxf(v, dpp_f(v, 0x141));
+  v = fmaxf(v, dpp_f(v, 0x140));
+  return fmaxf(fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), lane_f(v, 32)), lane_f(v, 48));
+}
+
 __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
 // Streaming (non-temporal) 16-byte load of weights that are read once per

@@ -82,11 +82,11 @@ __device__ __forceinline__ void attn_tile_query(const float4* __restrict__ qrow,
   }
   sc = sc * scale;
   const bool vis = (kt + lane) <= plim;
-  const float mt = wave_max(vis ? sc : -INFINITY);
+  const float mt = wave_max_dpp(vis ? sc : -INFINITY);
   const float mnew = fmaxf(mrun, mt);
   const float corr = expf(mrun - mnew);
   const float p = vis ? expf(sc - mnew) : 0.f;
-  lrun = lrun * corr + wave_sum(p);
+  lrun = lrun * corr + wave_sum_dpp(p);
   reinterpret_cast<float*>(pw)[lane] = p;
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
