@@ -5,7 +5,8 @@
 // bit):
 //   * dot products: lane l of a wavefront owns the 16-byte chunks l, l+64, ...
 //     of a weight row and accumulates them in order with fmaf; the 64 lane sums
-//     are then added by a fixed xor butterfly (32, 16, 8, 4, 2, 1);
+//     are then added by a fixed tree (wave_reduce_t: steps at offsets 32, 16,
+//     8, 4, 2, 1, exchanges in registers);
 //   * row reductions of 256-thread blocks (RMSNorm): each thread sums its
 //     elements k = tid + 256 j in order, then the same butterfly per wave, then
 //     the four wave sums in order 0..3;
@@ -298,13 +299,43 @@ struct WaveGemv {
   }
 };
 
+// Exchange with the partner lane of a reduction step at offset off, in
+// registers: off = 32 and 16 by the permlane swaps (partner l ^ off), 8 and 4
+// by the row and half-row mirrors (partner 15 - i / 7 - i within the 16 / 8
+// lanes), 2 and 1 by quad permutes (l ^ off).  At each step of a reduction
+// that goes 32, 16, 8, 4, 2, 1, the partner agrees with the lane on every bit
+// already reduced and differs in bit off, which is all a reduction needs.
+// All 64 lanes must be active.
+__device__ __forceinline__ float xchg(float x, int off) {
+  const int v = __builtin_bit_cast(int, x);
+  int r;
+  switch (off) {
+    case 32: {
+      const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+      r = (lane_id() < 32) ? p[1] : p[0];
+      break;
+    }
+    case 16: {
+      const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+      r = (lane_id() & 16) ? p[0] : p[1];
+      break;
+    }
+    case 8: r = __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false); break;  // row_mirror
+    case 4: r = __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false); break;  // row_half_mirror
+    case 2: r = __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false); break;   // quad_perm [2,3,0,1]
+    default: r = __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false); break;  // quad_perm [1,0,3,2]
+  }
+  return __builtin_bit_cast(float, r);
+}
+
 // Sums each of N (a power of two <= 64) per-lane values over the wavefront
-// with the tree of wave_sum (xor offsets 32, 16, ..., 1; at every node own +
-// partner), transposed: at each of the first log2 N steps a lane keeps half of
-// its values and trades the other half with its partner, so the wavefront
-// spends N - 1 + 6 - log2 N shuffles instead of 6 N.  The sums are bitwise
-// those of wave_sum.  Lane l returns the total of value i = l >> (6 - log2 N);
-// v is overwritten.
+// with a fixed tree (steps at offsets 32, 16, ..., 1, own + partner at every
+// node, partners as in xchg), transposed: at each of the first log2 N steps a
+// lane keeps half of its values -- the half its own bit at that offset
+// selects -- and trades the other half with its partner, so the wavefront
+// spends N - 1 + 6 - log2 N exchanges instead of 6 N, all in registers.  Lane
+// l returns the total of value i = l >> (6 - log2 N), and every lane holding
+// value i has the same bits; v is overwritten.
 template <int N>
 __device__ __forceinline__ float wave_reduce_t(float (&v)[N]) {
   static_assert(N >= 1 && N <= 64 && (N & (N - 1)) == 0, "N must be a power of two <= 64");
@@ -318,20 +349,20 @@ __device__ __forceinline__ float wave_reduce_t(float (&v)[N]) {
 #pragma unroll
     for (int j = 0; j < n / 2; ++j) {
       const float lo = v[j], hi = v[j + n / 2];
-      const float recv = __shfl_xor(up ? lo : hi, off, 64);
+      const float recv = xchg(up ? lo : hi, off);
       v[j] = (up ? hi : lo) + recv;
     }
   }
   float t = v[0];
 #pragma unroll
-  for (int off = 32 >> B; off >= 1; off >>= 1) t += __shfl_xor(t, off, 64);
+  for (int off = 32 >> B; off >= 1; off >>= 1) t += xchg(t, off);
   return t;
 }
 
 // Totals of a WaveGemv's lane partials acc[r][m] (R a power of two): lane l
 // receives the total of value i = l >> SH, i = m R + r, SH = 6 - log2(R MR),
-// through the transposed reduction (bitwise the per-value butterfly); `lead`
-// marks one lane per value.  All lanes construct it.
+// through the transposed reduction; `lead` marks one lane per value.  All
+// lanes construct it.
 template <int R, int MR>
 struct WaveTotals {
   static constexpr int N = R * MR;
