@@ -135,48 +135,6 @@ __device__ __forceinline__ float block_sum256(float v, float* red) {
   return t;
 }
 
-// Argmax stage 2 of one output row over the per-block bests rv[0..nblk),
-// ri[0..nblk) of the LM head (largest value, lowest id among equal ones: the
-// order of the comparisons does not matter), by a 256-thread block.  Each
-// thread loads AMG of them at a time, at indices clamped to the last block (a
-// repeat changes nothing), so the loads need no predicate and go out together.
-// `sv` / `si` are LDS scratch of 4 entries; two barriers inside; every thread
-// gets the id.
-constexpr int AMG = 8;
-__device__ __forceinline__ int argmax_block(const float* __restrict__ rv, const int* __restrict__ ri, int nblk,
-                                            float* sv, int* si) {
-  const int wave = wave_id(), lane = lane_id();
-  float v = -INFINITY;
-  int id = 0x7fffffff;
-  for (int b0 = 0; b0 < nblk; b0 += 256 * AMG) {
-    float pv[AMG];
-    int pi[AMG];
-#pragma unroll
-    for (int j = 0; j < AMG; ++j) {
-      const int b = min(b0 + (int)threadIdx.x + 256 * j, nblk - 1);
-      pv[j] = rv[b];
-      pi[j] = ri[b];
-    }
-#pragma unroll
-    for (int j = 0; j < AMG; ++j)
-      if (pv[j] > v || (pv[j] == v && pi[j] < id)) { v = pv[j]; id = pi[j]; }
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float ov = __shfl_xor(v, off, 64);
-    const int oi = __shfl_xor(id, off, 64);
-    if (ov > v || (ov == v && oi < id)) { v = ov; id = oi; }
-  }
-  if (lane == 0) { sv[wave] = v; si[wave] = id; }
-  __syncthreads();
-  v = sv[0];
-  id = si[0];
-#pragma unroll
-  for (int w = 1; w < 4; ++w)
-    if (sv[w] > v || (sv[w] == v && si[w] < id)) { v = sv[w]; id = si[w]; }
-  __syncthreads();
-  return id;
-}
 
 // RMSNorm of `m_rows` (<= MR) activation rows into LDS, by the block's four
 // wavefronts, one per row (rows w, w + 4, ...): lane l sums x[k]^2 over
@@ -306,8 +264,7 @@ struct WaveGemv {
 // that goes 32, 16, 8, 4, 2, 1, the partner agrees with the lane on every bit
 // already reduced and differs in bit off, which is all a reduction needs.
 // All 64 lanes must be active.
-__device__ __forceinline__ float xchg(float x, int off) {
-  const int v = __builtin_bit_cast(int, x);
+__device__ __forceinline__ int xchg_i(int v, int off) {
   int r;
   switch (off) {
     case 32: {
@@ -325,7 +282,10 @@ __device__ __forceinline__ float xchg(float x, int off) {
     case 2: r = __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false); break;   // quad_perm [2,3,0,1]
     default: r = __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false); break;  // quad_perm [1,0,3,2]
   }
-  return __builtin_bit_cast(float, r);
+  return r;
+}
+__device__ __forceinline__ float xchg(float x, int off) {
+  return __builtin_bit_cast(float, xchg_i(__builtin_bit_cast(int, x), off));
 }
 
 // Sums each of N (a power of two <= 64) per-lane values over the wavefront
@@ -357,6 +317,49 @@ __device__ __forceinline__ float wave_reduce_t(float (&v)[N]) {
 #pragma unroll
   for (int off = 32 >> B; off >= 1; off >>= 1) t += xchg(t, off);
   return t;
+}
+
+// Argmax stage 2 of one output row over the per-block bests rv[0..nblk),
+// ri[0..nblk) of the LM head (largest value, lowest id among equal ones: the
+// order of the comparisons does not matter), by a 256-thread block.  Each
+// thread loads AMG of them at a time, at indices clamped to the last block (a
+// repeat changes nothing), so the loads need no predicate and go out together.
+// `sv` / `si` are LDS scratch of 4 entries; two barriers inside; every thread
+// gets the id.
+constexpr int AMG = 8;
+__device__ __forceinline__ int argmax_block(const float* __restrict__ rv, const int* __restrict__ ri, int nblk,
+                                            float* sv, int* si) {
+  const int wave = wave_id(), lane = lane_id();
+  float v = -INFINITY;
+  int id = 0x7fffffff;
+  for (int b0 = 0; b0 < nblk; b0 += 256 * AMG) {
+    float pv[AMG];
+    int pi[AMG];
+#pragma unroll
+    for (int j = 0; j < AMG; ++j) {
+      const int b = min(b0 + (int)threadIdx.x + 256 * j, nblk - 1);
+      pv[j] = rv[b];
+      pi[j] = ri[b];
+    }
+#pragma unroll
+    for (int j = 0; j < AMG; ++j)
+      if (pv[j] > v || (pv[j] == v && pi[j] < id)) { v = pv[j]; id = pi[j]; }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {  // any pairing gives the same result
+    const float ov = xchg(v, off);
+    const int oi = xchg_i(id, off);
+    if (ov > v || (ov == v && oi < id)) { v = ov; id = oi; }
+  }
+  if (lane == 0) { sv[wave] = v; si[wave] = id; }
+  __syncthreads();
+  v = sv[0];
+  id = si[0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w)
+    if (sv[w] > v || (sv[w] == v && si[w] < id)) { v = sv[w]; id = si[w]; }
+  __syncthreads();
+  return id;
 }
 
 // Totals of a WaveGemv's lane partials acc[r][m] (R a power of two): lane l

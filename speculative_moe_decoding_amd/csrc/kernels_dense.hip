@@ -271,11 +271,13 @@ __global__ __launch_bounds__(256) void k_lmhead(const float* __restrict__ x, con
       if (logits != nullptr && tot.lead) logits[(long)(m0 + tot.m) * V + v] = tot.val;
     }
   }
-  // best over the four tile rows of each m (lanes differing in the bits of r)
+  // best over the four tile rows of each m: exchanges at offsets 2^SH and
+  // 2^(SH+1) (a mirror partner may sit at r ^ 3 rather than r ^ 2 in the second
+  // step, which is still the other pair of rows of the same m)
 #pragma unroll
   for (int off = 1 << SH; off <= 2 << SH; off <<= 1) {
-    const float ob = __shfl_xor(best, off, 64);
-    const int oi = __shfl_xor(besti, off, 64);
+    const float ob = xchg(best, off);
+    const int oi = xchg_i(besti, off);
     if (ob > best || (ob == best && oi < besti)) { best = ob; besti = oi; }
   }
   {

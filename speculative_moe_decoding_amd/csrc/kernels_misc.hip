@@ -382,9 +382,9 @@ __device__ __forceinline__ int argmax_wave(const float* __restrict__ rv, const i
       if (pv[j] > v || (pv[j] == v && pi[j] < id)) { v = pv[j]; id = pi[j]; }
   }
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float ov = __shfl_xor(v, off, 64);
-    const int oi = __shfl_xor(id, off, 64);
+  for (int off = 32; off >= 1; off >>= 1) {  // any pairing gives the same result
+    const float ov = xchg(v, off);
+    const int oi = xchg_i(id, off);
     if (ov > v || (ov == v && oi < id)) { v = ov; id = oi; }
   }
   return id;
