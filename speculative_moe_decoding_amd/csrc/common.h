@@ -67,15 +67,50 @@ template <> struct WT<bf16> {
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
+// The value of lane l ^ off (off a power of two <= 32), in registers:
+// permlane swaps at 32 and 16, a pair of DPP row shifts and a select at 8 and
+// 4, quad permutes at 2 and 1 (lane layouts checked on the GPU).  The same
+// result as __shfl_xor(v, off) without the LDS round trip; all 64 lanes must
+// be active.
+__device__ __forceinline__ int xor_lane_i(int v, int off) {
+  switch (off) {
+    case 32: {
+      const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+      return (lane_id() < 32) ? p[1] : p[0];
+    }
+    case 16: {
+      const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+      return (lane_id() & 16) ? p[0] : p[1];
+    }
+    case 8: {
+      const int up = __builtin_amdgcn_update_dpp(0, v, 0x108, 0xF, 0xF, false);  // row_shl:8 (lane + 8)
+      const int dn = __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8 (lane - 8)
+      return (lane_id() & 8) ? dn : up;
+    }
+    case 4: {
+      const int up = __builtin_amdgcn_update_dpp(0, v, 0x104, 0xF, 0xF, false);  // row_shl:4
+      const int dn = __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+      return (lane_id() & 4) ? dn : up;
+    }
+    case 2: return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+    default: return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+  }
+}
+__device__ __forceinline__ float xor_lane(float x, int off) {
+  return __builtin_bit_cast(float, xor_lane_i(__builtin_bit_cast(int, x), off));
+}
+
+// Xor butterfly over the wavefront (offsets 32, 16, ..., 1, own + partner at
+// every node): every lane gets the same bits.  All 64 lanes must be active.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  for (int off = 32; off >= 1; off >>= 1) v += xor_lane(v, off);
   return v;
 }
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, xor_lane(v, off));
   return v;
 }
 
@@ -387,8 +422,9 @@ struct WaveTotals {
     m = i / R;
     lead = (lane & ((1 << SH) - 1)) == 0;
   }
-  // The total of (r ^ x, m), from the lane that holds it; all lanes call it.
-  __device__ __forceinline__ float partner(int x) const { return __shfl_xor(val, x << SH, 64); }
+  // The total of (r ^ x, m), from the lane that holds it (x << SH a power of
+  // two); all lanes call it.
+  __device__ __forceinline__ float partner(int x) const { return xor_lane(val, x << SH); }
 };
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
