@@ -436,7 +436,7 @@ __global__ __launch_bounds__(256) void k_accept(int K, const int* __restrict__ p
     const int ol0 = sv.out_len[slot];
     const uint64_t miss = __ballot(!(lane < K && dv == gv));
     const int n = __builtin_ctzll(miss);  // <= K
-    const int gn = __shfl(gv, n, 64);
+    const int gn = __builtin_amdgcn_readlane(gv, n);  // n is the same on every lane
     if (lane <= n) {
       const int t = (lane < n) ? dv : gn;
       sv.cu_tok[slot * sv.cu_stride + lane] = t;

@@ -41,14 +41,18 @@ __device__ __forceinline__ void sort_pairs_wave(int P, RouteLds& r) {
   const int rank = valid ? __popcll(same & lt) : 0;
   if (valid && rank == 0) r.cnt[e] = __popcll(same);
   const int c = r.cnt[lane];
+  // inclusive scan of the counts: within each 16-lane row by DPP row shifts
+  // (lanes past the row's start read 0), then the row totals as scalars
   int incl = c;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int o = __shfl_up(incl, d, 64);
-    if (lane >= d) incl += o;
-  }
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x111, 0xF, 0xF, false);  // row_shr:1
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x112, 0xF, 0xF, false);  // row_shr:2
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x114, 0xF, 0xF, false);  // row_shr:4
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x118, 0xF, 0xF, false);  // row_shr:8
+  const int t0 = __builtin_amdgcn_readlane(incl, 15), t1 = __builtin_amdgcn_readlane(incl, 31);
+  const int t2 = __builtin_amdgcn_readlane(incl, 47), t3 = __builtin_amdgcn_readlane(incl, 63);
+  incl += (lane >= 16 ? t0 : 0) + (lane >= 32 ? t1 : 0) + (lane >= 48 ? t2 : 0);
   r.off[lane] = incl - c;
-  const int routed = __shfl(incl, 63, 64);
+  const int routed = t0 + t1 + t2 + t3;
   const uint64_t amask = __ballot(c > 0);
   if (c > 0) r.act[__popcll(amask & lt)] = lane;
   int na = __popcll(amask);
