@@ -291,15 +291,19 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
   };
   bool ok;
   float r;
-  if (n_chunks <= MERGE_ONE) {
-    // one batch of loads, issued with the plan reads (their addresses do not
-    // depend on it); chunks past nc unused
-    float mv[MERGE_ONE], lv[MERGE_ONE], ov[MERGE_ONE];
-    merge_load<MERGE_ONE>(pp, cstride, 0, n_chunks, d, mv, lv, ov);
-    r = merge_regs<MERGE_ONE>(mv, lv, ov, plan_nc(ok));
-  } else {
-    r = merge_loop(pp, cstride, plan_nc(ok), d);
-  }
+  // one batch of loads (as many as the launch's chunk count needs), issued
+  // with the plan reads (their addresses do not depend on it); chunks past nc
+  // unused.  Any batch size >= nc gives the same bits.
+  auto merge_one = [&](auto g) {
+    constexpr int G = decltype(g)::value;
+    float mv[G], lv[G], ov[G];
+    merge_load<G>(pp, cstride, 0, n_chunks, d, mv, lv, ov);
+    return merge_regs<G>(mv, lv, ov, plan_nc(ok));
+  };
+  if (n_chunks <= 8) r = merge_one(std::integral_constant<int, 8>{});
+  else if (n_chunks <= 16) r = merge_one(std::integral_constant<int, 16>{});
+  else if (n_chunks <= MERGE_ONE) r = merge_one(std::integral_constant<int, MERGE_ONE>{});
+  else r = merge_loop(pp, cstride, plan_nc(ok), d);
   *o = ok ? r : 0.f;
 }
 
