@@ -72,18 +72,12 @@ __device__ __forceinline__ void norm_row(const float* __restrict__ src, const fl
 
 // Draft fusion input of one row: [RMSNorm(h; g_h), RMSNorm(e; g_e)], e = E[tok]
 // (the arithmetic of norm_row; both rows' loads issued together).
-template <typename T>
-__device__ __forceinline__ void draft_cat_row(const float* __restrict__ h, int tok, const T* __restrict__ E,
-                                              const float* __restrict__ g_h, const float* __restrict__ g_e,
-                                              float eps, float* __restrict__ cat, float* red) {
+// cat from the two rows' values already in registers (vh[j], ve[j]: element
+// threadIdx.x + 256 j)
+__device__ __forceinline__ void draft_cat_regs(const float (&vh)[D / 256], const float (&ve)[D / 256],
+                                               const float* __restrict__ g_h, const float* __restrict__ g_e,
+                                               float eps, float* __restrict__ cat, float* red) {
   constexpr int J = D / 256;
-  const T* er = E + (long)tok * D;
-  float vh[J], ve[J];
-#pragma unroll
-  for (int j = 0; j < J; ++j) {
-    vh[j] = h[threadIdx.x + 256 * j];
-    ve[j] = WT<T>::load1(er + threadIdx.x + 256 * j);
-  }
   float sh = 0.f, se = 0.f;
 #pragma unroll
   for (int j = 0; j < J; ++j) {
@@ -99,6 +93,20 @@ __device__ __forceinline__ void draft_cat_row(const float* __restrict__ h, int t
     cat[k] = (vh[j] * rh) * g_h[k];
     cat[D + k] = (ve[j] * re) * g_e[k];
   }
+}
+template <typename T>
+__device__ __forceinline__ void draft_cat_row(const float* __restrict__ h, int tok, const T* __restrict__ E,
+                                              const float* __restrict__ g_h, const float* __restrict__ g_e,
+                                              float eps, float* __restrict__ cat, float* red) {
+  constexpr int J = D / 256;
+  const T* er = E + (long)tok * D;
+  float vh[J], ve[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    vh[j] = h[threadIdx.x + 256 * j];
+    ve[j] = WT<T>::load1(er + threadIdx.x + 256 * j);
+  }
+  draft_cat_regs(vh, ve, g_h, g_e, eps, cat, red);
 }
 
 // Catch-up pass: sequence b has cnt = n_prev + 1 valid rows at positions
@@ -208,11 +216,9 @@ __global__ __launch_bounds__(256) void k_draft_fuse(DraftIn<T> a, const T* __res
   WaveGemv<T, K2, R, MR> g;
   g.load(rows);
   const bool writer = blockIdx.x == 0 && threadIdx.x == 0;
-  for (int m = 0; m < m_act; ++m) {
-    const int r = m0 + m;
-    float* c = xs + m * K2;
-    if (a.step) {
-      const int b = r;
+  if (a.step) {
+    for (int m = 0; m < m_act; ++m) {
+      const int b = m0 + m;
       const int slot = a.plan_slot[b];
       const int pc = (a.Qprev == 1) ? 1 : max(1, min(a.sv.n_prev[slot] + 1, a.Qprev));
       const float* h = a.u_prev + (long)(b * a.Qprev + pc - 1) * D;
@@ -222,20 +228,48 @@ __global__ __launch_bounds__(256) void k_draft_fuse(DraftIn<T> a, const T* __res
         a.plan_base[b] = a.sv.kv_len[slot] + a.j - 1;
         a.plan_cnt[b] = 1;
       }
-      draft_cat_row(h, clamp_tok(id, a.V), a.E, a.g_h, a.g_e, a.eps, c, red);
-    } else {
-      const int b = r / a.Q, i = r - b * a.Q;
-      const int slot = clamp_slot(a.slots_in ? a.slots_in[b] : b, a.sv.n_slots);
-      const int cnt = max(1, min(a.sv.n_prev[slot] + 1, a.Q));
-      if (writer && i == 0) {
-        a.plan_slot[b] = slot;
-        a.plan_base[b] = a.sv.draft_len[slot];
-        a.plan_cnt[b] = cnt;
+      draft_cat_row(h, clamp_tok(id, a.V), a.E, a.g_h, a.g_e, a.eps, xs + m * K2, red);
+    }
+  } else {
+    // catch-up: every row's plan reads, then its token and hidden row, then its
+    // embedding row go out for all rows before the first reduction (row
+    // indices clamped into range; rows past cnt are zeroed, not built)
+    constexpr int J = D / 256;
+    int sl[MR], ii[MR], cn[MR], tk[MR];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      const int r = m0 + min(m, m_act - 1);
+      const int b = r / a.Q;
+      ii[m] = r - b * a.Q;
+      sl[m] = clamp_slot(a.slots_in ? a.slots_in[b] : b, a.sv.n_slots);
+      cn[m] = max(1, min(a.sv.n_prev[sl[m]] + 1, a.Q));
+      if (writer && m < m_act && ii[m] == 0) {
+        a.plan_slot[b] = sl[m];
+        a.plan_base[b] = a.sv.draft_len[sl[m]];
+        a.plan_cnt[b] = cn[m];
       }
-      if (i < cnt) {
-        const float* h = a.sv.hbuf + ((long)slot * a.sv.cu_stride + i) * D;
-        const int tok = clamp_tok(a.sv.cu_tok[slot * a.sv.cu_stride + i], a.V);
-        draft_cat_row(h, tok, a.E, a.g_h, a.g_e, a.eps, c, red);
+    }
+    float vh[MR][J], ve[MR][J];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      const long e = (long)sl[m] * a.sv.cu_stride + min(ii[m], cn[m] - 1);
+      tk[m] = clamp_tok(a.sv.cu_tok[e], a.V);
+      const float* h = a.sv.hbuf + e * D;
+#pragma unroll
+      for (int j = 0; j < J; ++j) vh[m][j] = h[threadIdx.x + 256 * j];
+    }
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      const T* er = a.E + (long)tk[m] * D;
+#pragma unroll
+      for (int j = 0; j < J; ++j) ve[m][j] = WT<T>::load1(er + threadIdx.x + 256 * j);
+    }
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      if (m >= m_act) break;
+      float* c = xs + m * K2;
+      if (ii[m] < cn[m]) {
+        draft_cat_regs(vh[m], ve[m], a.g_h, a.g_e, a.eps, c, red);
       } else {
         for (int k = threadIdx.x; k < K2; k += 256) c[k] = 0.f;
       }
