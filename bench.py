@@ -155,6 +155,8 @@ def main() -> int:
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 512 MiB device copy (calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
+    if args.instrumented_steps < 1 or args.replay_rounds < 1 or args.replay_routings < 1:
+        ap.error("--instrumented-steps, --replay-rounds and --replay-routings must be at least 1")
     if args.copy_probe:
         import torch
         a = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
