@@ -14,7 +14,11 @@ One step = draft (3 passes) + controlled override + verify (4 rows through
 12 MoE layers + LM head) + accept.  The default 405 steps are the 1,085 output
 tokens of one page (the pages' mean tokens per page).
 
-Prints one JSON line (stdout).  `value` = output tokens / s of the timed steps.
+Prints one JSON line (stdout).  `value` = output tokens / s at the workload's
+acceptance: tau = 1 + K alpha (alpha = 57.6 %) tokens per step over the measured
+time per step (a step does the same work whatever it accepts).  The timed
+window's own tau and tokens / s are reported beside it (`window`): over a short
+window the controlled drafts' realised acceptance wanders around the target.
 """
 from __future__ import annotations
 
@@ -69,13 +73,14 @@ def load_traffic():
     return None if t is None or not a else (t, t / a)
 
 
-def cpu_baseline(w, page, K, p, seed, n_prefix_vision=32, n_prompt=32, n_trace=12, n_steps=6):
-    """The oracle, as it stands, on a bounded sample of the same workload."""
+def cpu_baseline(w, page, K, p, seed, n_trace=12, n_steps=6):
+    """The oracle, as it stands, on a bounded sample of the same workload: the
+    page's whole 288-row prefix, then n_steps speculative steps."""
     import numpy as np
     from oracle import decoder as od
     orc = od.Oracle(w.cfg, w.f32)
-    vis = page.vision[:n_prefix_vision]
-    prm = page.prompt[:n_prompt]
+    vis = page.vision
+    prm = page.prompt
     t0 = time.time()
     trace, _ = orc.generate_ar(vis, prm, n_trace + K + 2)
     t1 = time.time()
@@ -98,9 +103,9 @@ def cpu_baseline(w, page, K, p, seed, n_prefix_vision=32, n_prompt=32, n_trace=1
     threads = int(os.environ.get("OMP_NUM_THREADS", cores))
     return dict(value=committed / t_steps, unit="tokens/s", cores=min(cores, threads), kind="oracle",
                 sample=(f"fp64 NumPy oracle, same 12-layer bf16 weights, {len(steps)} speculative steps "
-                        f"(K={K}, draft block run for cost, controlled drafts p={p:.4f}) after a "
-                        f"{vis.shape[0]}+{len(prm)}-row prefix (not the 288-row one, to bound the "
-                        f"prefill); {committed} tokens in {t_steps:.1f}s; AR trace {t1 - t0:.1f}s untimed"))
+                        f"(K={K}, draft block run for cost, controlled drafts p={p:.4f}) after the page's "
+                        f"{vis.shape[0]}+{len(prm)}-row prefix; {committed} tokens in {t_steps:.1f}s "
+                        f"(prefill {t_prefill:.1f}s untimed); AR trace {t1 - t0:.1f}s untimed"))
 
 
 def plain_read(dec, nbytes, n_launches, n_regions=L):
@@ -261,10 +266,12 @@ def main() -> int:
     committed = int(out_len.item()) - 1
     got = out_tokens[0, :committed + 1].cpu().numpy()
     lossless = bool(np.array_equal(got, ar[0][:committed + 1]))
-    tok_s = committed / elapsed
+    win_tok_s = committed / elapsed
     tau = (committed) / S
-    log(f"timed: {S} steps, {committed} tokens in {elapsed * 1e3:.1f} ms -> {tok_s:.1f} tok/s, tau {tau:.3f}, "
-        f"lossless {lossless}")
+    tau_target = 1.0 + K * args.alpha
+    tok_s = tau_target * S / elapsed        # at the workload's acceptance
+    log(f"timed: {S} steps, {committed} tokens in {elapsed * 1e3:.1f} ms -> {win_tok_s:.1f} tok/s at the window's "
+        f"tau {tau:.3f}; {tok_s:.1f} tok/s at tau {tau_target:.3f}; lossless {lossless}")
 
     # instrumented pass: events around draft / verify, per-launch events around the expert kernels
     Si = min(args.instrumented_steps, S)
@@ -373,8 +380,10 @@ def main() -> int:
             "plain_read_same_bytes": plain,
             "frac_of_plain_read": round(achieved / plain["GB_per_s"], 4),
         },
-        "tau": round(tau, 4),
-        "alpha": round((tau - 1) / K, 4),
+        "tau": round(tau_target, 4),
+        "alpha": args.alpha,
+        "window": {"tau": round(tau, 4), "alpha": round((tau - 1) / K, 4), "tokens": committed,
+                   "tok_per_s": round(win_tok_s, 2)},
         "lossless_vs_ar": lossless,
         "pages_per_s": round(1.0 / (t_prefill + 1085 / tok_s), 4),
         "prefill_ms": round(t_prefill * 1e3, 2),

@@ -97,71 +97,88 @@ int ocrdec_create(const ocrdec_config* cfg, const void* const* weight_ptrs, int 
                   void* state, void* workspace, void* stream, ocrdec_model** out);
 int ocrdec_destroy(ocrdec_model* m);
 
-/* Prefill B sequences (host arrays slots_host, n_vision_host, n_prompt_host):
- * rows 0..Nv-1 are the vision rows vision[b] (device fp32 [B][nv_stride][d]),
- * rows Nv..Nv+Np-1 the embeddings of prompt[b] (device int32 [B][np_stride]).
+/* Prefill B sequences (host arrays slots_host, n_vision_host, n_prompt_host).
+ * The blog's "Model and training" section (architecture figure caption and
+ * spec table) puts a page's visual tokens -- 256 for the global 1024x1024
+ * view plus 100 per local tile, at most 1,156 -- in front of the decoder; here
+ * they are the rows of the prefix.  Rows 0..Nv-1 are the vision rows
+ * vision[b] (device fp32 [B][nv_stride][d]), rows Nv..Nv+Np-1 the embeddings
+ * of prompt[b] (device int32 [B][np_stride]), at positions 0..Nv+Np-1.
  * Runs the verifier over the prefix (filling its KV cache), the draft block over
  * the same rows (filling the draft KV cache; draft row p takes the verifier
  * hidden of p-1), and writes the greedy token of the last prefix row -- output
  * token 0 -- to pending_out[b] (device int32 [B]).  After the call the slot's
- * committed-output count is 1.  OCRDEC_ECAPACITY if Nv+Np+max_k+1 > max_positions. */
+ * committed-output count is 1.  slots_host may be NULL (slots 0..B-1); slots
+ * must be distinct and < max_batch.  Errors: OCRDEC_EINVAL for a null or
+ * inconsistent argument or an empty prefix, OCRDEC_ECAPACITY if
+ * Nv+Np+max_k+1 > max_positions (nothing is enqueued). */
 int ocrdec_prefill(ocrdec_model* m, void* stream, int B, const int32_t* slots_host,
                    const float* vision, int nv_stride, const int32_t* n_vision_host,
                    const int32_t* prompt, int np_stride, const int32_t* n_prompt_host,
                    int32_t* pending_out);
 
-/* FastMTP draft (the pages' "one shared dense block applied recursively for K
- * steps"): pass 1 recomputes the rows accepted at the last verify plus the
- * pending token from the verifier's hidden states (catch-up) and proposes d_1;
- * passes 2..K feed the block's own output back.  draft_out: device int32 [B][K]. */
+/* FastMTP draft.  The blog's "Model and training" section (and the spec
+ * table's MTP head row) describes one shared dense block applied recursively
+ * for K steps, so draft parameters do not grow with depth; its "Getting
+ * started" section says the head was trained with recursive hidden-state
+ * feedback (an EAGLE-style proposer).  Pass 1 recomputes the rows accepted at
+ * the last verify plus the pending token from the verifier's hidden states
+ * (catch-up) and proposes d_1; passes 2..K feed the block's own output back.
+ * draft_out: device int32 [B][K], written in full.  1 <= K <= max_k.
+ * Errors: OCRDEC_EINVAL (null draft_out, K < 1), OCRDEC_ECAPACITY (B or K
+ * above the handle's capacity, or -- without a slot map -- positions past
+ * max_positions). */
 int ocrdec_draft(ocrdec_model* m, void* stream, int B, const int32_t* slots, int K, int32_t* draft_out);
 
-/* Verifier pass over rows [pending, d_1..d_K] of each sequence at positions
- * kv_len..kv_len+K through all layers; writes their keys/values to the cache and
- * the greedy token of every row to greedy_out (device int32 [B][K+1]).
- * logits_out (nullable, device fp32 [B][K+1][vocab]) receives the final logits.
- * K = 0 is plain autoregressive decoding (draft ignored, may be NULL). */
+/* Greedy verification, as the blog's "Model and training" section describes
+ * it: the verifier checks every proposal greedily in one pass.  Rows
+ * [pending, d_1..d_K] of each sequence at positions kv_len..kv_len+K go
+ * through all layers; their keys/values are written to the cache and the
+ * greedy token (argmax, lowest id on ties) of every row to greedy_out (device
+ * int32 [B][K+1]).  logits_out (nullable, device fp32 [B][K+1][vocab])
+ * receives the final logits.  K = 0 is plain autoregressive decoding (draft
+ * ignored, may be NULL).  A sequence whose rows would pass max_positions is
+ * not computed: its overflow flag is set (reported by ocrdec_sync_positions)
+ * and the accept that follows leaves it unchanged.  Errors: OCRDEC_EINVAL
+ * (null greedy_out, null draft with K > 0), OCRDEC_ECAPACITY (B or K above
+ * capacity; without a slot map, positions past max_positions). */
 int ocrdec_verify(ocrdec_model* m, void* stream, int B, const int32_t* slots, int K,
                   const int32_t* draft, int32_t* greedy_out, float* logits_out);
 
-/* Greedy longest-prefix acceptance (blog, "Model and training") with KV
- * rollback: n = the longest j <= K with d_i == g_{i-1} for all i <= j; commits
- * d_1..d_n and the bonus token g_n; the verifier cache keeps positions up to the
- * last committed token, rejected positions are dropped by a length update (no
- * data moves).  Writes n to n_accepted_out[b] (device int32 [B]) and appends the
- * n+1 tokens to out_tokens[b][out_len..] (device int32 [B][out_cap], tokens at
- * index >= out_cap are dropped); out_len (device int32 [B], nullable) receives
- * the new committed count (including output token 0 from the prefill). */
+/* Greedy longest-prefix acceptance (blog, "Model and training": the longest
+ * prefix on which draft and verifier agree is kept, so the committed sequence
+ * is the verifier's greedy sequence; the "Speculative decoding on L4" table
+ * caption counts the verifier's bonus token in tau) with KV rollback: n = the
+ * longest j <= K with d_i == g_{i-1} for all i <= j; commits d_1..d_n and the
+ * bonus token g_n; the verifier cache keeps positions up to the last committed
+ * token, rejected positions are dropped by a length update (no data moves).
+ * Writes n to n_accepted_out[b] (device int32 [B]; -1 for a sequence the
+ * verify did not compute because of max_positions, which is left unchanged)
+ * and appends the n+1 tokens to out_tokens[b][out_len..] (device int32
+ * [B][out_cap], tokens at index >= out_cap are dropped); out_len (device int32
+ * [B], nullable) receives the new committed count (including output token 0
+ * from the prefill).  It must directly follow the ocrdec_verify whose rows it
+ * accepts, with the same B, K and slots pointer (else OCRDEC_EINVAL, nothing
+ * enqueued); each verify is accepted at most once. */
 int ocrdec_accept_rollback(ocrdec_model* m, void* stream, int B, const int32_t* slots, int K,
                            const int32_t* draft, const int32_t* greedy, int32_t* n_accepted_out,
                            int32_t* out_tokens, int32_t* out_len, int out_cap);
 
-/* Benchmark harness (not part of the method): overwrite draft[b][j-1] with the
- * token a lossless run commits at that place, trace[b][out_len-1+j] (device
- * int32 [B][trace_stride], ids past trace_len read as 0), replaced -- when the
- * top 53 bits of H = SplitMix64-chain(seed, b_index, step, j) fall below
- * `threshold` -- by (true + 1 + (H mod 2^32) mod (vocab-1)) mod vocab, which is
- * never the true token.  b_index is the sequence's slot. */
-int ocrdec_controlled_drafts(ocrdec_model* m, void* stream, int B, const int32_t* slots, int K,
-                             const int32_t* trace, int trace_stride, int trace_len,
-                             uint64_t seed, uint64_t threshold, int32_t* draft_inout);
+/* Controlled-draft parameters of ocrdec_decode_steps (benchmark harness;
+ * defined in ocrdec_harness.h). */
+typedef struct ocrdec_controlled_cfg ocrdec_controlled_cfg;
 
-/* Controlled-draft parameters for ocrdec_decode_steps (see
- * ocrdec_controlled_drafts). */
-typedef struct {
-  const int32_t* trace;
-  int trace_stride, trace_len;
-  uint64_t seed, threshold;
-} ocrdec_controlled_cfg;
-
-/* n_steps speculative steps of the B sequences: per step ocrdec_draft (K >= 1),
- * the controlled override when ctrl is non-null (K >= 1), ocrdec_verify and
- * ocrdec_accept_rollback, with the same results as issuing those calls one by
- * one (K = 0: plain autoregressive steps, draft may be NULL).  Each step is recorded once per call shape as a HIP graph (on a
- * library-private capture stream) and replayed on `stream`; the graphs are
- * cached in the handle.  draft (device int32 [B][K]) and greedy ([B][K+1]) are
- * caller scratch; n_accepted / out_tokens / out_len as in
- * ocrdec_accept_rollback (values of the last step). */
+/* Whole speculative steps replayed as HIP graphs (the pages' CUDA-graph mode:
+ * announcement and blog L4 tables, "Graph" rows).  n_steps steps of the B
+ * sequences: per step ocrdec_draft (K >= 1), the controlled override when ctrl
+ * is non-null (K >= 1; harness), ocrdec_verify and ocrdec_accept_rollback,
+ * with the same results as issuing those calls one by one (K = 0: plain
+ * autoregressive steps, draft may be NULL).  Each step is recorded once per
+ * call shape as a HIP graph (on a library-private capture stream) and
+ * replayed on `stream`; the graphs are cached in the handle.  draft (device
+ * int32 [B][K]) and greedy ([B][K+1]) are caller scratch; n_accepted /
+ * out_tokens / out_len as in ocrdec_accept_rollback (values of the last
+ * step). */
 int ocrdec_decode_steps(ocrdec_model* m, void* stream, int B, const int32_t* slots, int K, int n_steps,
                         const ocrdec_controlled_cfg* ctrl, int32_t* draft, int32_t* greedy,
                         int32_t* n_accepted_out, int32_t* out_tokens, int32_t* out_len, int out_cap);
@@ -170,59 +187,11 @@ int ocrdec_decode_steps(ocrdec_model* m, void* stream, int B, const int32_t* slo
  * step commits K + 1 tokens (an upper bound that sizes the attention grids and
  * the OCRDEC_ECAPACITY checks).  This call synchronises `stream` and resets the
  * bound of every slot to its true cache length, so long generations are not
- * refused early.  Returns OCRDEC_EHIP if the read fails. */
+ * refused early.  It returns OCRDEC_ECAPACITY (naming the slots) if, since the
+ * last call, a step of some sequence was not taken because it would have
+ * passed max_positions (the flags are then cleared; the bounds are still
+ * updated), and OCRDEC_EHIP if the read fails. */
 int ocrdec_sync_positions(ocrdec_model* m, void* stream);
-
-/* Long-context benchmark harness (not part of the method).
- * ocrdec_load_sequence: fill slot `slot` with a caller-made verifier cache of
- * n_pos positions -- kv: device, model dtype, [n_layers][K|V][head][n_pos][128]
- * (keys already rotated) -- and make pending_token the token at position
- * n_pos, as a prefill would (the draft cache is not filled).  Errors:
- * OCRDEC_EINVAL for a bad slot / token / null pointer, OCRDEC_ECAPACITY if
- * n_pos + max_k + 1 > max_positions.
- * ocrdec_set_router_logits: later verify calls take each layer's router logits
- * from logits (device fp32 [n_layers][rows][64], rows = B*(K+1) of the call;
- * the caller keeps it alive) instead of the router weights; NULL restores the
- * router. */
-int ocrdec_load_sequence(ocrdec_model* m, void* stream, int slot, int n_pos, int pending_token, const void* kv);
-int ocrdec_set_router_logits(ocrdec_model* m, const float* logits);
-
-/* Parity taps (nullable device pointers, used by later verify/prefill calls):
- * route_idx int32 [n_layers][rows][8] receives each layer's routing (6 routed
- * experts by decreasing score, then the shared experts 64, 65); hidden fp32
- * [rows][d] receives the final pre-norm hidden rows of the last verify. */
-int ocrdec_set_taps(ocrdec_model* m, int32_t* route_idx, float* hidden);
-
-/* Kernel timing of the grouped expert GEMV (gate/up and down launches):
- * enable != 0 records HIP events around each launch from now on (clears the
- * totals).  ocrdec_expert_stats synchronises those events and returns the
- * total milliseconds and launch count of each of the two kernels, and the
- * number of (layer, expert) weight sets they streamed since timing was enabled,
- * counted on the device. */
-int ocrdec_expert_timing(ocrdec_model* m, int enable);  /* synchronises the device */
-int ocrdec_expert_stats(ocrdec_model* m, double* ms_gate_up, long long* n_gate_up, double* ms_down,
-                        long long* n_down, long long* expert_sets);
-
-/* Benchmark harness: replay the grouped expert gate/up GEMV n_rounds times over
- * the weights of every layer in turn (n_rounds * n_layers back-to-back launches
- * on `stream`), with the routing of the last verify call, so that a pair of
- * events around the call times the kernel alone.  If expert_sets_per_launch
- * (host, nullable) is given, the call first synchronises the stream and stores
- * that routing's active-expert count there. */
-int ocrdec_replay_expert_gate_up(ocrdec_model* m, void* stream, int n_rounds, int* expert_sets_per_launch);
-
-/* Calibration (not part of the method): n_launches back-to-back launches on
- * `stream` of a kernel that only reads `bytes` bytes (16-byte loads, 4,096
- * workgroups) and writes nothing but, in practice never, one word to sink
- * (device, >= 4 bytes).  Launch i reads region i mod n_regions of the device
- * buffer buf, which holds n_regions consecutive regions of `bytes` bytes: with
- * as many regions as a replay has layers, the reads do not hit the GPU's
- * last-level cache any more than the replayed kernel's do.  A pair of events
- * around the call gives the rate a plain streaming kernel reaches at that size,
- * the practical ceiling for the bandwidth-bound kernels above.  OCRDEC_EINVAL
- * if buf or sink is null, bytes < 16 or not a multiple of 256, n_regions < 1 or
- * n_launches < 0. */
-int ocrdec_read_probe(void* stream, const void* buf, size_t bytes, int n_regions, int n_launches, uint32_t* sink);
 
 const char* ocrdec_last_error(void);
 

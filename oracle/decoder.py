@@ -150,17 +150,25 @@ def swiglu(b: np.ndarray, W_g: np.ndarray, W_u: np.ndarray, W_d: np.ndarray) -> 
     return linear(silu(linear(b, W_g)) * linear(b, W_u), W_d)
 
 
-def moe(b: np.ndarray, W_r, W_g, W_u, W_d, n_experts: int, n_shared: int, top_k: int, router_logits=None):
+def moe(b: np.ndarray, W_r, W_g, W_u, W_d, n_experts: int, n_shared: int, top_k: int, router_logits=None,
+        pick=None):
     """y = sum_shared F_s(b) + sum_{j<k} gate_j F_{idx_j}(b).
 
     Expert tensors hold the routed experts first, then the shared ones.  With
     router_logits [T, E] given, the routing is taken from them instead of W_r b
-    (the long-context benchmark's synthetic skewed routing)."""
+    (the long-context benchmark's synthetic skewed routing).  pick (optional)
+    is called as pick(logits [T, E], idx [T, k]) and returns the selection to
+    use (a parity harness that follows another implementation's choice at a
+    near tie); the gates stay the softmax probabilities of the experts used."""
     b = np.asarray(b, F64)
     if router_logits is None:
-        idx, gate, _ = route(b, W_r, top_k)
+        logits = linear(b, W_r)
     else:
-        idx, gate = route_logits(router_logits, top_k)
+        logits = np.asarray(router_logits, F64)
+    idx, gate = route_logits(logits, top_k)
+    if pick is not None:
+        idx = np.asarray(pick(logits, idx), dtype=np.int64)
+        gate = np.take_along_axis(softmax(logits), idx, axis=-1)
     y = np.zeros_like(b)
     for s in range(n_shared):
         e = n_experts + s
@@ -185,6 +193,9 @@ def greedy(logits: np.ndarray) -> np.ndarray:
 
 
 def top2_margin(logits: np.ndarray) -> np.ndarray:
+    """Largest minus second-largest logit along the last axis (0 at a tie of
+    the two largest): the gap a rounding difference must close to change the
+    greedy token, so token mismatches are excused only where it is small."""
     lf = np.sort(np.asarray(logits, F64), axis=-1)
     return lf[..., -1] - lf[..., -2]
 
@@ -239,6 +250,7 @@ class StepRecord:
     accepted: int               # n
     logits: Optional[np.ndarray] = None   # [K+1, V] verifier logits (kept on request)
     draft_margins: Optional[List[float]] = None   # top-2 margin of each draft pass's logits
+    real_drafts: Optional[List[int]] = None       # the draft block's proposals (also when a proposer replaced them)
 
 
 class Oracle:
@@ -295,10 +307,12 @@ class Oracle:
         return x + linear(o.reshape(T, Hd), self.W(wo))
 
     def verifier_forward(self, st: "SeqState", x_in: np.ndarray, pos: Sequence[int], record=None,
-                         router_logits=None):
+                         router_logits=None, pick=None):
         """Rows x_in [T, d] at consecutive positions ``pos`` through all layers.
         Returns the pre-norm final hidden [T, d].  router_logits (optional
-        [n_layers][T][E]) replaces each layer's router logits."""
+        [n_layers][T][E]) replaces each layer's router logits; pick (optional)
+        is called as pick(layer, positions, logits, idx) and may replace the
+        selection (see moe)."""
         c = self.cfg
         x = np.asarray(x_in, F64).copy()
         pos = np.asarray(pos, dtype=np.int64)
@@ -306,9 +320,10 @@ class Oracle:
             x = self.attention_block(x, pos, f"l{l}.attn_norm", f"l{l}.wqkv", f"l{l}.wo",
                                      st.kv[l, 0], st.kv[l, 1])
             b = rmsnorm(x, self.w[f"l{l}.ffn_norm"], c.norm_eps)
+            lp = None if pick is None else (lambda lg, ix, _l=l: pick(_l, pos, lg, ix))
             y, idx = moe(b, self.W(f"l{l}.router"), self.w[f"l{l}.w_gate"], self.w[f"l{l}.w_up"],
                          self.w[f"l{l}.w_down"], c.n_experts, c.n_shared, c.top_k,
-                         None if router_logits is None else router_logits[l])
+                         None if router_logits is None else router_logits[l], lp)
             if record is not None:
                 record.append(idx)
             x = x + y
@@ -337,15 +352,20 @@ class Oracle:
         """Prefix layout: the vision rows, then the embeddings of the prompt ids."""
         return np.concatenate([np.asarray(vision, F64), self.embed(prompt)], axis=0)
 
-    def prefill(self, st: "SeqState", vision, prompt, with_draft: bool, chunk: int = 512):
+    def prefill(self, st: "SeqState", vision, prompt, with_draft: bool, chunk: int = 512, pick=None,
+                first_token: Optional[int] = None):
+        """Prefix rows through the verifier (and the draft block when with_draft);
+        output token 0 is the greedy token of the last prefix row, or
+        first_token when given (a parity harness following another
+        implementation's choice at a near tie)."""
         e = self.prefix_rows(vision, prompt)
         P = e.shape[0]
         h = np.empty_like(e)
         for lo in range(0, P, chunk):
             hi = min(P, lo + chunk)
-            h[lo:hi] = self.verifier_forward(st, e[lo:hi], np.arange(lo, hi))
+            h[lo:hi] = self.verifier_forward(st, e[lo:hi], np.arange(lo, hi), pick=pick)
         logits = self.lm_logits(h[-1:])
-        y0 = int(greedy(logits)[0])
+        y0 = int(greedy(logits)[0]) if first_token is None else int(first_token)
         if with_draft:
             hprev = np.concatenate([np.zeros((1, e.shape[1]), F64), h[:-1]], axis=0)
             for lo in range(0, P, chunk):
@@ -376,6 +396,39 @@ class Oracle:
                 logits_rows.append(lg[0])
         return st.out[:n_out], logits_rows
 
+    def teacher_forced(self, vision, prompt, tokens: Sequence[int], chunk: int = 512, pick=None,
+                       keep_at: Sequence[int] = ()):
+        """The verifier along a given output sequence (teacher forcing): the
+        prefix rows, then tokens[0..N-2] as inputs at positions P..P+N-2, in
+        batched forwards of ``chunk`` rows.  Output token t (0..N-1) is
+        predicted by the row at position P-1+t.  Returns (greedy [N] -- argmax
+        of the float32-rounded logits, lowest id on ties --, top-2 margin [N],
+        {t: logits [V]} for t in keep_at, the state, whose cache holds all
+        P+N-1 positions)."""
+        e = np.concatenate([self.prefix_rows(vision, prompt), self.embed(list(tokens)[:-1])], axis=0)
+        P = vision.shape[0] + len(prompt)
+        N = len(tokens)
+        st = self.new_state(P + N + 8)
+        keep = set(int(t) for t in keep_at)
+        g = np.empty(N, dtype=np.int64)
+        mg = np.empty(N, dtype=F64)
+        kept = {}
+        for lo in range(0, e.shape[0], chunk):
+            hi = min(e.shape[0], lo + chunk)
+            h = self.verifier_forward(st, e[lo:hi], np.arange(lo, hi), pick=pick)
+            r0 = max(lo, P - 1)                # rows that predict output tokens
+            if r0 >= hi:
+                continue
+            lg = self.lm_logits(h[r0 - lo:])
+            t0 = r0 - (P - 1)
+            g[t0:t0 + lg.shape[0]] = greedy(lg)
+            mg[t0:t0 + lg.shape[0]] = top2_margin(lg)
+            for i in range(lg.shape[0]):
+                if t0 + i in keep:
+                    kept[t0 + i] = lg[i].copy()
+        st.kv_len = e.shape[0]
+        return g, mg, kept, st
+
     def draft_propose(self, st: "SeqState", K: int) -> List[int]:
         """K recursive passes of the shared draft block.  Pass 1 re-runs the
         catch-up rows draft_len..kv_len from verifier hiddens; passes 2..K feed
@@ -397,37 +450,51 @@ class Oracle:
 
     def generate_spec(self, vision, prompt, n_out: int, K: int,
                       proposer: Optional[Callable] = None, keep_logits: bool = False,
-                      seq_index: int = 0, draft_for_cost: bool = False, max_steps: Optional[int] = None):
+                      seq_index: int = 0, draft_for_cost: bool = False, max_steps: Optional[int] = None,
+                      greedy_hook: Optional[Callable] = None, pick: Optional[Callable] = None,
+                      first_token: Optional[int] = None, state_out: Optional[list] = None):
         """FastMTP speculative decoding with greedy longest-prefix acceptance.
 
         proposer(step, committed_tokens, K) -> K tokens replaces the draft block
         (losslessness tests, controlled acceptance); None runs the draft block.
         draft_for_cost runs the draft block even when a proposer replaces its
-        tokens (as the controlled-acceptance benchmark does); max_steps bounds
-        the number of speculative steps.
-        Returns (tokens[:n_out], [StepRecord])."""
+        tokens (as the controlled-acceptance benchmark does); its proposals are
+        recorded as real_drafts.  max_steps bounds the number of speculative
+        steps.  greedy_hook(step, g, logits) -> tokens (optional) may replace
+        the verifier's greedy tokens of a step before acceptance, and pick the
+        routing (see verifier_forward): a parity harness uses them to follow
+        another implementation's choice at a near tie, so both keep one history;
+        first_token likewise replaces output token 0, and state_out (a list)
+        receives the sequence state.  Returns (tokens[:n_out], [StepRecord])."""
         P = vision.shape[0] + len(prompt)
         st = self.new_state(P + n_out + K + 2)
-        self.prefill(st, vision, prompt, with_draft=proposer is None or draft_for_cost)
+        self.prefill(st, vision, prompt, with_draft=proposer is None or draft_for_cost, pick=pick,
+                     first_token=first_token)
+        if state_out is not None:
+            state_out.append(st)
         steps: List[StepRecord] = []
         while len(st.out) < n_out and (max_steps is None or len(steps) < max_steps):
+            real = None
             if proposer is None:
                 d = self.draft_propose(st, K)
+                real = list(d)
             else:
                 if draft_for_cost:
-                    self.draft_propose(st, K)
+                    real = self.draft_propose(st, K)
                 d = [int(t) for t in proposer(len(steps), list(st.out), K)]
             q = st.kv_len
             rows = [st.out[-1]] + d
-            h = self.verifier_forward(st, self.embed(rows), np.arange(q, q + K + 1))
+            h = self.verifier_forward(st, self.embed(rows), np.arange(q, q + K + 1), pick=pick)
             lg = self.lm_logits(h)
             g = [int(t) for t in greedy(lg)]
+            if greedy_hook is not None:
+                g = [int(t) for t in greedy_hook(len(steps), g, lg)]
             n = 0
             while n < K and d[n] == g[n]:
                 n += 1
             st.out += d[:n] + [g[n]]
             steps.append(StepRecord(q, d, g, n, lg if keep_logits else None,
-                                    st.draft_margins if proposer is None else None))
+                                    st.draft_margins if real is not None else None, real))
             # rollback: verifier KV keeps positions < q + n + 1; the draft KV keeps
             # position q (computed from a true verifier hidden); the next catch-up
             # recomputes draft rows q+1 .. q+n+1 from the verifier hiddens h[0..n].

@@ -587,7 +587,7 @@ __global__ __launch_bounds__(256) void k_dense_ks(const float* __restrict__ a, l
   }
 }
 
-void launch_gemv_ks(hipStream_t s, int K, Epi epi, const float* a, long lda, const float* gain, float eps,
+bool launch_gemv_ks(hipStream_t s, int K, Epi epi, const float* a, long lda, const float* gain, float eps,
                     const bf16* W0, const bf16* W1, int N, int M, float* out, long ldo) {
   const dim3 grid(N / 16, (M + 15) / 16);
   const QkvOut none{};
@@ -598,7 +598,9 @@ void launch_gemv_ks(hipStream_t s, int K, Epi epi, const float* a, long lda, con
   else if (K == D && epi == EPI_STORE) OCR_DK(D, DM_STORE);
   else if (K == 2 * D && epi == EPI_STORE) OCR_DK(2 * D, DM_STORE);
   else if (K == DF && epi == EPI_ADD) OCR_DK(DF, DM_ADD);
+  else return false;
 #undef OCR_DK
+  return true;
 }
 
 void launch_qkv_rope_ks(hipStream_t s, const float* x, const float* gain, float eps, const bf16* wqkv, int M,
@@ -608,7 +610,7 @@ void launch_qkv_rope_ks(hipStream_t s, const float* x, const float* gain, float 
                      nullptr, M, nullptr, 0L, qo);
 }
 
-void launch_gemv_mfma(hipStream_t s, int K, Epi epi, const float* a, long lda, const float* gain, float eps,
+bool launch_gemv_mfma(hipStream_t s, int K, Epi epi, const float* a, long lda, const float* gain, float eps,
                       const bf16* W0, const bf16* W1, int N, int M, float* out, long ldo) {
   const dim3 grid(N / 64, (M + 15) / 16);
   const QkvOut none{};
@@ -619,7 +621,9 @@ void launch_gemv_mfma(hipStream_t s, int K, Epi epi, const float* a, long lda, c
   else if (K == D && epi == EPI_STORE) OCR_DM(D, DM_STORE);
   else if (K == 2 * D && epi == EPI_STORE) OCR_DM(2 * D, DM_STORE);
   else if (K == DF && epi == EPI_ADD) OCR_DM(DF, DM_ADD);
+  else return false;
 #undef OCR_DM
+  return true;
 }
 
 void launch_qkv_rope_mfma(hipStream_t s, const float* x, const float* gain, float eps, const bf16* wqkv, int M,

@@ -17,7 +17,10 @@ __device__ __forceinline__ void embed_row(const T* __restrict__ E, int tok, floa
 // Block b: sequence b of a verify call.  Rows b*(K+1) + i hold
 // [pending, d_1 .. d_K] at positions kv_len .. kv_len + K.  The draft tokens
 // are read with the slot, then every row's embedding loads go out at once
-// (row indices clamped to K, rows past K not stored).
+// (row indices clamped to K, rows past K not stored).  A sequence whose rows
+// would pass the cache (kv_len + K + 1 > max_pos) gets no valid rows (nothing
+// is written to its cache) and its overflow flag is set; the accept then
+// leaves it unchanged.
 constexpr int QV = 8;  // rows per sequence of a verify call: K + 1 <= 8
 template <typename T>
 __global__ __launch_bounds__(256) void k_plan_verify(int K, const int* __restrict__ slots_in, StateView sv,
@@ -31,9 +34,12 @@ __global__ __launch_bounds__(256) void k_plan_verify(int K, const int* __restric
   for (int i = 0; i < QV - 1; ++i) dt[i] = (K > 0) ? draft[b * K + min(i, K - 1)] : 0;
   const int slot = clamp_slot(slots_in ? slots_in[b] : b, sv.n_slots);
   if (threadIdx.x == 0) {
+    const int kl = sv.kv_len[slot];
+    const bool over = kl + K + 1 > sv.max_pos;
     plan_slot[b] = slot;
-    plan_base[b] = sv.kv_len[slot];
-    plan_cnt[b] = K + 1;
+    plan_base[b] = kl;
+    plan_cnt[b] = over ? 0 : K + 1;
+    if (over) sv.ovf[slot] = 1;
   }
   const int pend = sv.pending[slot];
   float v[QV][J];
@@ -368,6 +374,7 @@ __global__ __launch_bounds__(256) void k_prefill_finish(PrefillGroup g, const fl
     sv.out_len[slot] = 1;
     sv.step[slot] = 0;
     sv.prefix_len[slot] = P;
+    sv.ovf[slot] = 0;
     sv.cu_tok[slot * sv.cu_stride] = y0;
     pending_out[g.seq[j]] = y0;
   }
@@ -387,6 +394,7 @@ __global__ void k_set_sequence(int slot, int P, int tok, StateView sv) {
     sv.out_len[slot] = 1;
     sv.step[slot] = 0;
     sv.prefix_len[slot] = P;
+    sv.ovf[slot] = 0;
     sv.cu_tok[slot * sv.cu_stride] = tok;
   }
   float* hb = sv.hbuf + (long)slot * sv.cu_stride * D;
@@ -433,7 +441,7 @@ __global__ __launch_bounds__(256) void k_accept(int K, const int* __restrict__ p
                                                 const int* __restrict__ draft, const int* __restrict__ greedy,
                                                 const float* __restrict__ xfinal, StateView sv,
                                                 int* __restrict__ n_acc, int* __restrict__ out_tokens,
-                                                int* __restrict__ out_len_out, int out_cap,
+                                                int* __restrict__ out_len_out, int out_cap, StepTap tap,
                                                 const float* __restrict__ part_val, const int* __restrict__ part_idx,
                                                 int nblk, int* __restrict__ greedy_w) {
   constexpr int J = D / 256;
@@ -468,25 +476,34 @@ __global__ __launch_bounds__(256) void k_accept(int K, const int* __restrict__ p
     const int gv = (lane <= K) ? (AM ? gs[lane] : greedy[b * (K + 1) + lane]) : 0;
     const int old = sv.kv_len[slot];
     const int ol0 = sv.out_len[slot];
+    const int st = sv.step[slot];
+    const bool over = old + K + 1 > sv.max_pos;  // the verify computed no rows for it
     const uint64_t miss = __ballot(!(lane < K && dv == gv));
     const int n = __builtin_ctzll(miss);  // <= K
     const int gn = __builtin_amdgcn_readlane(gv, n);  // n is the same on every lane
-    if (lane <= n) {
+    if (!over && lane <= n) {
       const int t = (lane < n) ? dv : gn;
       sv.cu_tok[slot * sv.cu_stride + lane] = t;
       if (out_tokens != nullptr && ol0 + lane < out_cap) out_tokens[(long)b * out_cap + ol0 + lane] = t;
     }
     if (lane == 0) {
-      const int ol = ol0 + n + 1;
-      sv.out_len[slot] = ol;
-      sv.kv_len[slot] = old + n + 1;
-      sv.draft_len[slot] = old + 1;
-      sv.pending[slot] = gn;
-      sv.n_prev[slot] = n;
-      sv.step[slot] += 1;
-      if (n_acc != nullptr) n_acc[b] = n;
-      if (out_len_out != nullptr) out_len_out[b] = ol;
-      sn = n;
+      if (over) {
+        if (n_acc != nullptr) n_acc[b] = -1;
+        if (out_len_out != nullptr) out_len_out[b] = ol0;
+        sn = -1;
+      } else {
+        const int ol = ol0 + n + 1;
+        sv.out_len[slot] = ol;
+        sv.kv_len[slot] = old + n + 1;
+        sv.draft_len[slot] = old + 1;
+        sv.pending[slot] = gn;
+        sv.n_prev[slot] = n;
+        sv.step[slot] = st + 1;
+        if (n_acc != nullptr) n_acc[b] = n;
+        if (out_len_out != nullptr) out_len_out[b] = ol;
+        if (tap.acc != nullptr && st < tap.cap) tap.acc[(long)slot * tap.cap + st] = n;
+        sn = n;
+      }
     }
   }
   __syncthreads();
@@ -525,6 +542,17 @@ __global__ void k_controlled(int B, int K, const int* __restrict__ slots_in, Sta
   int tok = true_tok;
   if ((h >> 11) < thr) tok = (int)(((uint64_t)true_tok + 1 + (h & 0xFFFFFFFFull) % (uint64_t)(V - 1)) % (uint64_t)V);
   draft[b * K + j - 1] = tok;
+}
+
+// Drafts tap: the K proposals of sequence b at its slot's step number.
+__global__ void k_draft_tap(int B, int K, const int* __restrict__ plan_slot, StateView sv,
+                            const int* __restrict__ draft, StepTap tap) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= B * K) return;
+  const int b = t / K, j = t % K;
+  const int slot = plan_slot[b];
+  const int st = sv.step[slot];
+  if (st < tap.cap) tap.drafts[((long)slot * tap.cap + st) * QV + j] = draft[b * K + j];
 }
 
 __global__ void k_copy(const float* __restrict__ src, float* __restrict__ dst, long n) {
@@ -595,13 +623,18 @@ void launch_set_sequence(hipStream_t s, int slot, int P, int tok, StateView sv) 
 }
 void launch_accept(hipStream_t s, int B, int K, const int* plan_slot, const int* draft, const int* greedy,
                    const float* xfinal, StateView sv, int* n_acc, int* out_tokens, int* out_len_out, int out_cap,
-                   const float* part_val, const int* part_idx, int nblk, int* greedy_w) {
+                   const StepTap& tap, const float* part_val, const int* part_idx, int nblk, int* greedy_w) {
   if (part_val != nullptr)
     hipLaunchKernelGGL((k_accept<true>), dim3(B), dim3(256), 0, s, K, plan_slot, draft, greedy, xfinal, sv, n_acc,
-                       out_tokens, out_len_out, out_cap, part_val, part_idx, nblk, greedy_w);
+                       out_tokens, out_len_out, out_cap, tap, part_val, part_idx, nblk, greedy_w);
   else
     hipLaunchKernelGGL((k_accept<false>), dim3(B), dim3(256), 0, s, K, plan_slot, draft, greedy, xfinal, sv, n_acc,
-                       out_tokens, out_len_out, out_cap, part_val, part_idx, nblk, greedy_w);
+                       out_tokens, out_len_out, out_cap, tap, part_val, part_idx, nblk, greedy_w);
+}
+void launch_draft_tap(hipStream_t s, int B, int K, const int* plan_slot, StateView sv, const int* draft,
+                      const StepTap& tap) {
+  const int n = B * K;
+  hipLaunchKernelGGL(k_draft_tap, dim3((n + 255) / 256), dim3(256), 0, s, B, K, plan_slot, sv, draft, tap);
 }
 void launch_controlled(hipStream_t s, int B, int K, const int* slots_in, StateView sv, const int* trace,
                        int trace_stride, int trace_len, uint64_t seed, uint64_t thr, int V, int* draft) {

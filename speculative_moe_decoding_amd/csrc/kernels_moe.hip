@@ -121,10 +121,23 @@ __device__ __forceinline__ void route_rows(const float* __restrict__ rlogit, int
   __syncthreads();
 }
 
+// Routing taps of pair p = row m * 8 + k (expert e): the call's table, and the
+// table by position for the rows of the tapped slot.
+__device__ __forceinline__ void tap_pair(const RouteTap& tap, int m, int k, int e) {
+  if (tap.call != nullptr) tap.call[m * NSLOT + k] = e;
+  if (tap.pos != nullptr) {
+    const int b = m / tap.plan.Q, i = m - b * tap.plan.Q;
+    if (tap.plan.slot[b] == tap.pos_slot && i < tap.plan.cnt[b]) {
+      const int pos = tap.plan.base[b] + i;
+      if (pos >= 0 && pos < tap.pos_cap) tap.pos[(long)pos * NSLOT + k] = e;
+    }
+  }
+}
+
 // Publish the routing of the LDS copy for the kernels that follow (down,
 // combine) and the taps; stats[0] = st0 (its value at kernel start, read by
 // thread 0) + the active experts.
-__device__ __forceinline__ void publish_route(const RouteLds& r, int M, const MoeBufs& mb, int* tap,
+__device__ __forceinline__ void publish_route(const RouteLds& r, int M, const MoeBufs& mb, const RouteTap& tap,
                                               long long st0) {
   const int tid = threadIdx.x;
   const int P = M * NSLOT;
@@ -133,7 +146,7 @@ __device__ __forceinline__ void publish_route(const RouteLds& r, int M, const Mo
     mb.rgate[p] = r.pg[p];
     mb.perm[p] = r.perm[p];
     mb.inv[p] = r.inv[p];
-    if (tap != nullptr) tap[p] = r.pe[p];
+    tap_pair(tap, p / NSLOT, p % NSLOT, r.pe[p]);
   }
   for (int e = tid; e <= NX; e += 256) mb.off[e] = r.off[e];
   for (int sl = tid; sl < NX; sl += 256) {
@@ -180,7 +193,7 @@ __global__ __launch_bounds__(256) void k_router_logits(const float* __restrict__
 
 // M <= 8: top-6 per row and the sort by one block, published to global.
 __global__ __launch_bounds__(256) void k_route_small(const float* __restrict__ rlogit, int M, MoeBufs mb,
-                                                     int* __restrict__ tap) {
+                                                     RouteTap tap) {
   __shared__ RouteLds r;
   const long long st0 = (threadIdx.x == 0) ? mb.stats[0] : 0;  // read early: off the kernel's tail
   route_rows(rlogit, M, r);
@@ -190,7 +203,7 @@ __global__ __launch_bounds__(256) void k_route_small(const float* __restrict__ r
 // Larger batches (8 < M <= 1024): top-6 per row, one wavefront per row
 // (rank_and_gate) ...
 __global__ __launch_bounds__(256) void k_topk_rows(const float* __restrict__ rlogit, int M, MoeBufs mb,
-                                                   int* __restrict__ tap) {
+                                                   RouteTap tap) {
   __shared__ float lg[4][NE];
   const int wave = wave_id(), lane = lane_id();
   const int m = blockIdx.x * 4 + wave;
@@ -205,12 +218,12 @@ __global__ __launch_bounds__(256) void k_topk_rows(const float* __restrict__ rlo
   if (rank < TOPK) {
     mb.ridx[m * NSLOT + rank] = lane;
     mb.rgate[m * NSLOT + rank] = gate;
-    if (tap != nullptr) tap[m * NSLOT + rank] = lane;
+    tap_pair(tap, m, rank, lane);
   }
   if (lane < NSH) {
     mb.ridx[m * NSLOT + TOPK + lane] = NE + lane;
     mb.rgate[m * NSLOT + TOPK + lane] = 1.0f;
-    if (tap != nullptr) tap[m * NSLOT + TOPK + lane] = NE + lane;
+    tap_pair(tap, m, TOPK + lane, NE + lane);
   }
 }
 
@@ -320,7 +333,7 @@ int expert_slot_cap(int M) { return min(NE, TOPK * M) + NSH; }
 // block for M <= 8; a per-row top-6 kernel and a one-block sort beyond).
 template <typename T>
 void launch_router(hipStream_t s, const float* x, const float* gain, float eps, const T* wr, int M,
-                   const MoeBufs& mb, int* tap, const float* logit_override) {
+                   const MoeBufs& mb, const RouteTap& tap, const float* logit_override) {
 #define OCR_RL_CASE(MRV)                                                                                   \
   hipLaunchKernelGGL((k_router_logits<T, MRV>), dim3(NE / 4, (M + MRV - 1) / MRV), dim3(256),              \
                      (size_t)MRV * D * 4, s, x, gain, eps, wr, M, mb.bnorm, mb.rlogit);
@@ -501,7 +514,7 @@ constexpr int GU_UPW = OCR_GU_UPW;   // gate/up units per wavefront
 constexpr int DN_RPW = OCR_DN_RPW;   // down rows per wavefront
 
 template <typename T>
-void launch_expert_gate_up(hipStream_t s, const T* wg, const T* wu, int M, const MoeBufs& mb, int* tap) {
+void launch_expert_gate_up(hipStream_t s, const T* wg, const T* wu, int M, const MoeBufs& mb) {
   const dim3 grid(DI / (4 * GU_UPW), expert_slot_cap(M));
 #define OCR_GU_CASE(MRV) \
   hipLaunchKernelGGL((k_expert_gate_up<T, MRV, GU_UPW>), grid, dim3(256), (size_t)MRV * D * 4, s, wg, wu, M, mb);
@@ -553,8 +566,8 @@ void launch_moe_combine(hipStream_t s, float* x, int M, const MoeBufs& mb) {
 
 #define OCR_INST_MOE(T)                                                                                  \
   template void launch_router<T>(hipStream_t, const float*, const float*, float, const T*, int,          \
-                                 const MoeBufs&, int*, const float*);                                    \
-  template void launch_expert_gate_up<T>(hipStream_t, const T*, const T*, int, const MoeBufs&, int*);          \
+                                 const MoeBufs&, const RouteTap&, const float*);                         \
+  template void launch_expert_gate_up<T>(hipStream_t, const T*, const T*, int, const MoeBufs&);                \
   template void launch_expert_down<T>(hipStream_t, const T*, int, const MoeBufs&);
 OCR_INST_MOE(float)
 OCR_INST_MOE(bf16)

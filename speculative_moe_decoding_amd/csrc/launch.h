@@ -69,13 +69,26 @@ __device__ __forceinline__ int4 expert_work(const MoeBufs& mb, int y, int M) {
   return info;
 }
 
+// Routing taps of one layer (parity harness): call (nullable) receives the
+// routing of the call's rows, [M][8]; pos (nullable) receives, for the rows of
+// state slot pos_slot only, the routing by position, [pos_cap][8] (valid rows
+// at positions < pos_cap), so that a whole page's routing -- prefix and every
+// committed decode row, which is always the last row computed at its position
+// -- can be read after a run.
+struct RouteTap {
+  int* call;
+  int* pos;
+  int pos_slot, pos_cap;
+  RowPlan plan;
+};
+
 // Router logits (rlogit) and the routing tables; logit_override (nullable,
 // [M][64]) replaces the computed logits before the top-6.
 template <typename T>
 void launch_router(hipStream_t s, const float* x, const float* gain, float eps, const T* wr, int M,
-                   const MoeBufs& mb, int* tap, const float* logit_override);
+                   const MoeBufs& mb, const RouteTap& tap, const float* logit_override);
 template <typename T>
-void launch_expert_gate_up(hipStream_t s, const T* wg, const T* wu, int M, const MoeBufs& mb, int* tap);
+void launch_expert_gate_up(hipStream_t s, const T* wg, const T* wu, int M, const MoeBufs& mb);
 template <typename T>
 void launch_expert_down(hipStream_t s, const T* wd, int M, const MoeBufs& mb);
 void launch_moe_combine(hipStream_t s, float* x, int M, const MoeBufs& mb);
@@ -88,13 +101,14 @@ void launch_expert_down_mfma(hipStream_t s, const bf16* wd, int M, const MoeBufs
 // Dense layers on the matrix cores (bf16 weights): the outputs of launch_gemv
 // (K, epi) in {(1280, add / store / SwiGLU), (2560, store), (3584, add)}, N a
 // multiple of 64, and of launch_qkv_rope, with the inputs as bf16 hi + lo parts.
-void launch_gemv_mfma(hipStream_t s, int K, Epi epi, const float* a, long lda, const float* gain, float eps,
+// The gemv launchers return false, launching nothing, for any other (K, epi).
+bool launch_gemv_mfma(hipStream_t s, int K, Epi epi, const float* a, long lda, const float* gain, float eps,
                       const bf16* W0, const bf16* W1, int N, int M, float* out, long ldo);
 void launch_qkv_rope_mfma(hipStream_t s, const float* x, const float* gain, float eps, const bf16* wqkv, int M,
                           RowPlan plan, float* q, bf16* kv, int max_pos, const float2* rope);
 // The same with k split over the four wavefronts of 16-row blocks (decode-sized
 // calls: many blocks, no LDS staging).
-void launch_gemv_ks(hipStream_t s, int K, Epi epi, const float* a, long lda, const float* gain, float eps,
+bool launch_gemv_ks(hipStream_t s, int K, Epi epi, const float* a, long lda, const float* gain, float eps,
                     const bf16* W0, const bf16* W1, int N, int M, float* out, long ldo);
 void launch_qkv_rope_ks(hipStream_t s, const float* x, const float* gain, float eps, const bf16* wqkv, int M,
                         RowPlan plan, float* q, bf16* kv, int max_pos, const float2* rope);
@@ -106,10 +120,21 @@ void launch_lmhead_mfma(hipStream_t s, const float* x, const int* cnt, int Q, bo
 // ---- row plans, embeddings, acceptance --------------------------------------
 struct StateView {
   int* kv_len; int* draft_len; int* pending; int* n_prev; int* out_len; int* step; int* prefix_len;
+  int* ovf;        // [max_batch] set when a step would pass max_pos (the step is not taken)
   int* cu_tok;     // [max_batch][cu_stride]
   int cu_stride;
   float* hbuf;     // [max_batch][cu_stride][D]
   int n_slots;     // max_batch
+  int max_pos;     // cache positions per slot
+};
+
+// Step-history taps of the decode calls (parity harness; nullable): acc[slot]
+// [cap] receives n of the slot's step number t (t < cap) and drafts[slot][cap]
+// [8] the K proposals of that step as the draft block made them.
+struct StepTap {
+  int* acc;
+  int* drafts;
+  int cap;
 };
 
 template <typename T>
@@ -162,10 +187,17 @@ void launch_set_sequence(hipStream_t s, int slot, int P, int tok, StateView sv);
 // Acceptance; with part_val non-null the greedy tokens are first reduced from
 // the LM head's per-block bests (part_val / part_idx, nblk per row) and
 // written to greedy_w (the verify then skips its argmax stage 2).
+// A sequence whose step would pass the cache (kv_len + K + 1 > max_pos; the
+// verify plan has set its overflow flag and computed no rows for it) commits
+// nothing and keeps its state; n_acc[b] = -1.
 void launch_accept(hipStream_t s, int B, int K, const int* plan_slot, const int* draft, const int* greedy,
                    const float* xfinal, StateView sv, int* n_acc, int* out_tokens, int* out_len_out,
-                   int out_cap, const float* part_val = nullptr, const int* part_idx = nullptr, int nblk = 0,
-                   int* greedy_w = nullptr);
+                   int out_cap, const StepTap& tap, const float* part_val = nullptr, const int* part_idx = nullptr,
+                   int nblk = 0, int* greedy_w = nullptr);
+// drafts tap: the K proposals of each sequence of the call (draft[b][K]) at
+// the slot's current step number.
+void launch_draft_tap(hipStream_t s, int B, int K, const int* plan_slot, StateView sv, const int* draft,
+                      const StepTap& tap);
 void launch_controlled(hipStream_t s, int B, int K, const int* slots_in, StateView sv, const int* trace,
                        int trace_stride, int trace_len, uint64_t seed, uint64_t thr, int V, int* draft);
 void launch_copy_rows(hipStream_t s, const float* src, float* dst, long n);

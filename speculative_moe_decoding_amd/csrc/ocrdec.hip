@@ -12,6 +12,7 @@
 
 #include "launch.h"
 #include "ocrdec.h"
+#include "ocrdec_harness.h"
 
 using namespace ocr;
 
@@ -29,7 +30,7 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 // Offsets of every sub-buffer inside the state and the workspace.
 struct Plan {
   // derived sizes
-  int Qmax, M_max, prefill_group, cu_stride, tiles_per_chunk, chunk_keys, n_chunks_cap, lm_nblk;
+  int Qmax, M_max, prefill_group, cu_stride, tiles_per_chunk, chunk_keys, n_chunks_cap, lm_nblk, plan_n;
   size_t esz, kv_layer_elems;
   // state
   size_t s_kv, s_dkv, s_ints, s_cu, s_hbuf, s_rope, s_total;
@@ -68,12 +69,15 @@ bool use_matrix_path(const ocrdec_config* c) {
   return c->dtype == OCRDEC_BF16 && c->vocab >= 64 && c->max_batch * (c->max_k + 1) > MRG;
 }
 
-Plan make_plan(const ocrdec_config* c) {
+// decode_only: the scratch of decode calls alone (draft, verify, accept) of up
+// to max_batch sequences at depth max_k, without the prefill's buffers.
+Plan make_plan(const ocrdec_config* c, bool decode_only = false) {
   Plan p{};
   p.Qmax = std::max(c->max_k + 1, PREFILL_CHUNK);
   // prefill passes take up to prefill_group entries of PREFILL_CHUNK rows
-  p.prefill_group = PREFILL_GROUP;
+  p.prefill_group = decode_only ? 0 : PREFILL_GROUP;
   p.M_max = std::max(c->max_batch * (c->max_k + 1), PREFILL_CHUNK * p.prefill_group);
+  p.plan_n = std::max(c->max_batch, p.prefill_group);
   p.cu_stride = c->max_k + 1;
   p.tiles_per_chunk = c->max_positions > 4096 ? 4 : 1;
   p.chunk_keys = p.tiles_per_chunk * ATT_TILE;
@@ -85,7 +89,7 @@ Plan make_plan(const ocrdec_config* c) {
   auto take = [&](size_t bytes) { size_t r = o; o = align256(o + bytes); return r; };
   p.s_kv = take(p.kv_layer_elems * c->n_layers * p.esz);
   p.s_dkv = take(p.kv_layer_elems * p.esz);
-  p.s_ints = take((size_t)7 * c->max_batch * 4);
+  p.s_ints = take((size_t)8 * c->max_batch * 4);
   p.s_cu = take((size_t)c->max_batch * p.cu_stride * 4);
   p.s_hbuf = take((size_t)c->max_batch * p.cu_stride * D * 4);
   p.s_rope = take((size_t)c->max_positions * (HD / 2) * 8);
@@ -113,13 +117,59 @@ Plan make_plan(const ocrdec_config* c) {
   p.w_u = take(M * D * 4);
   p.w_u2 = take((size_t)c->max_batch * D * 4);  // second output buffer of the recursive draft passes
   p.w_dffn = take(M * DF * 4);
-  p.w_esave = take(M * D * 4);
-  p.w_hsave = take((size_t)2 * c->max_batch * D * 4);
+  p.w_esave = take(decode_only ? 0 : M * D * 4);
+  p.w_hsave = take(decode_only ? 0 : (size_t)2 * c->max_batch * D * 4);
   p.w_lmv = take(M * (size_t)p.lm_nblk * 4);
   p.w_lmi = take(M * (size_t)p.lm_nblk * 4);
-  p.w_plan = take((size_t)3 * std::max(c->max_batch, PREFILL_GROUP) * 4);
+  p.w_plan = take((size_t)3 * p.plan_n * 4);
   p.w_total = o;
   return p;
+}
+
+// The per-call scratch buffers of the decode calls, laid out by a Plan inside
+// one region (the caller's workspace, or the library's no-allocation scratch).
+struct WsPtrs {
+  float *x, *q, *attn, *part, *cat, *u, *u2, *dffn, *esave, *hsave[2], *lm_val;
+  int *lm_idx, *plan_base, *plan_cnt, *plan_slot, *tok_tmp;
+  MoeBufs mb;
+};
+
+WsPtrs bind_workspace(char* ws, const Plan& p, int max_batch) {
+  WsPtrs b{};
+  auto wf = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+  auto wi = [&](size_t off) { return reinterpret_cast<int*>(ws + off); };
+  b.x = wf(p.w_x);
+  b.q = wf(p.w_q);
+  b.attn = wf(p.w_attn);
+  b.part = wf(p.w_part);
+  b.cat = wf(p.w_cat);
+  b.u = wf(p.w_u);
+  b.u2 = wf(p.w_u2);
+  b.dffn = wf(p.w_dffn);
+  b.esave = wf(p.w_esave);
+  b.hsave[0] = wf(p.w_hsave);
+  b.hsave[1] = wf(p.w_hsave) + (size_t)max_batch * D;
+  b.lm_val = wf(p.w_lmv);
+  b.lm_idx = wi(p.w_lmi);
+  b.plan_base = wi(p.w_plan);
+  b.plan_cnt = wi(p.w_plan) + p.plan_n;
+  b.plan_slot = wi(p.w_plan) + 2 * p.plan_n;
+  int* misc = wi(p.w_misc);
+  b.mb.n_act = misc;
+  b.tok_tmp = misc + 16;
+  b.mb.bnorm = wf(p.w_bnorm);
+  b.mb.ridx = wi(p.w_ridx);
+  b.mb.rgate = wf(p.w_rgate);
+  b.mb.perm = wi(p.w_perm);
+  b.mb.inv = wi(p.w_inv);
+  b.mb.off = wi(p.w_off);
+  b.mb.act = wi(p.w_act);
+  b.mb.slot_info = reinterpret_cast<int4*>(ws + p.w_slot);
+  b.mb.rlogit = wf(p.w_rlogit);
+  b.mb.stats = reinterpret_cast<long long*>(ws + p.w_stats);
+  b.mb.hx = wf(p.w_hx);
+  b.mb.y = wf(p.w_y);
+  return b;
 }
 
 }  // namespace
@@ -131,16 +181,19 @@ struct ocrdec_model {
   char* state;
   char* ws;
   StateView sv;
-  float *x, *q, *attn, *part, *cat, *u, *u2, *dffn, *esave, *hsave[2], *lm_val;
-  int *lm_idx, *plan_base, *plan_cnt, *plan_slot, *tok_tmp;
-  MoeBufs mb;
+  WsPtrs b;                    // per-call scratch inside the workspace (or the no-allocation scratch)
   const float2* rope;
   // Host-side upper bound on (last position + 1) of every slot: set by prefill,
   // raised by K + 1 per accept.  It sizes the attention grids and the capacity
   // checks; the device clamps positions to the cache in any case.
   std::vector<int> slot_bound;
-  int32_t* tap_route;
-  float* tap_hidden;
+  ocrdec_taps taps;            // parity harness taps (all null when unused)
+  StepTap step_tap;
+  const char* launch_fail;     // set when a launcher met an unsupported shape (checked by hip_check)
+  // the last verify call (for the accept that must follow it): rows per
+  // sequence, sequences and slot map; B = 0 once an accept has consumed it
+  int lv_B, lv_K;
+  const int32_t* lv_slots;
   bool timing;
   std::vector<hipEvent_t> ev;  // triplets: before gate/up, between, after down
   size_t ev_used;
@@ -165,9 +218,14 @@ const float* wvec(const ocrdec_model* m, int i) { return static_cast<const float
 int lw(const ocrdec_model* m, int l, int k) { (void)m; return W_LAYER0 + L_N * l + k; }
 int dw(const ocrdec_model* m, int k) { return W_LAYER0 + L_N * m->cfg.n_layers + k; }
 
-int hip_check(const char* where) {
+int hip_check(ocrdec_model* m, const char* where) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(OCRDEC_EHIP, std::string(where) + ": " + hipGetErrorString(e));
+  if (m != nullptr && m->launch_fail != nullptr) {
+    const char* what = m->launch_fail;
+    m->launch_fail = nullptr;
+    return fail(OCRDEC_EINVAL, std::string(where) + ": unsupported launch shape (" + what + ")");
+  }
   return OCRDEC_OK;
 }
 
@@ -220,25 +278,25 @@ PassPath prefill_path(const ocrdec_model* m) {
 }
 
 template <typename T>
-void expert_gate_up(ocrdec_model* m, hipStream_t s, int l, int M, int* tap, bool mx) {
+void expert_gate_up(ocrdec_model* m, hipStream_t s, int l, int M, bool mx) {
   if constexpr (std::is_same<T, bf16>::value) {
     if (mx) {
-      launch_expert_gate_up_mfma(s, wmat<T>(m, lw(m, l, L_GATE)), wmat<T>(m, lw(m, l, L_UP)), M, m->mb);
+      launch_expert_gate_up_mfma(s, wmat<T>(m, lw(m, l, L_GATE)), wmat<T>(m, lw(m, l, L_UP)), M, m->b.mb);
       return;
     }
   }
-  launch_expert_gate_up<T>(s, wmat<T>(m, lw(m, l, L_GATE)), wmat<T>(m, lw(m, l, L_UP)), M, m->mb, tap);
+  launch_expert_gate_up<T>(s, wmat<T>(m, lw(m, l, L_GATE)), wmat<T>(m, lw(m, l, L_UP)), M, m->b.mb);
 }
 
 template <typename T>
 void expert_down(ocrdec_model* m, hipStream_t s, int l, int M, bool mx) {
   if constexpr (std::is_same<T, bf16>::value) {
     if (mx) {
-      launch_expert_down_mfma(s, wmat<T>(m, lw(m, l, L_DOWN)), M, m->mb);
+      launch_expert_down_mfma(s, wmat<T>(m, lw(m, l, L_DOWN)), M, m->b.mb);
       return;
     }
   }
-  launch_expert_down<T>(s, wmat<T>(m, lw(m, l, L_DOWN)), M, m->mb);
+  launch_expert_down<T>(s, wmat<T>(m, lw(m, l, L_DOWN)), M, m->b.mb);
 }
 
 // LM head + argmax over M output rows (see launch_lmhead).
@@ -248,13 +306,13 @@ void lm_head(ocrdec_model* m, hipStream_t s, const float* x, int Q, bool last_va
   const ocrdec_config& c = m->cfg;
   if constexpr (std::is_same<T, bf16>::value) {
     if (m->matrix) {
-      launch_lmhead_mfma(s, x, m->plan_cnt, Q, last_valid, gain, c.norm_eps, wmat<T>(m, W_LM), c.vocab, M,
-                         m->mb.bnorm, m->lm_val, m->lm_idx, logits, tok, tok_stride);
+      launch_lmhead_mfma(s, x, m->b.plan_cnt, Q, last_valid, gain, c.norm_eps, wmat<T>(m, W_LM), c.vocab, M,
+                         m->b.mb.bnorm, m->b.lm_val, m->b.lm_idx, logits, tok, tok_stride);
       return;
     }
   }
-  launch_lmhead<T>(s, x, m->plan_cnt, Q, last_valid, gain, c.norm_eps, wmat<T>(m, W_LM), c.vocab, M, m->lm_val,
-                   m->lm_idx, logits, tok, tok_stride);
+  launch_lmhead<T>(s, x, m->b.plan_cnt, Q, last_valid, gain, c.norm_eps, wmat<T>(m, W_LM), c.vocab, M, m->b.lm_val,
+                   m->b.lm_idx, logits, tok, tok_stride);
 }
 
 // Dense layers on the path dp (DensePath).
@@ -263,11 +321,13 @@ void dense_gemv(ocrdec_model* m, hipStream_t s, int dp, int K, Epi epi, const fl
                 const float* gain, const T* W0, const T* W1, int N, int M, float* out, long ldo) {
   if constexpr (std::is_same<T, bf16>::value) {
     if (dp == DENSE_STRIP) {
-      launch_gemv_mfma(s, K, epi, a, lda, gain, m->cfg.norm_eps, W0, W1, N, M, out, ldo);
+      if (!launch_gemv_mfma(s, K, epi, a, lda, gain, m->cfg.norm_eps, W0, W1, N, M, out, ldo))
+        m->launch_fail = "matrix-core dense layer: no kernel for this (K, epilogue)";
       return;
     }
     if (dp == DENSE_KSPLIT) {
-      launch_gemv_ks(s, K, epi, a, lda, gain, m->cfg.norm_eps, W0, W1, N, M, out, ldo);
+      if (!launch_gemv_ks(s, K, epi, a, lda, gain, m->cfg.norm_eps, W0, W1, N, M, out, ldo))
+        m->launch_fail = "k-split dense layer: no kernel for this (K, epilogue)";
       return;
     }
   }
@@ -279,15 +339,15 @@ void dense_qkv(ocrdec_model* m, hipStream_t s, int dp, const float* x, const flo
                RowPlan plan, T* kv) {
   if constexpr (std::is_same<T, bf16>::value) {
     if (dp == DENSE_STRIP) {
-      launch_qkv_rope_mfma(s, x, gain, m->cfg.norm_eps, W, M, plan, m->q, kv, m->cfg.max_positions, m->rope);
+      launch_qkv_rope_mfma(s, x, gain, m->cfg.norm_eps, W, M, plan, m->b.q, kv, m->cfg.max_positions, m->rope);
       return;
     }
     if (dp == DENSE_KSPLIT) {
-      launch_qkv_rope_ks(s, x, gain, m->cfg.norm_eps, W, M, plan, m->q, kv, m->cfg.max_positions, m->rope);
+      launch_qkv_rope_ks(s, x, gain, m->cfg.norm_eps, W, M, plan, m->b.q, kv, m->cfg.max_positions, m->rope);
       return;
     }
   }
-  launch_qkv_rope<T>(s, x, gain, m->cfg.norm_eps, W, M, plan, m->q, kv, m->cfg.max_positions, m->rope);
+  launch_qkv_rope<T>(s, x, gain, m->cfg.norm_eps, W, M, plan, m->b.q, kv, m->cfg.max_positions, m->rope);
 }
 
 template <typename T>
@@ -296,19 +356,26 @@ void verifier_layers(ocrdec_model* m, hipStream_t s, PassPath pp, int M, int B, 
   const ocrdec_config& c = m->cfg;
   for (int l = 0; l < c.n_layers; ++l) {
     T* kvl = static_cast<T*>((void*)(m->state + m->p.s_kv)) + (size_t)l * m->p.kv_layer_elems;
-    dense_qkv<T>(m, s, pp.dense, m->x, wvec(m, lw(m, l, L_ANORM)), wmat<T>(m, lw(m, l, L_QKV)), M, plan, kvl);
-    launch_attention<T>(s, m->q, kvl, c.max_positions, plan, B, nch, m->p.tiles_per_chunk, m->part, m->attn);
-    dense_gemv<T>(m, s, pp.dense, QD, EPI_ADD, m->attn, QD, nullptr, wmat<T>(m, lw(m, l, L_WO)), nullptr, D, M,
-                  m->x, D);
-    int* tap = (taps && m->tap_route) ? m->tap_route + (size_t)l * M * NSLOT : nullptr;
-    launch_router<T>(s, m->x, wvec(m, lw(m, l, L_FNORM)), c.norm_eps, wmat<T>(m, lw(m, l, L_ROUTER)), M, m->mb,
+    dense_qkv<T>(m, s, pp.dense, m->b.x, wvec(m, lw(m, l, L_ANORM)), wmat<T>(m, lw(m, l, L_QKV)), M, plan, kvl);
+    launch_attention<T>(s, m->b.q, kvl, c.max_positions, plan, B, nch, m->p.tiles_per_chunk, m->b.part, m->b.attn);
+    dense_gemv<T>(m, s, pp.dense, QD, EPI_ADD, m->b.attn, QD, nullptr, wmat<T>(m, lw(m, l, L_WO)), nullptr, D, M,
+                  m->b.x, D);
+    RouteTap tap{};
+    tap.call = (taps && m->taps.route_idx) ? m->taps.route_idx + (size_t)l * M * NSLOT : nullptr;
+    if (m->taps.route_pos != nullptr) {
+      tap.pos = m->taps.route_pos + (size_t)l * m->taps.route_pos_cap * NSLOT;
+      tap.pos_slot = m->taps.route_pos_slot;
+      tap.pos_cap = m->taps.route_pos_cap;
+    }
+    tap.plan = plan;
+    launch_router<T>(s, m->b.x, wvec(m, lw(m, l, L_FNORM)), c.norm_eps, wmat<T>(m, lw(m, l, L_ROUTER)), M, m->b.mb,
                      tap, rlog ? rlog + (size_t)l * M * NE : nullptr);
     timing_mark(m, s);
-    expert_gate_up<T>(m, s, l, M, tap, pp.experts);
+    expert_gate_up<T>(m, s, l, M, pp.experts);
     timing_mark(m, s);
     expert_down<T>(m, s, l, M, pp.experts);
     timing_mark(m, s);
-    launch_moe_combine(s, m->x, M, m->mb);
+    launch_moe_combine(s, m->b.x, M, m->b.mb);
   }
 }
 
@@ -321,14 +388,14 @@ void draft_layer(ocrdec_model* m, hipStream_t s, PassPath pp, int M, int B, RowP
   const int mx = pp.dense;
   T* dkv = static_cast<T*>((void*)(m->state + m->p.s_dkv));
   if (!fused_in)
-    dense_gemv<T>(m, s, mx, 2 * D, EPI_STORE, m->cat, 2 * D, nullptr, wmat<T>(m, dw(m, D_FUSE)), nullptr, D, M, u,
+    dense_gemv<T>(m, s, mx, 2 * D, EPI_STORE, m->b.cat, 2 * D, nullptr, wmat<T>(m, dw(m, D_FUSE)), nullptr, D, M, u,
                   D);
   dense_qkv<T>(m, s, mx, u, wvec(m, dw(m, D_ANORM)), wmat<T>(m, dw(m, D_QKV)), M, plan, dkv);
-  launch_attention<T>(s, m->q, dkv, c.max_positions, plan, B, nch, m->p.tiles_per_chunk, m->part, m->attn);
-  dense_gemv<T>(m, s, mx, QD, EPI_ADD, m->attn, QD, nullptr, wmat<T>(m, dw(m, D_WO)), nullptr, D, M, u, D);
+  launch_attention<T>(s, m->b.q, dkv, c.max_positions, plan, B, nch, m->p.tiles_per_chunk, m->b.part, m->b.attn);
+  dense_gemv<T>(m, s, mx, QD, EPI_ADD, m->b.attn, QD, nullptr, wmat<T>(m, dw(m, D_WO)), nullptr, D, M, u, D);
   dense_gemv<T>(m, s, mx, D, EPI_SWIGLU, u, D, wvec(m, dw(m, D_FNORM)), wmat<T>(m, dw(m, D_GATE)),
-                wmat<T>(m, dw(m, D_UP)), DF, M, m->dffn, DF);
-  dense_gemv<T>(m, s, mx, DF, EPI_ADD, m->dffn, DF, nullptr, wmat<T>(m, dw(m, D_DOWN)), nullptr, D, M, u, D);
+                wmat<T>(m, dw(m, D_UP)), DF, M, m->b.dffn, DF);
+  dense_gemv<T>(m, s, mx, DF, EPI_ADD, m->b.dffn, DF, nullptr, wmat<T>(m, dw(m, D_DOWN)), nullptr, D, M, u, D);
 }
 
 // Prefill in passes of up to prefill_group entries of PREFILL_CHUNK rows: the
@@ -346,8 +413,8 @@ int do_prefill(ocrdec_model* m, hipStream_t s, int B, const int32_t* slots_host,
     for (int p0 = 0; p0 < nv_host[b] + np_host[b]; p0 += PREFILL_CHUNK) ent.emplace_back(b, p0);
   int t = 0;
   for (size_t e0 = 0; e0 < ent.size(); e0 += m->p.prefill_group, ++t) {
-    const float* hprev = m->hsave[t & 1];
-    float* hnext = m->hsave[(t + 1) & 1];
+    const float* hprev = m->b.hsave[t & 1];
+    float* hnext = m->b.hsave[(t + 1) & 1];
     PrefillGroup g{};
     g.n = (int)std::min(ent.size() - e0, (size_t)m->p.prefill_group);
     bool finish = false;
@@ -364,20 +431,21 @@ int do_prefill(ocrdec_model* m, hipStream_t s, int B, const int32_t* slots_host,
       finish = finish || (p0 + g.cnt[j] == P);
       max_pos = std::max(max_pos, p0 + g.cnt[j] - 1);
     }
-    launch_plan_prefill<T>(s, g, vision, nv_stride, prompt, np_stride, wmat<T>(m, W_EMBED), c.vocab, m->plan_base,
-                           m->plan_cnt, m->plan_slot, m->x, m->esave);
+    launch_plan_prefill<T>(s, g, vision, nv_stride, prompt, np_stride, wmat<T>(m, W_EMBED), c.vocab, m->b.plan_base,
+                           m->b.plan_cnt, m->b.plan_slot, m->b.x, m->b.esave);
     const int M = g.n * PREFILL_CHUNK;
-    RowPlan plan{m->plan_base, m->plan_cnt, m->plan_slot, PREFILL_CHUNK, 0};
+    RowPlan plan{m->b.plan_base, m->b.plan_cnt, m->b.plan_slot, PREFILL_CHUNK, 0};
     const int nch = chunks_for(m, std::min(c.max_positions - 1, max_pos));
     verifier_layers<T>(m, s, prefill_path<T>(m), M, g.n, plan, nch, false, nullptr);
-    if (finish) lm_head<T>(m, s, m->x, PREFILL_CHUNK, true, wvec(m, W_FNORM), g.n, nullptr, m->tok_tmp, 1);
-    launch_draft_prefill_cat(s, g, m->x, m->esave, hprev, hnext, wvec(m, dw(m, D_NH)), wvec(m, dw(m, D_NE)),
-                             c.norm_eps, m->cat);
-    draft_layer<T>(m, s, prefill_path<T>(m), M, g.n, plan, nch, m->u, false);
-    if (finish) launch_prefill_finish(s, g, m->x, m->tok_tmp, m->sv, pending_out);
+    if (finish) lm_head<T>(m, s, m->b.x, PREFILL_CHUNK, true, wvec(m, W_FNORM), g.n, nullptr, m->b.tok_tmp, 1);
+    launch_draft_prefill_cat(s, g, m->b.x, m->b.esave, hprev, hnext, wvec(m, dw(m, D_NH)), wvec(m, dw(m, D_NE)),
+                             c.norm_eps, m->b.cat);
+    draft_layer<T>(m, s, prefill_path<T>(m), M, g.n, plan, nch, m->b.u, false);
+    if (finish) launch_prefill_finish(s, g, m->b.x, m->b.tok_tmp, m->sv, pending_out);
   }
   for (int b = 0; b < B; ++b) m->slot_bound[slots_host ? slots_host[b] : b] = nv_host[b] + np_host[b];
-  return hip_check("ocrdec_prefill");
+  m->lv_B = 0;
+  return hip_check(m, "ocrdec_prefill");
 }
 
 template <typename T>
@@ -388,8 +456,8 @@ int do_draft(ocrdec_model* m, hipStream_t s, int B, const int32_t* slots, int K,
   const int nch = chunks_for(m, std::min(c.max_positions - 1, call_bound(m, B, slots) + K));
   const PassPath pp = decode_path<T>(m);
   const int ident = slots == nullptr;
-  const RowPlan plan{m->plan_base, m->plan_cnt, m->plan_slot, Q, ident};
-  const RowPlan p1{m->plan_base, m->plan_cnt, m->plan_slot, 1, ident};
+  const RowPlan plan{m->b.plan_base, m->b.plan_cnt, m->b.plan_slot, Q, ident};
+  const RowPlan p1{m->b.plan_base, m->b.plan_cnt, m->b.plan_slot, 1, ident};
   if (pp.dense == DENSE_VECTOR) {
     // each pass's plan, input rows and fusion projection in one launch (pass j
     // >= 2 also takes d_{j-1} from the previous LM head's partials, so only the
@@ -398,35 +466,37 @@ int do_draft(ocrdec_model* m, hipStream_t s, int B, const int32_t* slots, int K,
     const int nblk = lmhead_blocks(c.vocab);
     const T* wf = wmat<T>(m, dw(m, D_FUSE));
     launch_draft_fuse<T>(s, 0, 1, Q, Q, K, slots, m->sv, wmat<T>(m, W_EMBED), c.vocab, wvec(m, dw(m, D_NH)),
-                         wvec(m, dw(m, D_NE)), c.norm_eps, nullptr, nullptr, nullptr, nblk, draft_out, m->plan_base,
-                         m->plan_cnt, m->plan_slot, wf, B * Q, m->u);
-    draft_layer<T>(m, s, pp, B * Q, B, plan, nch, m->u, true);
-    lm_head<T>(m, s, m->u, Q, true, wvec(m, dw(m, D_ONORM)), B, nullptr, K == 1 ? draft_out : nullptr, K);
-    float* uprev = m->u;
+                         wvec(m, dw(m, D_NE)), c.norm_eps, nullptr, nullptr, nullptr, nblk, draft_out, m->b.plan_base,
+                         m->b.plan_cnt, m->b.plan_slot, wf, B * Q, m->b.u);
+    draft_layer<T>(m, s, pp, B * Q, B, plan, nch, m->b.u, true);
+    lm_head<T>(m, s, m->b.u, Q, true, wvec(m, dw(m, D_ONORM)), B, nullptr, K == 1 ? draft_out : nullptr, K);
+    float* uprev = m->b.u;
     for (int j = 2; j <= K; ++j) {
-      float* u = (uprev == m->u) ? m->u2 : m->u;
+      float* u = (uprev == m->b.u) ? m->b.u2 : m->b.u;
       launch_draft_fuse<T>(s, 1, j, Q, (j == 2) ? Q : 1, K, nullptr, m->sv, wmat<T>(m, W_EMBED), c.vocab,
-                           wvec(m, dw(m, D_NH)), wvec(m, dw(m, D_NE)), c.norm_eps, uprev, m->lm_val, m->lm_idx, nblk,
-                           draft_out, m->plan_base, m->plan_cnt, m->plan_slot, wf, B, u);
+                           wvec(m, dw(m, D_NH)), wvec(m, dw(m, D_NE)), c.norm_eps, uprev, m->b.lm_val, m->b.lm_idx, nblk,
+                           draft_out, m->b.plan_base, m->b.plan_cnt, m->b.plan_slot, wf, B, u);
       draft_layer<T>(m, s, pp, B, B, p1, nch, u, true);
       lm_head<T>(m, s, u, 1, true, wvec(m, dw(m, D_ONORM)), B, nullptr, j == K ? draft_out + (j - 1) : nullptr, K);
       uprev = u;
     }
-    return hip_check("ocrdec_draft");
+    if (m->step_tap.drafts != nullptr) launch_draft_tap(s, B, K, m->b.plan_slot, m->sv, draft_out, m->step_tap);
+    return hip_check(m, "ocrdec_draft");
   }
   launch_plan_draft_catchup<T>(s, B, Q, slots, m->sv, wmat<T>(m, W_EMBED), c.vocab, wvec(m, dw(m, D_NH)),
-                               wvec(m, dw(m, D_NE)), c.norm_eps, m->plan_base, m->plan_cnt, m->plan_slot, m->cat);
-  draft_layer<T>(m, s, pp, B * Q, B, plan, nch, m->u, false);
-  lm_head<T>(m, s, m->u, Q, true, wvec(m, dw(m, D_ONORM)), B, nullptr, draft_out, K);
+                               wvec(m, dw(m, D_NE)), c.norm_eps, m->b.plan_base, m->b.plan_cnt, m->b.plan_slot, m->b.cat);
+  draft_layer<T>(m, s, pp, B * Q, B, plan, nch, m->b.u, false);
+  lm_head<T>(m, s, m->b.u, Q, true, wvec(m, dw(m, D_ONORM)), B, nullptr, draft_out, K);
   for (int j = 2; j <= K; ++j) {
     const int Qprev = (j == 2) ? Q : 1;
     launch_plan_draft_step<T>(s, B, j, Qprev, K, m->sv, draft_out, wmat<T>(m, W_EMBED), c.vocab,
-                              wvec(m, dw(m, D_NH)), wvec(m, dw(m, D_NE)), c.norm_eps, m->u, m->plan_base, m->plan_cnt,
-                              m->plan_slot, m->cat);
-    draft_layer<T>(m, s, pp, B, B, p1, nch, m->u, false);
-    lm_head<T>(m, s, m->u, 1, true, wvec(m, dw(m, D_ONORM)), B, nullptr, draft_out + (j - 1), K);
+                              wvec(m, dw(m, D_NH)), wvec(m, dw(m, D_NE)), c.norm_eps, m->b.u, m->b.plan_base, m->b.plan_cnt,
+                              m->b.plan_slot, m->b.cat);
+    draft_layer<T>(m, s, pp, B, B, p1, nch, m->b.u, false);
+    lm_head<T>(m, s, m->b.u, 1, true, wvec(m, dw(m, D_ONORM)), B, nullptr, draft_out + (j - 1), K);
   }
-  return hip_check("ocrdec_draft");
+  if (m->step_tap.drafts != nullptr) launch_draft_tap(s, B, K, m->b.plan_slot, m->sv, draft_out, m->step_tap);
+  return hip_check(m, "ocrdec_draft");
 }
 
 template <typename T>
@@ -435,15 +505,18 @@ int do_verify(ocrdec_model* m, hipStream_t s, int B, const int32_t* slots, int K
   const ocrdec_config& c = m->cfg;
   const int Q = K + 1, M = B * Q;
   const int nch = chunks_for(m, std::min(c.max_positions - 1, call_bound(m, B, slots) + K));
-  launch_plan_verify<T>(s, B, K, slots, m->sv, draft, wmat<T>(m, W_EMBED), c.vocab, m->plan_base, m->plan_cnt,
-                        m->plan_slot, m->x);
-  RowPlan plan{m->plan_base, m->plan_cnt, m->plan_slot, Q, slots == nullptr};
+  launch_plan_verify<T>(s, B, K, slots, m->sv, draft, wmat<T>(m, W_EMBED), c.vocab, m->b.plan_base, m->b.plan_cnt,
+                        m->b.plan_slot, m->b.x);
+  RowPlan plan{m->b.plan_base, m->b.plan_cnt, m->b.plan_slot, Q, slots == nullptr};
   verifier_layers<T>(m, s, decode_path<T>(m), M, B, plan, nch, true, m->router_override);
   m->last_verify_rows = M;
   // greedy_in_accept: the accept launch that follows reduces the greedy tokens
-  lm_head<T>(m, s, m->x, Q, false, wvec(m, W_FNORM), M, logits_out, greedy_in_accept ? nullptr : greedy_out, 1);
-  if (m->tap_hidden) launch_copy_rows(s, m->x, m->tap_hidden, (long)M * D);
-  return hip_check("ocrdec_verify");
+  lm_head<T>(m, s, m->b.x, Q, false, wvec(m, W_FNORM), M, logits_out, greedy_in_accept ? nullptr : greedy_out, 1);
+  if (m->taps.hidden) launch_copy_rows(s, m->b.x, m->taps.hidden, (long)M * D);
+  m->lv_B = B;
+  m->lv_K = K;
+  m->lv_slots = slots;
+  return hip_check(m, "ocrdec_verify");
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -511,48 +584,22 @@ int ocrdec_create(const ocrdec_config* cfg, const void* const* weight_ptrs, int 
   m->sv.out_len = ints + 4 * mb;
   m->sv.step = ints + 5 * mb;
   m->sv.prefix_len = ints + 6 * mb;
+  m->sv.ovf = ints + 7 * mb;
+  m->sv.max_pos = cfg->max_positions;
   m->sv.cu_tok = reinterpret_cast<int*>(m->state + p.s_cu);
   m->sv.cu_stride = p.cu_stride;
   m->sv.hbuf = reinterpret_cast<float*>(m->state + p.s_hbuf);
   m->sv.n_slots = mb;
   m->rope = reinterpret_cast<const float2*>(m->state + p.s_rope);
-  auto wf = [&](size_t off) { return reinterpret_cast<float*>(m->ws + off); };
-  auto wi = [&](size_t off) { return reinterpret_cast<int*>(m->ws + off); };
-  m->x = wf(p.w_x);
-  m->q = wf(p.w_q);
-  m->attn = wf(p.w_attn);
-  m->part = wf(p.w_part);
-  m->cat = wf(p.w_cat);
-  m->u = wf(p.w_u);
-  m->u2 = wf(p.w_u2);
-  m->dffn = wf(p.w_dffn);
-  m->esave = wf(p.w_esave);
-  m->hsave[0] = wf(p.w_hsave);
-  m->hsave[1] = wf(p.w_hsave) + (size_t)cfg->max_batch * D;
-  m->lm_val = wf(p.w_lmv);
-  m->lm_idx = wi(p.w_lmi);
-  const int pm = std::max(mb, PREFILL_GROUP);
-  m->plan_base = wi(p.w_plan);
-  m->plan_cnt = wi(p.w_plan) + pm;
-  m->plan_slot = wi(p.w_plan) + 2 * pm;
-  int* misc = wi(p.w_misc);
-  m->mb.n_act = misc;
-  m->tok_tmp = misc + 16;
-  m->mb.bnorm = wf(p.w_bnorm);
-  m->mb.ridx = wi(p.w_ridx);
-  m->mb.rgate = wf(p.w_rgate);
-  m->mb.perm = wi(p.w_perm);
-  m->mb.inv = wi(p.w_inv);
-  m->mb.off = wi(p.w_off);
-  m->mb.act = wi(p.w_act);
-  m->mb.slot_info = reinterpret_cast<int4*>(m->ws + p.w_slot);
-  m->mb.rlogit = wf(p.w_rlogit);
-  m->mb.stats = reinterpret_cast<long long*>(m->ws + p.w_stats);
-  m->mb.hx = wf(p.w_hx);
-  m->mb.y = wf(p.w_y);
+  m->b = bind_workspace(m->ws, p, mb);
+  int* misc = m->b.mb.n_act;
   m->slot_bound.assign(cfg->max_batch, 0);
-  m->tap_route = nullptr;
-  m->tap_hidden = nullptr;
+  m->taps = ocrdec_taps{};
+  m->step_tap = StepTap{};
+  m->launch_fail = nullptr;
+  m->lv_B = 0;
+  m->lv_K = 0;
+  m->lv_slots = nullptr;
   m->timing = false;
   m->ev_used = 0;
   m->stats_base = 0;
@@ -563,7 +610,7 @@ int ocrdec_create(const ocrdec_config* cfg, const void* const* weight_ptrs, int 
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // clear an error left by earlier, unrelated runtime calls
   hipError_t err = hipMemsetAsync(misc, 0, 64 * 4, s);
-  if (err == hipSuccess) err = hipMemsetAsync(m->mb.stats, 0, 64, s);
+  if (err == hipSuccess) err = hipMemsetAsync(m->b.mb.stats, 0, 64, s);
   if (err == hipSuccess) err = hipMemsetAsync(m->state + p.s_ints, 0, p.s_hbuf - p.s_ints, s);
   if (err == hipSuccess) {
     launch_rope_table(s, cfg->max_positions, cfg->rope_theta, reinterpret_cast<float2*>(m->state + p.s_rope));
@@ -644,11 +691,16 @@ int ocrdec_accept_rollback(ocrdec_model* m, void* stream, int B, const int32_t* 
   if (rc) return rc;
   if (!greedy || (K > 0 && !draft)) return fail(OCRDEC_EINVAL, "greedy is null, or draft is null with K > 0");
   if (out_tokens && out_cap < 1) return fail(OCRDEC_EINVAL, "out_cap must be >= 1 with out_tokens");
+  if (m->lv_B == 0) return fail(OCRDEC_EINVAL, "ocrdec_accept_rollback must follow an ocrdec_verify call");
+  if (B != m->lv_B || K != m->lv_K || slots != m->lv_slots)
+    return fail(OCRDEC_EINVAL, "ocrdec_accept_rollback must take the B, K and slots of the verify it follows");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  launch_accept(s, B, K, m->plan_slot, draft, greedy, m->x, m->sv, n_accepted_out, out_tokens, out_len, out_cap);
+  launch_accept(s, B, K, m->b.plan_slot, draft, greedy, m->b.x, m->sv, n_accepted_out, out_tokens, out_len, out_cap,
+                m->step_tap);
+  m->lv_B = 0;
   const int n = slots ? (int)m->slot_bound.size() : B;
   for (int i = 0; i < n; ++i) m->slot_bound[i] = std::min(m->cfg.max_positions, m->slot_bound[i] + K + 1);
-  return hip_check("ocrdec_accept_rollback");
+  return hip_check(m, "ocrdec_accept_rollback");
 }
 
 int ocrdec_controlled_drafts(ocrdec_model* m, void* stream, int B, const int32_t* slots, int K, const int32_t* trace,
@@ -659,7 +711,7 @@ int ocrdec_controlled_drafts(ocrdec_model* m, void* stream, int B, const int32_t
     return fail(OCRDEC_EINVAL, "bad controlled-draft arguments");
   hipStream_t s = static_cast<hipStream_t>(stream);
   launch_controlled(s, B, K, slots, m->sv, trace, trace_stride, trace_len, seed, threshold, m->cfg.vocab, draft_inout);
-  return hip_check("ocrdec_controlled_drafts");
+  return hip_check(m, "ocrdec_controlled_drafts");
 }
 
 int ocrdec_replay_expert_gate_up(ocrdec_model* m, void* stream, int n_rounds, int* expert_sets_per_launch) {
@@ -669,18 +721,18 @@ int ocrdec_replay_expert_gate_up(ocrdec_model* m, void* stream, int n_rounds, in
   if (expert_sets_per_launch) {
     int na = 0;
     if (hipStreamSynchronize(s) != hipSuccess ||
-        hipMemcpy(&na, m->mb.n_act, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess)
+        hipMemcpy(&na, m->b.mb.n_act, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess)
       return fail(OCRDEC_EHIP, "reading the active-expert count failed");
     *expert_sets_per_launch = na;
   }
   const int M = m->last_verify_rows;
   for (int r = 0; r < n_rounds; ++r) {
     for (int l = 0; l < m->cfg.n_layers; ++l) {
-      if (m->cfg.dtype == OCRDEC_BF16) expert_gate_up<bf16>(m, s, l, M, nullptr, decode_path<bf16>(m).experts);
-      else expert_gate_up<float>(m, s, l, M, nullptr, false);
+      if (m->cfg.dtype == OCRDEC_BF16) expert_gate_up<bf16>(m, s, l, M, decode_path<bf16>(m).experts);
+      else expert_gate_up<float>(m, s, l, M, false);
     }
   }
-  return hip_check("ocrdec_replay_expert_gate_up");
+  return hip_check(m, "ocrdec_replay_expert_gate_up");
 }
 
 int ocrdec_read_probe(void* stream, const void* buf, size_t bytes, int n_regions, int n_launches, uint32_t* sink) {
@@ -689,7 +741,7 @@ int ocrdec_read_probe(void* stream, const void* buf, size_t bytes, int n_regions
   hipStream_t s = static_cast<hipStream_t>(stream);
   for (int i = 0; i < n_launches; ++i)
     launch_read_probe(s, static_cast<const char*>(buf) + (size_t)(i % n_regions) * bytes, (long)(bytes / 16), sink);
-  return hip_check("ocrdec_read_probe");
+  return hip_check(nullptr, "ocrdec_read_probe");
 }
 
 int ocrdec_decode_steps(ocrdec_model* m, void* stream, int B, const int32_t* slots, int K, int n_steps,
@@ -710,10 +762,16 @@ int ocrdec_decode_steps(ocrdec_model* m, void* stream, int B, const int32_t* slo
     if (!slots && bound + K + 1 > m->cfg.max_positions)
       return fail(OCRDEC_ECAPACITY, "positions would exceed max_positions");
     const int nch = chunks_for(m, std::min(m->cfg.max_positions - 1, bound + K));
+    // everything a recorded step bakes in: the call's shape and pointers, the
+    // router override and the taps
     std::vector<uintptr_t> key = {(uintptr_t)B, (uintptr_t)K, (uintptr_t)nch, (uintptr_t)slots,
                                   (uintptr_t)draft, (uintptr_t)greedy, (uintptr_t)n_accepted_out,
                                   (uintptr_t)out_tokens, (uintptr_t)out_len, (uintptr_t)out_cap,
-                                  (uintptr_t)m->tap_route, (uintptr_t)m->tap_hidden};
+                                  (uintptr_t)m->router_override, (uintptr_t)m->taps.route_idx,
+                                  (uintptr_t)m->taps.hidden, (uintptr_t)m->taps.route_pos,
+                                  (uintptr_t)m->taps.route_pos_slot, (uintptr_t)m->taps.route_pos_cap,
+                                  (uintptr_t)m->step_tap.acc, (uintptr_t)m->step_tap.drafts,
+                                  (uintptr_t)m->step_tap.cap};
     if (ctrl) {
       key.push_back((uintptr_t)ctrl->trace);
       key.push_back((uintptr_t)ctrl->trace_stride);
@@ -742,8 +800,9 @@ int ocrdec_decode_steps(ocrdec_model* m, void* stream, int B, const int32_t* slo
         r1 = m->cfg.dtype == OCRDEC_BF16 ? do_verify<bf16>(m, cs, B, slots, K, draft, greedy, nullptr, true)
                                          : do_verify<float>(m, cs, B, slots, K, draft, greedy, nullptr, true);
       if (r1 == OCRDEC_OK)
-        launch_accept(cs, B, K, m->plan_slot, draft, greedy, m->x, m->sv, n_accepted_out, out_tokens, out_len,
-                      out_cap, m->lm_val, m->lm_idx, lmhead_blocks(m->cfg.vocab), greedy);
+        launch_accept(cs, B, K, m->b.plan_slot, draft, greedy, m->b.x, m->sv, n_accepted_out, out_tokens, out_len,
+                      out_cap, m->step_tap, m->b.lm_val, m->b.lm_idx, lmhead_blocks(m->cfg.vocab), greedy);
+      m->lv_B = 0;
       hipGraph_t graph = nullptr;
       const hipError_t ec = hipStreamEndCapture(cs, &graph);
       if (r1 != OCRDEC_OK || ec != hipSuccess) {
@@ -768,11 +827,21 @@ int ocrdec_decode_steps(ocrdec_model* m, void* stream, int B, const int32_t* slo
 int ocrdec_sync_positions(ocrdec_model* m, void* stream) {
   if (!m) return fail(OCRDEC_EINVAL, "model is null");
   const int n = m->cfg.max_batch;
-  std::vector<int> kv(n);
+  std::vector<int> kv(n), ovf(n);
   if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess ||
-      hipMemcpy(kv.data(), m->sv.kv_len, (size_t)n * sizeof(int), hipMemcpyDeviceToHost) != hipSuccess)
+      hipMemcpy(kv.data(), m->sv.kv_len, (size_t)n * sizeof(int), hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemcpy(ovf.data(), m->sv.ovf, (size_t)n * sizeof(int), hipMemcpyDeviceToHost) != hipSuccess)
     return fail(OCRDEC_EHIP, "reading the cache lengths failed");
   for (int i = 0; i < n; ++i) m->slot_bound[i] = std::max(0, std::min(kv[i], m->cfg.max_positions));
+  std::string over;
+  for (int i = 0; i < n; ++i)
+    if (ovf[i]) over += (over.empty() ? "" : ", ") + std::to_string(i);
+  if (!over.empty()) {
+    const std::vector<int> zero(n, 0);
+    if (hipMemcpy(m->sv.ovf, zero.data(), (size_t)n * sizeof(int), hipMemcpyHostToDevice) != hipSuccess)
+      return fail(OCRDEC_EHIP, "clearing the overflow flags failed");
+    return fail(OCRDEC_ECAPACITY, "slot(s) " + over + ": a step would pass max_positions and was not taken");
+  }
   return OCRDEC_OK;
 }
 
@@ -804,13 +873,24 @@ int ocrdec_load_sequence(ocrdec_model* m, void* stream, int slot, int n_pos, int
   }
   launch_set_sequence(s, slot, n_pos, pending_token, m->sv);
   m->slot_bound[slot] = n_pos;
-  return hip_check("ocrdec_load_sequence");
+  m->lv_B = 0;
+  return hip_check(m, "ocrdec_load_sequence");
 }
 
-int ocrdec_set_taps(ocrdec_model* m, int32_t* route_idx, float* hidden) {
+int ocrdec_set_taps(ocrdec_model* m, const ocrdec_taps* taps) {
   if (!m) return fail(OCRDEC_EINVAL, "model is null");
-  m->tap_route = route_idx;
-  m->tap_hidden = hidden;
+  if (taps == nullptr) {
+    m->taps = ocrdec_taps{};
+    m->step_tap = StepTap{};
+    return OCRDEC_OK;
+  }
+  if (taps->route_pos != nullptr &&
+      (taps->route_pos_slot < 0 || taps->route_pos_slot >= m->cfg.max_batch || taps->route_pos_cap < 1))
+    return fail(OCRDEC_EINVAL, "route_pos needs a slot in [0, max_batch) and route_pos_cap >= 1");
+  if ((taps->accepted != nullptr || taps->drafts != nullptr) && taps->step_cap < 1)
+    return fail(OCRDEC_EINVAL, "step taps need step_cap >= 1");
+  m->taps = *taps;
+  m->step_tap = StepTap{taps->accepted, taps->drafts, taps->step_cap};
   return OCRDEC_OK;
 }
 
@@ -820,7 +900,7 @@ int ocrdec_expert_timing(ocrdec_model* m, int enable) {
   m->ev_used = 0;
   m->stats_base = 0;
   if (hipDeviceSynchronize() != hipSuccess ||
-      hipMemcpy(&m->stats_base, m->mb.stats, sizeof(long long), hipMemcpyDeviceToHost) != hipSuccess)
+      hipMemcpy(&m->stats_base, m->b.mb.stats, sizeof(long long), hipMemcpyDeviceToHost) != hipSuccess)
     return fail(OCRDEC_EHIP, "reading the expert counter failed");
   return OCRDEC_OK;
 }
@@ -843,7 +923,7 @@ int ocrdec_expert_stats(ocrdec_model* m, double* ms_gate_up, long long* n_gate_u
     ++nb;
   }
   long long sets = 0;
-  if (hipMemcpy(&sets, m->mb.stats, sizeof(long long), hipMemcpyDeviceToHost) != hipSuccess)
+  if (hipMemcpy(&sets, m->b.mb.stats, sizeof(long long), hipMemcpyDeviceToHost) != hipSuccess)
     return fail(OCRDEC_EHIP, "hipMemcpy of the expert counter failed");
   if (ms_gate_up) *ms_gate_up = a;
   if (n_gate_up) *n_gate_up = na;

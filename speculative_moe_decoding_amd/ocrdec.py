@@ -1,4 +1,5 @@
-"""Python binding of the ``ocrdec`` C ABI (include/ocrdec.h).
+"""Python binding of the ``ocrdec`` C ABI (include/ocrdec.h, and the harness
+calls of include/ocrdec_harness.h).
 
 Argument marshalling only: every step of the decode path runs in the HIP
 kernels of libocrdec.so.  PyTorch supplies device memory and the stream.
@@ -41,6 +42,12 @@ class ocrdec_controlled_cfg(ctypes.Structure):
                 ("seed", ctypes.c_uint64), ("threshold", ctypes.c_uint64)]
 
 
+class ocrdec_taps(ctypes.Structure):
+    _fields_ = [("route_idx", ctypes.c_void_p), ("hidden", ctypes.c_void_p), ("route_pos", ctypes.c_void_p),
+                ("route_pos_slot", ctypes.c_int), ("route_pos_cap", ctypes.c_int), ("accepted", ctypes.c_void_p),
+                ("drafts", ctypes.c_void_p), ("step_cap", ctypes.c_int)]
+
+
 class OcrdecError(RuntimeError):
     def __init__(self, fn: str, code: int, msg: str):
         super().__init__(f"{fn} failed ({code}): {msg}")
@@ -71,7 +78,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "ocrdec_verify": (I, [P, P, I, P, I, P, P, P]),
         "ocrdec_accept_rollback": (I, [P, P, I, P, I, P, P, P, P, P, I]),
         "ocrdec_controlled_drafts": (I, [P, P, I, P, I, P, I, I, U64, U64, P]),
-        "ocrdec_set_taps": (I, [P, P, P]),
+        "ocrdec_set_taps": (I, [P, ctypes.POINTER(ocrdec_taps)]),
         "ocrdec_expert_timing": (I, [P, I]),
         "ocrdec_expert_stats": (I, [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_longlong),
                                     ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_longlong),
@@ -175,8 +182,19 @@ def ocrdec_set_router_logits(h, logits=None) -> None:
     _check("ocrdec_set_router_logits", load_library().ocrdec_set_router_logits(h, _ptr(logits)))
 
 
-def ocrdec_set_taps(h, route_idx=None, hidden=None):
-    _check("ocrdec_set_taps", load_library().ocrdec_set_taps(h, _ptr(route_idx), _ptr(hidden)))
+def ocrdec_set_taps(h, route_idx=None, hidden=None, route_pos=None, route_pos_slot=0, accepted=None, drafts=None):
+    """Parity taps (see ocrdec_harness.h).  route_pos: int32 [n_layers][cap][8] for slot
+    route_pos_slot; accepted: int32 [max_batch][cap]; drafts: int32 [max_batch][cap][8]."""
+    if all(t is None for t in (route_idx, hidden, route_pos, accepted, drafts)):
+        _check("ocrdec_set_taps", load_library().ocrdec_set_taps(h, None))
+        return
+    cap = 0
+    for t in (accepted, drafts):
+        if t is not None:
+            cap = int(t.shape[1])
+    taps = ocrdec_taps(_ptr(route_idx), _ptr(hidden), _ptr(route_pos), int(route_pos_slot),
+                       0 if route_pos is None else int(route_pos.shape[1]), _ptr(accepted), _ptr(drafts), cap)
+    _check("ocrdec_set_taps", load_library().ocrdec_set_taps(h, ctypes.byref(taps)))
 
 
 def ocrdec_expert_timing(h, enable: bool):

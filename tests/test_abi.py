@@ -1,4 +1,5 @@
-"""The C-ABI library loads, exports every function include/ocrdec.h declares,
+"""The C-ABI library loads, exports every function include/ocrdec.h and
+include/ocrdec_harness.h declare,
 and its host-only entry points (sizes, argument checks) behave as documented.
 No GPU compute is launched here."""
 import ctypes
@@ -11,13 +12,16 @@ import pytest
 from speculative_moe_decoding_amd import ocrdec, synth
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "ocrdec.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 
 def declared_functions():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(ocrdec_\w+)\s*\(", src)))
+    names = set()
+    for h in HEADERS:
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(ocrdec_\w+)\s*\(", src))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -97,7 +101,7 @@ def test_rejects_bad_paths_and_null_handles(lib):
     assert lib.ocrdec_sync_positions(None, None) == E
     assert lib.ocrdec_load_sequence(None, None, 0, 16, 0, None) == E
     assert lib.ocrdec_set_router_logits(None, None) == E
-    assert lib.ocrdec_set_taps(None, None, None) == E
+    assert lib.ocrdec_set_taps(None, None) == E
     assert lib.ocrdec_expert_timing(None, 1) == E
     assert lib.ocrdec_replay_expert_gate_up(None, None, 1, None) == E
     assert lib.ocrdec_read_probe(None, None, 256, 1, 1, None) == E

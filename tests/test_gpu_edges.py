@@ -17,19 +17,12 @@ torch = pytest.importorskip("torch")
 if not torch.cuda.is_available():
     pytest.skip("needs a GPU", allow_module_level=True)
 
-from gpu_util import compare_steps, log, make_pair, run_gpu_steps  # noqa: E402
+from gpu_util import compare_steps, forced_ar_parity, log, make_pair, run_gpu_steps  # noqa: E402
 from speculative_moe_decoding_amd import ocrdec  # noqa: E402
 
 
 def _ar_vs_oracle(dec, orc, page, N, tol):
-    g_ar, g_steps = run_gpu_steps(dec, page, N, 0)
-    r_ar, r_logits = orc.generate_ar(page.vision, page.prompt, N, keep_logits=True)
-    if g_ar[0] != r_ar[0]:
-        assert od.top2_margin(r_logits[0]) < tol, "first token differs without a near tie"
-        return g_ar, 0, 0.0
-    ref = [od.StepRecord(0, [], [r_ar[i + 1]], 0, r_logits[i + 1][None]) for i in range(N - 1)]
-    n, worst, note = compare_steps(g_steps, ref, tol)
-    assert worst < tol
+    g_ar, n, ex, worst = forced_ar_parity(dec, orc, page, N, tol, min_steps=N - 1)
     return g_ar, n, worst
 
 
@@ -55,7 +48,7 @@ def test_max_draft_length():
     r_sp, r_ss = orc.generate_spec(page.vision, page.prompt, N, 7, keep_logits=True)
     n, worst, note = compare_steps(g_ss, r_ss, 5e-2)
     log(f"K=7: {n}/{len(r_ss)} steps agree, max |dlogit| {worst:.2e}, {note}")
-    assert worst < 5e-2 and n >= 2
+    assert worst < 5e-2 and (n >= 4 or note is not None)
     # controlled drafts at K = 7: every slot right (threshold 0) accepts all 7
     trace = torch.from_numpy(np.asarray(g_ar + [0] * 16, dtype=np.int32)[None]).cuda()
     toks, acc, _ = dec.generate([page], 24, 7, trace=trace, seed=1, threshold=0, record=True, check_every=1)
@@ -123,3 +116,79 @@ def test_max_rows_per_call():
         dec.verify(1, K, torch.from_numpy(drafts[b:b + 1]).cuda(), slots=slot, logits=one)
         torch.cuda.synchronize()
         assert np.array_equal(one.cpu().numpy()[0], g_logits[b]), b
+
+
+def test_capacity_with_slot_map():
+    """A slot-mapped batch run to the cache limit: the step that would pass
+    max_positions is not taken for that sequence (no cache write, state and
+    output unchanged, n = -1), the other sequence goes on, and the next
+    ocrdec_sync_positions reports OCRDEC_ECAPACITY naming the slot; the tokens
+    committed before the limit equal those of a roomy handle."""
+    cfg = dataclasses.replace(synth.FULL, n_layers=2, vocab=3001, dtype="bf16")
+    w = synth.Weights(cfg, 81)
+    pages = synth.make_pages(cfg, 82, [10, 3], [2, 2], [40, 40])
+    K = 3
+    tight = ocrdec.Decoder(cfg, w.device_arrays(), max_batch=2, max_k=K, max_positions=32)
+    roomy = ocrdec.Decoder(cfg, w.device_arrays(), max_batch=2, max_k=K, max_positions=256)
+    ref, _, _ = roomy.generate(pages, 40, K, check_every=1)
+    slots = torch.tensor([1, 0], dtype=torch.int32, device="cuda")     # page b sits in slot 1 - b
+    out = torch.zeros(2, 64, dtype=torch.int32, device="cuda")
+    out[:, 0] = tight.prefill(pages, slots=[1, 0])
+    draft, greedy, n_acc, out_len = tight.i32(2, K), tight.i32(2, K + 1), tight.i32(2), tight.i32(2)
+    refused = None
+    lens_hist = []
+    for step in range(40):
+        tight.draft(2, K, slots=slots, out=draft)
+        tight.verify(2, K, draft, slots=slots, greedy=greedy)
+        tight.accept(2, K, draft, greedy, n_acc, out, out_len, slots=slots)
+        try:
+            ocrdec.ocrdec_sync_positions(tight.h, tight.stream)
+        except ocrdec.OcrdecError as e:
+            assert e.code == ocrdec.OCRDEC_ECAPACITY
+            refused = (step, str(e), n_acc.cpu().numpy().tolist())
+            break
+        lens_hist.append(out_len.cpu().numpy().tolist())
+    assert refused is not None, "the cache limit was never reached"
+    step, msg, na = refused
+    # page 0 (prefix 12, slot 1) reaches the 32-position limit first
+    assert "slot(s) 1" in msg and na[0] == -1 and na[1] >= 0, (msg, na)
+    lens = out_len.cpu().numpy().tolist()
+    assert lens[0] == lens_hist[-1][0]
+    got = out.cpu().numpy()
+    for b in range(2):
+        assert got[b, :lens[b]].tolist() == ref[b, :lens[b]].tolist(), b
+    # and it goes on being refused, without touching the sequence
+    tight.draft(2, K, slots=slots, out=draft)
+    tight.verify(2, K, draft, slots=slots, greedy=greedy)
+    tight.accept(2, K, draft, greedy, n_acc, out, out_len, slots=slots)
+    with pytest.raises(ocrdec.OcrdecError):
+        ocrdec.ocrdec_sync_positions(tight.h, tight.stream)
+    assert out_len.cpu().numpy().tolist()[0] == lens[0]
+    log(f"slot map at the cache limit: step {step} refused for slot 1 ({msg}); committed tokens match")
+
+
+def test_accept_must_follow_its_verify():
+    """ocrdec_accept_rollback takes the B, K and slots of the verify it
+    follows, once; anything else is refused before any launch."""
+    cfg = dataclasses.replace(synth.FULL, n_layers=1, vocab=301, dtype="f32")
+    w = synth.Weights(cfg, 83)
+    page = synth.make_pages(cfg, 84, [4], [2], [8])[0]
+    dec = ocrdec.Decoder(cfg, w.device_arrays(), max_batch=2, max_k=3, max_positions=64)
+    dec.prefill([page])
+    draft, greedy, n_acc, out_len = dec.i32(1, 3), dec.i32(1, 4), dec.i32(1), dec.i32(1)
+    out = torch.zeros(1, 16, dtype=torch.int32, device="cuda")
+    with pytest.raises(ocrdec.OcrdecError) as e:           # no verify yet
+        dec.accept(1, 3, draft, greedy, n_acc, out, out_len)
+    assert e.value.code == ocrdec.OCRDEC_EINVAL
+    dec.draft(1, 3, out=draft)
+    dec.verify(1, 3, draft, greedy=greedy)
+    with pytest.raises(ocrdec.OcrdecError):                # another K
+        ocrdec.ocrdec_accept_rollback(dec.h, dec.stream, 1, None, 2, draft, greedy, n_acc, out, out_len, 16)
+    slot0 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    with pytest.raises(ocrdec.OcrdecError):                # another slot map
+        dec.accept(1, 3, draft, greedy, n_acc, out, out_len, slots=slot0)
+    dec.accept(1, 3, draft, greedy, n_acc, out, out_len)    # the matching one
+    with pytest.raises(ocrdec.OcrdecError):                # only once
+        dec.accept(1, 3, draft, greedy, n_acc, out, out_len)
+    torch.cuda.synchronize()
+    assert 0 <= int(n_acc.item()) <= 3

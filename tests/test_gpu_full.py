@@ -3,13 +3,14 @@
 * 2-layer fp32 model, vocab 129,280, prefix 256 vision + 16 prompt rows, 64
   output tokens: AR and FastMTP K=3 with the real draft block, step by step
   against the oracle (tokens, drafts, accepted lengths exact; logits 1e-3).
-* 12-layer bf16 model (the benchmarked decoder), prefix 256 + 32: the first
-  decode steps against the oracle (logits 5e-2), speculative output equal to
-  AR output for the real draft and for the controlled-acceptance drafts at
-  K = 1, 2, 3, with accepted lengths equal to the oracle's prediction, in the
-  launch configuration bench.py times (batch 1, one stream, eager).
+* 12-layer bf16 model (the benchmarked decoder), prefix 256 + 32:
+  speculative output equal to AR output for the real draft and for the
+  controlled-acceptance drafts at K = 1, 2, 3, with accepted lengths equal to
+  the oracle's prediction (batch 1, one stream, eager).
 * Gundam page (1,156 + 32 prefix, 3,568 tokens, cache past 4,096 positions):
-  lossless with graphs, accepted lengths, first steps against the oracle.
+  lossless with graphs, accepted lengths.
+The bf16 decoder's tokens, routing and logits are checked against the oracle
+in test_gpu_teacher.py (teacher-forced, whole pages).
 """
 import dataclasses
 import time
@@ -66,22 +67,6 @@ def full():
     return w, dec, orc, page
 
 
-def test_full_model_first_steps_vs_oracle(full):
-    w, dec, orc, page = full
-    N = 6
-    g_ar, g_steps = run_gpu_steps(dec, page, N, 0)
-    t = time.time()
-    r_ar, r_logits = orc.generate_ar(page.vision, page.prompt, N, keep_logits=True)
-    log(f"oracle 12-layer prefill + {N} tokens: {time.time() - t:.1f}s")
-    ref = [od.StepRecord(0, [], [r_ar[i + 1]], 0, r_logits[i + 1][None]) for i in range(N - 1)]
-    if g_ar[0] != r_ar[0]:
-        assert od.top2_margin(r_logits[0]) < 5e-2, "first token differs without a near tie"
-        pytest.skip("excused near tie on the first token")
-    n, worst, note = compare_steps(g_steps, ref, 5e-2)
-    log(f"12-layer bf16 AR: {n}/{N - 1} steps agree, max |dlogit| {worst:.3e}, {note}")
-    assert worst < 5e-2
-
-
 def test_full_model_lossless(full):
     w, dec, orc, page = full
     N = 400
@@ -108,9 +93,8 @@ def test_gundam_page_lossless(full):
     at 57.6 % controlled acceptance, so the cache grows from 1,188 to 4,756
     positions (a handle past 4,096 positions uses 256-key attention chunks).
     The whole page is lossless against the K = 0 run (decode-step graphs);
-    accepted lengths equal the SplitMix64 prediction over the first 600 tokens;
-    the first decode steps agree with the oracle."""
-    w, _, orc, _ = full
+    accepted lengths equal the SplitMix64 prediction over the first 600 tokens."""
+    w, _, _, _ = full
     wl = synth.WORKLOADS["gundam_page_bf16"]
     cfg = wl["cfg"]
     from speculative_moe_decoding_amd import ocrdec
@@ -132,15 +116,3 @@ def test_gundam_page_lossless(full):
     toks, acc, _ = dec.generate([page], n_rec, 3, trace=trace, seed=3000, threshold=thr, record=True, check_every=8)
     assert toks[0].tolist() == ar[0][:n_rec].tolist()
     assert acc[0] == od.controlled_accepts(n_rec, 3, 3000, p)
-    n_chk = 4
-    _, g_steps = run_gpu_steps(dec, page, n_chk, 0)
-    t = time.time()
-    r_ar, r_logits = orc.generate_ar(page.vision, page.prompt, n_chk, keep_logits=True)
-    log(f"oracle 12-layer {P}-row prefill + {n_chk} tokens: {time.time() - t:.1f}s")
-    if int(ar[0][0]) != r_ar[0]:
-        assert od.top2_margin(r_logits[0]) < 5e-2, "first token differs without a near tie"
-        return
-    ref = [od.StepRecord(0, [], [r_ar[i + 1]], 0, r_logits[i + 1][None]) for i in range(n_chk - 1)]
-    n, worst, note = compare_steps(g_steps, ref, 5e-2)
-    log(f"Gundam page vs oracle: {n}/{n_chk - 1} steps agree, max |dlogit| {worst:.3e}, {note}")
-    assert worst < 5e-2

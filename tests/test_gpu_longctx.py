@@ -3,10 +3,11 @@ vocabulary) verifying 4 rows per sequence at positions 32,764..32,767 against a
 loaded cache of 32,764 positions (keys / values ~ N(0, 1) in bf16), with the
 skewed synthetic routing (router logits = log pi + Gumbel, pi ~ rank^-1.1).
 
-Batch 1 runs the vector path, batch 4 the matrix path (16 rows per call).  The
-logits of a sampled sequence's rows match the oracle (5e-2; greedy tokens
-exact unless the oracle's top-2 margin is under that), and the routing taps
-equal the oracle's selection from the same logits."""
+Batch 1 runs the vector path, batches 4, 16 and 64 the matrix path (16, 64
+and 256 rows per call).  The logits of the first and last sequence's rows
+match the oracle (5e-2; greedy tokens exact unless the oracle's top-2 margin
+is under that), and the routing taps equal the oracle's selection from the
+same logits."""
 import dataclasses
 
 import numpy as np
@@ -39,10 +40,11 @@ def setup():
     return wl, cfg, w, n_pos, kv_bits, kv_dev, orc
 
 
-@pytest.mark.parametrize("B", [1, 4])
+@pytest.mark.parametrize("B", [1, 4, 16, 64])
 def test_longctx_layer_vs_oracle(setup, B):
     wl, cfg, w, n_pos, kv_bits, kv_dev, orc = setup
     K = 3
+    log(f"case B={B}")
     dec = ocrdec.Decoder(cfg, w.device_arrays(), max_batch=B, max_k=K, max_positions=n_pos + K + 1)
     rng = np.random.default_rng([wl["input_seed"], B])
     pend = rng.integers(0, cfg.vocab, size=B)

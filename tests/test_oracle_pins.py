@@ -384,3 +384,118 @@ def test_gain_and_norm_terms_matter():
         m2 = od.Oracle(TINY, w)
         other = m2.lm_logits(m2.verifier_forward(m2.new_state(16), e, np.arange(8))[-1:])
         assert np.abs(other - base).max() > 1e-4, name
+
+
+# ---------------------------------------------------------------- parity helpers
+
+def test_top2_margin_worked_values():
+    """The excuse of every token mismatch: largest minus second-largest logit,
+    worked by hand (unsorted input, negatives, a tie of the two largest, a
+    repeated maximum among three, rows independent)."""
+    x = np.array([[1.0, 3.5, 2.0],            # 3.5 - 2.0
+                  [-1.0, -3.0, -0.25],        # -0.25 - (-1.0)
+                  [5.0, 5.0, 1.0],            # tie of the two largest -> 0
+                  [0.0, 7.0, 7.0],            # tie at the top again, not 7 - 0
+                  [4.0, -2.0, 3.9]])          # 4.0 - 3.9, not |4.0 - (-2.0)| (the first two) or a min gap
+    np.testing.assert_allclose(od.top2_margin(x), [1.5, 0.75, 0.0, 0.0, 0.1], atol=1e-15)
+    # brute force over pairs on random rows: the margin is the largest value minus the largest of the rest
+    rng = np.random.default_rng(3)
+    r = rng.standard_normal((20, 9))
+    for row, got in zip(r, od.top2_margin(r)):
+        best = max(row)
+        rest = max(v for i, v in enumerate(row) if i != int(np.argmax(row)))
+        assert got == best - rest
+        assert got >= 0.0
+
+
+def test_teacher_forced_matches_autoregressive_run():
+    """Run along the oracle's own greedy sequence, the batched teacher-forced
+    pass predicts every token of it and gives the row-wise AR loop's logits
+    (the same definition, computed in one pass over the positions)."""
+    m = tiny_model(scale=8.0)
+    vision, prompt = tiny_page()
+    N = 16
+    ar, lg = m.generate_ar(vision, prompt, N, keep_logits=True)
+    for chunk in (3, 64):
+        g, mg, kept, st = m.teacher_forced(vision, prompt, ar, chunk=chunk, keep_at=(0, 5, N - 1))
+        assert g.tolist() == ar
+        np.testing.assert_allclose(mg, od.top2_margin(np.array(lg)), rtol=1e-9, atol=1e-12)
+        for t, row in kept.items():
+            np.testing.assert_allclose(row, lg[t], rtol=1e-9, atol=1e-12)
+        assert st.kv_len == vision.shape[0] + len(prompt) + N - 1
+    # a token sequence that is not the greedy one is predicted only where it agrees
+    other = list(ar)
+    other[4] = (other[4] + 1) % TINY.vocab
+    g, _, _, _ = m.teacher_forced(vision, prompt, other)
+    assert g[4] == ar[4] != other[4]
+
+
+def test_routing_pick_hook():
+    """The parity hook that lets the oracle follow another implementation's
+    routing: returning the oracle's own choice changes nothing; a different
+    choice is used, with the softmax gate of the expert it names."""
+    m = tiny_model(scale=8.0)
+    vision, prompt = tiny_page()
+    e = m.prefix_rows(vision, prompt)
+    base = m.verifier_forward(m.new_state(16), e, np.arange(8))
+    same = m.verifier_forward(m.new_state(16), e, np.arange(8), pick=lambda l, pos, lg, ix: ix)
+    np.testing.assert_array_equal(same, base)
+    seen = []
+
+    def swap_last(l, pos, lg, ix):
+        ix = ix.copy()
+        if l == 1:
+            # row 0 of layer 1 takes its third-best expert instead of the second
+            order = np.lexsort((np.arange(lg.shape[1]), -lg[0]))
+            ix[0, 1] = order[2]
+            seen.append((lg[0].copy(), int(order[2])))
+        return ix
+    other = m.verifier_forward(m.new_state(16), e, np.arange(8), pick=swap_last)
+    assert np.abs(other[0] - base[0]).max() > 1e-6
+    # layer 1 (the last) acts row by row (a BLAS product over a different row subset may round differently)
+    np.testing.assert_allclose(other[1:], base[1:], rtol=1e-12, atol=1e-14)
+    # the changed row: recompute layer 1's MoE term by hand with the picked expert
+    st = m.new_state(16)
+    x = np.asarray(e, np.float64).copy()
+    pos = np.arange(8)
+    x = m.attention_block(x, pos, "l0.attn_norm", "l0.wqkv", "l0.wo", st.kv[0, 0], st.kv[0, 1])
+    b = od.rmsnorm(x, m.w["l0.ffn_norm"], TINY.norm_eps)
+    y, _ = od.moe(b, m.W("l0.router"), m.w["l0.w_gate"], m.w["l0.w_up"], m.w["l0.w_down"], TINY.n_experts,
+                  TINY.n_shared, TINY.top_k)
+    x = x + y
+    x = m.attention_block(x, pos, "l1.attn_norm", "l1.wqkv", "l1.wo", st.kv[1, 0], st.kv[1, 1])
+    b = od.rmsnorm(x, m.w["l1.ffn_norm"], TINY.norm_eps)
+    lg1 = od.linear(b, m.W("l1.router"))
+    p = np.exp(lg1[0] - lg1[0].max())
+    p /= p.sum()
+    order = np.lexsort((np.arange(TINY.n_experts), -lg1[0]))
+    experts = [order[0], order[2]]
+    ref = x[0].copy()
+    for s_ in range(TINY.n_shared):
+        ex = TINY.n_experts + s_
+        ref += od.swiglu(b[:1], m.w["l1.w_gate"][ex], m.w["l1.w_up"][ex], m.w["l1.w_down"][ex])[0]
+    for ex in experts:
+        ref += p[ex] * od.swiglu(b[:1], m.w["l1.w_gate"][ex], m.w["l1.w_up"][ex], m.w["l1.w_down"][ex])[0]
+    np.testing.assert_allclose(other[0], ref, rtol=1e-10, atol=1e-12)
+
+
+def test_greedy_hook_and_real_drafts():
+    """An identity greedy hook changes nothing; with a proposer and the draft
+    block run for cost, the block's own proposals are recorded, and the first
+    step's equal a draft call made right after the prefill."""
+    m = tiny_model(scale=8.0)
+    vision, prompt = tiny_page()
+    N, K = 14, 3
+    ar, _ = m.generate_ar(vision, prompt, N + K + 2)
+    prop = od.controlled_proposer(ar, 3000, 0.3, TINY.vocab)
+    t1, s1 = m.generate_spec(vision, prompt, N, K, proposer=prop, draft_for_cost=True)
+    t2, s2 = m.generate_spec(vision, prompt, N, K, proposer=prop, draft_for_cost=True,
+                             greedy_hook=lambda step, g, lg: g)
+    assert t1 == t2 == ar[:N]
+    assert [s.real_drafts for s in s1] == [s.real_drafts for s in s2]
+    assert all(s.real_drafts is not None and len(s.real_drafts) == K for s in s1)
+    st = m.new_state(64)
+    m.prefill(st, vision, prompt, with_draft=True)
+    assert m.draft_propose(st, K) == s1[0].real_drafts
+    # accepted lengths are the controlled generator's (n_prev then covers several values)
+    assert [s.accepted for s in s1] == od.controlled_accepts(N, K, 3000, 0.3)
