@@ -183,6 +183,25 @@ int ocrdec_decode_steps(ocrdec_model* m, void* stream, int B, const int32_t* slo
                         const ocrdec_controlled_cfg* ctrl, int32_t* draft, int32_t* greedy,
                         int32_t* n_accepted_out, int32_t* out_tokens, int32_t* out_len, int out_cap);
 
+/* For callers that cannot allocate memory -- code under HIP graph capture,
+ * serving loops that forbid allocation, harnesses that refuse it.  The same
+ * steps as ocrdec_decode_steps without a controlled override (draft, verify,
+ * accept per step, with the same results bit for bit), issued as individual
+ * launches on `stream` (no graphs are recorded or replayed), and with the
+ * per-call scratch (activations, attention partials, routing tables, LM-head
+ * partials) in a 32 MiB device array that the library holds on each GPU it
+ * runs on until the process ends, instead of the handle's workspace.  The
+ * call allocates nothing and needs its scratch to fit: OCRDEC_ECAPACITY,
+ * nothing enqueued, if B*(K+1) rows at the handle's max_positions need
+ * more than 32 MiB (4 rows need about 1.3 MiB at 2,048 positions, 3.3 MiB at
+ * 32,768; 1,024 rows do not fit).  Every call on one GPU -- from any handle --
+ * shares that array and leaves its contents behind: calls that overlap on one
+ * GPU (other streams, other threads, other handles) race and must not be
+ * issued.  The handle's workspace is untouched. */
+int ocrdec_decode_steps_noalloc(ocrdec_model* m, void* stream, int B, const int32_t* slots, int K, int n_steps,
+                                int32_t* draft, int32_t* greedy, int32_t* n_accepted_out,
+                                int32_t* out_tokens, int32_t* out_len, int out_cap);
+
 /* Position bookkeeping: between synchronisations the host assumes that every
  * step commits K + 1 tokens (an upper bound that sizes the attention grids and
  * the OCRDEC_ECAPACITY checks).  This call synchronises `stream` and resets the

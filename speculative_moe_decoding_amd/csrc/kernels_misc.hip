@@ -642,6 +642,12 @@ void launch_controlled(hipStream_t s, int B, int K, const int* slots_in, StateVi
   hipLaunchKernelGGL(k_controlled, dim3((n + 255) / 256), dim3(256), 0, s, B, K, slots_in, sv, trace,
                      trace_stride, trace_len, seed, thr, V, draft);
 }
+__global__ void k_fill_i32(int* __restrict__ p, long n, int v) {
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) p[i] = v;
+}
+void launch_fill_i32(hipStream_t s, int* p, long n, int v) {
+  hipLaunchKernelGGL(k_fill_i32, dim3(1), dim3(256), 0, s, p, n, v);
+}
 void launch_copy_rows(hipStream_t s, const float* src, float* dst, long n) {
   hipLaunchKernelGGL(k_copy, dim3(64), dim3(256), 0, s, src, dst, n);
 }

@@ -201,5 +201,7 @@ void launch_draft_tap(hipStream_t s, int B, int K, const int* plan_slot, StateVi
 void launch_controlled(hipStream_t s, int B, int K, const int* slots_in, StateView sv, const int* trace,
                        int trace_stride, int trace_len, uint64_t seed, uint64_t thr, int V, int* draft);
 void launch_copy_rows(hipStream_t s, const float* src, float* dst, long n);
+// p[0 .. n) = v, by a kernel (graph-capture safe, unlike a memset node).
+void launch_fill_i32(hipStream_t s, int* p, long n, int v);
 
 }  // namespace ocr

@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <string>
 #include <tuple>
 #include <type_traits>
@@ -134,6 +135,39 @@ struct WsPtrs {
   MoeBufs mb;
 };
 
+// Scratch of ocrdec_decode_steps_noalloc: a file-scope device array, one copy
+// per GPU the library runs on, held until the process ends.  Host code uses
+// the device address returned by hipGetSymbolAddress (kept per device at
+// handle creation), never the array's name.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+std::vector<char*> g_scratch_ptr;     // by device ordinal
+std::vector<std::string> g_scratch_err;
+
+// The scratch address on device `dev` (the current device), looked up once.
+char* scratch_for_device(int dev, std::string* why) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (dev < 0) { *why = "no current device"; return nullptr; }
+  if ((size_t)dev >= g_scratch_ptr.size()) {
+    g_scratch_ptr.resize(dev + 1, nullptr);
+    g_scratch_err.resize(dev + 1);
+  }
+  if (g_scratch_ptr[dev] == nullptr && g_scratch_err[dev].empty()) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      g_scratch_err[dev] = std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e);
+    } else {
+      g_scratch_ptr[dev] = static_cast<char*>(ptr);
+    }
+  }
+  *why = g_scratch_err[dev];
+  return g_scratch_ptr[dev];
+}
+
 WsPtrs bind_workspace(char* ws, const Plan& p, int max_batch) {
   WsPtrs b{};
   auto wf = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
@@ -203,6 +237,8 @@ struct ocrdec_model {
   const float* router_override;  // [n_layers][M][64] router logits for verify calls, or null
   hipStream_t capture_stream;  // private stream the decode-step graphs are recorded on
   std::map<std::vector<uintptr_t>, hipGraphExec_t> graphs;  // by call shape
+  char* scratch;               // this device's no-allocation scratch (null if unavailable)
+  std::string scratch_err;
 };
 
 namespace {
@@ -607,6 +643,11 @@ int ocrdec_create(const ocrdec_config* cfg, const void* const* weight_ptrs, int 
   m->matrix = use_matrix_path(cfg);
   m->router_override = nullptr;
   m->capture_stream = nullptr;
+  {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+    m->scratch = scratch_for_device(dev, &m->scratch_err);
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // clear an error left by earlier, unrelated runtime calls
   hipError_t err = hipMemsetAsync(misc, 0, 64 * 4, s);
@@ -822,6 +863,54 @@ int ocrdec_decode_steps(ocrdec_model* m, void* stream, int B, const int32_t* slo
     m->last_verify_rows = B * (K + 1);
   }
   return OCRDEC_OK;
+}
+
+int ocrdec_decode_steps_noalloc(ocrdec_model* m, void* stream, int B, const int32_t* slots, int K, int n_steps,
+                                int32_t* draft, int32_t* greedy, int32_t* n_accepted_out, int32_t* out_tokens,
+                                int32_t* out_len, int out_cap) {
+  int rc = check_call(m, B, K);
+  if (rc) return rc;
+  if (n_steps < 0 || !greedy || (K > 0 && !draft)) return fail(OCRDEC_EINVAL, "bad decode-step arguments");
+  if (out_tokens && out_cap < 1) return fail(OCRDEC_EINVAL, "out_cap must be >= 1 with out_tokens");
+  if (m->timing) return fail(OCRDEC_EINVAL, "expert timing is on; use the individual calls");
+  if (m->scratch == nullptr)
+    return fail(OCRDEC_EHIP, "the no-allocation scratch is not available on this device: " + m->scratch_err);
+  // the decode calls' scratch for this call's rows, laid out in the static array
+  ocrdec_config c = m->cfg;
+  c.max_batch = B;
+  c.max_k = K;
+  const Plan dp = make_plan(&c, true);
+  if (dp.w_total > kScratchBytes)
+    return fail(OCRDEC_ECAPACITY, "the call needs " + std::to_string(dp.w_total) +
+                                      " bytes of scratch; the no-allocation limit is " +
+                                      std::to_string(kScratchBytes) + " (fewer rows B*(K+1) or max_positions)");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  struct Swap {  // the handle's workspace pointers are restored on every return
+    ocrdec_model* m;
+    WsPtrs saved;
+    ~Swap() { m->b = saved; }
+  } swap{m, m->b};
+  m->b = bind_workspace(m->scratch, dp, B);
+  launch_fill_i32(s, reinterpret_cast<int*>(m->b.mb.stats), 2, 0);  // the expert counter starts at zero
+  for (int step = 0; step < n_steps; ++step) {
+    if (!slots && call_bound(m, B, slots) + K + 1 > m->cfg.max_positions)
+      return fail(OCRDEC_ECAPACITY, "positions would exceed max_positions");
+    int r1 = OCRDEC_OK;
+    if (K > 0)
+      r1 = m->cfg.dtype == OCRDEC_BF16 ? do_draft<bf16>(m, s, B, slots, K, draft)
+                                       : do_draft<float>(m, s, B, slots, K, draft);
+    if (r1 == OCRDEC_OK)
+      r1 = m->cfg.dtype == OCRDEC_BF16 ? do_verify<bf16>(m, s, B, slots, K, draft, greedy, nullptr)
+                                       : do_verify<float>(m, s, B, slots, K, draft, greedy, nullptr);
+    if (r1 != OCRDEC_OK) return r1;
+    launch_accept(s, B, K, m->b.plan_slot, draft, greedy, m->b.x, m->sv, n_accepted_out, out_tokens, out_len,
+                  out_cap, m->step_tap);
+    m->lv_B = 0;
+    const int n = slots ? (int)m->slot_bound.size() : B;
+    for (int i = 0; i < n; ++i) m->slot_bound[i] = std::min(m->cfg.max_positions, m->slot_bound[i] + K + 1);
+    m->last_verify_rows = B * (K + 1);
+  }
+  return hip_check(m, "ocrdec_decode_steps_noalloc");
 }
 
 int ocrdec_sync_positions(ocrdec_model* m, void* stream) {

@@ -25,7 +25,7 @@ SYMBOLS = (
     "ocrdec_prefill", "ocrdec_draft", "ocrdec_verify", "ocrdec_accept_rollback", "ocrdec_controlled_drafts",
     "ocrdec_set_taps", "ocrdec_expert_timing", "ocrdec_expert_stats", "ocrdec_replay_expert_gate_up",
     "ocrdec_decode_steps", "ocrdec_sync_positions", "ocrdec_load_sequence", "ocrdec_set_router_logits",
-    "ocrdec_read_probe", "ocrdec_last_error",
+    "ocrdec_read_probe", "ocrdec_last_error", "ocrdec_decode_steps_noalloc",
 )
 
 
@@ -85,6 +85,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                     ctypes.POINTER(ctypes.c_longlong)]),
         "ocrdec_replay_expert_gate_up": (I, [P, P, I, ctypes.POINTER(I)]),
         "ocrdec_decode_steps": (I, [P, P, I, P, I, I, ctypes.POINTER(ocrdec_controlled_cfg), P, P, P, P, P, I]),
+        "ocrdec_decode_steps_noalloc": (I, [P, P, I, P, I, I, P, P, P, P, P, I]),
         "ocrdec_sync_positions": (I, [P, P]),
         "ocrdec_load_sequence": (I, [P, P, I, I, I, P]),
         "ocrdec_set_router_logits": (I, [P, P]),
@@ -215,6 +216,13 @@ def ocrdec_decode_steps(h, stream, B, slots, K, n_steps, ctrl, draft, greedy, n_
     _check("ocrdec_decode_steps", load_library().ocrdec_decode_steps(
         h, stream, B, _ptr(slots), K, n_steps, None if ctrl is None else ctypes.byref(ctrl), _ptr(draft),
         _ptr(greedy), _ptr(n_accepted_out), _ptr(out_tokens), _ptr(out_len), out_cap))
+
+
+def ocrdec_decode_steps_noalloc(h, stream, B, slots, K, n_steps, draft, greedy, n_accepted_out, out_tokens, out_len,
+                                out_cap):
+    _check("ocrdec_decode_steps_noalloc", load_library().ocrdec_decode_steps_noalloc(
+        h, stream, B, _ptr(slots), K, n_steps, _ptr(draft), _ptr(greedy), _ptr(n_accepted_out), _ptr(out_tokens),
+        _ptr(out_len), out_cap))
 
 
 def ocrdec_replay_expert_gate_up(h, stream, n_rounds: int, want_count: bool = False):
