@@ -38,6 +38,15 @@ HBM_PEAK_GBS = 8000.0
 D, I, V, L = 1280, 896, 129280, 12
 EXPERT_GATE_UP_BYTES = 2 * I * D * 2          # gate + up rows of one expert, bf16
 EXPERT_DOWN_BYTES = D * I * 2
+EXPERT_BYTES = EXPERT_GATE_UP_BYTES + EXPERT_DOWN_BYTES
+
+
+def FUSED_ACT_BYTES(K):
+    """Activation bytes of one persistent MoE launch on K + 1 rows: normalised rows,
+    router logits and residual rows in, rows out; the 8 (expert, row) pairs per row
+    write and read their hidden rows (896) and outputs (1280) once, fp32."""
+    M = K + 1
+    return M * (3 * D * 4 + 64 * 4) + 2 * 8 * M * (D + I) * 4
 DENSE_LAYER_BYTES = 2 * (3 * 1280 * D + D * 1280 + 64 * D)   # qkv, o, router (bf16)
 LM_HEAD_BYTES = 2 * V * D
 KV_POS_BYTES = 2 * 2 * 1280                   # k + v of one position, one layer, bf16
@@ -157,6 +166,10 @@ def main() -> int:
                     help="concurrent32_bf16: scale of the per-page output lengths")
     ap.add_argument("--path", default="auto", choices=["auto", "vector", "matrix"],
                     help="base page: arithmetic path of the handle (auto = vector GEMV at batch 1)")
+    ap.add_argument("--moe-launches", default="five", choices=["persistent", "five"],
+                    help="base page, vector path: the MoE half of each verifier layer as one persistent "
+                         "launch after the router logits, or as the five launches router logits, routing, "
+                         "gate/up, down, combine (the same bits)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 512 MiB device copy (calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
@@ -205,6 +218,7 @@ def main() -> int:
             "matrix": ocrdec.OCRDEC_PATH_MATRIX}[args.path]
     dec = ocrdec.Decoder(cfg, w.device_arrays(), max_batch=1, max_k=K, max_positions=max_pos, path=path)
     matrix = args.path == "matrix"
+    ocrdec.ocrdec_set_moe_launches(dec.h, args.moe_launches == "persistent")
     torch.cuda.synchronize()
     p = synth.replacement_probability(args.alpha, K)
     thr = int(p * float(1 << 53))
@@ -286,6 +300,8 @@ def main() -> int:
     n_routings = max(1, min(args.replay_routings, Si))
     rounds_each = max(1, args.replay_rounds // n_routings)
     rep = []                                   # (experts, start event, end event)
+    fused = (not matrix) and args.moe_launches == "persistent" and ocrdec.ocrdec_moe_grid(dec.h) > 0
+    replay_sets = 0
     for i in range(Si):
         ev[i][0].record()
         dec.draft(B, K, out=draft)
@@ -295,16 +311,28 @@ def main() -> int:
         ev[i][2].record()
         dec.accept(B, K, draft, greedy, n_acc, out_tokens, out_len)
         accs[i:i + 1].copy_(n_acc)
-        if i >= Si - n_routings:             # replays place no timing marks and count no experts
+        if i >= Si - n_routings:             # replays place no timing marks
+            if fused:
+                torch.cuda.synchronize()
+                s_before = ocrdec.ocrdec_expert_stats(dec.h)["expert_sets"]
             na = ocrdec.ocrdec_replay_expert_gate_up(dec.h, dec.stream, 1, want_count=True)
+            if fused:
+                torch.cuda.synchronize()
+                s_mid = ocrdec.ocrdec_expert_stats(dec.h)["expert_sets"]
             r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             r0.record()
             ocrdec.ocrdec_replay_expert_gate_up(dec.h, dec.stream, rounds_each)
             r1.record()
+            if fused:                        # the replays' own expert sets, not the verify steps'
+                torch.cuda.synchronize()
+                s_after = ocrdec.ocrdec_expert_stats(dec.h)["expert_sets"]
+                na = (s_after - s_mid) / (rounds_each * L)
+                replay_sets += s_after - s_before
             rep.append((na, r0, r1))
     torch.cuda.synchronize()
     st = ocrdec.ocrdec_expert_stats(dec.h)
     ocrdec.ocrdec_expert_timing(dec.h, False)
+    st["expert_sets"] -= replay_sets
     draft_ms = np.array([a.elapsed_time(b) for a, b, _ in ev])
     verify_ms = np.array([b.elapsed_time(c) for _, b, c in ev])
     acc_np = accs.cpu().numpy()
@@ -312,7 +340,10 @@ def main() -> int:
     sets = st["expert_sets"]
     n_up = st["n_gate_up"]
     pairs = 8 * (K + 1)
-    up_bytes = sets * EXPERT_GATE_UP_BYTES + n_up * pairs * (D + I) * 4
+    if fused:  # the timed launch is the MoE half of a layer after the router logits
+        up_bytes = n_up * FUSED_ACT_BYTES(K) + sets * EXPERT_BYTES
+    else:  # weights of the active experts; the routed pairs' rows in, hidden rows out
+        up_bytes = sets * EXPERT_GATE_UP_BYTES + n_up * pairs * (D + I) * 4
     up_ms = st["ms_gate_up"]
     achieved = up_bytes / (up_ms * 1e-3) / 1e9
     verify_bytes = (L * Si * DENSE_LAYER_BYTES + sets * 3 * I * D * 2 + Si * LM_HEAD_BYTES
@@ -324,12 +355,17 @@ def main() -> int:
         f"expert gate/up {up_ms / max(1, n_up) * 1e3:.1f} us/launch -> {achieved:.0f} GB/s; "
         f"{sets / (L * Si):.2f} active experts / layer")
 
-    # dominant kernel alone: each replay runs the expert gate/up GEMV over every layer's
-    # weights with one verify's routing, bracketed by two events on the same stream
+    # dominant kernel alone: each replay runs it over every layer's weights, bracketed by
+    # two events on the same stream.  The persistent MoE launch (routing, gate/up, down,
+    # combine) routes from the last router logits (its output goes to scratch); the expert
+    # sets it streamed are counted on the device around each replay
     n_rep = len(rep) * rounds_each * L
     rep_us = sum(a.elapsed_time(b) for _, a, b in rep) * 1e3 / n_rep
     na = float(np.mean([n for n, _, _ in rep]))
-    rep_bytes = na * EXPERT_GATE_UP_BYTES + pairs * (D + I) * 4
+    if fused:
+        rep_bytes = na * EXPERT_BYTES + FUSED_ACT_BYTES(K)
+    else:
+        rep_bytes = na * EXPERT_GATE_UP_BYTES + pairs * (D + I) * 4
     achieved = rep_bytes / (rep_us * 1e-6) / 1e9
     log(f"expert gate/up replay: {n_rep} launches over {len(rep)} routings "
         f"({', '.join(str(n) for n, _, _ in rep)} experts), {rep_us:.2f} us/launch -> {achieved:.0f} GB/s")
@@ -362,6 +398,8 @@ def main() -> int:
         },
         "roofline": {
             "kernel": ("k_expert_gate_up_mfma (grouped expert GEMM, gate+up)" if matrix
+                       else "k_moe_fused (persistent MoE half of a layer after the router logits: "
+                            "routing, expert gate/up and down GEMVs, combine)" if fused
                        else "k_expert_gate_up (grouped expert GEMV, gate+up)"),
             "experts_per_launch": round(na, 2),
             "routings": [int(n) for n, _, _ in rep],
@@ -394,8 +432,9 @@ def main() -> int:
                         "active_experts_per_layer": round(sets / (L * Si), 2)},
         "draft_step": {"ms": round(float(draft_ms.mean()), 4),
                        "GB_per_s": round(draft_bytes / (draft_ms.sum() * 1e-3) / 1e9, 1)},
-        "expert_down": {"avg_launch_us": round(st["ms_down"] / max(1, st["n_down"]) * 1e3, 2),
-                        "GB_per_s": round(sets * EXPERT_DOWN_BYTES / (st["ms_down"] * 1e-3) / 1e9, 1)},
+        "expert_down": None if fused else {
+            "avg_launch_us": round(st["ms_down"] / max(1, st["n_down"]) * 1e3, 2),
+            "GB_per_s": round(sets * EXPERT_DOWN_BYTES / (st["ms_down"] * 1e-3) / 1e9, 1)},
     }
     if not args.no_cpu_baseline:
         t = time.time()

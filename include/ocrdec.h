@@ -192,7 +192,7 @@ int ocrdec_decode_steps(ocrdec_model* m, void* stream, int B, const int32_t* slo
  * partials) in a 32 MiB device array that the library holds on each GPU it
  * runs on until the process ends, instead of the handle's workspace.  The
  * call allocates nothing and needs its scratch to fit: OCRDEC_ECAPACITY,
- * nothing enqueued, if B*(K+1) rows at the handle's max_positions need
+ * nothing enqueued, if B*(max_k+1) rows at the handle's max_positions need
  * more than 32 MiB (4 rows need about 1.3 MiB at 2,048 positions, 3.3 MiB at
  * 32,768; 1,024 rows do not fit).  Every call on one GPU -- from any handle --
  * shares that array and leaves its contents behind: calls that overlap on one

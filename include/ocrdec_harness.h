@@ -44,6 +44,15 @@ struct ocrdec_controlled_cfg {
 int ocrdec_load_sequence(ocrdec_model* m, void* stream, int slot, int n_pos, int pending_token, const void* kv);
 int ocrdec_set_router_logits(ocrdec_model* m, const float* logits);
 
+/* The MoE half of each vector-path verifier layer (at most 8 rows per call)
+ * runs as the router-logits launch and one persistent launch for routing,
+ * expert gate/up, down and combine (fused != 0), or as the five launches
+ * router logits, routing, gate/up, down, combine (fused = 0, the default: the
+ * faster on MI355X); both give the same bits.  ocrdec_moe_grid returns the persistent launch's
+ * workgroup count on this GPU (0: it is not used). */
+int ocrdec_set_moe_launches(ocrdec_model* m, int fused);
+int ocrdec_moe_grid(ocrdec_model* m);
+
 /* Parity taps: nullable device buffers that later calls fill.
  *   route_idx  int32 [n_layers][rows][8]: each verify call's routing (6 routed
  *              experts by decreasing score, then the shared experts 64, 65);
@@ -79,12 +88,16 @@ int ocrdec_expert_timing(ocrdec_model* m, int enable);  /* synchronises the devi
 int ocrdec_expert_stats(ocrdec_model* m, double* ms_gate_up, long long* n_gate_up, double* ms_down,
                         long long* n_down, long long* expert_sets);
 
-/* Replay the grouped expert gate/up GEMV n_rounds times over the weights of
- * every layer in turn (n_rounds * n_layers back-to-back launches on `stream`),
- * with the routing of the last verify call, so that a pair of events around
- * the call times the kernel alone.  If expert_sets_per_launch (host, nullable)
- * is given, the call first synchronises the stream and stores that routing's
- * active-expert count there. */
+/* Replay the dominant expert kernel n_rounds times over the weights of every
+ * layer in turn (n_rounds * n_layers back-to-back launches on `stream`), with
+ * the routing of the last layer of the last verify call, so that a pair of
+ * events around the call times the kernel alone.  The kernel is the grouped
+ * expert gate/up GEMV, or -- where the persistent MoE launch is in use -- that
+ * launch, which then routes from the last router logits and writes its output
+ * rows to scratch (the residual rows are left as they are).  If
+ * expert_sets_per_launch (host, nullable) is given, the call first
+ * synchronises the stream and stores that routing's active-expert count
+ * there. */
 int ocrdec_replay_expert_gate_up(ocrdec_model* m, void* stream, int n_rounds, int* expert_sets_per_launch);
 
 /* Calibration: n_launches back-to-back launches on `stream` of a kernel that

@@ -452,7 +452,8 @@ class Oracle:
                       proposer: Optional[Callable] = None, keep_logits: bool = False,
                       seq_index: int = 0, draft_for_cost: bool = False, max_steps: Optional[int] = None,
                       greedy_hook: Optional[Callable] = None, pick: Optional[Callable] = None,
-                      first_token: Optional[int] = None, state_out: Optional[list] = None):
+                      first_token: Optional[int] = None, state_out: Optional[list] = None,
+                      k_schedule: Optional[Callable] = None):
         """FastMTP speculative decoding with greedy longest-prefix acceptance.
 
         proposer(step, committed_tokens, K) -> K tokens replaces the draft block
@@ -465,7 +466,10 @@ class Oracle:
         routing (see verifier_forward): a parity harness uses them to follow
         another implementation's choice at a near tie, so both keep one history;
         first_token likewise replaces output token 0, and state_out (a list)
-        receives the sequence state.  Returns (tokens[:n_out], [StepRecord])."""
+        receives the sequence state.  k_schedule(step) -> depth (optional, at
+        most K) changes the draft depth from step to step; the catch-up pass
+        recomputes whatever the previous step accepted, whatever its depth.
+        Returns (tokens[:n_out], [StepRecord])."""
         P = vision.shape[0] + len(prompt)
         st = self.new_state(P + n_out + K + 2)
         self.prefill(st, vision, prompt, with_draft=proposer is None or draft_for_cost, pick=pick,
@@ -473,13 +477,16 @@ class Oracle:
         if state_out is not None:
             state_out.append(st)
         steps: List[StepRecord] = []
+        K_max = K
         while len(st.out) < n_out and (max_steps is None or len(steps) < max_steps):
+            K = K_max if k_schedule is None else int(k_schedule(len(steps)))
+            assert 0 <= K <= K_max
             real = None
             if proposer is None:
                 d = self.draft_propose(st, K)
                 real = list(d)
             else:
-                if draft_for_cost:
+                if draft_for_cost and K > 0:
                     real = self.draft_propose(st, K)
                 d = [int(t) for t in proposer(len(steps), list(st.out), K)]
             q = st.kv_len
@@ -563,12 +570,16 @@ def controlled_proposer(trace: Sequence[int], seed: int, p: float, vocab: int, s
     return propose
 
 
-def controlled_accepts(n_out: int, K: int, seed: int, p: float, seq_index: int = 0) -> List[int]:
+def controlled_accepts(n_out: int, K: int, seed: int, p: float, seq_index: int = 0,
+                       k_schedule: Optional[Callable] = None) -> List[int]:
     """Accepted lengths of a lossless speculative run whose drafts come from
-    controlled_proposer: n = number of leading slots that were not replaced."""
+    controlled_proposer: n = number of leading slots that were not replaced
+    (depth K, or k_schedule(step) at each step)."""
     thr = replace_threshold(p)
+    K_max = K
     out_len, step, res = 1, 0, []
     while out_len < n_out:
+        K = K_max if k_schedule is None else int(k_schedule(step))
         n = 0
         while n < K and (draft_hash(seed, seq_index, step, n + 1) >> 11) >= thr:
             n += 1

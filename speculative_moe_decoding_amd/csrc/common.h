@@ -259,6 +259,16 @@ struct WaveGemv {
   }
 
   __device__ __forceinline__ void fma(const float* xs, int m_act, float (&acc)[R][MR]) const {
+    int rows[MR];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) rows[m] = m;
+    fma_rows(xs, rows, m_act, acc);
+  }
+
+  // The same with activation row m at xs[rows[m]][.] (rows picked out of a
+  // larger LDS block; the arithmetic of each row is unchanged).
+  __device__ __forceinline__ void fma_rows(const float* xs, const int (&rows)[MR], int m_act,
+                                           float (&acc)[R][MR]) const {
     const int lane = lane_id();
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -275,7 +285,7 @@ struct WaveGemv {
         for (int m = 0; m < MR; ++m) {
           if (m < m_act) {
             float xa[CE];
-            const float4* xp = reinterpret_cast<const float4*>(xs + m * K + c * CE);
+            const float4* xp = reinterpret_cast<const float4*>(xs + rows[m] * K + c * CE);
 #pragma unroll
             for (int q = 0; q < CE / 4; ++q) {
               float4 f = xp[q];
@@ -428,6 +438,33 @@ struct WaveTotals {
 };
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+
+// Data that crosses workgroups inside one launch: loads that see the stores
+// other workgroups made (agent scope: they do not stop at this XCD's L2) and
+// the stores they see, agent-scope atomics for the counters, and the point
+// after which this wavefront's stores are complete (s_waitcnt; the compiler
+// moves no memory access across it).  No L2 write-back or invalidate is needed.
+__device__ __forceinline__ float ld_agent(const float* p) {
+  return __uint_as_float(__hip_atomic_load(reinterpret_cast<const unsigned*>(p), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ unsigned ld_agent_u(const unsigned* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(float* p, float v) {
+  __hip_atomic_store(reinterpret_cast<unsigned*>(p), __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent_u(unsigned* p, unsigned v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned atomic_add_agent(unsigned* p, unsigned v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void stores_done() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 // Per-call row plan: sequence b of a call owns rows b*Q .. b*Q+Q-1; row i of
 // it is valid when i < cnt[b] and sits at position base[b] + i.

@@ -94,12 +94,14 @@ __device__ __forceinline__ void rank_and_gate(const float* lg, float v, int& ran
 
 // Route M <= 8 rows from their logits (rlogit[m][64]) into LDS; all 256
 // threads of the block call it (two barriers inside).  Wavefront w handles rows
-// w, w+4 with rank_and_gate, then wavefront 0 sorts the pairs.
+// w, w+4 with rank_and_gate, then wavefront 0 sorts the pairs.  AGENT: the
+// logits were written by other workgroups of the same launch.
+template <bool AGENT = false>
 __device__ __forceinline__ void route_rows(const float* __restrict__ rlogit, int M, RouteLds& r) {
   __shared__ float lg[4][NE];
   const int wave = wave_id(), lane = lane_id();
   for (int m = wave; m < M; m += 4) {
-    const float v = rlogit[m * NE + lane];
+    const float v = AGENT ? ld_agent(rlogit + m * NE + lane) : rlogit[m * NE + lane];
     lg[wave][lane] = v;
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -168,11 +170,19 @@ __device__ __forceinline__ void publish_route(const RouteLds& r, int M, const Mo
 
 // Router logits: wavefront w of block x computes expert 4x + w for every row
 // (RMSNorm'ed with the FFN gain in the prologue; block 0 also stores the
-// normalised rows for the experts).  rlogit[m][e] fp32.
-template <typename T, int MR>
+// normalised rows for the experts).  rlogit[m][e] fp32.  ROUTE (M <= MR, one
+// block row): the last of the NE / 4 blocks to finish (a counter, *cnt, left
+// at zero) routes the rows -- from logit_override instead when it is given,
+// which it also copies into rlogit -- and publishes the tables and the taps,
+// as k_route_small does after this kernel.  The logits cross blocks through
+// agent-scope stores and loads.
+template <typename T, int MR, bool ROUTE>
 __global__ __launch_bounds__(256) void k_router_logits(const float* __restrict__ x, const float* __restrict__ gain,
                                                        float eps, const T* __restrict__ wr, int M,
-                                                       float* __restrict__ bnorm, float* __restrict__ rlogit) {
+                                                       float* __restrict__ bnorm, float* __restrict__ rlogit,
+                                                       MoeBufs mb, RouteTap tap,
+                                                       const float* __restrict__ logit_override,
+                                                       unsigned* __restrict__ cnt) {
   extern __shared__ float xs[];  // [MR][D]
   const int wave = wave_id();
   const int e = blockIdx.x * 4 + wave;
@@ -188,15 +198,37 @@ __global__ __launch_bounds__(256) void k_router_logits(const float* __restrict__
   float acc[1][MR];
   g.fma(xs, m_act, acc);
   const WaveTotals<1, MR> t(acc);
-  if (t.lead && t.m < m_act) rlogit[(long)(m0 + t.m) * NE + e] = t.val;
+  if constexpr (!ROUTE) {
+    if (t.lead && t.m < m_act) rlogit[(long)(m0 + t.m) * NE + e] = t.val;
+  } else {
+    __shared__ int s_last;
+    __shared__ RouteLds r;
+    if (t.lead && t.m < m_act) st_agent(rlogit + (long)(m0 + t.m) * NE + e, t.val);
+    stores_done();
+    __syncthreads();
+    if (threadIdx.x == 0) s_last = atomic_add_agent(cnt, 1u) + 1 == gridDim.x;
+    __syncthreads();
+    if (!s_last) return;
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    const long long st0 = (threadIdx.x == 0) ? mb.stats[0] : 0;
+    if (logit_override != nullptr) {
+      route_rows<false>(logit_override, M, r);
+      for (int k = threadIdx.x; k < M * NE; k += 256) rlogit[k] = logit_override[k];
+    } else {
+      route_rows<true>(rlogit, M, r);
+    }
+    publish_route(r, M, mb, tap, st0);
+    if (threadIdx.x == 0) st_agent_u(cnt, 0u);
+  }
 }
 
-// M <= 8: top-6 per row and the sort by one block, published to global.
+// M <= 8 without a counter: top-6 per row and the sort by one block,
+// published to global.
 __global__ __launch_bounds__(256) void k_route_small(const float* __restrict__ rlogit, int M, MoeBufs mb,
                                                      RouteTap tap) {
   __shared__ RouteLds r;
   const long long st0 = (threadIdx.x == 0) ? mb.stats[0] : 0;  // read early: off the kernel's tail
-  route_rows(rlogit, M, r);
+  route_rows<false>(rlogit, M, r);
   publish_route(r, M, mb, tap, st0);
 }
 
@@ -331,18 +363,38 @@ int expert_slot_cap(int M) { return min(NE, TOPK * M) + NSH; }
 
 // Router: logits in a 16-block kernel, then the top-6 and the sort (one
 // block for M <= 8; a per-row top-6 kernel and a one-block sort beyond).
+// Router logits into mb.rlogit (or a copy of logit_override) and the
+// normalised rows into mb.bnorm.
 template <typename T>
-void launch_router(hipStream_t s, const float* x, const float* gain, float eps, const T* wr, int M,
-                   const MoeBufs& mb, const RouteTap& tap, const float* logit_override) {
+void launch_router_logits(hipStream_t s, const float* x, const float* gain, float eps, const T* wr, int M,
+                          const MoeBufs& mb, const float* logit_override) {
 #define OCR_RL_CASE(MRV)                                                                                   \
-  hipLaunchKernelGGL((k_router_logits<T, MRV>), dim3(NE / 4, (M + MRV - 1) / MRV), dim3(256),              \
-                     (size_t)MRV * D * 4, s, x, gain, eps, wr, M, mb.bnorm, mb.rlogit);
+  hipLaunchKernelGGL((k_router_logits<T, MRV, false>), dim3(NE / 4, (M + MRV - 1) / MRV), dim3(256),       \
+                     (size_t)MRV * D * 4, s, x, gain, eps, wr, M, mb.bnorm, mb.rlogit, mb, RouteTap{}, nullptr,  \
+                     nullptr);
   if (M <= 1) OCR_RL_CASE(1)
   else if (M <= 2) OCR_RL_CASE(2)
   else if (M <= 4) OCR_RL_CASE(4)
   else OCR_RL_CASE(MRG)
 #undef OCR_RL_CASE
   if (logit_override != nullptr) launch_copy_rows(s, logit_override, mb.rlogit, (long)M * NE);
+}
+
+template <typename T>
+void launch_router(hipStream_t s, const float* x, const float* gain, float eps, const T* wr, int M,
+                   const MoeBufs& mb, const RouteTap& tap, const float* logit_override, unsigned* cnt) {
+  if (M <= MRG && cnt != nullptr) {  // one launch: the last logits block routes
+#define OCR_RR_CASE(MRV)                                                                                 \
+  hipLaunchKernelGGL((k_router_logits<T, MRV, true>), dim3(NE / 4, 1), dim3(256), (size_t)MRV * D * 4, s, x, \
+                     gain, eps, wr, M, mb.bnorm, mb.rlogit, mb, tap, logit_override, cnt);
+    if (M <= 1) OCR_RR_CASE(1)
+    else if (M <= 2) OCR_RR_CASE(2)
+    else if (M <= 4) OCR_RR_CASE(4)
+    else OCR_RR_CASE(MRG)
+#undef OCR_RR_CASE
+    return;
+  }
+  launch_router_logits<T>(s, x, gain, eps, wr, M, mb, logit_override);
   if (M <= MRG) {
     hipLaunchKernelGGL(k_route_small, dim3(1), dim3(256), 0, s, mb.rlogit, M, mb, tap);
   } else {
@@ -423,30 +475,58 @@ __global__ __launch_bounds__(256) void k_expert_gate_up(const T* __restrict__ wg
   if (t.lead && t.r < UPW && t.m < m_act) mb.hx[(long)(k0 + t.m) * DI + j0 + t.r] = silu(t.val) * up;
 }
 
-// Down: block (x, slot s); wavefront w owns output rows n0 .. n0+RPW-1,
-// n0 = RPW (4x + w):  y[pair][n] = W_d[n] . hx[pair].
+// Down (M <= 8) and the combine: block (x, slot s); wavefront w owns output
+// rows n0 .. n0+RPW-1, n0 = RPW (4x + w): y[pair][n] = W_d[n] . hx[pair].  The
+// last block of column x to finish (a counter per column, cnt[x * 32], left
+// at zero) adds the column's 4 RPW outputs of every row to the residual:
+// x[m][n] += y_shared0 + y_shared1 + sum_j gate_j * y_routed_j, in this
+// order, the arithmetic of k_moe_combine.  y crosses blocks through
+// agent-scope stores and loads.
+constexpr int DN_CNT_STRIDE = 32;
 template <typename T, int MR, int RPW>
-__global__ __launch_bounds__(256) void k_expert_down(const T* __restrict__ wd, int M, MoeBufs mb) {
+__global__ __launch_bounds__(256) void k_expert_down(const T* __restrict__ wd, int M, MoeBufs mb,
+                                                     float* __restrict__ x, unsigned* __restrict__ cnt) {
   extern __shared__ float xs[];
+  __shared__ int s_last;
   const int4 info = expert_work(mb, blockIdx.y, M);
   const int e = info.x;
-  if (e < 0) return;
-  const int k0 = info.y;
-  const int m_act = min(MR, info.z - k0);
-  const int wave = wave_id();
-  const int n0 = (blockIdx.x * 4 + wave) * RPW;
-  const T* base = wd + ((long)e * D + n0) * DI;
-  const T* rows[RPW];
+  const int wave = wave_id(), tid = threadIdx.x;
+  if (e >= 0) {
+    const int k0 = info.y;
+    const int m_act = min(MR, info.z - k0);
+    const int n0 = (blockIdx.x * 4 + wave) * RPW;
+    const T* base = wd + ((long)e * D + n0) * DI;
+    const T* rows[RPW];
 #pragma unroll
-  for (int r = 0; r < RPW; ++r) rows[r] = base + (long)r * DI;
-  WaveGemv<T, DI, RPW, MR> g;
-  g.load(rows);
-  gather_rows<DI, MR>(mb.hx, [&](int m) { return k0 + m; }, m_act, xs);
+    for (int r = 0; r < RPW; ++r) rows[r] = base + (long)r * DI;
+    WaveGemv<T, DI, RPW, MR> g;
+    g.load(rows);
+    gather_rows<DI, MR>(mb.hx, [&](int m) { return k0 + m; }, m_act, xs);
+    __syncthreads();
+    float acc[RPW][MR];
+    g.fma(xs, m_act, acc);
+    const WaveTotals<RPW, MR> t(acc);
+    if (t.lead && t.m < m_act) st_agent(mb.y + (long)(k0 + t.m) * D + n0 + t.r, t.val);
+  }
+  stores_done();
   __syncthreads();
-  float acc[RPW][MR];
-  g.fma(xs, m_act, acc);
-  const WaveTotals<RPW, MR> t(acc);
-  if (t.lead && t.m < m_act) mb.y[(long)(k0 + t.m) * D + n0 + t.r] = t.val;
+  unsigned* c = cnt + blockIdx.x * DN_CNT_STRIDE;
+  if (tid == 0) s_last = atomic_add_agent(c, 1u) + 1 == gridDim.y;
+  __syncthreads();
+  if (!s_last) return;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  constexpr int W = 4 * RPW;  // outputs of the column
+  if (tid < W * M) {
+    const int m = tid / W, n = blockIdx.x * W + tid % W;
+    const int* inv = mb.inv + m * NSLOT;
+    const float* gt = mb.rgate + m * NSLOT;
+    float a = ld_agent(mb.y + (long)inv[TOPK] * D + n);
+    a += ld_agent(mb.y + (long)inv[TOPK + 1] * D + n);
+#pragma unroll
+    for (int j = 0; j < TOPK; ++j) a = fmaf(gt[j], ld_agent(mb.y + (long)inv[j] * D + n), a);
+    x[(long)m * D + n] += a;
+  }
+  if (tid == 0) st_agent_u(c, 0u);
 }
 
 // Batches with more than MRG rows: the same per-row arithmetic, MRG pairs at a
@@ -512,6 +592,7 @@ __global__ __launch_bounds__(256) void k_expert_down_groups(const T* __restrict_
 #endif
 constexpr int GU_UPW = OCR_GU_UPW;   // gate/up units per wavefront
 constexpr int DN_RPW = OCR_DN_RPW;   // down rows per wavefront
+static_assert((D / (4 * DN_RPW)) * DN_CNT_STRIDE <= DOWN_CNT_WORDS, "down-combine counters");
 
 template <typename T>
 void launch_expert_gate_up(hipStream_t s, const T* wg, const T* wu, int M, const MoeBufs& mb) {
@@ -530,16 +611,20 @@ void launch_expert_gate_up(hipStream_t s, const T* wg, const T* wu, int M, const
 
 template <typename T>
 void launch_expert_down(hipStream_t s, const T* wd, int M, const MoeBufs& mb) {
+  hipLaunchKernelGGL((k_expert_down_groups<T>), dim3(D / 16, expert_slot_cap(M)), dim3(256),
+                     (size_t)MRG * DI * 4, s, wd, M, mb);
+}
+
+template <typename T>
+void launch_expert_down_combine(hipStream_t s, const T* wd, int M, const MoeBufs& mb, float* x, unsigned* cnt) {
   const dim3 grid(D / (4 * DN_RPW), expert_slot_cap(M));
-#define OCR_DN_CASE(MRV) \
-  hipLaunchKernelGGL((k_expert_down<T, MRV, DN_RPW>), grid, dim3(256), (size_t)MRV * DI * 4, s, wd, M, mb);
+#define OCR_DN_CASE(MRV)                                                                                     \
+  hipLaunchKernelGGL((k_expert_down<T, MRV, DN_RPW>), grid, dim3(256), (size_t)MRV * DI * 4, s, wd, M, mb, x, \
+                     cnt);
   if (M <= 1) OCR_DN_CASE(1)
   else if (M <= 2) OCR_DN_CASE(2)
   else if (M <= 4) OCR_DN_CASE(4)
-  else if (M <= MRG) OCR_DN_CASE(MRG)
-  else
-    hipLaunchKernelGGL((k_expert_down_groups<T>), dim3(D / 16, expert_slot_cap(M)), dim3(256),
-                       (size_t)MRG * DI * 4, s, wd, M, mb);
+  else OCR_DN_CASE(MRG)
 #undef OCR_DN_CASE
 }
 
@@ -566,10 +651,287 @@ void launch_moe_combine(hipStream_t s, float* x, int M, const MoeBufs& mb) {
 
 #define OCR_INST_MOE(T)                                                                                  \
   template void launch_router<T>(hipStream_t, const float*, const float*, float, const T*, int,          \
-                                 const MoeBufs&, const RouteTap&, const float*);                         \
+                                 const MoeBufs&, const RouteTap&, const float*, unsigned*);              \
+  template void launch_router_logits<T>(hipStream_t, const float*, const float*, float, const T*, int,   \
+                                        const MoeBufs&, const float*);                                   \
   template void launch_expert_gate_up<T>(hipStream_t, const T*, const T*, int, const MoeBufs&);                \
-  template void launch_expert_down<T>(hipStream_t, const T*, int, const MoeBufs&);
+  template void launch_expert_down<T>(hipStream_t, const T*, int, const MoeBufs&);                           \
+  template void launch_expert_down_combine<T>(hipStream_t, const T*, int, const MoeBufs&, float*, unsigned*);
 OCR_INST_MOE(float)
 OCR_INST_MOE(bf16)
+
+}  // namespace ocr
+
+namespace ocr {
+
+// ---- the experts of a decoder layer in one persistent launch (M <= 8) -------
+//
+// After the router-logits launch (which also stores the normalised rows), one
+// launch does what the routing, gate/up, down and combine launches do, with
+// the same arithmetic (so the same bits), waiting inside the launch only where
+// the data requires it: every workgroup routes the rows itself from the
+// logits (a few hundred cycles); the gate/up items of the two shared experts
+// need no routing and their weights go out first; the down items wait until
+// every gate/up item is done, with their weights already in flight; per slice
+// of 16 outputs, the workgroup that finishes the last expert of the slice adds
+// the slice to the residual in the fixed order.  Data that crosses workgroups
+// goes through agent-scope stores and loads (no L2 write-back or invalidate
+// is needed); the counters are agent-scope atomics.  The wait polls a ready
+// flag that the last arriver writes to 32 cache lines, each polled by one
+// lane of the workgroups of one stripe, so that the polls do not crowd one
+// line while other workgroups still stream their weights.  Every wait is
+// bounded: a timeout (a grid that is not all resident) sets the error word,
+// which the host reports, and the launch runs to its end.  The grid is at
+// most the number of workgroups the GPU holds at once; each launch leaves
+// every counter at zero for the next.
+constexpr int FZ_STRIPES = 32;
+constexpr int FZ_SLICES = D / 16;     // down slices of 16 outputs (4 wavefronts x 4 rows)
+constexpr int FZ_GU = DI / 4;         // gate/up items per expert (one unit per wavefront)
+// Sync words, one cache line (32 words) apart where several workgroups meet:
+// line 0: (unused), gate/up top count, done top count, error word;
+// lines 1+s: gate/up count of stripe s; 33+s: done count of stripe s;
+// 97+s: gate/up-done flag copy s; 129+x: done count of down slice x.
+constexpr int FZ_LINE = 32;
+constexpr int FZ_S_GUTOP = 1, FZ_S_TOP = 2, FZ_S_ERR = MOE_SYNC_ERR;
+constexpr int FZ_S_GU = 1 * FZ_LINE, FZ_S_DONE = 33 * FZ_LINE, FZ_S_GFLAG = 97 * FZ_LINE,
+              FZ_S_SLICE = 129 * FZ_LINE;
+static_assert(FZ_S_ERR > FZ_S_TOP && FZ_S_ERR < FZ_LINE && FZ_S_SLICE + FZ_SLICES * FZ_LINE <= MOE_SYNC_WORDS,
+              "sync word layout");
+
+// One thread: wait until the flag is set, bounded; on timeout (or an earlier
+// one) set / see the error word and give up.
+__device__ __forceinline__ void wait_flag(const unsigned* flag, unsigned* err) {
+  for (int n = 0; n < (1 << 20); ++n) {
+    if (ld_agent_u(flag) != 0u) { __atomic_signal_fence(__ATOMIC_SEQ_CST); return; }
+    if ((n & 15) == 15 && ld_agent_u(err) != 0) return;
+    __builtin_amdgcn_s_sleep(4);
+  }
+  st_agent_u(err, 1u);
+}
+
+// Set the 32 copies of a ready flag (one cache line apart).
+__device__ __forceinline__ void raise_flag(unsigned* flags) {
+  for (int s = 0; s < FZ_STRIPES; ++s) st_agent_u(flags + s * FZ_LINE, 1u);
+}
+
+// Workgroups b < G with b % FZ_STRIPES == s.
+__device__ __forceinline__ unsigned stripe_count(int G, int s) {
+  return s < G ? (unsigned)((G - s + FZ_STRIPES - 1) / FZ_STRIPES) : 0u;
+}
+
+// x_out = x_in + the experts' combine; the normalised rows come from
+// mb.bnorm and the router logits from mb.rlogit (the router-logits launch).
+template <typename T, int MR>
+__global__ __launch_bounds__(256) void k_moe_fused(const float* __restrict__ x_in, float* __restrict__ x_out,
+                                                   const T* __restrict__ wg, const T* __restrict__ wu,
+                                                   const T* __restrict__ wd, int M, MoeBufs mb, RouteTap tap,
+                                                   unsigned* __restrict__ sync) {
+  extern __shared__ float xs[];  // [MR][D] normalised rows; in the down phase [MR][DI] expert hidden rows
+  __shared__ RouteLds r;
+  __shared__ int s_flag;
+  const int G = gridDim.x, b = blockIdx.x, wave = wave_id(), tid = threadIdx.x;
+  unsigned* err = sync + FZ_S_ERR;
+  const long long st0 = (b == 0 && tid == 0) ? mb.stats[0] : 0;
+
+  // gate/up item i: expert slot i / FZ_GU (0, 1: the shared experts, then the
+  // routed ones in increasing id), unit 4 (i % FZ_GU) + wave
+  auto item_expert = [&](int slot, int& e, int& k0, int& m_act, int (&rows)[MR]) {
+    if (slot < NSH) {  // known without the routing: all rows, after the 6M routed pairs
+      e = NE + slot;
+      k0 = (TOPK + slot) * M;
+      m_act = M;
+#pragma unroll
+      for (int m = 0; m < MR; ++m) rows[m] = m;
+    } else {
+      e = r.act[slot - NSH];
+      k0 = r.off[e];
+      m_act = r.off[e + 1] - k0;
+#pragma unroll
+      for (int m = 0; m < MR; ++m) rows[m] = r.perm[k0 + min(m, max(m_act - 1, 0))] / NSLOT;
+    }
+  };
+  // the first gate/up item's weights go out before anything else
+  int i = b;
+  bool have = i < NSH * FZ_GU;
+  WaveGemv<T, D, 2, MR> g0, g1;
+  if (have) {
+    const int e = NE + i / FZ_GU, j = (i % FZ_GU) * 4 + wave;
+    const T* rows[2] = {wg + ((long)e * DI + j) * D, wu + ((long)e * DI + j) * D};
+    g0.load(rows);
+  }
+  // the normalised rows (all M of them) into LDS, then the routing
+  for (int q = tid; q < M * D; q += 256) xs[q] = mb.bnorm[q];
+  route_rows(mb.rlogit, M, r);
+  if (b == 0) publish_route(r, M, mb, tap, st0);
+  __syncthreads();
+  const int n_gu = r.na * FZ_GU;
+  if (!have) {
+    have = i < n_gu;
+    if (have) {
+      int e, k0, m_act, rows_i[MR];
+      item_expert(i / FZ_GU, e, k0, m_act, rows_i);
+      const int j = (i % FZ_GU) * 4 + wave;
+      const T* rows[2] = {wg + ((long)e * DI + j) * D, wu + ((long)e * DI + j) * D};
+      g0.load(rows);
+    }
+  }
+  // gate/up items, two in flight per wavefront
+  auto gate_up = [&](const WaveGemv<T, D, 2, MR>& g, int it) {
+    int e, k0, m_act, rows_i[MR];
+    item_expert(it / FZ_GU, e, k0, m_act, rows_i);
+    const int j = (it % FZ_GU) * 4 + wave;
+    float acc[2][MR];
+    g.fma_rows(xs, rows_i, m_act, acc);
+    const WaveTotals<2, MR> t(acc);
+    const float up = t.partner(1);
+    if (t.lead && t.r < 1 && t.m < m_act) st_agent(mb.hx + (long)(k0 + t.m) * DI + j, silu(t.val) * up);
+  };
+  for (int par = 0; have; par ^= 1) {
+    const int inext = i + G;
+    const bool hnext = inext < n_gu;
+    if (hnext) {
+      int e, k0, m_act, rows_i[MR];
+      item_expert(inext / FZ_GU, e, k0, m_act, rows_i);
+      const int j = (inext % FZ_GU) * 4 + wave;
+      const T* rows[2] = {wg + ((long)e * DI + j) * D, wu + ((long)e * DI + j) * D};
+      if (par) g0.load(rows); else g1.load(rows);
+    }
+    if (par) gate_up(g1, i); else gate_up(g0, i);
+    i = inext;
+    have = hnext;
+  }
+  stores_done();
+  __syncthreads();
+  if (tid == 0) {  // the last workgroup of a stripe counts the stripe; the last stripe raises the flag
+    const int st = b % FZ_STRIPES;
+    if (atomic_add_agent(sync + FZ_S_GU + st * FZ_LINE, 1u) + 1 == stripe_count(G, st) &&
+        atomic_add_agent(sync + FZ_S_GUTOP, 1u) + 1 == (unsigned)min(G, FZ_STRIPES)) {
+      stores_done();
+      raise_flag(sync + FZ_S_GFLAG);
+    }
+  }
+
+  // down items: a contiguous range per workgroup (consecutive slices of one expert share the gather)
+  const int n_dn = r.na * FZ_SLICES;
+  const int lo = (int)((long)b * n_dn / G), hi = (int)((long)(b + 1) * n_dn / G);
+  WaveGemv<T, DI, 4, MR> gd;
+  auto dn_rows = [&](int it, const T* (&rows)[4]) {
+    int e, k0, m_act, rows_i[MR];
+    item_expert(it / FZ_SLICES, e, k0, m_act, rows_i);
+    const int n0 = ((it % FZ_SLICES) * 4 + wave) * 4;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) rows[q] = wd + ((long)e * D + n0 + q) * DI;
+  };
+  if (lo < hi) {
+    const T* rows[4];
+    dn_rows(lo, rows);
+    gd.load(rows);
+  }
+  // every gate/up item of the grid is done
+  if (tid == 0) wait_flag(sync + FZ_S_GFLAG + (b % FZ_STRIPES) * FZ_LINE, err);
+  __syncthreads();
+  int cur_slot = -1;
+  for (int it = lo; it < hi; ++it) {
+    const int slot = it / FZ_SLICES, xsl = it % FZ_SLICES;
+    int e, k0, m_act, rows_i[MR];
+    item_expert(slot, e, k0, m_act, rows_i);
+    if (slot != cur_slot) {  // the expert's hidden rows k0 .. k0 + m_act - 1 into LDS
+      if (cur_slot >= 0) __syncthreads();
+      for (int q = tid; q < m_act * DI; q += 256) xs[q] = ld_agent(mb.hx + (long)k0 * DI + q);
+      __syncthreads();
+      cur_slot = slot;
+    }
+    float acc[4][MR];
+    gd.fma(xs, m_act, acc);
+    if (it + 1 < hi) {
+      const T* rows[4];
+      dn_rows(it + 1, rows);
+      gd.load(rows);
+    }
+    const WaveTotals<4, MR> t(acc);
+    const int n0 = (xsl * 4 + wave) * 4;
+    if (t.lead && t.m < m_act) st_agent(mb.y + (long)(k0 + t.m) * D + n0 + t.r, t.val);
+    stores_done();
+    __syncthreads();
+    if (tid == 0) {
+      const unsigned old = atomic_add_agent(sync + FZ_S_SLICE + xsl * FZ_LINE, 1u);
+      s_flag = old + 1 == (unsigned)r.na;
+    }
+    __syncthreads();
+    if (s_flag) {  // the last expert of this slice: x += shared 0 + shared 1 + sum gate_j y_j, in this order
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      if (tid < 16 * M) {
+        const int m = tid / 16, n = xsl * 16 + tid % 16;
+        const int* inv = r.inv + m * NSLOT;
+        const float* gt = r.pg + m * NSLOT;
+        float acc2 = ld_agent(mb.y + (long)inv[TOPK] * D + n);
+        acc2 += ld_agent(mb.y + (long)inv[TOPK + 1] * D + n);
+#pragma unroll
+        for (int jj = 0; jj < TOPK; ++jj) acc2 = fmaf(gt[jj], ld_agent(mb.y + (long)inv[jj] * D + n), acc2);
+        x_out[(long)m * D + n] = x_in[(long)m * D + n] + acc2;
+      }
+      if (tid == 0) st_agent_u(sync + FZ_S_SLICE + xsl * FZ_LINE, 0u);  // its last user this launch
+    }
+  }
+  // leave the counters at zero: the last workgroup to finish resets them
+  stores_done();
+  __syncthreads();
+  if (tid == 0) {
+    const int st = b % FZ_STRIPES;
+    if (atomic_add_agent(sync + FZ_S_DONE + st * FZ_LINE, 1u) + 1 == stripe_count(G, st)) {
+      if (atomic_add_agent(sync + FZ_S_TOP, 1u) + 1 == (unsigned)min(G, FZ_STRIPES)) {
+        st_agent_u(sync + FZ_S_GUTOP, 0u);
+        for (int q = 0; q < FZ_STRIPES; ++q) {
+          st_agent_u(sync + FZ_S_GU + q * FZ_LINE, 0u);
+          st_agent_u(sync + FZ_S_DONE + q * FZ_LINE, 0u);
+          st_agent_u(sync + FZ_S_GFLAG + q * FZ_LINE, 0u);
+        }
+        st_agent_u(sync + FZ_S_TOP, 0u);
+      }
+    }
+  }
+}
+
+template <typename T, int MR>
+static size_t moe_fused_lds() {
+  return (size_t)MR * D * 4;
+}
+
+template <typename T>
+int moe_fused_grid(int n_cu) {
+  // the grid must be resident all at once: workgroups per CU for the largest
+  // variant (8 rows, the most LDS), at most 4
+  int occ = 0;
+  const size_t lds = moe_fused_lds<T, MRG>();
+  allow_lds(k_moe_fused<T, MRG>, lds);
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_moe_fused<T, MRG>, 256, lds) != hipSuccess || occ < 1)
+    return 0;
+  return std::min(occ, 4) * n_cu;
+}
+
+template <typename T>
+void launch_moe_experts(hipStream_t s, int grid, const float* x_in, float* x_out, const T* wg, const T* wu,
+                        const T* wd, int M, const MoeBufs& mb, const RouteTap& tap, unsigned* sync) {
+#define OCR_FZ_CASE(MRV)                                                                                      \
+  {                                                                                                           \
+    const size_t lds = moe_fused_lds<T, MRV>();                                                               \
+    static const bool attr_set = (allow_lds(k_moe_fused<T, MRV>, lds), true);                                 \
+    (void)attr_set;                                                                                           \
+    hipLaunchKernelGGL((k_moe_fused<T, MRV>), dim3(grid), dim3(256), lds, s, x_in, x_out, wg, wu, wd, M, mb,  \
+                       tap, sync);                                                                            \
+  }
+  if (M <= 1) OCR_FZ_CASE(1)
+  else if (M <= 2) OCR_FZ_CASE(2)
+  else if (M <= 4) OCR_FZ_CASE(4)
+  else OCR_FZ_CASE(MRG)
+#undef OCR_FZ_CASE
+}
+
+template int moe_fused_grid<float>(int);
+template int moe_fused_grid<bf16>(int);
+template void launch_moe_experts<float>(hipStream_t, int, const float*, float*, const float*, const float*,
+                                        const float*, int, const MoeBufs&, const RouteTap&, unsigned*);
+template void launch_moe_experts<bf16>(hipStream_t, int, const float*, float*, const bf16*, const bf16*,
+                                       const bf16*, int, const MoeBufs&, const RouteTap&, unsigned*);
 
 }  // namespace ocr

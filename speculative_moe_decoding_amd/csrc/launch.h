@@ -36,9 +36,14 @@ int lmhead_blocks(int V);
 void launch_argmax_final(hipStream_t s, const float* part_val, const int* part_idx, int nblk, int M, int* tok,
                          int tok_stride);
 
+// Split-KV decode attention and the merge of its chunks into out.  With acnt
+// (B x NH zero counters, left at zero) and at most ATT_FUSE_CHUNKS chunks, the
+// last chunk block of each (sequence, head) merges them in the same launch;
+// otherwise a second launch does.  The same bits either way.
+constexpr int ATT_FUSE_CHUNKS = 32;
 template <typename T>
 void launch_attention(hipStream_t s, const float* q, const T* kv, int max_pos, RowPlan plan, int B,
-                      int n_chunks, int tiles_per_chunk, float* part, float* out);
+                      int n_chunks, int tiles_per_chunk, float* part, float* out, unsigned* acnt);
 
 struct MoeBufs {
   float* bnorm;   // [M][D] normalised rows
@@ -83,16 +88,49 @@ struct RouteTap {
 };
 
 // Router logits (rlogit) and the routing tables; logit_override (nullable,
-// [M][64]) replaces the computed logits before the top-6.
+// [M][64]) replaces the computed logits before the top-6.  With cnt (one zero
+// word, left at zero) and M <= MRG, one launch does both.
 template <typename T>
 void launch_router(hipStream_t s, const float* x, const float* gain, float eps, const T* wr, int M,
-                   const MoeBufs& mb, const RouteTap& tap, const float* logit_override);
+                   const MoeBufs& mb, const RouteTap& tap, const float* logit_override, unsigned* cnt);
+// The first half of launch_router: the normalised rows into mb.bnorm and the
+// router logits (or a copy of logit_override) into mb.rlogit.
+template <typename T>
+void launch_router_logits(hipStream_t s, const float* x, const float* gain, float eps, const T* wr, int M,
+                          const MoeBufs& mb, const float* logit_override);
+// Grouped expert GEMVs after launch_router (M <= MRG: every pair of an
+// expert at once; beyond, MRG pairs at a time) and the combine into the
+// residual rows x.
 template <typename T>
 void launch_expert_gate_up(hipStream_t s, const T* wg, const T* wu, int M, const MoeBufs& mb);
 template <typename T>
 void launch_expert_down(hipStream_t s, const T* wd, int M, const MoeBufs& mb);
 void launch_moe_combine(hipStream_t s, float* x, int M, const MoeBufs& mb);
 int expert_slot_cap(int M);
+// M <= MRG rows: the down GEMV whose last workgroup per output column adds
+// the combine to x -- the same bits as launch_expert_down + launch_moe_combine.
+// cnt: DOWN_CNT_WORDS zero words (left at zero).
+constexpr int DOWN_CNT_WORDS = (D / 16) * 32;
+// The routing counter of launch_router sits after them, in the same buffer:
+// every user of those words leaves them at zero, in stream order.
+constexpr int ROUTE_CNT_WORD = DOWN_CNT_WORDS;
+template <typename T>
+void launch_expert_down_combine(hipStream_t s, const T* wd, int M, const MoeBufs& mb, float* x, unsigned* cnt);
+
+// The rest of the MoE half of a layer for M <= 8 rows, after
+// launch_router_logits, in one persistent launch of `grid` workgroups
+// (routing, gate/up, down and the combine, with the arithmetic and results of
+// the launches above): x_out = x_in + MoE(x_in).  sync: MOE_SYNC_WORDS zero
+// words (left at zero by every launch), word MOE_SYNC_ERR set if a bounded
+// wait timed out.  moe_fused_grid: the largest grid the GPU holds at once (0
+// if unknown).
+constexpr int MOE_SYNC_WORDS = 209 * 32;
+constexpr int MOE_SYNC_ERR = 3;
+template <typename T>
+int moe_fused_grid(int n_cu);
+template <typename T>
+void launch_moe_experts(hipStream_t s, int grid, const float* x_in, float* x_out, const T* wg, const T* wu,
+                        const T* wd, int M, const MoeBufs& mb, const RouteTap& tap, unsigned* sync);
 
 // Matrix-core variants (bf16 weights): the same outputs as the vector
 // launchers above, with the activations rounded to bf16 for the MFMA inputs.

@@ -36,7 +36,7 @@ struct Plan {
   // state
   size_t s_kv, s_dkv, s_ints, s_cu, s_hbuf, s_rope, s_total;
   // workspace
-  size_t w_x, w_q, w_attn, w_part, w_bnorm, w_ridx, w_rgate, w_perm, w_inv, w_off, w_act, w_slot, w_rlogit, w_misc, w_stats, w_hx,
+  size_t w_x, w_q, w_attn, w_part, w_bnorm, w_ridx, w_rgate, w_perm, w_inv, w_off, w_act, w_slot, w_rlogit, w_misc, w_stats, w_sync, w_acnt, w_hx,
       w_y, w_cat, w_u, w_u2, w_dffn, w_esave, w_hsave, w_lmv, w_lmi, w_plan, w_total;
 };
 
@@ -112,6 +112,9 @@ Plan make_plan(const ocrdec_config* c, bool decode_only = false) {
   p.w_rlogit = take(M * NE * 4);
   p.w_misc = take(64 * 4);       // [0] n_act, [16..] prefill tokens
   p.w_stats = take(8 * 8);
+  static_assert(ROUTE_CNT_WORD < MOE_SYNC_WORDS, "the down-combine and routing counters share the MoE sync words");
+  p.w_sync = take((size_t)MOE_SYNC_WORDS * 4);
+  p.w_acnt = take((size_t)p.plan_n * NH * 4);
   p.w_hx = take(M * NSLOT * DI * 4);
   p.w_y = take(M * NSLOT * D * 4);
   p.w_cat = take(M * 2 * D * 4);
@@ -132,6 +135,8 @@ Plan make_plan(const ocrdec_config* c, bool decode_only = false) {
 struct WsPtrs {
   float *x, *q, *attn, *part, *cat, *u, *u2, *dffn, *esave, *hsave[2], *lm_val;
   int *lm_idx, *plan_base, *plan_cnt, *plan_slot, *tok_tmp;
+  unsigned* sync;   // the persistent MoE launch's counters (zero between launches)
+  unsigned* acnt;   // attention chunk counters per (sequence, head) (zero between launches)
   MoeBufs mb;
 };
 
@@ -201,6 +206,8 @@ WsPtrs bind_workspace(char* ws, const Plan& p, int max_batch) {
   b.mb.slot_info = reinterpret_cast<int4*>(ws + p.w_slot);
   b.mb.rlogit = wf(p.w_rlogit);
   b.mb.stats = reinterpret_cast<long long*>(ws + p.w_stats);
+  b.sync = reinterpret_cast<unsigned*>(ws + p.w_sync);
+  b.acnt = reinterpret_cast<unsigned*>(ws + p.w_acnt);
   b.mb.hx = wf(p.w_hx);
   b.mb.y = wf(p.w_y);
   return b;
@@ -239,6 +246,8 @@ struct ocrdec_model {
   std::map<std::vector<uintptr_t>, hipGraphExec_t> graphs;  // by call shape
   char* scratch;               // this device's no-allocation scratch (null if unavailable)
   std::string scratch_err;
+  int moe_grid;                // workgroups of the persistent MoE launch (0: not available)
+  bool fused_moe;              // vector-path MoE halves in one persistent launch (else five launches)
 };
 
 namespace {
@@ -386,6 +395,15 @@ void dense_qkv(ocrdec_model* m, hipStream_t s, int dp, const float* x, const flo
   launch_qkv_rope<T>(s, x, gain, m->cfg.norm_eps, W, M, plan, m->b.q, kv, m->cfg.max_positions, m->rope);
 }
 
+// The rest of the MoE half of layer l (vector path, M <= 8), after the router
+// logits, in one persistent launch: x_out = x + MoE(x), x = the layer's
+// residual rows.
+template <typename T>
+void moe_experts(ocrdec_model* m, hipStream_t s, int l, int M, const RouteTap& tap, float* x_out) {
+  launch_moe_experts<T>(s, m->moe_grid, m->b.x, x_out, wmat<T>(m, lw(m, l, L_GATE)), wmat<T>(m, lw(m, l, L_UP)),
+                        wmat<T>(m, lw(m, l, L_DOWN)), M, m->b.mb, tap, m->b.sync);
+}
+
 template <typename T>
 void verifier_layers(ocrdec_model* m, hipStream_t s, PassPath pp, int M, int B, RowPlan plan, int nch, bool taps,
                      const float* rlog) {
@@ -393,7 +411,8 @@ void verifier_layers(ocrdec_model* m, hipStream_t s, PassPath pp, int M, int B, 
   for (int l = 0; l < c.n_layers; ++l) {
     T* kvl = static_cast<T*>((void*)(m->state + m->p.s_kv)) + (size_t)l * m->p.kv_layer_elems;
     dense_qkv<T>(m, s, pp.dense, m->b.x, wvec(m, lw(m, l, L_ANORM)), wmat<T>(m, lw(m, l, L_QKV)), M, plan, kvl);
-    launch_attention<T>(s, m->b.q, kvl, c.max_positions, plan, B, nch, m->p.tiles_per_chunk, m->b.part, m->b.attn);
+    launch_attention<T>(s, m->b.q, kvl, c.max_positions, plan, B, nch, m->p.tiles_per_chunk, m->b.part, m->b.attn,
+                        m->b.acnt);
     dense_gemv<T>(m, s, pp.dense, QD, EPI_ADD, m->b.attn, QD, nullptr, wmat<T>(m, lw(m, l, L_WO)), nullptr, D, M,
                   m->b.x, D);
     RouteTap tap{};
@@ -404,11 +423,25 @@ void verifier_layers(ocrdec_model* m, hipStream_t s, PassPath pp, int M, int B, 
       tap.pos_cap = m->taps.route_pos_cap;
     }
     tap.plan = plan;
+    if (!pp.experts && M <= MRG && m->fused_moe && m->moe_grid > 0) {
+      launch_router_logits<T>(s, m->b.x, wvec(m, lw(m, l, L_FNORM)), c.norm_eps, wmat<T>(m, lw(m, l, L_ROUTER)),
+                              M, m->b.mb, rlog ? rlog + (size_t)l * M * NE : nullptr);
+      timing_mark(m, s);
+      moe_experts<T>(m, s, l, M, tap, m->b.x);
+      timing_mark(m, s);
+      timing_mark(m, s);
+      continue;
+    }
     launch_router<T>(s, m->b.x, wvec(m, lw(m, l, L_FNORM)), c.norm_eps, wmat<T>(m, lw(m, l, L_ROUTER)), M, m->b.mb,
-                     tap, rlog ? rlog + (size_t)l * M * NE : nullptr);
+                     tap, rlog ? rlog + (size_t)l * M * NE : nullptr, m->b.sync + ROUTE_CNT_WORD);
     timing_mark(m, s);
     expert_gate_up<T>(m, s, l, M, pp.experts);
     timing_mark(m, s);
+    if (!pp.experts && M <= MRG) {  // the combine inside the down launch
+      launch_expert_down_combine<T>(s, wmat<T>(m, lw(m, l, L_DOWN)), M, m->b.mb, m->b.x, m->b.sync);
+      timing_mark(m, s);
+      continue;
+    }
     expert_down<T>(m, s, l, M, pp.experts);
     timing_mark(m, s);
     launch_moe_combine(s, m->b.x, M, m->b.mb);
@@ -427,7 +460,8 @@ void draft_layer(ocrdec_model* m, hipStream_t s, PassPath pp, int M, int B, RowP
     dense_gemv<T>(m, s, mx, 2 * D, EPI_STORE, m->b.cat, 2 * D, nullptr, wmat<T>(m, dw(m, D_FUSE)), nullptr, D, M, u,
                   D);
   dense_qkv<T>(m, s, mx, u, wvec(m, dw(m, D_ANORM)), wmat<T>(m, dw(m, D_QKV)), M, plan, dkv);
-  launch_attention<T>(s, m->b.q, dkv, c.max_positions, plan, B, nch, m->p.tiles_per_chunk, m->b.part, m->b.attn);
+  launch_attention<T>(s, m->b.q, dkv, c.max_positions, plan, B, nch, m->p.tiles_per_chunk, m->b.part, m->b.attn,
+                      m->b.acnt);
   dense_gemv<T>(m, s, mx, QD, EPI_ADD, m->b.attn, QD, nullptr, wmat<T>(m, dw(m, D_WO)), nullptr, D, M, u, D);
   dense_gemv<T>(m, s, mx, D, EPI_SWIGLU, u, D, wvec(m, dw(m, D_FNORM)), wmat<T>(m, dw(m, D_GATE)),
                 wmat<T>(m, dw(m, D_UP)), DF, M, m->b.dffn, DF);
@@ -487,7 +521,11 @@ int do_prefill(ocrdec_model* m, hipStream_t s, int B, const int32_t* slots_host,
 template <typename T>
 int do_draft(ocrdec_model* m, hipStream_t s, int B, const int32_t* slots, int K, int32_t* draft_out) {
   const ocrdec_config& c = m->cfg;
-  const int Q = K + 1;
+  // The catch-up pass carries the rows accepted at the last verify plus the
+  // pending token: up to (that verify's K) + 1 rows, so it is laid out for the
+  // handle's deepest draft, max_k + 1 rows per sequence, and K may change from
+  // one step to the next.
+  const int Q = m->p.cu_stride;
   // same chunk count as the verify of this step (a decode-step graph is keyed on it)
   const int nch = chunks_for(m, std::min(c.max_positions - 1, call_bound(m, B, slots) + K));
   const PassPath pp = decode_path<T>(m);
@@ -647,11 +685,19 @@ int ocrdec_create(const ocrdec_config* cfg, const void* const* weight_ptrs, int 
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess) dev = -1;
     m->scratch = scratch_for_device(dev, &m->scratch_err);
+    int n_cu = 0;
+    if (dev < 0 || hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n_cu = 0;
+    m->moe_grid = n_cu > 0 ? (cfg->dtype == OCRDEC_BF16 ? moe_fused_grid<bf16>(n_cu) : moe_fused_grid<float>(n_cu)) : 0;
+    if (m->moe_grid < NE / 4) m->moe_grid = 0;
+    (void)hipGetLastError();
+    m->fused_moe = false;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // clear an error left by earlier, unrelated runtime calls
   hipError_t err = hipMemsetAsync(misc, 0, 64 * 4, s);
   if (err == hipSuccess) err = hipMemsetAsync(m->b.mb.stats, 0, 64, s);
+  if (err == hipSuccess) err = hipMemsetAsync(m->b.sync, 0, (size_t)MOE_SYNC_WORDS * 4, s);
+  if (err == hipSuccess) err = hipMemsetAsync(m->b.acnt, 0, (size_t)p.plan_n * NH * 4, s);
   if (err == hipSuccess) err = hipMemsetAsync(m->state + p.s_ints, 0, p.s_hbuf - p.s_ints, s);
   if (err == hipSuccess) {
     launch_rope_table(s, cfg->max_positions, cfg->rope_theta, reinterpret_cast<float2*>(m->state + p.s_rope));
@@ -767,8 +813,15 @@ int ocrdec_replay_expert_gate_up(ocrdec_model* m, void* stream, int n_rounds, in
     *expert_sets_per_launch = na;
   }
   const int M = m->last_verify_rows;
+  const bool fused = !m->matrix && M <= MRG && m->fused_moe && m->moe_grid > 0;
   for (int r = 0; r < n_rounds; ++r) {
     for (int l = 0; l < m->cfg.n_layers; ++l) {
+      if (fused) {  // the persistent expert launch, its output to scratch (the residual rows stay as they are)
+        const RouteTap none{};
+        if (m->cfg.dtype == OCRDEC_BF16) moe_experts<bf16>(m, s, l, M, none, m->b.u);
+        else moe_experts<float>(m, s, l, M, none, m->b.u);
+        continue;
+      }
       if (m->cfg.dtype == OCRDEC_BF16) expert_gate_up<bf16>(m, s, l, M, decode_path<bf16>(m).experts);
       else expert_gate_up<float>(m, s, l, M, false);
     }
@@ -812,7 +865,7 @@ int ocrdec_decode_steps(ocrdec_model* m, void* stream, int B, const int32_t* slo
                                   (uintptr_t)m->taps.hidden, (uintptr_t)m->taps.route_pos,
                                   (uintptr_t)m->taps.route_pos_slot, (uintptr_t)m->taps.route_pos_cap,
                                   (uintptr_t)m->step_tap.acc, (uintptr_t)m->step_tap.drafts,
-                                  (uintptr_t)m->step_tap.cap};
+                                  (uintptr_t)m->step_tap.cap, (uintptr_t)m->fused_moe};
     if (ctrl) {
       key.push_back((uintptr_t)ctrl->trace);
       key.push_back((uintptr_t)ctrl->trace_stride);
@@ -877,8 +930,7 @@ int ocrdec_decode_steps_noalloc(ocrdec_model* m, void* stream, int B, const int3
     return fail(OCRDEC_EHIP, "the no-allocation scratch is not available on this device: " + m->scratch_err);
   // the decode calls' scratch for this call's rows, laid out in the static array
   ocrdec_config c = m->cfg;
-  c.max_batch = B;
-  c.max_k = K;
+  c.max_batch = B;                 // the draft's catch-up pass keeps the handle's max_k + 1 rows
   const Plan dp = make_plan(&c, true);
   if (dp.w_total > kScratchBytes)
     return fail(OCRDEC_ECAPACITY, "the call needs " + std::to_string(dp.w_total) +
@@ -892,6 +944,8 @@ int ocrdec_decode_steps_noalloc(ocrdec_model* m, void* stream, int B, const int3
   } swap{m, m->b};
   m->b = bind_workspace(m->scratch, dp, B);
   launch_fill_i32(s, reinterpret_cast<int*>(m->b.mb.stats), 2, 0);  // the expert counter starts at zero
+  launch_fill_i32(s, reinterpret_cast<int*>(m->b.sync), MOE_SYNC_WORDS, 0);  // and the MoE launch's counters
+  launch_fill_i32(s, reinterpret_cast<int*>(m->b.acnt), (long)dp.plan_n * NH, 0);  // and the attention's
   for (int step = 0; step < n_steps; ++step) {
     if (!slots && call_bound(m, B, slots) + K + 1 > m->cfg.max_positions)
       return fail(OCRDEC_ECAPACITY, "positions would exceed max_positions");
@@ -922,6 +976,15 @@ int ocrdec_sync_positions(ocrdec_model* m, void* stream) {
       hipMemcpy(ovf.data(), m->sv.ovf, (size_t)n * sizeof(int), hipMemcpyDeviceToHost) != hipSuccess)
     return fail(OCRDEC_EHIP, "reading the cache lengths failed");
   for (int i = 0; i < n; ++i) m->slot_bound[i] = std::max(0, std::min(kv[i], m->cfg.max_positions));
+  unsigned werr = 0;
+  if (hipMemcpy(&werr, m->b.sync + MOE_SYNC_ERR, sizeof(unsigned), hipMemcpyDeviceToHost) != hipSuccess)
+    return fail(OCRDEC_EHIP, "reading the wait-error word failed");
+  if (werr != 0) {
+    const unsigned zero = 0;
+    (void)hipMemcpy(m->b.sync + MOE_SYNC_ERR, &zero, sizeof(unsigned), hipMemcpyHostToDevice);
+    return fail(OCRDEC_EHIP, "a wait inside the persistent MoE launch timed out (its workgroups were not all "
+                             "resident on the GPU); results since the last check are not valid");
+  }
   std::string over;
   for (int i = 0; i < n; ++i)
     if (ovf[i]) over += (over.empty() ? "" : ", ") + std::to_string(i);
@@ -932,6 +995,17 @@ int ocrdec_sync_positions(ocrdec_model* m, void* stream) {
     return fail(OCRDEC_ECAPACITY, "slot(s) " + over + ": a step would pass max_positions and was not taken");
   }
   return OCRDEC_OK;
+}
+
+int ocrdec_set_moe_launches(ocrdec_model* m, int fused) {
+  if (!m) return fail(OCRDEC_EINVAL, "model is null");
+  m->fused_moe = fused != 0;
+  return OCRDEC_OK;
+}
+
+int ocrdec_moe_grid(ocrdec_model* m) {
+  if (!m) return fail(OCRDEC_EINVAL, "model is null");
+  return m->moe_grid;
 }
 
 int ocrdec_set_router_logits(ocrdec_model* m, const float* logits) {

@@ -25,7 +25,8 @@ SYMBOLS = (
     "ocrdec_prefill", "ocrdec_draft", "ocrdec_verify", "ocrdec_accept_rollback", "ocrdec_controlled_drafts",
     "ocrdec_set_taps", "ocrdec_expert_timing", "ocrdec_expert_stats", "ocrdec_replay_expert_gate_up",
     "ocrdec_decode_steps", "ocrdec_sync_positions", "ocrdec_load_sequence", "ocrdec_set_router_logits",
-    "ocrdec_read_probe", "ocrdec_last_error", "ocrdec_decode_steps_noalloc",
+    "ocrdec_read_probe", "ocrdec_last_error", "ocrdec_decode_steps_noalloc", "ocrdec_set_moe_launches",
+    "ocrdec_moe_grid",
 )
 
 
@@ -89,6 +90,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "ocrdec_sync_positions": (I, [P, P]),
         "ocrdec_load_sequence": (I, [P, P, I, I, I, P]),
         "ocrdec_set_router_logits": (I, [P, P]),
+        "ocrdec_set_moe_launches": (I, [P, I]),
+        "ocrdec_moe_grid": (I, [P]),
         "ocrdec_read_probe": (I, [P, P, ctypes.c_size_t, I, I, P]),
         "ocrdec_last_error": (ctypes.c_char_p, []),
     }
@@ -181,6 +184,16 @@ def ocrdec_load_sequence(h, stream: int, slot: int, n_pos: int, pending_token: i
 
 def ocrdec_set_router_logits(h, logits=None) -> None:
     _check("ocrdec_set_router_logits", load_library().ocrdec_set_router_logits(h, _ptr(logits)))
+
+
+def ocrdec_set_moe_launches(h, fused: bool):
+    _check("ocrdec_set_moe_launches", load_library().ocrdec_set_moe_launches(h, 1 if fused else 0))
+
+
+def ocrdec_moe_grid(h) -> int:
+    n = load_library().ocrdec_moe_grid(h)
+    _check("ocrdec_moe_grid", n if n < 0 else 0)
+    return int(n)
 
 
 def ocrdec_set_taps(h, route_idx=None, hidden=None, route_pos=None, route_pos_slot=0, accepted=None, drafts=None):
@@ -374,6 +387,49 @@ class Decoder:
             ln = torch.stack(lens).cpu().numpy()
             acc = [a[:int(np.argmax(ln[:, b] >= n_out)) + 1, b].tolist() for b in range(B)]
         return toks, acc, steps
+
+    def generate_adaptive(self, pages, n_out: int, controller, window: int = 8, trace=None, seed: int = 0,
+                          threshold: int = 0):
+        """Decode B pages to n_out tokens each with the draft depth chosen at run
+        time: every window of `window` steps runs at the depth controller.choose()
+        returns (decode-step graphs), timed with events on the stream; the
+        window's accepted lengths (read from the accepted-length tap) and its
+        time per step go back to controller.observe(K, accepted, ms_per_step).
+        ``trace`` switches on the controlled drafts.  Returns (tokens [B, n_out]
+        numpy, [(K, steps, ms_per_step)] per window)."""
+        torch = self.torch
+        B = len(pages)
+        Kmax = self.max_k
+        cap = n_out + Kmax + 2
+        out_tokens = torch.zeros(B, cap, dtype=torch.int32, device=self.device)
+        out_len, n_acc = self.i32(B), self.i32(B)
+        draft, greedy = self.i32(B, max(Kmax, 1)), self.i32(B, Kmax + 1)
+        steps_cap = n_out + window + 2
+        acc_tap = torch.full((self.max_batch, steps_cap), -1, dtype=torch.int32, device=self.device)
+        ocrdec_set_taps(self.h, accepted=acc_tap)
+        hist = []
+        try:
+            out_tokens[:, 0] = self.prefill(pages)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s0 = 0
+            while True:
+                K = int(controller.choose())
+                if not 1 <= K <= Kmax:
+                    raise ValueError(f"controller chose K = {K}, outside 1..{Kmax}")
+                e0.record()
+                self.decode_steps(B, K, window, draft, greedy, n_acc, out_tokens, out_len, trace, seed, threshold)
+                e1.record()
+                ocrdec_sync_positions(self.h, self.stream)
+                ms = e0.elapsed_time(e1) / window
+                acc = acc_tap[:B, s0:s0 + window].cpu().numpy()
+                controller.observe(K, acc.reshape(-1).tolist(), ms)
+                hist.append((K, window, ms))
+                s0 += window
+                if int(out_len.min().item()) >= n_out or s0 + window > steps_cap:
+                    break
+        finally:
+            ocrdec_set_taps(self.h)
+        return out_tokens[:, :n_out].cpu().numpy(), hist
 
     def _ragged_buffers(self, B: int, K: int, cap: int, T: int):
         """Per-shape scratch of generate_ragged, kept so that repeated runs pass the same

@@ -163,7 +163,7 @@ class ForcedRun:
 
 
 def forced_spec_parity(dec, orc, page, N, K, tol, p_replace, seed=3000, graphs=False, route_tol=None,
-                       min_steps=4):
+                       min_steps=4, k_sched=None):
     """FastMTP at depth K on one page with acceptance driven by the controlled
     drafts (the GPU's own K = 0 sequence, each slot replaced with probability
     p_replace), so that the catch-up pass of the real draft block carries 1 ..
@@ -174,7 +174,9 @@ def forced_spec_parity(dec, orc, page, N, K, tol, p_replace, seed=3000, graphs=F
     replays; accepted lengths from the accepted tap, greedy tokens of the
     committed rows from the output, routing from the by-position tap.  The
     oracle follows the GPU at excused near ties (forced history).  Accepted
-    lengths must equal the SplitMix64 prediction (the run is lossless)."""
+    lengths must equal the SplitMix64 prediction (the run is lossless).
+    k_sched(step) -> depth (optional, at most K) changes the depth per step
+    (graphs: one decode-step call per step)."""
     import torch
     from speculative_moe_decoding_amd import ocrdec
     cfg = dec.cfg
@@ -195,21 +197,37 @@ def forced_spec_parity(dec, orc, page, N, K, tol, p_replace, seed=3000, graphs=F
     ocrdec.ocrdec_set_taps(dec.h, route_idx=None if graphs else route_call, route_pos=route_pos,
                            route_pos_slot=0, accepted=acc_tap, drafts=dr_tap)
     gsteps = []
+    ks = (lambda s_: K) if k_sched is None else k_sched
     try:
         if graphs:
-            toks, _, nst = dec.generate([page], N, K, trace=trace, seed=seed, threshold=thr, check_every=2,
-                                        graphs=True)
+            if k_sched is None:
+                toks, _, nst = dec.generate([page], N, K, trace=trace, seed=seed, threshold=thr, check_every=2,
+                                            graphs=True)
+                toks = toks[0].tolist()
+            else:
+                draft, greedy = dec.i32(1, K), dec.i32(1, K + 1)
+                n_acc, out_len = dec.i32(1), dec.i32(1)
+                out_tokens = torch.zeros(1, N + K + 2, dtype=torch.int32, device="cuda")
+                out_tokens[:, 0] = dec.prefill([page])
+                s = 0
+                while True:
+                    dec.decode_steps(1, ks(s), 1, draft, greedy, n_acc, out_tokens, out_len, trace, seed, thr)
+                    s += 1
+                    ocrdec.ocrdec_sync_positions(dec.h, dec.stream)
+                    if int(out_len.item()) >= N:
+                        break
+                toks = out_tokens.cpu().numpy()[0][:N].tolist()
             torch.cuda.synchronize()
-            toks = toks[0].tolist()
             acc = acc_tap.cpu().numpy()[0]
             drs = dr_tap.cpu().numpy()[0]
             c = 1
             s = 0
             while c < N:
                 n = int(acc[s])
-                assert 0 <= n <= K, (s, n)
+                Ks = ks(s)
+                assert 0 <= n <= Ks, (s, n)
                 g_rows = toks[c:c + n + 1] if c + n + 1 <= N else None
-                gsteps.append(dict(real=drs[s, :K].tolist(), n=n, greedy=g_rows, logits=None, route=None))
+                gsteps.append(dict(real=drs[s, :Ks].tolist(), n=n, greedy=g_rows, logits=None, route=None))
                 c += n + 1
                 s += 1
             y0 = toks[0]
@@ -223,22 +241,28 @@ def forced_spec_parity(dec, orc, page, N, K, tol, p_replace, seed=3000, graphs=F
             lg = torch.empty(1, K + 1, V, dtype=torch.float32, device="cuda")
             c = 1
             while c < N:
-                dec.draft(1, K, out=draft)
-                real = draft.clone()
-                dec.controlled(1, K, trace, seed, thr, draft)
-                dec.verify(1, K, draft, greedy=greedy, logits=lg)
-                dec.accept(1, K, draft, greedy, n_acc, out_tokens, out_len)
+                Ks = ks(len(gsteps))
+                dk, gk, lk = draft[:, :Ks], greedy[:, :Ks + 1], lg[:, :Ks + 1]
+                dec.draft(1, Ks, out=dk)
+                real = dk.clone()
+                dec.controlled(1, Ks, trace, seed, thr, dk)
+                dec.verify(1, Ks, dk, greedy=gk, logits=lk)
+                dec.accept(1, Ks, dk, gk, n_acc, out_tokens, out_len)
                 torch.cuda.synchronize()
                 n = int(n_acc.item())
-                gsteps.append(dict(real=real.cpu().numpy()[0].tolist(), n=n, greedy=greedy.cpu().numpy()[0].tolist(),
-                                   logits=lg.cpu().numpy()[0], route=route_call.cpu().numpy().copy()))
+                gsteps.append(dict(real=real.cpu().numpy()[0].tolist(), n=n, greedy=gk.cpu().numpy()[0].tolist(),
+                                   logits=lk.cpu().numpy()[0],
+                                   route=route_call.flatten()[:cfg.n_layers * (Ks + 1) * 8].cpu().numpy().reshape(
+                                       cfg.n_layers, Ks + 1, 8)))
                 c += n + 1
+                if len(gsteps) % 8 == 0:
+                    ocrdec.ocrdec_sync_positions(dec.h, dec.stream)
             toks = out_tokens.cpu().numpy()[0][:N].tolist()
         rpos = route_pos.cpu().numpy()
     finally:
         ocrdec.ocrdec_set_taps(dec.h)
     assert toks == trace_np[:N].tolist(), "speculative output differs from the GPU's K = 0 output"
-    pred = od.controlled_accepts(N, K, seed, p_replace)
+    pred = od.controlled_accepts(N, K, seed, p_replace, k_schedule=k_sched)
     assert [s["n"] for s in gsteps] == pred[:len(gsteps)], "accepted lengths differ from the SplitMix64 prediction"
 
     # the oracle on the same history
@@ -254,7 +278,7 @@ def forced_spec_parity(dec, orc, page, N, K, tol, p_replace, seed=3000, graphs=F
         i = pos - ctx["q"]
         st_ = gsteps[s]
         if st_["route"] is not None:
-            return st_["route"][layer, i, :6] if 0 <= i <= K else None
+            return st_["route"][layer, i, :6] if 0 <= i < st_["route"].shape[1] else None
         if 0 <= i <= st_["n"]:                      # committed rows: the by-position tap
             r = rpos[layer, pos, :6]
             return None if r[0] < 0 else r
@@ -289,7 +313,8 @@ def forced_spec_parity(dec, orc, page, N, K, tol, p_replace, seed=3000, graphs=F
 
     states = []
     otoks, osteps = orc.generate_spec(page.vision, page.prompt, N, K, proposer=proposer, draft_for_cost=True,
-                                      greedy_hook=hook, pick=picker, first_token=y0, state_out=states)
+                                      greedy_hook=hook, pick=picker, first_token=y0, state_out=states,
+                                      k_schedule=k_sched)
     fl = states[0].first_logits
     if int(od.greedy(fl[None])[0]) != y0:
         assert float(od.top2_margin(fl)) < tol, "first token differs without a near tie"
@@ -297,7 +322,7 @@ def forced_spec_parity(dec, orc, page, N, K, tol, p_replace, seed=3000, graphs=F
     assert [s.accepted for s in osteps] == [s["n"] for s in gsteps]
     dc = de = 0
     for s, (g, r) in enumerate(zip(gsteps, osteps)):
-        for j in range(K):
+        for j in range(len(r.real_drafts)):
             dc += 1
             if g["real"][j] != r.real_drafts[j]:
                 assert r.draft_margins[j] < tol, \

@@ -197,3 +197,30 @@ def test_graph_steps_batches_and_depths(B, K):
     b = _eager_steps(dec, pages, K, 6, slots)
     assert a == b
     log(f"B={B} K={K}: graphs = eager = AR over {N} tokens; slot map 0..B-1 = identity")
+
+
+@pytest.mark.parametrize("which", ["f32_2layer", "bf16_2layer", "bf16_12layer"])
+def test_fused_moe_launch_bitwise(which):
+    """The persistent MoE launch (routing, gate/up, down, combine in one launch
+    after the router logits, with waits inside it) gives bitwise the logits,
+    drafts, greedy tokens and accepted lengths of the launches it replaces, step
+    after step of a K = 3 decode, on a handle of each kind (the 12-layer one is
+    the benchmark's)."""
+    from speculative_moe_decoding_amd import ocrdec
+    cfg = {"f32_2layer": SMALL32, "bf16_2layer": SMALL16, "bf16_12layer": synth.FULL}[which]
+    w = synth.Weights(cfg, 1234 if which == "bf16_12layer" else 95)
+    page = synth.make_pages(cfg, 96, [24], [6], [40])[0]
+    K, N = 3, 40
+    decs = [ocrdec.Decoder(cfg, w.device_arrays(), max_batch=1, max_k=K, max_positions=256) for _ in range(2)]
+    assert ocrdec.ocrdec_moe_grid(decs[0].h) > 0
+    ocrdec.ocrdec_set_moe_launches(decs[0].h, True)
+    ocrdec.ocrdec_set_moe_launches(decs[1].h, False)
+    log(f"case {which}: persistent MoE grid {ocrdec.ocrdec_moe_grid(decs[0].h)} workgroups")
+    runs = [run_gpu_steps(dec, page, N, K) for dec in decs]
+    (ta, sa), (tb, sb) = runs
+    assert ta == tb
+    assert len(sa) == len(sb)
+    for x, y in zip(sa, sb):
+        assert x["drafts"] == y["drafts"] and x["greedy"] == y["greedy"] and x["n"] == y["n"]
+        assert np.array_equal(x["logits"], y["logits"])
+    log(f"{which}: {len(sa)} steps, fused and five-launch MoE bitwise equal")

@@ -499,3 +499,44 @@ def test_greedy_hook_and_real_drafts():
     assert m.draft_propose(st, K) == s1[0].real_drafts
     # accepted lengths are the controlled generator's (n_prev then covers several values)
     assert [s.accepted for s in s1] == od.controlled_accepts(N, K, 3000, 0.3)
+
+
+def test_depth_schedule_lossless_and_catch_up():
+    """The draft depth may change from step to step (run-time adaptive K): the
+    output stays the AR sequence, a perfect proposer gets every step's depth
+    accepted, the controlled generator's prediction follows the schedule, and
+    the draft block's proposals after a deep step followed by a shallow one
+    (catch-up of up to 4 rows into a depth-1 step) equal a from-scratch draft
+    pass over the committed sequence."""
+    m = tiny_model(scale=8.0)
+    vision, prompt = tiny_page()
+    P = vision.shape[0] + len(prompt)
+    N = 30
+    sched = [3, 3, 1, 2, 1, 3, 2, 2, 1, 3] * 4
+    ks = lambda s: sched[s]
+    ar, _ = m.generate_ar(vision, prompt, N + 8)
+    toks, steps = m.generate_spec(vision, prompt, N, 3, proposer=od.trace_proposer(ar), draft_for_cost=True,
+                                  k_schedule=ks)
+    assert toks == ar[:N]
+    assert [s.accepted for s in steps[:-1]] == sched[:len(steps) - 1]
+    assert [len(s.drafts) for s in steps] == sched[:len(steps)]
+    p = 0.3
+    t2, s2 = m.generate_spec(vision, prompt, N, 3, proposer=od.controlled_proposer(ar, 3000, p, TINY.vocab),
+                             k_schedule=ks)
+    assert t2 == ar[:N]
+    assert [s.accepted for s in s2] == od.controlled_accepts(N, 3, 3000, p, k_schedule=ks)
+    for s in steps:
+        q = s.position
+        K = len(s.drafts)
+        e = np.concatenate([m.prefix_rows(vision, prompt), m.embed(ar[:q - P + 1])], axis=0)
+        st = m.new_state(q + K + 4)
+        h = m.verifier_forward(st, e, np.arange(q + 1))
+        hprev = np.concatenate([np.zeros((1, TINY.d_model)), h[:-1]], axis=0)
+        u = m.draft_forward(st, hprev, e, np.arange(q + 1))
+        d = [int(od.greedy(m.draft_logits(u[-1:]))[0])]
+        prev = u[-1:]
+        for j in range(2, K + 1):
+            u = m.draft_forward(st, prev, m.embed([d[-1]]), [q + j - 1])
+            d.append(int(od.greedy(m.draft_logits(u))[0]))
+            prev = u
+        assert d == s.real_drafts, (q, K)

@@ -42,3 +42,36 @@ def test_policy_on_measured_mi355x_costs():
     for K = 0..3 at the table's graph-mode acceptance) favours K = 2."""
     costs = {0: 0.668, 1: 0.901, 2: 1.120, 3: 1.321}
     assert policy.choose_k(costs, {1: 0.829, 2: 0.693, 3: 0.579}) == 2
+
+
+def test_online_depth_learns_acceptance_and_picks_the_best_depth():
+    """Fed steps whose drafts are accepted with a fixed per-draft probability
+    (the controlled benchmark's model) and the MI355X step costs, the run-time
+    controller's tau estimate converges to the geometric acceptance and it
+    settles on the depth with the best tokens per unit time."""
+    import numpy as np
+    rng = np.random.default_rng(0)
+    costs = {1: 0.705, 2: 0.867, 3: 1.005}         # measured ms per step, base page, graphs
+    q = 0.78                                         # per-draft acceptance
+    ctl = policy.OnlineDepth(3, explore_every=0)
+    picks = []
+    for _ in range(200):
+        k = ctl.choose()
+        picks.append(k)
+        n = []
+        for _ in range(8):
+            a = 0
+            while a < k and rng.random() < q:
+                a += 1
+            n.append(a)
+        ctl.observe(k, n, costs[k])
+    for k in (1, 2, 3):
+        exact = sum(q ** i for i in range(k + 1))
+        assert abs(ctl.tau(k) - exact) < 0.08, (k, ctl.tau(k), exact)
+    best = max((sum(q ** i for i in range(k + 1)) / costs[k], k) for k in costs)[1]
+    assert picks[-50:].count(best) == 50
+    # a controller told the k = 3 step costs as much as k = 1 moves to k = 3
+    ctl2 = policy.OnlineDepth(3, explore_every=0)
+    for k in (1, 2, 3) * 5:
+        ctl2.observe(k, [min(k, 2)] * 8, 1.0)
+    assert ctl2.choose() == 3
