@@ -166,7 +166,7 @@ def main() -> int:
                     help="concurrent32_bf16: scale of the per-page output lengths")
     ap.add_argument("--path", default="auto", choices=["auto", "vector", "matrix"],
                     help="base page: arithmetic path of the handle (auto = vector GEMV at batch 1)")
-    ap.add_argument("--moe-launches", default="five", choices=["persistent", "five"],
+    ap.add_argument("--moe-launches", default="separate", choices=["separate", "persistent"],
                     help="base page, vector path: the MoE half of each verifier layer as one persistent "
                          "launch after the router logits, or as the five launches router logits, routing, "
                          "gate/up, down, combine (the same bits)")

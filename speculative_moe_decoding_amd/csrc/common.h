@@ -29,7 +29,7 @@ constexpr int NSLOT = TOPK + NSH;  // routing slots per row: 6 routed then 2 sha
 constexpr int DI = 896;          // expert width
 constexpr int DF = 3584;         // draft FFN width
 constexpr int MRG = 8;           // activation rows per GEMV group
-constexpr int PREFILL_CHUNK = 8; // prefix rows per prefill pass
+constexpr int PREFILL_CHUNK = 32;  // prefix rows per prefill entry (positions 32 j .. 32 j + 31)
 constexpr int ATT_TILE = 64;     // keys per LDS tile in decode attention
 constexpr int LM_ROWS_PER_BLOCK = 64;
 
@@ -147,6 +147,41 @@ __device__ __forceinline__ float wave_max_dpp(float v) {
 }
 
 __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// v_mfma_f32_16x16x32_bf16 (wave64): lane l supplies A[l % 16][8 (l / 16) ..
+// +7] and B[8 (l / 16) .. +7][l % 16] (8 bf16 in 16 bytes each) and receives
+// D[4 (l / 16) + r][l % 16] in result register r.
+typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));
+typedef float f32x4_v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4_v mfma_bf16(const uint4& a, const uint4& b, f32x4_v c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, a), __builtin_bit_cast(bf16x8_v, b),
+                                                 c, 0, 0, 0);
+}
+
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+typedef float f32x2_v __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 (round to nearest even; gfx950 converts in hardware).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2_v f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_v));
+}
+
+// a - bf16(a) for the two halves of a packed pair (exact in fp32).
+__device__ __forceinline__ float rem_lo(float a, uint32_t h) { return a - __uint_as_float(h << 16); }
+__device__ __forceinline__ float rem_hi(float a, uint32_t h) { return a - __uint_as_float(h & 0xffff0000u); }
+
+// Eight fp32 as bf16 hi = bf16(a) and lo = bf16(a - hi) fragments.
+__device__ __forceinline__ void split_bf16x8(const float4& a, const float4& b, uint4& hi, uint4& lo) {
+  hi.x = pack_bf16x2(a.x, a.y);
+  hi.y = pack_bf16x2(a.z, a.w);
+  hi.z = pack_bf16x2(b.x, b.y);
+  hi.w = pack_bf16x2(b.z, b.w);
+  lo.x = pack_bf16x2(rem_lo(a.x, hi.x), rem_hi(a.y, hi.x));
+  lo.y = pack_bf16x2(rem_lo(a.z, hi.y), rem_hi(a.w, hi.y));
+  lo.z = pack_bf16x2(rem_lo(b.x, hi.z), rem_hi(b.y, hi.z));
+  lo.w = pack_bf16x2(rem_lo(b.z, hi.w), rem_hi(b.w, hi.w));
+}
 
 // Streaming (non-temporal) 16-byte load of weights that are read once per
 // launch: keeps them from displacing the activations and KV tiles in the caches.

@@ -395,6 +395,241 @@ void launch_attention(hipStream_t s, const float* q, const T* kv, int max_pos, R
                      tiles_per_chunk * ATT_TILE, max_pos, out);
 }
 
+// ---- prefill attention --------------------------------------------------
+//
+// Block (entry b, head h) serves the entry's PREFILL_CHUNK = 32 query rows,
+// wavefront w rows 16 w .. 16 w + 15, over 64-key tiles 0, 64, .. up to the
+// entry's last position.  Per tile and wavefront, on the matrix cores:
+//   S = Q K^T / sqrt(128): four 16x16 blocks (keys 16 n .. 16 n + 15), Q in
+//     bf16 hi + lo parts (the fp32 queries to about 16 bits), keys exact;
+//   the online softmax per row: row max over the 64 keys (the four blocks in
+//     a lane, then the 16 lanes of the row), correction exp(m_old - m_new),
+//     p = exp(s - m_new) for visible keys (key <= the row's position), else 0;
+//   O += P V: eight 16x16 blocks of 16 value dims, P (via LDS, in the A
+//     layout) in hi + lo parts, values from an LDS copy of the tile stored
+//     transposed, eight bf16 of one dim per 16 bytes; the values of keys past
+//     the entry's last position (cache rows not yet written, whatever their
+//     bits) are staged as zeros, so that p = 0 there adds exact zeros.
+// Tiles start at multiples of 64 and a masked key adds exact zeros (in a
+// fully masked tile the row's max, sum and output stay as they are), so a
+// row's result does not depend on the other rows of the launch.
+constexpr int PA_VT_STRIDE = ATT_TILE / 2 + 4;  // 32-bit words per transposed value row (+4: spreads banks)
+
+__global__ __launch_bounds__(128) void k_attn_prefill_mfma(const float* __restrict__ q, const bf16* __restrict__ kv,
+                                                           int max_pos, RowPlan plan, float* __restrict__ out) {
+  __shared__ __align__(16) uint32_t vt[HD][PA_VT_STRIDE];  // vt[d][k / 2] = (v[k][d], v[k + 1][d]) as bf16 pairs
+  __shared__ __align__(16) float pl[2][16][ATT_TILE + 4];  // per wavefront: P rows
+  const int b = blockIdx.x, h = blockIdx.y;
+  const int wave = wave_id(), lane = lane_id(), tid = threadIdx.x;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int Q = plan.Q;
+  const int base = plan.base[b], cnt = min(plan.cnt[b], Q);
+  const long slot = plan.slot[b];
+  const bf16* Kc = kv + slot * (2L * NH * max_pos * HD) + (long)h * max_pos * HD;
+  const bf16* Vc = Kc + (long)NH * max_pos * HD;
+  const int p_last = min(base + cnt - 1, max_pos - 1);
+  // A fragments of this wavefront's 16 query rows (row c16, dims 32 s + 8 g ..)
+  const int qi = 16 * wave + c16;
+  uint4 qh[4], ql[4];
+  {
+    const bool ok = qi < cnt;
+    const float4* qp = reinterpret_cast<const float4*>(q + (long)(b * Q + (ok ? qi : 0)) * QD + h * HD);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      float4 a = qp[8 * st + 2 * g], c = qp[8 * st + 2 * g + 1];
+      if (!ok) a = c = make_float4(0.f, 0.f, 0.f, 0.f);
+      split_bf16x8(a, c, qh[st], ql[st]);
+    }
+  }
+  // this lane's rows of the S / O blocks: i = 16 wave + 4 g + r
+  int plim[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int i = 16 * wave + 4 * g + r;
+    plim[r] = i < cnt ? base + i : -1;  // last visible key (-1: none)
+  }
+  float mrun[4], lrun[4];
+  f32x4_v o[8];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) { mrun[r] = -INFINITY; lrun[r] = 0.f; }
+#pragma unroll
+  for (int d = 0; d < 8; ++d) o[d] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+  // tile loads: key fragments (key kt + 16 n + c16, dims 32 s + 8 g ..) and
+  // this thread's value chunks (keys 2 kp, 2 kp + 1, dims 8 dc ..)
+  uint4 kf[4][4], vc[4][2];
+  auto load_tile = [&](int kt) {
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const long k = min(kt + 16 * n + c16, max_pos - 1);
+#pragma unroll
+      for (int st = 0; st < 4; ++st) kf[n][st] = ldg16(Kc + k * HD + 32 * st + 8 * g);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = tid + 128 * j, kp = e >> 4, dc = e & 15;  // 32 key pairs x 16 dim chunks
+      const long k0 = min(kt + 2 * kp, max_pos - 1), k1 = min(kt + 2 * kp + 1, max_pos - 1);
+      vc[j][0] = ldg16(Vc + k0 * HD + 8 * dc);
+      vc[j][1] = ldg16(Vc + k1 * HD + 8 * dc);
+    }
+  };
+  const int n_tiles = cnt > 0 && base >= 0 ? p_last / ATT_TILE + 1 : 0;
+  const float scale = 0.08838834764831845f;  // 1 / sqrt(128)
+  if (n_tiles > 0) load_tile(0);
+  for (int t = 0; t < n_tiles; ++t) {
+    const int kt = t * ATT_TILE;
+    // S blocks from the key fragments in registers
+    f32x4_v sb[4];
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      sb[n] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        sb[n] = mfma_bf16(qh[st], kf[n][st], sb[n]);
+        sb[n] = mfma_bf16(ql[st], kf[n][st], sb[n]);
+      }
+    }
+    __syncthreads();  // the previous tile's reads of vt are done
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {  // transposed value staging; keys past p_last (never written) as zeros
+      const int e = tid + 128 * j, kp = e >> 4, dc = e & 15;
+      if (kt + 2 * kp > p_last) vc[j][0] = make_uint4(0, 0, 0, 0);
+      if (kt + 2 * kp + 1 > p_last) vc[j][1] = make_uint4(0, 0, 0, 0);
+      const uint32_t* a = reinterpret_cast<const uint32_t*>(&vc[j][0]);
+      const uint32_t* c = reinterpret_cast<const uint32_t*>(&vc[j][1]);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {  // dims 8 dc + 2 w, 8 dc + 2 w + 1
+        vt[8 * dc + 2 * w][kp] = (a[w] & 0xffffu) | (c[w] << 16);
+        vt[8 * dc + 2 * w + 1][kp] = (a[w] >> 16) | (c[w] & 0xffff0000u);
+      }
+    }
+    if (t + 1 < n_tiles) load_tile(kt + ATT_TILE);  // next tile in flight during this one's arithmetic
+    // online softmax of this lane's four rows
+    float corr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float s4[4];
+      float mt = -INFINITY;
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const int key = kt + 16 * n + c16;
+        s4[n] = sb[n][r] * scale;
+        if (key > plim[r]) s4[n] = -INFINITY;
+        mt = fmaxf(mt, s4[n]);
+      }
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) mt = fmaxf(mt, xor_lane(mt, off));
+      const float mnew = fmaxf(mrun[r], mt);
+      corr[r] = (mnew == -INFINITY) ? 1.f : expf(mrun[r] - mnew);
+      float ps = 0.f;
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const float p = (s4[n] == -INFINITY) ? 0.f : expf(s4[n] - mnew);
+        pl[wave][4 * g + r][16 * n + c16] = p;
+        ps += p;
+      }
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) ps += xor_lane(ps, off);
+      lrun[r] = lrun[r] * corr[r] + ps;
+      mrun[r] = mnew;
+    }
+#pragma unroll
+    for (int d = 0; d < 8; ++d)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[d][r] *= corr[r];
+    __syncthreads();  // vt staged, P written
+    // O += P V over the tile's two 32-key steps
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const float* pr = &pl[wave][c16][32 * st + 8 * g];
+      const float4 pa = *reinterpret_cast<const float4*>(pr), pb = *reinterpret_cast<const float4*>(pr + 4);
+      uint4 ph, plo;
+      split_bf16x8(pa, pb, ph, plo);
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        const uint4 vb = *reinterpret_cast<const uint4*>(&vt[16 * d + c16][16 * st + 4 * g]);
+        o[d] = mfma_bf16(ph, vb, o[d]);
+        o[d] = mfma_bf16(plo, vb, o[d]);
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int i = 16 * wave + 4 * g + r;
+    float* orow = out + (long)(b * Q + i) * QD + h * HD;
+    const bool ok = plim[r] >= 0;
+    const float inv = ok ? 1.0f / lrun[r] : 0.f;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) orow[16 * d + c16] = ok ? o[d][r] * inv : 0.f;
+  }
+}
+
+// The fp32 cache: block (entry b, head h), wavefront w serves rows w, w + 4,
+// ..; per 64-key tile, lane = key for the scores (q . k in order over the 128
+// dims), the online softmax, then lane = value-dim pair for the output.
+__global__ __launch_bounds__(256) void k_attn_prefill_f32(const float* __restrict__ q, const float* __restrict__ kv,
+                                                          int max_pos, RowPlan plan, float* __restrict__ out) {
+  __shared__ float pw[4][ATT_TILE];
+  const int b = blockIdx.x, h = blockIdx.y;
+  const int wave = wave_id(), lane = lane_id();
+  const int Q = plan.Q;
+  const int base = plan.base[b], cnt = min(plan.cnt[b], Q);
+  const long slot = plan.slot[b];
+  const float* Kc = kv + slot * (2L * NH * max_pos * HD) + (long)h * max_pos * HD;
+  const float* Vc = Kc + (long)NH * max_pos * HD;
+  const float scale = 0.08838834764831845f;
+  for (int i = wave; i < Q; i += 4) {
+    float* orow = out + (long)(b * Q + i) * QD + h * HD;
+    const int plim = min(base + i, max_pos - 1);
+    if (i >= cnt || base < 0) {
+      orow[2 * lane] = 0.f;
+      orow[2 * lane + 1] = 0.f;
+      continue;
+    }
+    const float* qr = q + (long)(b * Q + i) * QD + h * HD;
+    float mrun = -INFINITY, lrun = 0.f, o0 = 0.f, o1 = 0.f;
+    for (int kt = 0; kt <= plim; kt += ATT_TILE) {
+      const int key = kt + lane;
+      const bool vis = key <= plim;
+      const float* kr = Kc + (long)min(key, max_pos - 1) * HD;
+      float sc = 0.f;
+      for (int d = 0; d < HD; ++d) sc = fmaf(qr[d], kr[d], sc);
+      sc *= scale;
+      const float mt = wave_max(vis ? sc : -INFINITY);
+      const float mnew = fmaxf(mrun, mt);
+      const float corr = expf(mrun - mnew);
+      const float p = vis ? expf(sc - mnew) : 0.f;
+      lrun = lrun * corr + wave_sum(p);
+      pw[wave][lane] = p;
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      float a0 = o0 * corr, a1 = o1 * corr;
+      const int nk = min(ATT_TILE, plim + 1 - kt);
+      for (int t = 0; t < nk; ++t) {
+        const float2 v = *reinterpret_cast<const float2*>(Vc + (long)(kt + t) * HD + 2 * lane);
+        a0 = fmaf(pw[wave][t], v.x, a0);
+        a1 = fmaf(pw[wave][t], v.y, a1);
+      }
+      o0 = a0;
+      o1 = a1;
+      mrun = mnew;
+      __builtin_amdgcn_wave_barrier();
+    }
+    orow[2 * lane] = o0 / lrun;
+    orow[2 * lane + 1] = o1 / lrun;
+  }
+}
+
+template <>
+void launch_attention_prefill<bf16>(hipStream_t s, const float* q, const bf16* kv, int max_pos, RowPlan plan, int n,
+                                    float* out) {
+  hipLaunchKernelGGL(k_attn_prefill_mfma, dim3(n, NH), dim3(128), 0, s, q, kv, max_pos, plan, out);
+}
+template <>
+void launch_attention_prefill<float>(hipStream_t s, const float* q, const float* kv, int max_pos, RowPlan plan, int n,
+                                     float* out) {
+  hipLaunchKernelGGL(k_attn_prefill_f32, dim3(n, NH), dim3(256), 0, s, q, kv, max_pos, plan, out);
+}
+
 template void launch_attention<float>(hipStream_t, const float*, const float*, int, RowPlan, int, int, int, float*,
                                       float*, unsigned*);
 template void launch_attention<bf16>(hipStream_t, const float*, const bf16*, int, RowPlan, int, int, int, float*,

@@ -24,22 +24,6 @@
 
 namespace ocr {
 
-typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));
-typedef float f32x4_v __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ f32x4_v mfma_bf16(const uint4& a, const uint4& b, f32x4_v c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, a), __builtin_bit_cast(bf16x8_v, b),
-                                                 c, 0, 0, 0);
-}
-
-typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
-typedef float f32x2_v __attribute__((ext_vector_type(2)));
-
-// Two fp32 -> packed bf16 (round to nearest even; gfx950 converts in hardware).
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const f32x2_v f = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_v));
-}
 
 constexpr int MF_KC = 128;           // k per LDS chunk
 constexpr int MF_SC = MF_KC / 32;    // MFMA k-steps per chunk
@@ -100,9 +84,6 @@ __device__ __forceinline__ float4 mf_norm(const float4& a, float r, const float4
   return make_float4((a.x * r) * g.x, (a.y * r) * g.y, (a.z * r) * g.z, (a.w * r) * g.w);
 }
 
-// a - bf16(a) for the two halves of a packed pair (exact in fp32).
-__device__ __forceinline__ float rem_lo(float a, uint32_t h) { return a - __uint_as_float(h << 16); }
-__device__ __forceinline__ float rem_hi(float a, uint32_t h) { return a - __uint_as_float(h & 0xffff0000u); }
 
 // Parts NP = 1: ch[0] = bf16(a); NP = 2: also ch[1] = bf16(a - bf16(a)).
 // NORM: a is first normalised with the thread's row scales rsv and gains gq.

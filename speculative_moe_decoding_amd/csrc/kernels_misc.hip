@@ -289,9 +289,10 @@ __global__ __launch_bounds__(256) void k_draft_fuse(DraftIn<T> a, const T* __res
   if (t.lead && t.m < m_act && n < D) out[(long)(m0 + t.m) * D + n] = t.val;
 }
 
-// Prefill pass: rows j*8 + i (entry j, i < cnt[j]) hold positions p0[j] + i
-// of sequence seq[j] -- vision rows, then prompt ids; rows past cnt[j] are
-// zero.  esave keeps the input rows for the draft prefill.  Grid (8, n).
+// Prefill pass: rows j * PREFILL_CHUNK + i (entry j, i < cnt[j]) hold
+// positions p0[j] + i of sequence seq[j] -- vision rows, then prompt ids; rows
+// past cnt[j] are zero.  esave keeps the input rows for the draft prefill.
+// Grid (PREFILL_CHUNK, n).
 template <typename T>
 __global__ __launch_bounds__(256) void k_plan_prefill(PrefillGroup g, const float* __restrict__ vision,
                                                       int nv_stride, const int* __restrict__ prompt, int np_stride,
@@ -324,7 +325,8 @@ __global__ __launch_bounds__(256) void k_plan_prefill(PrefillGroup g, const floa
 // (h_{p-1}, e_p); h of an entry's first row is the last verifier hidden of
 // the entry before it when that is the same sequence, else of the sequence's
 // previous pass (hprev[slot]; a zero row at p = 0).  The last verifier hidden
-// of a sequence's last entry in the pass goes to hnext[slot].  Grid (8, n).
+// of a sequence's last entry in the pass goes to hnext[slot].  Grid
+// (PREFILL_CHUNK, n).
 __global__ __launch_bounds__(256) void k_draft_prefill_cat(PrefillGroup g, const float* __restrict__ xfinal,
                                                            const float* __restrict__ esave,
                                                            const float* __restrict__ hprev,

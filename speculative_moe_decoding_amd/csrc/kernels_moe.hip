@@ -232,7 +232,7 @@ __global__ __launch_bounds__(256) void k_route_small(const float* __restrict__ r
   publish_route(r, M, mb, tap, st0);
 }
 
-// Larger batches (8 < M <= 1024): top-6 per row, one wavefront per row
+// Larger batches (8 < M <= 2048): top-6 per row, one wavefront per row
 // (rank_and_gate) ...
 __global__ __launch_bounds__(256) void k_topk_rows(const float* __restrict__ rlogit, int M, MoeBufs mb,
                                                    RouteTap tap) {
@@ -269,7 +269,7 @@ __global__ __launch_bounds__(256) void k_topk_rows(const float* __restrict__ rlo
 // order) and per-range bases; pair p lands at off[e] + base[w][e] + rank --
 // the permutation of any stable sort by expert id.
 constexpr int RL_WAVES = 16;
-constexpr int RL_SEGS = 8;  // segments per wavefront: M <= RL_WAVES * RL_SEGS * 8 = 1024
+constexpr int RL_SEGS = 16;  // segments per wavefront: M <= RL_WAVES * RL_SEGS * 8 = 2048
 __global__ __launch_bounds__(1024) void k_sort_pairs(int M, MoeBufs mb) {
   __shared__ int wcnt[RL_WAVES][NX + 1];  // per range: counts, then exclusive bases
   __shared__ int off[NX + 1], act[NX + 1];

@@ -45,6 +45,15 @@ template <typename T>
 void launch_attention(hipStream_t s, const float* q, const T* kv, int max_pos, RowPlan plan, int B,
                       int n_chunks, int tiles_per_chunk, float* part, float* out, unsigned* acnt);
 
+// Prefill attention: n entries of plan.Q = PREFILL_CHUNK rows; row i of entry
+// b (i < cnt[b]) is the query at position base[b] + i of slot slot[b] and sees
+// keys 0 .. base[b] + i of the cache, all of them written before the call.
+// out[b * Q + i] = the head outputs (rows past cnt: zero).  bf16 caches on the
+// matrix cores, fp32 caches on the vector units.
+template <typename T>
+void launch_attention_prefill(hipStream_t s, const float* q, const T* kv, int max_pos, RowPlan plan, int n,
+                              float* out);
+
 struct MoeBufs {
   float* bnorm;   // [M][D] normalised rows
   int* ridx;      // [M][8]
@@ -203,7 +212,7 @@ void launch_plan_draft_step(hipStream_t s, int B, int j, int Qprev, int K, State
 // slot[j], n_vision nvis[j], prefix length plen[j]), in activation rows
 // j * PREFILL_CHUNK + i.  Entries of one sequence are consecutive and in
 // position order, so a long prefix fills several entries of one pass.
-constexpr int PREFILL_GROUP = 32;
+constexpr int PREFILL_GROUP = 64;
 struct PrefillGroup {
   int n;
   int seq[PREFILL_GROUP], slot[PREFILL_GROUP], p0[PREFILL_GROUP], cnt[PREFILL_GROUP], nvis[PREFILL_GROUP],

@@ -31,7 +31,7 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 // Offsets of every sub-buffer inside the state and the workspace.
 struct Plan {
   // derived sizes
-  int Qmax, M_max, prefill_group, cu_stride, tiles_per_chunk, chunk_keys, n_chunks_cap, lm_nblk, plan_n;
+  int M_max, prefill_group, cu_stride, tiles_per_chunk, chunk_keys, n_chunks_cap, lm_nblk, plan_n;
   size_t esz, kv_layer_elems;
   // state
   size_t s_kv, s_dkv, s_ints, s_cu, s_hbuf, s_rope, s_total;
@@ -74,7 +74,6 @@ bool use_matrix_path(const ocrdec_config* c) {
 // to max_batch sequences at depth max_k, without the prefill's buffers.
 Plan make_plan(const ocrdec_config* c, bool decode_only = false) {
   Plan p{};
-  p.Qmax = std::max(c->max_k + 1, PREFILL_CHUNK);
   // prefill passes take up to prefill_group entries of PREFILL_CHUNK rows
   p.prefill_group = decode_only ? 0 : PREFILL_GROUP;
   p.M_max = std::max(c->max_batch * (c->max_k + 1), PREFILL_CHUNK * p.prefill_group);
@@ -100,7 +99,8 @@ Plan make_plan(const ocrdec_config* c, bool decode_only = false) {
   p.w_x = take(M * D * 4);
   p.w_q = take(M * QD * 4);
   p.w_attn = take(M * QD * 4);
-  p.w_part = take(M * NH * (size_t)p.n_chunks_cap * (HD + 2) * 4);
+  // split-KV partials of the decode calls (prefill passes use the prefill attention)
+  p.w_part = take((size_t)c->max_batch * (c->max_k + 1) * NH * (size_t)p.n_chunks_cap * (HD + 2) * 4);
   p.w_bnorm = take(M * D * 4);
   p.w_ridx = take(M * NSLOT * 4);
   p.w_rgate = take(M * NSLOT * 4);
@@ -307,19 +307,20 @@ enum DensePath { DENSE_VECTOR = 0, DENSE_KSPLIT = 1, DENSE_STRIP = 2 };
 struct PassPath {
   bool experts;  // grouped experts on the matrix cores
   int dense;     // DensePath of the QKV / O / draft GEMVs
+  bool prefill;  // prefix entries: the prefill attention
 };
 
 template <typename T>
 PassPath decode_path(const ocrdec_model* m) {
   const bool mx = std::is_same<T, bf16>::value && m->matrix;
-  return PassPath{mx, mx ? DENSE_KSPLIT : DENSE_VECTOR};
+  return PassPath{mx, mx ? DENSE_KSPLIT : DENSE_VECTOR, false};
 }
 
 template <typename T>
 PassPath prefill_path(const ocrdec_model* m) {
   (void)m;
   const bool bf = std::is_same<T, bf16>::value;
-  return PassPath{bf, bf ? DENSE_STRIP : DENSE_VECTOR};
+  return PassPath{bf, bf ? DENSE_STRIP : DENSE_VECTOR, true};
 }
 
 template <typename T>
@@ -404,6 +405,19 @@ void moe_experts(ocrdec_model* m, hipStream_t s, int l, int M, const RouteTap& t
                         wmat<T>(m, lw(m, l, L_DOWN)), M, m->b.mb, tap, m->b.sync);
 }
 
+// Attention of the pass's rows into b.attn: the prefill attention for prefix
+// entries, else split-KV decode attention.
+template <typename T>
+void attention(ocrdec_model* m, hipStream_t s, PassPath pp, const float* q, const T* kv, RowPlan plan, int B,
+               int nch) {
+  if (pp.prefill) {
+    launch_attention_prefill<T>(s, q, kv, m->cfg.max_positions, plan, B, m->b.attn);
+    return;
+  }
+  launch_attention<T>(s, q, kv, m->cfg.max_positions, plan, B, nch, m->p.tiles_per_chunk, m->b.part, m->b.attn,
+                      m->b.acnt);
+}
+
 template <typename T>
 void verifier_layers(ocrdec_model* m, hipStream_t s, PassPath pp, int M, int B, RowPlan plan, int nch, bool taps,
                      const float* rlog) {
@@ -411,8 +425,7 @@ void verifier_layers(ocrdec_model* m, hipStream_t s, PassPath pp, int M, int B, 
   for (int l = 0; l < c.n_layers; ++l) {
     T* kvl = static_cast<T*>((void*)(m->state + m->p.s_kv)) + (size_t)l * m->p.kv_layer_elems;
     dense_qkv<T>(m, s, pp.dense, m->b.x, wvec(m, lw(m, l, L_ANORM)), wmat<T>(m, lw(m, l, L_QKV)), M, plan, kvl);
-    launch_attention<T>(s, m->b.q, kvl, c.max_positions, plan, B, nch, m->p.tiles_per_chunk, m->b.part, m->b.attn,
-                        m->b.acnt);
+    attention<T>(m, s, pp, m->b.q, kvl, plan, B, nch);
     dense_gemv<T>(m, s, pp.dense, QD, EPI_ADD, m->b.attn, QD, nullptr, wmat<T>(m, lw(m, l, L_WO)), nullptr, D, M,
                   m->b.x, D);
     RouteTap tap{};
@@ -460,8 +473,7 @@ void draft_layer(ocrdec_model* m, hipStream_t s, PassPath pp, int M, int B, RowP
     dense_gemv<T>(m, s, mx, 2 * D, EPI_STORE, m->b.cat, 2 * D, nullptr, wmat<T>(m, dw(m, D_FUSE)), nullptr, D, M, u,
                   D);
   dense_qkv<T>(m, s, mx, u, wvec(m, dw(m, D_ANORM)), wmat<T>(m, dw(m, D_QKV)), M, plan, dkv);
-  launch_attention<T>(s, m->b.q, dkv, c.max_positions, plan, B, nch, m->p.tiles_per_chunk, m->b.part, m->b.attn,
-                      m->b.acnt);
+  attention<T>(m, s, pp, m->b.q, dkv, plan, B, nch);
   dense_gemv<T>(m, s, mx, QD, EPI_ADD, m->b.attn, QD, nullptr, wmat<T>(m, dw(m, D_WO)), nullptr, D, M, u, D);
   dense_gemv<T>(m, s, mx, D, EPI_SWIGLU, u, D, wvec(m, dw(m, D_FNORM)), wmat<T>(m, dw(m, D_GATE)),
                 wmat<T>(m, dw(m, D_UP)), DF, M, m->b.dffn, DF);

@@ -31,7 +31,7 @@ def test_smoke():
 @pytest.mark.parametrize("cfg,tol", [(SMALL32, 1e-3), (SMALL16, 5e-2)], ids=["f32", "bf16"])
 def test_small_model_ar_and_spec(cfg, tol):
     """2 layers, vocab 5003 (ragged against the 64-row LM-head tiles), prefix
-    20 vision + 5 prompt rows (prefill passes of 8, 8, 8, 1 rows)."""
+    20 vision + 5 prompt rows (one prefill entry of 25 rows)."""
     w, dec, orc = make_pair(cfg, 41)
     page = synth.make_pages(cfg, 42, [20], [5], [24])[0]
     N = 24
