@@ -218,20 +218,20 @@ __device__ __forceinline__ void gate_up_pass(const bf16* const (&w)[2], const fl
   }
 }
 
+// Block (x, y): work item y (an expert and at most 64 of its pairs, so that a
+// shared expert's rows of a long prefill spread over many blocks).
 __global__ __launch_bounds__(256) void k_expert_gate_up_mfma(const bf16* __restrict__ wg,
                                                              const bf16* __restrict__ wu, int M, MoeBufs mb) {
   __shared__ MfChunk buf[2][2];
-  const int4 info = expert_work(mb, blockIdx.y, M);
-  const int e = info.x;
+  const int4 it = mb.items[blockIdx.y];
+  const int e = it.x;
   if (e < 0) return;
   const int j0 = blockIdx.x * 64 + wave_id() * 16;
   const bf16* const w[2] = {wg + ((long)e * DI + j0) * D, wu + ((long)e * DI + j0) * D};
-  for (int kb = info.y; kb < info.z; kb += MF_ROWS) {
-    const int rows = min(MF_ROWS, info.z - kb);
-    if (rows <= 16) gate_up_pass<1>(w, mb.bnorm, mb.perm, kb, rows, mb.hx, j0, buf);
-    else if (rows <= 32) gate_up_pass<2>(w, mb.bnorm, mb.perm, kb, rows, mb.hx, j0, buf);
-    else gate_up_pass<4>(w, mb.bnorm, mb.perm, kb, rows, mb.hx, j0, buf);
-  }
+  const int kb = it.y, rows = it.z - it.y;
+  if (rows <= 16) gate_up_pass<1>(w, mb.bnorm, mb.perm, kb, rows, mb.hx, j0, buf);
+  else if (rows <= 32) gate_up_pass<2>(w, mb.bnorm, mb.perm, kb, rows, mb.hx, j0, buf);
+  else gate_up_pass<4>(w, mb.bnorm, mb.perm, kb, rows, mb.hx, j0, buf);
 }
 
 // Down: block (x, slot s) computes outputs n0 .. n0+31, n0 = 128 x + 32 w:
@@ -258,32 +258,31 @@ __device__ __forceinline__ void down_pass(const bf16* const (&w)[1], const float
 
 __global__ __launch_bounds__(256) void k_expert_down_mfma(const bf16* __restrict__ wd, int M, MoeBufs mb) {
   __shared__ MfChunk buf[2][2];
-  const int4 info = expert_work(mb, blockIdx.y, M);
-  const int e = info.x;
+  const int4 it = mb.items[blockIdx.y];
+  const int e = it.x;
   if (e < 0) return;
   const int n0 = blockIdx.x * 128 + wave_id() * 32;
   const bf16* const w[1] = {wd + ((long)e * D + n0) * DI};
-  for (int kb = info.y; kb < info.z; kb += MF_ROWS) {
-    const int rows = min(MF_ROWS, info.z - kb);
-    if (rows <= 16) down_pass<1>(w, mb.hx, kb, rows, mb.y, n0, buf);
-    else if (rows <= 32) down_pass<2>(w, mb.hx, kb, rows, mb.y, n0, buf);
-    else down_pass<4>(w, mb.hx, kb, rows, mb.y, n0, buf);
-  }
+  const int kb = it.y, rows = it.z - it.y;
+  if (rows <= 16) down_pass<1>(w, mb.hx, kb, rows, mb.y, n0, buf);
+  else if (rows <= 32) down_pass<2>(w, mb.hx, kb, rows, mb.y, n0, buf);
+  else down_pass<4>(w, mb.hx, kb, rows, mb.y, n0, buf);
 }
 
 void launch_expert_gate_up_mfma(hipStream_t s, const bf16* wg, const bf16* wu, int M, const MoeBufs& mb) {
-  hipLaunchKernelGGL(k_expert_gate_up_mfma, dim3(DI / 64, expert_slot_cap(M)), dim3(256), 0, s, wg, wu, M, mb);
+  hipLaunchKernelGGL(k_expert_gate_up_mfma, dim3(DI / 64, expert_item_cap(M)), dim3(256), 0, s, wg, wu, M, mb);
 }
 
 void launch_expert_down_mfma(hipStream_t s, const bf16* wd, int M, const MoeBufs& mb) {
-  hipLaunchKernelGGL(k_expert_down_mfma, dim3(D / 128, expert_slot_cap(M)), dim3(256), 0, s, wd, M, mb);
+  hipLaunchKernelGGL(k_expert_down_mfma, dim3(D / 128, expert_item_cap(M)), dim3(256), 0, s, wd, M, mb);
 }
 
 // ---- dense layers on the matrix cores -------------------------------------
-// Block (strip x, row tile y) multiplies activation rows 16 y .. 16 y + 15
+// Block (strip x, row block y) multiplies activation rows 64 y .. 64 y + 63
 // (RMSNorm'ed first when a gain is given: the scale of each row as in
 // norm_rows_wave) with its strip of weight rows, one 16-row tile per
-// wavefront and per matrix, in one mfma_pass (inputs as bf16 hi + lo parts).
+// wavefront and per matrix, in one mfma_pass of 1, 2 or 4 row tiles (inputs as
+// bf16 hi + lo parts), so a strip is read once per 64 rows.
 //   DM_STORE / DM_ADD: out[m][n] = / += W0[n] . a_m, strip = rows 64 x ..;
 //   DM_SWIGLU: out[m][n] = silu(W0[n] . a_m) * (W1[n] . a_m);
 //   DM_QKV (fused RoPE and cache append, as k_qkv_rope): strip x = section
@@ -300,17 +299,74 @@ struct QkvOut {
   const float2* rope;
 };
 
+template <int K, int MODE, int NT>
+__device__ __forceinline__ void dense_mfma_rows(const float* __restrict__ a, long lda, const float* __restrict__ gain,
+                                                const bf16* const (&w)[(MODE == DM_SWIGLU || MODE == DM_QKV) ? 2 : 1],
+                                                int m0, int rows, float* __restrict__ out, long ldo,
+                                                const QkvOut& qo, int sec, int h, int n0, MfChunk (&buf)[2][2],
+                                                const float* rs) {
+  constexpr int NB = (MODE == DM_SWIGLU || MODE == DM_QKV) ? 2 : 1;
+  const int wave = wave_id(), lane = lane_id();
+  auto rowp = [=](int r) { return a + (long)(m0 + r) * lda; };
+  f32x4_v acc[NT][NB][1];
+  if (gain != nullptr) mfma_pass<K, NT, NB, 1, 2, decltype(rowp), true>(w, rowp, rows, buf, acc, gain, rs);
+  else mfma_pass<K, NT, NB, 1, 2, decltype(rowp), false>(w, rowp, rows, buf, acc);
+  const int j = lane & 15;
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const int r = 16 * i + 4 * (lane >> 4) + qq;
+      if (r >= rows) continue;
+      const int m = m0 + r;
+      const float v0 = acc[i][0][0][qq];
+      if constexpr (MODE == DM_STORE) {
+        out[(long)m * ldo + n0 + j] = v0;
+      } else if constexpr (MODE == DM_ADD) {
+        out[(long)m * ldo + n0 + j] += v0;
+      } else if constexpr (MODE == DM_SWIGLU) {
+        out[(long)m * ldo + n0 + j] = silu(v0) * acc[i][NB - 1][0][qq];
+      } else {
+        const float v1 = acc[i][NB - 1][0][qq];
+        const RowPlan& plan = qo.plan;
+        const int b = m / plan.Q, ii = m - b * plan.Q;
+        const int pos = plan.base[b] + ii;
+        const bool valid = ii < plan.cnt[b] && pos >= 0 && pos < qo.max_pos;
+        const long slot_stride = 2L * NH * qo.max_pos * HD;
+        if (sec < 2) {
+          const int u = 16 * wave + j;
+          const float2 cs = qo.rope[(long)min(max(pos, 0), qo.max_pos - 1) * (HD / 2) + u];
+          const float o0 = fmaf(v0, cs.x, -(v1 * cs.y));
+          const float o1 = fmaf(v1, cs.x, v0 * cs.y);
+          if (sec == 0) {
+            qo.q[(long)m * QD + h * HD + u] = o0;
+            qo.q[(long)m * QD + h * HD + u + 64] = o1;
+          } else if (valid) {
+            bf16* kd = qo.kv + (long)plan.slot[b] * slot_stride + ((long)h * qo.max_pos + pos) * HD;
+            kd[u] = f2bf(o0);
+            kd[u + 64] = f2bf(o1);
+          }
+        } else if (valid) {
+          bf16* vd = qo.kv + (long)plan.slot[b] * slot_stride + ((long)(NH + h) * qo.max_pos + pos) * HD;
+          vd[32 * wave + j] = f2bf(v0);
+          vd[32 * wave + 16 + j] = f2bf(v1);
+        }
+      }
+    }
+  }
+}
+
 template <int K, int MODE>
 __global__ __launch_bounds__(256) void k_dense_mfma(const float* __restrict__ a, long lda,
                                                     const float* __restrict__ gain, float eps,
                                                     const bf16* __restrict__ W0, const bf16* __restrict__ W1, int M,
                                                     float* __restrict__ out, long ldo, QkvOut qo) {
   constexpr int NB = (MODE == DM_SWIGLU || MODE == DM_QKV) ? 2 : 1;
-  __shared__ MfChunkT<1> buf[2][2];
-  __shared__ float rs[16];
+  __shared__ MfChunk buf[2][2];
+  __shared__ float rs[MF_ROWS];
   const int wave = wave_id(), lane = lane_id();
-  const int m0 = blockIdx.y * 16;
-  const int rows = min(16, M - m0);
+  const int m0 = blockIdx.y * MF_ROWS;
+  const int rows = min(MF_ROWS, M - m0);
   const bf16* w[NB];
   int sec = 0, h = 0, n0 = 0;
   if constexpr (MODE == DM_QKV) {
@@ -324,10 +380,8 @@ __global__ __launch_bounds__(256) void k_dense_mfma(const float* __restrict__ a,
     w[0] = W0 + (long)n0 * K;
     if constexpr (NB == 2) w[1] = W1 + (long)n0 * K;
   }
-  auto rowp = [=](int r) { return a + (long)(m0 + r) * lda; };
-  f32x4_v acc[1][NB][1];
   if (gain != nullptr) {
-    for (int r = wave; r < 16; r += 4) {
+    for (int r = wave; r < MF_ROWS; r += 4) {
       float ss = 0.f;
       if (r < rows) {
         const float* xr = a + (long)(m0 + r) * lda;
@@ -341,50 +395,10 @@ __global__ __launch_bounds__(256) void k_dense_mfma(const float* __restrict__ a,
       if (lane == 0) rs[r] = 1.0f / sqrtf(ss / (float)K + eps);
     }
     __syncthreads();
-    mfma_pass<K, 1, NB, 1, 2, decltype(rowp), true, 1>(w, rowp, rows, buf, acc, gain, rs);
-  } else {
-    mfma_pass<K, 1, NB, 1, 2, decltype(rowp), false, 1>(w, rowp, rows, buf, acc);
   }
-  const int j = lane & 15;
-#pragma unroll
-  for (int qq = 0; qq < 4; ++qq) {
-    const int r = 4 * (lane >> 4) + qq;
-    if (r >= rows) continue;
-    const int m = m0 + r;
-    const float v0 = acc[0][0][0][qq];
-    if constexpr (MODE == DM_STORE) {
-      out[(long)m * ldo + n0 + j] = v0;
-    } else if constexpr (MODE == DM_ADD) {
-      out[(long)m * ldo + n0 + j] += v0;
-    } else if constexpr (MODE == DM_SWIGLU) {
-      out[(long)m * ldo + n0 + j] = silu(v0) * acc[0][1][0][qq];
-    } else {
-      const float v1 = acc[0][1][0][qq];
-      const RowPlan& plan = qo.plan;
-      const int b = m / plan.Q, i = m - b * plan.Q;
-      const int pos = plan.base[b] + i;
-      const bool valid = i < plan.cnt[b] && pos >= 0 && pos < qo.max_pos;
-      const long slot_stride = 2L * NH * qo.max_pos * HD;
-      if (sec < 2) {
-        const int u = 16 * wave + j;
-        const float2 cs = qo.rope[(long)min(max(pos, 0), qo.max_pos - 1) * (HD / 2) + u];
-        const float o0 = fmaf(v0, cs.x, -(v1 * cs.y));
-        const float o1 = fmaf(v1, cs.x, v0 * cs.y);
-        if (sec == 0) {
-          qo.q[(long)m * QD + h * HD + u] = o0;
-          qo.q[(long)m * QD + h * HD + u + 64] = o1;
-        } else if (valid) {
-          bf16* kd = qo.kv + (long)plan.slot[b] * slot_stride + ((long)h * qo.max_pos + pos) * HD;
-          kd[u] = f2bf(o0);
-          kd[u + 64] = f2bf(o1);
-        }
-      } else if (valid) {
-        bf16* vd = qo.kv + (long)plan.slot[b] * slot_stride + ((long)(NH + h) * qo.max_pos + pos) * HD;
-        vd[32 * wave + j] = f2bf(v0);
-        vd[32 * wave + 16 + j] = f2bf(v1);
-      }
-    }
-  }
+  if (rows <= 16) dense_mfma_rows<K, MODE, 1>(a, lda, gain, w, m0, rows, out, ldo, qo, sec, h, n0, buf, rs);
+  else if (rows <= 32) dense_mfma_rows<K, MODE, 2>(a, lda, gain, w, m0, rows, out, ldo, qo, sec, h, n0, buf, rs);
+  else dense_mfma_rows<K, MODE, 4>(a, lda, gain, w, m0, rows, out, ldo, qo, sec, h, n0, buf, rs);
 }
 
 // Decode-sized calls: the same outputs with more, smaller blocks.  Block
@@ -593,7 +607,7 @@ void launch_qkv_rope_ks(hipStream_t s, const float* x, const float* gain, float 
 
 bool launch_gemv_mfma(hipStream_t s, int K, Epi epi, const float* a, long lda, const float* gain, float eps,
                       const bf16* W0, const bf16* W1, int N, int M, float* out, long ldo) {
-  const dim3 grid(N / 64, (M + 15) / 16);
+  const dim3 grid(N / 64, (M + MF_ROWS - 1) / MF_ROWS);
   const QkvOut none{};
 #define OCR_DM(KV, MODEV) \
   hipLaunchKernelGGL((k_dense_mfma<KV, MODEV>), grid, dim3(256), 0, s, a, lda, gain, eps, W0, W1, M, out, ldo, none)
@@ -610,8 +624,8 @@ bool launch_gemv_mfma(hipStream_t s, int K, Epi epi, const float* a, long lda, c
 void launch_qkv_rope_mfma(hipStream_t s, const float* x, const float* gain, float eps, const bf16* wqkv, int M,
                           RowPlan plan, float* q, bf16* kv, int max_pos, const float2* rope) {
   const QkvOut qo{plan, q, kv, max_pos, rope};
-  hipLaunchKernelGGL((k_dense_mfma<D, DM_QKV>), dim3(3 * NH, (M + 15) / 16), dim3(256), 0, s, x, (long)D, gain, eps,
-                     wqkv, nullptr, M, nullptr, 0L, qo);
+  hipLaunchKernelGGL((k_dense_mfma<D, DM_QKV>), dim3(3 * NH, (M + MF_ROWS - 1) / MF_ROWS), dim3(256), 0, s, x,
+                     (long)D, gain, eps, wqkv, nullptr, M, nullptr, 0L, qo);
 }
 
 // LM head rows for the matrix cores: xn[m] = RMSNorm(x[src(m)]) * gain, one

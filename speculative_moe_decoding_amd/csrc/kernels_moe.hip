@@ -151,15 +151,17 @@ __device__ __forceinline__ void publish_route(const RouteLds& r, int M, const Mo
     tap_pair(tap, p / NSLOT, p % NSLOT, r.pe[p]);
   }
   for (int e = tid; e <= NX; e += 256) mb.off[e] = r.off[e];
-  for (int sl = tid; sl < NX; sl += 256) {
+  for (int sl = tid; sl < expert_item_cap(M); sl += 256) {  // M <= 8: one item per active expert
     if (sl < r.na) {
       const int e = r.act[sl];
       int rows = 0;  // bit m: row m has a pair routed to e (pairs sort by row)
       for (int p = r.off[e]; p < r.off[e + 1]; ++p) rows |= 1 << (r.perm[p] / NSLOT);
       mb.act[sl] = e;
       mb.slot_info[sl] = make_int4(e, r.off[e], r.off[e + 1], rows);
+      mb.items[sl] = make_int4(e, r.off[e], r.off[e + 1], 0);
     } else {
-      mb.slot_info[sl] = make_int4(-1, 0, 0, 0);
+      if (sl < NX) mb.slot_info[sl] = make_int4(-1, 0, 0, 0);
+      mb.items[sl] = make_int4(-1, 0, 0, 0);
     }
   }
   if (tid == 0) {
@@ -272,7 +274,7 @@ constexpr int RL_WAVES = 16;
 constexpr int RL_SEGS = 16;  // segments per wavefront: M <= RL_WAVES * RL_SEGS * 8 = 2048
 __global__ __launch_bounds__(1024) void k_sort_pairs(int M, MoeBufs mb) {
   __shared__ int wcnt[RL_WAVES][NX + 1];  // per range: counts, then exclusive bases
-  __shared__ int off[NX + 1], act[NX + 1];
+  __shared__ int off[NX + 1], act[NX + 1], ioff[NX + 1];
   __shared__ int na_s;
   const int wave = threadIdx.x >> 6, lane = lane_id(), tid = threadIdx.x;
   const int p_lo = NSLOT * (M * wave / RL_WAVES), p_hi = NSLOT * (M * (wave + 1) / RL_WAVES);
@@ -331,12 +333,24 @@ __global__ __launch_bounds__(1024) void k_sort_pairs(int M, MoeBufs mb) {
       if (c > 0) act[na++] = e;  // na <= e: entries not yet read are never overwritten
     }
     off[NX] = acc;
+    int it = 0;  // first work item of each active expert (64 pairs per item)
+    for (int sl = 0; sl < na; ++sl) {
+      ioff[sl] = it;
+      it += (off[act[sl] + 1] - off[act[sl]] + 63) / 64;
+    }
+    ioff[na] = it;
     na_s = na;
     *mb.n_act = na;
     mb.stats[0] += na;
   }
   __syncthreads();
   const int na = na_s;
+  for (int sl = tid; sl < na; sl += 1024) {
+    const int e = act[sl];
+    for (int i = ioff[sl], k = off[e]; i < ioff[sl + 1]; ++i, k += 64)
+      mb.items[i] = make_int4(e, k, min(k + 64, off[e + 1]), 0);
+  }
+  for (int i = ioff[na] + tid; i < expert_item_cap(M); i += 1024) mb.items[i] = make_int4(-1, 0, 0, 0);
   for (int e = tid; e <= NX; e += 1024) mb.off[e] = off[e];
   for (int sl = tid; sl < NX; sl += 1024) {
     if (sl < na) {

@@ -64,6 +64,8 @@ struct MoeBufs {
   int* act;       // [NX] active experts in increasing id
   int* n_act;     // [1]
   int4* slot_info;  // [NX] (expert, first pair, end pair, n_act); expert -1 past n_act
+  int4* items;    // [expert_item_cap(M)] matrix-core work items: (expert, first pair, end pair, 0),
+                  // at most 64 pairs each, experts in slot order; expert -1 past the last
   long long* stats;  // [0] += active experts per layer
   float* rlogit;  // [M][64] router logits
   float* hx;      // [8M][DI]
@@ -116,6 +118,8 @@ template <typename T>
 void launch_expert_down(hipStream_t s, const T* wd, int M, const MoeBufs& mb);
 void launch_moe_combine(hipStream_t s, float* x, int M, const MoeBufs& mb);
 int expert_slot_cap(int M);
+// Upper bound on the work items of a call: sum over experts of ceil(pairs / 64).
+__host__ __device__ inline int expert_item_cap(int M) { return NX + (NSLOT * M + 63) / 64; }
 // M <= MRG rows: the down GEMV whose last workgroup per output column adds
 // the combine to x -- the same bits as launch_expert_down + launch_moe_combine.
 // cnt: DOWN_CNT_WORDS zero words (left at zero).

@@ -36,7 +36,7 @@ struct Plan {
   // state
   size_t s_kv, s_dkv, s_ints, s_cu, s_hbuf, s_rope, s_total;
   // workspace
-  size_t w_x, w_q, w_attn, w_part, w_bnorm, w_ridx, w_rgate, w_perm, w_inv, w_off, w_act, w_slot, w_rlogit, w_misc, w_stats, w_sync, w_acnt, w_hx,
+  size_t w_x, w_q, w_attn, w_part, w_bnorm, w_ridx, w_rgate, w_perm, w_inv, w_off, w_act, w_slot, w_items, w_rlogit, w_misc, w_stats, w_sync, w_acnt, w_hx,
       w_y, w_cat, w_u, w_u2, w_dffn, w_esave, w_hsave, w_lmv, w_lmi, w_plan, w_total;
 };
 
@@ -109,6 +109,7 @@ Plan make_plan(const ocrdec_config* c, bool decode_only = false) {
   p.w_off = take((NX + 1) * 4);
   p.w_act = take(NX * 4);
   p.w_slot = take(NX * 16);
+  p.w_items = take((size_t)expert_item_cap(p.M_max) * 16);
   p.w_rlogit = take(M * NE * 4);
   p.w_misc = take(64 * 4);       // [0] n_act, [16..] prefill tokens
   p.w_stats = take(8 * 8);
@@ -204,6 +205,7 @@ WsPtrs bind_workspace(char* ws, const Plan& p, int max_batch) {
   b.mb.off = wi(p.w_off);
   b.mb.act = wi(p.w_act);
   b.mb.slot_info = reinterpret_cast<int4*>(ws + p.w_slot);
+  b.mb.items = reinterpret_cast<int4*>(ws + p.w_items);
   b.mb.rlogit = wf(p.w_rlogit);
   b.mb.stats = reinterpret_cast<long long*>(ws + p.w_stats);
   b.sync = reinterpret_cast<unsigned*>(ws + p.w_sync);
