@@ -29,6 +29,7 @@ constexpr int MF_KC = 128;           // k per LDS chunk
 constexpr int MF_SC = MF_KC / 32;    // MFMA k-steps per chunk
 constexpr int MF_MT = 4;             // 16-row tiles per pass
 constexpr int MF_ROWS = 16 * MF_MT;  // activation rows per pass
+constexpr int MF_BP = 3;             // weight chunks in flight per wavefront
 
 // One LDS chunk of CT tiles: f[tile][step][mf_slot(step, lane)] is lane's A
 // fragment, i.e. row 16 tile + lane % 16, k = 32 step + 8 (lane / 16) .. +7
@@ -115,6 +116,10 @@ __device__ __forceinline__ void mf_store_a(MfChunkT<CT> (&ch)[NP], float4 (&ar)[
   }
 }
 
+// Per k-step: the hi part against every (tile, matrix, strip) accumulator,
+// then the lo part, so that consecutive MFMAs into one accumulator are
+// NT * NB * NS instructions apart (the same sums, in the same order, per
+// accumulator).
 template <int NT, int NB, int NS, int NP, int CT>
 __device__ __forceinline__ void mf_compute(const MfChunkT<CT> (&ch)[NP], const uint4 (&bq)[NB][NS][MF_SC],
                                            f32x4_v (&acc)[NT][NB][NS]) {
@@ -122,9 +127,9 @@ __device__ __forceinline__ void mf_compute(const MfChunkT<CT> (&ch)[NP], const u
 #pragma unroll
   for (int s = 0; s < MF_SC; ++s) {
 #pragma unroll
-    for (int i = 0; i < NT; ++i) {
+    for (int p = 0; p < NP; ++p) {
 #pragma unroll
-      for (int p = 0; p < NP; ++p) {
+      for (int i = 0; i < NT; ++i) {
         const uint4 a = ch[p].f[i][s][mf_slot(s, lane)];
 #pragma unroll
         for (int b = 0; b < NB; ++b)
@@ -162,39 +167,33 @@ __device__ __forceinline__ void mfma_pass(const bf16* const (&w)[NB], RowPtr row
     rsv[i] = NORM ? rs[ok[i] ? r : 0] : 1.f;
   }
   const float* gn = NORM ? g : nullptr;
-  float4 gq[2];
 #pragma unroll
   for (int i = 0; i < NT; ++i)
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int n = 0; n < NS; ++n) acc[i][b][n] = f32x4_v{0.f, 0.f, 0.f, 0.f};
-  uint4 bq0[NB][NS][MF_SC], bq1[NB][NS][MF_SC];
-  float4 ar[NT][2];
-  mf_load_a(ar, gq, src, ok, gn, kg, 0);
-  mf_load_b<K, NB, NS>(bq0, w, woff, 0);
-  mf_store_a<NT, NP, NORM, CT>(buf[0], ar, gq, rsv, kg, ri);
+  // Weights: a ring of MF_BP chunks in registers; activations: two chunks in
+  // registers and two in LDS.  Chunk c + 2's rows are loaded before chunk c's
+  // arithmetic and chunk c + MF_BP's weights after it, so that waiting for
+  // chunk c + 1's rows (loads complete in issue order) never waits for the
+  // weights of chunks c + 2 .. c + MF_BP.  One barrier per chunk.
+  constexpr int BP = NC < MF_BP ? NC : MF_BP;
+  uint4 bq[MF_BP][NB][NS][MF_SC];
+  float4 ar[2][NT][2], gq[2][2];
+  mf_load_a(ar[0], gq[0], src, ok, gn, kg, 0);
+  if (NC > 1) mf_load_a(ar[1], gq[1], src, ok, gn, kg, 1);
+#pragma unroll
+  for (int c = 0; c < BP; ++c) mf_load_b<K, NB, NS>(bq[c], w, woff, c);
+  mf_store_a<NT, NP, NORM, CT>(buf[0], ar[0], gq[0], rsv, kg, ri);
   __syncthreads();
-  // Chunk c computes from LDS buffer c % 2 and registers bq(c % 2) while
-  // chunk c + 1 is loaded into the other pair; one barrier per chunk.
-#pragma unroll 1
-  for (int c = 0; c < NC; c += 2) {
-    if (c + 1 < NC) {
-      mf_load_a(ar, gq, src, ok, gn, kg, c + 1);  // activations first: waiting for them does not wait for the weights
-      mf_load_b<K, NB, NS>(bq1, w, woff, c + 1);
-    }
-    mf_compute<NT, NB, NS, NP, CT>(buf[0], bq0, acc);
-    if (c + 1 < NC) mf_store_a<NT, NP, NORM, CT>(buf[1], ar, gq, rsv, kg, ri);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    if (c + 2 < NC) mf_load_a(ar[c & 1], gq[c & 1], src, ok, gn, kg, c + 2);
+    mf_compute<NT, NB, NS, NP, CT>(buf[c & 1], bq[c % MF_BP], acc);
+    if (c + MF_BP < NC) mf_load_b<K, NB, NS>(bq[c % MF_BP], w, woff, c + MF_BP);
+    if (c + 1 < NC) mf_store_a<NT, NP, NORM, CT>(buf[(c + 1) & 1], ar[(c + 1) & 1], gq[(c + 1) & 1], rsv, kg, ri);
     __syncthreads();
-    if (c + 1 < NC) {
-      if (c + 2 < NC) {
-        mf_load_a(ar, gq, src, ok, gn, kg, c + 2);
-        mf_load_b<K, NB, NS>(bq0, w, woff, c + 2);
-      }
-      mf_compute<NT, NB, NS, NP, CT>(buf[1], bq1, acc);
-      if (c + 2 < NC) mf_store_a<NT, NP, NORM, CT>(buf[0], ar, gq, rsv, kg, ri);
-      __syncthreads();
-    }
   }
 }
 
@@ -356,9 +355,30 @@ __device__ __forceinline__ void dense_mfma_rows(const float* __restrict__ a, lon
   }
 }
 
+// RMSNorm scales of M rows of K: rs[m] = 1 / sqrt(mean(x_m^2) + eps), one
+// wavefront per row (lane l sums x[k]^2 over k = l + 64 j in order, then the
+// xor butterfly, as norm_rows_wave does).
+template <int K>
+__global__ __launch_bounds__(256) void k_row_rms(const float* __restrict__ a, long lda, int M, float eps,
+                                                 float* __restrict__ rs) {
+  const int m = blockIdx.x * 4 + wave_id();
+  if (m >= M) return;
+  const int lane = lane_id();
+  const float* xr = a + (long)m * lda;
+  float v[K / 64];
+#pragma unroll
+  for (int j = 0; j < K / 64; ++j) v[j] = xr[lane + 64 * j];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < K / 64; ++j) ss = fmaf(v[j], v[j], ss);
+  ss = wave_sum(ss);
+  if (lane == 0) rs[m] = 1.0f / sqrtf(ss / (float)K + eps);
+}
+
+// rsc: the rows' RMSNorm scales (k_row_rms) when a gain is given.
 template <int K, int MODE>
 __global__ __launch_bounds__(256) void k_dense_mfma(const float* __restrict__ a, long lda,
-                                                    const float* __restrict__ gain, float eps,
+                                                    const float* __restrict__ gain, const float* __restrict__ rsc,
                                                     const bf16* __restrict__ W0, const bf16* __restrict__ W1, int M,
                                                     float* __restrict__ out, long ldo, QkvOut qo) {
   constexpr int NB = (MODE == DM_SWIGLU || MODE == DM_QKV) ? 2 : 1;
@@ -381,19 +401,7 @@ __global__ __launch_bounds__(256) void k_dense_mfma(const float* __restrict__ a,
     if constexpr (NB == 2) w[1] = W1 + (long)n0 * K;
   }
   if (gain != nullptr) {
-    for (int r = wave; r < MF_ROWS; r += 4) {
-      float ss = 0.f;
-      if (r < rows) {
-        const float* xr = a + (long)(m0 + r) * lda;
-#pragma unroll 4
-        for (int j = 0; j < K / 64; ++j) {
-          const float v = xr[lane + 64 * j];
-          ss = fmaf(v, v, ss);
-        }
-      }
-      ss = wave_sum(ss);
-      if (lane == 0) rs[r] = 1.0f / sqrtf(ss / (float)K + eps);
-    }
+    if (threadIdx.x < MF_ROWS) rs[threadIdx.x] = rsc[m0 + min((int)threadIdx.x, rows - 1)];
     __syncthreads();
   }
   if (rows <= 16) dense_mfma_rows<K, MODE, 1>(a, lda, gain, w, m0, rows, out, ldo, qo, sec, h, n0, buf, rs);
@@ -606,11 +614,16 @@ void launch_qkv_rope_ks(hipStream_t s, const float* x, const float* gain, float 
 }
 
 bool launch_gemv_mfma(hipStream_t s, int K, Epi epi, const float* a, long lda, const float* gain, float eps,
-                      const bf16* W0, const bf16* W1, int N, int M, float* out, long ldo) {
+                      const bf16* W0, const bf16* W1, int N, int M, float* out, long ldo, float* rscale) {
   const dim3 grid(N / 64, (M + MF_ROWS - 1) / MF_ROWS);
   const QkvOut none{};
+  if (gain != nullptr) {
+    if (K != D) return false;  // the normed inputs are model rows
+    hipLaunchKernelGGL((k_row_rms<D>), dim3((M + 3) / 4), dim3(256), 0, s, a, lda, M, eps, rscale);
+  }
 #define OCR_DM(KV, MODEV) \
-  hipLaunchKernelGGL((k_dense_mfma<KV, MODEV>), grid, dim3(256), 0, s, a, lda, gain, eps, W0, W1, M, out, ldo, none)
+  hipLaunchKernelGGL((k_dense_mfma<KV, MODEV>), grid, dim3(256), 0, s, a, lda, gain, rscale, W0, W1, M, out, ldo, \
+                     none)
   if (K == D && epi == EPI_ADD) OCR_DM(D, DM_ADD);
   else if (K == D && epi == EPI_SWIGLU) OCR_DM(D, DM_SWIGLU);
   else if (K == D && epi == EPI_STORE) OCR_DM(D, DM_STORE);
@@ -622,10 +635,11 @@ bool launch_gemv_mfma(hipStream_t s, int K, Epi epi, const float* a, long lda, c
 }
 
 void launch_qkv_rope_mfma(hipStream_t s, const float* x, const float* gain, float eps, const bf16* wqkv, int M,
-                          RowPlan plan, float* q, bf16* kv, int max_pos, const float2* rope) {
+                          RowPlan plan, float* q, bf16* kv, int max_pos, const float2* rope, float* rscale) {
   const QkvOut qo{plan, q, kv, max_pos, rope};
+  hipLaunchKernelGGL((k_row_rms<D>), dim3((M + 3) / 4), dim3(256), 0, s, x, (long)D, M, eps, rscale);
   hipLaunchKernelGGL((k_dense_mfma<D, DM_QKV>), dim3(3 * NH, (M + MF_ROWS - 1) / MF_ROWS), dim3(256), 0, s, x,
-                     (long)D, gain, eps, wqkv, nullptr, M, nullptr, 0L, qo);
+                     (long)D, gain, rscale, wqkv, nullptr, M, nullptr, 0L, qo);
 }
 
 // LM head rows for the matrix cores: xn[m] = RMSNorm(x[src(m)]) * gain, one

@@ -152,11 +152,13 @@ void launch_expert_down_mfma(hipStream_t s, const bf16* wd, int M, const MoeBufs
 // Dense layers on the matrix cores (bf16 weights): the outputs of launch_gemv
 // (K, epi) in {(1280, add / store / SwiGLU), (2560, store), (3584, add)}, N a
 // multiple of 64, and of launch_qkv_rope, with the inputs as bf16 hi + lo parts.
-// The gemv launchers return false, launching nothing, for any other (K, epi).
+// The gemv launchers return false, launching nothing, for any other (K, epi)
+// (a gain only with K = 1280).  rscale: scratch of M floats (the rows' RMSNorm
+// scales, computed by a launch of their own when a gain is given).
 bool launch_gemv_mfma(hipStream_t s, int K, Epi epi, const float* a, long lda, const float* gain, float eps,
-                      const bf16* W0, const bf16* W1, int N, int M, float* out, long ldo);
+                      const bf16* W0, const bf16* W1, int N, int M, float* out, long ldo, float* rscale);
 void launch_qkv_rope_mfma(hipStream_t s, const float* x, const float* gain, float eps, const bf16* wqkv, int M,
-                          RowPlan plan, float* q, bf16* kv, int max_pos, const float2* rope);
+                          RowPlan plan, float* q, bf16* kv, int max_pos, const float2* rope, float* rscale);
 // The same with k split over the four wavefronts of 16-row blocks (decode-sized
 // calls: many blocks, no LDS staging).
 bool launch_gemv_ks(hipStream_t s, int K, Epi epi, const float* a, long lda, const float* gain, float eps,

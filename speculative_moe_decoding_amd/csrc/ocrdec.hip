@@ -36,7 +36,7 @@ struct Plan {
   // state
   size_t s_kv, s_dkv, s_ints, s_cu, s_hbuf, s_rope, s_total;
   // workspace
-  size_t w_x, w_q, w_attn, w_part, w_bnorm, w_ridx, w_rgate, w_perm, w_inv, w_off, w_act, w_slot, w_items, w_rlogit, w_misc, w_stats, w_sync, w_acnt, w_hx,
+  size_t w_x, w_rscale, w_q, w_attn, w_part, w_bnorm, w_ridx, w_rgate, w_perm, w_inv, w_off, w_act, w_slot, w_items, w_rlogit, w_misc, w_stats, w_sync, w_acnt, w_hx,
       w_y, w_cat, w_u, w_u2, w_dffn, w_esave, w_hsave, w_lmv, w_lmi, w_plan, w_total;
 };
 
@@ -97,6 +97,7 @@ Plan make_plan(const ocrdec_config* c, bool decode_only = false) {
   o = 0;
   const size_t M = p.M_max;
   p.w_x = take(M * D * 4);
+  p.w_rscale = take(M * 4);
   p.w_q = take(M * QD * 4);
   p.w_attn = take(M * QD * 4);
   // split-KV partials of the decode calls (prefill passes use the prefill attention)
@@ -134,7 +135,7 @@ Plan make_plan(const ocrdec_config* c, bool decode_only = false) {
 // The per-call scratch buffers of the decode calls, laid out by a Plan inside
 // one region (the caller's workspace, or the library's no-allocation scratch).
 struct WsPtrs {
-  float *x, *q, *attn, *part, *cat, *u, *u2, *dffn, *esave, *hsave[2], *lm_val;
+  float *x, *rscale, *q, *attn, *part, *cat, *u, *u2, *dffn, *esave, *hsave[2], *lm_val;
   int *lm_idx, *plan_base, *plan_cnt, *plan_slot, *tok_tmp;
   unsigned* sync;   // the persistent MoE launch's counters (zero between launches)
   unsigned* acnt;   // attention chunk counters per (sequence, head) (zero between launches)
@@ -179,6 +180,7 @@ WsPtrs bind_workspace(char* ws, const Plan& p, int max_batch) {
   auto wf = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
   auto wi = [&](size_t off) { return reinterpret_cast<int*>(ws + off); };
   b.x = wf(p.w_x);
+  b.rscale = wf(p.w_rscale);
   b.q = wf(p.w_q);
   b.attn = wf(p.w_attn);
   b.part = wf(p.w_part);
@@ -369,7 +371,7 @@ void dense_gemv(ocrdec_model* m, hipStream_t s, int dp, int K, Epi epi, const fl
                 const float* gain, const T* W0, const T* W1, int N, int M, float* out, long ldo) {
   if constexpr (std::is_same<T, bf16>::value) {
     if (dp == DENSE_STRIP) {
-      if (!launch_gemv_mfma(s, K, epi, a, lda, gain, m->cfg.norm_eps, W0, W1, N, M, out, ldo))
+      if (!launch_gemv_mfma(s, K, epi, a, lda, gain, m->cfg.norm_eps, W0, W1, N, M, out, ldo, m->b.rscale))
         m->launch_fail = "matrix-core dense layer: no kernel for this (K, epilogue)";
       return;
     }
@@ -387,7 +389,8 @@ void dense_qkv(ocrdec_model* m, hipStream_t s, int dp, const float* x, const flo
                RowPlan plan, T* kv) {
   if constexpr (std::is_same<T, bf16>::value) {
     if (dp == DENSE_STRIP) {
-      launch_qkv_rope_mfma(s, x, gain, m->cfg.norm_eps, W, M, plan, m->b.q, kv, m->cfg.max_positions, m->rope);
+      launch_qkv_rope_mfma(s, x, gain, m->cfg.norm_eps, W, M, plan, m->b.q, kv, m->cfg.max_positions, m->rope,
+                           m->b.rscale);
       return;
     }
     if (dp == DENSE_KSPLIT) {
