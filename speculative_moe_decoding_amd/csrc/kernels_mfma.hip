@@ -116,10 +116,6 @@ __device__ __forceinline__ void mf_store_a(MfChunkT<CT> (&ch)[NP], float4 (&ar)[
   }
 }
 
-// Per k-step: the hi part against every (tile, matrix, strip) accumulator,
-// then the lo part, so that consecutive MFMAs into one accumulator are
-// NT * NB * NS instructions apart (the same sums, in the same order, per
-// accumulator).
 template <int NT, int NB, int NS, int NP, int CT>
 __device__ __forceinline__ void mf_compute(const MfChunkT<CT> (&ch)[NP], const uint4 (&bq)[NB][NS][MF_SC],
                                            f32x4_v (&acc)[NT][NB][NS]) {
@@ -127,9 +123,9 @@ __device__ __forceinline__ void mf_compute(const MfChunkT<CT> (&ch)[NP], const u
 #pragma unroll
   for (int s = 0; s < MF_SC; ++s) {
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
+    for (int i = 0; i < NT; ++i) {
 #pragma unroll
-      for (int i = 0; i < NT; ++i) {
+      for (int p = 0; p < NP; ++p) {
         const uint4 a = ch[p].f[i][s][mf_slot(s, lane)];
 #pragma unroll
         for (int b = 0; b < NB; ++b)
@@ -146,7 +142,8 @@ __device__ __forceinline__ void mf_compute(const MfChunkT<CT> (&ch)[NP], const u
 // W_b[16 n + lane % 16][k], with A in NP bf16 parts.  With a gain g, row r of
 // A is RMSNorm'ed first: (a * rs[r]) * g (rs in LDS, one scale per pass row).
 // All 256 threads must call it; contains barriers.
-template <int K, int NT, int NB, int NS, int NP, typename RowPtr, bool NORM = false, int CT = MF_MT>
+template <int K, int NT, int NB, int NS, int NP, typename RowPtr, bool NORM = false, int CT = MF_MT,
+          bool DEEP = false>
 __device__ __forceinline__ void mfma_pass(const bf16* const (&w)[NB], RowPtr rowp, int rows, MfChunkT<CT> (&buf)[2][NP],
                                           f32x4_v (&acc)[NT][NB][NS], const float* __restrict__ g = nullptr,
                                           const float* rs = nullptr) {
@@ -173,40 +170,73 @@ __device__ __forceinline__ void mfma_pass(const bf16* const (&w)[NB], RowPtr row
     for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int n = 0; n < NS; ++n) acc[i][b][n] = f32x4_v{0.f, 0.f, 0.f, 0.f};
-  // Weights: a ring of MF_BP chunks in registers; activations: two chunks in
-  // registers and two in LDS.  Chunk c + 2's rows are loaded before chunk c's
-  // arithmetic and chunk c + MF_BP's weights after it, so that waiting for
-  // chunk c + 1's rows (loads complete in issue order) never waits for the
-  // weights of chunks c + 2 .. c + MF_BP.  One barrier per chunk.
-  constexpr int BP = NC < MF_BP ? NC : MF_BP;
-  uint4 bq[MF_BP][NB][NS][MF_SC];
-  float4 ar[2][NT][2], gq[2][2];
-  mf_load_a(ar[0], gq[0], src, ok, gn, kg, 0);
-  if (NC > 1) mf_load_a(ar[1], gq[1], src, ok, gn, kg, 1);
+  if constexpr (DEEP) {
+    // Long passes (prefill): weights in a ring of MF_BP chunks in registers,
+    // activations two chunks in registers and two in LDS.  Chunk c + 2's rows
+    // are loaded before chunk c's arithmetic and chunk c + MF_BP's weights
+    // after it, so that waiting for chunk c + 1's rows (loads complete in
+    // issue order) never waits for the weights of chunks c + 2 .. c + MF_BP.
+    constexpr int BP = NC < MF_BP ? NC : MF_BP;
+    uint4 bq[MF_BP][NB][NS][MF_SC];
+    float4 ar[2][NT][2], gq[2][2];
+    mf_load_a(ar[0], gq[0], src, ok, gn, kg, 0);
+    if (NC > 1) mf_load_a(ar[1], gq[1], src, ok, gn, kg, 1);
 #pragma unroll
-  for (int c = 0; c < BP; ++c) mf_load_b<K, NB, NS>(bq[c], w, woff, c);
-  mf_store_a<NT, NP, NORM, CT>(buf[0], ar[0], gq[0], rsv, kg, ri);
-  __syncthreads();
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    if (c + 2 < NC) mf_load_a(ar[c & 1], gq[c & 1], src, ok, gn, kg, c + 2);
-    mf_compute<NT, NB, NS, NP, CT>(buf[c & 1], bq[c % MF_BP], acc);
-    if (c + MF_BP < NC) mf_load_b<K, NB, NS>(bq[c % MF_BP], w, woff, c + MF_BP);
-    if (c + 1 < NC) mf_store_a<NT, NP, NORM, CT>(buf[(c + 1) & 1], ar[(c + 1) & 1], gq[(c + 1) & 1], rsv, kg, ri);
+    for (int c = 0; c < BP; ++c) mf_load_b<K, NB, NS>(bq[c], w, woff, c);
+    mf_store_a<NT, NP, NORM, CT>(buf[0], ar[0], gq[0], rsv, kg, ri);
     __syncthreads();
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if (c + 2 < NC) mf_load_a(ar[c & 1], gq[c & 1], src, ok, gn, kg, c + 2);
+      mf_compute<NT, NB, NS, NP, CT>(buf[c & 1], bq[c % MF_BP], acc);
+      if (c + MF_BP < NC) mf_load_b<K, NB, NS>(bq[c % MF_BP], w, woff, c + MF_BP);
+      if (c + 1 < NC) mf_store_a<NT, NP, NORM, CT>(buf[(c + 1) & 1], ar[(c + 1) & 1], gq[(c + 1) & 1], rsv, kg, ri);
+      __syncthreads();
+    }
+  } else {
+    // Decode-sized passes: chunk c computes from LDS buffer c % 2 and
+    // registers bq(c % 2) while chunk c + 1 is loaded into the other pair
+    // (fewer registers: more workgroups in flight); one barrier per chunk.
+    float4 gq[2];
+    uint4 bq0[NB][NS][MF_SC], bq1[NB][NS][MF_SC];
+    float4 ar[NT][2];
+    mf_load_a(ar, gq, src, ok, gn, kg, 0);
+    mf_load_b<K, NB, NS>(bq0, w, woff, 0);
+    mf_store_a<NT, NP, NORM, CT>(buf[0], ar, gq, rsv, kg, ri);
+    __syncthreads();
+#pragma unroll 1
+    for (int c = 0; c < NC; c += 2) {
+      if (c + 1 < NC) {
+        mf_load_a(ar, gq, src, ok, gn, kg, c + 1);  // activations first: waiting for them does not wait for the weights
+        mf_load_b<K, NB, NS>(bq1, w, woff, c + 1);
+      }
+      mf_compute<NT, NB, NS, NP, CT>(buf[0], bq0, acc);
+      if (c + 1 < NC) mf_store_a<NT, NP, NORM, CT>(buf[1], ar, gq, rsv, kg, ri);
+      __syncthreads();
+      if (c + 1 < NC) {
+        if (c + 2 < NC) {
+          mf_load_a(ar, gq, src, ok, gn, kg, c + 2);
+          mf_load_b<K, NB, NS>(bq0, w, woff, c + 2);
+        }
+        mf_compute<NT, NB, NS, NP, CT>(buf[1], bq1, acc);
+        if (c + 2 < NC) mf_store_a<NT, NP, NORM, CT>(buf[0], ar, gq, rsv, kg, ri);
+        __syncthreads();
+      }
+    }
   }
 }
 
 // Gate/up: block (x, slot s) computes units j0 .. j0+15, j0 = 64 x + 16 w, of
 // active expert s for every pair routed to it:
 // hx[pair][j] = silu(gate_j . b) * (up_j . b), b the pair's normalised row.
-template <int NT>
+template <int NT, bool DEEP>
 __device__ __forceinline__ void gate_up_pass(const bf16* const (&w)[2], const float* __restrict__ bnorm,
                                              const int* __restrict__ perm, int kb, int rows, float* __restrict__ hx,
                                              int j0, MfChunk (&buf)[2][2]) {
   const int lane = lane_id();
   f32x4_v acc[NT][2][1];
-  mfma_pass<D, NT, 2, 1, 2>(w, [=](int r) { return bnorm + (long)(perm[kb + r] / NSLOT) * D; }, rows, buf, acc);
+  auto rowp = [=](int r) { return bnorm + (long)(perm[kb + r] / NSLOT) * D; };
+  mfma_pass<D, NT, 2, 1, 2, decltype(rowp), false, MF_MT, DEEP>(w, rowp, rows, buf, acc);
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
 #pragma unroll
@@ -217,30 +247,36 @@ __device__ __forceinline__ void gate_up_pass(const bf16* const (&w)[2], const fl
   }
 }
 
-// Block (x, y): work item y (an expert and at most 64 of its pairs, so that a
-// shared expert's rows of a long prefill spread over many blocks).
+// Block (x, y).  DEEP (prefill passes): work item y, an expert and at most 64
+// of its pairs, so that a shared expert's rows of a long prefix spread over
+// many blocks.  Decode calls: expert slot y (the shared experts' blocks load
+// their weights with no routing read) and every pass of 64 of its pairs.
+template <bool DEEP>
 __global__ __launch_bounds__(256) void k_expert_gate_up_mfma(const bf16* __restrict__ wg,
                                                              const bf16* __restrict__ wu, int M, MoeBufs mb) {
   __shared__ MfChunk buf[2][2];
-  const int4 it = mb.items[blockIdx.y];
+  const int4 it = DEEP ? mb.items[blockIdx.y] : expert_work(mb, blockIdx.y, M);
   const int e = it.x;
   if (e < 0) return;
   const int j0 = blockIdx.x * 64 + wave_id() * 16;
   const bf16* const w[2] = {wg + ((long)e * DI + j0) * D, wu + ((long)e * DI + j0) * D};
-  const int kb = it.y, rows = it.z - it.y;
-  if (rows <= 16) gate_up_pass<1>(w, mb.bnorm, mb.perm, kb, rows, mb.hx, j0, buf);
-  else if (rows <= 32) gate_up_pass<2>(w, mb.bnorm, mb.perm, kb, rows, mb.hx, j0, buf);
-  else gate_up_pass<4>(w, mb.bnorm, mb.perm, kb, rows, mb.hx, j0, buf);
+  for (int kb = it.y; kb < it.z; kb += MF_ROWS) {
+    const int rows = min(MF_ROWS, it.z - kb);
+    if (rows <= 16) gate_up_pass<1, DEEP>(w, mb.bnorm, mb.perm, kb, rows, mb.hx, j0, buf);
+    else if (rows <= 32) gate_up_pass<2, DEEP>(w, mb.bnorm, mb.perm, kb, rows, mb.hx, j0, buf);
+    else gate_up_pass<4, DEEP>(w, mb.bnorm, mb.perm, kb, rows, mb.hx, j0, buf);
+  }
 }
 
 // Down: block (x, slot s) computes outputs n0 .. n0+31, n0 = 128 x + 32 w:
 // y[pair][n] = W_d[n] . hx[pair].
-template <int NT>
+template <int NT, bool DEEP>
 __device__ __forceinline__ void down_pass(const bf16* const (&w)[1], const float* __restrict__ hx, int kb, int rows,
                                           float* __restrict__ y, int n0, MfChunk (&buf)[2][2]) {
   const int lane = lane_id();
   f32x4_v acc[NT][1][2];
-  mfma_pass<DI, NT, 1, 2, 2>(w, [=](int r) { return hx + (long)(kb + r) * DI; }, rows, buf, acc);
+  auto rowp = [=](int r) { return hx + (long)(kb + r) * DI; };
+  mfma_pass<DI, NT, 1, 2, 2, decltype(rowp), false, MF_MT, DEEP>(w, rowp, rows, buf, acc);
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
 #pragma unroll
@@ -255,25 +291,32 @@ __device__ __forceinline__ void down_pass(const bf16* const (&w)[1], const float
   }
 }
 
+template <bool DEEP>
 __global__ __launch_bounds__(256) void k_expert_down_mfma(const bf16* __restrict__ wd, int M, MoeBufs mb) {
   __shared__ MfChunk buf[2][2];
-  const int4 it = mb.items[blockIdx.y];
+  const int4 it = DEEP ? mb.items[blockIdx.y] : expert_work(mb, blockIdx.y, M);
   const int e = it.x;
   if (e < 0) return;
   const int n0 = blockIdx.x * 128 + wave_id() * 32;
   const bf16* const w[1] = {wd + ((long)e * D + n0) * DI};
-  const int kb = it.y, rows = it.z - it.y;
-  if (rows <= 16) down_pass<1>(w, mb.hx, kb, rows, mb.y, n0, buf);
-  else if (rows <= 32) down_pass<2>(w, mb.hx, kb, rows, mb.y, n0, buf);
-  else down_pass<4>(w, mb.hx, kb, rows, mb.y, n0, buf);
+  for (int kb = it.y; kb < it.z; kb += MF_ROWS) {
+    const int rows = min(MF_ROWS, it.z - kb);
+    if (rows <= 16) down_pass<1, DEEP>(w, mb.hx, kb, rows, mb.y, n0, buf);
+    else if (rows <= 32) down_pass<2, DEEP>(w, mb.hx, kb, rows, mb.y, n0, buf);
+    else down_pass<4, DEEP>(w, mb.hx, kb, rows, mb.y, n0, buf);
+  }
 }
 
-void launch_expert_gate_up_mfma(hipStream_t s, const bf16* wg, const bf16* wu, int M, const MoeBufs& mb) {
-  hipLaunchKernelGGL(k_expert_gate_up_mfma, dim3(DI / 64, expert_item_cap(M)), dim3(256), 0, s, wg, wu, M, mb);
+void launch_expert_gate_up_mfma(hipStream_t s, const bf16* wg, const bf16* wu, int M, const MoeBufs& mb, bool deep) {
+  const dim3 grid(DI / 64, deep ? expert_item_cap(M) : expert_slot_cap(M));
+  if (deep) hipLaunchKernelGGL(k_expert_gate_up_mfma<true>, grid, dim3(256), 0, s, wg, wu, M, mb);
+  else hipLaunchKernelGGL(k_expert_gate_up_mfma<false>, grid, dim3(256), 0, s, wg, wu, M, mb);
 }
 
-void launch_expert_down_mfma(hipStream_t s, const bf16* wd, int M, const MoeBufs& mb) {
-  hipLaunchKernelGGL(k_expert_down_mfma, dim3(D / 128, expert_item_cap(M)), dim3(256), 0, s, wd, M, mb);
+void launch_expert_down_mfma(hipStream_t s, const bf16* wd, int M, const MoeBufs& mb, bool deep) {
+  const dim3 grid(D / 128, deep ? expert_item_cap(M) : expert_slot_cap(M));
+  if (deep) hipLaunchKernelGGL(k_expert_down_mfma<true>, grid, dim3(256), 0, s, wd, M, mb);
+  else hipLaunchKernelGGL(k_expert_down_mfma<false>, grid, dim3(256), 0, s, wd, M, mb);
 }
 
 // ---- dense layers on the matrix cores -------------------------------------
@@ -308,8 +351,8 @@ __device__ __forceinline__ void dense_mfma_rows(const float* __restrict__ a, lon
   const int wave = wave_id(), lane = lane_id();
   auto rowp = [=](int r) { return a + (long)(m0 + r) * lda; };
   f32x4_v acc[NT][NB][1];
-  if (gain != nullptr) mfma_pass<K, NT, NB, 1, 2, decltype(rowp), true>(w, rowp, rows, buf, acc, gain, rs);
-  else mfma_pass<K, NT, NB, 1, 2, decltype(rowp), false>(w, rowp, rows, buf, acc);
+  if (gain != nullptr) mfma_pass<K, NT, NB, 1, 2, decltype(rowp), true, MF_MT, true>(w, rowp, rows, buf, acc, gain, rs);
+  else mfma_pass<K, NT, NB, 1, 2, decltype(rowp), false, MF_MT, true>(w, rowp, rows, buf, acc);
   const int j = lane & 15;
 #pragma unroll
   for (int i = 0; i < NT; ++i) {

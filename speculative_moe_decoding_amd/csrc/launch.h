@@ -147,8 +147,10 @@ void launch_moe_experts(hipStream_t s, int grid, const float* x_in, float* x_out
 
 // Matrix-core variants (bf16 weights): the same outputs as the vector
 // launchers above, with the activations rounded to bf16 for the MFMA inputs.
-void launch_expert_gate_up_mfma(hipStream_t s, const bf16* wg, const bf16* wu, int M, const MoeBufs& mb);
-void launch_expert_down_mfma(hipStream_t s, const bf16* wd, int M, const MoeBufs& mb);
+// deep: prefill passes (weights three chunks ahead, activations two; more
+// registers), else decode calls (one chunk ahead, more workgroups in flight).
+void launch_expert_gate_up_mfma(hipStream_t s, const bf16* wg, const bf16* wu, int M, const MoeBufs& mb, bool deep);
+void launch_expert_down_mfma(hipStream_t s, const bf16* wd, int M, const MoeBufs& mb, bool deep);
 // Dense layers on the matrix cores (bf16 weights): the outputs of launch_gemv
 // (K, epi) in {(1280, add / store / SwiGLU), (2560, store), (3584, add)}, N a
 // multiple of 64, and of launch_qkv_rope, with the inputs as bf16 hi + lo parts.

@@ -328,10 +328,10 @@ PassPath prefill_path(const ocrdec_model* m) {
 }
 
 template <typename T>
-void expert_gate_up(ocrdec_model* m, hipStream_t s, int l, int M, bool mx) {
+void expert_gate_up(ocrdec_model* m, hipStream_t s, int l, int M, bool mx, bool deep = false) {
   if constexpr (std::is_same<T, bf16>::value) {
     if (mx) {
-      launch_expert_gate_up_mfma(s, wmat<T>(m, lw(m, l, L_GATE)), wmat<T>(m, lw(m, l, L_UP)), M, m->b.mb);
+      launch_expert_gate_up_mfma(s, wmat<T>(m, lw(m, l, L_GATE)), wmat<T>(m, lw(m, l, L_UP)), M, m->b.mb, deep);
       return;
     }
   }
@@ -339,10 +339,10 @@ void expert_gate_up(ocrdec_model* m, hipStream_t s, int l, int M, bool mx) {
 }
 
 template <typename T>
-void expert_down(ocrdec_model* m, hipStream_t s, int l, int M, bool mx) {
+void expert_down(ocrdec_model* m, hipStream_t s, int l, int M, bool mx, bool deep = false) {
   if constexpr (std::is_same<T, bf16>::value) {
     if (mx) {
-      launch_expert_down_mfma(s, wmat<T>(m, lw(m, l, L_DOWN)), M, m->b.mb);
+      launch_expert_down_mfma(s, wmat<T>(m, lw(m, l, L_DOWN)), M, m->b.mb, deep);
       return;
     }
   }
@@ -453,14 +453,14 @@ void verifier_layers(ocrdec_model* m, hipStream_t s, PassPath pp, int M, int B, 
     launch_router<T>(s, m->b.x, wvec(m, lw(m, l, L_FNORM)), c.norm_eps, wmat<T>(m, lw(m, l, L_ROUTER)), M, m->b.mb,
                      tap, rlog ? rlog + (size_t)l * M * NE : nullptr, m->b.sync + ROUTE_CNT_WORD);
     timing_mark(m, s);
-    expert_gate_up<T>(m, s, l, M, pp.experts);
+    expert_gate_up<T>(m, s, l, M, pp.experts, pp.prefill);
     timing_mark(m, s);
     if (!pp.experts && M <= MRG) {  // the combine inside the down launch
       launch_expert_down_combine<T>(s, wmat<T>(m, lw(m, l, L_DOWN)), M, m->b.mb, m->b.x, m->b.sync);
       timing_mark(m, s);
       continue;
     }
-    expert_down<T>(m, s, l, M, pp.experts);
+    expert_down<T>(m, s, l, M, pp.experts, pp.prefill);
     timing_mark(m, s);
     launch_moe_combine(s, m->b.x, M, m->b.mb);
   }
