@@ -171,74 +171,10 @@ __device__ __forceinline__ float merge_loop(const float* __restrict__ pp, long c
   return O / L;
 }
 
-// The merge of the combine kernel below for the rows of one (sequence b, head
-// h), by the block that finished its last chunk: every block of the (b, h)
-// counts itself in acnt[b NH + h] once its partials are stored; the one that
-// brings the count to n_chunks merges chunks 0 .. p / C of each row i < Q in
-// order (max of the m, then L and O with weights exp(m_c - max), O / L; rows
-// outside the plan: zero) and resets the counter.  All threads call it.
-template <bool FUSE>
-__device__ __forceinline__ void attn_merge_last(const float* __restrict__ part, const RowPlan& plan, int n_chunks,
-                                                int C, int max_pos, int b, int h, float* __restrict__ out,
-                                                unsigned* __restrict__ acnt) {
-  __shared__ int s_last;
-  stores_done();
-  __syncthreads();
-  if (threadIdx.x == 0) s_last = atomic_add_agent(acnt + b * NH + h, 1u) + 1 == (unsigned)n_chunks;
-  __syncthreads();
-  if (!s_last) return;
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  const int Q = plan.Q, d = threadIdx.x & 127;
-  const long cstride = (long)Q * (HD + 2);
-  const int base = plan.base[b], pcnt = plan.cnt[b];
-  for (int i = threadIdx.x >> 7; i < Q; i += 2) {
-    const int p = base + i;
-    const bool ok = i < pcnt && p >= 0 && p < max_pos;
-    const int nc = ok ? min(p / C + 1, n_chunks) : 1;
-    const float* pp = part + (((long)b * NH + h) * n_chunks) * cstride + (long)i * (HD + 2);
-    constexpr int G = 8;
-    float mg = -INFINITY;
-    for (int c0 = 0; c0 < nc; c0 += G) {
-      float mv[G];
-#pragma unroll
-      for (int j = 0; j < G; ++j) mv[j] = ld_agent(pp + min(c0 + j, nc - 1) * cstride + HD);
-#pragma unroll
-      for (int j = 0; j < G; ++j) mg = fmaxf(mg, mv[j]);
-    }
-    float L = 0.f, O = 0.f;
-    for (int c0 = 0; c0 < nc; c0 += G) {
-      float mv[G], lv[G], ov[G];
-#pragma unroll
-      for (int j = 0; j < G; ++j) {
-        const float* qp = pp + min(c0 + j, nc - 1) * cstride;
-        mv[j] = ld_agent(qp + HD);
-        lv[j] = ld_agent(qp + HD + 1);
-        ov[j] = ld_agent(qp + d);
-      }
-#pragma unroll
-      for (int j = 0; j < G; ++j) {
-        if (c0 + j < nc) {
-          const float w = expf(mv[j] - mg);
-          L = fmaf(lv[j], w, L);
-          O = fmaf(ov[j], w, O);
-        }
-      }
-    }
-    out[(long)(b * Q + i) * QD + h * HD + d] = ok ? O / L : 0.f;
-  }
-  if (threadIdx.x == 0) st_agent_u(acnt + b * NH + h, 0u);
-}
-
-// FUSE: the block that finishes the last chunk of its (sequence, head) merges
-// the chunks itself (the combine kernel's arithmetic and order, so the same
-// bits) into out: partials go out with agent-scope stores, one agent-scope
-// counter per (sequence, head) counts the chunk blocks done, and its last user
-// sets it back to zero.
-template <typename T, bool FUSE>
+template <typename T>
 __global__ __launch_bounds__(256) void k_attn_partial(const float* __restrict__ q, const T* __restrict__ kv,
                                                       int max_pos, RowPlan plan, int n_chunks,
-                                                      int tiles_per_chunk, float* __restrict__ part,
-                                                      float* __restrict__ out, unsigned* __restrict__ acnt) {
+                                                      int tiles_per_chunk, float* __restrict__ part) {
   typedef AttTile<T> AT;
   // keys transposed in groups of 4 dims: Kq[d/4][t] = (k_t[d..d+3]); values row-major
   __shared__ typename AT::K4 Kq[HD / 4][KQ_STRIDE];
@@ -305,10 +241,7 @@ __global__ __launch_bounds__(256) void k_attn_partial(const float* __restrict__ 
     const int e = tid + 256 * j, i = e / (HD / 4);
     qs[i][e % (HD / 4)] = (i < cnt) ? qv[j] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  if (cnt <= 0 || k0 > p_last) {
-    if constexpr (FUSE) attn_merge_last<FUSE>(part, plan, n_chunks, C, max_pos, b, h, out, acnt);
-    return;
-  }
+  if (cnt <= 0 || k0 > p_last) return;
   const int n_tiles = min(tiles_per_chunk, (p_last - k0) / ATT_TILE + 1);
   float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
   float o0[2] = {0.f, 0.f}, o1[2] = {0.f, 0.f};
@@ -334,16 +267,9 @@ __global__ __launch_bounds__(256) void k_attn_partial(const float* __restrict__ 
     const int i = wave + 4 * qq;
     if (i >= cnt || k0 > base + i) continue;
     float* pp = part + ((((long)b * NH + h) * n_chunks + c) * Q + i) * (HD + 2);
-    if constexpr (FUSE) {
-      st_agent(pp + 2 * lane, o0[qq]);
-      st_agent(pp + 2 * lane + 1, o1[qq]);
-      if (lane == 0) { st_agent(pp + HD, mrun[qq]); st_agent(pp + HD + 1, lrun[qq]); }
-    } else {
-      reinterpret_cast<float2*>(pp)[lane] = make_float2(o0[qq], o1[qq]);
-      if (lane == 0) { pp[HD] = mrun[qq]; pp[HD + 1] = lrun[qq]; }
-    }
+    reinterpret_cast<float2*>(pp)[lane] = make_float2(o0[qq], o1[qq]);
+    if (lane == 0) { pp[HD] = mrun[qq]; pp[HD + 1] = lrun[qq]; }
   }
-  if constexpr (FUSE) attn_merge_last<FUSE>(part, plan, n_chunks, C, max_pos, b, h, out, acnt);
 }
 
 // Merge chunks 0..p/C of each (row, head) in order.  Block = 2 heads x 128 dims.
@@ -383,14 +309,9 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
 
 template <typename T>
 void launch_attention(hipStream_t s, const float* q, const T* kv, int max_pos, RowPlan plan, int B, int n_chunks,
-                      int tiles_per_chunk, float* part, float* out, unsigned* acnt) {
-  if (acnt != nullptr && n_chunks <= ATT_FUSE_CHUNKS) {
-    hipLaunchKernelGGL((k_attn_partial<T, true>), dim3(n_chunks, NH, B), dim3(256), 0, s, q, kv, max_pos, plan,
-                       n_chunks, tiles_per_chunk, part, out, acnt);
-    return;
-  }
-  hipLaunchKernelGGL((k_attn_partial<T, false>), dim3(n_chunks, NH, B), dim3(256), 0, s, q, kv, max_pos, plan,
-                     n_chunks, tiles_per_chunk, part, nullptr, nullptr);
+                      int tiles_per_chunk, float* part, float* out) {
+  hipLaunchKernelGGL((k_attn_partial<T>), dim3(n_chunks, NH, B), dim3(256), 0, s, q, kv, max_pos, plan, n_chunks,
+                     tiles_per_chunk, part);
   hipLaunchKernelGGL(k_attn_combine, dim3(B * plan.Q, NH / 2), dim3(256), 0, s, part, plan, n_chunks,
                      tiles_per_chunk * ATT_TILE, max_pos, out);
 }
@@ -631,8 +552,8 @@ void launch_attention_prefill<float>(hipStream_t s, const float* q, const float*
 }
 
 template void launch_attention<float>(hipStream_t, const float*, const float*, int, RowPlan, int, int, int, float*,
-                                      float*, unsigned*);
+                                      float*);
 template void launch_attention<bf16>(hipStream_t, const float*, const bf16*, int, RowPlan, int, int, int, float*,
-                                     float*, unsigned*);
+                                     float*);
 
 }  // namespace ocr

@@ -36,14 +36,11 @@ int lmhead_blocks(int V);
 void launch_argmax_final(hipStream_t s, const float* part_val, const int* part_idx, int nblk, int M, int* tok,
                          int tok_stride);
 
-// Split-KV decode attention and the merge of its chunks into out.  With acnt
-// (B x NH zero counters, left at zero) and at most ATT_FUSE_CHUNKS chunks, the
-// last chunk block of each (sequence, head) merges them in the same launch;
-// otherwise a second launch does.  The same bits either way.
-constexpr int ATT_FUSE_CHUNKS = 32;
+// Split-KV decode attention (partials per chunk) and the merge of the chunks
+// into out, in two launches.
 template <typename T>
 void launch_attention(hipStream_t s, const float* q, const T* kv, int max_pos, RowPlan plan, int B,
-                      int n_chunks, int tiles_per_chunk, float* part, float* out, unsigned* acnt);
+                      int n_chunks, int tiles_per_chunk, float* part, float* out);
 
 // Prefill attention: n entries of plan.Q = PREFILL_CHUNK rows; row i of entry
 // b (i < cnt[b]) is the query at position base[b] + i of slot slot[b] and sees

@@ -36,7 +36,7 @@ struct Plan {
   // state
   size_t s_kv, s_dkv, s_ints, s_cu, s_hbuf, s_rope, s_total;
   // workspace
-  size_t w_x, w_rscale, w_q, w_attn, w_part, w_bnorm, w_ridx, w_rgate, w_perm, w_inv, w_off, w_act, w_slot, w_items, w_rlogit, w_misc, w_stats, w_sync, w_acnt, w_hx,
+  size_t w_x, w_rscale, w_q, w_attn, w_part, w_bnorm, w_ridx, w_rgate, w_perm, w_inv, w_off, w_act, w_slot, w_items, w_rlogit, w_misc, w_stats, w_sync, w_hx,
       w_y, w_cat, w_u, w_u2, w_dffn, w_esave, w_hsave, w_lmv, w_lmi, w_plan, w_total;
 };
 
@@ -116,7 +116,6 @@ Plan make_plan(const ocrdec_config* c, bool decode_only = false) {
   p.w_stats = take(8 * 8);
   static_assert(ROUTE_CNT_WORD < MOE_SYNC_WORDS, "the down-combine and routing counters share the MoE sync words");
   p.w_sync = take((size_t)MOE_SYNC_WORDS * 4);
-  p.w_acnt = take((size_t)p.plan_n * NH * 4);
   p.w_hx = take(M * NSLOT * DI * 4);
   p.w_y = take(M * NSLOT * D * 4);
   p.w_cat = take(M * 2 * D * 4);
@@ -138,7 +137,6 @@ struct WsPtrs {
   float *x, *rscale, *q, *attn, *part, *cat, *u, *u2, *dffn, *esave, *hsave[2], *lm_val;
   int *lm_idx, *plan_base, *plan_cnt, *plan_slot, *tok_tmp;
   unsigned* sync;   // the persistent MoE launch's counters (zero between launches)
-  unsigned* acnt;   // attention chunk counters per (sequence, head) (zero between launches)
   MoeBufs mb;
 };
 
@@ -211,7 +209,6 @@ WsPtrs bind_workspace(char* ws, const Plan& p, int max_batch) {
   b.mb.rlogit = wf(p.w_rlogit);
   b.mb.stats = reinterpret_cast<long long*>(ws + p.w_stats);
   b.sync = reinterpret_cast<unsigned*>(ws + p.w_sync);
-  b.acnt = reinterpret_cast<unsigned*>(ws + p.w_acnt);
   b.mb.hx = wf(p.w_hx);
   b.mb.y = wf(p.w_y);
   return b;
@@ -419,8 +416,7 @@ void attention(ocrdec_model* m, hipStream_t s, PassPath pp, const float* q, cons
     launch_attention_prefill<T>(s, q, kv, m->cfg.max_positions, plan, B, m->b.attn);
     return;
   }
-  launch_attention<T>(s, q, kv, m->cfg.max_positions, plan, B, nch, m->p.tiles_per_chunk, m->b.part, m->b.attn,
-                      m->b.acnt);
+  launch_attention<T>(s, q, kv, m->cfg.max_positions, plan, B, nch, m->p.tiles_per_chunk, m->b.part, m->b.attn);
 }
 
 template <typename T>
@@ -714,7 +710,6 @@ int ocrdec_create(const ocrdec_config* cfg, const void* const* weight_ptrs, int 
   hipError_t err = hipMemsetAsync(misc, 0, 64 * 4, s);
   if (err == hipSuccess) err = hipMemsetAsync(m->b.mb.stats, 0, 64, s);
   if (err == hipSuccess) err = hipMemsetAsync(m->b.sync, 0, (size_t)MOE_SYNC_WORDS * 4, s);
-  if (err == hipSuccess) err = hipMemsetAsync(m->b.acnt, 0, (size_t)p.plan_n * NH * 4, s);
   if (err == hipSuccess) err = hipMemsetAsync(m->state + p.s_ints, 0, p.s_hbuf - p.s_ints, s);
   if (err == hipSuccess) {
     launch_rope_table(s, cfg->max_positions, cfg->rope_theta, reinterpret_cast<float2*>(m->state + p.s_rope));
@@ -961,8 +956,7 @@ int ocrdec_decode_steps_noalloc(ocrdec_model* m, void* stream, int B, const int3
   } swap{m, m->b};
   m->b = bind_workspace(m->scratch, dp, B);
   launch_fill_i32(s, reinterpret_cast<int*>(m->b.mb.stats), 2, 0);  // the expert counter starts at zero
-  launch_fill_i32(s, reinterpret_cast<int*>(m->b.sync), MOE_SYNC_WORDS, 0);  // and the MoE launch's counters
-  launch_fill_i32(s, reinterpret_cast<int*>(m->b.acnt), (long)dp.plan_n * NH, 0);  // and the attention's
+  launch_fill_i32(s, reinterpret_cast<int*>(m->b.sync), MOE_SYNC_WORDS, 0);  // and the MoE counters
   for (int step = 0; step < n_steps; ++step) {
     if (!slots && call_bound(m, B, slots) + K + 1 > m->cfg.max_positions)
       return fail(OCRDEC_ECAPACITY, "positions would exceed max_positions");
