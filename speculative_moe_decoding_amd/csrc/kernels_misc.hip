@@ -357,17 +357,38 @@ __global__ __launch_bounds__(256) void k_draft_prefill_cat(PrefillGroup g, const
     for (int k = threadIdx.x; k < D; k += 256) hnext[(long)slot * D + k] = xfinal[row * D + k];
 }
 
+// Entry j ends its sequence's prefix in this pass.
+__device__ __forceinline__ bool prefill_ends(const PrefillGroup& g, int j) { return g.p0[j] + g.cnt[j] == g.plen[j]; }
+// Finishing entries before entry j.
+__device__ __forceinline__ int prefill_rank(const PrefillGroup& g, int j) {
+  int f = 0;
+  for (int i = 0; i < j; ++i) f += prefill_ends(g, i) ? 1 : 0;
+  return f;
+}
+
+// The last prefix row of each sequence that ends in this pass, compacted:
+// dst[f] = xfinal[row of entry j's last row], f = j's rank among the
+// finishing entries (the LM head then runs on these rows only).  Grid n.
+__global__ __launch_bounds__(256) void k_prefill_last_rows(PrefillGroup g, const float* __restrict__ xfinal,
+                                                           float* __restrict__ dst) {
+  const int j = blockIdx.x;
+  if (!prefill_ends(g, j)) return;
+  const int f = prefill_rank(g, j);
+  const float* src = xfinal + ((long)j * PREFILL_CHUNK + g.cnt[j] - 1) * D;
+  for (int k = threadIdx.x; k < D; k += 256) dst[(long)f * D + k] = src[k];
+}
+
 // Entries that end their sequence's prefix: state of the slot, and output
-// token 0 (the greedy token of the last prefix row, tok[j]) to
-// pending_out[seq].  Grid n.
+// token 0 (the greedy token of the last prefix row, tok[f], f the entry's
+// rank among the finishing entries) to pending_out[seq].  Grid n.
 __global__ __launch_bounds__(256) void k_prefill_finish(PrefillGroup g, const float* __restrict__ xfinal,
                                                         const int* __restrict__ tok, StateView sv,
                                                         int* __restrict__ pending_out) {
   const int j = blockIdx.x;
   const int P = g.plen[j];
-  if (g.p0[j] + g.cnt[j] != P) return;
+  if (!prefill_ends(g, j)) return;
   const int slot = g.slot[j];
-  const int y0 = tok[j];
+  const int y0 = tok[prefill_rank(g, j)];
   if (threadIdx.x == 0) {
     sv.kv_len[slot] = P;
     sv.draft_len[slot] = P;
@@ -615,6 +636,9 @@ void launch_draft_prefill_cat(hipStream_t s, const PrefillGroup& g, const float*
                               float* cat) {
   hipLaunchKernelGGL(k_draft_prefill_cat, dim3(PREFILL_CHUNK, g.n), dim3(256), 0, s, g, xfinal, esave, hprev, hnext,
                      g_h, g_e, eps, cat);
+}
+void launch_prefill_last_rows(hipStream_t s, const PrefillGroup& g, const float* xfinal, float* dst) {
+  hipLaunchKernelGGL(k_prefill_last_rows, dim3(g.n), dim3(256), 0, s, g, xfinal, dst);
 }
 void launch_prefill_finish(hipStream_t s, const PrefillGroup& g, const float* xfinal, const int* tok, StateView sv,
                            int* pending_out) {

@@ -264,10 +264,9 @@ __global__ __launch_bounds__(256) void k_topk_rows(const float* __restrict__ rlo
 // ... then a stable counting sort of the 8M pairs by expert in one 1024-thread
 // block.  Wavefront w owns rows [w M / 16, (w + 1) M / 16), i.e. a contiguous
 // pair range, read in segments of 64 pairs (lane = pair; all segments' loads
-// issued together).  Ballots over a segment's distinct experts give each pair
-// its rank among the range's earlier pairs of the same expert (the range's
-// running count of expert e sits in lane e, or lane e - 64 for the shared
-// experts).  The per-range counts give per-expert offsets (experts in id
+// issued together).  Seven ballots over a segment's expert-id bits give each
+// pair its rank among the range's earlier pairs of the same expert (the
+// range's running counts in LDS).  The per-range counts give per-expert offsets (experts in id
 // order) and per-range bases; pair p lands at off[e] + base[w][e] + rank --
 // the permutation of any stable sort by expert id.
 constexpr int RL_WAVES = 16;
@@ -286,32 +285,34 @@ __global__ __launch_bounds__(1024) void k_sort_pairs(int M, MoeBufs mb) {
     seg_e[sg] = (p < p_hi) ? mb.ridx[p] : -1;
     seg_rank[sg] = 0;
   }
-  int c_lo = 0, c_hi = 0;
+  // running count of each expert in this range (LDS, one row per wavefront):
+  // a segment's equal experts are found from seven ballots over the id bits;
+  // a pair's rank = the expert's count before the segment + the equal lanes
+  // below it; the lowest of them then adds the segment's count
+  int* cnt = wcnt[wave];
+  for (int x = lane; x <= NX; x += 64) cnt[x] = 0;
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
 #pragma unroll
   for (int sg = 0; sg < RL_SEGS; ++sg) {
     if (p_lo + 64 * sg >= p_hi) break;
     const int e = seg_e[sg];
     const bool valid = e >= 0;
-    uint64_t todo = __ballot(valid);
-    int rank = 0;
-    while (todo) {
-      const int leader = __builtin_ctzll(todo);
-      const int el = __builtin_amdgcn_readlane(e, leader);
-      const uint64_t same = __ballot(e == el);
-      const int n = __popcll(same);
-      const int before = (el < NE) ? __builtin_amdgcn_readlane(c_lo, el) : __builtin_amdgcn_readlane(c_hi, el - NE);
-      if (e == el) rank = before + __popcll(same & lt);
-      if (el < NE) {
-        if (lane == el) c_lo += n;
-      } else if (lane == el - NE) {
-        c_hi += n;
-      }
-      todo &= ~same;
+    uint64_t same = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < 7; ++bit) {
+      const uint64_t set = __ballot(valid && ((e >> bit) & 1));
+      same &= (valid && ((e >> bit) & 1)) ? set : ~set;
     }
-    seg_rank[sg] = rank;
+    const int below = __popcll(same & lt);
+    const int before = valid ? cnt[e] : 0;
+    seg_rank[sg] = before + below;
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+    if (valid && below == 0) cnt[e] = before + __popcll(same);
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
   }
-  wcnt[wave][lane] = c_lo;
-  if (lane < NSH) wcnt[wave][NE + lane] = c_hi;
   __syncthreads();
   // per-expert totals -> offsets; per-range exclusive bases
   if (tid < NX) {

@@ -232,7 +232,10 @@ void launch_plan_prefill(hipStream_t s, const PrefillGroup& g, const float* visi
 void launch_draft_prefill_cat(hipStream_t s, const PrefillGroup& g, const float* xfinal, const float* esave,
                               const float* hprev, float* hnext, const float* g_h, const float* g_e, float eps,
                               float* cat);
-// tok: [n] greedy tokens of the group's last valid rows; pending_out: [B] of the call.
+// dst[f] = the last prefix row of the f-th entry (in entry order) that ends its
+// sequence in this pass.
+void launch_prefill_last_rows(hipStream_t s, const PrefillGroup& g, const float* xfinal, float* dst);
+// tok: greedy tokens of those rows, by the same rank; pending_out: [B] of the call.
 void launch_prefill_finish(hipStream_t s, const PrefillGroup& g, const float* xfinal, const int* tok, StateView sv,
                            int* pending_out);
 void launch_set_sequence(hipStream_t s, int slot, int P, int tok, StateView sv);

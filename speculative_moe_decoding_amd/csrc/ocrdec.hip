@@ -500,7 +500,7 @@ int do_prefill(ocrdec_model* m, hipStream_t s, int B, const int32_t* slots_host,
     float* hnext = m->b.hsave[(t + 1) & 1];
     PrefillGroup g{};
     g.n = (int)std::min(ent.size() - e0, (size_t)m->p.prefill_group);
-    bool finish = false;
+    int n_finish = 0;
     int max_pos = 0;
     for (int j = 0; j < g.n; ++j) {
       const int b = ent[e0 + j].first, p0 = ent[e0 + j].second;
@@ -511,7 +511,7 @@ int do_prefill(ocrdec_model* m, hipStream_t s, int B, const int32_t* slots_host,
       g.cnt[j] = std::min(PREFILL_CHUNK, P - p0);
       g.nvis[j] = nv_host[b];
       g.plen[j] = P;
-      finish = finish || (p0 + g.cnt[j] == P);
+      n_finish += (p0 + g.cnt[j] == P) ? 1 : 0;
       max_pos = std::max(max_pos, p0 + g.cnt[j] - 1);
     }
     launch_plan_prefill<T>(s, g, vision, nv_stride, prompt, np_stride, wmat<T>(m, W_EMBED), c.vocab, m->b.plan_base,
@@ -520,11 +520,14 @@ int do_prefill(ocrdec_model* m, hipStream_t s, int B, const int32_t* slots_host,
     RowPlan plan{m->b.plan_base, m->b.plan_cnt, m->b.plan_slot, PREFILL_CHUNK, 0};
     const int nch = chunks_for(m, std::min(c.max_positions - 1, max_pos));
     verifier_layers<T>(m, s, prefill_path<T>(m), M, g.n, plan, nch, false, nullptr);
-    if (finish) lm_head<T>(m, s, m->b.x, PREFILL_CHUNK, true, wvec(m, W_FNORM), g.n, nullptr, m->b.tok_tmp, 1);
+    if (n_finish > 0) {  // the LM head on each finishing sequence's last row only
+      launch_prefill_last_rows(s, g, m->b.x, m->b.u);
+      lm_head<T>(m, s, m->b.u, 1, false, wvec(m, W_FNORM), n_finish, nullptr, m->b.tok_tmp, 1);
+    }
     launch_draft_prefill_cat(s, g, m->b.x, m->b.esave, hprev, hnext, wvec(m, dw(m, D_NH)), wvec(m, dw(m, D_NE)),
                              c.norm_eps, m->b.cat);
     draft_layer<T>(m, s, prefill_path<T>(m), M, g.n, plan, nch, m->b.u, false);
-    if (finish) launch_prefill_finish(s, g, m->b.x, m->b.tok_tmp, m->sv, pending_out);
+    if (n_finish > 0) launch_prefill_finish(s, g, m->b.x, m->b.tok_tmp, m->sv, pending_out);
   }
   for (int b = 0; b < B; ++b) m->slot_bound[slots_host ? slots_host[b] : b] = nv_host[b] + np_host[b];
   m->lv_B = 0;
