@@ -49,14 +49,20 @@ typedef MfChunkT<MF_MT> MfChunk;
 // Passes use NT (1, 2 or 4) tiles, the fewest that hold their rows; rows of a
 // tile past the pass's row count are zero.
 
-template <int K, int NB, int NS>
+// Weight fragments of chunk c: non-temporal loads for decode-sized passes
+// (read once per launch), ordinary ones in prefill passes (CACHED), whose
+// workgroups read their strip once per 64 rows of a work item.
+template <int K, int NB, int NS, bool CACHED = false>
 __device__ __forceinline__ void mf_load_b(uint4 (&bq)[NB][NS][MF_SC], const bf16* const (&w)[NB], long woff, int c) {
 #pragma unroll
   for (int s = 0; s < MF_SC; ++s)
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int n = 0; n < NS; ++n) bq[b][n][s] = ldg16_stream(w[b] + (long)n * 16 * K + woff + c * MF_KC + 32 * s);
+      for (int n = 0; n < NS; ++n) {
+        const bf16* p = w[b] + (long)n * 16 * K + woff + c * MF_KC + 32 * s;
+        bq[b][n][s] = CACHED ? ldg16(p) : ldg16_stream(p);
+      }
 }
 
 // Thread tid stages the 8-element group kg = tid % 16 of row tid / 16 + 16 i
@@ -182,14 +188,14 @@ __device__ __forceinline__ void mfma_pass(const bf16* const (&w)[NB], RowPtr row
     mf_load_a(ar[0], gq[0], src, ok, gn, kg, 0);
     if (NC > 1) mf_load_a(ar[1], gq[1], src, ok, gn, kg, 1);
 #pragma unroll
-    for (int c = 0; c < BP; ++c) mf_load_b<K, NB, NS>(bq[c], w, woff, c);
+    for (int c = 0; c < BP; ++c) mf_load_b<K, NB, NS, true>(bq[c], w, woff, c);
     mf_store_a<NT, NP, NORM, CT>(buf[0], ar[0], gq[0], rsv, kg, ri);
     __syncthreads();
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       if (c + 2 < NC) mf_load_a(ar[c & 1], gq[c & 1], src, ok, gn, kg, c + 2);
       mf_compute<NT, NB, NS, NP, CT>(buf[c & 1], bq[c % MF_BP], acc);
-      if (c + MF_BP < NC) mf_load_b<K, NB, NS>(bq[c % MF_BP], w, woff, c + MF_BP);
+      if (c + MF_BP < NC) mf_load_b<K, NB, NS, true>(bq[c % MF_BP], w, woff, c + MF_BP);
       if (c + 1 < NC) mf_store_a<NT, NP, NORM, CT>(buf[(c + 1) & 1], ar[(c + 1) & 1], gq[(c + 1) & 1], rsv, kg, ri);
       __syncthreads();
     }
@@ -247,10 +253,11 @@ __device__ __forceinline__ void gate_up_pass(const bf16* const (&w)[2], const fl
   }
 }
 
-// Block (x, y).  DEEP (prefill passes): work item y, an expert and at most 64
-// of its pairs, so that a shared expert's rows of a long prefix spread over
-// many blocks.  Decode calls: expert slot y (the shared experts' blocks load
-// their weights with no routing read) and every pass of 64 of its pairs.
+// Block (x, y).  DEEP (prefill passes): work item y, an expert and at most
+// ITEM_PAIRS of its pairs, so that a shared expert's rows of a long prefix
+// spread over several blocks.  Decode calls: expert slot y (the shared
+// experts' blocks load their weights with no routing read).  Either way,
+// passes of 64 pairs.
 template <bool DEEP>
 __global__ __launch_bounds__(256) void k_expert_gate_up_mfma(const bf16* __restrict__ wg,
                                                              const bf16* __restrict__ wu, int M, MoeBufs mb) {

@@ -334,10 +334,10 @@ __global__ __launch_bounds__(1024) void k_sort_pairs(int M, MoeBufs mb) {
       if (c > 0) act[na++] = e;  // na <= e: entries not yet read are never overwritten
     }
     off[NX] = acc;
-    int it = 0;  // first work item of each active expert (64 pairs per item)
+    int it = 0;  // first work item of each active expert (ITEM_PAIRS pairs per item)
     for (int sl = 0; sl < na; ++sl) {
       ioff[sl] = it;
-      it += (off[act[sl] + 1] - off[act[sl]] + 63) / 64;
+      it += (off[act[sl] + 1] - off[act[sl]] + ITEM_PAIRS - 1) / ITEM_PAIRS;
     }
     ioff[na] = it;
     na_s = na;
@@ -348,8 +348,8 @@ __global__ __launch_bounds__(1024) void k_sort_pairs(int M, MoeBufs mb) {
   const int na = na_s;
   for (int sl = tid; sl < na; sl += 1024) {
     const int e = act[sl];
-    for (int i = ioff[sl], k = off[e]; i < ioff[sl + 1]; ++i, k += 64)
-      mb.items[i] = make_int4(e, k, min(k + 64, off[e + 1]), 0);
+    for (int i = ioff[sl], k = off[e]; i < ioff[sl + 1]; ++i, k += ITEM_PAIRS)
+      mb.items[i] = make_int4(e, k, min(k + ITEM_PAIRS, off[e + 1]), 0);
   }
   for (int i = ioff[na] + tid; i < expert_item_cap(M); i += 1024) mb.items[i] = make_int4(-1, 0, 0, 0);
   for (int e = tid; e <= NX; e += 1024) mb.off[e] = off[e];

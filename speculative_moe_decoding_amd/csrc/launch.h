@@ -62,7 +62,7 @@ struct MoeBufs {
   int* n_act;     // [1]
   int4* slot_info;  // [NX] (expert, first pair, end pair, n_act); expert -1 past n_act
   int4* items;    // [expert_item_cap(M)] matrix-core work items: (expert, first pair, end pair, 0),
-                  // at most 64 pairs each, experts in slot order; expert -1 past the last
+                  // at most ITEM_PAIRS pairs each, experts in slot order; expert -1 past the last
   long long* stats;  // [0] += active experts per layer
   float* rlogit;  // [M][64] router logits
   float* hx;      // [8M][DI]
@@ -115,8 +115,13 @@ template <typename T>
 void launch_expert_down(hipStream_t s, const T* wd, int M, const MoeBufs& mb);
 void launch_moe_combine(hipStream_t s, float* x, int M, const MoeBufs& mb);
 int expert_slot_cap(int M);
-// Upper bound on the work items of a call: sum over experts of ceil(pairs / 64).
-__host__ __device__ inline int expert_item_cap(int M) { return NX + (NSLOT * M + 63) / 64; }
+// Matrix-core work items of prefill passes: at most ITEM_PAIRS pairs of one
+// expert, so a shared expert's rows of a long prefix spread over many
+// workgroups (their re-reads of the expert's weights come from the caches:
+// prefill passes load weights with ordinary, not non-temporal, loads).  Upper
+// bound on the items of a call: sum over experts of ceil(pairs / ITEM_PAIRS).
+constexpr int ITEM_PAIRS = 64;
+__host__ __device__ inline int expert_item_cap(int M) { return NX + (NSLOT * M + ITEM_PAIRS - 1) / ITEM_PAIRS; }
 // M <= MRG rows: the down GEMV whose last workgroup per output column adds
 // the combine to x -- the same bits as launch_expert_down + launch_moe_combine.
 // cnt: DOWN_CNT_WORDS zero words (left at zero).
