@@ -149,7 +149,7 @@ __device__ __forceinline__ void mf_compute(const MfChunkT<CT> (&ch)[NP], const u
 // A is RMSNorm'ed first: (a * rs[r]) * g (rs in LDS, one scale per pass row).
 // All 256 threads must call it; contains barriers.
 template <int K, int NT, int NB, int NS, int NP, typename RowPtr, bool NORM = false, int CT = MF_MT,
-          bool DEEP = false>
+          bool DEEP = false, bool CACHED = false>
 __device__ __forceinline__ void mfma_pass(const bf16* const (&w)[NB], RowPtr rowp, int rows, MfChunkT<CT> (&buf)[2][NP],
                                           f32x4_v (&acc)[NT][NB][NS], const float* __restrict__ g = nullptr,
                                           const float* rs = nullptr) {
@@ -203,18 +203,20 @@ __device__ __forceinline__ void mfma_pass(const bf16* const (&w)[NB], RowPtr row
     // Decode-sized passes: chunk c computes from LDS buffer c % 2 and
     // registers bq(c % 2) while chunk c + 1 is loaded into the other pair
     // (fewer registers: more workgroups in flight); one barrier per chunk.
+    // CACHED: ordinary weight loads, for workgroups that run several passes
+    // over the same weight strip.
     float4 gq[2];
     uint4 bq0[NB][NS][MF_SC], bq1[NB][NS][MF_SC];
     float4 ar[NT][2];
     mf_load_a(ar, gq, src, ok, gn, kg, 0);
-    mf_load_b<K, NB, NS>(bq0, w, woff, 0);
+    mf_load_b<K, NB, NS, CACHED>(bq0, w, woff, 0);
     mf_store_a<NT, NP, NORM, CT>(buf[0], ar, gq, rsv, kg, ri);
     __syncthreads();
 #pragma unroll 1
     for (int c = 0; c < NC; c += 2) {
       if (c + 1 < NC) {
         mf_load_a(ar, gq, src, ok, gn, kg, c + 1);  // activations first: waiting for them does not wait for the weights
-        mf_load_b<K, NB, NS>(bq1, w, woff, c + 1);
+        mf_load_b<K, NB, NS, CACHED>(bq1, w, woff, c + 1);
       }
       mf_compute<NT, NB, NS, NP, CT>(buf[0], bq0, acc);
       if (c + 1 < NC) mf_store_a<NT, NP, NORM, CT>(buf[1], ar, gq, rsv, kg, ri);
@@ -222,7 +224,7 @@ __device__ __forceinline__ void mfma_pass(const bf16* const (&w)[NB], RowPtr row
       if (c + 1 < NC) {
         if (c + 2 < NC) {
           mf_load_a(ar, gq, src, ok, gn, kg, c + 2);
-          mf_load_b<K, NB, NS>(bq0, w, woff, c + 2);
+          mf_load_b<K, NB, NS, CACHED>(bq0, w, woff, c + 2);
         }
         mf_compute<NT, NB, NS, NP, CT>(buf[1], bq1, acc);
         if (c + 2 < NC) mf_store_a<NT, NP, NORM, CT>(buf[0], ar, gq, rsv, kg, ri);
@@ -235,14 +237,14 @@ __device__ __forceinline__ void mfma_pass(const bf16* const (&w)[NB], RowPtr row
 // Gate/up: block (x, slot s) computes units j0 .. j0+15, j0 = 64 x + 16 w, of
 // active expert s for every pair routed to it:
 // hx[pair][j] = silu(gate_j . b) * (up_j . b), b the pair's normalised row.
-template <int NT, bool DEEP>
+template <int NT, bool DEEP, bool CACHED>
 __device__ __forceinline__ void gate_up_pass(const bf16* const (&w)[2], const float* __restrict__ bnorm,
                                              const int* __restrict__ perm, int kb, int rows, float* __restrict__ hx,
                                              int j0, MfChunk (&buf)[2][2]) {
   const int lane = lane_id();
   f32x4_v acc[NT][2][1];
   auto rowp = [=](int r) { return bnorm + (long)(perm[kb + r] / NSLOT) * D; };
-  mfma_pass<D, NT, 2, 1, 2, decltype(rowp), false, MF_MT, DEEP>(w, rowp, rows, buf, acc);
+  mfma_pass<D, NT, 2, 1, 2, decltype(rowp), false, MF_MT, DEEP, CACHED>(w, rowp, rows, buf, acc);
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
 #pragma unroll
@@ -258,7 +260,7 @@ __device__ __forceinline__ void gate_up_pass(const bf16* const (&w)[2], const fl
 // spread over several blocks.  Decode calls: expert slot y (the shared
 // experts' blocks load their weights with no routing read).  Either way,
 // passes of 64 pairs.
-template <bool DEEP>
+template <bool DEEP, bool CACHED>
 __global__ __launch_bounds__(256) void k_expert_gate_up_mfma(const bf16* __restrict__ wg,
                                                              const bf16* __restrict__ wu, int M, MoeBufs mb) {
   __shared__ MfChunk buf[2][2];
@@ -269,21 +271,21 @@ __global__ __launch_bounds__(256) void k_expert_gate_up_mfma(const bf16* __restr
   const bf16* const w[2] = {wg + ((long)e * DI + j0) * D, wu + ((long)e * DI + j0) * D};
   for (int kb = it.y; kb < it.z; kb += MF_ROWS) {
     const int rows = min(MF_ROWS, it.z - kb);
-    if (rows <= 16) gate_up_pass<1, DEEP>(w, mb.bnorm, mb.perm, kb, rows, mb.hx, j0, buf);
-    else if (rows <= 32) gate_up_pass<2, DEEP>(w, mb.bnorm, mb.perm, kb, rows, mb.hx, j0, buf);
-    else gate_up_pass<4, DEEP>(w, mb.bnorm, mb.perm, kb, rows, mb.hx, j0, buf);
+    if (rows <= 16) gate_up_pass<1, DEEP, CACHED>(w, mb.bnorm, mb.perm, kb, rows, mb.hx, j0, buf);
+    else if (rows <= 32) gate_up_pass<2, DEEP, CACHED>(w, mb.bnorm, mb.perm, kb, rows, mb.hx, j0, buf);
+    else gate_up_pass<4, DEEP, CACHED>(w, mb.bnorm, mb.perm, kb, rows, mb.hx, j0, buf);
   }
 }
 
 // Down: block (x, slot s) computes outputs n0 .. n0+31, n0 = 128 x + 32 w:
 // y[pair][n] = W_d[n] . hx[pair].
-template <int NT, bool DEEP>
+template <int NT, bool DEEP, bool CACHED>
 __device__ __forceinline__ void down_pass(const bf16* const (&w)[1], const float* __restrict__ hx, int kb, int rows,
                                           float* __restrict__ y, int n0, MfChunk (&buf)[2][2]) {
   const int lane = lane_id();
   f32x4_v acc[NT][1][2];
   auto rowp = [=](int r) { return hx + (long)(kb + r) * DI; };
-  mfma_pass<DI, NT, 1, 2, 2, decltype(rowp), false, MF_MT, DEEP>(w, rowp, rows, buf, acc);
+  mfma_pass<DI, NT, 1, 2, 2, decltype(rowp), false, MF_MT, DEEP, CACHED>(w, rowp, rows, buf, acc);
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
 #pragma unroll
@@ -298,7 +300,7 @@ __device__ __forceinline__ void down_pass(const bf16* const (&w)[1], const float
   }
 }
 
-template <bool DEEP>
+template <bool DEEP, bool CACHED>
 __global__ __launch_bounds__(256) void k_expert_down_mfma(const bf16* __restrict__ wd, int M, MoeBufs mb) {
   __shared__ MfChunk buf[2][2];
   const int4 it = DEEP ? mb.items[blockIdx.y] : expert_work(mb, blockIdx.y, M);
@@ -308,22 +310,22 @@ __global__ __launch_bounds__(256) void k_expert_down_mfma(const bf16* __restrict
   const bf16* const w[1] = {wd + ((long)e * D + n0) * DI};
   for (int kb = it.y; kb < it.z; kb += MF_ROWS) {
     const int rows = min(MF_ROWS, it.z - kb);
-    if (rows <= 16) down_pass<1, DEEP>(w, mb.hx, kb, rows, mb.y, n0, buf);
-    else if (rows <= 32) down_pass<2, DEEP>(w, mb.hx, kb, rows, mb.y, n0, buf);
-    else down_pass<4, DEEP>(w, mb.hx, kb, rows, mb.y, n0, buf);
+    if (rows <= 16) down_pass<1, DEEP, CACHED>(w, mb.hx, kb, rows, mb.y, n0, buf);
+    else if (rows <= 32) down_pass<2, DEEP, CACHED>(w, mb.hx, kb, rows, mb.y, n0, buf);
+    else down_pass<4, DEEP, CACHED>(w, mb.hx, kb, rows, mb.y, n0, buf);
   }
 }
 
 void launch_expert_gate_up_mfma(hipStream_t s, const bf16* wg, const bf16* wu, int M, const MoeBufs& mb, bool deep) {
   const dim3 grid(DI / 64, deep ? expert_item_cap(M) : expert_slot_cap(M));
-  if (deep) hipLaunchKernelGGL(k_expert_gate_up_mfma<true>, grid, dim3(256), 0, s, wg, wu, M, mb);
-  else hipLaunchKernelGGL(k_expert_gate_up_mfma<false>, grid, dim3(256), 0, s, wg, wu, M, mb);
+  if (deep) hipLaunchKernelGGL((k_expert_gate_up_mfma<true, true>), grid, dim3(256), 0, s, wg, wu, M, mb);
+  else hipLaunchKernelGGL((k_expert_gate_up_mfma<false, false>), grid, dim3(256), 0, s, wg, wu, M, mb);
 }
 
 void launch_expert_down_mfma(hipStream_t s, const bf16* wd, int M, const MoeBufs& mb, bool deep) {
   const dim3 grid(D / 128, deep ? expert_item_cap(M) : expert_slot_cap(M));
-  if (deep) hipLaunchKernelGGL(k_expert_down_mfma<true>, grid, dim3(256), 0, s, wd, M, mb);
-  else hipLaunchKernelGGL(k_expert_down_mfma<false>, grid, dim3(256), 0, s, wd, M, mb);
+  if (deep) hipLaunchKernelGGL((k_expert_down_mfma<true, true>), grid, dim3(256), 0, s, wd, M, mb);
+  else hipLaunchKernelGGL((k_expert_down_mfma<false, false>), grid, dim3(256), 0, s, wd, M, mb);
 }
 
 // ---- dense layers on the matrix cores -------------------------------------
@@ -719,13 +721,14 @@ __global__ __launch_bounds__(256) void k_lm_norm(const float* __restrict__ x, co
 // rows 64 x .. 64 x + 63 (16 per wavefront) for all M rows, passes of 64 rows,
 // and writes the best (value, lowest id) per row to part[row][x]; logits
 // optionally stored to logits[row][V].
-template <int NT>
+template <int NT, bool CACHED>
 __device__ __forceinline__ void lm_pass(const bf16* const (&w)[1], const float* __restrict__ xn, int p0, int rows,
                                         int vj, bool vok, int V, float* __restrict__ logits, float (&bv)[4][MF_ROWS],
                                         int (&bi)[4][MF_ROWS], MfChunk (&buf)[2][1]) {
   const int wave = wave_id(), lane = lane_id();
   f32x4_v acc[NT][1][1];
-  mfma_pass<D, NT, 1, 1, 1>(w, [=](int r) { return xn + (long)(p0 + r) * D; }, rows, buf, acc);
+  auto rowp = [=](int r) { return xn + (long)(p0 + r) * D; };
+  mfma_pass<D, NT, 1, 1, 1, decltype(rowp), false, MF_MT, false, CACHED>(w, rowp, rows, buf, acc);
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
 #pragma unroll
@@ -747,6 +750,9 @@ __device__ __forceinline__ void lm_pass(const bf16* const (&w)[1], const float* 
   }
 }
 
+// CACHED (more than 64 rows): ordinary weight loads, so that the strip's
+// later passes find it in the caches.
+template <bool CACHED>
 __global__ __launch_bounds__(256) void k_lmhead_mfma(const float* __restrict__ xn, const bf16* __restrict__ W,
                                                      int V, int M, float* __restrict__ part_val,
                                                      int* __restrict__ part_idx, float* __restrict__ logits) {
@@ -764,9 +770,9 @@ __global__ __launch_bounds__(256) void k_lmhead_mfma(const float* __restrict__ x
   const bool vok = vj >= v0 && vj < V;
   for (int p0 = 0; p0 < M; p0 += MF_ROWS) {
     const int rows = min(MF_ROWS, M - p0);
-    if (rows <= 16) lm_pass<1>(w, xn, p0, rows, vj, vok, V, logits, bv, bi, buf);
-    else if (rows <= 32) lm_pass<2>(w, xn, p0, rows, vj, vok, V, logits, bv, bi, buf);
-    else lm_pass<4>(w, xn, p0, rows, vj, vok, V, logits, bv, bi, buf);
+    if (rows <= 16) lm_pass<1, CACHED>(w, xn, p0, rows, vj, vok, V, logits, bv, bi, buf);
+    else if (rows <= 32) lm_pass<2, CACHED>(w, xn, p0, rows, vj, vok, V, logits, bv, bi, buf);
+    else lm_pass<4, CACHED>(w, xn, p0, rows, vj, vok, V, logits, bv, bi, buf);
     __syncthreads();
     if ((int)threadIdx.x < rows) {
       const int r = threadIdx.x;
@@ -786,7 +792,10 @@ void launch_lmhead_mfma(hipStream_t s, const float* x, const int* cnt, int Q, bo
                         float* logits, int* tok, int tok_stride) {
   hipLaunchKernelGGL(k_lm_norm, dim3((M + 3) / 4), dim3(256), 0, s, x, cnt, Q, (int)last_valid, gain, eps, M, xn);
   const int nb = lmhead_blocks(V);
-  hipLaunchKernelGGL(k_lmhead_mfma, dim3(nb), dim3(256), 0, s, xn, W, V, M, part_val, part_idx, logits);
+  if (M > MF_ROWS)
+    hipLaunchKernelGGL(k_lmhead_mfma<true>, dim3(nb), dim3(256), 0, s, xn, W, V, M, part_val, part_idx, logits);
+  else
+    hipLaunchKernelGGL(k_lmhead_mfma<false>, dim3(nb), dim3(256), 0, s, xn, W, V, M, part_val, part_idx, logits);
   if (tok != nullptr) launch_argmax_final(s, part_val, part_idx, nb, M, tok, tok_stride);
 }
 
