@@ -60,13 +60,24 @@ extern "C" {
  * values of those fields are rejected with OCRDEC_EINVAL.  n_layers >= 1,
  * vocab >= 2, max_positions <= 32768 (the pages' position limit),
  * max_batch in [1, 1024], max_k in [0, 7], max_batch * (max_k + 1) <= 1024
- * (rows of one verify call). */
+ * (rows of one verify call).
+ *
+ * KV cache: paged.  A page holds 64 consecutive positions of one sequence
+ * (keys and values of every head, every verifier layer, and the draft
+ * block's); a slot takes pages as its sequence grows and gives them back when
+ * it is released or prefilled anew, so concurrent sequences share the pool by
+ * their actual lengths (the French model card's concurrency-32 serving).
+ * kv_pages = the pool's size in pages; 0 = max_batch * ceil(max_positions /
+ * 64), enough for every slot at max_positions (never exhausted).  A call
+ * whose sequences would need more pages than are free returns
+ * OCRDEC_ECAPACITY with nothing enqueued. */
 typedef struct {
   int n_layers, d_model, n_heads, head_dim, n_experts, n_shared, top_k, d_expert, d_draft_ffn, vocab;
   float rope_theta, norm_eps;
   int dtype;                                   /* OCRDEC_F32 | OCRDEC_BF16 */
   int max_batch, max_k, max_positions;
   int path;                                    /* OCRDEC_PATH_* */
+  int kv_pages;                                /* KV page pool size; 0: the full size */
 } ocrdec_config;
 
 typedef struct ocrdec_model ocrdec_model;
@@ -211,6 +222,18 @@ int ocrdec_decode_steps_noalloc(ocrdec_model* m, void* stream, int B, const int3
  * passed max_positions (the flags are then cleared; the bounds are still
  * updated), and OCRDEC_EHIP if the read fails. */
 int ocrdec_sync_positions(ocrdec_model* m, void* stream);
+
+/* KV pages.  ocrdec_release_slot returns the pages of `slot` to the pool (the
+ * table update is enqueued on `stream`; issue every call of a handle on one
+ * stream, so that earlier work on the pages finishes first); the slot must be
+ * prefilled again before its next decode call.  Decode calls give pages to
+ * the slots they touch -- slots 0..B-1, or, with a device slot map, every slot
+ * that holds pages -- for their positions up to the host's bound (see
+ * ocrdec_sync_positions) plus what the call adds, so release finished
+ * sequences.  A slot without pages writes no cache rows.  ocrdec_kv_pages
+ * reports the pool's size and its free pages (host pointers, nullable). */
+int ocrdec_release_slot(ocrdec_model* m, void* stream, int slot);
+int ocrdec_kv_pages(ocrdec_model* m, int* total, int* free_pages);
 
 const char* ocrdec_last_error(void);
 

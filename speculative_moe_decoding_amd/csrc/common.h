@@ -501,6 +501,36 @@ __device__ __forceinline__ void stores_done() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Paged KV cache of one layer (verifier or draft).  A page holds KV_PAGE
+// consecutive positions (one attention tile) of one sequence, keys and
+// values of every head: [K|V][head][KV_PAGE][128].  table[slot * max_blocks
+// + pos / KV_PAGE] is the page of that block of positions, negative for none.
+// Readers take a missing page as page 0 (they only read rows they mask: chunks
+// past a sequence's end, or a slot released while the caller still decodes
+// it); writers skip rows without a page.  max_pos: positions per slot.
+constexpr int KV_PAGE = 64;
+template <typename T>
+struct KvView {
+  T* base;
+  const int* table;
+  int max_blocks;
+  int max_pos;
+  __device__ __forceinline__ int raw_page(long slot, int pos) const {
+    return table[slot * max_blocks + (min(max(pos, 0), max_pos - 1) / KV_PAGE)];
+  }
+  __device__ __forceinline__ long page_of(long slot, int pos) const {
+    const int p = raw_page(slot, pos);
+    return p < 0 ? 0 : p;
+  }
+  // the KV_PAGE rows of head h (kvsel 0: keys, 1: values) in a page
+  __device__ __forceinline__ T* rows(long page, int kvsel, int h) const {
+    return base + ((page * 2 + kvsel) * NH + h) * (long)(KV_PAGE * HD);
+  }
+  __device__ __forceinline__ T* at(long page, int kvsel, int h, int pos) const {
+    return rows(page, kvsel, h) + (long)(pos % KV_PAGE) * HD;
+  }
+};
+
 // Per-call row plan: sequence b of a call owns rows b*Q .. b*Q+Q-1; row i of
 // it is valid when i < cnt[b] and sits at position base[b] + i.
 struct RowPlan {

@@ -171,10 +171,11 @@ __device__ __forceinline__ float merge_loop(const float* __restrict__ pp, long c
   return O / L;
 }
 
+constexpr int ATT_MAX_TPC = 4;  // tiles per chunk at most
 template <typename T>
-__global__ __launch_bounds__(256) void k_attn_partial(const float* __restrict__ q, const T* __restrict__ kv,
-                                                      int max_pos, RowPlan plan, int n_chunks,
-                                                      int tiles_per_chunk, float* __restrict__ part) {
+__global__ __launch_bounds__(256) void k_attn_partial(const float* __restrict__ q, KvView<T> kv, RowPlan plan,
+                                                      int n_chunks, int tiles_per_chunk,
+                                                      float* __restrict__ part) {
   typedef AttTile<T> AT;
   // keys transposed in groups of 4 dims: Kq[d/4][t] = (k_t[d..d+3]); values row-major
   __shared__ typename AT::K4 Kq[HD / 4][KQ_STRIDE];
@@ -186,25 +187,28 @@ __global__ __launch_bounds__(256) void k_attn_partial(const float* __restrict__ 
   const int Q = plan.Q;
   const int C = tiles_per_chunk * ATT_TILE;
   const int k0 = c * C;
-  // The tile's addresses need only the slot: with identity slots the first
-  // tile's loads go out with the plan reads and this head's query rows (i < Q)
-  // (key indices clamped into the cache; rows past the last query's key are
-  // zeroed when staged).
+  const int max_pos = kv.max_pos;
+  // The tiles' addresses need only the slot and the pages of the chunk's
+  // tiles (one page per tile): with identity slots the page reads go out with
+  // the plan reads and this head's query rows (i < Q), then the first tile's
+  // loads (rows past the last query's key are zeroed when staged).
   const long slot = plan.ident ? (long)b : (long)plan.slot[b];
-  const T* Kc = kv + slot * (2L * NH * max_pos * HD) + (long)h * max_pos * HD;
-  const T* Vc = Kc + (long)NH * max_pos * HD;
+  long pg[ATT_MAX_TPC];
+#pragma unroll
+  for (int tt = 0; tt < ATT_MAX_TPC; ++tt) pg[tt] = tt < tiles_per_chunk ? kv.page_of(slot, k0 + tt * ATT_TILE) : 0;
   constexpr int CE = WT<T>::CE;
   constexpr int CPR = HD / CE;                         // 16-byte chunks per key row
   constexpr int NLD = ATT_TILE * CPR / 256;            // chunks per thread per tile
   uint4 kr[NLD], vr[NLD];
   auto load_tile = [&](int tt) {
-    const int kt = k0 + tt * ATT_TILE;
+    const long p = tt == 0 ? pg[0] : tt == 1 ? pg[1] : tt == 2 ? pg[2] : pg[3];  // selects, no indexing
+    const T* Kt = kv.rows(p, 0, h);
+    const T* Vt = kv.rows(p, 1, h);
 #pragma unroll
     for (int j = 0; j < NLD; ++j) {
       const int e = tid + 256 * j, t = e / CPR, d0 = (e % CPR) * CE;
-      const long k = min(kt + t, max_pos - 1);
-      kr[j] = ldg16(Kc + k * HD + d0);
-      vr[j] = ldg16(Vc + k * HD + d0);
+      kr[j] = ldg16(Kt + (long)t * HD + d0);
+      vr[j] = ldg16(Vt + (long)t * HD + d0);
     }
   };
   load_tile(0);
@@ -308,12 +312,12 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
 }
 
 template <typename T>
-void launch_attention(hipStream_t s, const float* q, const T* kv, int max_pos, RowPlan plan, int B, int n_chunks,
+void launch_attention(hipStream_t s, const float* q, KvView<T> kv, RowPlan plan, int B, int n_chunks,
                       int tiles_per_chunk, float* part, float* out) {
-  hipLaunchKernelGGL((k_attn_partial<T>), dim3(n_chunks, NH, B), dim3(256), 0, s, q, kv, max_pos, plan, n_chunks,
+  hipLaunchKernelGGL((k_attn_partial<T>), dim3(n_chunks, NH, B), dim3(256), 0, s, q, kv, plan, n_chunks,
                      tiles_per_chunk, part);
   hipLaunchKernelGGL(k_attn_combine, dim3(B * plan.Q, NH / 2), dim3(256), 0, s, part, plan, n_chunks,
-                     tiles_per_chunk * ATT_TILE, max_pos, out);
+                     tiles_per_chunk * ATT_TILE, kv.max_pos, out);
 }
 
 // ---- prefill attention --------------------------------------------------
@@ -336,8 +340,8 @@ void launch_attention(hipStream_t s, const float* q, const T* kv, int max_pos, R
 // row's result does not depend on the other rows of the launch.
 constexpr int PA_VT_STRIDE = ATT_TILE / 2 + 4;  // 32-bit words per transposed value row (+4: spreads banks)
 
-__global__ __launch_bounds__(128) void k_attn_prefill_mfma(const float* __restrict__ q, const bf16* __restrict__ kv,
-                                                           int max_pos, RowPlan plan, float* __restrict__ out) {
+__global__ __launch_bounds__(128) void k_attn_prefill_mfma(const float* __restrict__ q, KvView<bf16> kv,
+                                                           RowPlan plan, float* __restrict__ out) {
   __shared__ __align__(16) uint32_t vt[HD][PA_VT_STRIDE];  // vt[d][k / 2] = (v[k][d], v[k + 1][d]) as bf16 pairs
   __shared__ __align__(16) float pl[2][16][ATT_TILE + 4];  // per wavefront: P rows
   const int b = blockIdx.x, h = blockIdx.y;
@@ -346,8 +350,7 @@ __global__ __launch_bounds__(128) void k_attn_prefill_mfma(const float* __restri
   const int Q = plan.Q;
   const int base = plan.base[b], cnt = min(plan.cnt[b], Q);
   const long slot = plan.slot[b];
-  const bf16* Kc = kv + slot * (2L * NH * max_pos * HD) + (long)h * max_pos * HD;
-  const bf16* Vc = Kc + (long)NH * max_pos * HD;
+  const int max_pos = kv.max_pos;
   const int p_last = min(base + cnt - 1, max_pos - 1);
   // A fragments of this wavefront's 16 query rows (row c16, dims 32 s + 8 g ..)
   const int qi = 16 * wave + c16;
@@ -376,21 +379,24 @@ __global__ __launch_bounds__(128) void k_attn_prefill_mfma(const float* __restri
 #pragma unroll
   for (int d = 0; d < 8; ++d) o[d] = f32x4_v{0.f, 0.f, 0.f, 0.f};
   // tile loads: key fragments (key kt + 16 n + c16, dims 32 s + 8 g ..) and
-  // this thread's value chunks (keys 2 kp, 2 kp + 1, dims 8 dc ..)
+  // this thread's value chunks (keys 2 kp, 2 kp + 1, dims 8 dc ..), from the
+  // tile's page
   uint4 kf[4][4], vc[4][2];
   auto load_tile = [&](int kt) {
+    const long pgt = kv.page_of(slot, kt);
+    const bf16* Kt = kv.rows(pgt, 0, h);
+    const bf16* Vt = kv.rows(pgt, 1, h);
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
-      const long k = min(kt + 16 * n + c16, max_pos - 1);
+      const long k = 16 * n + c16;
 #pragma unroll
-      for (int st = 0; st < 4; ++st) kf[n][st] = ldg16(Kc + k * HD + 32 * st + 8 * g);
+      for (int st = 0; st < 4; ++st) kf[n][st] = ldg16(Kt + k * HD + 32 * st + 8 * g);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = tid + 128 * j, kp = e >> 4, dc = e & 15;  // 32 key pairs x 16 dim chunks
-      const long k0 = min(kt + 2 * kp, max_pos - 1), k1 = min(kt + 2 * kp + 1, max_pos - 1);
-      vc[j][0] = ldg16(Vc + k0 * HD + 8 * dc);
-      vc[j][1] = ldg16(Vc + k1 * HD + 8 * dc);
+      vc[j][0] = ldg16(Vt + (long)(2 * kp) * HD + 8 * dc);
+      vc[j][1] = ldg16(Vt + (long)(2 * kp + 1) * HD + 8 * dc);
     }
   };
   const int n_tiles = cnt > 0 && base >= 0 ? p_last / ATT_TILE + 1 : 0;
@@ -487,16 +493,15 @@ __global__ __launch_bounds__(128) void k_attn_prefill_mfma(const float* __restri
 // The fp32 cache: block (entry b, head h), wavefront w serves rows w, w + 4,
 // ..; per 64-key tile, lane = key for the scores (q . k in order over the 128
 // dims), the online softmax, then lane = value-dim pair for the output.
-__global__ __launch_bounds__(256) void k_attn_prefill_f32(const float* __restrict__ q, const float* __restrict__ kv,
-                                                          int max_pos, RowPlan plan, float* __restrict__ out) {
+__global__ __launch_bounds__(256) void k_attn_prefill_f32(const float* __restrict__ q, KvView<float> kv,
+                                                          RowPlan plan, float* __restrict__ out) {
   __shared__ float pw[4][ATT_TILE];
   const int b = blockIdx.x, h = blockIdx.y;
   const int wave = wave_id(), lane = lane_id();
   const int Q = plan.Q;
   const int base = plan.base[b], cnt = min(plan.cnt[b], Q);
   const long slot = plan.slot[b];
-  const float* Kc = kv + slot * (2L * NH * max_pos * HD) + (long)h * max_pos * HD;
-  const float* Vc = Kc + (long)NH * max_pos * HD;
+  const int max_pos = kv.max_pos;
   const float scale = 0.08838834764831845f;
   for (int i = wave; i < Q; i += 4) {
     float* orow = out + (long)(b * Q + i) * QD + h * HD;
@@ -511,7 +516,9 @@ __global__ __launch_bounds__(256) void k_attn_prefill_f32(const float* __restric
     for (int kt = 0; kt <= plim; kt += ATT_TILE) {
       const int key = kt + lane;
       const bool vis = key <= plim;
-      const float* kr = Kc + (long)min(key, max_pos - 1) * HD;
+      const long pgt = kv.page_of(slot, kt);
+      const float* kr = kv.rows(pgt, 0, h) + (long)lane * HD;
+      const float* Vt = kv.rows(pgt, 1, h);
       float sc = 0.f;
       for (int d = 0; d < HD; ++d) sc = fmaf(qr[d], kr[d], sc);
       sc *= scale;
@@ -526,7 +533,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill_f32(const float* __restric
       float a0 = o0 * corr, a1 = o1 * corr;
       const int nk = min(ATT_TILE, plim + 1 - kt);
       for (int t = 0; t < nk; ++t) {
-        const float2 v = *reinterpret_cast<const float2*>(Vc + (long)(kt + t) * HD + 2 * lane);
+        const float2 v = *reinterpret_cast<const float2*>(Vt + (long)t * HD + 2 * lane);
         a0 = fmaf(pw[wave][t], v.x, a0);
         a1 = fmaf(pw[wave][t], v.y, a1);
       }
@@ -541,19 +548,18 @@ __global__ __launch_bounds__(256) void k_attn_prefill_f32(const float* __restric
 }
 
 template <>
-void launch_attention_prefill<bf16>(hipStream_t s, const float* q, const bf16* kv, int max_pos, RowPlan plan, int n,
-                                    float* out) {
-  hipLaunchKernelGGL(k_attn_prefill_mfma, dim3(n, NH), dim3(128), 0, s, q, kv, max_pos, plan, out);
+void launch_attention_prefill<bf16>(hipStream_t s, const float* q, KvView<bf16> kv, RowPlan plan, int n, float* out) {
+  hipLaunchKernelGGL(k_attn_prefill_mfma, dim3(n, NH), dim3(128), 0, s, q, kv, plan, out);
 }
 template <>
-void launch_attention_prefill<float>(hipStream_t s, const float* q, const float* kv, int max_pos, RowPlan plan, int n,
+void launch_attention_prefill<float>(hipStream_t s, const float* q, KvView<float> kv, RowPlan plan, int n,
                                      float* out) {
-  hipLaunchKernelGGL(k_attn_prefill_f32, dim3(n, NH), dim3(256), 0, s, q, kv, max_pos, plan, out);
+  hipLaunchKernelGGL(k_attn_prefill_f32, dim3(n, NH), dim3(256), 0, s, q, kv, plan, out);
 }
 
-template void launch_attention<float>(hipStream_t, const float*, const float*, int, RowPlan, int, int, int, float*,
+template void launch_attention<float>(hipStream_t, const float*, KvView<float>, RowPlan, int, int, int, float*,
                                       float*);
-template void launch_attention<bf16>(hipStream_t, const float*, const bf16*, int, RowPlan, int, int, int, float*,
+template void launch_attention<bf16>(hipStream_t, const float*, KvView<bf16>, RowPlan, int, int, int, float*,
                                      float*);
 
 }  // namespace ocr

@@ -41,8 +41,9 @@ __device__ __forceinline__ void rot(float a, float b, float c, float s, float& o
 template <typename T, int MR>
 __global__ __launch_bounds__(256) void k_qkv_rope(const float* __restrict__ x, const float* __restrict__ gain,
                                                   float eps, const T* __restrict__ wqkv, int M, RowPlan plan,
-                                                  float* __restrict__ q, T* __restrict__ kv, int max_pos,
+                                                  float* __restrict__ q, KvView<T> kv,
                                                   const float2* __restrict__ rope) {
+  const int max_pos = kv.max_pos;
   extern __shared__ float smem[];
   float* xs = smem;
   const int wave = wave_id(), lane = lane_id();
@@ -61,8 +62,8 @@ __global__ __launch_bounds__(256) void k_qkv_rope(const float* __restrict__ x, c
   const T* rows[2] = {wqkv + (long)r0 * D, wqkv + (long)r1 * D};
   WaveGemv<T, D, 2, MR> g;
   g.load(rows);
-  // lane m < m_act: this row's position, validity, cache slot and rotation
-  int pos = 0, b = 0, i = 0, slot = 0;
+  // lane m < m_act: this row's position, validity, cache page and rotation
+  int pos = 0, b = 0, i = 0, slot = 0, page = 0;
   bool valid = false;
   float2 cs = make_float2(1.f, 0.f);
   if (lane < m_act) {
@@ -73,6 +74,10 @@ __global__ __launch_bounds__(256) void k_qkv_rope(const float* __restrict__ x, c
     pos = plan.base[b] + i;
     valid = i < plan.cnt[b] && pos >= 0 && pos < max_pos;
     if (sec < 2) cs = rope[(long)min(max(pos, 0), max_pos - 1) * (HD / 2) + u];
+    if (sec > 0) {
+      page = kv.raw_page(slot, pos);
+      valid = valid && page >= 0;
+    }
   }
   norm_rows_wave<D, MR>(x, D, RowIdentity{m0}, m_act, gain, eps, xs);
   __syncthreads();
@@ -81,13 +86,11 @@ __global__ __launch_bounds__(256) void k_qkv_rope(const float* __restrict__ x, c
   // lane with (r, m): row m's position data from lane m, the pair's other total
   const WaveTotals<2, MR> t(acc);
   const float other = t.partner(1);
-  const int tpos = __shfl(pos, t.m, 64), tslot = __shfl(slot, t.m, 64);
+  const int tpos = __shfl(pos, t.m, 64), tpage = __shfl(page, t.m, 64);
   const bool tvalid = __shfl((int)valid, t.m, 64) != 0;
   const float tc = __shfl(cs.x, t.m, 64), ts = __shfl(cs.y, t.m, 64);
   if (t.lead && t.m < m_act) {
     const int row = m0 + t.m;
-    const long slot_stride = 2L * NH * max_pos * HD;
-    const long slot = tslot;
     if (sec < 2) {
       // rows u (r = 0) and u + 64 (r = 1) of a head: each lane rotates its own
       float o;
@@ -96,21 +99,21 @@ __global__ __launch_bounds__(256) void k_qkv_rope(const float* __restrict__ x, c
       if (sec == 0) {
         q[(long)row * QD + h * HD + u + 64 * t.r] = o;
       } else if (tvalid) {
-        kv[slot * slot_stride + ((long)h * max_pos + tpos) * HD + u + 64 * t.r] = WT<T>::store_cvt(o);
+        kv.at(tpage, 0, h, tpos)[u + 64 * t.r] = WT<T>::store_cvt(o);
       }
     } else if (tvalid) {
-      kv[slot * slot_stride + ((long)(NH + h) * max_pos + tpos) * HD + 2 * u + t.r] = WT<T>::store_cvt(t.val);
+      kv.at(tpage, 1, h, tpos)[2 * u + t.r] = WT<T>::store_cvt(t.val);
     }
   }
 }
 
 template <typename T>
 void launch_qkv_rope(hipStream_t s, const float* x, const float* gain, float eps, const T* wqkv, int M,
-                     RowPlan plan, float* q, T* kv, int max_pos, const float2* rope) {
+                     RowPlan plan, float* q, KvView<T> kv, const float2* rope) {
   const dim3 blk(256);
 #define OCR_QKV_CASE(MRV)                                                                                     \
   hipLaunchKernelGGL((k_qkv_rope<T, MRV>), dim3(480, (M + MRV - 1) / MRV), blk, (size_t)MRV * D * 4, s, x, gain, \
-                     eps, wqkv, M, plan, q, kv, max_pos, rope);
+                     eps, wqkv, M, plan, q, kv, rope);
   if (M <= 1) OCR_QKV_CASE(1)
   else if (M <= 2) OCR_QKV_CASE(2)
   else if (M <= 4) OCR_QKV_CASE(4)
@@ -334,7 +337,7 @@ void launch_lmhead(hipStream_t s, const float* x, const int* cnt, int Q, bool la
 
 #define OCR_INST_DENSE(T)                                                                                       \
   template void launch_qkv_rope<T>(hipStream_t, const float*, const float*, float, const T*, int, RowPlan,     \
-                                   float*, T*, int, const float2*);                                            \
+                                   float*, KvView<T>, const float2*);                                            \
   template void launch_gemv<T>(hipStream_t, int, Epi, const float*, long, const float*, float, const T*,       \
                                const T*, int, int, float*, long);                                              \
   template void launch_lmhead<T>(hipStream_t, const float*, const int*, int, bool, const float*, float,        \

@@ -345,8 +345,7 @@ enum DenseMode { DM_STORE = 0, DM_ADD = 1, DM_SWIGLU = 2, DM_QKV = 3 };
 struct QkvOut {
   RowPlan plan;
   float* q;
-  bf16* kv;
-  int max_pos;
+  KvView<bf16> kv;
   const float2* rope;
 };
 
@@ -382,25 +381,30 @@ __device__ __forceinline__ void dense_mfma_rows(const float* __restrict__ a, lon
         const RowPlan& plan = qo.plan;
         const int b = m / plan.Q, ii = m - b * plan.Q;
         const int pos = plan.base[b] + ii;
-        const bool valid = ii < plan.cnt[b] && pos >= 0 && pos < qo.max_pos;
-        const long slot_stride = 2L * NH * qo.max_pos * HD;
+        const bool valid = ii < plan.cnt[b] && pos >= 0 && pos < qo.kv.max_pos;
         if (sec < 2) {
           const int u = 16 * wave + j;
-          const float2 cs = qo.rope[(long)min(max(pos, 0), qo.max_pos - 1) * (HD / 2) + u];
+          const float2 cs = qo.rope[(long)min(max(pos, 0), qo.kv.max_pos - 1) * (HD / 2) + u];
           const float o0 = fmaf(v0, cs.x, -(v1 * cs.y));
           const float o1 = fmaf(v1, cs.x, v0 * cs.y);
           if (sec == 0) {
             qo.q[(long)m * QD + h * HD + u] = o0;
             qo.q[(long)m * QD + h * HD + u + 64] = o1;
           } else if (valid) {
-            bf16* kd = qo.kv + (long)plan.slot[b] * slot_stride + ((long)h * qo.max_pos + pos) * HD;
-            kd[u] = f2bf(o0);
-            kd[u + 64] = f2bf(o1);
+            const int pg = qo.kv.raw_page(plan.slot[b], pos);
+            if (pg >= 0) {
+              bf16* kd = qo.kv.at(pg, 0, h, pos);
+              kd[u] = f2bf(o0);
+              kd[u + 64] = f2bf(o1);
+            }
           }
         } else if (valid) {
-          bf16* vd = qo.kv + (long)plan.slot[b] * slot_stride + ((long)(NH + h) * qo.max_pos + pos) * HD;
-          vd[32 * wave + j] = f2bf(v0);
-          vd[32 * wave + 16 + j] = f2bf(v1);
+          const int pg = qo.kv.raw_page(plan.slot[b], pos);
+          if (pg >= 0) {
+            bf16* vd = qo.kv.at(pg, 1, h, pos);
+            vd[32 * wave + j] = f2bf(v0);
+            vd[32 * wave + 16 + j] = f2bf(v1);
+          }
         }
       }
     }
@@ -512,7 +516,7 @@ __global__ __launch_bounds__(256) void k_dense_ks(const float* __restrict__ a, l
   // finishes (row 4 (lane / 16) + wave, column lane % 16), fetched before the
   // main loop so that the epilogue waits on no memory
   int e_pos = 0;
-  long e_slot = 0;
+  long e_page = 0;
   bool e_valid = false;
   float2 e_cs = make_float2(1.f, 0.f);
   if constexpr (MODE == DM_QKV) {
@@ -520,10 +524,13 @@ __global__ __launch_bounds__(256) void k_dense_ks(const float* __restrict__ a, l
     if (r < rows) {
       const RowPlan& plan = qo.plan;
       const int m = m0 + r, b = m / plan.Q, i = m - b * plan.Q;
-      e_slot = plan.slot[b];
       e_pos = plan.base[b] + i;
-      e_valid = i < plan.cnt[b] && e_pos >= 0 && e_pos < qo.max_pos;
-      if (sec < 2) e_cs = qo.rope[(long)min(max(e_pos, 0), qo.max_pos - 1) * (HD / 2) + c0 + (lane & 15)];
+      e_valid = i < plan.cnt[b] && e_pos >= 0 && e_pos < qo.kv.max_pos;
+      if (sec > 0) {
+        e_page = qo.kv.raw_page(plan.slot[b], e_pos);
+        e_valid = e_valid && e_page >= 0;
+      }
+      if (sec < 2) e_cs = qo.rope[(long)min(max(e_pos, 0), qo.kv.max_pos - 1) * (HD / 2) + c0 + (lane & 15)];
     }
   }
   if (gain != nullptr) {
@@ -621,7 +628,6 @@ __global__ __launch_bounds__(256) void k_dense_ks(const float* __restrict__ a, l
   } else if constexpr (MODE == DM_SWIGLU) {
     out[(long)m * ldo + c0 + j] = silu(v[0]) * v[NB - 1];
   } else {
-    const long slot_stride = 2L * NH * qo.max_pos * HD;
     if (sec < 2) {
       const int u = c0 + j;
       const float o0 = fmaf(v[0], e_cs.x, -(v[NB - 1] * e_cs.y));
@@ -630,12 +636,12 @@ __global__ __launch_bounds__(256) void k_dense_ks(const float* __restrict__ a, l
         qo.q[(long)m * QD + h * HD + u] = o0;
         qo.q[(long)m * QD + h * HD + u + 64] = o1;
       } else if (e_valid) {
-        bf16* kd = qo.kv + e_slot * slot_stride + ((long)h * qo.max_pos + e_pos) * HD;
+        bf16* kd = qo.kv.at(e_page, 0, h, e_pos);
         kd[u] = f2bf(o0);
         kd[u + 64] = f2bf(o1);
       }
     } else if (e_valid) {
-      bf16* vd = qo.kv + e_slot * slot_stride + ((long)(NH + h) * qo.max_pos + e_pos) * HD;
+      bf16* vd = qo.kv.at(e_page, 1, h, e_pos);
       vd[c0 + j] = f2bf(v[0]);
       vd[c0 + 16 + j] = f2bf(v[NB - 1]);
     }
@@ -659,8 +665,8 @@ bool launch_gemv_ks(hipStream_t s, int K, Epi epi, const float* a, long lda, con
 }
 
 void launch_qkv_rope_ks(hipStream_t s, const float* x, const float* gain, float eps, const bf16* wqkv, int M,
-                        RowPlan plan, float* q, bf16* kv, int max_pos, const float2* rope) {
-  const QkvOut qo{plan, q, kv, max_pos, rope};
+                        RowPlan plan, float* q, KvView<bf16> kv, const float2* rope) {
+  const QkvOut qo{plan, q, kv, rope};
   hipLaunchKernelGGL((k_dense_ks<D, DM_QKV>), dim3(120, (M + 15) / 16), dim3(256), 0, s, x, (long)D, gain, eps, wqkv,
                      nullptr, M, nullptr, 0L, qo);
 }
@@ -687,8 +693,8 @@ bool launch_gemv_mfma(hipStream_t s, int K, Epi epi, const float* a, long lda, c
 }
 
 void launch_qkv_rope_mfma(hipStream_t s, const float* x, const float* gain, float eps, const bf16* wqkv, int M,
-                          RowPlan plan, float* q, bf16* kv, int max_pos, const float2* rope, float* rscale) {
-  const QkvOut qo{plan, q, kv, max_pos, rope};
+                          RowPlan plan, float* q, KvView<bf16> kv, const float2* rope, float* rscale) {
+  const QkvOut qo{plan, q, kv, rope};
   hipLaunchKernelGGL((k_row_rms<D>), dim3((M + 3) / 4), dim3(256), 0, s, x, (long)D, M, eps, rscale);
   hipLaunchKernelGGL((k_dense_mfma<D, DM_QKV>), dim3(3 * NH, (M + MF_ROWS - 1) / MF_ROWS), dim3(256), 0, s, x,
                      (long)D, gain, rscale, wqkv, nullptr, M, nullptr, 0L, qo);

@@ -644,6 +644,35 @@ void launch_prefill_finish(hipStream_t s, const PrefillGroup& g, const float* xf
                            int* pending_out) {
   hipLaunchKernelGGL(k_prefill_finish, dim3(g.n), dim3(256), 0, s, g, xfinal, tok, sv, pending_out);
 }
+// Page-table updates: table[ps.idx[i]] = ps.page[i], i < ps.n.
+__global__ void k_set_pages(int* __restrict__ table, PageSet ps) {
+  const int i = threadIdx.x;
+  if (i < ps.n) table[ps.idx[i]] = ps.page[i];
+}
+void launch_set_pages(hipStream_t s, int* table, const PageSet& ps) {
+  hipLaunchKernelGGL(k_set_pages, dim3(1), dim3(256), 0, s, table, ps);
+}
+
+// A caller's cache of one layer, [K|V][head][n_pos][HD], into the pages of
+// `slot`: block (block j of positions, plane K|V x head) copies its rows.
+template <typename T>
+__global__ __launch_bounds__(256) void k_load_kv(const T* __restrict__ src, int n_pos, KvView<T> kv, int slot) {
+  const int j = blockIdx.x, plane = blockIdx.y;
+  const int rows = min(KV_PAGE, n_pos - j * KV_PAGE);
+  const int pg = kv.raw_page(slot, j * KV_PAGE);
+  if (pg < 0) return;
+  T* dst = kv.rows(pg, plane / NH, plane % NH);
+  const T* from = src + ((long)plane * n_pos + (long)j * KV_PAGE) * HD;
+  for (int e = threadIdx.x; e < rows * HD; e += 256) dst[e] = from[e];
+}
+template <typename T>
+void launch_load_kv(hipStream_t s, const T* src, int n_pos, KvView<T> kv, int slot) {
+  hipLaunchKernelGGL((k_load_kv<T>), dim3((n_pos + KV_PAGE - 1) / KV_PAGE, 2 * NH), dim3(256), 0, s, src, n_pos, kv,
+                     slot);
+}
+template void launch_load_kv<float>(hipStream_t, const float*, int, KvView<float>, int);
+template void launch_load_kv<bf16>(hipStream_t, const bf16*, int, KvView<bf16>, int);
+
 void launch_set_sequence(hipStream_t s, int slot, int P, int tok, StateView sv) {
   hipLaunchKernelGGL(k_set_sequence, dim3(1), dim3(256), 0, s, slot, P, tok, sv);
 }

@@ -9,11 +9,11 @@ namespace ocr {
 enum Epi { EPI_STORE = 0, EPI_ADD = 1, EPI_SWIGLU = 2 };
 
 // x: [M][D] residual rows; gain: RMSNorm gain (never null here).
-// Writes q (RoPE'd, fp32 [M][QD]) and, for valid rows, k / v into the cache
-// kv[slot][0|1][head][pos][HD] (slot stride = 2*NH*max_pos*HD elements).
+// Writes q (RoPE'd, fp32 [M][QD]) and, for valid rows, k / v into the paged
+// cache kv (the page of each row's position must exist).
 template <typename T>
 void launch_qkv_rope(hipStream_t s, const float* x, const float* gain, float eps, const T* wqkv, int M,
-                     RowPlan plan, float* q, T* kv, int max_pos, const float2* rope);
+                     RowPlan plan, float* q, KvView<T> kv, const float2* rope);
 // tab[pos][i] = (cos, sin)(pos * theta^(-2i/128)), i < 64, for pos < max_pos.
 void launch_rope_table(hipStream_t s, int max_pos, float theta, float2* tab);
 
@@ -39,8 +39,8 @@ void launch_argmax_final(hipStream_t s, const float* part_val, const int* part_i
 // Split-KV decode attention (partials per chunk) and the merge of the chunks
 // into out, in two launches.
 template <typename T>
-void launch_attention(hipStream_t s, const float* q, const T* kv, int max_pos, RowPlan plan, int B,
-                      int n_chunks, int tiles_per_chunk, float* part, float* out);
+void launch_attention(hipStream_t s, const float* q, KvView<T> kv, RowPlan plan, int B, int n_chunks,
+                      int tiles_per_chunk, float* part, float* out);
 
 // Prefill attention: n entries of plan.Q = PREFILL_CHUNK rows; row i of entry
 // b (i < cnt[b]) is the query at position base[b] + i of slot slot[b] and sees
@@ -48,8 +48,7 @@ void launch_attention(hipStream_t s, const float* q, const T* kv, int max_pos, R
 // out[b * Q + i] = the head outputs (rows past cnt: zero).  bf16 caches on the
 // matrix cores, fp32 caches on the vector units.
 template <typename T>
-void launch_attention_prefill(hipStream_t s, const float* q, const T* kv, int max_pos, RowPlan plan, int n,
-                              float* out);
+void launch_attention_prefill(hipStream_t s, const float* q, KvView<T> kv, RowPlan plan, int n, float* out);
 
 struct MoeBufs {
   float* bnorm;   // [M][D] normalised rows
@@ -162,13 +161,13 @@ void launch_expert_down_mfma(hipStream_t s, const bf16* wd, int M, const MoeBufs
 bool launch_gemv_mfma(hipStream_t s, int K, Epi epi, const float* a, long lda, const float* gain, float eps,
                       const bf16* W0, const bf16* W1, int N, int M, float* out, long ldo, float* rscale);
 void launch_qkv_rope_mfma(hipStream_t s, const float* x, const float* gain, float eps, const bf16* wqkv, int M,
-                          RowPlan plan, float* q, bf16* kv, int max_pos, const float2* rope, float* rscale);
+                          RowPlan plan, float* q, KvView<bf16> kv, const float2* rope, float* rscale);
 // The same with k split over the four wavefronts of 16-row blocks (decode-sized
 // calls: many blocks, no LDS staging).
 bool launch_gemv_ks(hipStream_t s, int K, Epi epi, const float* a, long lda, const float* gain, float eps,
                     const bf16* W0, const bf16* W1, int N, int M, float* out, long ldo);
 void launch_qkv_rope_ks(hipStream_t s, const float* x, const float* gain, float eps, const bf16* wqkv, int M,
-                        RowPlan plan, float* q, bf16* kv, int max_pos, const float2* rope);
+                        RowPlan plan, float* q, KvView<bf16> kv, const float2* rope);
 // LM head + argmax: xn ([M][D] scratch) receives the normalised rows; V >= 16.
 void launch_lmhead_mfma(hipStream_t s, const float* x, const int* cnt, int Q, bool last_valid, const float* gain,
                         float eps, const bf16* W, int V, int M, float* xn, float* part_val, int* part_idx,
@@ -244,6 +243,17 @@ void launch_prefill_last_rows(hipStream_t s, const PrefillGroup& g, const float*
 void launch_prefill_finish(hipStream_t s, const PrefillGroup& g, const float* xfinal, const int* tok, StateView sv,
                            int* pending_out);
 void launch_set_sequence(hipStream_t s, int slot, int P, int tok, StateView sv);
+// KV page-table entries set by value (at most PAGESET_N per launch, each
+// entry once: the launch's threads store in no set order).
+constexpr int PAGESET_N = 240;
+struct PageSet {
+  int n;
+  int idx[PAGESET_N], page[PAGESET_N];
+};
+void launch_set_pages(hipStream_t s, int* table, const PageSet& ps);
+// Copy a caller's cache of one layer ([K|V][head][n_pos][128]) into a slot's pages.
+template <typename T>
+void launch_load_kv(hipStream_t s, const T* src, int n_pos, KvView<T> kv, int slot);
 // Acceptance; with part_val non-null the greedy tokens are first reduced from
 // the LM head's per-block bests (part_val / part_idx, nblk per row) and
 // written to greedy_w (the verify then skips its argmax stage 2).

@@ -9,6 +9,7 @@
 #include <string>
 #include <tuple>
 #include <type_traits>
+#include <unordered_map>
 #include <vector>
 
 #include "launch.h"
@@ -31,10 +32,10 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 // Offsets of every sub-buffer inside the state and the workspace.
 struct Plan {
   // derived sizes
-  int M_max, prefill_group, cu_stride, tiles_per_chunk, chunk_keys, n_chunks_cap, lm_nblk, plan_n;
+  int max_blocks, n_pages, M_max, prefill_group, cu_stride, tiles_per_chunk, chunk_keys, n_chunks_cap, lm_nblk, plan_n;
   size_t esz, kv_layer_elems;
   // state
-  size_t s_kv, s_dkv, s_ints, s_cu, s_hbuf, s_rope, s_total;
+  size_t s_kv, s_dkv, s_table, s_ints, s_cu, s_hbuf, s_rope, s_total;
   // workspace
   size_t w_x, w_rscale, w_q, w_attn, w_part, w_bnorm, w_ridx, w_rgate, w_perm, w_inv, w_off, w_act, w_slot, w_items, w_rlogit, w_misc, w_stats, w_sync, w_hx,
       w_y, w_cat, w_u, w_u2, w_dffn, w_esave, w_hsave, w_lmv, w_lmi, w_plan, w_total;
@@ -56,6 +57,7 @@ bool shape_ok(const ocrdec_config* c, std::string* why) {
   if (c->max_positions < 16 || c->max_positions > 32768) { *why = "max_positions must be in [16, 32768]"; return false; }
   if (!(c->norm_eps > 0.f) || !(c->rope_theta > 1.f)) { *why = "norm_eps must be > 0 and rope_theta > 1"; return false; }
   if (c->path < OCRDEC_PATH_AUTO || c->path > OCRDEC_PATH_MATRIX) { *why = "path must be OCRDEC_PATH_*"; return false; }
+  if (c->kv_pages < 0) { *why = "kv_pages must be >= 0 (0: one page per 64 positions of every slot)"; return false; }
   if (c->path == OCRDEC_PATH_MATRIX && (c->dtype != OCRDEC_BF16 || c->vocab < 64)) {
     *why = "the matrix-core path needs bf16 weights and vocab >= 64";
     return false;
@@ -84,11 +86,16 @@ Plan make_plan(const ocrdec_config* c, bool decode_only = false) {
   p.n_chunks_cap = (c->max_positions + p.chunk_keys - 1) / p.chunk_keys;
   p.lm_nblk = lmhead_blocks(c->vocab);
   p.esz = c->dtype == OCRDEC_BF16 ? 2 : 4;
-  p.kv_layer_elems = (size_t)c->max_batch * 2 * NH * (size_t)c->max_positions * HD;
+  // KV pages: KV_PAGE positions of one sequence each, for every head, keys
+  // and values; one table row of max_blocks pages per slot
+  p.max_blocks = (c->max_positions + KV_PAGE - 1) / KV_PAGE;
+  p.n_pages = c->kv_pages > 0 ? std::min(c->kv_pages, c->max_batch * p.max_blocks) : c->max_batch * p.max_blocks;
+  p.kv_layer_elems = (size_t)p.n_pages * 2 * NH * KV_PAGE * HD;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o = align256(o + bytes); return r; };
   p.s_kv = take(p.kv_layer_elems * c->n_layers * p.esz);
   p.s_dkv = take(p.kv_layer_elems * p.esz);
+  p.s_table = take((size_t)c->max_batch * p.max_blocks * 4);
   p.s_ints = take((size_t)8 * c->max_batch * 4);
   p.s_cu = take((size_t)c->max_batch * p.cu_stride * 4);
   p.s_hbuf = take((size_t)c->max_batch * p.cu_stride * D * 4);
@@ -249,6 +256,9 @@ struct ocrdec_model {
   std::string scratch_err;
   int moe_grid;                // workgroups of the persistent MoE launch (0: not available)
   bool fused_moe;              // vector-path MoE halves in one persistent launch (else five launches)
+  // KV page pool: free pages (a stack) and each slot's pages by block
+  std::vector<int> free_pages;
+  std::vector<std::vector<int>> slot_pages;
 };
 
 namespace {
@@ -285,6 +295,95 @@ int call_bound(const ocrdec_model* m, int B, const int32_t* slots) {
   int b = 0;
   for (int i = 0; i < n; ++i) b = std::max(b, m->slot_bound[i]);
   return b;
+}
+
+// ---- KV page pool --------------------------------------------------------
+// A slot holds pages for its blocks 0 .. n-1 (positions 0 .. 64 n - 1); pages
+// come from a free stack and return to it when the slot is released or
+// prefilled anew.  Table updates are queued and written by small kernels on
+// the call's stream before its work.
+struct PageUpdates {
+  std::vector<std::pair<int, int>> v;  // (table index, page)
+};
+
+int pages_for(const ocrdec_model* m, int n_pos) {
+  return (std::min(n_pos, m->cfg.max_positions) + KV_PAGE - 1) / KV_PAGE;
+}
+
+void flush_pages(ocrdec_model* m, hipStream_t s, PageUpdates& u) {
+  // an entry updated twice (a slot released, then given pages again) keeps
+  // its last value: one launch writes each entry once, since its threads
+  // store in no set order
+  std::vector<std::pair<int, int>> last;
+  std::unordered_map<int, size_t> at;
+  last.reserve(u.v.size());
+  for (const auto& e : u.v) {
+    auto it = at.find(e.first);
+    if (it != at.end()) {
+      last[it->second].second = e.second;
+    } else {
+      at.emplace(e.first, last.size());
+      last.push_back(e);
+    }
+  }
+  int* table = reinterpret_cast<int*>(m->state + m->p.s_table);
+  for (size_t i = 0; i < last.size(); i += PAGESET_N) {
+    PageSet ps{};
+    ps.n = (int)std::min<size_t>(PAGESET_N, last.size() - i);
+    for (int j = 0; j < ps.n; ++j) {
+      ps.idx[j] = last[i + j].first;
+      ps.page[j] = last[i + j].second;
+    }
+    launch_set_pages(s, table, ps);
+  }
+  u.v.clear();
+}
+
+void release_pages(ocrdec_model* m, int slot, PageUpdates& u) {
+  std::vector<int>& own = m->slot_pages[slot];
+  for (size_t j = 0; j < own.size(); ++j) {
+    m->free_pages.push_back(own[j]);
+    u.v.emplace_back(slot * m->p.max_blocks + (int)j, -1);
+  }
+  own.clear();
+}
+
+// Pages for positions 0 .. n_pos - 1 of slot; false (nothing taken) if the
+// pool cannot supply them.
+bool grow_pages(ocrdec_model* m, int slot, int n_pos, PageUpdates& u) {
+  std::vector<int>& own = m->slot_pages[slot];
+  const int need = pages_for(m, n_pos);
+  if (need <= (int)own.size()) return true;
+  if ((size_t)(need - (int)own.size()) > m->free_pages.size()) return false;
+  while ((int)own.size() < need) {
+    const int pg = m->free_pages.back();
+    m->free_pages.pop_back();
+    u.v.emplace_back(slot * m->p.max_blocks + (int)own.size(), pg);
+    own.push_back(pg);
+  }
+  return true;
+}
+
+// Every slot a decode call may touch (0 .. B-1, or every slot that holds
+// pages when the call maps slots on the device) gets pages through its bound
+// + extra positions; if the pool cannot supply all of them, nothing is taken.
+int ensure_pages(ocrdec_model* m, hipStream_t s, int B, const int32_t* slots, int extra) {
+  const int n = slots ? m->cfg.max_batch : B;
+  long need = 0;
+  for (int i = 0; i < n; ++i) {
+    if (slots && m->slot_pages[i].empty()) continue;
+    need += std::max(0, pages_for(m, m->slot_bound[i] + extra) - (int)m->slot_pages[i].size());
+  }
+  if (need == 0) return OCRDEC_OK;
+  if (need > (long)m->free_pages.size())
+    return fail(OCRDEC_ECAPACITY, "KV page pool exhausted: the call needs " + std::to_string(need) + " more pages, " +
+                                      std::to_string(m->free_pages.size()) +
+                                      " are free (release finished slots with ocrdec_release_slot)");
+  PageUpdates u;
+  for (int i = 0; i < n; ++i)
+    if (!(slots && m->slot_pages[i].empty())) grow_pages(m, i, m->slot_bound[i] + extra, u);
+  flush_pages(m, s, u);
+  return OCRDEC_OK;
 }
 
 void timing_mark(ocrdec_model* m, hipStream_t s) {
@@ -381,21 +480,28 @@ void dense_gemv(ocrdec_model* m, hipStream_t s, int dp, int K, Epi epi, const fl
   launch_gemv<T>(s, K, epi, a, lda, gain, m->cfg.norm_eps, W0, W1, N, M, out, ldo);
 }
 
+// The paged KV cache of verifier layer l (l < 0: the draft block's).
+template <typename T>
+KvView<T> kv_view(const ocrdec_model* m, int l) {
+  char* base = m->state + (l < 0 ? m->p.s_dkv : m->p.s_kv + (size_t)l * m->p.kv_layer_elems * m->p.esz);
+  return KvView<T>{reinterpret_cast<T*>(base), reinterpret_cast<const int*>(m->state + m->p.s_table),
+                   m->p.max_blocks, m->cfg.max_positions};
+}
+
 template <typename T>
 void dense_qkv(ocrdec_model* m, hipStream_t s, int dp, const float* x, const float* gain, const T* W, int M,
-               RowPlan plan, T* kv) {
+               RowPlan plan, KvView<T> kv) {
   if constexpr (std::is_same<T, bf16>::value) {
     if (dp == DENSE_STRIP) {
-      launch_qkv_rope_mfma(s, x, gain, m->cfg.norm_eps, W, M, plan, m->b.q, kv, m->cfg.max_positions, m->rope,
-                           m->b.rscale);
+      launch_qkv_rope_mfma(s, x, gain, m->cfg.norm_eps, W, M, plan, m->b.q, kv, m->rope, m->b.rscale);
       return;
     }
     if (dp == DENSE_KSPLIT) {
-      launch_qkv_rope_ks(s, x, gain, m->cfg.norm_eps, W, M, plan, m->b.q, kv, m->cfg.max_positions, m->rope);
+      launch_qkv_rope_ks(s, x, gain, m->cfg.norm_eps, W, M, plan, m->b.q, kv, m->rope);
       return;
     }
   }
-  launch_qkv_rope<T>(s, x, gain, m->cfg.norm_eps, W, M, plan, m->b.q, kv, m->cfg.max_positions, m->rope);
+  launch_qkv_rope<T>(s, x, gain, m->cfg.norm_eps, W, M, plan, m->b.q, kv, m->rope);
 }
 
 // The rest of the MoE half of layer l (vector path, M <= 8), after the router
@@ -410,13 +516,13 @@ void moe_experts(ocrdec_model* m, hipStream_t s, int l, int M, const RouteTap& t
 // Attention of the pass's rows into b.attn: the prefill attention for prefix
 // entries, else split-KV decode attention.
 template <typename T>
-void attention(ocrdec_model* m, hipStream_t s, PassPath pp, const float* q, const T* kv, RowPlan plan, int B,
+void attention(ocrdec_model* m, hipStream_t s, PassPath pp, const float* q, KvView<T> kv, RowPlan plan, int B,
                int nch) {
   if (pp.prefill) {
-    launch_attention_prefill<T>(s, q, kv, m->cfg.max_positions, plan, B, m->b.attn);
+    launch_attention_prefill<T>(s, q, kv, plan, B, m->b.attn);
     return;
   }
-  launch_attention<T>(s, q, kv, m->cfg.max_positions, plan, B, nch, m->p.tiles_per_chunk, m->b.part, m->b.attn);
+  launch_attention<T>(s, q, kv, plan, B, nch, m->p.tiles_per_chunk, m->b.part, m->b.attn);
 }
 
 template <typename T>
@@ -424,7 +530,7 @@ void verifier_layers(ocrdec_model* m, hipStream_t s, PassPath pp, int M, int B, 
                      const float* rlog) {
   const ocrdec_config& c = m->cfg;
   for (int l = 0; l < c.n_layers; ++l) {
-    T* kvl = static_cast<T*>((void*)(m->state + m->p.s_kv)) + (size_t)l * m->p.kv_layer_elems;
+    const KvView<T> kvl = kv_view<T>(m, l);
     dense_qkv<T>(m, s, pp.dense, m->b.x, wvec(m, lw(m, l, L_ANORM)), wmat<T>(m, lw(m, l, L_QKV)), M, plan, kvl);
     attention<T>(m, s, pp, m->b.q, kvl, plan, B, nch);
     dense_gemv<T>(m, s, pp.dense, QD, EPI_ADD, m->b.attn, QD, nullptr, wmat<T>(m, lw(m, l, L_WO)), nullptr, D, M,
@@ -469,7 +575,7 @@ void draft_layer(ocrdec_model* m, hipStream_t s, PassPath pp, int M, int B, RowP
                  bool fused_in) {
   const ocrdec_config& c = m->cfg;
   const int mx = pp.dense;
-  T* dkv = static_cast<T*>((void*)(m->state + m->p.s_dkv));
+  const KvView<T> dkv = kv_view<T>(m, -1);
   if (!fused_in)
     dense_gemv<T>(m, s, mx, 2 * D, EPI_STORE, m->b.cat, 2 * D, nullptr, wmat<T>(m, dw(m, D_FUSE)), nullptr, D, M, u,
                   D);
@@ -684,6 +790,10 @@ int ocrdec_create(const ocrdec_config* cfg, const void* const* weight_ptrs, int 
   m->b = bind_workspace(m->ws, p, mb);
   int* misc = m->b.mb.n_act;
   m->slot_bound.assign(cfg->max_batch, 0);
+  m->slot_pages.assign(cfg->max_batch, {});
+  m->free_pages.reserve(p.n_pages);
+  m->free_pages.resize(p.n_pages);
+  for (int i = 0; i < p.n_pages; ++i) m->free_pages[i] = p.n_pages - 1 - i;  // page 0 is taken first
   m->taps = ocrdec_taps{};
   m->step_tap = StepTap{};
   m->launch_fail = nullptr;
@@ -714,6 +824,8 @@ int ocrdec_create(const ocrdec_config* cfg, const void* const* weight_ptrs, int 
   if (err == hipSuccess) err = hipMemsetAsync(m->b.mb.stats, 0, 64, s);
   if (err == hipSuccess) err = hipMemsetAsync(m->b.sync, 0, (size_t)MOE_SYNC_WORDS * 4, s);
   if (err == hipSuccess) err = hipMemsetAsync(m->state + p.s_ints, 0, p.s_hbuf - p.s_ints, s);
+  if (err == hipSuccess)  // every table entry -1: no page
+    err = hipMemsetAsync(m->state + p.s_table, 0xff, (size_t)cfg->max_batch * p.max_blocks * 4, s);
   if (err == hipSuccess) {
     launch_rope_table(s, cfg->max_positions, cfg->rope_theta, reinterpret_cast<float2*>(m->state + p.s_rope));
     err = hipGetLastError();
@@ -755,6 +867,24 @@ int ocrdec_prefill(ocrdec_model* m, void* stream, int B, const int32_t* slots_ho
       return fail(OCRDEC_ECAPACITY, "prefix + max_k + 1 exceeds max_positions");
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
+  {  // the slots' old pages go back to the pool, then pages for the prefixes
+    long need = 0, have = (long)m->free_pages.size();
+    for (int b = 0; b < B; ++b) {
+      need += pages_for(m, n_vision_host[b] + n_prompt_host[b]);
+      have += (long)m->slot_pages[slots_host ? slots_host[b] : b].size();
+    }
+    if (need > have)
+      return fail(OCRDEC_ECAPACITY, "KV page pool exhausted: the prefixes need " + std::to_string(need) +
+                                        " pages, " + std::to_string(have) + " are free or held by these slots");
+    PageUpdates u;
+    for (int b = 0; b < B; ++b) release_pages(m, slots_host ? slots_host[b] : b, u);
+    for (int b = 0; b < B; ++b) {
+      const int slot = slots_host ? slots_host[b] : b;
+      m->slot_bound[slot] = 0;
+      grow_pages(m, slot, n_vision_host[b] + n_prompt_host[b], u);
+    }
+    flush_pages(m, s, u);
+  }
   if (m->cfg.dtype == OCRDEC_BF16)
     return do_prefill<bf16>(m, s, B, slots_host, vision, nv_stride, n_vision_host, prompt, np_stride, n_prompt_host,
                             pending_out);
@@ -770,6 +900,7 @@ int ocrdec_draft(ocrdec_model* m, void* stream, int B, const int32_t* slots, int
   if (!slots && call_bound(m, B, slots) + K > m->cfg.max_positions)
     return fail(OCRDEC_ECAPACITY, "positions would exceed max_positions");
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((rc = ensure_pages(m, s, B, slots, K + 1)) != OCRDEC_OK) return rc;
   if (m->cfg.dtype == OCRDEC_BF16) return do_draft<bf16>(m, s, B, slots, K, draft_out);
   return do_draft<float>(m, s, B, slots, K, draft_out);
 }
@@ -782,6 +913,7 @@ int ocrdec_verify(ocrdec_model* m, void* stream, int B, const int32_t* slots, in
   if (!slots && call_bound(m, B, slots) + K + 1 > m->cfg.max_positions)
     return fail(OCRDEC_ECAPACITY, "positions would exceed max_positions");
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((rc = ensure_pages(m, s, B, slots, K + 1)) != OCRDEC_OK) return rc;
   if (m->cfg.dtype == OCRDEC_BF16) return do_verify<bf16>(m, s, B, slots, K, draft, greedy_out, logits_out);
   return do_verify<float>(m, s, B, slots, K, draft, greedy_out, logits_out);
 }
@@ -866,6 +998,8 @@ int ocrdec_decode_steps(ocrdec_model* m, void* stream, int B, const int32_t* slo
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (!m->capture_stream && hipStreamCreateWithFlags(&m->capture_stream, hipStreamNonBlocking) != hipSuccess)
     return fail(OCRDEC_EHIP, "creating the capture stream failed");
+  // pages for every step of the call, before any of them runs
+  if ((rc = ensure_pages(m, s, B, slots, std::min(n_steps, m->cfg.max_positions) * (K + 1))) != OCRDEC_OK) return rc;
   for (int step = 0; step < n_steps; ++step) {
     const int bound = call_bound(m, B, slots);
     if (!slots && bound + K + 1 > m->cfg.max_positions)
@@ -960,6 +1094,8 @@ int ocrdec_decode_steps_noalloc(ocrdec_model* m, void* stream, int B, const int3
   m->b = bind_workspace(m->scratch, dp, B);
   launch_fill_i32(s, reinterpret_cast<int*>(m->b.mb.stats), 2, 0);  // the expert counter starts at zero
   launch_fill_i32(s, reinterpret_cast<int*>(m->b.sync), MOE_SYNC_WORDS, 0);  // and the MoE counters
+  // pages for every step of the call (the pool is host-side: no device allocation)
+  if ((rc = ensure_pages(m, s, B, slots, std::min(n_steps, m->cfg.max_positions) * (K + 1))) != OCRDEC_OK) return rc;
   for (int step = 0; step < n_steps; ++step) {
     if (!slots && call_bound(m, B, slots) + K + 1 > m->cfg.max_positions)
       return fail(OCRDEC_ECAPACITY, "positions would exceed max_positions");
@@ -1028,6 +1164,23 @@ int ocrdec_set_router_logits(ocrdec_model* m, const float* logits) {
   return OCRDEC_OK;
 }
 
+int ocrdec_release_slot(ocrdec_model* m, void* stream, int slot) {
+  if (!m) return fail(OCRDEC_EINVAL, "model is null");
+  if (slot < 0 || slot >= m->cfg.max_batch) return fail(OCRDEC_EINVAL, "slot out of range");
+  PageUpdates u;
+  release_pages(m, slot, u);
+  m->slot_bound[slot] = 0;
+  flush_pages(m, static_cast<hipStream_t>(stream), u);
+  return hip_check(m, "ocrdec_release_slot");
+}
+
+int ocrdec_kv_pages(ocrdec_model* m, int* total, int* free_pages) {
+  if (!m) return fail(OCRDEC_EINVAL, "model is null");
+  if (total) *total = m->p.n_pages;
+  if (free_pages) *free_pages = (int)m->free_pages.size();
+  return OCRDEC_OK;
+}
+
 int ocrdec_load_sequence(ocrdec_model* m, void* stream, int slot, int n_pos, int pending_token, const void* kv) {
   (void)hipGetLastError();
   if (!m || !kv) return fail(OCRDEC_EINVAL, "model or kv is null");
@@ -1036,17 +1189,21 @@ int ocrdec_load_sequence(ocrdec_model* m, void* stream, int slot, int n_pos, int
     return fail(OCRDEC_ECAPACITY, "n_pos + max_k + 1 exceeds max_positions");
   if (pending_token < 0 || pending_token >= m->cfg.vocab) return fail(OCRDEC_EINVAL, "pending_token out of range");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const size_t esz = m->p.esz, mp = (size_t)m->cfg.max_positions;
-  const char* src = static_cast<const char*>(kv);
+  {
+    if (pages_for(m, n_pos) > (int)(m->free_pages.size() + m->slot_pages[slot].size()))
+      return fail(OCRDEC_ECAPACITY, "KV page pool exhausted: the sequence needs more pages than are free");
+    PageUpdates u;
+    release_pages(m, slot, u);
+    m->slot_bound[slot] = 0;
+    grow_pages(m, slot, n_pos, u);
+    flush_pages(m, s, u);
+  }
+  const size_t layer_src = (size_t)2 * NH * n_pos * HD;  // elements of one layer in the source
   for (int l = 0; l < m->cfg.n_layers; ++l) {
-    char* dst = m->state + m->p.s_kv + ((size_t)l * m->p.kv_layer_elems + (size_t)slot * 2 * NH * mp * HD) * esz;
-    // [K|V][head] planes: n_pos rows of HD in the source, max_positions rows in the cache
-    for (int j = 0; j < 2 * NH; ++j) {
-      const hipError_t e = hipMemcpyAsync(dst + (size_t)j * mp * HD * esz,
-                                          src + (((size_t)l * 2 * NH + j) * n_pos) * HD * esz,
-                                          (size_t)n_pos * HD * esz, hipMemcpyDeviceToDevice, s);
-      if (e != hipSuccess) return fail(OCRDEC_EHIP, std::string("hipMemcpyAsync: ") + hipGetErrorString(e));
-    }
+    if (m->cfg.dtype == OCRDEC_BF16)
+      launch_load_kv<bf16>(s, static_cast<const bf16*>(kv) + l * layer_src, n_pos, kv_view<bf16>(m, l), slot);
+    else
+      launch_load_kv<float>(s, static_cast<const float*>(kv) + l * layer_src, n_pos, kv_view<float>(m, l), slot);
   }
   launch_set_sequence(s, slot, n_pos, pending_token, m->sv);
   m->slot_bound[slot] = n_pos;

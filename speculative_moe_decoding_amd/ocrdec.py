@@ -26,7 +26,7 @@ SYMBOLS = (
     "ocrdec_set_taps", "ocrdec_expert_timing", "ocrdec_expert_stats", "ocrdec_replay_expert_gate_up",
     "ocrdec_decode_steps", "ocrdec_sync_positions", "ocrdec_load_sequence", "ocrdec_set_router_logits",
     "ocrdec_read_probe", "ocrdec_last_error", "ocrdec_decode_steps_noalloc", "ocrdec_set_moe_launches",
-    "ocrdec_moe_grid",
+    "ocrdec_moe_grid", "ocrdec_release_slot", "ocrdec_kv_pages",
 )
 
 
@@ -35,7 +35,7 @@ class ocrdec_config(ctypes.Structure):
                                             "top_k", "d_expert", "d_draft_ffn", "vocab")] + [
         ("rope_theta", ctypes.c_float), ("norm_eps", ctypes.c_float), ("dtype", ctypes.c_int),
         ("max_batch", ctypes.c_int), ("max_k", ctypes.c_int), ("max_positions", ctypes.c_int),
-        ("path", ctypes.c_int)]
+        ("path", ctypes.c_int), ("kv_pages", ctypes.c_int)]
 
 
 class ocrdec_controlled_cfg(ctypes.Structure):
@@ -92,6 +92,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "ocrdec_set_router_logits": (I, [P, P]),
         "ocrdec_set_moe_launches": (I, [P, I]),
         "ocrdec_moe_grid": (I, [P]),
+        "ocrdec_release_slot": (I, [P, P, I]),
+        "ocrdec_kv_pages": (I, [P, ctypes.POINTER(I), ctypes.POINTER(I)]),
         "ocrdec_read_probe": (I, [P, P, ctypes.c_size_t, I, I, P]),
         "ocrdec_last_error": (ctypes.c_char_p, []),
     }
@@ -108,11 +110,12 @@ def _check(fn: str, rc: int) -> None:
         raise OcrdecError(fn, rc, load_library().ocrdec_last_error().decode())
 
 
-def make_config(cfg, max_batch: int, max_k: int, max_positions: int, path: int = 0) -> ocrdec_config:
+def make_config(cfg, max_batch: int, max_k: int, max_positions: int, path: int = 0,
+                kv_pages: int = 0) -> ocrdec_config:
     return ocrdec_config(cfg.n_layers, cfg.d_model, cfg.n_heads, cfg.head_dim, cfg.n_experts, cfg.n_shared,
                          cfg.top_k, cfg.d_expert, cfg.d_draft_ffn, cfg.vocab, float(cfg.rope_theta),
                          float(cfg.norm_eps), OCRDEC_BF16 if cfg.dtype == "bf16" else OCRDEC_F32,
-                         max_batch, max_k, max_positions, path)
+                         max_batch, max_k, max_positions, path, kv_pages)
 
 
 def _ptr(t) -> Optional[int]:
@@ -180,6 +183,17 @@ def ocrdec_sync_positions(h, stream: int):
 def ocrdec_load_sequence(h, stream: int, slot: int, n_pos: int, pending_token: int, kv) -> None:
     _check("ocrdec_load_sequence", load_library().ocrdec_load_sequence(h, stream, slot, n_pos, pending_token,
                                                                           kv.data_ptr()))
+
+
+def ocrdec_release_slot(h, stream: int, slot: int) -> None:
+    _check("ocrdec_release_slot", load_library().ocrdec_release_slot(h, stream, slot))
+
+
+def ocrdec_kv_pages(h):
+    """(pages in the pool, free pages)."""
+    total, free = ctypes.c_int(0), ctypes.c_int(0)
+    _check("ocrdec_kv_pages", load_library().ocrdec_kv_pages(h, ctypes.byref(total), ctypes.byref(free)))
+    return total.value, free.value
 
 
 def ocrdec_set_router_logits(h, logits=None) -> None:
@@ -255,13 +269,13 @@ class Decoder:
     (torch allocations) and drives the four decode calls on one stream."""
 
     def __init__(self, cfg, weight_arrays: List[np.ndarray], max_batch: int, max_k: int, max_positions: int,
-                 device: str = "cuda", path: int = 0):
+                 device: str = "cuda", path: int = 0, kv_pages: int = 0):
         import torch
         self.torch = torch
         load_library()
         self.cfg = cfg
         self.device = torch.device(device)
-        self.c = make_config(cfg, max_batch, max_k, max_positions, path)
+        self.c = make_config(cfg, max_batch, max_k, max_positions, path, kv_pages)
         n = ocrdec_num_weights(self.c)
         if n != len(weight_arrays):
             raise ValueError(f"expected {n} weight tensors, got {len(weight_arrays)}")
@@ -287,6 +301,14 @@ class Decoder:
             self.close()
         except Exception:
             pass
+
+    def release(self, slot: int):
+        """Return the KV pages of ``slot`` to the pool (prefill it before its next decode)."""
+        ocrdec_release_slot(self.h, self.stream, slot)
+
+    def kv_pages(self):
+        """(pages in the KV pool, free pages); a page holds 64 positions of one sequence."""
+        return ocrdec_kv_pages(self.h)
 
     # -- helpers -------------------------------------------------------------
     def i32(self, *shape):
@@ -594,6 +616,7 @@ class Decoder:
             for s in done:
                 results[slot_page[s]] = host[s, :n_out[slot_page[s]]].copy()
                 slot_page[s] = -1
+                self.release(s)  # its KV pages go back to the pool at once
             free += done
             if queue < n and (len(free) >= refill_min or all(p < 0 for p in slot_page)):
                 refill(free)

@@ -107,6 +107,25 @@ def test_rejects_bad_paths_and_null_handles(lib):
     assert lib.ocrdec_read_probe(None, None, 256, 1, 1, None) == E
     assert lib.ocrdec_set_moe_launches(None, 1) == E
     assert lib.ocrdec_moe_grid(None) == E
+    assert lib.ocrdec_release_slot(None, None, 0) == E
+    assert lib.ocrdec_kv_pages(None, None, None) == E
+
+
+def test_kv_page_pool_sizes_the_state(lib):
+    """The KV cache is a pool of pages of 64 positions: its size follows
+    kv_pages (0 = every slot at max_positions), clipped to that full size;
+    a negative pool is refused."""
+    full = ocrdec.ocrdec_state_bytes(ocrdec.make_config(synth.FULL, 8, 3, 2048))
+    assert ocrdec.ocrdec_state_bytes(ocrdec.make_config(synth.FULL, 8, 3, 2048, kv_pages=8 * 32)) == full
+    assert ocrdec.ocrdec_state_bytes(ocrdec.make_config(synth.FULL, 8, 3, 2048, kv_pages=10 ** 6)) == full
+    small = ocrdec.ocrdec_state_bytes(ocrdec.make_config(synth.FULL, 8, 3, 2048, kv_pages=64))
+    esz = 2 if synth.FULL.dtype == "bf16" else 4
+    page = 2 * synth.FULL.n_heads * 64 * synth.FULL.head_dim * esz  # keys and values of one page, one layer
+    # every verifier layer and the draft block hold the pages (256-byte alignment per region)
+    saved = (8 * 32 - 64) * page * (synth.FULL.n_layers + 1)
+    assert abs((full - small) - saved) < 4096
+    assert ocrdec.ocrdec_state_bytes(ocrdec.make_config(synth.FULL, 8, 3, 2048, kv_pages=-1)) == 0
+    assert "kv_pages" in lib.ocrdec_last_error().decode()
 
 
 def test_prefill_argument_checks_need_no_device(lib):
