@@ -176,6 +176,9 @@ def main() -> int:
                     help="base page, vector path: the MoE half of each verifier layer as one persistent "
                          "launch after the router logits, or as the five launches router logits, routing, "
                          "gate/up, down, combine (the same bits)")
+    ap.add_argument("--kv-pages", type=int, default=0,
+                    help="stream workload: KV page pool size in pages of 64 positions (0: every slot at the "
+                         "longest sequence)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 512 MiB device copy (calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
@@ -683,7 +686,12 @@ def bench_stream(args) -> int:
     pages = synth.make_pages(cfg, wl["input_seed"] + 100, prefix.tolist(), [wl["n_prompt"]] * n, n_out.tolist())
     check = 8
     max_pos = min(32768, int(prefix.max()) + wl["n_prompt"] + int(n_out.max()) + (check + 2) * (K + 1) + 16)
-    dec = ocrdec.Decoder(cfg, w.device_arrays(), max_batch=C, max_k=K, max_positions=max_pos)
+    dec = ocrdec.Decoder(cfg, w.device_arrays(), max_batch=C, max_k=K, max_positions=max_pos,
+                         kv_pages=args.kv_pages)
+    n_pages, _ = dec.kv_pages()
+    page_bytes = 2 * cfg.n_heads * 64 * cfg.head_dim * 2 * (cfg.n_layers + 1)  # bf16 keys + values, all layers
+    log(f"KV pool: {n_pages} pages of 64 positions, {n_pages * page_bytes / 1e9:.2f} GB "
+        f"(every slot at max_positions {max_pos}: {C * -(-max_pos // 64) * page_bytes / 1e9:.2f} GB)")
     t = time.time()
     ar, _ = dec.generate_stream(pages, n_out + K + 2, 0, C, check_every=check, refill_min=8)
     torch.cuda.synchronize()
@@ -717,7 +725,8 @@ def bench_stream(args) -> int:
                                + (f", scaled x{args.out_scale}" if args.out_scale != 1.0 else "")
                                + ") through 32 slots, refilled 8 at a time, FastMTP K=1, controlled "
                                "acceptance 0.829",
-                   "pages": n, "concurrency": C, "K": K, "refill_min": refill_min},
+                   "pages": n, "concurrency": C, "K": K, "refill_min": refill_min, "kv_pages": n_pages,
+                   "kv_cache_GB": round(n_pages * page_bytes / 1e9, 3)},
         "tokens_per_s": round(n_tok / el, 1), "seconds": round(el, 3), "lossless_vs_ar": bool(lossless),
         "roofline": None, "cpu_baseline": None}), flush=True)
     return 0

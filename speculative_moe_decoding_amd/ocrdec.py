@@ -541,9 +541,13 @@ class Decoder:
         flight, one state slot each; when a page has its n_out[i] tokens, its slot is
         prefilled with the next queued page (all refills of a check in one prefill call;
         with refill_min > 1, free slots wait until that many are free or nothing else
-        runs, so prefills run several pages per pass) while the other slots keep decoding.  ``trace`` (device int32 [n_pages, T])
-        switches on the controlled drafts (each page reads its own row).  Returns (list
-        of token arrays per page, total sequence-steps run)."""
+        runs, so prefills run several pages per pass) while the other slots keep decoding.
+        A page is admitted only while the KV page pool can hold every page in flight
+        at its full length (prefix + n_out[i] + the positions a check can run past
+        it), in queue order; a finished page's slot returns its pages at once.
+        ``trace`` (device int32 [n_pages, T]) switches on the controlled drafts (each
+        page reads its own row).  Returns (list of token arrays per page, total
+        sequence-steps run)."""
         torch = self.torch
         n = len(pages)
         n_out = np.asarray(n_out, dtype=np.int64)
@@ -557,13 +561,21 @@ class Decoder:
         results = [None] * n
         queue = 0
         seq_steps = 0
+        pool, _ = self.kv_pages()
+        run_past = (check_every + 2) * (K + 1) + 1
+        need = [-(-(pg.prefix_len + int(n_out[i]) + run_past) // 64) for i, pg in enumerate(pages)]
+        if max(need) > pool:
+            raise ValueError(f"a page needs {max(need)} KV pages, the pool has {pool}")
+        reserved = 0
 
         def refill(free):
-            nonlocal queue
+            """Admit queued pages into the free slots; returns the slots left free."""
+            nonlocal queue, reserved
             take = []
             for s in free:
-                if queue < n:
+                if queue < n and reserved + need[queue] <= pool:
                     slot_page[s] = queue
+                    reserved += need[queue]
                     queue += 1
                     take.append(s)
                 else:
@@ -575,9 +587,9 @@ class Decoder:
                     out_full[s, 0] = pend[j]
                     if tr_full is not None:
                         tr_full[s].copy_(trace[slot_page[s]])
+            return [s for s in free if s not in take]
 
-        refill(list(range(C)))
-        free = []
+        free = refill(list(range(C)))
         while any(p >= 0 for p in slot_page):
             active = np.array([s for s in range(C) if slot_page[s] >= 0], dtype=np.int64)
             Bb = len(active)
@@ -615,10 +627,10 @@ class Decoder:
             host = out_full.cpu().numpy()
             for s in done:
                 results[slot_page[s]] = host[s, :n_out[slot_page[s]]].copy()
+                reserved -= need[slot_page[s]]
                 slot_page[s] = -1
                 self.release(s)  # its KV pages go back to the pool at once
             free += done
             if queue < n and (len(free) >= refill_min or all(p < 0 for p in slot_page)):
-                refill(free)
-                free = []
+                free = refill(free)
         return results, seq_steps
