@@ -255,16 +255,17 @@ __device__ __forceinline__ void gate_up_pass(const bf16* const (&w)[2], const fl
   }
 }
 
-// Block (x, y).  DEEP (prefill passes): work item y, an expert and at most
-// ITEM_PAIRS of its pairs, so that a shared expert's rows of a long prefix
-// spread over several blocks.  Decode calls: expert slot y (the shared
-// experts' blocks load their weights with no routing read).  Either way,
-// passes of 64 pairs.
-template <bool DEEP, bool CACHED>
+// Block (x, y).  ITEMS (prefill passes, and decode calls of more than 64
+// rows): work item y, an expert and at most ITEM_PAIRS of its pairs, so that
+// a shared expert's many rows spread over several blocks.  Otherwise expert
+// slot y (the shared experts' blocks load their weights with no routing
+// read).  Either way, passes of 64 pairs with the same arithmetic per row.
+// DEEP: the deeper load pipeline (prefill passes).
+template <bool ITEMS, bool DEEP, bool CACHED>
 __global__ __launch_bounds__(256) void k_expert_gate_up_mfma(const bf16* __restrict__ wg,
                                                              const bf16* __restrict__ wu, int M, MoeBufs mb) {
   __shared__ MfChunk buf[2][2];
-  const int4 it = DEEP ? mb.items[blockIdx.y] : expert_work(mb, blockIdx.y, M);
+  const int4 it = ITEMS ? mb.items[blockIdx.y] : expert_work(mb, blockIdx.y, M);
   const int e = it.x;
   if (e < 0) return;
   const int j0 = blockIdx.x * 64 + wave_id() * 16;
@@ -300,10 +301,10 @@ __device__ __forceinline__ void down_pass(const bf16* const (&w)[1], const float
   }
 }
 
-template <bool DEEP, bool CACHED>
+template <bool ITEMS, bool DEEP, bool CACHED>
 __global__ __launch_bounds__(256) void k_expert_down_mfma(const bf16* __restrict__ wd, int M, MoeBufs mb) {
   __shared__ MfChunk buf[2][2];
-  const int4 it = DEEP ? mb.items[blockIdx.y] : expert_work(mb, blockIdx.y, M);
+  const int4 it = ITEMS ? mb.items[blockIdx.y] : expert_work(mb, blockIdx.y, M);
   const int e = it.x;
   if (e < 0) return;
   const int n0 = blockIdx.x * 128 + wave_id() * 32;
@@ -316,16 +317,23 @@ __global__ __launch_bounds__(256) void k_expert_down_mfma(const bf16* __restrict
   }
 }
 
+// Decode calls of more than MF_ROWS rows take work items (the shared experts
+// then spread over several blocks instead of looping in one), with ordinary
+// weight loads, since a shared expert's blocks read the same strips.
 void launch_expert_gate_up_mfma(hipStream_t s, const bf16* wg, const bf16* wu, int M, const MoeBufs& mb, bool deep) {
-  const dim3 grid(DI / 64, deep ? expert_item_cap(M) : expert_slot_cap(M));
-  if (deep) hipLaunchKernelGGL((k_expert_gate_up_mfma<true, true>), grid, dim3(256), 0, s, wg, wu, M, mb);
-  else hipLaunchKernelGGL((k_expert_gate_up_mfma<false, false>), grid, dim3(256), 0, s, wg, wu, M, mb);
+  const bool items = deep || M > MF_ROWS;
+  const dim3 grid(DI / 64, items ? expert_item_cap(M) : expert_slot_cap(M));
+  if (deep) hipLaunchKernelGGL((k_expert_gate_up_mfma<true, true, true>), grid, dim3(256), 0, s, wg, wu, M, mb);
+  else if (items) hipLaunchKernelGGL((k_expert_gate_up_mfma<true, false, true>), grid, dim3(256), 0, s, wg, wu, M, mb);
+  else hipLaunchKernelGGL((k_expert_gate_up_mfma<false, false, false>), grid, dim3(256), 0, s, wg, wu, M, mb);
 }
 
 void launch_expert_down_mfma(hipStream_t s, const bf16* wd, int M, const MoeBufs& mb, bool deep) {
-  const dim3 grid(D / 128, deep ? expert_item_cap(M) : expert_slot_cap(M));
-  if (deep) hipLaunchKernelGGL((k_expert_down_mfma<true, true>), grid, dim3(256), 0, s, wd, M, mb);
-  else hipLaunchKernelGGL((k_expert_down_mfma<false, false>), grid, dim3(256), 0, s, wd, M, mb);
+  const bool items = deep || M > MF_ROWS;
+  const dim3 grid(D / 128, items ? expert_item_cap(M) : expert_slot_cap(M));
+  if (deep) hipLaunchKernelGGL((k_expert_down_mfma<true, true, true>), grid, dim3(256), 0, s, wd, M, mb);
+  else if (items) hipLaunchKernelGGL((k_expert_down_mfma<true, false, true>), grid, dim3(256), 0, s, wd, M, mb);
+  else hipLaunchKernelGGL((k_expert_down_mfma<false, false, false>), grid, dim3(256), 0, s, wd, M, mb);
 }
 
 // ---- dense layers on the matrix cores -------------------------------------
