@@ -237,14 +237,14 @@ __device__ __forceinline__ void mfma_pass(const bf16* const (&w)[NB], RowPtr row
 // Gate/up: block (x, slot s) computes units j0 .. j0+15, j0 = 64 x + 16 w, of
 // active expert s for every pair routed to it:
 // hx[pair][j] = silu(gate_j . b) * (up_j . b), b the pair's normalised row.
-template <int NT, bool DEEP, bool CACHED>
+template <int NT, bool DEEP, bool CACHED, int CT>
 __device__ __forceinline__ void gate_up_pass(const bf16* const (&w)[2], const float* __restrict__ bnorm,
                                              const int* __restrict__ perm, int kb, int rows, float* __restrict__ hx,
-                                             int j0, MfChunk (&buf)[2][2]) {
+                                             int j0, MfChunkT<CT> (&buf)[2][2]) {
   const int lane = lane_id();
   f32x4_v acc[NT][2][1];
   auto rowp = [=](int r) { return bnorm + (long)(perm[kb + r] / NSLOT) * D; };
-  mfma_pass<D, NT, 2, 1, 2, decltype(rowp), false, MF_MT, DEEP, CACHED>(w, rowp, rows, buf, acc);
+  mfma_pass<D, NT, 2, 1, 2, decltype(rowp), false, CT, DEEP, CACHED>(w, rowp, rows, buf, acc);
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
 #pragma unroll
@@ -260,33 +260,35 @@ __device__ __forceinline__ void gate_up_pass(const bf16* const (&w)[2], const fl
 // a shared expert's many rows spread over several blocks.  Otherwise expert
 // slot y (the shared experts' blocks load their weights with no routing
 // read).  Either way, passes of 64 pairs with the same arithmetic per row.
-// DEEP: the deeper load pipeline (prefill passes).
-template <bool ITEMS, bool DEEP, bool CACHED>
+// DEEP: the deeper load pipeline (prefill passes).  CT: row tiles per pass
+// (passes of 16 CT pairs; the LDS chunks are sized to them).
+template <bool ITEMS, bool DEEP, bool CACHED, int CT>
 __global__ __launch_bounds__(256) void k_expert_gate_up_mfma(const bf16* __restrict__ wg,
                                                              const bf16* __restrict__ wu, int M, MoeBufs mb) {
-  __shared__ MfChunk buf[2][2];
+  __shared__ MfChunkT<CT> buf[2][2];
   const int4 it = ITEMS ? mb.items[blockIdx.y] : expert_work(mb, blockIdx.y, M);
   const int e = it.x;
   if (e < 0) return;
   const int j0 = blockIdx.x * 64 + wave_id() * 16;
   const bf16* const w[2] = {wg + ((long)e * DI + j0) * D, wu + ((long)e * DI + j0) * D};
-  for (int kb = it.y; kb < it.z; kb += MF_ROWS) {
-    const int rows = min(MF_ROWS, it.z - kb);
-    if (rows <= 16) gate_up_pass<1, DEEP, CACHED>(w, mb.bnorm, mb.perm, kb, rows, mb.hx, j0, buf);
-    else if (rows <= 32) gate_up_pass<2, DEEP, CACHED>(w, mb.bnorm, mb.perm, kb, rows, mb.hx, j0, buf);
-    else gate_up_pass<4, DEEP, CACHED>(w, mb.bnorm, mb.perm, kb, rows, mb.hx, j0, buf);
+  for (int kb = it.y; kb < it.z; kb += 16 * CT) {
+    const int rows = min(16 * CT, it.z - kb);
+    if (CT == 1 || rows <= 16) gate_up_pass<1, DEEP, CACHED, CT>(w, mb.bnorm, mb.perm, kb, rows, mb.hx, j0, buf);
+    else if (CT == 2 || rows <= 32)
+      gate_up_pass<(CT < 2 ? CT : 2), DEEP, CACHED, CT>(w, mb.bnorm, mb.perm, kb, rows, mb.hx, j0, buf);
+    else gate_up_pass<CT, DEEP, CACHED, CT>(w, mb.bnorm, mb.perm, kb, rows, mb.hx, j0, buf);
   }
 }
 
 // Down: block (x, slot s) computes outputs n0 .. n0+31, n0 = 128 x + 32 w:
 // y[pair][n] = W_d[n] . hx[pair].
-template <int NT, bool DEEP, bool CACHED>
+template <int NT, bool DEEP, bool CACHED, int CT>
 __device__ __forceinline__ void down_pass(const bf16* const (&w)[1], const float* __restrict__ hx, int kb, int rows,
-                                          float* __restrict__ y, int n0, MfChunk (&buf)[2][2]) {
+                                          float* __restrict__ y, int n0, MfChunkT<CT> (&buf)[2][2]) {
   const int lane = lane_id();
   f32x4_v acc[NT][1][2];
   auto rowp = [=](int r) { return hx + (long)(kb + r) * DI; };
-  mfma_pass<DI, NT, 1, 2, 2, decltype(rowp), false, MF_MT, DEEP, CACHED>(w, rowp, rows, buf, acc);
+  mfma_pass<DI, NT, 1, 2, 2, decltype(rowp), false, CT, DEEP, CACHED>(w, rowp, rows, buf, acc);
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
 #pragma unroll
@@ -301,39 +303,60 @@ __device__ __forceinline__ void down_pass(const bf16* const (&w)[1], const float
   }
 }
 
-template <bool ITEMS, bool DEEP, bool CACHED>
+template <bool ITEMS, bool DEEP, bool CACHED, int CT>
 __global__ __launch_bounds__(256) void k_expert_down_mfma(const bf16* __restrict__ wd, int M, MoeBufs mb) {
-  __shared__ MfChunk buf[2][2];
+  __shared__ MfChunkT<CT> buf[2][2];
   const int4 it = ITEMS ? mb.items[blockIdx.y] : expert_work(mb, blockIdx.y, M);
   const int e = it.x;
   if (e < 0) return;
   const int n0 = blockIdx.x * 128 + wave_id() * 32;
   const bf16* const w[1] = {wd + ((long)e * D + n0) * DI};
-  for (int kb = it.y; kb < it.z; kb += MF_ROWS) {
-    const int rows = min(MF_ROWS, it.z - kb);
-    if (rows <= 16) down_pass<1, DEEP, CACHED>(w, mb.hx, kb, rows, mb.y, n0, buf);
-    else if (rows <= 32) down_pass<2, DEEP, CACHED>(w, mb.hx, kb, rows, mb.y, n0, buf);
-    else down_pass<4, DEEP, CACHED>(w, mb.hx, kb, rows, mb.y, n0, buf);
+  for (int kb = it.y; kb < it.z; kb += 16 * CT) {
+    const int rows = min(16 * CT, it.z - kb);
+    if (CT == 1 || rows <= 16) down_pass<1, DEEP, CACHED, CT>(w, mb.hx, kb, rows, mb.y, n0, buf);
+    else if (CT == 2 || rows <= 32) down_pass<(CT < 2 ? CT : 2), DEEP, CACHED, CT>(w, mb.hx, kb, rows, mb.y, n0, buf);
+    else down_pass<CT, DEEP, CACHED, CT>(w, mb.hx, kb, rows, mb.y, n0, buf);
   }
 }
 
 // Decode calls of more than MF_ROWS rows take work items (the shared experts
 // then spread over several blocks instead of looping in one), with ordinary
 // weight loads, since a shared expert's blocks read the same strips.
+// Row tiles per pass (CT) and weight-load kind of each use, as measured
+// best.  Decode gate/up: passes of 32 pairs (half the LDS: more workgroups per
+// compute unit keep more weight loads in flight), ordinary loads (a shared
+// expert's 64 rows take two passes over its strips).  Decode down: passes of
+// 64, non-temporal loads.  Prefill down: passes of 32 pairs.
+constexpr int GU_DEC_CT = 2;
+constexpr bool GU_DEC_CACHED = true;
+constexpr int DN_DEC_CT = 4;
+constexpr bool DN_DEC_CACHED = false;
+constexpr int GU_ITEM_CT = 4;  // work items: decode calls of more than 64 rows
+constexpr int DN_ITEM_CT = 4;
+constexpr int GU_DEEP_CT = 4;  // prefill passes
+constexpr int DN_DEEP_CT = 2;
 void launch_expert_gate_up_mfma(hipStream_t s, const bf16* wg, const bf16* wu, int M, const MoeBufs& mb, bool deep) {
   const bool items = deep || M > MF_ROWS;
   const dim3 grid(DI / 64, items ? expert_item_cap(M) : expert_slot_cap(M));
-  if (deep) hipLaunchKernelGGL((k_expert_gate_up_mfma<true, true, true>), grid, dim3(256), 0, s, wg, wu, M, mb);
-  else if (items) hipLaunchKernelGGL((k_expert_gate_up_mfma<true, false, true>), grid, dim3(256), 0, s, wg, wu, M, mb);
-  else hipLaunchKernelGGL((k_expert_gate_up_mfma<false, false, false>), grid, dim3(256), 0, s, wg, wu, M, mb);
+  if (deep)
+    hipLaunchKernelGGL((k_expert_gate_up_mfma<true, true, true, GU_DEEP_CT>), grid, dim3(256), 0, s, wg, wu, M, mb);
+  else if (items)
+    hipLaunchKernelGGL((k_expert_gate_up_mfma<true, false, true, GU_ITEM_CT>), grid, dim3(256), 0, s, wg, wu, M, mb);
+  else
+    hipLaunchKernelGGL((k_expert_gate_up_mfma<false, false, GU_DEC_CACHED, GU_DEC_CT>), grid, dim3(256), 0, s, wg,
+                       wu, M, mb);
 }
 
 void launch_expert_down_mfma(hipStream_t s, const bf16* wd, int M, const MoeBufs& mb, bool deep) {
   const bool items = deep || M > MF_ROWS;
   const dim3 grid(D / 128, items ? expert_item_cap(M) : expert_slot_cap(M));
-  if (deep) hipLaunchKernelGGL((k_expert_down_mfma<true, true, true>), grid, dim3(256), 0, s, wd, M, mb);
-  else if (items) hipLaunchKernelGGL((k_expert_down_mfma<true, false, true>), grid, dim3(256), 0, s, wd, M, mb);
-  else hipLaunchKernelGGL((k_expert_down_mfma<false, false, false>), grid, dim3(256), 0, s, wd, M, mb);
+  if (deep)
+    hipLaunchKernelGGL((k_expert_down_mfma<true, true, true, DN_DEEP_CT>), grid, dim3(256), 0, s, wd, M, mb);
+  else if (items)
+    hipLaunchKernelGGL((k_expert_down_mfma<true, false, true, DN_ITEM_CT>), grid, dim3(256), 0, s, wd, M, mb);
+  else
+    hipLaunchKernelGGL((k_expert_down_mfma<false, false, DN_DEC_CACHED, DN_DEC_CT>), grid, dim3(256), 0, s, wd, M,
+                       mb);
 }
 
 // ---- dense layers on the matrix cores -------------------------------------
@@ -735,14 +758,14 @@ __global__ __launch_bounds__(256) void k_lm_norm(const float* __restrict__ x, co
 // rows 64 x .. 64 x + 63 (16 per wavefront) for all M rows, passes of 64 rows,
 // and writes the best (value, lowest id) per row to part[row][x]; logits
 // optionally stored to logits[row][V].
-template <int NT, bool CACHED>
+template <int NT, bool CACHED, int CT>
 __device__ __forceinline__ void lm_pass(const bf16* const (&w)[1], const float* __restrict__ xn, int p0, int rows,
-                                        int vj, bool vok, int V, float* __restrict__ logits, float (&bv)[4][MF_ROWS],
-                                        int (&bi)[4][MF_ROWS], MfChunk (&buf)[2][1]) {
+                                        int vj, bool vok, int V, float* __restrict__ logits, float (&bv)[4][16 * CT],
+                                        int (&bi)[4][16 * CT], MfChunkT<CT> (&buf)[2][1]) {
   const int wave = wave_id(), lane = lane_id();
   f32x4_v acc[NT][1][1];
   auto rowp = [=](int r) { return xn + (long)(p0 + r) * D; };
-  mfma_pass<D, NT, 1, 1, 1, decltype(rowp), false, MF_MT, false, CACHED>(w, rowp, rows, buf, acc);
+  mfma_pass<D, NT, 1, 1, 1, decltype(rowp), false, CT, false, CACHED>(w, rowp, rows, buf, acc);
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
 #pragma unroll
@@ -764,15 +787,16 @@ __device__ __forceinline__ void lm_pass(const bf16* const (&w)[1], const float* 
   }
 }
 
-// CACHED (more than 64 rows): ordinary weight loads, so that the strip's
-// later passes find it in the caches.
-template <bool CACHED>
+// CACHED (more than one pass): ordinary weight loads, so that the strip's
+// later passes find it in the caches.  CT: row tiles per pass.
+template <bool CACHED, int CT>
 __global__ __launch_bounds__(256) void k_lmhead_mfma(const float* __restrict__ xn, const bf16* __restrict__ W,
                                                      int V, int M, float* __restrict__ part_val,
                                                      int* __restrict__ part_idx, float* __restrict__ logits) {
-  __shared__ MfChunk buf[2][1];
-  __shared__ float bv[4][MF_ROWS];
-  __shared__ int bi[4][MF_ROWS];
+  constexpr int RB = 16 * CT;
+  __shared__ MfChunkT<CT> buf[2][1];
+  __shared__ float bv[4][RB];
+  __shared__ int bi[4][RB];
   const int wave = wave_id(), lane = lane_id();
   const int nblk = gridDim.x;
   const int v0 = blockIdx.x * LM_ROWS_PER_BLOCK + wave * 16;
@@ -782,11 +806,11 @@ __global__ __launch_bounds__(256) void k_lmhead_mfma(const float* __restrict__ x
   const bf16* const w[1] = {W + (long)(shifted ? V - 16 : v0) * D};
   const int vj = (shifted ? V - 16 : v0) + (lane & 15);
   const bool vok = vj >= v0 && vj < V;
-  for (int p0 = 0; p0 < M; p0 += MF_ROWS) {
-    const int rows = min(MF_ROWS, M - p0);
-    if (rows <= 16) lm_pass<1, CACHED>(w, xn, p0, rows, vj, vok, V, logits, bv, bi, buf);
-    else if (rows <= 32) lm_pass<2, CACHED>(w, xn, p0, rows, vj, vok, V, logits, bv, bi, buf);
-    else lm_pass<4, CACHED>(w, xn, p0, rows, vj, vok, V, logits, bv, bi, buf);
+  for (int p0 = 0; p0 < M; p0 += RB) {
+    const int rows = min(RB, M - p0);
+    if (CT == 1 || rows <= 16) lm_pass<1, CACHED, CT>(w, xn, p0, rows, vj, vok, V, logits, bv, bi, buf);
+    else if (CT == 2 || rows <= 32) lm_pass<(CT < 2 ? CT : 2), CACHED, CT>(w, xn, p0, rows, vj, vok, V, logits, bv, bi, buf);
+    else lm_pass<CT, CACHED, CT>(w, xn, p0, rows, vj, vok, V, logits, bv, bi, buf);
     __syncthreads();
     if ((int)threadIdx.x < rows) {
       const int r = threadIdx.x;
@@ -801,15 +825,18 @@ __global__ __launch_bounds__(256) void k_lmhead_mfma(const float* __restrict__ x
   }
 }
 
+constexpr int LM_CT = 4;  // row tiles per pass of the LM head
 void launch_lmhead_mfma(hipStream_t s, const float* x, const int* cnt, int Q, bool last_valid, const float* gain,
                         float eps, const bf16* W, int V, int M, float* xn, float* part_val, int* part_idx,
                         float* logits, int* tok, int tok_stride) {
   hipLaunchKernelGGL(k_lm_norm, dim3((M + 3) / 4), dim3(256), 0, s, x, cnt, Q, (int)last_valid, gain, eps, M, xn);
   const int nb = lmhead_blocks(V);
-  if (M > MF_ROWS)
-    hipLaunchKernelGGL(k_lmhead_mfma<true>, dim3(nb), dim3(256), 0, s, xn, W, V, M, part_val, part_idx, logits);
+  if (M > 16 * LM_CT)
+    hipLaunchKernelGGL((k_lmhead_mfma<true, LM_CT>), dim3(nb), dim3(256), 0, s, xn, W, V, M, part_val, part_idx,
+                       logits);
   else
-    hipLaunchKernelGGL(k_lmhead_mfma<false>, dim3(nb), dim3(256), 0, s, xn, W, V, M, part_val, part_idx, logits);
+    hipLaunchKernelGGL((k_lmhead_mfma<false, LM_CT>), dim3(nb), dim3(256), 0, s, xn, W, V, M, part_val, part_idx,
+                       logits);
   if (tok != nullptr) launch_argmax_final(s, part_val, part_idx, nb, M, tok, tok_stride);
 }
 
