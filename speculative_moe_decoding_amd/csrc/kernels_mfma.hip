@@ -322,11 +322,14 @@ __global__ __launch_bounds__(256) void k_expert_down_mfma(const bf16* __restrict
 // Decode calls of more than MF_ROWS rows take work items (the shared experts
 // then spread over several blocks instead of looping in one), with ordinary
 // weight loads, since a shared expert's blocks read the same strips.
-// Row tiles per pass (CT) and weight-load kind of each use, as measured
-// best.  Decode gate/up: passes of 32 pairs (half the LDS: more workgroups per
-// compute unit keep more weight loads in flight), ordinary loads (a shared
-// expert's 64 rows take two passes over its strips).  Decode down: passes of
-// 64, non-temporal loads.  Prefill down: passes of 32 pairs.
+// Row tiles per pass (CT), weight-load kind and pipeline depth of each use, as
+// measured best.  Decode gate/up: passes of 32 pairs (half the LDS: more
+// workgroups per compute unit keep more weight loads in flight), ordinary
+// loads (a shared expert's 64 rows take two passes over its strips).  Decode
+// down: passes of 64, non-temporal loads.  Prefill passes (64-pair work
+// items, ordinary loads): passes of 64 with the two-chunk pipeline (the
+// deeper one costs registers, hence workgroups in flight, and measured slower
+// since the work items keep every block's pass short).
 constexpr int GU_DEC_CT = 2;
 constexpr bool GU_DEC_CACHED = true;
 constexpr int DN_DEC_CT = 4;
@@ -334,12 +337,15 @@ constexpr bool DN_DEC_CACHED = false;
 constexpr int GU_ITEM_CT = 4;  // work items: decode calls of more than 64 rows
 constexpr int DN_ITEM_CT = 4;
 constexpr int GU_DEEP_CT = 4;  // prefill passes
-constexpr int DN_DEEP_CT = 2;
+constexpr int DN_DEEP_CT = 4;
+constexpr bool GU_PF_DEEP = false;  // the deeper pipeline in prefill passes
+constexpr bool DN_PF_DEEP = false;
 void launch_expert_gate_up_mfma(hipStream_t s, const bf16* wg, const bf16* wu, int M, const MoeBufs& mb, bool deep) {
   const bool items = deep || M > MF_ROWS;
   const dim3 grid(DI / 64, items ? expert_item_cap(M) : expert_slot_cap(M));
   if (deep)
-    hipLaunchKernelGGL((k_expert_gate_up_mfma<true, true, true, GU_DEEP_CT>), grid, dim3(256), 0, s, wg, wu, M, mb);
+    hipLaunchKernelGGL((k_expert_gate_up_mfma<true, GU_PF_DEEP, true, GU_DEEP_CT>), grid, dim3(256), 0, s, wg, wu, M,
+                       mb);
   else if (items)
     hipLaunchKernelGGL((k_expert_gate_up_mfma<true, false, true, GU_ITEM_CT>), grid, dim3(256), 0, s, wg, wu, M, mb);
   else
@@ -351,7 +357,7 @@ void launch_expert_down_mfma(hipStream_t s, const bf16* wd, int M, const MoeBufs
   const bool items = deep || M > MF_ROWS;
   const dim3 grid(D / 128, items ? expert_item_cap(M) : expert_slot_cap(M));
   if (deep)
-    hipLaunchKernelGGL((k_expert_down_mfma<true, true, true, DN_DEEP_CT>), grid, dim3(256), 0, s, wd, M, mb);
+    hipLaunchKernelGGL((k_expert_down_mfma<true, DN_PF_DEEP, true, DN_DEEP_CT>), grid, dim3(256), 0, s, wd, M, mb);
   else if (items)
     hipLaunchKernelGGL((k_expert_down_mfma<true, false, true, DN_ITEM_CT>), grid, dim3(256), 0, s, wd, M, mb);
   else
@@ -380,6 +386,7 @@ struct QkvOut {
   const float2* rope;
 };
 
+constexpr bool DENSE_DEEP = true;  // the deeper pipeline in the strip GEMMs
 template <int K, int MODE, int NT>
 __device__ __forceinline__ void dense_mfma_rows(const float* __restrict__ a, long lda, const float* __restrict__ gain,
                                                 const bf16* const (&w)[(MODE == DM_SWIGLU || MODE == DM_QKV) ? 2 : 1],
@@ -390,8 +397,10 @@ __device__ __forceinline__ void dense_mfma_rows(const float* __restrict__ a, lon
   const int wave = wave_id(), lane = lane_id();
   auto rowp = [=](int r) { return a + (long)(m0 + r) * lda; };
   f32x4_v acc[NT][NB][1];
-  if (gain != nullptr) mfma_pass<K, NT, NB, 1, 2, decltype(rowp), true, MF_MT, true>(w, rowp, rows, buf, acc, gain, rs);
-  else mfma_pass<K, NT, NB, 1, 2, decltype(rowp), false, MF_MT, true>(w, rowp, rows, buf, acc);
+  if (gain != nullptr)
+    mfma_pass<K, NT, NB, 1, 2, decltype(rowp), true, MF_MT, DENSE_DEEP, true>(w, rowp, rows, buf, acc, gain, rs);
+  else
+    mfma_pass<K, NT, NB, 1, 2, decltype(rowp), false, MF_MT, DENSE_DEEP, true>(w, rowp, rows, buf, acc);
   const int j = lane & 15;
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
