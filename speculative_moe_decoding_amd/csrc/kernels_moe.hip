@@ -20,6 +20,21 @@ struct RouteLds {
   int na;
 };
 
+// Inclusive prefix sum over the 64 lanes of a wavefront: within each 16-lane
+// row by DPP row shifts (lanes past the row's start read 0), then the row
+// totals as scalars.
+__device__ __forceinline__ int wave_incl_scan(int c) {
+  const int lane = lane_id();
+  int incl = c;
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x111, 0xF, 0xF, false);  // row_shr:1
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x112, 0xF, 0xF, false);  // row_shr:2
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x114, 0xF, 0xF, false);  // row_shr:4
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x118, 0xF, 0xF, false);  // row_shr:8
+  const int t0 = __builtin_amdgcn_readlane(incl, 15), t1 = __builtin_amdgcn_readlane(incl, 31);
+  const int t2 = __builtin_amdgcn_readlane(incl, 47);
+  return incl + (lane >= 16 ? t0 : 0) + (lane >= 32 ? t1 : 0) + (lane >= 48 ? t2 : 0);
+}
+
 // Stable counting sort of P <= 64 pairs by one wavefront (lane = pair): the
 // lanes holding the same expert found from one ballot per bit of the id (7
 // bits cover 0..65), rank = those below this lane, count written by the
@@ -41,18 +56,9 @@ __device__ __forceinline__ void sort_pairs_wave(int P, RouteLds& r) {
   const int rank = valid ? __popcll(same & lt) : 0;
   if (valid && rank == 0) r.cnt[e] = __popcll(same);
   const int c = r.cnt[lane];
-  // inclusive scan of the counts: within each 16-lane row by DPP row shifts
-  // (lanes past the row's start read 0), then the row totals as scalars
-  int incl = c;
-  incl += __builtin_amdgcn_update_dpp(0, incl, 0x111, 0xF, 0xF, false);  // row_shr:1
-  incl += __builtin_amdgcn_update_dpp(0, incl, 0x112, 0xF, 0xF, false);  // row_shr:2
-  incl += __builtin_amdgcn_update_dpp(0, incl, 0x114, 0xF, 0xF, false);  // row_shr:4
-  incl += __builtin_amdgcn_update_dpp(0, incl, 0x118, 0xF, 0xF, false);  // row_shr:8
-  const int t0 = __builtin_amdgcn_readlane(incl, 15), t1 = __builtin_amdgcn_readlane(incl, 31);
-  const int t2 = __builtin_amdgcn_readlane(incl, 47), t3 = __builtin_amdgcn_readlane(incl, 63);
-  incl += (lane >= 16 ? t0 : 0) + (lane >= 32 ? t1 : 0) + (lane >= 48 ? t2 : 0);
+  const int incl = wave_incl_scan(c);
   r.off[lane] = incl - c;
-  const int routed = t0 + t1 + t2 + t3;
+  const int routed = __builtin_amdgcn_readlane(incl, 63);
   const uint64_t amask = __ballot(c > 0);
   if (c > 0) r.act[__popcll(amask & lt)] = lane;
   int na = __popcll(amask);
@@ -235,30 +241,40 @@ __global__ __launch_bounds__(256) void k_route_small(const float* __restrict__ r
 }
 
 // Larger batches (8 < M <= 2048): top-6 per row, one wavefront per row
-// (rank_and_gate) ...
+// (rank_and_gate; lg: the wavefront's 64-float LDS row), published to the
+// routing tables and taps; pe (optional, LDS): the row's 8 experts by slot.
+__device__ __forceinline__ void topk_row(float v, int m, float* lg, const MoeBufs& mb, const RouteTap& tap,
+                                         int* pe) {
+  const int lane = lane_id();
+  lg[lane] = v;
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  int rank;
+  float gate;
+  rank_and_gate(lg, v, rank, gate);
+  if (rank < TOPK) {
+    mb.ridx[m * NSLOT + rank] = lane;
+    mb.rgate[m * NSLOT + rank] = gate;
+    tap_pair(tap, m, rank, lane);
+    if (pe != nullptr) pe[rank] = lane;
+  }
+  if (lane < NSH) {
+    mb.ridx[m * NSLOT + TOPK + lane] = NE + lane;
+    mb.rgate[m * NSLOT + TOPK + lane] = 1.0f;
+    tap_pair(tap, m, TOPK + lane, NE + lane);
+    if (pe != nullptr) pe[TOPK + lane] = NE + lane;
+  }
+  __builtin_amdgcn_wave_barrier();  // lg is read by every lane before the next row overwrites it
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+}
+
 __global__ __launch_bounds__(256) void k_topk_rows(const float* __restrict__ rlogit, int M, MoeBufs mb,
                                                    RouteTap tap) {
   __shared__ float lg[4][NE];
   const int wave = wave_id(), lane = lane_id();
   const int m = blockIdx.x * 4 + wave;
   if (m >= M) return;
-  const float v = rlogit[(long)m * NE + lane];
-  lg[wave][lane] = v;
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  int rank;
-  float gate;
-  rank_and_gate(lg[wave], v, rank, gate);
-  if (rank < TOPK) {
-    mb.ridx[m * NSLOT + rank] = lane;
-    mb.rgate[m * NSLOT + rank] = gate;
-    tap_pair(tap, m, rank, lane);
-  }
-  if (lane < NSH) {
-    mb.ridx[m * NSLOT + TOPK + lane] = NE + lane;
-    mb.rgate[m * NSLOT + TOPK + lane] = 1.0f;
-    tap_pair(tap, m, TOPK + lane, NE + lane);
-  }
+  topk_row(rlogit[(long)m * NE + lane], m, lg[wave], mb, tap, nullptr);
 }
 
 // ... then a stable counting sort of the 8M pairs by expert in one 1024-thread
@@ -268,22 +284,47 @@ __global__ __launch_bounds__(256) void k_topk_rows(const float* __restrict__ rlo
 // pair its rank among the range's earlier pairs of the same expert (the
 // range's running counts in LDS).  The per-range counts give per-expert offsets (experts in id
 // order) and per-range bases; pair p lands at off[e] + base[w][e] + rank --
-// the permutation of any stable sort by expert id.
+// the permutation of any stable sort by expert id.  TOPK_IN (M <= RL_TOPK_ROWS):
+// each wavefront first takes the top-6 of its own rows (as k_topk_rows does),
+// keeping the pairs' experts in LDS -- one launch instead of two.
 constexpr int RL_WAVES = 16;
 constexpr int RL_SEGS = 16;  // segments per wavefront: M <= RL_WAVES * RL_SEGS * 8 = 2048
-__global__ __launch_bounds__(1024) void k_sort_pairs(int M, MoeBufs mb) {
+constexpr int RL_TOPK_ROWS = 128;
+constexpr int RL_TOPK_RPW = RL_TOPK_ROWS / RL_WAVES;  // rows per wavefront at most
+template <bool TOPK_IN>
+__global__ __launch_bounds__(1024) void k_sort_pairs(int M, MoeBufs mb, RouteTap tap) {
   __shared__ int wcnt[RL_WAVES][NX + 1];  // per range: counts, then exclusive bases
-  __shared__ int off[NX + 1], act[NX + 1], ioff[NX + 1];
+  __shared__ int tot[NX + 1], off[NX + 1], act[NX + 1], ioff[NX + 1];
   __shared__ int na_s;
   const int wave = threadIdx.x >> 6, lane = lane_id(), tid = threadIdx.x;
-  const int p_lo = NSLOT * (M * wave / RL_WAVES), p_hi = NSLOT * (M * (wave + 1) / RL_WAVES);
+  const int r_lo = M * wave / RL_WAVES, r_hi = M * (wave + 1) / RL_WAVES;
+  const int p_lo = NSLOT * r_lo, p_hi = NSLOT * r_hi;
   const uint64_t lt = (1ull << lane) - 1ull;
   int seg_e[RL_SEGS], seg_rank[RL_SEGS];
+  if constexpr (TOPK_IN) {
+    __shared__ float lg[RL_WAVES][NE];
+    __shared__ int pe[RL_WAVES][RL_TOPK_RPW * NSLOT];
+    float v[RL_TOPK_RPW];
 #pragma unroll
-  for (int sg = 0; sg < RL_SEGS; ++sg) {
-    const int p = p_lo + 64 * sg + lane;
-    seg_e[sg] = (p < p_hi) ? mb.ridx[p] : -1;
-    seg_rank[sg] = 0;
+    for (int j = 0; j < RL_TOPK_RPW; ++j) v[j] = (r_lo + j < r_hi) ? mb.rlogit[(long)(r_lo + j) * NE + lane] : 0.f;
+#pragma unroll
+    for (int j = 0; j < RL_TOPK_RPW; ++j)
+      if (r_lo + j < r_hi) topk_row(v[j], r_lo + j, lg[wave], mb, tap, &pe[wave][j * NSLOT]);
+    static_assert(RL_TOPK_RPW * NSLOT <= 64, "one segment per wavefront");
+    seg_e[0] = (p_lo + lane < p_hi) ? pe[wave][lane] : -1;
+    seg_rank[0] = 0;
+#pragma unroll
+    for (int sg = 1; sg < RL_SEGS; ++sg) {
+      seg_e[sg] = -1;
+      seg_rank[sg] = 0;
+    }
+  } else {
+#pragma unroll
+    for (int sg = 0; sg < RL_SEGS; ++sg) {
+      const int p = p_lo + 64 * sg + lane;
+      seg_e[sg] = (p < p_hi) ? mb.ridx[p] : -1;
+      seg_rank[sg] = 0;
+    }
   }
   // running count of each expert in this range (LDS, one row per wavefront):
   // a segment's equal experts are found from seven ballots over the id bits;
@@ -314,7 +355,7 @@ __global__ __launch_bounds__(1024) void k_sort_pairs(int M, MoeBufs mb) {
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
   }
   __syncthreads();
-  // per-expert totals -> offsets; per-range exclusive bases
+  // per-expert totals; per-range exclusive bases
   if (tid < NX) {
     int acc = 0;
     for (int w = 0; w < RL_WAVES; ++w) {
@@ -322,27 +363,47 @@ __global__ __launch_bounds__(1024) void k_sort_pairs(int M, MoeBufs mb) {
       wcnt[w][tid] = acc;
       acc += c;
     }
-    act[tid] = acc;  // total of expert tid (reused below as the active list)
+    tot[tid] = acc;
   }
   __syncthreads();
-  if (tid == 0) {
-    int acc = 0, na = 0;
-    for (int e = 0; e < NX; ++e) {
-      const int c = act[e];
-      off[e] = acc;
-      acc += c;
-      if (c > 0) act[na++] = e;  // na <= e: entries not yet read are never overwritten
+  // offsets (experts in id order), the active list (routed experts in id
+  // order, then the shared ones) and each active expert's first work item
+  // (ITEM_PAIRS pairs per item), by wavefront scans in wavefront 0
+  if (wave == 0) {
+    const int c = tot[lane];  // routed expert `lane`
+    const int c64 = tot[NE], c65 = tot[NE + 1];
+    const int incl = wave_incl_scan(c);
+    const int routed = __builtin_amdgcn_readlane(incl, 63);
+    off[lane] = incl - c;
+    const uint64_t am = __ballot(c > 0);
+    const int nr = __popcll(am);
+    const int nit = (c + ITEM_PAIRS - 1) / ITEM_PAIRS;  // 0 for an idle expert
+    const int iincl = wave_incl_scan(nit);
+    if (c > 0) {
+      const int sl = __popcll(am & lt);
+      act[sl] = lane;
+      ioff[sl] = iincl - nit;
     }
-    off[NX] = acc;
-    int it = 0;  // first work item of each active expert (ITEM_PAIRS pairs per item)
-    for (int sl = 0; sl < na; ++sl) {
-      ioff[sl] = it;
-      it += (off[act[sl] + 1] - off[act[sl]] + ITEM_PAIRS - 1) / ITEM_PAIRS;
+    if (lane == 0) {
+      off[NE] = routed;
+      off[NE + 1] = routed + c64;
+      off[NX] = routed + c64 + c65;
+      int na = nr, it = __builtin_amdgcn_readlane(iincl, 63);
+      if (c64 > 0) {
+        act[na] = NE;
+        ioff[na++] = it;
+        it += (c64 + ITEM_PAIRS - 1) / ITEM_PAIRS;
+      }
+      if (c65 > 0) {
+        act[na] = NE + 1;
+        ioff[na++] = it;
+        it += (c65 + ITEM_PAIRS - 1) / ITEM_PAIRS;
+      }
+      ioff[na] = it;
+      na_s = na;
+      *mb.n_act = na;
+      mb.stats[0] += na;
     }
-    ioff[na] = it;
-    na_s = na;
-    *mb.n_act = na;
-    mb.stats[0] += na;
   }
   __syncthreads();
   const int na = na_s;
@@ -412,9 +473,11 @@ void launch_router(hipStream_t s, const float* x, const float* gain, float eps, 
   launch_router_logits<T>(s, x, gain, eps, wr, M, mb, logit_override);
   if (M <= MRG) {
     hipLaunchKernelGGL(k_route_small, dim3(1), dim3(256), 0, s, mb.rlogit, M, mb, tap);
+  } else if (M <= RL_TOPK_ROWS) {
+    hipLaunchKernelGGL(k_sort_pairs<true>, dim3(1), dim3(1024), 0, s, M, mb, tap);
   } else {
     hipLaunchKernelGGL(k_topk_rows, dim3((M + 3) / 4), dim3(256), 0, s, mb.rlogit, M, mb, tap);
-    hipLaunchKernelGGL(k_sort_pairs, dim3(1), dim3(1024), 0, s, M, mb);
+    hipLaunchKernelGGL(k_sort_pairs<false>, dim3(1), dim3(1024), 0, s, M, mb, RouteTap{});
   }
 }
 
