@@ -314,8 +314,10 @@ class Decoder:
     def i32(self, *shape):
         return self.torch.empty(*shape, dtype=self.torch.int32, device=self.device)
 
-    def prefill(self, pages, slots: Optional[Sequence[int]] = None):
-        """pages: list of synth.Page.  Returns the device int32 [B] first output tokens."""
+    def stage_pages(self, pages):
+        """Upload the prefixes of ``pages`` (list of synth.Page) to the device: the
+        vision rows [B, nvs, d] fp32 and prompt ids [B, nps] int32, zero-padded,
+        with the host-side lengths.  The result feeds ``prefill_staged``."""
         torch = self.torch
         B = len(pages)
         nv = np.array([p.vision.shape[0] for p in pages], dtype=np.int32)
@@ -326,12 +328,22 @@ class Decoder:
         for b, p in enumerate(pages):
             vis[b, :p.vision.shape[0]] = p.vision
             pr[b, :p.prompt.shape[0]] = p.prompt
-        vis_t = torch.from_numpy(vis).to(self.device)
-        pr_t = torch.from_numpy(pr).to(self.device)
-        pending = self.i32(B)
+        return (torch.from_numpy(vis).to(self.device), nvs, nv, torch.from_numpy(pr).to(self.device), nps, npr)
+
+    def prefill_staged(self, staged, slots: Optional[Sequence[int]] = None, pending=None):
+        """Prefill from device-resident prefixes (``stage_pages``).  Returns the
+        device int32 [B] first output tokens (into ``pending`` when given)."""
+        vis_t, nvs, nv, pr_t, nps, npr = staged
+        B = len(nv)
+        if pending is None:
+            pending = self.i32(B)
         sl = None if slots is None else np.asarray(slots, dtype=np.int32)
         ocrdec_prefill(self.h, self.stream, B, sl, vis_t, nvs, nv, pr_t, nps, npr, pending)
         return pending
+
+    def prefill(self, pages, slots: Optional[Sequence[int]] = None):
+        """pages: list of synth.Page.  Returns the device int32 [B] first output tokens."""
+        return self.prefill_staged(self.stage_pages(pages), slots)
 
     def draft(self, B, K, slots=None, out=None):
         out = self.i32(B, K) if out is None else out
