@@ -796,30 +796,50 @@ __device__ __forceinline__ void lm_pass(const bf16* const (&w)[1], const float* 
   }
 }
 
-// CACHED (more than one pass): ordinary weight loads, so that the strip's
-// later passes find it in the caches.  CT: row tiles per pass.
-template <bool CACHED, int CT>
+constexpr int N_XCD = 8;  // dies of the chip, each with its own L2
+
+// CT: row tiles per pass.  One pass (SPLIT false, at most 16 CT rows): block
+// x = blockIdx.x.  More rows (SPLIT): each pass of a strip is a block of its
+// own, and the passes of strip x run as consecutive blocks of one XCD (the
+// dispatcher deals blocks to the 8 XCDs in turn), so that one L2 serves the
+// strip's repeated reads; the row passes then run side by side instead of
+// one after another.  Ordinary weight loads either way (measured faster than
+// non-temporal ones here, also for one pass).
+template <bool SPLIT, int CT>
 __global__ __launch_bounds__(256) void k_lmhead_mfma(const float* __restrict__ xn, const bf16* __restrict__ W,
-                                                     int V, int M, float* __restrict__ part_val,
+                                                     int V, int M, int nblk, float* __restrict__ part_val,
                                                      int* __restrict__ part_idx, float* __restrict__ logits) {
   constexpr int RB = 16 * CT;
+  constexpr bool CACHED = true;
   __shared__ MfChunkT<CT> buf[2][1];
   __shared__ float bv[4][RB];
   __shared__ int bi[4][RB];
   const int wave = wave_id(), lane = lane_id();
-  const int nblk = gridDim.x;
-  const int v0 = blockIdx.x * LM_ROWS_PER_BLOCK + wave * 16;
+  int x = blockIdx.x, pass_lo = 0, pass_hi = (M + RB - 1) / RB;
+  if constexpr (SPLIT) {
+    const int L = blockIdx.x;
+    x = L % N_XCD + N_XCD * (L / (N_XCD * pass_hi));
+    pass_lo = (L / N_XCD) % pass_hi;
+    pass_hi = pass_lo + 1;
+    if (x >= nblk) return;
+  }
+  const int v0 = x * LM_ROWS_PER_BLOCK + wave * 16;
   // A strip reaching past the vocabulary is moved back to rows V-16 .. V-1;
   // its lanes then keep only the ids >= v0 (the others belong to the strip before).
   const bool shifted = v0 > V - 16;
   const bf16* const w[1] = {W + (long)(shifted ? V - 16 : v0) * D};
   const int vj = (shifted ? V - 16 : v0) + (lane & 15);
   const bool vok = vj >= v0 && vj < V;
-  for (int p0 = 0; p0 < M; p0 += RB) {
+  for (int pi = pass_lo; pi < pass_hi; ++pi) {
+    const int p0 = pi * RB;
     const int rows = min(RB, M - p0);
-    if (CT == 1 || rows <= 16) lm_pass<1, CACHED, CT>(w, xn, p0, rows, vj, vok, V, logits, bv, bi, buf);
-    else if (CT == 2 || rows <= 32) lm_pass<(CT < 2 ? CT : 2), CACHED, CT>(w, xn, p0, rows, vj, vok, V, logits, bv, bi, buf);
-    else lm_pass<CT, CACHED, CT>(w, xn, p0, rows, vj, vok, V, logits, bv, bi, buf);
+    if (CT == 1 || rows <= 16) {
+      lm_pass<1, CACHED, CT>(w, xn, p0, rows, vj, vok, V, logits, bv, bi, buf);
+    } else if (CT == 2 || rows <= 32) {
+      lm_pass<(CT < 2 ? CT : 2), CACHED, CT>(w, xn, p0, rows, vj, vok, V, logits, bv, bi, buf);
+    } else {
+      lm_pass<CT, CACHED, CT>(w, xn, p0, rows, vj, vok, V, logits, bv, bi, buf);
+    }
     __syncthreads();
     if ((int)threadIdx.x < rows) {
       const int r = threadIdx.x;
@@ -827,8 +847,8 @@ __global__ __launch_bounds__(256) void k_lmhead_mfma(const float* __restrict__ x
       int id = bi[0][r];
       for (int ww = 1; ww < 4; ++ww)
         if (bv[ww][r] > b || (bv[ww][r] == b && bi[ww][r] < id)) { b = bv[ww][r]; id = bi[ww][r]; }
-      part_val[(long)(p0 + r) * nblk + blockIdx.x] = b;
-      part_idx[(long)(p0 + r) * nblk + blockIdx.x] = id;
+      part_val[(long)(p0 + r) * nblk + x] = b;
+      part_idx[(long)(p0 + r) * nblk + x] = id;
     }
     __syncthreads();
   }
@@ -840,11 +860,12 @@ void launch_lmhead_mfma(hipStream_t s, const float* x, const int* cnt, int Q, bo
                         float* logits, int* tok, int tok_stride) {
   hipLaunchKernelGGL(k_lm_norm, dim3((M + 3) / 4), dim3(256), 0, s, x, cnt, Q, (int)last_valid, gain, eps, M, xn);
   const int nb = lmhead_blocks(V);
-  if (M > 16 * LM_CT)
-    hipLaunchKernelGGL((k_lmhead_mfma<true, LM_CT>), dim3(nb), dim3(256), 0, s, xn, W, V, M, part_val, part_idx,
-                       logits);
+  const int passes = (M + 16 * LM_CT - 1) / (16 * LM_CT);
+  if (passes > 1)
+    hipLaunchKernelGGL((k_lmhead_mfma<true, LM_CT>), dim3((nb + N_XCD - 1) / N_XCD * N_XCD * passes), dim3(256), 0, s,
+                       xn, W, V, M, nb, part_val, part_idx, logits);
   else
-    hipLaunchKernelGGL((k_lmhead_mfma<false, LM_CT>), dim3(nb), dim3(256), 0, s, xn, W, V, M, part_val, part_idx,
+    hipLaunchKernelGGL((k_lmhead_mfma<false, LM_CT>), dim3(nb), dim3(256), 0, s, xn, W, V, M, nb, part_val, part_idx,
                        logits);
   if (tok != nullptr) launch_argmax_final(s, part_val, part_idx, nb, M, tok, tok_stride);
 }
