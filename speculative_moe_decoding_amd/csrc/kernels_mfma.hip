@@ -767,24 +767,30 @@ __global__ __launch_bounds__(256) void k_lm_norm(const float* __restrict__ x, co
 // rows 64 x .. 64 x + 63 (16 per wavefront) for all M rows, passes of 64 rows,
 // and writes the best (value, lowest id) per row to part[row][x]; logits
 // optionally stored to logits[row][V].
-template <int NT, bool CACHED, int CT>
-__device__ __forceinline__ void lm_pass(const bf16* const (&w)[1], const float* __restrict__ xn, int p0, int rows,
-                                        int vj, bool vok, int V, float* __restrict__ logits, float (&bv)[4][16 * CT],
-                                        int (&bi)[4][16 * CT], MfChunkT<CT> (&buf)[2][1]) {
+// G groups of 16 vocab rows per wavefront: w[g] the group's rows, vj[g] this
+// lane's id in it, vok[g] whether that id is the group's to score.
+template <int NT, bool CACHED, int CT, int G>
+__device__ __forceinline__ void lm_pass(const bf16* const (&w)[G], const float* __restrict__ xn, int p0, int rows,
+                                        const int (&vj)[G], const bool (&vok)[G], int V, float* __restrict__ logits,
+                                        float (&bv)[4][16 * CT], int (&bi)[4][16 * CT], MfChunkT<CT> (&buf)[2][1]) {
   const int wave = wave_id(), lane = lane_id();
-  f32x4_v acc[NT][1][1];
+  f32x4_v acc[NT][G][1];
   auto rowp = [=](int r) { return xn + (long)(p0 + r) * D; };
-  mfma_pass<D, NT, 1, 1, 1, decltype(rowp), false, CT, false, CACHED>(w, rowp, rows, buf, acc);
+  mfma_pass<D, NT, G, 1, 1, decltype(rowp), false, CT, false, CACHED>(w, rowp, rows, buf, acc);
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int r = 16 * i + 4 * (lane >> 4) + q;
-      const bool ok = vok && r < rows;
-      const float val = acc[i][0][0][q];
-      if (ok && logits != nullptr) logits[(long)(p0 + r) * V + vj] = val;
-      float b = ok ? val : -INFINITY;
-      int id = ok ? vj : 0x7fffffff;
+      float b = -INFINITY;
+      int id = 0x7fffffff;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const bool ok = vok[g] && r < rows;
+        const float val = acc[i][g][0][q];
+        if (ok && logits != nullptr) logits[(long)(p0 + r) * V + vj[g]] = val;
+        if (ok && (val > b || (val == b && vj[g] < id))) { b = val; id = vj[g]; }
+      }
 #pragma unroll
       for (int off = 8; off >= 1; off >>= 1) {
         const float ob = __shfl_xor(b, off, 64);
@@ -797,10 +803,15 @@ __device__ __forceinline__ void lm_pass(const bf16* const (&w)[1], const float* 
 }
 
 constexpr int N_XCD = 8;  // dies of the chip, each with its own L2
+constexpr int LM_G = 2;   // groups of 16 vocab rows per wavefront of the matrix-core LM head
 
-// CT: row tiles per pass.  One pass (SPLIT false, at most 16 CT rows): block
-// x = blockIdx.x.  More rows (SPLIT): each pass of a strip is a block of its
-// own, and the passes of strip x run as consecutive blocks of one XCD (the
+// Block x scores vocab rows 64 G x .. 64 G x + 64 G - 1 (wavefront w: 16 G of
+// them) and writes, per row, the best (value, lowest id) of each 64-row slab
+// (the partials of the stage-2 argmax, slab k = rows 64 k ..).  More vocab
+// rows per block share one staging of the activation rows.  CT: row tiles
+// per pass.  One pass (SPLIT false, at most 16 CT rows): block x =
+// blockIdx.x.  More rows (SPLIT): each pass of a strip is a block of its own,
+// and the passes of strip x run as consecutive blocks of one XCD (the
 // dispatcher deals blocks to the 8 XCDs in turn), so that one L2 serves the
 // strip's repeated reads; the row passes then run side by side instead of
 // one after another.  Ordinary weight loads either way (measured faster than
@@ -815,40 +826,53 @@ __global__ __launch_bounds__(256) void k_lmhead_mfma(const float* __restrict__ x
   __shared__ float bv[4][RB];
   __shared__ int bi[4][RB];
   const int wave = wave_id(), lane = lane_id();
+  const int nx = (nblk + LM_G - 1) / LM_G;  // blocks per pass
   int x = blockIdx.x, pass_lo = 0, pass_hi = (M + RB - 1) / RB;
   if constexpr (SPLIT) {
     const int L = blockIdx.x;
     x = L % N_XCD + N_XCD * (L / (N_XCD * pass_hi));
     pass_lo = (L / N_XCD) % pass_hi;
     pass_hi = pass_lo + 1;
-    if (x >= nblk) return;
+    if (x >= nx) return;
   }
-  const int v0 = x * LM_ROWS_PER_BLOCK + wave * 16;
-  // A strip reaching past the vocabulary is moved back to rows V-16 .. V-1;
-  // its lanes then keep only the ids >= v0 (the others belong to the strip before).
-  const bool shifted = v0 > V - 16;
-  const bf16* const w[1] = {W + (long)(shifted ? V - 16 : v0) * D};
-  const int vj = (shifted ? V - 16 : v0) + (lane & 15);
-  const bool vok = vj >= v0 && vj < V;
+  // A group reaching past the vocabulary is moved back to rows V-16 .. V-1;
+  // its lanes then keep only the ids >= its start (the others belong to the
+  // group before, or lie past the vocabulary).
+  const bf16* w[LM_G];
+  int vj[LM_G];
+  bool vok[LM_G];
+#pragma unroll
+  for (int g = 0; g < LM_G; ++g) {
+    const int v0 = x * 64 * LM_G + wave * 16 * LM_G + 16 * g;
+    const int vb = v0 > V - 16 ? V - 16 : v0;
+    w[g] = W + (long)vb * D;
+    vj[g] = vb + (lane & 15);
+    vok[g] = vj[g] >= v0 && vj[g] < V;
+  }
+  const bf16* const (&wc)[LM_G] = w;
   for (int pi = pass_lo; pi < pass_hi; ++pi) {
     const int p0 = pi * RB;
     const int rows = min(RB, M - p0);
     if (CT == 1 || rows <= 16) {
-      lm_pass<1, CACHED, CT>(w, xn, p0, rows, vj, vok, V, logits, bv, bi, buf);
+      lm_pass<1, CACHED, CT, LM_G>(wc, xn, p0, rows, vj, vok, V, logits, bv, bi, buf);
     } else if (CT == 2 || rows <= 32) {
-      lm_pass<(CT < 2 ? CT : 2), CACHED, CT>(w, xn, p0, rows, vj, vok, V, logits, bv, bi, buf);
+      lm_pass<(CT < 2 ? CT : 2), CACHED, CT, LM_G>(wc, xn, p0, rows, vj, vok, V, logits, bv, bi, buf);
     } else {
-      lm_pass<CT, CACHED, CT>(w, xn, p0, rows, vj, vok, V, logits, bv, bi, buf);
+      lm_pass<CT, CACHED, CT, LM_G>(wc, xn, p0, rows, vj, vok, V, logits, bv, bi, buf);
     }
     __syncthreads();
-    if ((int)threadIdx.x < rows) {
-      const int r = threadIdx.x;
-      float b = bv[0][r];
-      int id = bi[0][r];
-      for (int ww = 1; ww < 4; ++ww)
+    // slab h of the block: wavefronts 4 h / G .. 4 (h + 1) / G - 1
+    for (int t = threadIdx.x; t < rows * LM_G; t += 256) {
+      const int r = t % rows, h = t / rows;
+      const int k = x * LM_G + h;
+      if (k >= nblk) continue;
+      constexpr int WPS = 4 / LM_G;  // wavefronts per slab
+      float b = bv[h * WPS][r];
+      int id = bi[h * WPS][r];
+      for (int ww = h * WPS + 1; ww < (h + 1) * WPS; ++ww)
         if (bv[ww][r] > b || (bv[ww][r] == b && bi[ww][r] < id)) { b = bv[ww][r]; id = bi[ww][r]; }
-      part_val[(long)(p0 + r) * nblk + x] = b;
-      part_idx[(long)(p0 + r) * nblk + x] = id;
+      part_val[(long)(p0 + r) * nblk + k] = b;
+      part_idx[(long)(p0 + r) * nblk + k] = id;
     }
     __syncthreads();
   }
@@ -860,12 +884,13 @@ void launch_lmhead_mfma(hipStream_t s, const float* x, const int* cnt, int Q, bo
                         float* logits, int* tok, int tok_stride) {
   hipLaunchKernelGGL(k_lm_norm, dim3((M + 3) / 4), dim3(256), 0, s, x, cnt, Q, (int)last_valid, gain, eps, M, xn);
   const int nb = lmhead_blocks(V);
+  const int nx = (nb + LM_G - 1) / LM_G;
   const int passes = (M + 16 * LM_CT - 1) / (16 * LM_CT);
   if (passes > 1)
-    hipLaunchKernelGGL((k_lmhead_mfma<true, LM_CT>), dim3((nb + N_XCD - 1) / N_XCD * N_XCD * passes), dim3(256), 0, s,
+    hipLaunchKernelGGL((k_lmhead_mfma<true, LM_CT>), dim3((nx + N_XCD - 1) / N_XCD * N_XCD * passes), dim3(256), 0, s,
                        xn, W, V, M, nb, part_val, part_idx, logits);
   else
-    hipLaunchKernelGGL((k_lmhead_mfma<false, LM_CT>), dim3(nb), dim3(256), 0, s, xn, W, V, M, nb, part_val, part_idx,
+    hipLaunchKernelGGL((k_lmhead_mfma<false, LM_CT>), dim3(nx), dim3(256), 0, s, xn, W, V, M, nb, part_val, part_idx,
                        logits);
   if (tok != nullptr) launch_argmax_final(s, part_val, part_idx, nb, M, tok, tok_stride);
 }
