@@ -234,6 +234,70 @@ __device__ __forceinline__ void mfma_pass(const bf16* const (&w)[NB], RowPtr row
   }
 }
 
+// The same pass (decode-sized pipeline, one bf16 part) for activation rows
+// already in bf16: the staging copies them into the A fragments as they are.
+template <int NT>
+__device__ __forceinline__ void mf_load_a_bf(uint4 (&ar)[NT], const bf16* const (&src)[NT], const bool (&ok)[NT],
+                                             int c) {
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    const uint4 v = *reinterpret_cast<const uint4*>(src[i] + c * MF_KC);
+    ar[i] = ok[i] ? v : make_uint4(0, 0, 0, 0);
+  }
+}
+template <int NT, int CT>
+__device__ __forceinline__ void mf_store_a_bf(MfChunkT<CT>& ch, const uint4 (&ar)[NT], int kg, int ri) {
+  static_assert(NT <= CT, "chunk too small for the pass");
+#pragma unroll
+  for (int i = 0; i < NT; ++i) ch.f[i][kg >> 2][mf_slot(kg >> 2, (kg & 3) * 16 + ri)] = ar[i];
+}
+template <int K, int NT, int NB, int CT, bool CACHED, typename RowPtr>
+__device__ __forceinline__ void mfma_pass_abf(const bf16* const (&w)[NB], RowPtr rowp, int rows,
+                                              MfChunkT<CT> (&buf)[2][1], f32x4_v (&acc)[NT][NB][1]) {
+  static_assert(K % MF_KC == 0, "K must be a multiple of the chunk");
+  constexpr int NC = K / MF_KC;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const long woff = (long)(lane & 15) * K + 8 * (lane >> 4);
+  const int kg = tid & 15, ri = tid >> 4;
+  const bf16* src[NT];
+  bool ok[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    const int r = ri + 16 * i;
+    ok[i] = r < rows;
+    src[i] = rowp(ok[i] ? r : 0) + 8 * kg;
+  }
+#pragma unroll
+  for (int i = 0; i < NT; ++i)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[i][b][0] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+  uint4 bq0[NB][1][MF_SC], bq1[NB][1][MF_SC];
+  uint4 ar[NT];
+  mf_load_a_bf(ar, src, ok, 0);
+  mf_load_b<K, NB, 1, CACHED>(bq0, w, woff, 0);
+  mf_store_a_bf<NT, CT>(buf[0][0], ar, kg, ri);
+  __syncthreads();
+#pragma unroll 1
+  for (int c = 0; c < NC; c += 2) {
+    if (c + 1 < NC) {
+      mf_load_a_bf(ar, src, ok, c + 1);
+      mf_load_b<K, NB, 1, CACHED>(bq1, w, woff, c + 1);
+    }
+    mf_compute<NT, NB, 1, 1, CT>(buf[0], bq0, acc);
+    if (c + 1 < NC) mf_store_a_bf<NT, CT>(buf[1][0], ar, kg, ri);
+    __syncthreads();
+    if (c + 1 < NC) {
+      if (c + 2 < NC) {
+        mf_load_a_bf(ar, src, ok, c + 2);
+        mf_load_b<K, NB, 1, CACHED>(bq0, w, woff, c + 2);
+      }
+      mf_compute<NT, NB, 1, 1, CT>(buf[1], bq1, acc);
+      if (c + 2 < NC) mf_store_a_bf<NT, CT>(buf[0][0], ar, kg, ri);
+      __syncthreads();
+    }
+  }
+}
+
 // Gate/up: block (x, slot s) computes units j0 .. j0+15, j0 = 64 x + 16 w, of
 // active expert s for every pair routed to it:
 // hx[pair][j] = silu(gate_j . b) * (up_j . b), b the pair's normalised row.
@@ -745,7 +809,7 @@ void launch_qkv_rope_mfma(hipStream_t s, const float* x, const float* gain, floa
 // Lane l sums x[k]^2 over k = l + 64 j in order, then the xor butterfly.
 __global__ __launch_bounds__(256) void k_lm_norm(const float* __restrict__ x, const int* __restrict__ cnt, int Q,
                                                  int last_valid, const float* __restrict__ gain, float eps, int M,
-                                                 float* __restrict__ xn) {
+                                                 bf16* __restrict__ xn) {
   constexpr int J = D / 64;
   const int m = blockIdx.x * 4 + wave_id();
   if (m >= M) return;
@@ -759,8 +823,15 @@ __global__ __launch_bounds__(256) void k_lm_norm(const float* __restrict__ x, co
   for (int j = 0; j < J; ++j) ss = fmaf(v[j], v[j], ss);
   ss = wave_sum(ss);
   const float r = 1.0f / sqrtf(ss / (float)D + eps);
+  // the normalised row rounded to bf16 (the LM head's one part), element
+  // pairs (2 i, 2 i + 1) packed by the even lanes
 #pragma unroll
-  for (int j = 0; j < J; ++j) xn[(long)m * D + lane + 64 * j] = (v[j] * r) * gain[lane + 64 * j];
+  for (int j = 0; j < J; ++j) {
+    const float y = (v[j] * r) * gain[lane + 64 * j];
+    const float yn = __shfl_down(y, 1, 64);
+    if ((lane & 1) == 0)
+      reinterpret_cast<uint32_t*>(xn + (long)m * D + 64 * j)[lane >> 1] = pack_bf16x2(y, yn);
+  }
 }
 
 // LM head + argmax stage 1 on the matrix cores (V >= 16): block x scores vocab
@@ -770,13 +841,13 @@ __global__ __launch_bounds__(256) void k_lm_norm(const float* __restrict__ x, co
 // G groups of 16 vocab rows per wavefront: w[g] the group's rows, vj[g] this
 // lane's id in it, vok[g] whether that id is the group's to score.
 template <int NT, bool CACHED, int CT, int G>
-__device__ __forceinline__ void lm_pass(const bf16* const (&w)[G], const float* __restrict__ xn, int p0, int rows,
+__device__ __forceinline__ void lm_pass(const bf16* const (&w)[G], const bf16* __restrict__ xn, int p0, int rows,
                                         const int (&vj)[G], const bool (&vok)[G], int V, float* __restrict__ logits,
                                         float (&bv)[4][16 * CT], int (&bi)[4][16 * CT], MfChunkT<CT> (&buf)[2][1]) {
   const int wave = wave_id(), lane = lane_id();
   f32x4_v acc[NT][G][1];
   auto rowp = [=](int r) { return xn + (long)(p0 + r) * D; };
-  mfma_pass<D, NT, G, 1, 1, decltype(rowp), false, CT, false, CACHED>(w, rowp, rows, buf, acc);
+  mfma_pass_abf<D, NT, G, CT, CACHED>(w, rowp, rows, buf, acc);
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
 #pragma unroll
@@ -817,7 +888,7 @@ constexpr int LM_G = 2;   // groups of 16 vocab rows per wavefront of the matrix
 // one after another.  Ordinary weight loads either way (measured faster than
 // non-temporal ones here, also for one pass).
 template <bool SPLIT, int CT>
-__global__ __launch_bounds__(256) void k_lmhead_mfma(const float* __restrict__ xn, const bf16* __restrict__ W,
+__global__ __launch_bounds__(256) void k_lmhead_mfma(const bf16* __restrict__ xn, const bf16* __restrict__ W,
                                                      int V, int M, int nblk, float* __restrict__ part_val,
                                                      int* __restrict__ part_idx, float* __restrict__ logits) {
   constexpr int RB = 16 * CT;
@@ -882,15 +953,16 @@ constexpr int LM_CT = 4;  // row tiles per pass of the LM head
 void launch_lmhead_mfma(hipStream_t s, const float* x, const int* cnt, int Q, bool last_valid, const float* gain,
                         float eps, const bf16* W, int V, int M, float* xn, float* part_val, int* part_idx,
                         float* logits, int* tok, int tok_stride) {
-  hipLaunchKernelGGL(k_lm_norm, dim3((M + 3) / 4), dim3(256), 0, s, x, cnt, Q, (int)last_valid, gain, eps, M, xn);
+  bf16* xb = reinterpret_cast<bf16*>(xn);  // the rows in bf16, in the first half of the fp32 buffer
+  hipLaunchKernelGGL(k_lm_norm, dim3((M + 3) / 4), dim3(256), 0, s, x, cnt, Q, (int)last_valid, gain, eps, M, xb);
   const int nb = lmhead_blocks(V);
   const int nx = (nb + LM_G - 1) / LM_G;
   const int passes = (M + 16 * LM_CT - 1) / (16 * LM_CT);
   if (passes > 1)
     hipLaunchKernelGGL((k_lmhead_mfma<true, LM_CT>), dim3((nx + N_XCD - 1) / N_XCD * N_XCD * passes), dim3(256), 0, s,
-                       xn, W, V, M, nb, part_val, part_idx, logits);
+                       xb, W, V, M, nb, part_val, part_idx, logits);
   else
-    hipLaunchKernelGGL((k_lmhead_mfma<false, LM_CT>), dim3(nx), dim3(256), 0, s, xn, W, V, M, nb, part_val, part_idx,
+    hipLaunchKernelGGL((k_lmhead_mfma<false, LM_CT>), dim3(nx), dim3(256), 0, s, xb, W, V, M, nb, part_val, part_idx,
                        logits);
   if (tok != nullptr) launch_argmax_final(s, part_val, part_idx, nb, M, tok, tok_stride);
 }
