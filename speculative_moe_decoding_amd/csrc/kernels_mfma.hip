@@ -390,14 +390,14 @@ __global__ __launch_bounds__(256) void k_expert_down_mfma(const bf16* __restrict
 // measured best.  Decode gate/up: passes of 32 pairs (half the LDS: more
 // workgroups per compute unit keep more weight loads in flight), ordinary
 // loads (a shared expert's 64 rows take two passes over its strips).  Decode
-// down: passes of 64, non-temporal loads.  Prefill passes (64-pair work
+// down: passes of 64, ordinary loads.  Prefill passes (64-pair work
 // items, ordinary loads): passes of 64 with the two-chunk pipeline (the
 // deeper one costs registers, hence workgroups in flight, and measured slower
 // since the work items keep every block's pass short).
 constexpr int GU_DEC_CT = 2;
 constexpr bool GU_DEC_CACHED = true;
 constexpr int DN_DEC_CT = 4;
-constexpr bool DN_DEC_CACHED = false;
+constexpr bool DN_DEC_CACHED = true;
 constexpr int GU_ITEM_CT = 4;  // work items: decode calls of more than 64 rows
 constexpr int DN_ITEM_CT = 4;
 constexpr int GU_DEEP_CT = 4;  // prefill passes
