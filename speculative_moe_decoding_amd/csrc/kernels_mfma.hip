@@ -665,7 +665,7 @@ __global__ __launch_bounds__(256) void k_dense_ks(const float* __restrict__ a, l
   float4 aq[DKS_PF][2], gq[DKS_PF][2];
   auto load = [&](int t, int slot) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b) bq[slot][b] = ldg16_stream(wb[b] + 32 * t);
+    for (int b = 0; b < NB; ++b) bq[slot][b] = ldg16(wb[b] + 32 * t);  // row tiles of a strip share it in L2
     const float4* ap = reinterpret_cast<const float4*>(arow + kl + 32 * t);
     aq[slot][0] = ap[0];
     aq[slot][1] = ap[1];
