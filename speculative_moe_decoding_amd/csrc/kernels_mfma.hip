@@ -10,7 +10,7 @@
 // lo = bf16(a - hi) (round to nearest even), and both are multiplied (about 16
 // significant bits of the fp32 activation survive, so the rounding does not
 // compound over the layers); the LM head takes hi alone (one rounding at the
-// end of the network).  Each 16x16 output block accumulates
+// end of the network, made when its rows are normalised).  Each 16x16 output block accumulates
 // v_mfma_f32_16x16x32_bf16 over k (hi then lo per k-step) in a fixed order, so
 // a row's result depends only on that row and the weights: the row count of a
 // call never changes it (speculative == autoregressive, bit for bit, on one
@@ -49,9 +49,8 @@ typedef MfChunkT<MF_MT> MfChunk;
 // Passes use NT (1, 2 or 4) tiles, the fewest that hold their rows; rows of a
 // tile past the pass's row count are zero.
 
-// Weight fragments of chunk c: non-temporal loads for decode-sized passes
-// (read once per launch), ordinary ones in prefill passes (CACHED), whose
-// workgroups read their strip once per 64 rows of a work item.
+// Weight fragments of chunk c: ordinary loads (CACHED), or non-temporal ones
+// for a strip read once per launch where that measured faster.
 template <int K, int NB, int NS, bool CACHED = false>
 __device__ __forceinline__ void mf_load_b(uint4 (&bq)[NB][NS][MF_SC], const bf16* const (&w)[NB], long woff, int c) {
 #pragma unroll
@@ -203,8 +202,8 @@ __device__ __forceinline__ void mfma_pass(const bf16* const (&w)[NB], RowPtr row
     // Decode-sized passes: chunk c computes from LDS buffer c % 2 and
     // registers bq(c % 2) while chunk c + 1 is loaded into the other pair
     // (fewer registers: more workgroups in flight); one barrier per chunk.
-    // CACHED: ordinary weight loads, for workgroups that run several passes
-    // over the same weight strip.
+    // CACHED: ordinary weight loads (see the launchers for where each kind
+    // is used).
     float4 gq[2];
     uint4 bq0[NB][NS][MF_SC], bq1[NB][NS][MF_SC];
     float4 ar[NT][2];
