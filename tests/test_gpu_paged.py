@@ -134,3 +134,33 @@ def test_continuous_batching_on_a_small_pool():
         assert ref[i].tolist() == got[i].tolist(), i
     assert paged.kv_pages() == (6, 6)
     log(f"continuous batching: {n} pages through 3 slots on a 6-page pool, bitwise equal to the full pool")
+
+
+def test_load_sequence_on_a_small_pool():
+    """A caller's cache loaded into the pages of a slot (ocrdec_load_sequence):
+    on a 6-page pool a second 200-position sequence (4 pages) is refused with
+    the pool unchanged, and once the first slot is released it loads into the
+    pages that slot gave back; a verify over it then equals bitwise the same
+    verify on the full pool."""
+    cfg = dataclasses.replace(SMALL, dtype="bf16")
+    w = synth.Weights(cfg, 101)
+    n_pos = 200
+    kv_dev = torch.from_numpy(synth.longctx_kv(cfg, 102, n_pos).view(np.int16)).cuda()
+    other = torch.from_numpy(synth.longctx_kv(cfg, 103, n_pos).view(np.int16)).cuda()
+    full = _dec(cfg, w, 2, 3, 512)
+    paged = _dec(cfg, w, 2, 3, 512, kv_pages=6)
+    ocrdec.ocrdec_load_sequence(full.h, full.stream, 0, n_pos, 17, kv_dev)
+    ocrdec.ocrdec_load_sequence(paged.h, paged.stream, 1, n_pos, 5, other)
+    assert paged.kv_pages() == (6, 2)
+    with pytest.raises(ocrdec.OcrdecError) as e:
+        ocrdec.ocrdec_load_sequence(paged.h, paged.stream, 0, n_pos, 17, kv_dev)
+    assert e.value.code == ocrdec.OCRDEC_ECAPACITY
+    assert paged.kv_pages() == (6, 2)
+    paged.release(1)
+    ocrdec.ocrdec_load_sequence(paged.h, paged.stream, 0, n_pos, 17, kv_dev)
+    assert paged.kv_pages() == (6, 2)
+    draft = torch.tensor([[3, 4, 5]], dtype=torch.int32, device="cuda")
+    g0, l0 = _verify_logits(full, 1, 3, draft)
+    g1, l1 = _verify_logits(paged, 1, 3, draft)
+    assert np.array_equal(g0, g1) and np.array_equal(l0, l1), float(np.abs(l0 - l1).max())
+    log("loaded cache on a small pool: refused when full, equal to the full pool after a release")
