@@ -341,7 +341,7 @@ void launch_attention(hipStream_t s, const float* q, KvView<T> kv, RowPlan plan,
 constexpr int PA_VT_STRIDE = ATT_TILE / 2 + 4;  // 32-bit words per transposed value row (+4: spreads banks)
 
 __global__ __launch_bounds__(128) void k_attn_prefill_mfma(const float* __restrict__ q, KvView<bf16> kv,
-                                                           RowPlan plan, float* __restrict__ out) {
+                                                           RowPlan plan, float* __restrict__ part) {
   __shared__ __align__(16) uint32_t vt[HD][PA_VT_STRIDE];  // vt[d][k / 2] = (v[k][d], v[k + 1][d]) as bf16 pairs
   __shared__ __align__(16) float pl[2][16][ATT_TILE + 4];  // per wavefront: P rows
   const int b = blockIdx.x, h = blockIdx.y;
@@ -352,6 +352,9 @@ __global__ __launch_bounds__(128) void k_attn_prefill_mfma(const float* __restri
   const long slot = plan.slot[b];
   const int max_pos = kv.max_pos;
   const int p_last = min(base + cnt - 1, max_pos - 1);
+  // this block's share of the entry's key tiles (split blockIdx.z)
+  int t0, t1;
+  if (!prefill_split(cnt > 0 && base >= 0 ? p_last / ATT_TILE + 1 : 0, blockIdx.z, t0, t1)) return;
   // A fragments of this wavefront's 16 query rows (row c16, dims 32 s + 8 g ..)
   const int qi = 16 * wave + c16;
   uint4 qh[4], ql[4];
@@ -399,10 +402,9 @@ __global__ __launch_bounds__(128) void k_attn_prefill_mfma(const float* __restri
       vc[j][1] = ldg16(Vt + (long)(2 * kp + 1) * HD + 8 * dc);
     }
   };
-  const int n_tiles = cnt > 0 && base >= 0 ? p_last / ATT_TILE + 1 : 0;
   const float scale = 0.08838834764831845f;  // 1 / sqrt(128)
-  if (n_tiles > 0) load_tile(0);
-  for (int t = 0; t < n_tiles; ++t) {
+  load_tile(t0 * ATT_TILE);
+  for (int t = t0; t < t1; ++t) {
     const int kt = t * ATT_TILE;
     // S blocks from the key fragments in registers
     f32x4_v sb[4];
@@ -429,7 +431,7 @@ __global__ __launch_bounds__(128) void k_attn_prefill_mfma(const float* __restri
         vt[8 * dc + 2 * w + 1][kp] = (a[w] >> 16) | (c[w] & 0xffff0000u);
       }
     }
-    if (t + 1 < n_tiles) load_tile(kt + ATT_TILE);  // next tile in flight during this one's arithmetic
+    if (t + 1 < t1) load_tile(kt + ATT_TILE);  // next tile in flight during this one's arithmetic
     // online softmax of this lane's four rows
     float corr[4];
 #pragma unroll
@@ -479,15 +481,65 @@ __global__ __launch_bounds__(128) void k_attn_prefill_mfma(const float* __restri
       }
     }
   }
+  // the split's partial of each query row: o (unnormalised), m, l (a row
+  // that sees none of the split's keys: 0, -inf, 0)
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int i = 16 * wave + 4 * g + r;
-    float* orow = out + (long)(b * Q + i) * QD + h * HD;
-    const bool ok = plim[r] >= 0;
-    const float inv = ok ? 1.0f / lrun[r] : 0.f;
+    if (i >= cnt) continue;
+    float* pp = part + ((((long)b * NH + h) * PF_SPLITS + blockIdx.z) * Q + i) * (HD + 2);
 #pragma unroll
-    for (int d = 0; d < 8; ++d) orow[16 * d + c16] = ok ? o[d][r] * inv : 0.f;
+    for (int d = 0; d < 8; ++d) pp[16 * d + c16] = o[d][r];
+    if (c16 == 0) {
+      pp[HD] = mrun[r];
+      pp[HD + 1] = lrun[r];
+    }
   }
+}
+
+// Merge of the splits of each prefill row, in split order: O / L with
+// weights exp(m_s - max m); rows past the entry's count are zero.  Block =
+// (row, pair of heads), thread = (head, dim) as in k_attn_combine.
+__global__ __launch_bounds__(256) void k_attn_prefill_merge(const float* __restrict__ part, RowPlan plan, int max_pos,
+                                                            float* __restrict__ out) {
+  const int row = blockIdx.x;
+  const int h = blockIdx.y * 2 + (threadIdx.x >> 7);
+  const int d = threadIdx.x & 127;
+  const int Q = plan.Q;
+  const int b = row / Q, i = row - b * Q;
+  const int base = plan.base[b], cnt = min(plan.cnt[b], Q);
+  const int p_last = min(base + cnt - 1, max_pos - 1);
+  float* o = out + (long)row * QD + h * HD + d;
+  int t0, t1, ns = 0;
+  const int n_tiles = cnt > 0 && base >= 0 ? p_last / ATT_TILE + 1 : 0;
+  while (ns < PF_SPLITS && prefill_split(n_tiles, ns, t0, t1)) ++ns;
+  if (i >= cnt || ns == 0) {
+    *o = 0.f;
+    return;
+  }
+  const float* pp = part + (((long)b * NH + h) * PF_SPLITS * Q + i) * (HD + 2);
+  const long sstride = (long)Q * (HD + 2);
+  float mv[PF_SPLITS], lv[PF_SPLITS], ov[PF_SPLITS];
+#pragma unroll
+  for (int sp = 0; sp < PF_SPLITS; ++sp) {
+    const float* q = pp + min(sp, ns - 1) * sstride;
+    mv[sp] = q[HD];
+    lv[sp] = q[HD + 1];
+    ov[sp] = q[d];
+  }
+  float mg = -INFINITY;
+#pragma unroll
+  for (int sp = 0; sp < PF_SPLITS; ++sp) mg = fmaxf(mg, sp < ns ? mv[sp] : -INFINITY);
+  float L = 0.f, O = 0.f;
+#pragma unroll
+  for (int sp = 0; sp < PF_SPLITS; ++sp) {
+    if (sp < ns) {
+      const float w = expf(mv[sp] - mg);
+      L = fmaf(lv[sp], w, L);
+      O = fmaf(ov[sp], w, O);
+    }
+  }
+  *o = O / L;
 }
 
 // The fp32 cache: block (entry b, head h), wavefront w serves rows w, w + 4,
@@ -548,12 +600,15 @@ __global__ __launch_bounds__(256) void k_attn_prefill_f32(const float* __restric
 }
 
 template <>
-void launch_attention_prefill<bf16>(hipStream_t s, const float* q, KvView<bf16> kv, RowPlan plan, int n, float* out) {
-  hipLaunchKernelGGL(k_attn_prefill_mfma, dim3(n, NH), dim3(128), 0, s, q, kv, plan, out);
+void launch_attention_prefill<bf16>(hipStream_t s, const float* q, KvView<bf16> kv, RowPlan plan, int n, float* part,
+                                    float* out) {
+  hipLaunchKernelGGL(k_attn_prefill_mfma, dim3(n, NH, PF_SPLITS), dim3(128), 0, s, q, kv, plan, part);
+  hipLaunchKernelGGL(k_attn_prefill_merge, dim3(n * plan.Q, NH / 2), dim3(256), 0, s, part, plan, kv.max_pos, out);
 }
 template <>
 void launch_attention_prefill<float>(hipStream_t s, const float* q, KvView<float> kv, RowPlan plan, int n,
-                                     float* out) {
+                                     float* part, float* out) {
+  (void)part;
   hipLaunchKernelGGL(k_attn_prefill_f32, dim3(n, NH), dim3(256), 0, s, q, kv, plan, out);
 }
 

@@ -47,8 +47,22 @@ void launch_attention(hipStream_t s, const float* q, KvView<T> kv, RowPlan plan,
 // keys 0 .. base[b] + i of the cache, all of them written before the call.
 // out[b * Q + i] = the head outputs (rows past cnt: zero).  bf16 caches on the
 // matrix cores, fp32 caches on the vector units.
+// bf16: the entry's key tiles are split into at most PF_SPLITS runs of equal
+// length (the last one shorter), one block each, whose partials (o, m, l per
+// row, [entry][head][split][row][130] in part) are merged in split order; the
+// split depends only on the entry's own last position, so a row's result
+// never depends on the other entries of the pass.
+constexpr int PF_SPLITS = 4;
+// Split s of an entry with n_tiles key tiles: tiles [t0, t1); false if empty.
+__host__ __device__ inline bool prefill_split(int n_tiles, int s, int& t0, int& t1) {
+  const int per = (n_tiles + PF_SPLITS - 1) / PF_SPLITS;
+  t0 = s * per;
+  t1 = t0 + per < n_tiles ? t0 + per : n_tiles;
+  return per > 0 && t0 < t1;
+}
 template <typename T>
-void launch_attention_prefill(hipStream_t s, const float* q, KvView<T> kv, RowPlan plan, int n, float* out);
+void launch_attention_prefill(hipStream_t s, const float* q, KvView<T> kv, RowPlan plan, int n, float* part,
+                              float* out);
 
 struct MoeBufs {
   float* bnorm;   // [M][D] normalised rows

@@ -107,8 +107,10 @@ Plan make_plan(const ocrdec_config* c, bool decode_only = false) {
   p.w_rscale = take(M * 4);
   p.w_q = take(M * QD * 4);
   p.w_attn = take(M * QD * 4);
-  // split-KV partials of the decode calls (prefill passes use the prefill attention)
-  p.w_part = take((size_t)c->max_batch * (c->max_k + 1) * NH * (size_t)p.n_chunks_cap * (HD + 2) * 4);
+  // split-KV partials of the decode calls, or of a prefill pass's key splits
+  p.w_part = take(std::max((size_t)c->max_batch * (c->max_k + 1) * NH * (size_t)p.n_chunks_cap,
+                           (size_t)p.prefill_group * NH * PF_SPLITS * PREFILL_CHUNK) *
+                  (HD + 2) * 4);
   p.w_bnorm = take(M * D * 4);
   p.w_ridx = take(M * NSLOT * 4);
   p.w_rgate = take(M * NSLOT * 4);
@@ -519,7 +521,7 @@ template <typename T>
 void attention(ocrdec_model* m, hipStream_t s, PassPath pp, const float* q, KvView<T> kv, RowPlan plan, int B,
                int nch) {
   if (pp.prefill) {
-    launch_attention_prefill<T>(s, q, kv, plan, B, m->b.attn);
+    launch_attention_prefill<T>(s, q, kv, plan, B, m->b.part, m->b.attn);
     return;
   }
   launch_attention<T>(s, q, kv, plan, B, nch, m->p.tiles_per_chunk, m->b.part, m->b.attn);
