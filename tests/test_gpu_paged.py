@@ -164,3 +164,32 @@ def test_load_sequence_on_a_small_pool():
     g1, l1 = _verify_logits(paged, 1, 3, draft)
     assert np.array_equal(g0, g1) and np.array_equal(l0, l1), float(np.abs(l0 - l1).max())
     log("loaded cache on a small pool: refused when full, equal to the full pool after a release")
+
+
+def test_stream_on_a_small_pool_matches_the_oracle():
+    """Continuous batching on a small KV pool checked against the oracle
+    itself (fp32 model on the vector path): six pages through two slots on a
+    4-page pool, K = 3 with the real draft block; for the first and the last
+    page the oracle's teacher-forced pass over the GPU's tokens gives the same
+    greedy token at every position (a mismatch excused only where the
+    oracle's top-2 margin is under 1e-3)."""
+    from oracle import decoder as od
+    cfg = dataclasses.replace(SMALL, dtype="f32")
+    w = synth.Weights(cfg, 104)
+    rng = np.random.default_rng(105)
+    n = 6
+    nv = rng.integers(3, 40, size=n).tolist()
+    npr = rng.integers(1, 6, size=n).tolist()
+    n_out = rng.integers(8, 24, size=n)
+    pages = synth.make_pages(cfg, 106, nv, npr, n_out.tolist())
+    paged = _dec(cfg, w, 2, 3, 128, kv_pages=4)
+    toks, _ = paged.generate_stream(pages, n_out, 3, 2, check_every=2, refill_min=1)
+    assert paged.kv_pages() == (4, 4)
+    orc = od.Oracle(cfg, w.f32)
+    for i in (0, n - 1):
+        g, mg, _, _ = orc.teacher_forced(pages[i].vision, pages[i].prompt, toks[i].tolist())
+        bad = [t for t in range(len(toks[i])) if int(g[t]) != int(toks[i][t])]
+        hard = [(t, int(toks[i][t]), int(g[t]), float(mg[t])) for t in bad if mg[t] >= 1e-3]
+        assert not hard, hard[:5]
+        log(f"stream page {i}: {len(toks[i])} tokens, {len(toks[i]) - len(bad)} equal to the oracle's greedy token, "
+            f"{len(bad)} near ties")
