@@ -176,6 +176,10 @@ def main() -> int:
                     help="base page, vector path: the MoE half of each verifier layer as one persistent "
                          "launch after the router logits, or as the five launches router logits, routing, "
                          "gate/up, down, combine (the same bits)")
+    ap.add_argument("--check-every", type=int, default=8,
+                    help="stream workload: decode steps between host checks of the sequences' lengths")
+    ap.add_argument("--refill-min", type=int, default=4,
+                    help="stream workload: free slots gathered before a batched refill prefill")
     ap.add_argument("--kv-pages", type=int, default=0,
                     help="stream workload: KV page pool size in pages of 64 positions (0: every slot at the "
                          "longest sequence)")
@@ -687,7 +691,7 @@ def bench_stream(args) -> int:
     n_out = np.maximum(np.rint(out_len * args.out_scale).astype(np.int64), 4)
     w = synth.Weights(cfg, wl["weight_seed"])
     pages = synth.make_pages(cfg, wl["input_seed"] + 100, prefix.tolist(), [wl["n_prompt"]] * n, n_out.tolist())
-    check = 8
+    check = max(1, args.check_every)
     max_pos = min(32768, int(prefix.max()) + wl["n_prompt"] + int(n_out.max()) + (check + 2) * (K + 1) + 16)
     dec = ocrdec.Decoder(cfg, w.device_arrays(), max_batch=C, max_k=K, max_positions=max_pos,
                          kv_pages=args.kv_pages)
@@ -705,7 +709,7 @@ def bench_stream(args) -> int:
         trace[i, :len(ar[i])] = torch.from_numpy(ar[i].astype(np.int32))
     trace = trace.cuda()
     thr = int(synth.replacement_probability(0.829, K) * float(1 << 53))
-    refill_min = 8
+    refill_min = max(1, args.refill_min)
     dec.generate_stream(pages, n_out, K, C, trace=trace, seed=3000, threshold=thr, check_every=check, graphs=True,
                         refill_min=refill_min)
     torch.cuda.synchronize()
@@ -726,9 +730,10 @@ def bench_stream(args) -> int:
         "config": {"workload": f"stream_bf16: {n} pages (prefix 256+100n vision rows, n ~ U{{0..9}}, + 32 ids; "
                                "output lengths LogNormal(mean 1085, sigma 0.5) capped at 4096"
                                + (f", scaled x{args.out_scale}" if args.out_scale != 1.0 else "")
-                               + ") through 32 slots, refilled 8 at a time, FastMTP K=1, controlled "
+                               + f") through 32 slots, refilled {refill_min} at a time, FastMTP K=1, controlled "
                                "acceptance 0.829",
-                   "pages": n, "concurrency": C, "K": K, "refill_min": refill_min, "kv_pages": n_pages,
+                   "pages": n, "concurrency": C, "K": K, "refill_min": refill_min, "check_every": check,
+                   "kv_pages": n_pages,
                    "kv_cache_GB": round(n_pages * page_bytes / 1e9, 3)},
         "tokens_per_s": round(n_tok / el, 1), "seconds": round(el, 3), "lossless_vs_ar": bool(lossless),
         "roofline": None, "cpu_baseline": None}), flush=True)
