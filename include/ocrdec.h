@@ -208,7 +208,10 @@ int ocrdec_decode_steps(ocrdec_model* m, void* stream, int B, const int32_t* slo
  * 32,768; 1,024 rows do not fit).  Every call on one GPU -- from any handle --
  * shares that array and leaves its contents behind: calls that overlap on one
  * GPU (other streams, other threads, other handles) race and must not be
- * issued.  The handle's workspace is untouched. */
+ * issued.  The handle's workspace is untouched.  Under capture the call's host
+ * work -- the KV pages it takes, the attention grids sized for the positions
+ * it can reach, the position bookkeeping -- happens once, at capture: record
+ * the call anew for each use rather than replaying one recording. */
 int ocrdec_decode_steps_noalloc(ocrdec_model* m, void* stream, int B, const int32_t* slots, int K, int n_steps,
                                 int32_t* draft, int32_t* greedy, int32_t* n_accepted_out,
                                 int32_t* out_tokens, int32_t* out_len, int out_cap);
