@@ -297,6 +297,48 @@ __device__ __forceinline__ void mfma_pass_abf(const bf16* const (&w)[NB], RowPtr
   }
 }
 
+// The same with the long pipeline of mfma_pass: weights MF_BP chunks ahead in
+// a register ring, rows two chunks in registers and two in LDS (each
+// output's sum over k in the same order: the same bits).
+template <int K, int NT, int NB, int CT, bool CACHED, typename RowPtr>
+__device__ __forceinline__ void mfma_pass_abf_deep(const bf16* const (&w)[NB], RowPtr rowp, int rows,
+                                                   MfChunkT<CT> (&buf)[2][1], f32x4_v (&acc)[NT][NB][1]) {
+  static_assert(K % MF_KC == 0, "K must be a multiple of the chunk");
+  constexpr int NC = K / MF_KC;
+  constexpr int BP = NC < MF_BP ? NC : MF_BP;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const long woff = (long)(lane & 15) * K + 8 * (lane >> 4);
+  const int kg = tid & 15, ri = tid >> 4;
+  const bf16* src[NT];
+  bool ok[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    const int r = ri + 16 * i;
+    ok[i] = r < rows;
+    src[i] = rowp(ok[i] ? r : 0) + 8 * kg;
+  }
+#pragma unroll
+  for (int i = 0; i < NT; ++i)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[i][b][0] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+  uint4 bq[MF_BP][NB][1][MF_SC];
+  uint4 ar[2][NT];
+  mf_load_a_bf(ar[0], src, ok, 0);
+  if (NC > 1) mf_load_a_bf(ar[1], src, ok, 1);
+#pragma unroll
+  for (int c = 0; c < BP; ++c) mf_load_b<K, NB, 1, CACHED>(bq[c], w, woff, c);
+  mf_store_a_bf<NT, CT>(buf[0][0], ar[0], kg, ri);
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    if (c + 2 < NC) mf_load_a_bf(ar[c & 1], src, ok, c + 2);
+    mf_compute<NT, NB, 1, 1, CT>(buf[c & 1], bq[c % MF_BP], acc);
+    if (c + MF_BP < NC) mf_load_b<K, NB, 1, CACHED>(bq[c % MF_BP], w, woff, c + MF_BP);
+    if (c + 1 < NC) mf_store_a_bf<NT, CT>(buf[(c + 1) & 1][0], ar[(c + 1) & 1], kg, ri);
+    __syncthreads();
+  }
+}
+
 // Gate/up: block (x, slot s) computes units j0 .. j0+15, j0 = 64 x + 16 w, of
 // active expert s for every pair routed to it:
 // hx[pair][j] = silu(gate_j . b) * (up_j . b), b the pair's normalised row.
@@ -839,14 +881,17 @@ __global__ __launch_bounds__(256) void k_lm_norm(const float* __restrict__ x, co
 // optionally stored to logits[row][V].
 // G groups of 16 vocab rows per wavefront: w[g] the group's rows, vj[g] this
 // lane's id in it, vok[g] whether that id is the group's to score.
-template <int NT, bool CACHED, int CT, int G>
+template <int NT, bool CACHED, int CT, int G, bool DEEP>
 __device__ __forceinline__ void lm_pass(const bf16* const (&w)[G], const bf16* __restrict__ xn, int p0, int rows,
                                         const int (&vj)[G], const bool (&vok)[G], int V, float* __restrict__ logits,
                                         float (&bv)[4][16 * CT], int (&bi)[4][16 * CT], MfChunkT<CT> (&buf)[2][1]) {
   const int wave = wave_id(), lane = lane_id();
   f32x4_v acc[NT][G][1];
   auto rowp = [=](int r) { return xn + (long)(p0 + r) * D; };
-  mfma_pass_abf<D, NT, G, CT, CACHED>(w, rowp, rows, buf, acc);
+  if constexpr (DEEP)
+    mfma_pass_abf_deep<D, NT, G, CT, CACHED>(w, rowp, rows, buf, acc);
+  else
+    mfma_pass_abf<D, NT, G, CT, CACHED>(w, rowp, rows, buf, acc);
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
 #pragma unroll
@@ -885,7 +930,10 @@ constexpr int LM_G = 2;   // groups of 16 vocab rows per wavefront of the matrix
 // dispatcher deals blocks to the 8 XCDs in turn), so that one L2 serves the
 // strip's repeated reads; the row passes then run side by side instead of
 // one after another.  Ordinary weight loads either way (measured faster than
-// non-temporal ones here, also for one pass).
+// non-temporal ones here, also for one pass).  The split passes take the long
+// load pipeline (mfma_pass_abf_deep: 2.59-2.61 against 2.63 ms per 256-row
+// verify call over 32,768 positions); one pass keeps the short one (the long
+// one measured the same there, at half the occupancy).
 template <bool SPLIT, int CT>
 __global__ __launch_bounds__(256) void k_lmhead_mfma(const bf16* __restrict__ xn, const bf16* __restrict__ W,
                                                      int V, int M, int nblk, float* __restrict__ part_val,
@@ -924,11 +972,11 @@ __global__ __launch_bounds__(256) void k_lmhead_mfma(const bf16* __restrict__ xn
     const int p0 = pi * RB;
     const int rows = min(RB, M - p0);
     if (CT == 1 || rows <= 16) {
-      lm_pass<1, CACHED, CT, LM_G>(wc, xn, p0, rows, vj, vok, V, logits, bv, bi, buf);
+      lm_pass<1, CACHED, CT, LM_G, SPLIT>(wc, xn, p0, rows, vj, vok, V, logits, bv, bi, buf);
     } else if (CT == 2 || rows <= 32) {
-      lm_pass<(CT < 2 ? CT : 2), CACHED, CT, LM_G>(wc, xn, p0, rows, vj, vok, V, logits, bv, bi, buf);
+      lm_pass<(CT < 2 ? CT : 2), CACHED, CT, LM_G, SPLIT>(wc, xn, p0, rows, vj, vok, V, logits, bv, bi, buf);
     } else {
-      lm_pass<CT, CACHED, CT, LM_G>(wc, xn, p0, rows, vj, vok, V, logits, bv, bi, buf);
+      lm_pass<CT, CACHED, CT, LM_G, SPLIT>(wc, xn, p0, rows, vj, vok, V, logits, bv, bi, buf);
     }
     __syncthreads();
     // slab h of the block: wavefronts 4 h / G .. 4 (h + 1) / G - 1
