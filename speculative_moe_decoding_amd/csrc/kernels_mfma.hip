@@ -29,6 +29,11 @@ constexpr int MF_KC = 128;           // k per LDS chunk
 constexpr int MF_SC = MF_KC / 32;    // MFMA k-steps per chunk
 constexpr int MF_MT = 4;             // 16-row tiles per pass
 constexpr int MF_ROWS = 16 * MF_MT;  // activation rows per pass
+// Activation rows per block of the strip GEMMs: 32 for passes of up to 512
+// rows (more blocks in flight: base-page prefill 2.94 against 3.05 ms), else
+// MF_ROWS (Gundam page 6.55 against 6.68 ms).  Each output's sum over k is the
+// same either way.
+inline int dense_rows_per_block(int M) { return M <= 512 ? 32 : MF_ROWS; }
 constexpr int MF_BP = 3;             // weight chunks in flight per wavefront
 
 // One LDS chunk of CT tiles: f[tile][step][mf_slot(step, lane)] is lane's A
@@ -581,13 +586,13 @@ template <int K, int MODE>
 __global__ __launch_bounds__(256) void k_dense_mfma(const float* __restrict__ a, long lda,
                                                     const float* __restrict__ gain, const float* __restrict__ rsc,
                                                     const bf16* __restrict__ W0, const bf16* __restrict__ W1, int M,
-                                                    float* __restrict__ out, long ldo, QkvOut qo) {
+                                                    float* __restrict__ out, long ldo, QkvOut qo, int rt) {
   constexpr int NB = (MODE == DM_SWIGLU || MODE == DM_QKV) ? 2 : 1;
   __shared__ MfChunk buf[2][2];
   __shared__ float rs[MF_ROWS];
   const int wave = wave_id(), lane = lane_id();
-  const int m0 = blockIdx.y * MF_ROWS;
-  const int rows = min(MF_ROWS, M - m0);
+  const int m0 = blockIdx.y * rt;
+  const int rows = min(rt, M - m0);
   const bf16* w[NB];
   int sec = 0, h = 0, n0 = 0;
   if constexpr (MODE == DM_QKV) {
@@ -818,7 +823,8 @@ void launch_qkv_rope_ks(hipStream_t s, const float* x, const float* gain, float 
 
 bool launch_gemv_mfma(hipStream_t s, int K, Epi epi, const float* a, long lda, const float* gain, float eps,
                       const bf16* W0, const bf16* W1, int N, int M, float* out, long ldo, float* rscale) {
-  const dim3 grid(N / 64, (M + MF_ROWS - 1) / MF_ROWS);
+  const int rt = dense_rows_per_block(M);
+  const dim3 grid(N / 64, (M + rt - 1) / rt);
   const QkvOut none{};
   if (gain != nullptr) {
     if (K != D) return false;  // the normed inputs are model rows
@@ -826,7 +832,7 @@ bool launch_gemv_mfma(hipStream_t s, int K, Epi epi, const float* a, long lda, c
   }
 #define OCR_DM(KV, MODEV) \
   hipLaunchKernelGGL((k_dense_mfma<KV, MODEV>), grid, dim3(256), 0, s, a, lda, gain, rscale, W0, W1, M, out, ldo, \
-                     none)
+                     none, rt)
   if (K == D && epi == EPI_ADD) OCR_DM(D, DM_ADD);
   else if (K == D && epi == EPI_SWIGLU) OCR_DM(D, DM_SWIGLU);
   else if (K == D && epi == EPI_STORE) OCR_DM(D, DM_STORE);
@@ -841,8 +847,9 @@ void launch_qkv_rope_mfma(hipStream_t s, const float* x, const float* gain, floa
                           RowPlan plan, float* q, KvView<bf16> kv, const float2* rope, float* rscale) {
   const QkvOut qo{plan, q, kv, rope};
   hipLaunchKernelGGL((k_row_rms<D>), dim3((M + 3) / 4), dim3(256), 0, s, x, (long)D, M, eps, rscale);
-  hipLaunchKernelGGL((k_dense_mfma<D, DM_QKV>), dim3(3 * NH, (M + MF_ROWS - 1) / MF_ROWS), dim3(256), 0, s, x,
-                     (long)D, gain, rscale, wqkv, nullptr, M, nullptr, 0L, qo);
+  const int rt = dense_rows_per_block(M);
+  hipLaunchKernelGGL((k_dense_mfma<D, DM_QKV>), dim3(3 * NH, (M + rt - 1) / rt), dim3(256), 0, s, x, (long)D, gain,
+                     rscale, wqkv, nullptr, M, nullptr, 0L, qo, rt);
 }
 
 // LM head rows for the matrix cores: xn[m] = RMSNorm(x[src(m)]) * gain, one
