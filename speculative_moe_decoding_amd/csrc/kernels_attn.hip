@@ -27,6 +27,14 @@ template <typename T> struct AttTile;
 template <> struct AttTile<float> {
   typedef float4 K4;   // 4 key dims
   typedef float2 V2;   // 2 value dims
+  __device__ static __forceinline__ float4 stage_q(const float4& q) { return q; }
+  __device__ static __forceinline__ float dot4(const float4& qv, const K4& kv4, float sc) {
+    sc = fmaf(qv.x, kv4.x, sc);
+    sc = fmaf(qv.y, kv4.y, sc);
+    sc = fmaf(qv.z, kv4.z, sc);
+    sc = fmaf(qv.w, kv4.w, sc);
+    return sc;
+  }
   __device__ static __forceinline__ float4 k(const K4& v) { return v; }
   __device__ static __forceinline__ float2 v(const V2& x) { return x; }
   __device__ static __forceinline__ void stage(const uint4& kr, const uint4& vr, int d0, int t, K4 (*Kq)[KQ_STRIDE],
@@ -41,6 +49,27 @@ template <> struct AttTile<float> {
 template <> struct AttTile<bf16> {
   typedef uint2 K4;
   typedef uint32_t V2;
+  // The query's 4 dims as bf16 pairs: hi = bf16(q), lo = bf16(q - hi) (q to
+  // about 16 bits), laid out (hi d0 d1, hi d2 d3, lo d0 d1, lo d2 d3).
+  __device__ static __forceinline__ float4 stage_q(const float4& q) {
+    const uint32_t h01 = pack_bf16x2(q.x, q.y), h23 = pack_bf16x2(q.z, q.w);
+    const uint32_t l01 = pack_bf16x2(rem_lo(q.x, h01), rem_hi(q.y, h01));
+    const uint32_t l23 = pack_bf16x2(rem_lo(q.z, h23), rem_hi(q.w, h23));
+    return make_float4(__uint_as_float(h01), __uint_as_float(h23), __uint_as_float(l01), __uint_as_float(l23));
+  }
+  // sc + q . k over 4 dims: the bf16 key pairs against the query's hi and lo
+  // pairs by v_dot2c_f32_bf16 (products of bf16 values are exact in fp32)
+  __device__ static __forceinline__ float dot4(const float4& qp, const K4& k, float sc) {
+    sc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, __float_as_uint(qp.x)),
+                                         __builtin_bit_cast(bf16x2_v, k.x), sc, false);
+    sc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, __float_as_uint(qp.y)),
+                                         __builtin_bit_cast(bf16x2_v, k.y), sc, false);
+    sc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, __float_as_uint(qp.z)),
+                                         __builtin_bit_cast(bf16x2_v, k.x), sc, false);
+    sc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, __float_as_uint(qp.w)),
+                                         __builtin_bit_cast(bf16x2_v, k.y), sc, false);
+    return sc;
+  }
   __device__ static __forceinline__ float4 k(const K4& v) {
     return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u), __uint_as_float(v.y << 16),
                        __uint_as_float(v.y & 0xffff0000u));
@@ -59,7 +88,8 @@ template <> struct AttTile<bf16> {
 
 // One query row (query i of the block's sequence, visible keys 0..plim) against
 // the staged tile of keys kt .. kt+63, by one wavefront: lane = key for the
-// scores (q . k over 128 dims, 4 at a time, in order), then lane = value-dim
+// scores (q . k over 128 dims, 4 at a time, in order; bf16 caches: the query's
+// hi and lo bf16 parts against the keys, AttTile::dot4), then lane = value-dim
 // pair for the output; the online-softmax state (mrun, lrun, o0, o1) is the
 // query's.  pw is the wavefront's 64-float LDS row for the probabilities.
 template <typename T>
@@ -72,14 +102,7 @@ __device__ __forceinline__ void attn_tile_query(const float4* __restrict__ qrow,
   const float scale = 0.08838834764831845f;  // 1 / sqrt(128)
   float sc = 0.f;
 #pragma unroll 8
-  for (int d4 = 0; d4 < HD / 4; ++d4) {
-    const float4 qv = qrow[d4];
-    const float4 kv4 = AT::k(Kq[d4][lane]);
-    sc = fmaf(qv.x, kv4.x, sc);
-    sc = fmaf(qv.y, kv4.y, sc);
-    sc = fmaf(qv.z, kv4.z, sc);
-    sc = fmaf(qv.w, kv4.w, sc);
-  }
+  for (int d4 = 0; d4 < HD / 4; ++d4) sc = AT::dot4(qrow[d4], Kq[d4][lane], sc);
   sc = sc * scale;
   const bool vis = (kt + lane) <= plim;
   const float mt = wave_max_dpp(vis ? sc : -INFINITY);
@@ -243,7 +266,7 @@ __global__ __launch_bounds__(256) void k_attn_partial(const float* __restrict__ 
 #pragma unroll
   for (int j = 0; j < NQV; ++j) {
     const int e = tid + 256 * j, i = e / (HD / 4);
-    qs[i][e % (HD / 4)] = (i < cnt) ? qv[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+    qs[i][e % (HD / 4)] = (i < cnt) ? AT::stage_q(qv[j]) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   if (cnt <= 0 || k0 > p_last) return;
   const int n_tiles = min(tiles_per_chunk, (p_last - k0) / ATT_TILE + 1);
