@@ -159,12 +159,13 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="base_page_bf16",
                     choices=["base_page_bf16", "concurrent32_bf16", "stream_bf16", "longctx_layer_bf16",
-                             "prefill_bf16"],
+                             "prefill_bf16", "crossover_bf16"],
                     help="base_page_bf16 (default): batch 1, K=3; concurrent32_bf16: static batch of 32 "
                          "pages, K=1, on the matrix-core path; longctx_layer_bf16: one MoE layer + LM head "
                          "verifying 4 rows per sequence over 32,764 cached positions, B = 1, 4, 16, 64; "
                          "prefill_bf16: the prefill of one base page (288 rows) and of one Gundam page "
-                         "(1,188 rows), --steps timed repetitions each")
+                         "(1,188 rows), --steps timed repetitions each; crossover_bf16: the 12-layer verify "
+                         "call on the vector and the matrix-core path at B = 1, 2, 4, 8, 16 base pages, K = 3")
     ap.add_argument("--sweep-k", action="store_true",
                     help="base page: output tokens/s for K = 0..3, graph-replayed and eager steps, at the pages' "
                          "per-K acceptance rates")
@@ -214,6 +215,8 @@ def main() -> int:
         return bench_longctx(args)
     if args.workload == "prefill_bf16":
         return bench_prefill(args)
+    if args.workload == "crossover_bf16":
+        return bench_crossover(args)
 
     import numpy as np
     import torch
@@ -874,6 +877,86 @@ def bench_longctx(args) -> int:
         "roofline": {"bound": "hbm", "achieved": best["GB_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(best["GB_per_s"] / HBM_PEAK_GBS, 4), "traffic": None,
                      "kernel": f"whole verify call at B={best['B']}"},
+        "batches": rows_out,
+        "cpu_baseline": None,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def bench_crossover(args) -> int:
+    """Where the matrix cores overtake the wavefront GEMV: the verify call of the
+    12-layer bf16 decoder (weights seed 1234) on the vector path and on the
+    matrix-core path, for B = 1, 2, 4, 8, 16 sequences x (K + 1) = 4 rows (4 to 64
+    rows per call), each sequence after its own base-page prefix (256 vision + 32
+    prompt rows, input seed 2001) and random drafts.  Per path and batch: the
+    verify-call time (HIP events around back-to-back calls), its algorithmic bytes
+    and rate, and the expert kernels' time (gate/up + down)."""
+    import numpy as np
+    import torch
+    from speculative_moe_decoding_amd import ocrdec, synth
+
+    wl = synth.WORKLOADS["base_page_bf16"]
+    cfg, K = wl["cfg"], 3
+    t = time.time()
+    w = synth.Weights(cfg, wl["weight_seed"])
+    log(f"weights generated in {time.time() - t:.1f}s")
+    reps = max(4, min(args.steps, 40))
+    P = wl["n_vision"] + wl["n_prompt"]
+    rows_out = []
+    for path_name, path in (("vector", ocrdec.OCRDEC_PATH_VECTOR), ("matrix", ocrdec.OCRDEC_PATH_MATRIX)):
+        for B in (1, 2, 4, 8, 16):
+            dec = ocrdec.Decoder(cfg, w.device_arrays(), max_batch=B, max_k=K, max_positions=P + 64, path=path)
+            pages = synth.make_pages(cfg, wl["input_seed"], [wl["n_vision"]] * B, [wl["n_prompt"]] * B, [1] * B)
+            dec.prefill(pages)
+            rng = np.random.default_rng([6000, B])
+            draft = torch.from_numpy(rng.integers(0, cfg.vocab, size=(B, K)).astype(np.int32)).cuda()
+            greedy = dec.i32(B, K + 1)
+            for _ in range(3):
+                dec.verify(B, K, draft, greedy=greedy)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                dec.verify(B, K, draft, greedy=greedy)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            ocrdec.ocrdec_expert_timing(dec.h, True)
+            for _ in range(reps):
+                dec.verify(B, K, draft, greedy=greedy)
+            st = ocrdec.ocrdec_expert_stats(dec.h)
+            ocrdec.ocrdec_expert_timing(dec.h, False)
+            U = st["expert_sets"] / max(1, st["n_gate_up"])
+            kv_bytes = B * (P * KV_POS_BYTES + (K + 1) * KV_POS_BYTES)
+            nbytes = L * (DENSE_LAYER_BYTES + U * 3 * I * D * 2 + kv_bytes) + LM_HEAD_BYTES
+            up_us = st["ms_gate_up"] / max(1, st["n_gate_up"]) * 1e3
+            dn_us = st["ms_down"] / max(1, st["n_down"]) * 1e3
+            row = {"path": path_name, "B": B, "rows": B * (K + 1), "verify_ms": round(ms, 4),
+                   "GB_per_call": round(nbytes / 1e9, 4), "GB_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                   "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                   "active_experts": round(U, 2), "expert_gate_up_us": round(up_us, 2),
+                   "expert_down_us": round(dn_us, 2),
+                   "expert_GB_per_s": round(U * 3 * I * D * 2 / ((up_us + dn_us) * 1e-6) / 1e9, 1)}
+            rows_out.append(row)
+            log(json.dumps(row))
+            dec.close()
+            del dec
+            torch.cuda.empty_cache()
+    by = {(r["path"], r["B"]): r for r in rows_out}
+    cross = [B for B in (1, 2, 4, 8, 16) if by[("matrix", B)]["verify_ms"] < by[("vector", B)]["verify_ms"]]
+    best = by[("vector", 1)]
+    result = {
+        "metric": "verify-call time, 12-layer MoE decoder (bf16), vector GEMV against matrix cores",
+        "value": best["GB_per_s"], "unit": "GB/s", "n_gpus": 1, "steps": reps, "warmup": 3,
+        "ms_per_step": best["verify_ms"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "crossover_bf16: 12-layer verify calls, K = 3, B = 1..16 base pages (288-row "
+                               "prefixes), vector and matrix-core paths", "batches": [1, 2, 4, 8, 16]},
+        "roofline": {"bound": "hbm", "achieved": best["GB_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(best["GB_per_s"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "whole verify call, vector path, B=1"},
+        "matrix_faster_from_batch": min(cross) if cross else None,
         "batches": rows_out,
         "cpu_baseline": None,
     }
