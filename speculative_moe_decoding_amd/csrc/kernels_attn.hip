@@ -22,7 +22,8 @@ constexpr int KQ_STRIDE = ATT_TILE + 1;
 
 // LDS tile formats: the fp32 model stages keys / values widened to fp32; the
 // bf16 model keeps them in bf16 (half the LDS, so more blocks per CU keep more
-// KV reads in flight) and widens them as they are read.
+// KV reads in flight): its scores take the keys as they are (dot4), its
+// values are widened as they are read.
 template <typename T> struct AttTile;
 template <> struct AttTile<float> {
   typedef float4 K4;   // 4 key dims
@@ -35,7 +36,6 @@ template <> struct AttTile<float> {
     sc = fmaf(qv.w, kv4.w, sc);
     return sc;
   }
-  __device__ static __forceinline__ float4 k(const K4& v) { return v; }
   __device__ static __forceinline__ float2 v(const V2& x) { return x; }
   __device__ static __forceinline__ void stage(const uint4& kr, const uint4& vr, int d0, int t, K4 (*Kq)[KQ_STRIDE],
                                                V2 (*Vs)[HD / 2]) {
@@ -69,10 +69,6 @@ template <> struct AttTile<bf16> {
     sc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, __float_as_uint(qp.w)),
                                          __builtin_bit_cast(bf16x2_v, k.y), sc, false);
     return sc;
-  }
-  __device__ static __forceinline__ float4 k(const K4& v) {
-    return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u), __uint_as_float(v.y << 16),
-                       __uint_as_float(v.y & 0xffff0000u));
   }
   __device__ static __forceinline__ float2 v(const V2& x) {
     return make_float2(__uint_as_float(x << 16), __uint_as_float(x & 0xffff0000u));
