@@ -482,20 +482,22 @@ void launch_router(hipStream_t s, const float* x, const float* gain, float eps, 
 }
 
 // Gather the activation rows m < m_act <= MR (row_of(m) into src) into LDS;
-// 256 threads, the loads of every row issued before any LDS store.
+// 256 threads, 16-byte loads (rows are whole multiples of 16 bytes), the loads
+// of every row issued before any LDS store.
 template <int K, int MR, typename SrcRow>
 __device__ __forceinline__ void gather_rows(const float* __restrict__ src, SrcRow row_of, int m_act, float* xs) {
-  static_assert(K % 256 == 0 || K == DI, "row length");
-  constexpr int J = (K + 255) / 256;
-  float v[MR][J];
+  static_assert(K % 4 == 0, "row length");
+  constexpr int K4 = K / 4;
+  constexpr int J = (K4 + 255) / 256;
+  float4 v[MR][J];
 #pragma unroll
   for (int m = 0; m < MR; ++m) {
     if (m < m_act) {
-      const float* r = src + (long)row_of(m) * K;
+      const float4* r = reinterpret_cast<const float4*>(src + (long)row_of(m) * K);
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         const int k = threadIdx.x + 256 * j;
-        v[m][j] = (k < K) ? r[k] : 0.f;
+        v[m][j] = (k < K4) ? r[k] : make_float4(0.f, 0.f, 0.f, 0.f);
       }
     }
   }
@@ -505,7 +507,7 @@ __device__ __forceinline__ void gather_rows(const float* __restrict__ src, SrcRo
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         const int k = threadIdx.x + 256 * j;
-        if (k < K) xs[m * K + k] = v[m][j];
+        if (k < K4) reinterpret_cast<float4*>(xs + m * K)[k] = v[m][j];
       }
     }
   }
