@@ -159,13 +159,15 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="base_page_bf16",
                     choices=["base_page_bf16", "concurrent32_bf16", "stream_bf16", "longctx_layer_bf16",
-                             "prefill_bf16", "crossover_bf16"],
+                             "prefill_bf16", "crossover_bf16", "oracle_cpu"],
                     help="base_page_bf16 (default): batch 1, K=3; concurrent32_bf16: static batch of 32 "
                          "pages, K=1, on the matrix-core path; longctx_layer_bf16: one MoE layer + LM head "
                          "verifying 4 rows per sequence over 32,764 cached positions, B = 1, 4, 16, 64; "
                          "prefill_bf16: the prefill of one base page (288 rows) and of one Gundam page "
                          "(1,188 rows), --steps timed repetitions each; crossover_bf16: the 12-layer verify "
-                         "call on the vector and the matrix-core path at B = 1, 2, 4, 8, 16 base pages, K = 3")
+                         "call on the vector and the matrix-core path at B = 1, 2, 4, 8, 16 base pages, K = 3; oracle_cpu: "
+                         "the oracle alone on the host cores (no GPU work), bounded samples of the 2-layer "
+                         "fp32 model, the base page and the Gundam page")
     ap.add_argument("--sweep-k", action="store_true",
                     help="base page: output tokens/s for K = 0..3, graph-replayed and eager steps, at the pages' "
                          "per-K acceptance rates")
@@ -217,6 +219,8 @@ def main() -> int:
         return bench_prefill(args)
     if args.workload == "crossover_bf16":
         return bench_crossover(args)
+    if args.workload == "oracle_cpu":
+        return bench_oracle_cpu(args)
 
     import numpy as np
     import torch
@@ -960,6 +964,85 @@ def bench_crossover(args) -> int:
         "batches": rows_out,
         "cpu_baseline": None,
     }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def bench_oracle_cpu(args) -> int:
+    """The cpu_baseline leg over more of the workloads: the oracle, as it stands,
+    timed on the host cores with no GPU work, free-running over bounded samples
+    -- a few steps after each page's prefix, the prefill timed apart and left
+    out: the 2-layer fp32 model (K = 0, and K = 3 with the real draft block),
+    the base page of the 12-layer bf16 model (K = 0, and K = 3 with the
+    controlled drafts of its acceptance, the draft block run for cost) and the
+    Gundam page (K = 3, controlled).  Tokens per second of those steps."""
+    from oracle import decoder as od
+    from speculative_moe_decoding_amd import synth
+
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except Exception:
+        cores = os.cpu_count()
+    cores = min(cores, int(os.environ.get("OMP_NUM_THREADS", cores)))
+
+    def timed(orc, page, K, proposer, draft_for_cost, n_steps):
+        """(tokens, tokens committed by the steps, seconds of the steps, seconds
+        of the prefill): the clock starts when the first step asks for its depth."""
+        n_out = n_steps * (K + 1) + 2
+        mark = []
+
+        def depth(step):
+            if step == 0:
+                mark.append(time.time())
+            return K
+
+        t0 = time.time()
+        toks, steps = orc.generate_spec(page.vision, page.prompt, n_out, K, proposer=proposer,
+                                        draft_for_cost=draft_for_cost, max_steps=n_steps, k_schedule=depth)
+        t1 = time.time()
+        committed = sum(s.accepted + 1 for s in steps)
+        return toks, committed, t1 - mark[0], mark[0] - t0
+
+    def ar_proposer(step, out, K):
+        return []
+
+    rows = []
+    plan = [("tiny_fp32_2layer", [(0, 16, "autoregressive"), (3, 8, "real draft")]),
+            ("base_page_bf16", [(0, 16, "autoregressive"), (3, 4, "controlled")]),
+            ("gundam_page_bf16", [(0, 14, "autoregressive, untimed (its trace feeds the controlled drafts)"),
+                                  (3, 3, "controlled")])]
+    for wl_name, runs in plan:
+        wl = synth.WORKLOADS[wl_name]
+        t = time.time()
+        w = synth.Weights(wl["cfg"], wl["weight_seed"])
+        page = synth.make_pages(wl["cfg"], wl["input_seed"], [wl["n_vision"]], [wl["n_prompt"]],
+                                [wl["n_out"]])[0]
+        orc = od.Oracle(wl["cfg"], w.f32)
+        log(f"{wl_name}: weights in {time.time() - t:.1f}s")
+        trace = None
+        for K, n_steps, kind in runs:
+            if K == 0:
+                toks, committed, ts, tp = timed(orc, page, 0, ar_proposer, False, n_steps)
+                trace = toks
+            elif kind == "real draft":
+                toks, committed, ts, tp = timed(orc, page, K, None, False, n_steps)
+            else:
+                p = synth.replacement_probability(0.576, K)
+                prop = od.controlled_proposer(trace, 3000, p, wl["cfg"].vocab)
+                toks, committed, ts, tp = timed(orc, page, K, prop, True, n_steps)
+                assert toks == trace[:len(toks)], "controlled run is not lossless"
+            row = {"workload": wl_name, "K": K, "drafts": kind, "steps": n_steps, "tokens": committed,
+                   "seconds": round(ts, 2), "tok_per_s": round(committed / ts, 3),
+                   "prefill_s_untimed": round(tp, 2), "prefix_rows": page.prefix_len}
+            if not kind.endswith("untimed (its trace feeds the controlled drafts)"):
+                rows.append(row)
+            log(json.dumps(row))
+        del orc, w
+    result = {"metric": "oracle tokens/s on the host cores (fp64 NumPy; a baseline, not the target)",
+              "value": next(r["tok_per_s"] for r in rows if r["workload"] == "base_page_bf16" and r["K"] == 3),
+              "unit": "tokens/s", "n_gpus": 0, "cores": cores, "dtype": "f64", "data": "synthetic",
+              "config": {"workload": "oracle_cpu: bounded free-running samples, prefill untimed"},
+              "runs": rows}
     print(json.dumps(result), flush=True)
     return 0
 
