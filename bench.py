@@ -148,7 +148,9 @@ def plain_read(dec, nbytes, n_launches, n_regions=L):
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=405)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed decode steps (default: one page's output at K = 3: 405 steps for the base "
+                         "page's 1,085 tokens, 1,332 for the Gundam page's 3,568; 405 for the other workloads)")
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--k", type=int, default=3)
     ap.add_argument("--alpha", type=float, default=0.576)
@@ -158,9 +160,11 @@ def main() -> int:
     ap.add_argument("--eager", action="store_true", help="issue the four calls per step instead of graph replays")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="base_page_bf16",
-                    choices=["base_page_bf16", "concurrent32_bf16", "stream_bf16", "longctx_layer_bf16",
+                    choices=["base_page_bf16", "gundam_page_bf16", "concurrent32_bf16", "stream_bf16",
+                             "longctx_layer_bf16",
                              "prefill_bf16", "crossover_bf16", "oracle_cpu"],
-                    help="base_page_bf16 (default): batch 1, K=3; concurrent32_bf16: static batch of 32 "
+                    help="base_page_bf16 (default): batch 1, K=3; gundam_page_bf16: the same on a Gundam "
+                         "page (1,156 vision + 32 prompt rows, 3,568 output tokens); concurrent32_bf16: static batch of 32 "
                          "pages, K=1, on the matrix-core path; longctx_layer_bf16: one MoE layer + LM head "
                          "verifying 4 rows per sequence over 32,764 cached positions, B = 1, 4, 16, 64; "
                          "prefill_bf16: the prefill of one base page (288 rows) and of one Gundam page "
@@ -189,6 +193,8 @@ def main() -> int:
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 512 MiB device copy (calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
+    if args.steps is None:
+        args.steps = 1332 if args.workload == "gundam_page_bf16" else 405
     if args.instrumented_steps < 1 or args.replay_rounds < 1 or args.replay_routings < 1:
         ap.error("--instrumented-steps, --replay-rounds and --replay-routings must be at least 1")
     if args.copy_probe:
@@ -226,8 +232,10 @@ def main() -> int:
     import torch
     from speculative_moe_decoding_amd import ocrdec, synth
 
-    K, S, W = args.k, args.steps, args.warmup
-    wl = synth.WORKLOADS["base_page_bf16"]
+    wl_name = "gundam_page_bf16" if args.workload == "gundam_page_bf16" else "base_page_bf16"
+    wl = synth.WORKLOADS[wl_name]
+    K, W = args.k, args.warmup
+    S = args.steps
     cfg = wl["cfg"]
     t = time.time()
     w = synth.Weights(cfg, wl["weight_seed"])
@@ -417,9 +425,10 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "base_page_bf16: 12-layer DeepSeek-3B-MoE decoder (d=1280, 64+2 experts, top-6, "
-                        "V=129280), random-init bf16 weights, one page = 256 vision + 32 prompt rows, "
-                        "batch 1, FastMTP K=3 with controlled acceptance 57.6%",
+            "workload": f"{wl_name}: 12-layer DeepSeek-3B-MoE decoder (d=1280, 64+2 experts, top-6, "
+                        f"V=129280), random-init bf16 weights, one page = {wl['n_vision']} vision + "
+                        f"{wl['n_prompt']} prompt rows, batch 1, FastMTP K={K} with controlled acceptance "
+                        f"{100 * args.alpha:.1f}%",
             "batch": B, "K": K, "alpha_target": args.alpha, "prefix_rows": P,
             "compute": "bf16 weights and KV cache, fp32 activations and accumulation",
             "launch": "eager calls" if args.eager else "HIP graph per decode step",
@@ -452,7 +461,7 @@ def main() -> int:
         "window": {"tau": round(tau, 4), "alpha": round((tau - 1) / K, 4), "tokens": committed,
                    "tok_per_s": round(win_tok_s, 2)},
         "lossless_vs_ar": lossless,
-        "pages_per_s": round(1.0 / (t_prefill + 1085 / tok_s), 4),
+        "pages_per_s": round(1.0 / (t_prefill + wl["n_out"] / tok_s), 4),
         "prefill_ms": round(t_prefill * 1e3, 2),
         "ar_tok_per_s": round((n_trace - 1) / t_ar, 1),
         "verify_step": {"ms": round(float(verify_ms.mean()), 4), "GB_per_s": round(verify_gbs, 1),
